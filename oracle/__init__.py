@@ -1,0 +1,226 @@
+"""Oracle: plain CPU reference of LUT-based approximate FP32 multiplication.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package. The product library does not import
+it, and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C99, single-threaded, double
+accumulation); this module only builds and loads it and marshals numpy arrays.
+Sources: "ApproxTrain: Fast Simulation of Approximate Multipliers for DNN
+Training and Inference" (arXiv 2209.04161) -- Section V-A Algorithm 1 (table
+generation), Section V Algorithm 2 (AMSim product), Section VI-B Algorithms 3-4
+(Conv2D forward and backprop).
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+MUL_FN = ctypes.CFUNCTYPE(ctypes.c_float, ctypes.c_float, ctypes.c_float)
+
+
+def build():
+    """Compile oracle.c with gcc (no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-o", _LIB, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if (not os.path.exists(_LIB)) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.POINTER
+        c_int, c_i64 = ctypes.c_int, ctypes.c_int64
+        vp = ctypes.c_void_p
+        L.orc_mul_exact.argtypes = [ctypes.c_float, ctypes.c_float]
+        L.orc_mul_exact.restype = ctypes.c_float
+        L.orc_mul_mitchell.argtypes = [ctypes.c_float, ctypes.c_float]
+        L.orc_mul_mitchell.restype = ctypes.c_float
+        L.orc_lut_generate.argtypes = [c_int, vp, vp]
+        L.orc_lut_generate.restype = c_int
+        L.orc_lut_perturb.argtypes = [c_int, vp, vp]
+        L.orc_lut_perturb.restype = None
+        L.orc_amsim_bits.argtypes = [ctypes.c_uint32, ctypes.c_uint32, vp, c_int]
+        L.orc_amsim_bits.restype = ctypes.c_uint32
+        L.orc_amsim_many.argtypes = [c_i64, vp, vp, vp, c_int, vp]
+        L.orc_amsim_many.restype = None
+        L.orc_gemm.argtypes = [c_int] * 5 + [vp, c_int, vp, c_int, vp, c_int, vp, vp]
+        L.orc_gemm.restype = None
+        L.orc_gemm_at.argtypes = [c_int] * 5 + [vp, c_int, vp, c_int, vp, c_int,
+                                                 c_i64, vp, vp, vp, vp]
+        L.orc_gemm_at.restype = None
+        for name in ("orc_conv2d_fwd", "orc_conv2d_dgrad", "orc_conv2d_wgrad"):
+            f = getattr(L, name)
+            f.argtypes = [c_int] * 11 + [vp, vp, vp, c_int, c_i64, vp, vp, vp]
+            f.restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+# ---------------------------------------------------------------- tables
+
+def lut_generate(M, model):
+    """Algorithm 1. ``model`` is "exact", "mitchell" or a Python callable
+    float(float, float). Returns a uint16 array of 4**M entries."""
+    L = lib()
+    out = np.zeros(1 << (2 * M), dtype=np.uint16)
+    keep = None
+    if model == "exact":
+        fp = ctypes.cast(L.orc_mul_exact, ctypes.c_void_p)
+    elif model == "mitchell":
+        fp = ctypes.cast(L.orc_mul_mitchell, ctypes.c_void_p)
+    else:
+        keep = MUL_FN(lambda a, b: float(model(a, b)))
+        fp = ctypes.cast(keep, ctypes.c_void_p)
+    rc = L.orc_lut_generate(M, fp, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"orc_lut_generate failed with {rc}")
+    return out
+
+
+def lut_perturb(M, lut, delta):
+    """Move each entry's mantissa field by delta (+1/-1), saturating; carry kept."""
+    out = np.array(lut, dtype=np.uint16, copy=True)
+    d = np.ascontiguousarray(delta, dtype=np.int8)
+    assert d.size == out.size == (1 << (2 * M))
+    lib().orc_lut_perturb(M, _ptr(out), _ptr(d))
+    return out
+
+
+# ---------------------------------------------------------------- products
+
+def amsim_bits(a_bits, b_bits, lut, M):
+    """Algorithm 2 element-wise on uint32 bit patterns (same shapes)."""
+    a = np.ascontiguousarray(a_bits, dtype=np.uint32).ravel()
+    b = np.ascontiguousarray(b_bits, dtype=np.uint32).ravel()
+    assert a.size == b.size
+    lut = np.ascontiguousarray(lut, dtype=np.uint16)
+    out = np.empty_like(a)
+    lib().orc_amsim_many(a.size, _ptr(a), _ptr(b), _ptr(lut), M, _ptr(out))
+    return out.reshape(np.shape(a_bits))
+
+
+def amsim(a, b, lut, M):
+    """Algorithm 2 on float32 arrays; returns float32."""
+    a = _f32(a)
+    b = _f32(b)
+    return amsim_bits(a.view(np.uint32), b.view(np.uint32), lut, M).view(np.float32)
+
+
+# ---------------------------------------------------------------- GEMM
+
+def gemm(A, B, lut, M, transA=False, transB=False):
+    """R = sum of approximate products (float64) and S = sum of their
+    magnitudes, for op(A) @ op(B). A and B are 2-D float32 arrays stored
+    row-major (op = transpose of the stored matrix when trans is set)."""
+    A = _f32(A)
+    B = _f32(B)
+    m = A.shape[1] if transA else A.shape[0]
+    k = A.shape[0] if transA else A.shape[1]
+    kb = B.shape[1] if transB else B.shape[0]
+    n = B.shape[0] if transB else B.shape[1]
+    assert k == kb
+    R = np.zeros((m, n), dtype=np.float64)
+    S = np.zeros((m, n), dtype=np.float64)
+    lut = np.ascontiguousarray(lut, dtype=np.uint16)
+    lib().orc_gemm(int(transA), int(transB), m, n, k, _ptr(A), A.shape[1],
+                   _ptr(B), B.shape[1], _ptr(lut), M, _ptr(R), _ptr(S))
+    return R, S
+
+
+def gemm_at(A, B, lut, M, rows, cols, transA=False, transB=False):
+    """The same sums at the (rows[t], cols[t]) outputs only."""
+    A = _f32(A)
+    B = _f32(B)
+    m = A.shape[1] if transA else A.shape[0]
+    k = A.shape[0] if transA else A.shape[1]
+    n = B.shape[0] if transB else B.shape[1]
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    cols = np.ascontiguousarray(cols, dtype=np.int32)
+    assert rows.shape == cols.shape
+    R = np.zeros(rows.size, dtype=np.float64)
+    S = np.zeros(rows.size, dtype=np.float64)
+    lut = np.ascontiguousarray(lut, dtype=np.uint16)
+    lib().orc_gemm_at(int(transA), int(transB), m, n, k, _ptr(A), A.shape[1],
+                      _ptr(B), B.shape[1], _ptr(lut), M, rows.size,
+                      _ptr(rows), _ptr(cols), _ptr(R), _ptr(S))
+    return R, S
+
+
+# ---------------------------------------------------------------- Conv2D
+
+def conv_out_hw(H, W, R, S, stride, pad):
+    sh, sw = stride
+    ph, pw = pad
+    return (H + 2 * ph - R) // sh + 1, (W + 2 * pw - S) // sw + 1
+
+
+def _conv(name, shape_out, geomargs, t1, t2, lut, M, idx):
+    t1 = _f32(t1)
+    t2 = _f32(t2)
+    lut = np.ascontiguousarray(lut, dtype=np.uint16)
+    if idx is None:
+        total = int(np.prod(shape_out))
+        R = np.zeros(total, dtype=np.float64)
+        S = np.zeros(total, dtype=np.float64)
+        getattr(lib(), name)(*geomargs, _ptr(t1), _ptr(t2), _ptr(lut), M, 0, None,
+                             _ptr(R), _ptr(S))
+        return R.reshape(shape_out), S.reshape(shape_out)
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    R = np.zeros(idx.size, dtype=np.float64)
+    S = np.zeros(idx.size, dtype=np.float64)
+    getattr(lib(), name)(*geomargs, _ptr(t1), _ptr(t2), _ptr(lut), M, idx.size,
+                         _ptr(idx), _ptr(R), _ptr(S))
+    return R, S
+
+
+def conv2d_fwd(x, w, lut, M, stride=(1, 1), pad=(0, 0), idx=None):
+    """x: NHWC, w: RSCK. Returns (Y, YS) of shape NPQK (or at flat idx)."""
+    N, H, W, C = x.shape
+    R, S, C2, K = w.shape
+    assert C == C2
+    P, Q = conv_out_hw(H, W, R, S, stride, pad)
+    g = (N, H, W, C, K, R, S, stride[0], stride[1], pad[0], pad[1])
+    return _conv("orc_conv2d_fwd", (N, P, Q, K), g, x, w, lut, M, idx)
+
+
+def conv2d_dgrad(dy, w, x_shape, lut, M, stride=(1, 1), pad=(0, 0), idx=None):
+    """dy: NPQK, w: RSCK, x_shape = (N, H, W, C). Returns (dX, dXS)."""
+    N, H, W, C = x_shape
+    R, S, C2, K = w.shape
+    assert C == C2
+    P, Q = conv_out_hw(H, W, R, S, stride, pad)
+    assert dy.shape == (N, P, Q, K)
+    g = (N, H, W, C, K, R, S, stride[0], stride[1], pad[0], pad[1])
+    return _conv("orc_conv2d_dgrad", (N, H, W, C), g, dy, w, lut, M, idx)
+
+
+def conv2d_wgrad(x, dy, w_shape, lut, M, stride=(1, 1), pad=(0, 0), idx=None):
+    """x: NHWC, dy: NPQK, w_shape = (R, S, C, K). Returns (dW, dWS)."""
+    N, H, W, C = x.shape
+    R, S, C2, K = w_shape
+    assert C == C2
+    P, Q = conv_out_hw(H, W, R, S, stride, pad)
+    assert dy.shape == (N, P, Q, K)
+    g = (N, H, W, C, K, R, S, stride[0], stride[1], pad[0], pad[1])
+    return _conv("orc_conv2d_wgrad", (R, S, C, K), g, x, dy, lut, M, idx)

@@ -1,0 +1,377 @@
+/*
+ * oracle.c -- plain, slow, single-threaded CPU reference for LUT-based
+ * approximate FP32 multiplication and the GEMM / Conv2D passes built on it.
+ *
+ * TEST INFRASTRUCTURE. Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this file's library. The product library
+ * never links, includes or calls it, and it shares no code, header, table or
+ * helper with the HIP path.
+ *
+ * What it follows (all from "ApproxTrain: Fast Simulation of Approximate
+ * Multipliers for DNN Training and Inference", arXiv 2209.04161):
+ *   - Section V-A, Algorithm 1: generation of the mantissa-product lookup
+ *     table from a C model of the multiplier, with carry detection by
+ *     comparing the product's exponent with the un-normalised exponent.
+ *   - Section V, Algorithm 2 (AMSim): one approximate product from the sign
+ *     XOR, the exponent sum plus the table's carry, and the table's mantissa,
+ *     with the zero / underflow / overflow cases.
+ *   - Section III (Fig. 3): forward product, weight gradient (errors x
+ *     activations) and preceding-layer gradient (weights x errors).
+ *   - Section VI-B (Algorithms 3 and 4, Fig. 8): Conv2D forward as
+ *     IM2COL + GEMM, weight gradient as IM2COL_Weight + GEMM, and the
+ *     preceding-layer gradient as GEMM over the padded, dilated errors with
+ *     the transposed-and-reversed filter.
+ * Convolution is cross-correlation (the deep-learning convention, as in
+ * "Binarized Convolutional Neural Networks for Efficient Inference on GPUs",
+ * arXiv 1808.00209, eq. (3)).
+ *
+ * Readings taken where the pages are silent or loose (each is restated in the
+ * design notes of the repository):
+ *   R1  Table entry: 16 bits. Bit 15 is the carry, bits 14..0 are the top 15
+ *       bits of the product's 23-bit fraction (truncated).
+ *   R2  Operand mantissa = the top M bits of the 23-bit fraction (truncated).
+ *   R3  Index = (mantissa of the first operand << M) | mantissa of the second.
+ *   R4  The underflow / overflow tests use the exponent after the carry is
+ *       added: e = EA + EB - 127 + carry; e <= 0 gives a signed zero and
+ *       e >= 255 a signed infinity.
+ *   R5  Subnormal inputs count as zero (the table assumes a hidden leading 1).
+ *   R6  NaN in either input gives NaN (0x7FC00000); infinity times zero gives
+ *       NaN; infinity times a non-zero gives a signed infinity. Otherwise a
+ *       zero input gives a signed zero.
+ *   R7  Algorithm 1 supports products whose mantissa lies in [1, 4): the
+ *       product exponent equals the un-normalised exponent (carry 0) or
+ *       exceeds it by one (carry 1). Anything else is rejected.
+ *   R8  Convolution padding and dilation slots are zero operands that are
+ *       multiplied (the IM2COL buffer holds zeros there), not omitted terms.
+ *   R9  Sums are taken in double precision here; the sum of absolute
+ *       products is returned beside each output for the error gate.
+ *
+ * Build: gcc -O2 -std=c99 -fPIC -shared -ffp-contract=off oracle.c -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* bit views of a float                                               */
+/* ------------------------------------------------------------------ */
+static uint32_t bits_of(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float float_of(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t sign_of(uint32_t u) { return u >> 31; }
+static uint32_t exp_of(uint32_t u) { return (u >> 23) & 0xFFu; }
+static uint32_t frac_of(uint32_t u) { return u & 0x7FFFFFu; }
+
+/* ------------------------------------------------------------------ */
+/* C models of multipliers (the user-supplied approx_mul of Fig. 7)    */
+/* ------------------------------------------------------------------ */
+
+/* The exact multiplier: the hardware FP32 product. With M-bit operand
+ * mantissas (M <= 11) the product of the two significands needs at most
+ * 2M+2 <= 24 bits, so it is exact in FP32. */
+float orc_mul_exact(float a, float b) { return a * b; }
+
+/* Mitchell's logarithmic multiplier (J. N. Mitchell, "Computer
+ * multiplication and division using binary logarithms", 1962), applied to
+ * the significands of two normal floats. With a = (1+x)2^ea and
+ * b = (1+y)2^eb, log2 is approximated by its chord: log2(1+x) ~ x. The
+ * antilogarithm of ea+eb+x+y is then (1+x+y)2^(ea+eb) when x+y < 1, and
+ * 2(x+y)2^(ea+eb) = (1+(x+y-1))2^(ea+eb+1) when x+y >= 1. Zero, subnormal,
+ * infinite and NaN operands are not modelled: Algorithm 1 never passes them. */
+float orc_mul_mitchell(float a, float b)
+{
+    uint32_t ua = bits_of(a), ub = bits_of(b);
+    int ea = (int)exp_of(ua) - 127, eb = (int)exp_of(ub) - 127;
+    double x = (double)frac_of(ua) / 8388608.0;
+    double y = (double)frac_of(ub) / 8388608.0;
+    double sig = (x + y < 1.0) ? 1.0 + x + y : 2.0 * (x + y);
+    double v = ldexp(sig, ea + eb);
+    if (sign_of(ua) ^ sign_of(ub)) v = -v;
+    return (float)v;
+}
+
+/* ------------------------------------------------------------------ */
+/* Algorithm 1: mantissa-product lookup table generation (Section V-A) */
+/* ------------------------------------------------------------------ */
+
+/* Fills lut[(ia << M) | ib] for every pair of M-bit mantissas. Returns 0, or
+ * -1 for M out of [1, 11], or -2 when the model's product falls outside the
+ * supported shape (reading R7).
+ *
+ * The operands are built with sign + and biased exponent 127 (value in
+ * [1, 2)), so neither they nor their product can be a special case. The
+ * un-normalised exponent of the product is 127 + 127 - 127 = 127; the carry
+ * is set when the model's product has a larger exponent. */
+int orc_lut_generate(int M, float (*approx_mul)(float, float), uint16_t *lut)
+{
+    if (M < 1 || M > 11) return -1;
+    const uint32_t n = 1u << M;
+    const uint32_t exp_a = 127, exp_b = 127;
+    const int un_normalized_exp = (int)exp_a + (int)exp_b - 127;
+    for (uint32_t ia = 0; ia < n; ++ia) {
+        for (uint32_t ib = 0; ib < n; ++ib) {
+            float A = float_of((exp_a << 23) | (ia << (23 - M)));
+            float B = float_of((exp_b << 23) | (ib << (23 - M)));
+            uint32_t c = bits_of(approx_mul(A, B));
+            int real_exp = (int)exp_of(c);
+            uint32_t carry;
+            if (sign_of(c) != 0) return -2;
+            if (real_exp == un_normalized_exp) carry = 0;
+            else if (real_exp == un_normalized_exp + 1) carry = 1;
+            else return -2;
+            uint32_t mantissa15 = frac_of(c) >> 8; /* top 15 fraction bits */
+            lut[(ia << M) | ib] = (uint16_t)((carry << 15) | mantissa15);
+        }
+    }
+    return 0;
+}
+
+/* A synthetic multiplier: a table whose every entry's 15-bit mantissa field
+ * is moved by delta[i] (+1 or -1 units of the field), saturating at 0 and
+ * 0x7FFF; the carry bit is left as it is. delta comes from the caller. */
+void orc_lut_perturb(int M, uint16_t *lut, const int8_t *delta)
+{
+    const uint32_t n = 1u << (2 * M);
+    for (uint32_t i = 0; i < n; ++i) {
+        int carry = lut[i] >> 15;
+        int mant = lut[i] & 0x7FFF;
+        mant += delta[i];
+        if (mant < 0) mant = 0;
+        if (mant > 0x7FFF) mant = 0x7FFF;
+        lut[i] = (uint16_t)((carry << 15) | mant);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Algorithm 2: AMSim, one approximate product (Section V)             */
+/* ------------------------------------------------------------------ */
+uint32_t orc_amsim_bits(uint32_t a, uint32_t b, const uint16_t *lut, int M)
+{
+    /* extract the mantissas (top M fraction bits) and form the index */
+    uint32_t mant_a = frac_of(a) >> (23 - M);
+    uint32_t mant_b = frac_of(b) >> (23 - M);
+    uint32_t index = (mant_a << M) | mant_b;
+    /* decouple the table entry into mantissa and carry; sign is the XOR */
+    uint32_t entry = lut[index];
+    uint32_t mantissa = entry & 0x7FFFu;
+    uint32_t carry = entry >> 15;
+    uint32_t sign = sign_of(a) ^ sign_of(b);
+
+    /* classes (readings R5, R6) */
+    uint32_t ea = exp_of(a), eb = exp_of(b);
+    int a_nan = (ea == 255) && frac_of(a) != 0, b_nan = (eb == 255) && frac_of(b) != 0;
+    int a_inf = (ea == 255) && frac_of(a) == 0, b_inf = (eb == 255) && frac_of(b) == 0;
+    int a_zero = (ea == 0), b_zero = (eb == 0);
+    if (a_nan || b_nan) return 0x7FC00000u;
+    if (a_inf || b_inf) {
+        if (a_zero || b_zero) return 0x7FC00000u;
+        return (sign << 31) | 0x7F800000u;
+    }
+    if (a_zero || b_zero) return sign << 31;
+
+    /* normal case: biased exponent with the carry (reading R4) */
+    int e = (int)ea + (int)eb - 127 + (int)carry;
+    if (e <= 0) return sign << 31;
+    if (e >= 255) return (sign << 31) | 0x7F800000u;
+    return (sign << 31) | ((uint32_t)e << 23) | (mantissa << 8);
+}
+
+float orc_amsim(float a, float b, const uint16_t *lut, int M)
+{
+    return float_of(orc_amsim_bits(bits_of(a), bits_of(b), lut, M));
+}
+
+/* element-wise products of two bit arrays (for exhaustive checks) */
+void orc_amsim_many(int64_t count, const uint32_t *a, const uint32_t *b,
+                    const uint16_t *lut, int M, uint32_t *out)
+{
+    for (int64_t t = 0; t < count; ++t) out[t] = orc_amsim_bits(a[t], b[t], lut, M);
+}
+
+/* ------------------------------------------------------------------ */
+/* GEMM: C = op(A) op(B) with every product approximate                */
+/* ------------------------------------------------------------------ */
+/* Row-major operands. op(A)(i,p) = transA ? A[p*lda+i] : A[i*lda+p];
+ * op(B)(p,j) = transB ? B[j*ldb+p] : B[p*ldb+j]. The first operand of each
+ * product is op(A)(i,p), the second op(B)(p,j) (reading R3). */
+static void gemm_one(int transA, int transB, int i, int j, int k,
+                     const float *A, long lda, const float *B, long ldb,
+                     const uint16_t *lut, int M, double *r, double *s)
+{
+    double sum = 0.0, abs_sum = 0.0;
+    for (int p = 0; p < k; ++p) {
+        float a = transA ? A[(long)p * lda + i] : A[(long)i * lda + p];
+        float b = transB ? B[(long)j * ldb + p] : B[(long)p * ldb + j];
+        double prod = (double)orc_amsim(a, b, lut, M);
+        sum += prod;
+        abs_sum += fabs(prod);
+    }
+    *r = sum;
+    *s = abs_sum;
+}
+
+void orc_gemm(int transA, int transB, int m, int n, int k,
+              const float *A, int lda, const float *B, int ldb,
+              const uint16_t *lut, int M, double *R, double *S)
+{
+    for (int i = 0; i < m; ++i)
+        for (int j = 0; j < n; ++j)
+            gemm_one(transA, transB, i, j, k, A, lda, B, ldb, lut, M,
+                     &R[(long)i * n + j], &S[(long)i * n + j]);
+}
+
+/* the same sums at chosen (row, column) pairs only */
+void orc_gemm_at(int transA, int transB, int m, int n, int k,
+                 const float *A, int lda, const float *B, int ldb,
+                 const uint16_t *lut, int M,
+                 int64_t count, const int32_t *rows, const int32_t *cols,
+                 double *R, double *S)
+{
+    (void)m; (void)n;
+    for (int64_t t = 0; t < count; ++t)
+        gemm_one(transA, transB, rows[t], cols[t], k, A, lda, B, ldb, lut, M, &R[t], &S[t]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Conv2D, NHWC activations and RSCK (HWIO) weights                    */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    int N, H, W, C, K, R, S, sh, sw, ph, pw, P, Q;
+} geom;
+
+static geom make_geom(int N, int H, int W, int C, int K, int R, int S,
+                      int sh, int sw, int ph, int pw)
+{
+    geom g = {N, H, W, C, K, R, S, sh, sw, ph, pw, 0, 0};
+    g.P = (H + 2 * ph - R) / sh + 1;
+    g.Q = (W + 2 * pw - S) / sw + 1;
+    return g;
+}
+
+/* activation value with zero padding outside the image (reading R8) */
+static float x_at(const geom *g, const float *x, int n, int h, int w, int c)
+{
+    if (h < 0 || h >= g->H || w < 0 || w >= g->W) return 0.0f;
+    return x[(((long)n * g->H + h) * g->W + w) * g->C + c];
+}
+
+/* Padded, dilated errors (Section VI-B, the IM2COL_PLG input): at an input
+ * coordinate offset hh = h + ph - r the error of output row hh / sh is used
+ * when hh is a multiple of the stride and in range, and zero otherwise. */
+static float dilated_dy_at(const geom *g, const float *dy, int n, int hh, int ww, int k)
+{
+    if (hh < 0 || ww < 0) return 0.0f;
+    if (hh % g->sh != 0 || ww % g->sw != 0) return 0.0f;
+    int p = hh / g->sh, q = ww / g->sw;
+    if (p >= g->P || q >= g->Q) return 0.0f;
+    return dy[(((long)n * g->P + p) * g->Q + q) * g->K + k];
+}
+
+static float w_at(const geom *g, const float *w, int r, int s, int c, int k)
+{
+    return w[(((long)r * g->S + s) * g->C + c) * g->K + k];
+}
+
+/* forward: y[n,p,q,k] = sum_{r,s,c} approx(x[n, p*sh-ph+r, q*sw-pw+s, c], w[r,s,c,k]) */
+static void fwd_one(const geom *g, const float *x, const float *w, long idx,
+                    const uint16_t *lut, int M, double *r_out, double *s_out)
+{
+    int k = (int)(idx % g->K); idx /= g->K;
+    int q = (int)(idx % g->Q); idx /= g->Q;
+    int p = (int)(idx % g->P);
+    int n = (int)(idx / g->P);
+    double sum = 0.0, abs_sum = 0.0;
+    for (int r = 0; r < g->R; ++r)
+        for (int s = 0; s < g->S; ++s)
+            for (int c = 0; c < g->C; ++c) {
+                float a = x_at(g, x, n, p * g->sh - g->ph + r, q * g->sw - g->pw + s, c);
+                double prod = (double)orc_amsim(a, w_at(g, w, r, s, c, k), lut, M);
+                sum += prod;
+                abs_sum += fabs(prod);
+            }
+    *r_out = sum;
+    *s_out = abs_sum;
+}
+
+/* preceding-layer gradient:
+ * dx[n,h,w,c] = sum_{r,s,k} approx(D[n, h+ph-r, w+pw-s, k], w[r,s,c,k])
+ * with D the padded, dilated errors above. */
+static void dgrad_one(const geom *g, const float *dy, const float *w, long idx,
+                      const uint16_t *lut, int M, double *r_out, double *s_out)
+{
+    int c = (int)(idx % g->C); idx /= g->C;
+    int ww = (int)(idx % g->W); idx /= g->W;
+    int h = (int)(idx % g->H);
+    int n = (int)(idx / g->H);
+    double sum = 0.0, abs_sum = 0.0;
+    for (int r = 0; r < g->R; ++r)
+        for (int s = 0; s < g->S; ++s)
+            for (int k = 0; k < g->K; ++k) {
+                float a = dilated_dy_at(g, dy, n, h + g->ph - r, ww + g->pw - s, k);
+                double prod = (double)orc_amsim(a, w_at(g, w, r, s, c, k), lut, M);
+                sum += prod;
+                abs_sum += fabs(prod);
+            }
+    *r_out = sum;
+    *s_out = abs_sum;
+}
+
+/* weight gradient:
+ * dw[r,s,c,k] = sum_{n,p,q} approx(x[n, p*sh-ph+r, q*sw-pw+s, c], dy[n,p,q,k]) */
+static void wgrad_one(const geom *g, const float *x, const float *dy, long idx,
+                      const uint16_t *lut, int M, double *r_out, double *s_out)
+{
+    int k = (int)(idx % g->K); idx /= g->K;
+    int c = (int)(idx % g->C); idx /= g->C;
+    int s = (int)(idx % g->S);
+    int r = (int)(idx / g->S);
+    double sum = 0.0, abs_sum = 0.0;
+    for (int n = 0; n < g->N; ++n)
+        for (int p = 0; p < g->P; ++p)
+            for (int q = 0; q < g->Q; ++q) {
+                float a = x_at(g, x, n, p * g->sh - g->ph + r, q * g->sw - g->pw + s, c);
+                float b = dy[(((long)n * g->P + p) * g->Q + q) * g->K + k];
+                double prod = (double)orc_amsim(a, b, lut, M);
+                sum += prod;
+                abs_sum += fabs(prod);
+            }
+    *r_out = sum;
+    *s_out = abs_sum;
+}
+
+/* Full passes (idx == NULL: every output in order) or chosen outputs (flat
+ * indices into the NHWC / RSCK output). */
+void orc_conv2d_fwd(int N, int H, int W, int C, int K, int R, int S,
+                    int sh, int sw, int ph, int pw,
+                    const float *x, const float *w, const uint16_t *lut, int M,
+                    int64_t count, const int64_t *idx, double *Y, double *YS)
+{
+    geom g = make_geom(N, H, W, C, K, R, S, sh, sw, ph, pw);
+    long total = (long)N * g.P * g.Q * K;
+    long cnt = idx ? (long)count : total;
+    for (long t = 0; t < cnt; ++t)
+        fwd_one(&g, x, w, idx ? (long)idx[t] : t, lut, M, &Y[t], &YS[t]);
+}
+
+void orc_conv2d_dgrad(int N, int H, int W, int C, int K, int R, int S,
+                      int sh, int sw, int ph, int pw,
+                      const float *dy, const float *w, const uint16_t *lut, int M,
+                      int64_t count, const int64_t *idx, double *DX, double *DXS)
+{
+    geom g = make_geom(N, H, W, C, K, R, S, sh, sw, ph, pw);
+    long total = (long)N * H * W * C;
+    long cnt = idx ? (long)count : total;
+    for (long t = 0; t < cnt; ++t)
+        dgrad_one(&g, dy, w, idx ? (long)idx[t] : t, lut, M, &DX[t], &DXS[t]);
+}
+
+void orc_conv2d_wgrad(int N, int H, int W, int C, int K, int R, int S,
+                      int sh, int sw, int ph, int pw,
+                      const float *x, const float *dy, const uint16_t *lut, int M,
+                      int64_t count, const int64_t *idx, double *DW, double *DWS)
+{
+    geom g = make_geom(N, H, W, C, K, R, S, sh, sw, ph, pw);
+    long total = (long)R * S * C * K;
+    long cnt = idx ? (long)count : total;
+    for (long t = 0; t < cnt; ++t)
+        wgrad_one(&g, x, dy, idx ? (long)idx[t] : t, lut, M, &DW[t], &DWS[t]);
+}
