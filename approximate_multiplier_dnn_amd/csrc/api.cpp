@@ -1,0 +1,556 @@
+// api.cpp -- the C ABI: argument checks, per-device table state, per-stream
+// scratch arenas, and the plan (decode layouts, tiling, reduction split) of
+// each GEMM / Conv2D call. Every arithmetic step runs in kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "../../include/approx_mul.h"
+#include "internal.h"
+
+namespace {
+
+using amx::DecodeParams;
+using amx::MainParams;
+using amx::ReduceParams;
+using amx::Word;
+
+constexpr int kMaxDevices = 64;
+constexpr int kRowsPerWave = 256;   // 64 lanes x 4 rows
+constexpr int kColsPerWave = 16;
+constexpr int kSplitBelowTiles = 256;
+constexpr int kSplitTargetItems = 512;
+constexpr int64_t kMaxPanelWords = (int64_t)1 << 31;
+
+struct DeviceTable {
+    uint16_t* image = nullptr;  // lane-first LDS image
+    int M = 0;
+};
+
+struct Arena {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_mu;
+DeviceTable g_tables[kMaxDevices];
+bool g_profile = false;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events;   // GEMM-kernel launches while profiling
+std::map<std::pair<int, hipStream_t>, Arena> g_arenas;
+
+int current_device(int* dev)
+{
+    if (hipGetDevice(dev) != hipSuccess) return APPROX_EHIP;
+    if (*dev < 0 || *dev >= kMaxDevices) return APPROX_EHIP;
+    return APPROX_OK;
+}
+
+// Scratch memory for one call on (device, stream). Grows only. Before
+// freeing a smaller arena the stream is synchronised, so earlier calls on it
+// have finished reading their operands.
+int arena_get(int dev, hipStream_t stream, size_t bytes, char** out)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    Arena& a = g_arenas[{dev, stream}];
+    if (a.bytes < bytes) {
+        if (a.ptr != nullptr) {
+            if (hipStreamSynchronize(stream) != hipSuccess) return APPROX_EHIP;
+            if (hipFree(a.ptr) != hipSuccess) return APPROX_EHIP;
+            a.ptr = nullptr;
+            a.bytes = 0;
+        }
+        size_t want = bytes + bytes / 8;
+        if (hipMalloc(&a.ptr, want) != hipSuccess) {
+            a.ptr = nullptr;
+            return APPROX_EHIP;
+        }
+        a.bytes = want;
+    }
+    *out = static_cast<char*>(a.ptr);
+    return APPROX_OK;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int table_of(int dev, const uint16_t** image, int* M)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (g_tables[dev].image == nullptr) return APPROX_ENOLUT;
+    *image = g_tables[dev].image;
+    *M = g_tables[dev].M;
+    return APPROX_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Waves of a workgroup are arranged wr x wc (wr * wc = 8); wc follows the
+// number of 16-column groups so narrow outputs waste few waves.
+void pick_waves(int n, int* wr, int* wc)
+{
+    const int64_t groups = cdiv(n, kColsPerWave);
+    *wc = groups >= 8 ? 8 : groups >= 4 ? 4 : groups >= 2 ? 2 : 1;
+    *wr = 8 / *wc;
+}
+
+// Reduction split: only when the output tiles cannot occupy the GPU. A
+// function of the shapes alone, so results do not depend on the device.
+void pick_split(int64_t tiles, int KB, int* splits, int* chunk)
+{
+    int s = 1;
+    if (tiles < kSplitBelowTiles) {
+        s = (int)std::min<int64_t>(cdiv(kSplitTargetItems, tiles), std::max(1, KB / 4));
+        s = std::max(1, s);
+    }
+    int c = (int)cdiv(KB, s);
+    if (c < 1) c = 1;
+    *chunk = c;
+    *splits = (int)cdiv(KB, c);
+    if (*splits < 1) *splits = 1;
+}
+
+bool force_checked()
+{
+    const char* v = std::getenv("APPROX_FORCE_CHECKED");
+    return v != nullptr && v[0] == '1';
+}
+
+// One planned call: the decode of both operands, the GEMM kernel and the
+// optional reduction, queued on `stream`.
+struct Plan {
+    DecodeParams lane{}, uni{};
+    MainParams mp{};
+    int64_t lane_words = 0, uni_words = 0;    // per batch entry
+    int batch = 1;
+    int gather = 0;
+    float* C = nullptr;
+    int64_t strideC = 0;
+};
+
+int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M)
+{
+    MainParams& mp = pl.mp;
+    if (pl.lane_words * pl.batch >= kMaxPanelWords || pl.uni_words * pl.batch >= kMaxPanelWords)
+        return APPROX_EUNSUPPORTED;
+    const int lds_class = M <= 7 ? 0 : 1;
+    const int64_t tiles = (int64_t)mp.tiles_m * mp.tiles_n * pl.batch;
+    pick_split(tiles, mp.KB, &mp.splits, &mp.chunk);
+    mp.items = tiles * mp.splits;
+
+    const size_t stats_b = 256;
+    const size_t lane_b = align256((size_t)pl.lane_words * pl.batch * sizeof(Word));
+    const size_t uni_b = align256((size_t)pl.uni_words * pl.batch * sizeof(Word));
+    const size_t part_b = mp.splits > 1 ? align256((size_t)mp.splits * pl.batch * mp.m_out * mp.n_out * sizeof(float)) : 0;
+    char* base = nullptr;
+    int rc = arena_get(dev, stream, stats_b + lane_b + uni_b + part_b, &base);
+    if (rc != APPROX_OK) return rc;
+    int* stats = reinterpret_cast<int*>(base);
+    Word* lane_panel = reinterpret_cast<Word*>(base + stats_b);
+    Word* uni_panel = reinterpret_cast<Word*>(base + stats_b + lane_b);
+    float* partials = reinterpret_cast<float*>(base + stats_b + lane_b + uni_b);
+
+    pl.lane.dst = lane_panel;
+    pl.lane.stats = stats;
+    pl.lane.count = pl.lane_words;
+    pl.lane.dst_batch_stride = pl.lane_words;
+    pl.lane.batch = pl.batch;
+    pl.lane.lane_role = 1;
+    pl.lane.M = M;
+    pl.uni.dst = uni_panel;
+    pl.uni.stats = stats + 2;
+    pl.uni.count = pl.uni_words;
+    pl.uni.dst_batch_stride = pl.uni_words;
+    pl.uni.batch = pl.batch;
+    pl.uni.lane_role = 0;
+    pl.uni.M = M;
+
+    mp.panel = lane_panel;
+    mp.bpanel = uni_panel;
+    mp.lut = image;
+    mp.lut_bytes = amx::lut_image_bytes(M);
+    mp.stats = stats;
+    mp.panel_batch = pl.lane_words;
+    mp.bpanel_batch = pl.uni_words;
+    mp.batch = pl.batch;
+    mp.force_checked = force_checked() ? 1 : 0;
+    if (mp.splits > 1) {
+        mp.out = partials;
+    } else {
+        mp.out = pl.C;
+        mp.out_batch = pl.strideC;
+    }
+
+    if (amx::launch_init_stats(stats, stream) != hipSuccess) return APPROX_EHIP;
+    if (amx::launch_decode(pl.lane, stream) != hipSuccess) return APPROX_EHIP;
+    if (amx::launch_decode(pl.uni, stream) != hipSuccess) return APPROX_EHIP;
+
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+    const int64_t slots = (int64_t)cus * amx::main_blocks_per_cu(lds_class, pl.gather);
+    const int grid = (int)std::min<int64_t>(mp.items, slots);
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    bool prof;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        prof = g_profile;
+    }
+    if (prof) {
+        if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess) return APPROX_EHIP;
+        if (hipEventRecord(ev0, stream) != hipSuccess) return APPROX_EHIP;
+    }
+    if (amx::launch_main(mp, lds_class, pl.gather, grid, stream) != hipSuccess) return APPROX_EHIP;
+    if (prof) {
+        if (hipEventRecord(ev1, stream) != hipSuccess) return APPROX_EHIP;
+        std::lock_guard<std::mutex> lock(g_mu);
+        g_events.emplace_back(ev0, ev1);
+    }
+
+    if (mp.splits > 1) {
+        ReduceParams rp{};
+        rp.ws = partials;
+        rp.out = pl.C;
+        rp.m = mp.m_out;
+        rp.n = mp.n_out;
+        rp.ldc = mp.ldc;
+        rp.splits = mp.splits;
+        rp.batch = pl.batch;
+        rp.out_batch = pl.strideC;
+        if (amx::launch_reduce(rp, stream) != hipSuccess) return APPROX_EHIP;
+    }
+    return APPROX_OK;
+}
+
+int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int lda, long long strideA,
+              const float* B, int ldb, long long strideB, float* C, int ldc, long long strideC, int batch,
+              void* stream_v)
+{
+    if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1)) return APPROX_EINVAL;
+    if (m < 0 || n < 0 || k < 0 || batch < 0) return APPROX_EINVAL;
+    if (strideA < 0 || strideB < 0 || strideC < 0) return APPROX_EINVAL;
+    if (lda < std::max(1, transA ? m : k)) return APPROX_EINVAL;
+    if (ldb < std::max(1, transB ? k : n)) return APPROX_EINVAL;
+    if (ldc < std::max(1, n)) return APPROX_EINVAL;
+    if (batch > 65535) return APPROX_EUNSUPPORTED;
+    if (m == 0 || n == 0 || batch == 0) return APPROX_OK;
+    if (C == nullptr) return APPROX_EINVAL;
+    if (k > 0 && (A == nullptr || B == nullptr)) return APPROX_EINVAL;
+
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc != APPROX_OK) return rc;
+    const uint16_t* image = nullptr;
+    int M = 0;
+    rc = table_of(dev, &image, &M);
+    if (rc != APPROX_OK) return rc;
+    hipStream_t stream = static_cast<hipStream_t>(stream_v);
+
+    if (k == 0) {
+        return amx::launch_fill_zero(C, m, n, ldc, batch, strideC, stream) == hipSuccess ? APPROX_OK : APPROX_EHIP;
+    }
+
+    Plan pl;
+    pl.batch = batch;
+    pl.C = C;
+    pl.strideC = strideC;
+    int wr, wc;
+    pick_waves(n, &wr, &wc);
+    MainParams& mp = pl.mp;
+    mp.wr = wr;
+    mp.wc = wc;
+    const int TM = wr * kRowsPerWave, TN = wc * kColsPerWave;
+    mp.tiles_m = (int)cdiv(m, TM);
+    mp.tiles_n = (int)cdiv(n, TN);
+    const int Mp = mp.tiles_m * TM, Np = mp.tiles_n * TN;
+    const int KB = (int)cdiv(k, 4);
+
+    DecodeParams& a = pl.lane;
+    a.src = A;
+    a.src_batch_stride = strideA;
+    a.layout = amx::L_DENSE_LANE;
+    a.m = m; a.n = n; a.k = k; a.ld = lda; a.trans = transA;
+    a.Mp = Mp; a.Np = Np; a.KB = KB;
+    pl.lane_words = (int64_t)KB * Mp * 4;
+
+    DecodeParams& u = pl.uni;
+    u.src = B;
+    u.src_batch_stride = strideB;
+    u.layout = amx::L_DENSE_UNIFORM;
+    u.m = m; u.n = n; u.k = k; u.ld = ldb; u.trans = transB;
+    u.Mp = Mp; u.Np = Np; u.KB = KB;
+    pl.uni_words = (int64_t)KB * 4 * Np;
+
+    mp.m_rows = Mp;
+    mp.m_out = m;
+    mp.n_out = n;
+    mp.ldc = ldc;
+    mp.Np = Np;
+    mp.E2 = 1; mp.E3 = Mp; mp.L1 = 0; mp.L2 = 0; mp.L3 = 4;
+    mp.U1 = KB; mp.U2 = 1; mp.U3 = 1; mp.K1 = Mp * 4; mp.K2 = 0; mp.K3 = 0;
+    mp.KB = KB;
+    pl.gather = 0;
+    return run_plan(pl, dev, stream, image, M);
+}
+
+struct ConvShape {
+    int N, H, W, C, K, R, S, sh, sw, ph, pw, P, Q;
+};
+
+int conv_check(int N, int H, int W, int C, int K, int R, int S, int sh, int sw, int ph, int pw,
+               const void* t1, const void* t2, const void* out, ConvShape* cs)
+{
+    if (N < 1 || H < 1 || W < 1 || C < 1 || K < 1 || R < 1 || S < 1) return APPROX_EINVAL;
+    if (sh < 1 || sw < 1 || ph < 0 || pw < 0) return APPROX_EINVAL;
+    if (R > H + 2 * ph || S > W + 2 * pw) return APPROX_EINVAL;
+    if (t1 == nullptr || t2 == nullptr || out == nullptr) return APPROX_EINVAL;
+    *cs = ConvShape{N, H, W, C, K, R, S, sh, sw, ph, pw, (H + 2 * ph - R) / sh + 1, (W + 2 * pw - S) / sw + 1};
+    return APPROX_OK;
+}
+
+void fill_geom(DecodeParams& d, const ConvShape& s)
+{
+    d.N = s.N; d.H = s.H; d.W = s.W; d.C = s.C; d.K = s.K; d.R = s.R; d.S = s.S;
+    d.sh = s.sh; d.sw = s.sw; d.ph = s.ph; d.pw = s.pw; d.P = s.P; d.Q = s.Q;
+}
+
+enum ConvKind { CONV_FWD, CONV_DGRAD, CONV_WGRAD };
+
+int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t2, float* out, void* stream_v)
+{
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc != APPROX_OK) return rc;
+    const uint16_t* image = nullptr;
+    int M = 0;
+    rc = table_of(dev, &image, &M);
+    if (rc != APPROX_OK) return rc;
+    hipStream_t stream = static_cast<hipStream_t>(stream_v);
+
+    Plan pl;
+    pl.batch = 1;
+    pl.C = out;
+    MainParams& mp = pl.mp;
+    DecodeParams& a = pl.lane;
+    DecodeParams& u = pl.uni;
+    fill_geom(a, s);
+    fill_geom(u, s);
+    a.src = t1;
+    u.src = t2;
+
+    int m, n;
+    if (kind == CONV_FWD) { m = s.N * s.P * s.Q; n = s.K; }
+    else if (kind == CONV_DGRAD) { m = s.N * s.H * s.W; n = s.C; }
+    else { m = s.R * s.S * s.C; n = s.K; }
+    int wr, wc;
+    pick_waves(n, &wr, &wc);
+    mp.wr = wr;
+    mp.wc = wc;
+    const int TM = wr * kRowsPerWave, TN = wc * kColsPerWave;
+    mp.tiles_m = (int)cdiv(m, TM);
+    mp.tiles_n = (int)cdiv(n, TN);
+    const int Np = mp.tiles_n * TN;
+    mp.m_rows = m;
+    mp.m_out = m;
+    mp.n_out = n;
+    mp.ldc = n;
+    mp.Np = Np;
+    a.Np = u.Np = Np;
+
+    if (kind == CONV_FWD) {
+        const int Hp = s.H + 2 * s.ph, Wp = s.W + 2 * s.pw, Cb = (int)cdiv(s.C, 4), Cp = Cb * 4;
+        a.layout = amx::L_IMG_FWD;
+        a.Hp = Hp; a.Wp = Wp; a.Cb = Cb;
+        pl.lane_words = (int64_t)s.N * Hp * Cb * Wp * 4;
+        u.layout = amx::L_W_FWD;
+        u.Cp = Cp;
+        mp.KB = s.R * s.S * Cb;
+        pl.uni_words = (int64_t)mp.KB * 4 * Np;
+        const int rowB = Cb * Wp * 4;                 // one padded image row, in Words
+        mp.E2 = s.P; mp.E3 = s.Q;
+        mp.L1 = Hp * rowB; mp.L2 = s.sh * rowB; mp.L3 = s.sw * 4;
+        mp.U1 = s.R; mp.U2 = s.S; mp.U3 = Cb;
+        mp.K1 = rowB; mp.K2 = 4; mp.K3 = Wp * 4;
+        pl.gather = 0;
+    } else if (kind == CONV_DGRAD) {
+        const int Hd = s.H + s.R - 1, Wd = s.W + s.S - 1, Kb = (int)cdiv(s.K, 4), Kp = Kb * 4;
+        a.layout = amx::L_IMG_DGRAD;
+        a.Hp = Hd; a.Wp = Wd; a.Kb = Kb;
+        pl.lane_words = (int64_t)s.N * Hd * Kb * Wd * 4;
+        u.layout = amx::L_W_DGRAD;
+        u.Kp = Kp;
+        mp.KB = s.R * s.S * Kb;
+        pl.uni_words = (int64_t)mp.KB * 4 * Np;
+        const int rowB = Kb * Wd * 4;
+        mp.E2 = s.H; mp.E3 = s.W;
+        mp.L1 = Hd * rowB; mp.L2 = rowB; mp.L3 = 4;
+        mp.U1 = s.R; mp.U2 = s.S; mp.U3 = Kb;
+        mp.K1 = rowB; mp.K2 = 4; mp.K3 = Wd * 4;
+        pl.gather = 0;
+    } else {
+        const int Hp = s.H + 2 * s.ph, Wp = s.W + 2 * s.pw;
+        const int64_t body = (int64_t)s.N * Hp * s.C * Wp;
+        const int64_t npq = (int64_t)s.N * s.P * s.Q;
+        if (body + (int64_t)s.R * s.C * Wp >= kMaxPanelWords || npq >= kMaxPanelWords) return APPROX_EUNSUPPORTED;
+        a.layout = amx::L_IMG_WGRAD;
+        a.Hp = Hp; a.Wp = Wp;
+        pl.lane_words = body + (int64_t)s.R * s.C * Wp;
+        u.layout = amx::L_DY_WGRAD;
+        mp.KB = (int)cdiv(npq, 4);
+        u.Kp = mp.KB * 4;
+        pl.uni_words = (int64_t)mp.KB * 4 * Np;
+        mp.E2 = s.S; mp.E3 = s.C;
+        mp.L1 = s.C * Wp; mp.L2 = 1; mp.L3 = Wp;
+        mp.U1 = s.N; mp.U2 = s.P; mp.U3 = s.Q;
+        mp.K1 = Hp * s.C * Wp; mp.K2 = s.sh * s.C * Wp; mp.K3 = s.sw;
+        mp.nku = (int)npq;
+        mp.zoff = (int)body;
+        pl.gather = 1;
+    }
+    return run_plan(pl, dev, stream, image, M);
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" int approx_lut_load(const uint16_t* lut, int M)
+{
+    if (lut == nullptr) return APPROX_EINVAL;
+    if (M < 1 || M > 8) return APPROX_EUNSUPPORTED;
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc != APPROX_OK) return rc;
+    // lane-first image: column ib holds entries (ia, ib) for ia = 0..2^M-1, then two zeros
+    const int side = 1 << M, cs = amx::lut_col_entries(M);
+    std::vector<uint16_t> img((size_t)side * cs, 0);
+    for (int ib = 0; ib < side; ++ib)
+        for (int ia = 0; ia < side; ++ia) img[(size_t)ib * cs + ia] = lut[((size_t)ia << M) | ib];
+    uint16_t* d = nullptr;
+    if (hipMalloc(&d, img.size() * sizeof(uint16_t)) != hipSuccess) return APPROX_EHIP;
+    if (hipMemcpy(d, img.data(), img.size() * sizeof(uint16_t), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(d);
+        return APPROX_EHIP;
+    }
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (g_tables[dev].image != nullptr) {
+        if (hipDeviceSynchronize() != hipSuccess) { (void)hipFree(d); return APPROX_EHIP; }
+        (void)hipFree(g_tables[dev].image);
+    }
+    g_tables[dev].image = d;
+    g_tables[dev].M = M;
+    return APPROX_OK;
+}
+
+extern "C" int approx_lut_bits(void)
+{
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc != APPROX_OK) return rc;
+    std::lock_guard<std::mutex> lock(g_mu);
+    return g_tables[dev].image ? g_tables[dev].M : APPROX_ENOLUT;
+}
+
+extern "C" int approx_gemm(int transA, int transB, int m, int n, int k, const float* A, int lda, const float* B,
+                           int ldb, float* C, int ldc, void* stream)
+{
+    return gemm_impl(transA, transB, m, n, k, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, stream);
+}
+
+extern "C" int approx_gemm_strided_batched(int transA, int transB, int m, int n, int k, const float* A, int lda,
+                                           long long strideA, const float* B, int ldb, long long strideB, float* C,
+                                           int ldc, long long strideC, int batch, void* stream)
+{
+    return gemm_impl(transA, transB, m, n, k, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, stream);
+}
+
+extern "C" int approx_conv2d_fwd(int N, int H, int W, int C, int K, int R, int S, int stride_h, int stride_w,
+                                 int pad_h, int pad_w, const float* x, const float* w, float* y, void* stream)
+{
+    ConvShape s;
+    int rc = conv_check(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, x, w, y, &s);
+    if (rc != APPROX_OK) return rc;
+    return conv_impl(CONV_FWD, s, x, w, y, stream);
+}
+
+extern "C" int approx_conv2d_dgrad(int N, int H, int W, int C, int K, int R, int S, int stride_h, int stride_w,
+                                   int pad_h, int pad_w, const float* dy, const float* w, float* dx, void* stream)
+{
+    ConvShape s;
+    int rc = conv_check(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, dy, w, dx, &s);
+    if (rc != APPROX_OK) return rc;
+    return conv_impl(CONV_DGRAD, s, dy, w, dx, stream);
+}
+
+extern "C" int approx_conv2d_wgrad(int N, int H, int W, int C, int K, int R, int S, int stride_h, int stride_w,
+                                   int pad_h, int pad_w, const float* x, const float* dy, float* dw, void* stream)
+{
+    ConvShape s;
+    int rc = conv_check(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, x, dy, dw, &s);
+    if (rc != APPROX_OK) return rc;
+    return conv_impl(CONV_WGRAD, s, x, dy, dw, stream);
+}
+
+extern "C" int approx_profile_enable(int on)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_profile = on != 0;
+    return APPROX_OK;
+}
+
+extern "C" int approx_profile_read(int* launches, double* total_ms)
+{
+    if (launches == nullptr || total_ms == nullptr) return APPROX_EINVAL;
+    std::lock_guard<std::mutex> lock(g_mu);
+    int rc = APPROX_OK;
+    double sum = 0.0;
+    for (auto& ev : g_events) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(ev.second) != hipSuccess || hipEventElapsedTime(&ms, ev.first, ev.second) != hipSuccess)
+            rc = APPROX_EHIP;
+        sum += ms;
+        (void)hipEventDestroy(ev.first);
+        (void)hipEventDestroy(ev.second);
+    }
+    *launches = (int)g_events.size();
+    *total_ms = sum;
+    g_events.clear();
+    return rc;
+}
+
+extern "C" const char* approx_status_string(int status)
+{
+    switch (status) {
+    case APPROX_OK: return "ok";
+    case APPROX_EINVAL: return "invalid argument";
+    case APPROX_ENOLUT: return "no table loaded on this device";
+    case APPROX_EUNSUPPORTED: return "unsupported (table size or problem size)";
+    case APPROX_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+extern "C" int approx_release(void)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    int rc = APPROX_OK;
+    int saved = -1;
+    (void)hipGetDevice(&saved);
+    for (auto& kv : g_arenas) {
+        if (kv.second.ptr == nullptr) continue;
+        if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess) rc = APPROX_EHIP;
+        if (hipFree(kv.second.ptr) != hipSuccess) rc = APPROX_EHIP;
+    }
+    g_arenas.clear();
+    for (int d = 0; d < kMaxDevices; ++d) {
+        if (g_tables[d].image == nullptr) continue;
+        if (hipSetDevice(d) != hipSuccess || hipDeviceSynchronize() != hipSuccess) rc = APPROX_EHIP;
+        if (hipFree(g_tables[d].image) != hipSuccess) rc = APPROX_EHIP;
+        g_tables[d] = DeviceTable{};
+    }
+    if (saved >= 0) (void)hipSetDevice(saved);
+    return rc;
+}

@@ -1,0 +1,108 @@
+// internal.h -- parameter blocks and launchers shared by the host API
+// (api.cpp) and the gfx950 kernels (kernels.hip). Not part of the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace amx {
+
+// Decoded operand word, one per FP32 element, written by the decode pass and
+// read by the GEMM kernel. Two roles:
+//  - lane operand (varies across the 64 lanes of a wave): w = byte offset of
+//    its mantissa row inside a table column (2 * index), or of the column's
+//    zero pad entry for zero / subnormal / Inf / NaN;
+//  - uniform operand (the same for every lane at a given step): w = byte
+//    offset of its table column.
+// se = sign | exponent bits for normals (the float +-2^(E-127) * 2^0 with the
+//      exponent field kept), 0 for zero and subnormal, +-Inf for Inf and
+//      0x7FC00000 for NaN.
+struct Word {
+    uint32_t w;
+    uint32_t se;
+};
+
+// Table image in device memory, laid out as the LDS copy the kernels use:
+// column c holds the 2^M entries of one uniform-operand mantissa followed by
+// two zero entries (the pad). Column stride = (2^M + 2) entries.
+inline int lut_col_entries(int M) { return (1 << M) + 2; }
+inline int lut_image_bytes(int M) { return (1 << M) * lut_col_entries(M) * 2; }
+
+// LDS footprint classes of the GEMM kernel.
+constexpr int LDS_SMALL = (1 << 7) * ((1 << 7) + 2) * 2;  // M <= 7: 33,280 bytes
+constexpr int LDS_LARGE = (1 << 8) * ((1 << 8) + 2) * 2;  // M == 8: 132,096 bytes
+
+enum Layout : int {
+    L_DENSE_LANE = 0,    // A of a GEMM -> [batch][KB][Mp][4]
+    L_DENSE_UNIFORM,     // B of a GEMM -> [batch][Kp][Np]
+    L_IMG_FWD,           // conv x  -> [N][H+2ph][Cb][W+2pw][4]   (lane)
+    L_IMG_DGRAD,         // conv dy -> padded dilated [N][H+R-1][Kb][W+S-1][4] (lane)
+    L_W_FWD,             // conv w  -> [R*S*Cp][Np] (uniform)
+    L_W_DGRAD,           // conv w  -> reversed, transposed [R*S*Kp][Np] (uniform)
+    L_IMG_WGRAD,         // conv x  -> [N][H+2ph][C][W+2pw] + zero tail (lane)
+    L_DY_WGRAD,          // conv dy -> [Kp = NPQ rounded up to 4][Np] (uniform)
+};
+
+struct DecodeParams {
+    const float* src;
+    Word* dst;
+    int* stats;          // [2]: min and max biased exponent of normals seen
+    int64_t count;       // words per batch entry
+    int64_t src_batch_stride;  // elements
+    int64_t dst_batch_stride;  // words
+    int batch;
+    int layout;
+    int lane_role;       // 1: lane operand, 0: uniform operand
+    int M;
+    // geometry (meaning depends on layout)
+    int m, n, k, ld, trans;    // dense
+    int Mp, Np, KB;            // padded extents
+    int N, H, W, C, K, R, S, sh, sw, ph, pw, P, Q;
+    int Hp, Wp, Cb, Cp, Kb, Kp;
+};
+
+// GEMM kernel parameters. The lane operand of row i and k-step u is read at
+// panel + lane_base(i) + koff(u) (in Words); lane_base decomposes i into
+// (i1, i2, i3) with extents (., E2, E3) and strides (L1, L2, L3); koff
+// decomposes u into (u1, u2, u3) with extents (U1, U2, U3) and strides
+// (K1, K2, K3), u3 fastest. In vector mode a k-step covers 4 consecutive
+// reduction indices stored contiguously; in gather mode every reduction index
+// is its own step and steps >= nku read the zero region at zoff.
+struct MainParams {
+    const Word* panel;        // lane operand words
+    const Word* bpanel;       // uniform operand words [Kp][Np]
+    const uint16_t* lut;      // table image (lane-first layout)
+    const int* stats;         // [4]: lane min/max, uniform min/max exponent
+    float* out;               // C (or split partials when splits > 1)
+    int64_t panel_batch;      // Words between batch entries of the lane panel
+    int64_t bpanel_batch;     // Words between batch entries of the uniform panel
+    int64_t out_batch;        // floats between batch entries of C
+    int lut_bytes;
+    int m_rows;               // valid rows (lane rows are clamped below this)
+    int m_out, n_out, ldc;    // output extent and leading dimension
+    int Np;
+    int E2, E3, L1, L2, L3;
+    int U1, U2, U3, K1, K2, K3;
+    int nku, zoff;            // gather mode
+    int KB;                   // k-steps of 4 reduction indices (vector) / 4-groups (gather)
+    int wr, wc;               // waves per workgroup along rows / columns (wr*wc = 8)
+    int tiles_m, tiles_n, splits, chunk;  // chunk = k-steps (of 4) per split
+    int batch;
+    int64_t items;
+    int force_checked;        // 1: always use the per-product checked path
+};
+
+struct ReduceParams {
+    const float* ws;
+    float* out;
+    int m, n, ldc, splits, batch;
+    int64_t out_batch;
+};
+
+hipError_t launch_init_stats(int* stats, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+hipError_t launch_main(const MainParams& p, int lds_class, int gather, int grid, hipStream_t s);
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
+hipError_t launch_fill_zero(float* C, int m, int n, int ldc, int batch, int64_t strideC, hipStream_t s);
+int main_blocks_per_cu(int lds_class, int gather);
+
+}  // namespace amx

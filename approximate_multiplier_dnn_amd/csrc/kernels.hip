@@ -1,0 +1,539 @@
+// kernels.hip -- gfx950 kernels of the LUT-based approximate GEMM.
+//
+// The product of every multiply-accumulate is the AMSim approximate product
+// ("ApproxTrain", arXiv 2209.04161, Section V, Algorithm 2). Three kernels
+// make up one call:
+//   1. decode  : each FP32 operand element is decoded once into a Word
+//                (table offset + sign|exponent bits), laid out for step 3.
+//                This is also where implicit-GEMM layouts for Conv2D are
+//                produced (zero-padded images, the padded and dilated errors
+//                and the transposed, reversed filter of Section VI-B).
+//   2. main    : the table is staged in LDS once per persistent workgroup;
+//                each lane owns 4 rows x 16 columns of the output; per MAC it
+//                forms the LDS address, reads one 16-bit entry and folds it
+//                into the FP32 accumulator.
+//   3. reduce  : when the reduction is split, sums the chunk partials in
+//                ascending chunk order.
+//
+// Fast path (3 VALU ops + 1 LDS read per MAC). When no product of the call
+// can leave the normal range, the AMSim product equals exactly
+//     fma(as_float(seA + (entry << 8)), as_float(seB), acc)
+// where seA/seB are the operands' sign|exponent bits: seA + (entry << 8) is
+// +-(1.f) * 2^(EA-127+carry) and seB is +-2^(EB-127), so the FMA's product is
+// exact and its single rounding is the rounding of acc + product. Zero, Inf
+// and NaN operands are encoded (zero pad entry, se = 0 / +-Inf / NaN) so the
+// same FMA produces the rule's zero, infinity and NaN cases. The exponent
+// range test is made from the per-operand min/max exponents gathered by the
+// decode pass. Otherwise the checked path evaluates Algorithm 2 per product.
+#include "internal.h"
+
+namespace amx {
+
+constexpr int NT = 512;   // threads per GEMM workgroup (8 waves, 2 per SIMD)
+constexpr int RPL = 4;    // output rows per lane
+constexpr int CPW = 16;   // output columns per wave
+
+// ------------------------------------------------------------------ decode
+
+__device__ __forceinline__ Word decode_bits(uint32_t bits, int M, int lane_role, int& emin, int& emax)
+{
+    const uint32_t e = (bits >> 23) & 0xFFu;
+    const uint32_t frac = bits & 0x7FFFFFu;
+    const uint32_t idx = frac >> (23 - M);
+    const uint32_t pad = (1u << M) * 2u;            // zero entry at the end of a column
+    const uint32_t colb = ((1u << M) + 2u) * 2u;    // column stride in bytes
+    Word o;
+    if (e == 0u) {                                  // zero or subnormal (counts as zero)
+        o.se = 0u;
+        o.w = lane_role ? pad : 0u;
+    } else if (e == 255u) {                         // Inf or NaN
+        o.se = frac ? 0x7FC00000u : (bits & 0xFF800000u);
+        o.w = lane_role ? pad : 0u;
+    } else {
+        o.se = bits & 0xFF800000u;
+        o.w = lane_role ? idx * 2u : idx * colb;
+        emin = min(emin, (int)e);
+        emax = max(emax, (int)e);
+    }
+    return o;
+}
+
+// Source element (within one batch entry) of output word o, or -1 for a
+// zero word (padding, dilation slot, or out-of-range tail).
+__device__ __forceinline__ int64_t decode_source(const DecodeParams& p, uint32_t o)
+{
+    switch (p.layout) {
+    case L_DENSE_LANE: {        // [KB][Mp][4]: element (i, kb*4+t) of op(A)
+        uint32_t t = o & 3u, r = o >> 2;
+        uint32_t i = r % (uint32_t)p.Mp, kb = r / (uint32_t)p.Mp;
+        uint32_t kk = kb * 4u + t;
+        if (i >= (uint32_t)p.m || kk >= (uint32_t)p.k) return -1;
+        return p.trans ? (int64_t)kk * p.ld + i : (int64_t)i * p.ld + kk;
+    }
+    case L_DENSE_UNIFORM: {     // [Kp][Np]: element (kk, j) of op(B)
+        uint32_t j = o % (uint32_t)p.Np, kk = o / (uint32_t)p.Np;
+        if (j >= (uint32_t)p.n || kk >= (uint32_t)p.k) return -1;
+        return p.trans ? (int64_t)j * p.ld + kk : (int64_t)kk * p.ld + j;
+    }
+    case L_IMG_FWD: {           // [N][Hp][Cb][Wp][4]
+        uint32_t t = o & 3u, r = o >> 2;
+        int wq = (int)(r % (uint32_t)p.Wp); r /= (uint32_t)p.Wp;
+        int cb = (int)(r % (uint32_t)p.Cb); r /= (uint32_t)p.Cb;
+        int hq = (int)(r % (uint32_t)p.Hp);
+        int n = (int)(r / (uint32_t)p.Hp);
+        int c = cb * 4 + (int)t, h = hq - p.ph, w = wq - p.pw;
+        if (c >= p.C || h < 0 || h >= p.H || w < 0 || w >= p.W) return -1;
+        return (((int64_t)n * p.H + h) * p.W + w) * p.C + c;
+    }
+    case L_IMG_DGRAD: {         // padded, dilated errors [N][Hd][Kb][Wd][4]
+        uint32_t t = o & 3u, r = o >> 2;
+        int bq = (int)(r % (uint32_t)p.Wp); r /= (uint32_t)p.Wp;
+        int kb = (int)(r % (uint32_t)p.Kb); r /= (uint32_t)p.Kb;
+        int aq = (int)(r % (uint32_t)p.Hp);
+        int n = (int)(r / (uint32_t)p.Hp);
+        int ko = kb * 4 + (int)t;
+        int hh = aq - (p.R - 1 - p.ph), ww = bq - (p.S - 1 - p.pw);
+        if (ko >= p.K || hh < 0 || ww < 0 || hh % p.sh != 0 || ww % p.sw != 0) return -1;
+        int pp = hh / p.sh, qq = ww / p.sw;
+        if (pp >= p.P || qq >= p.Q) return -1;
+        return (((int64_t)n * p.P + pp) * p.Q + qq) * p.K + ko;
+    }
+    case L_W_FWD: {             // [R*S*Cp][Np]: row (r, s, c), column k
+        uint32_t j = o % (uint32_t)p.Np, row = o / (uint32_t)p.Np;
+        uint32_t c = row % (uint32_t)p.Cp, rs = row / (uint32_t)p.Cp;
+        if (c >= (uint32_t)p.C || j >= (uint32_t)p.K) return -1;
+        return ((int64_t)rs * p.C + c) * p.K + j;
+    }
+    case L_W_DGRAD: {           // [R*S*Kp][Np]: row (R-1-r, S-1-s, k), column c
+        uint32_t j = o % (uint32_t)p.Np, row = o / (uint32_t)p.Np;
+        uint32_t ko = row % (uint32_t)p.Kp, rs = row / (uint32_t)p.Kp;
+        if (ko >= (uint32_t)p.K || j >= (uint32_t)p.C) return -1;
+        int rr = p.R - 1 - (int)(rs / (uint32_t)p.S), ss = p.S - 1 - (int)(rs % (uint32_t)p.S);
+        return (((int64_t)rr * p.S + ss) * p.C + j) * p.K + ko;
+    }
+    case L_IMG_WGRAD: {         // [N][Hp][C][Wp], then a zero tail
+        uint32_t body = (uint32_t)p.N * p.Hp * p.C * p.Wp;
+        if (o >= body) return -1;
+        uint32_t r = o;
+        int wq = (int)(r % (uint32_t)p.Wp); r /= (uint32_t)p.Wp;
+        int c = (int)(r % (uint32_t)p.C); r /= (uint32_t)p.C;
+        int hq = (int)(r % (uint32_t)p.Hp);
+        int n = (int)(r / (uint32_t)p.Hp);
+        int h = hq - p.ph, w = wq - p.pw;
+        if (h < 0 || h >= p.H || w < 0 || w >= p.W) return -1;
+        return (((int64_t)n * p.H + h) * p.W + w) * p.C + c;
+    }
+    case L_DY_WGRAD: {          // [Kp][Np]: row = output pixel, column = k
+        uint32_t j = o % (uint32_t)p.Np, kk = o / (uint32_t)p.Np;
+        if (j >= (uint32_t)p.K || kk >= (uint32_t)(p.N * p.P * p.Q)) return -1;
+        return (int64_t)kk * p.K + j;
+    }
+    }
+    return -1;
+}
+
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p)
+{
+    int emin = 255, emax = 0;
+    const int b = blockIdx.y;
+    const float* src = p.src + b * p.src_batch_stride;
+    Word* dst = p.dst + b * p.dst_batch_stride;
+    const uint32_t stride = gridDim.x * 256u;
+    for (uint32_t o = blockIdx.x * 256u + threadIdx.x; o < (uint32_t)p.count; o += stride) {
+        const int64_t s = decode_source(p, o);
+        Word wd;
+        if (s >= 0) {
+            wd = decode_bits(__float_as_uint(src[s]), p.M, p.lane_role, emin, emax);
+        } else {
+            wd.se = 0u;
+            wd.w = p.lane_role ? (1u << p.M) * 2u : 0u;
+        }
+        dst[o] = wd;
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        emin = min(emin, __shfl_xor(emin, off, 64));
+        emax = max(emax, __shfl_xor(emax, off, 64));
+    }
+    if ((threadIdx.x & 63) == 0 && emin <= emax) {
+        atomicMin(&p.stats[0], emin);
+        atomicMax(&p.stats[1], emax);
+    }
+}
+
+__global__ void init_stats_kernel(int* stats)
+{
+    if (threadIdx.x < 4) stats[threadIdx.x] = (threadIdx.x & 1) ? 0 : 255;
+}
+
+// ------------------------------------------------------------------ products
+
+// ------------------------------------------------------------------ GEMM
+
+struct KCounter {
+    int u1, u2, u3, off;
+};
+
+__device__ __forceinline__ KCounter kc_init(const MainParams& p, int u)
+{
+    KCounter c;
+    c.u3 = u % p.U3;
+    const int r = u / p.U3;
+    c.u2 = r % p.U2;
+    c.u1 = r / p.U2;
+    c.off = c.u1 * p.K1 + c.u2 * p.K2 + c.u3 * p.K3;
+    return c;
+}
+
+__device__ __forceinline__ void kc_next(const MainParams& p, KCounter& c)
+{
+    c.off += p.K3;
+    if (++c.u3 == p.U3) {
+        c.u3 = 0;
+        c.off += p.K2 - p.U3 * p.K3;
+        if (++c.u2 == p.U2) {
+            c.u2 = 0;
+            c.off += p.K1 - p.U2 * p.K2;
+            ++c.u1;
+        }
+    }
+}
+
+// Offsets (in Words, relative to a lane's base) of the 4 reduction indices of
+// k-step kb. Vector mode: 4 consecutive Words at one offset. Gather mode:
+// one offset per reduction index, or the zero region past the last one.
+template <bool GATHER>
+__device__ __forceinline__ void step_offsets(const MainParams& p, KCounter& kc, int& ku, int (&off)[4])
+{
+    if (!GATHER) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) off[t] = kc.off + t;
+        kc_next(p, kc);
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            off[t] = ku < p.nku ? kc.off : p.zoff;
+            ++ku;
+            kc_next(p, kc);
+        }
+    }
+}
+
+// Lane operand words (w, se) of the RPL rows of this lane at one offset.
+__device__ __forceinline__ void load_lane(const Word* panel, const uint32_t (&base)[RPL], int off,
+                                          uint32_t (&wa)[RPL], uint32_t (&sa)[RPL])
+{
+#pragma unroll
+    for (int x = 0; x < RPL; ++x) {
+        const uint2 q = *reinterpret_cast<const uint2*>(panel + base[x] + off);
+        wa[x] = q.x;
+        sa[x] = q.y;
+    }
+}
+
+// A group is RPL rows x 2 columns of products at one reduction index: the
+// two columns' uniform words come from one broadcast LDS read (issued two
+// groups ahead), then one table lookup per product (issued one group ahead).
+struct Group {
+    uint4 q;                 // (w, se) of column 2jp, (w, se) of column 2jp+1
+    uint32_t e[2 * RPL];     // table entries
+};
+
+__device__ __forceinline__ void group_lookup(const uint32_t (&wa)[RPL], const uint4& q, const unsigned char* lut,
+                                             uint32_t (&e)[2 * RPL])
+{
+#pragma unroll
+    for (int x = 0; x < RPL; ++x) {
+        e[2 * x] = *reinterpret_cast<const uint16_t*>(lut + (wa[x] + q.x));
+        e[2 * x + 1] = *reinterpret_cast<const uint16_t*>(lut + (wa[x] + q.z));
+    }
+}
+
+// Fast path: fma(as_float(seA + (entry << 8)), as_float(seB), acc).
+__device__ __forceinline__ float fast_product_acc(float acc, uint32_t e, uint32_t seA, uint32_t seB)
+{
+    return __builtin_fmaf(__uint_as_float((e << 8) + seA), __uint_as_float(seB), acc);
+}
+
+// Checked path: Algorithm 2 with every special case, as selects (no
+// divergence), then acc + product.
+__device__ __forceinline__ float checked_product_acc(float acc, uint32_t e, uint32_t seA, uint32_t seB)
+{
+    const uint32_t ea = (seA >> 23) & 0xFFu, eb = (seB >> 23) & 0xFFu;
+    const uint32_t sign = (seA ^ seB) & 0x80000000u;
+    const int ex = (int)ea + (int)eb - 127 + (int)(e >> 15);
+    uint32_t bits = sign | ((uint32_t)ex << 23) | ((e & 0x7FFFu) << 8);
+    bits = ex >= 255 ? (sign | 0x7F800000u) : bits;           // overflow -> signed Inf
+    bits = ex <= 0 ? sign : bits;                              // underflow -> signed zero
+    const bool zero = ea == 0u || eb == 0u;                    // zero or subnormal operand
+    const bool a_inf = ea == 255u && (seA & 0x7FFFFFu) == 0u;
+    const bool b_inf = eb == 255u && (seB & 0x7FFFFFu) == 0u;
+    const bool nan = (ea == 255u && (seA & 0x7FFFFFu) != 0u) || (eb == 255u && (seB & 0x7FFFFFu) != 0u);
+    bits = zero ? sign : bits;
+    bits = (a_inf || b_inf) ? (zero ? 0x7FC00000u : (sign | 0x7F800000u)) : bits;
+    bits = nan ? 0x7FC00000u : bits;
+    return acc + __uint_as_float(bits);
+}
+
+template <bool FAST>
+__device__ __forceinline__ void group_compute(const uint32_t (&sa)[RPL], const uint4& q, const uint32_t (&e)[2 * RPL],
+                                              int jp, float (&acc)[RPL][CPW])
+{
+#pragma unroll
+    for (int x = 0; x < RPL; ++x) {
+        if (FAST) {
+            acc[x][2 * jp] = fast_product_acc(acc[x][2 * jp], e[2 * x], sa[x], q.y);
+            acc[x][2 * jp + 1] = fast_product_acc(acc[x][2 * jp + 1], e[2 * x + 1], sa[x], q.w);
+        } else {
+            acc[x][2 * jp] = checked_product_acc(acc[x][2 * jp], e[2 * x], sa[x], q.y);
+            acc[x][2 * jp + 1] = checked_product_acc(acc[x][2 * jp + 1], e[2 * x + 1], sa[x], q.w);
+        }
+    }
+}
+
+constexpr int BT_WORDS = 4 * 8 * CPW;   // uniform words of one k-step for a workgroup (<= 8 column groups)
+constexpr int GROUPS = 4 * (CPW / 2);   // groups per k-step (4 reduction indices)
+
+template <bool FAST, bool GATHER>
+__device__ __forceinline__ void mainloop(const MainParams& p, const Word* panel, const Word* bsrc,
+                                         const uint32_t (&base)[RPL], int kb0, int kb1, int wcol,
+                                         const unsigned char* lut, Word* bbuf, float (&acc)[RPL][CPW])
+{
+    const int TN = p.wc * CPW;
+    const int nb = 4 * TN;                       // Words of one uniform k-step tile
+    // uniform tile copy: thread t moves Word t of the [4][TN] tile
+    const int ct = threadIdx.x;
+    const int crow = ct / TN, ccol = ct - crow * TN;
+    const bool copier = ct < nb;
+
+    KCounter kc = kc_init(p, GATHER ? kb0 * 4 : kb0);
+    int ku = kb0 * 4;
+    int off[4];
+    step_offsets<GATHER>(p, kc, ku, off);
+    uint32_t wa[4][RPL], sa[4][RPL];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) load_lane(panel, base, off[t], wa[t], sa[t]);
+
+    if (copier) bbuf[ct] = bsrc[((int64_t)kb0 * 4 + crow) * p.Np + ccol];
+    __syncthreads();
+
+    for (int kb = kb0; kb < kb1; ++kb) {
+        const int cur = (kb - kb0) & 1;
+        const bool more = kb + 1 < kb1;
+        Word nextb;
+        if (copier && more) nextb = bsrc[((int64_t)(kb + 1) * 4 + crow) * p.Np + ccol];
+        uint32_t wn[4][RPL], sn[4][RPL];
+        if (more) {
+            step_offsets<GATHER>(p, kc, ku, off);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) load_lane(panel, base, off[t], wn[t], sn[t]);
+        }
+        const Word* bt = bbuf + cur * BT_WORDS + wcol * CPW;
+
+        // software pipeline over the 32 groups of this k-step. Stage g issues
+        // the uniform-word read of group g+2, the lookups of group g+1, and
+        // folds group g into acc, so every LDS result has a stage to arrive.
+        constexpr int HJ = CPW / 2;
+        uint4 q[3];
+        uint32_t e[2][2 * RPL];
+        q[0] = *reinterpret_cast<const uint4*>(bt);
+        q[1] = *reinterpret_cast<const uint4*>(bt + 2);
+        group_lookup(wa[0], q[0], lut, e[0]);
+#pragma unroll
+        for (int g = 0; g < GROUPS; ++g) {
+            if (g + 2 < GROUPS) {
+                const int t2 = (g + 2) / HJ, j2 = (g + 2) % HJ;
+                q[(g + 2) % 3] = *reinterpret_cast<const uint4*>(bt + t2 * TN + 2 * j2);
+            }
+            if (g + 1 < GROUPS) group_lookup(wa[(g + 1) / HJ], q[(g + 1) % 3], lut, e[(g + 1) & 1]);
+            group_compute<FAST>(sa[g / HJ], q[g % 3], e[g & 1], g % HJ, acc);
+            // keep this group's folds here: without the anchor the compiler
+            // sinks them below every later lookup and spills the entries
+#pragma unroll
+            for (int x = 0; x < RPL; ++x) {
+                asm volatile("" : "+v"(acc[x][2 * (g % HJ)]));
+                asm volatile("" : "+v"(acc[x][2 * (g % HJ) + 1]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        if (copier && more) bbuf[(cur ^ 1) * BT_WORDS + ct] = nextb;
+        if (more) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int x = 0; x < RPL; ++x) { wa[t][x] = wn[t][x]; sa[t][x] = sn[t][x]; }
+        }
+        __syncthreads();
+    }
+}
+
+template <int LDSB, bool GATHER>
+__global__ __launch_bounds__(NT, 1) void main_kernel(MainParams p)
+{
+    __shared__ __align__(16) unsigned char lut[LDSB];
+    __shared__ __align__(16) Word bbuf[2 * BT_WORDS];
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(p.lut);
+        uint4* dst = reinterpret_cast<uint4*>(lut);
+        const int n16 = p.lut_bytes >> 4;
+        for (int t = threadIdx.x; t < n16; t += NT) dst[t] = src[t];
+    }
+    const int a_min = p.stats[0], a_max = p.stats[1], b_min = p.stats[2], b_max = p.stats[3];
+    const bool fast = !p.force_checked &&
+                      ((a_min > a_max) || (b_min > b_max) ||
+                       (a_min + b_min - 127 >= 1 && a_max + b_max - 126 <= 254 && a_max <= 253));
+    __syncthreads();
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wrow = wave / p.wc, wcol = wave - wrow * p.wc;
+    const int G = gridDim.x;
+    // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, so give
+    // the workgroups of one XCD consecutive work items (shared rows in its L2).
+    const int v = (G & 7) == 0 ? (int)((blockIdx.x & 7u) * (unsigned)(G >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
+    const int TM = p.wr * 64 * RPL, TN = p.wc * CPW;
+    const int items = (int)p.items;
+
+    for (int item = v; item < items; item += G) {
+        int t = item;
+        const int tn = t % p.tiles_n; t /= p.tiles_n;
+        const int tm = t % p.tiles_m; t /= p.tiles_m;
+        const int split = t % p.splits;
+        const int b = t / p.splits;
+        const int row0 = tm * TM + wrow * 64 * RPL;
+        const int col0 = tn * TN + wcol * CPW;
+        uint32_t base[RPL];
+#pragma unroll
+        for (int x = 0; x < RPL; ++x) {
+            const int i = min(row0 + x * 64 + lane, p.m_rows - 1);
+            const int i3 = i % p.E3, r2 = i / p.E3;
+            const int i2 = r2 % p.E2, i1 = r2 / p.E2;
+            base[x] = (uint32_t)(i1 * p.L1 + i2 * p.L2 + i3 * p.L3);
+        }
+        const Word* panel = p.panel + (int64_t)b * p.panel_batch;
+        const Word* bsrc = p.bpanel + (int64_t)b * p.bpanel_batch + (int64_t)tn * TN;
+        const int kb0 = split * p.chunk;
+        const int kb1 = min(p.KB, kb0 + p.chunk);
+
+        float acc[RPL][CPW];
+#pragma unroll
+        for (int x = 0; x < RPL; ++x)
+#pragma unroll
+            for (int j = 0; j < CPW; ++j) acc[x][j] = 0.0f;
+
+        if (kb0 < kb1) {
+            if (fast) mainloop<true, GATHER>(p, panel, bsrc, base, kb0, kb1, wcol, lut, bbuf, acc);
+            else mainloop<false, GATHER>(p, panel, bsrc, base, kb0, kb1, wcol, lut, bbuf, acc);
+        }
+
+        float* out;
+        int ld;
+        if (p.splits > 1) {
+            out = p.out + ((int64_t)b * p.splits + split) * (int64_t)p.m_out * p.n_out;
+            ld = p.n_out;
+        } else {
+            out = p.out + (int64_t)b * p.out_batch;
+            ld = p.ldc;
+        }
+#pragma unroll
+        for (int x = 0; x < RPL; ++x) {
+            const int i = row0 + x * 64 + lane;
+            if (i < p.m_out) {
+                float* o = out + (int64_t)i * ld + col0;
+#pragma unroll
+                for (int j = 0; j < CPW; ++j)
+                    if (col0 + j < p.n_out) o[j] = acc[x][j];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ reduce / fill
+
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p)
+{
+    const int64_t mn = (int64_t)p.m * p.n;
+    const int64_t total = mn * p.batch;
+    for (int64_t g = blockIdx.x * 256LL + threadIdx.x; g < total; g += (int64_t)gridDim.x * 256) {
+        const int64_t b = g / mn, r = g - b * mn;
+        const float* src = p.ws + b * p.splits * mn + r;
+        float s = 0.0f;
+        for (int sp = 0; sp < p.splits; ++sp) s += src[sp * mn];
+        const int64_t i = r / p.n, j = r - i * p.n;
+        p.out[b * p.out_batch + i * p.ldc + j] = s;
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* C, int m, int n, int ldc, int batch, int64_t strideC)
+{
+    const int64_t mn = (int64_t)m * n, total = mn * batch;
+    for (int64_t g = blockIdx.x * 256LL + threadIdx.x; g < total; g += (int64_t)gridDim.x * 256) {
+        const int64_t b = g / mn, r = g - b * mn, i = r / n, j = r - i * n;
+        C[b * strideC + i * ldc + j] = 0.0f;
+    }
+}
+
+// ------------------------------------------------------------------ launchers
+
+static int grid_for(int64_t work, int per_block, int cap)
+{
+    int64_t g = (work + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return (int)g;
+}
+
+hipError_t launch_init_stats(int* stats, hipStream_t s)
+{
+    hipLaunchKernelGGL(init_stats_kernel, dim3(1), dim3(64), 0, s, stats);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s)
+{
+    const int gx = grid_for(p.count, 256, 8192);
+    hipLaunchKernelGGL(decode_kernel, dim3(gx, p.batch), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_main(const MainParams& p, int lds_class, int gather, int grid, hipStream_t s)
+{
+    if (lds_class == 0) {
+        if (gather) hipLaunchKernelGGL((main_kernel<LDS_SMALL, true>), dim3(grid), dim3(NT), 0, s, p);
+        else hipLaunchKernelGGL((main_kernel<LDS_SMALL, false>), dim3(grid), dim3(NT), 0, s, p);
+    } else {
+        if (gather) hipLaunchKernelGGL((main_kernel<LDS_LARGE, true>), dim3(grid), dim3(NT), 0, s, p);
+        else hipLaunchKernelGGL((main_kernel<LDS_LARGE, false>), dim3(grid), dim3(NT), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+int main_blocks_per_cu(int lds_class, int gather)
+{
+    int n = 0;
+    hipError_t e;
+    if (lds_class == 0)
+        e = gather ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, main_kernel<LDS_SMALL, true>, NT, 0)
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, main_kernel<LDS_SMALL, false>, NT, 0);
+    else
+        e = gather ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, main_kernel<LDS_LARGE, true>, NT, 0)
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, main_kernel<LDS_LARGE, false>, NT, 0);
+    if (e != hipSuccess || n < 1) n = 1;
+    return n;
+}
+
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t s)
+{
+    const int64_t total = (int64_t)p.m * p.n * p.batch;
+    hipLaunchKernelGGL(reduce_kernel, dim3(grid_for(total, 256, 16384)), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* C, int m, int n, int ldc, int batch, int64_t strideC, hipStream_t s)
+{
+    const int64_t total = (int64_t)m * n * batch;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(total, 256, 16384)), dim3(256), 0, s,
+                       C, m, n, ldc, batch, strideC);
+    return hipGetLastError();
+}
+
+}  // namespace amx

@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of the LUT-based approximate FP32 GEMM on one MI355X.
+
+Default workload: one approximate GEMM C = A B with m = n = k = 8192, A and B
+~ N(0, 1) (seeded, synthetic), and the M = 8 table of the exact mantissa
+product with a seeded +/-1 perturbation of every entry. A step is one
+``approx_gemm`` call (decode pass + GEMM kernel) with the inputs already in
+HBM. Other workloads (--config 1, 2, 3, 5) are available for reference runs.
+
+Prints ONE JSON line: the metric (G approximate MAC/s), the GEMM kernel's
+roofline record (timed with HIP events inside the library, on the stream the
+kernel runs on) and the oracle's single-thread CPU throughput on a bounded
+sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X figures used by the roofline record
+CUS, LANES_PER_CU, CLOCK_HZ = 256, 64, 2.4e9
+VALU_PEAK_TOPS = CUS * LANES_PER_CU * CLOCK_HZ / 1e12     # 39.32 T 32-bit lane-ops/s
+OPS_PER_MAC = 3                                           # address, assemble, accumulate
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    p = os.path.join(ROOT, "approximate_multiplier_dnn_amd", "csrc", "kernels.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_record(workload):
+    """HBM bytes per GEMM-kernel launch from the committed counter summary,
+    if it was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f).get(workload)
+    if not rec or rec.get("kernel_sha") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def build_workload(config, am, torch):
+    from datagen import configs as cfg
+
+    model, M, pert = cfg.lut_spec(config)
+    lut = am.approx_lut_build(am.MODEL_EXACT if model == "exact" else am.MODEL_MITCHELL, M, pert)
+    am.approx_lut_load(lut, M)
+    d = lambda a: torch.from_numpy(a).cuda()
+    info = {}
+    if config in (1, 4):
+        size = 64 if config == 1 else 8192
+        A, B = cfg.gemm_square(config, size)
+        Ad, Bd = d(A), d(B)
+        Cd = torch.empty((size, size), dtype=torch.float32, device="cuda")
+
+        def step():
+            am.approx_gemm(0, 0, size, size, size, Ad, size, Bd, size, Cd, size)
+
+        workload = f"gemm_{size}x{size}x{size}_lut_m{M}_{'perturbed' if pert is not None else model}"
+        info = dict(m=size, n=size, k=size, table=f"{model} M={M}" + (" +-1 perturbed" if pert is not None else ""))
+        host = dict(A=A, B=B, lut=lut, M=M)
+    elif config == 2:
+        layers = cfg.mlp_tensors()
+        dev_layers = [tuple(d(t) for t in L) for L in layers]
+        calls = []
+        for (name, ta, tb, m, n, k, an, bn) in cfg.mlp_gemms():
+            X, W, dY = dev_layers[int(name[-1])]
+            ops = {"X": X, "W": W, "dY": dY}
+            A, B = ops[an], ops[bn]
+            C = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            calls.append((ta, tb, m, n, k, A, A.shape[1], B, B.shape[1], C, n))
+
+        def step():
+            for c in calls:
+                am.approx_gemm(*c)
+
+        workload = "mlp_784-1024-1024-10_b256_fwd_dgrad_wgrad_lut_m7_mitchell"
+        info = dict(batch=256, widths=[784, 1024, 1024, 10])
+        host = dict(layers=layers, lut=lut, M=M)
+    elif config == 3:
+        s = cfg.CONV_SHAPE
+        x, w, dy = cfg.conv_tensors()
+        xd, wd, dyd = d(x), d(w), d(dy)
+        N, H, W, C, K, R, S = s["N"], s["H"], s["W"], s["C"], s["K"], s["R"], s["S"]
+        st, pd = s["stride"], s["pad"]
+        y = torch.empty((N, H, W, K), dtype=torch.float32, device="cuda")
+        dx = torch.empty((N, H, W, C), dtype=torch.float32, device="cuda")
+        dw = torch.empty((R, S, C, K), dtype=torch.float32, device="cuda")
+
+        def step():
+            am.approx_conv2d_fwd(N, H, W, C, K, R, S, st, pd, xd, wd, y)
+            am.approx_conv2d_dgrad(N, H, W, C, K, R, S, st, pd, dyd, wd, dx)
+            am.approx_conv2d_wgrad(N, H, W, C, K, R, S, st, pd, xd, dyd, dw)
+
+        workload = "conv2d_3x3_s1_p1_nhwc_128x32x32x64_to_64_fwd_dgrad_wgrad_lut_m7_mitchell"
+        info = dict(N=N, H=H, W=W, C=C, K=K, R=R, S=S)
+        host = dict(x=x, w=w, dy=dy, lut=lut, M=M)
+    elif config == 5:
+        s = cfg.MHA_SHAPE
+        Bz, T, D, Hh = s["batch"], s["seq"], s["d_model"], s["heads"]
+        dh = D // Hh
+        X, Wqkv, Wo = cfg.mha_tensors()
+        Xd, Wqkvd, Wod = d(X), d(Wqkv), d(Wo)
+        qkv = torch.empty((Bz * T, 3 * D), dtype=torch.float32, device="cuda")
+        S_ = torch.empty((Bz, Hh, T, T), dtype=torch.float32, device="cuda")
+        O = torch.empty((Bz * T, D), dtype=torch.float32, device="cuda")
+        Y = torch.empty((Bz * T, D), dtype=torch.float32, device="cuda")
+
+        def step():
+            am.approx_gemm(0, 0, Bz * T, 3 * D, D, Xd, D, Wqkvd, 3 * D, qkv, 3 * D)
+            for b in range(Bz):
+                q = qkv[b * T:(b + 1) * T]
+                am.approx_gemm_strided_batched(0, 1, T, T, dh, q, 3 * D, dh, q[:, D:], 3 * D, dh,
+                                               S_[b], T, T * T, Hh)
+            P = torch.softmax(S_ * (1.0 / dh ** 0.5), dim=-1)
+            for b in range(Bz):
+                v = qkv[b * T:(b + 1) * T, 2 * D:]
+                am.approx_gemm_strided_batched(0, 0, T, dh, T, P[b], T, T * T, v, 3 * D, dh,
+                                               O[b * T:(b + 1) * T], D, dh, Hh)
+            am.approx_gemm(0, 0, Bz * T, D, D, O, D, Wod, D, Y, D)
+
+        workload = "mha_b16_s512_d768_h12_qkv_qk_pv_out_lut_m7_mitchell"
+        info = dict(batch=Bz, seq=T, d_model=D, heads=Hh, note="softmax between the products is in the step time")
+        host = dict(X=X, Wqkv=Wqkv, lut=lut, M=M)
+    else:
+        raise SystemExit(f"unknown config {config}")
+    return step, workload, info, host
+
+
+def cpu_baseline(config, host):
+    """The oracle, single-threaded, on a bounded sample of the workload."""
+    import numpy as np
+
+    import oracle
+    from datagen import configs as cfg
+
+    t0 = time.perf_counter()
+    if config in (1, 4):
+        rows = 64 if config == 1 else 4
+        A, B = host["A"], host["B"]
+        oracle.gemm(np.ascontiguousarray(A[:rows]), B, host["lut"], host["M"])
+        macs = rows * B.shape[0] * B.shape[1]
+        sample = f"rows 0-{rows - 1} of the {A.shape[0]}x{B.shape[1]}x{B.shape[0]} GEMM ({macs:.3g} MACs)"
+    elif config == 2:
+        macs = 0
+        for (name, ta, tb, m, n, k, an, bn) in cfg.mlp_gemms():
+            X, W, dY = host["layers"][int(name[-1])]
+            ops = {"X": X, "W": W, "dY": dY}
+            if name.startswith("wgrad"):
+                continue   # the three weight gradients are skipped to bound the sample
+            oracle.gemm(ops[an], ops[bn], host["lut"], host["M"], transA=bool(ta), transB=bool(tb))
+            macs += m * n * k
+        sample = f"the 6 forward and input-gradient GEMMs of one pass ({macs:.3g} MACs)"
+    elif config == 3:
+        x, w, dy = host["x"][:1], host["w"], host["dy"][:1]
+        oracle.conv2d_fwd(x, w, host["lut"], host["M"], (1, 1), (1, 1))
+        oracle.conv2d_dgrad(dy, w, x.shape, host["lut"], host["M"], (1, 1), (1, 1))
+        oracle.conv2d_wgrad(x, dy, w.shape, host["lut"], host["M"], (1, 1), (1, 1))
+        macs = 3 * 32 * 32 * 64 * 9 * 64
+        sample = f"image 0 of 128, fwd + dgrad + wgrad ({macs:.3g} MACs)"
+    else:
+        rows = 64
+        X, Wqkv = host["X"], host["Wqkv"]
+        oracle.gemm(np.ascontiguousarray(X[:rows]), Wqkv, host["lut"], host["M"])
+        macs = rows * Wqkv.shape[0] * Wqkv.shape[1]
+        sample = f"rows 0-{rows - 1} of the QKV projection ({macs:.3g} MACs)"
+    dt = time.perf_counter() - t0
+    return {"value": macs / dt / 1e9, "unit": "G approximate MAC/s", "cores": 1, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=4, help="workload 1-5 (4: 8192^3 GEMM, the headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the approximate GEMM is not sharded across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import approximate_multiplier_dnn_amd as am
+    from datagen import configs as cfg
+
+    assert torch.cuda.is_available(), "no GPU"
+    torch.cuda.set_device(0)
+    log(f"building workload {args.config} ...")
+    step, workload, info, host = build_workload(args.config, am, torch)
+    macs = cfg.macs(args.config)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    am.approx_profile_read()           # drop anything recorded so far
+    am.approx_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    am.approx_profile_enable(False)
+    launches, kern_ms = am.approx_profile_read()
+    ms_per_step = dt * 1e3 / args.steps
+    value = macs * args.steps / dt / 1e9
+    log(f"{workload}: {ms_per_step:.3f} ms/step, {value:.1f} G approx-MAC/s; "
+        f"GEMM kernel {launches} launches, {kern_ms / max(launches, 1):.3f} ms avg")
+
+    # roofline of the GEMM kernel: algorithmic lane-ops over kernel time
+    kern_s = kern_ms / 1e3
+    achieved = OPS_PER_MAC * macs * args.steps / kern_s / 1e12 if kern_s > 0 else 0.0
+    traffic = traffic_record(workload)
+    roofline = {
+        "bound": "alu",
+        "achieved": round(achieved, 3),
+        "peak": round(VALU_PEAK_TOPS, 2),
+        "unit": "TOP/s",
+        "frac": round(achieved / VALU_PEAK_TOPS, 4),
+        "traffic": traffic,
+        "kernel": "amx::main_kernel",
+        "kernel_ms_avg": round(kern_ms / max(launches, 1), 4),
+        "launches_per_step": launches // max(args.steps, 1),
+        "ops_per_mac": OPS_PER_MAC,
+        "kernel_G_mac_per_s": round(macs * args.steps / kern_s / 1e9, 1) if kern_s > 0 else 0.0,
+    }
+    rec = {
+        "metric": "G approximate MAC/s (LUT-simulated FP32 GEMM)",
+        "value": round(value, 2),
+        "unit": "G approximate MAC/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": dict(workload=workload, **info),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a CPU sample ...")
+        rec["cpu_baseline"] = cpu_baseline(args.config, host)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,29 +22,76 @@ _M2 = np.uint64(0x94D049BB133111EB)
 PERTURB_SEED = 0x5EED0008
 
 
+_CHUNK = 1 << 20
+
+
+def _draws_into(seed, start, z, tmp, base):
+    """z[:] = draws start .. start+len(z)-1 of stream ``seed`` (in place)."""
+    n = z.size
+    np.add(base[:n], np.uint64(start), out=z)
+    with np.errstate(over="ignore"):
+        np.multiply(z, _GOLDEN, out=z)
+        np.add(z, np.uint64(seed), out=z)
+        np.right_shift(z, np.uint64(30), out=tmp[:n])
+        np.bitwise_xor(z, tmp[:n], out=z)
+        np.multiply(z, _M1, out=z)
+        np.right_shift(z, np.uint64(27), out=tmp[:n])
+        np.bitwise_xor(z, tmp[:n], out=z)
+        np.multiply(z, _M2, out=z)
+        np.right_shift(z, np.uint64(31), out=tmp[:n])
+        np.bitwise_xor(z, tmp[:n], out=z)
+
+
+def _chunks(count):
+    for s in range(0, count, _CHUNK):
+        yield s, min(_CHUNK, count - s)
+
+
+def _buffers():
+    base = np.arange(1, _CHUNK + 1, dtype=np.uint64)
+    return np.empty(_CHUNK, np.uint64), np.empty(_CHUNK, np.uint64), base
+
+
 def splitmix64(seed, count, start=0):
     """Draws start .. start+count-1 of stream ``seed`` as uint64."""
-    with np.errstate(over="ignore"):
-        t = np.arange(start + 1, start + count + 1, dtype=np.uint64)
-        z = np.uint64(seed) + t * _GOLDEN
-        z = (z ^ (z >> np.uint64(30))) * _M1
-        z = (z ^ (z >> np.uint64(27))) * _M2
-        z = z ^ (z >> np.uint64(31))
-    return z
+    out = np.empty(count, dtype=np.uint64)
+    z, tmp, base = _buffers()
+    for s, n in _chunks(count):
+        _draws_into(seed, start + s, z[:n], tmp, base)
+        out[s:s + n] = z[:n]
+    return out
 
 
 def uniform01(seed, count):
-    """float64 in [0, 1)."""
-    return (splitmix64(seed, count) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+    """float64 in [0, 1): the top 53 bits of each draw."""
+    out = np.empty(count, dtype=np.float64)
+    z, tmp, base = _buffers()
+    for s, n in _chunks(count):
+        _draws_into(seed, s, z[:n], tmp, base)
+        np.right_shift(z[:n], np.uint64(11), out=z[:n])
+        np.multiply(z[:n], 2.0 ** -53, out=out[s:s + n], casting="unsafe")
+    return out
 
 
 def normal(seed, shape, std=1.0, mean=0.0):
-    """float32 N(mean, std**2) of the given shape (Box-Muller, cosine branch)."""
+    """float32 N(mean, std**2) of the given shape (Box-Muller, cosine branch):
+    value t uses uniform draws 2t and 2t+1."""
     n = int(np.prod(shape))
-    u = uniform01(seed, 2 * n)
-    u1, u2 = u[0::2], u[1::2]
-    z = np.sqrt(-2.0 * np.log1p(-u1)) * np.cos(2.0 * np.pi * u2)
-    return (mean + std * z).astype(np.float32).reshape(shape)
+    out = np.empty(n, dtype=np.float32)
+    z, tmp, base = _buffers()
+    u = np.empty(_CHUNK, np.float64)
+    half = _CHUNK // 2
+    for s in range(0, n, half):
+        c = min(half, n - s)
+        _draws_into(seed, 2 * s, z[:2 * c], tmp, base)
+        np.right_shift(z[:2 * c], np.uint64(11), out=z[:2 * c])
+        np.multiply(z[:2 * c], 2.0 ** -53, out=u[:2 * c], casting="unsafe")
+        u1 = u[0:2 * c:2]
+        u2 = u[1:2 * c:2]
+        r = np.sqrt(-2.0 * np.log1p(-u1))
+        v = r * np.cos(2.0 * np.pi * u2)
+        out[s:s + c] = (mean + std * v).astype(np.float32)
+    return out.reshape(shape)
 
 
 def uniform(seed, shape, low=0.0, high=1.0):

@@ -1,0 +1,175 @@
+/*
+ * approx_mul.h -- C ABI of the LUT-based approximate FP32 multiplication
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * Every product inside the GEMM and Conv2D passes below is the AMSim
+ * approximate product of "ApproxTrain: Fast Simulation of Approximate
+ * Multipliers for DNN Training and Inference" (arXiv 2209.04161), Section V,
+ * Algorithm 2: sign = XOR of the signs; biased exponent = EA + EB - 127 plus
+ * the carry read from the table; mantissa = the 15-bit mantissa read from the
+ * table at index (top M fraction bits of the first operand << M) | (top M
+ * fraction bits of the second operand). The resulting exponent decides the
+ * special cases: e <= 0 gives a signed zero, e >= 255 a signed infinity.
+ * Subnormal inputs count as zero; NaN inputs give NaN; infinity times zero
+ * gives NaN; infinity times a non-zero gives a signed infinity.
+ *
+ * Products are accumulated in FP32 (round to nearest even), starting from
+ * +0.0, in ascending order of the reduction index. When a reduction is split
+ * into chunks, each chunk is summed in ascending order and the chunk sums are
+ * added in ascending chunk order; the chunking depends only on the shapes.
+ * Results are therefore bitwise reproducible for the same inputs.
+ *
+ * Conventions shared by all calls:
+ *  - Tensors are FP32, row-major (C order), in device memory owned by the
+ *    caller. The library never frees or keeps them. Outputs are overwritten
+ *    (there is no alpha / beta) and must not alias an input.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *    The current HIP device is used. Compute calls are asynchronous: they
+ *    return once the work is queued, and faults surface at the caller's next
+ *    synchronisation with the stream.
+ *  - The library keeps, per device, the loaded table and a scratch arena per
+ *    stream (decoded operands, split-reduction partials). Calls queued on one
+ *    stream reuse that stream's arena in order; calls on different streams
+ *    use different arenas. The arena only grows; approx_release() frees it.
+ *  - Return value: APPROX_OK (0) or a negative status. Argument checks run
+ *    before any work is queued; on an error nothing is written.
+ */
+#ifndef APPROX_MUL_H
+#define APPROX_MUL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define APPROX_OK 0
+#define APPROX_EINVAL (-1)       /* bad size, leading dimension, flag or NULL pointer */
+#define APPROX_ENOLUT (-2)       /* no table loaded on the current device */
+#define APPROX_EUNSUPPORTED (-3) /* M outside [1, 8], or a table the generator cannot express */
+#define APPROX_EHIP (-4)         /* a HIP runtime call failed (allocation, copy, launch) */
+
+/* Built-in C models of multipliers for approx_lut_build. */
+#define APPROX_MODEL_EXACT 0    /* the exact product of the M-bit mantissas */
+#define APPROX_MODEL_MITCHELL 1 /* Mitchell's logarithmic multiplier: 1+x+y, or 2(x+y) when x+y >= 1 */
+
+/*
+ * Table generation, ApproxTrain Section V-A, Algorithm 1 (host only; makes no
+ * HIP call and needs no GPU).
+ *
+ * Writes 4^M uint16 entries to lut_out (caller-owned host memory): entry
+ * (ia << M) | ib is the product of the operands 1.ia and 1.ib (M fraction
+ * bits each, sign + and exponent 2^0) under the chosen model, as
+ * bit 15 = carry (the product's exponent exceeds the un-normalised exponent
+ * by one) and bits 14..0 = the top 15 bits of the product's fraction.
+ * `perturb` is NULL or 4^M int8 values added to each entry's 15-bit mantissa
+ * field, saturating at 0 and 0x7FFF, carry unchanged (a synthetic model).
+ * Errors: APPROX_EINVAL (NULL lut_out, unknown model),
+ * APPROX_EUNSUPPORTED (M outside [1, 11]).
+ */
+int approx_lut_build(int model, int M, const int8_t *perturb, uint16_t *lut_out);
+
+/*
+ * The same generation for a caller-supplied C model `mul(a, b)` of the
+ * multiplier (ApproxTrain Fig. 7: the user's functional model). mul is
+ * called once per mantissa pair with two normal floats in [1, 2). Its
+ * product must lie in [1, 4) (carry 0 or 1); otherwise
+ * APPROX_EUNSUPPORTED is returned and lut_out is left partly written.
+ */
+int approx_lut_build_from_model(int M, float (*mul)(float a, float b), uint16_t *lut_out);
+
+/*
+ * Load a table for use by the compute calls on the current device
+ * (ApproxTrain Section VI: tables are loaded into the run-time library at run
+ * time). `lut` is caller-owned host memory of 4^M entries in the format
+ * above; it is copied during the call. Synchronous: the device is
+ * synchronised before a previous table is released, so do not call it while
+ * other threads queue work. Errors: APPROX_EINVAL (NULL lut),
+ * APPROX_EUNSUPPORTED (M outside [1, 8]: the table must fit in LDS),
+ * APPROX_EHIP.
+ */
+int approx_lut_load(const uint16_t *lut, int M);
+
+/* M of the table loaded on the current device, or APPROX_ENOLUT. */
+int approx_lut_bits(void);
+
+/*
+ * C[i*ldc + j] = sum_p approx(op(A)(i,p), op(B)(p,j)),  0 <= i < m, 0 <= j < n,
+ * op(A)(i,p) = transA ? A[p*lda + i] : A[i*lda + p],
+ * op(B)(p,j) = transB ? B[j*ldb + p] : B[p*ldb + j].
+ * The first table operand of each product is the element of op(A).
+ * (The GEMM kernel of ApproxTrain Section VI-D, behind Dense and, through
+ * IM2COL, Conv2D.) m = 0 or n = 0 does nothing; k = 0 writes zeros.
+ * Errors: APPROX_EINVAL (negative sizes, NULL pointers with non-empty
+ * operands, lda/ldb/ldc smaller than the stored row length, flags not 0/1),
+ * APPROX_ENOLUT, APPROX_EHIP.
+ */
+int approx_gemm(int transA, int transB, int m, int n, int k,
+                const float *A, int lda, const float *B, int ldb,
+                float *C, int ldc, void *stream);
+
+/*
+ * `batch` independent GEMMs: matrix b uses A + b*strideA, B + b*strideB and
+ * C + b*strideC (strides in elements, >= 0), each as approx_gemm. Used for
+ * the per-head products of attention (ApproxTrain Section III: attention is
+ * matrix multiplication underneath). Output matrices must not overlap.
+ */
+int approx_gemm_strided_batched(int transA, int transB, int m, int n, int k,
+                                const float *A, int lda, long long strideA,
+                                const float *B, int ldb, long long strideB,
+                                float *C, int ldc, long long strideC,
+                                int batch, void *stream);
+
+/*
+ * Conv2D as implicit GEMM (ApproxTrain Section VI-B, Algorithms 3 and 4).
+ * Activations NHWC [N,H,W,C]; weights RSCK (HWIO) [R,S,C,K]; outputs NHWC
+ * [N,P,Q,K] with P = (H + 2*pad_h - R)/stride_h + 1, Q likewise.
+ * Cross-correlation (no filter flip in the forward pass), no dilation, no
+ * groups. Padding positions are zero operands that are multiplied, exactly
+ * as the zeros an explicit IM2COL buffer would hold.
+ *
+ * fwd:   y[n,p,q,k]  = sum_{r,s,c} approx(x[n, p*sh-ph+r, q*sw-pw+s, c], w[r,s,c,k])
+ * dgrad: dx[n,h,w,c] = sum_{r,s,k} approx(D[n, h+ph-r, w+pw-s, k], w[r,s,c,k])
+ *        where D holds dy[n, a/sh, b/sw, k] at offsets (a, b) that are
+ *        multiples of the strides inside the output, and zero elsewhere (the
+ *        padded, dilated errors, with the filter transposed and reversed).
+ * wgrad: dw[r,s,c,k] = sum_{n,p,q} approx(x[n, p*sh-ph+r, q*sw-pw+s, c], dy[n,p,q,k])
+ * Table operand order: (x, w), (dy, w) and (x, dy).
+ * Errors: APPROX_EINVAL (non-positive sizes or strides, negative pads,
+ * R > H + 2*pad_h or S > W + 2*pad_w, NULL pointers), APPROX_ENOLUT,
+ * APPROX_EHIP.
+ */
+int approx_conv2d_fwd(int N, int H, int W, int C, int K, int R, int S,
+                      int stride_h, int stride_w, int pad_h, int pad_w,
+                      const float *x, const float *w, float *y, void *stream);
+
+int approx_conv2d_dgrad(int N, int H, int W, int C, int K, int R, int S,
+                        int stride_h, int stride_w, int pad_h, int pad_w,
+                        const float *dy, const float *w, float *dx, void *stream);
+
+int approx_conv2d_wgrad(int N, int H, int W, int C, int K, int R, int S,
+                        int stride_h, int stride_w, int pad_h, int pad_w,
+                        const float *x, const float *dy, float *dw, void *stream);
+
+/*
+ * Kernel timing for benchmarks. While enabled (on != 0), every compute call
+ * records a HIP event pair around its GEMM kernel, on the call's stream.
+ * approx_profile_read waits for the recorded events, returns the number of
+ * GEMM-kernel launches and their summed duration in milliseconds, and clears
+ * the record. Errors: APPROX_EINVAL (NULL outputs), APPROX_EHIP.
+ */
+int approx_profile_enable(int on);
+int approx_profile_read(int *launches, double *total_ms);
+
+/* Static text for a status code. */
+const char *approx_status_string(int status);
+
+/* Synchronise every device the library used, then free its tables and
+ * arenas. A table must be loaded again before the next compute call. */
+int approx_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* APPROX_MUL_H */

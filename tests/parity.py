@@ -1,0 +1,34 @@
+"""Comparison of GPU results with the oracle.
+
+Gate (the reading of "max relative error 1e-5" that FP32 accumulation can
+meet): for every output, |c - r| <= tol * S, where r is the oracle's float64
+sum of the same approximate products and S the float64 sum of their
+magnitudes; S = 0 requires c = 0. Non-finite oracle values must be matched
+exactly (same infinity, or NaN for NaN).
+"""
+import numpy as np
+
+TOL = 1e-5
+
+
+def gate(c, r, s, tol=TOL, what=""):
+    c = np.asarray(c, dtype=np.float64).ravel()
+    r = np.asarray(r, dtype=np.float64).ravel()
+    s = np.asarray(s, dtype=np.float64).ravel()
+    assert c.shape == r.shape == s.shape, (c.shape, r.shape, s.shape)
+    fin = np.isfinite(r) & np.isfinite(s)
+    nan_r = np.isnan(r) | (np.isnan(s) & ~np.isinf(r))
+    if np.any(nan_r):
+        assert np.all(np.isnan(c[nan_r])), f"{what}: expected NaN"
+    inf_r = np.isinf(r) & ~nan_r
+    if np.any(inf_r):
+        assert np.array_equal(c[inf_r], r[inf_r]), f"{what}: expected matching infinities"
+    # finite oracle sums whose magnitudes overflow double would be a test bug
+    cf, rf, sf = c[fin], r[fin], s[fin]
+    assert np.all(np.isfinite(cf)), f"{what}: non-finite result where the oracle is finite"
+    zero = sf == 0
+    assert np.all(cf[zero] == 0), f"{what}: non-zero result where every product is zero"
+    err = np.abs(cf[~zero] - rf[~zero]) / sf[~zero]
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= tol, f"{what}: max |c-r|/S = {worst:.3e} > {tol}"
+    return worst

@@ -103,3 +103,11 @@ def test_perturbed_table():
     # the table is no longer symmetric: operand order matters
     t = p.reshape(256, 256)
     assert np.count_nonzero(t != t.T) > 1000
+
+
+def test_datagen_generator_matches_published_splitmix64():
+    """First outputs of splitmix64 seeded with 1234567, as printed by the
+    reference implementation of the generator (Steele, Lea and Flood 2014)."""
+    from datagen import splitmix64
+    assert [int(v) for v in splitmix64(1234567, 3)] == [
+        6457827717110365317, 3203168211198807973, 9817491932198370423]
