@@ -166,9 +166,11 @@ def test_gemm_special_values_and_extremes(am):
     A[5, 7] = np.float32(1e-40)         # subnormal
     A[6, 2] = np.inf
     B[9, 4] = np.nan
-    B[:, 10] = np.float32(3e37)
+    B[:, 10] = np.float32(1e35)         # large but the FP32 sums stay finite
     A[7, :] = np.float32(1e-30)
     B[:, 11] = np.float32(1e-20)        # products underflow
+    A[8, 5] = np.float32(1e30)
+    B[5, 12] = np.float32(1e30)         # one product overflows to +-Inf
     R, S = oracle.gemm(A, B, t, M)
     with np.errstate(invalid="ignore"):
         C = host(am.gemm(dev(A), dev(B)))
@@ -308,7 +310,8 @@ def test_workload3_conv_full_size_sampled(am):
         ("wgrad", dw, oracle.conv2d_wgrad, (x, dy, w.shape), 512),
     ):
         idx = (r[:count] % np.uint64(full.size)).astype(np.int64)
-        idx = np.concatenate([idx, [0, full.size - 1, 31 * 64, 32 * 64 * 31]])   # corners and borders
+        edges = np.array([0, full.size - 1, 31 * 64, 32 * 64 * 31, 32 * 32 * 64 - 1]) % full.size
+        idx = np.concatenate([idx, edges])   # corners and image borders
         R, S = fn(*args, t, M, st, pd, idx=idx)
         print(f"w3 {name}: {idx.size} samples", flush=True)
         gate(full[idx], R, S, what=f"w3 {name}")
