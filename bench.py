@@ -189,6 +189,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=4, help="workload 1-5 (4: 8192^3 GEMM, the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the workload, run one plain device copy of this many bytes "
+                         "(calibrates the HBM byte counters used for roofline.traffic)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -199,11 +202,20 @@ def main():
 
     import torch
 
-    import approximate_multiplier_dnn_amd as am
-    from datagen import configs as cfg
-
     assert torch.cuda.is_available(), "no GPU"
     torch.cuda.set_device(0)
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "read_bytes": n * 4, "written_bytes": n * 4}), flush=True)
+        return
+
+    import approximate_multiplier_dnn_amd as am
+    from datagen import configs as cfg
     log(f"building workload {args.config} ...")
     step, workload, info, host = build_workload(args.config, am, torch)
     macs = cfg.macs(args.config)
