@@ -290,80 +290,72 @@ __device__ __forceinline__ void group_compute(const uint32_t (&sa)[RPL], const u
     }
 }
 
-constexpr int BT_WORDS = 4 * 8 * CPW;   // uniform words of one k-step for a workgroup (<= 8 column groups)
 constexpr int GROUPS = 4 * (CPW / 2);   // groups per k-step (4 reduction indices)
+constexpr int TILE_GROUP_M = 4;         // row tiles per swizzle group (L2 reuse inside an XCD)
+
+// Uniform words of one reduction index for this wave's 16 columns, loaded
+// straight into VGPRs. `zero` is a VGPR that holds 0: adding it keeps the
+// uniform address in vector registers, so the loads stay on the vector
+// memory path and never share the LDS wait counter with scalar loads.
+__device__ __forceinline__ void load_uniform(const Word* row, uint32_t zero, uint4 (&q)[CPW / 2])
+{
+    const uint4* src = reinterpret_cast<const uint4*>(row) + zero;
+#pragma unroll
+    for (int j = 0; j < CPW / 2; ++j) q[j] = src[j];
+}
 
 template <bool FAST, bool GATHER>
 __device__ __forceinline__ void mainloop(const MainParams& p, const Word* panel, const Word* bsrc,
-                                         const uint32_t (&base)[RPL], int kb0, int kb1, int wcol,
-                                         const unsigned char* lut, Word* bbuf, float (&acc)[RPL][CPW])
+                                         const uint32_t (&base)[RPL], int kb0, int kb1, uint32_t zero,
+                                         const unsigned char* lut, float (&acc)[RPL][CPW])
 {
-    const int TN = p.wc * CPW;
-    const int nb = 4 * TN;                       // Words of one uniform k-step tile
-    // uniform tile copy: thread t moves Word t of the [4][TN] tile
-    const int ct = threadIdx.x;
-    const int crow = ct / TN, ccol = ct - crow * TN;
-    const bool copier = ct < nb;
-
+    constexpr int HJ = CPW / 2;
     KCounter kc = kc_init(p, GATHER ? kb0 * 4 : kb0);
     int ku = kb0 * 4;
     int off[4];
     step_offsets<GATHER>(p, kc, ku, off);
-    uint32_t wa[4][RPL], sa[4][RPL];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) load_lane(panel, base, off[t], wa[t], sa[t]);
-
-    if (copier) bbuf[ct] = bsrc[((int64_t)kb0 * 4 + crow) * p.Np + ccol];
-    __syncthreads();
+    // operand words of reduction index t are loaded while index t-1 is folded
+    uint32_t wa[2][RPL], sa[2][RPL];
+    uint4 qb[2][HJ];
+    load_lane(panel, base, off[0], wa[0], sa[0]);
+    load_uniform(bsrc + (int64_t)kb0 * 4 * p.Np, zero, qb[0]);
 
     for (int kb = kb0; kb < kb1; ++kb) {
-        const int cur = (kb - kb0) & 1;
         const bool more = kb + 1 < kb1;
-        Word nextb;
-        if (copier && more) nextb = bsrc[((int64_t)(kb + 1) * 4 + crow) * p.Np + ccol];
-        uint32_t wn[4][RPL], sn[4][RPL];
-        if (more) {
-            step_offsets<GATHER>(p, kc, ku, off);
+        int noff[4];
+        if (more) step_offsets<GATHER>(p, kc, ku, noff);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) load_lane(panel, base, off[t], wn[t], sn[t]);
-        }
-        const Word* bt = bbuf + cur * BT_WORDS + wcol * CPW;
-
-        // software pipeline over the 32 groups of this k-step. Stage g issues
-        // the uniform-word read of group g+2, the lookups of group g+1, and
-        // folds group g into acc, so every LDS result has a stage to arrive.
-        constexpr int HJ = CPW / 2;
-        uint4 q[3];
-        uint32_t e[2][2 * RPL];
-        q[0] = *reinterpret_cast<const uint4*>(bt);
-        q[1] = *reinterpret_cast<const uint4*>(bt + 2);
-        group_lookup(wa[0], q[0], lut, e[0]);
-#pragma unroll
-        for (int g = 0; g < GROUPS; ++g) {
-            if (g + 2 < GROUPS) {
-                const int t2 = (g + 2) / HJ, j2 = (g + 2) % HJ;
-                q[(g + 2) % 3] = *reinterpret_cast<const uint4*>(bt + t2 * TN + 2 * j2);
+        for (int t = 0; t < 4; ++t) {
+            const int cur = t & 1, nxt = cur ^ 1;
+            if (t < 3) {
+                load_lane(panel, base, off[t + 1], wa[nxt], sa[nxt]);
+                load_uniform(bsrc + ((int64_t)kb * 4 + t + 1) * p.Np, zero, qb[nxt]);
+            } else if (more) {
+                load_lane(panel, base, noff[0], wa[nxt], sa[nxt]);
+                load_uniform(bsrc + ((int64_t)kb + 1) * 4 * p.Np, zero, qb[nxt]);
             }
-            if (g + 1 < GROUPS) group_lookup(wa[(g + 1) / HJ], q[(g + 1) % 3], lut, e[(g + 1) & 1]);
-            group_compute<FAST>(sa[g / HJ], q[g % 3], e[g & 1], g % HJ, acc);
-            // keep this group's folds here: without the anchor the compiler
-            // sinks them below every later lookup and spills the entries
+            // software pipeline over the 8 groups of this reduction index: the
+            // lookups of group g+1 are in flight while group g is folded
+            uint32_t e[2][2 * RPL];
+            group_lookup(wa[cur], qb[cur][0], lut, e[0]);
 #pragma unroll
-            for (int x = 0; x < RPL; ++x) {
-                asm volatile("" : "+v"(acc[x][2 * (g % HJ)]));
-                asm volatile("" : "+v"(acc[x][2 * (g % HJ) + 1]));
+            for (int g = 0; g < HJ; ++g) {
+                if (g + 1 < HJ) group_lookup(wa[cur], qb[cur][g + 1], lut, e[(g + 1) & 1]);
+                group_compute<FAST>(sa[cur], qb[cur][g], e[g & 1], g, acc);
+                // keep this group's folds here: without the anchor the compiler
+                // sinks them below every later lookup and spills the entries
+#pragma unroll
+                for (int x = 0; x < RPL; ++x) {
+                    asm volatile("" : "+v"(acc[x][2 * g]));
+                    asm volatile("" : "+v"(acc[x][2 * g + 1]));
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
-
-        if (copier && more) bbuf[(cur ^ 1) * BT_WORDS + ct] = nextb;
         if (more) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int x = 0; x < RPL; ++x) { wa[t][x] = wn[t][x]; sa[t][x] = sn[t][x]; }
+            for (int t = 0; t < 4; ++t) off[t] = noff[t];
         }
-        __syncthreads();
     }
 }
 
@@ -371,7 +363,6 @@ template <int LDSB, bool GATHER>
 __global__ __launch_bounds__(NT, 1) void main_kernel(MainParams p)
 {
     __shared__ __align__(16) unsigned char lut[LDSB];
-    __shared__ __align__(16) Word bbuf[2 * BT_WORDS];
     {
         const uint4* src = reinterpret_cast<const uint4*>(p.lut);
         uint4* dst = reinterpret_cast<uint4*>(lut);
@@ -383,24 +374,35 @@ __global__ __launch_bounds__(NT, 1) void main_kernel(MainParams p)
                       ((a_min > a_max) || (b_min > b_max) ||
                        (a_min + b_min - 127 >= 1 && a_max + b_max - 126 <= 254 && a_max <= 253));
     __syncthreads();
+    uint32_t zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wrow = wave / p.wc, wcol = wave - wrow * p.wc;
     const int G = gridDim.x;
     // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, so give
-    // the workgroups of one XCD consecutive work items (shared rows in its L2).
+    // the workgroups of one XCD consecutive work items; consecutive items form
+    // TILE_GROUP_M x (n) blocks of output tiles, so they share rows and columns
+    // of the operands in that XCD's L2.
     const int v = (G & 7) == 0 ? (int)((blockIdx.x & 7u) * (unsigned)(G >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
     const int TM = p.wr * 64 * RPL, TN = p.wc * CPW;
     const int items = (int)p.items;
+    const int tiles = p.tiles_m * p.tiles_n;
 
     for (int item = v; item < items; item += G) {
-        int t = item;
-        const int tn = t % p.tiles_n; t /= p.tiles_n;
-        const int tm = t % p.tiles_m; t /= p.tiles_m;
-        const int split = t % p.splits;
-        const int b = t / p.splits;
+        const int tile = item % tiles;
+        const int rest = item / tiles;
+        const int split = rest % p.splits;
+        const int b = rest / p.splits;
+        const int group = tile / (TILE_GROUP_M * p.tiles_n);
+        const int first_m = group * TILE_GROUP_M;
+        const int gm = min(p.tiles_m - first_m, TILE_GROUP_M);
+        const int in_group = tile - group * TILE_GROUP_M * p.tiles_n;
+        const int tm = first_m + in_group % gm;
+        const int tn = in_group / gm;
         const int row0 = tm * TM + wrow * 64 * RPL;
         const int col0 = tn * TN + wcol * CPW;
+        if (row0 >= p.m_out || col0 >= p.n_out) continue;   // this wave has no output in the tile
         uint32_t base[RPL];
 #pragma unroll
         for (int x = 0; x < RPL; ++x) {
@@ -410,7 +412,7 @@ __global__ __launch_bounds__(NT, 1) void main_kernel(MainParams p)
             base[x] = (uint32_t)(i1 * p.L1 + i2 * p.L2 + i3 * p.L3);
         }
         const Word* panel = p.panel + (int64_t)b * p.panel_batch;
-        const Word* bsrc = p.bpanel + (int64_t)b * p.bpanel_batch + (int64_t)tn * TN;
+        const Word* bsrc = p.bpanel + (int64_t)b * p.bpanel_batch + col0;
         const int kb0 = split * p.chunk;
         const int kb1 = min(p.KB, kb0 + p.chunk);
 
@@ -421,8 +423,8 @@ __global__ __launch_bounds__(NT, 1) void main_kernel(MainParams p)
             for (int j = 0; j < CPW; ++j) acc[x][j] = 0.0f;
 
         if (kb0 < kb1) {
-            if (fast) mainloop<true, GATHER>(p, panel, bsrc, base, kb0, kb1, wcol, lut, bbuf, acc);
-            else mainloop<false, GATHER>(p, panel, bsrc, base, kb0, kb1, wcol, lut, bbuf, acc);
+            if (fast) mainloop<true, GATHER>(p, panel, bsrc, base, kb0, kb1, zero, lut, acc);
+            else mainloop<false, GATHER>(p, panel, bsrc, base, kb0, kb1, zero, lut, acc);
         }
 
         float* out;
