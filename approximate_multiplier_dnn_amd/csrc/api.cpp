@@ -78,6 +78,22 @@ int arena_get(int dev, hipStream_t stream, size_t bytes, char** out)
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Resident GEMM workgroups per device (CUs x blocks per CU), per kernel
+// variant; queried once per device and kept.
+int64_t g_slots[kMaxDevices][2][2];
+
+int64_t launch_slots(int dev, int lds_class, int gather)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    int64_t& s = g_slots[dev][lds_class][gather];
+    if (s == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+        s = (int64_t)cus * amx::main_blocks_per_cu(lds_class, gather);
+    }
+    return s;
+}
+
 int table_of(int dev, const uint16_t** image, int* M)
 {
     std::lock_guard<std::mutex> lock(g_mu);
@@ -189,9 +205,7 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     if (amx::launch_decode(pl.lane, stream) != hipSuccess) return APPROX_EHIP;
     if (amx::launch_decode(pl.uni, stream) != hipSuccess) return APPROX_EHIP;
 
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
-    const int64_t slots = (int64_t)cus * amx::main_blocks_per_cu(lds_class, pl.gather);
+    const int64_t slots = launch_slots(dev, lds_class, pl.gather);
     const int grid = (int)std::min<int64_t>(mp.items, slots);
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     bool prof;

@@ -42,6 +42,22 @@ enum Layout : int {
     L_DY_WGRAD,          // conv dy -> [Kp = NPQ rounded up to 4][Np] (uniform)
 };
 
+// Division by a divisor fixed for the launch (Granlund & Montgomery,
+// "Division by invariant integers using multiplication", 1994): for
+// n < 2^31, n / d = (umulhi(n, m) + n) >> l with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1.
+struct FastDiv {
+    uint32_t d, m, l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    uint32_t l = 0;
+    while (((uint64_t)1 << l) < d) ++l;
+    const uint64_t m = (((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1;
+    return FastDiv{d, (uint32_t)m, l};
+}
+
 struct DecodeParams {
     const float* src;
     Word* dst;
@@ -58,6 +74,10 @@ struct DecodeParams {
     int Mp, Np, KB;            // padded extents
     int N, H, W, C, K, R, S, sh, sw, ph, pw, P, Q;
     int Hp, Wp, Cb, Cp, Kb, Kp;
+    // divisors of the per-element index math (set by the host for the layout)
+    FastDiv fd_Mp, fd_Np, fd_Cp, fd_Kp, fd_S, fd_Wp, fd_Cb, fd_Kb, fd_Hp, fd_C;
+    int rows;            // image layouts: output rows (N * rows per image)
+    int row_floats;      // image layouts: floats in one source row
 };
 
 // GEMM kernel parameters. The lane operand of row i and k-step u is read at

@@ -58,73 +58,111 @@ __device__ __forceinline__ Word decode_bits(uint32_t bits, int M, int lane_role,
     return o;
 }
 
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f)
+{
+    return (__umulhi(n, f.m) + n) >> f.l;
+}
+
+__device__ __forceinline__ Word zero_word(int M, int lane_role)
+{
+    Word w;
+    w.se = 0u;
+    w.w = lane_role ? (1u << M) * 2u : 0u;
+    return w;
+}
+
+// Fold this thread's exponent range into the call's stats: wave reduction,
+// then one atomic per wave.
+__device__ __forceinline__ void flush_stats(int* stats, int emin, int emax)
+{
+    for (int off = 32; off > 0; off >>= 1) {
+        emin = min(emin, __shfl_xor(emin, off, 64));
+        emax = max(emax, __shfl_xor(emax, off, 64));
+    }
+    if ((threadIdx.x & 63) == 0 && emin <= emax) {
+        atomicMin(&stats[0], emin);
+        atomicMax(&stats[1], emax);
+    }
+}
+
 // Source element (within one batch entry) of output word o, or -1 for a
-// zero word (padding, dilation slot, or out-of-range tail).
+// zero word (padding, dilation slot, or out-of-range tail). Used by the
+// generic decode kernel; the image and tile kernels below cover the large
+// layouts with coalesced accesses.
 __device__ __forceinline__ int64_t decode_source(const DecodeParams& p, uint32_t o)
 {
     switch (p.layout) {
     case L_DENSE_LANE: {        // [KB][Mp][4]: element (i, kb*4+t) of op(A)
-        uint32_t t = o & 3u, r = o >> 2;
-        uint32_t i = r % (uint32_t)p.Mp, kb = r / (uint32_t)p.Mp;
-        uint32_t kk = kb * 4u + t;
+        const uint32_t t = o & 3u, r = o >> 2;
+        const uint32_t kb = fdiv(r, p.fd_Mp), i = r - kb * (uint32_t)p.Mp;
+        const uint32_t kk = kb * 4u + t;
         if (i >= (uint32_t)p.m || kk >= (uint32_t)p.k) return -1;
         return p.trans ? (int64_t)kk * p.ld + i : (int64_t)i * p.ld + kk;
     }
     case L_DENSE_UNIFORM: {     // [Kp][Np]: element (kk, j) of op(B)
-        uint32_t j = o % (uint32_t)p.Np, kk = o / (uint32_t)p.Np;
+        const uint32_t kk = fdiv(o, p.fd_Np), j = o - kk * (uint32_t)p.Np;
         if (j >= (uint32_t)p.n || kk >= (uint32_t)p.k) return -1;
         return p.trans ? (int64_t)j * p.ld + kk : (int64_t)kk * p.ld + j;
     }
     case L_IMG_FWD: {           // [N][Hp][Cb][Wp][4]
-        uint32_t t = o & 3u, r = o >> 2;
-        int wq = (int)(r % (uint32_t)p.Wp); r /= (uint32_t)p.Wp;
-        int cb = (int)(r % (uint32_t)p.Cb); r /= (uint32_t)p.Cb;
-        int hq = (int)(r % (uint32_t)p.Hp);
-        int n = (int)(r / (uint32_t)p.Hp);
-        int c = cb * 4 + (int)t, h = hq - p.ph, w = wq - p.pw;
+        const uint32_t t = o & 3u;
+        uint32_t r = o >> 2;
+        uint32_t q = fdiv(r, p.fd_Wp);
+        const int wq = (int)(r - q * (uint32_t)p.Wp);
+        r = q; q = fdiv(r, p.fd_Cb);
+        const int cb = (int)(r - q * (uint32_t)p.Cb);
+        r = q; q = fdiv(r, p.fd_Hp);
+        const int hq = (int)(r - q * (uint32_t)p.Hp), n = (int)q;
+        const int c = cb * 4 + (int)t, h = hq - p.ph, w = wq - p.pw;
         if (c >= p.C || h < 0 || h >= p.H || w < 0 || w >= p.W) return -1;
         return (((int64_t)n * p.H + h) * p.W + w) * p.C + c;
     }
     case L_IMG_DGRAD: {         // padded, dilated errors [N][Hd][Kb][Wd][4]
-        uint32_t t = o & 3u, r = o >> 2;
-        int bq = (int)(r % (uint32_t)p.Wp); r /= (uint32_t)p.Wp;
-        int kb = (int)(r % (uint32_t)p.Kb); r /= (uint32_t)p.Kb;
-        int aq = (int)(r % (uint32_t)p.Hp);
-        int n = (int)(r / (uint32_t)p.Hp);
-        int ko = kb * 4 + (int)t;
-        int hh = aq - (p.R - 1 - p.ph), ww = bq - (p.S - 1 - p.pw);
+        const uint32_t t = o & 3u;
+        uint32_t r = o >> 2;
+        uint32_t q = fdiv(r, p.fd_Wp);
+        const int bq = (int)(r - q * (uint32_t)p.Wp);
+        r = q; q = fdiv(r, p.fd_Kb);
+        const int kb = (int)(r - q * (uint32_t)p.Kb);
+        r = q; q = fdiv(r, p.fd_Hp);
+        const int aq = (int)(r - q * (uint32_t)p.Hp), n = (int)q;
+        const int ko = kb * 4 + (int)t;
+        const int hh = aq - (p.R - 1 - p.ph), ww = bq - (p.S - 1 - p.pw);
         if (ko >= p.K || hh < 0 || ww < 0 || hh % p.sh != 0 || ww % p.sw != 0) return -1;
-        int pp = hh / p.sh, qq = ww / p.sw;
+        const int pp = hh / p.sh, qq = ww / p.sw;
         if (pp >= p.P || qq >= p.Q) return -1;
         return (((int64_t)n * p.P + pp) * p.Q + qq) * p.K + ko;
     }
     case L_W_FWD: {             // [R*S*Cp][Np]: row (r, s, c), column k
-        uint32_t j = o % (uint32_t)p.Np, row = o / (uint32_t)p.Np;
-        uint32_t c = row % (uint32_t)p.Cp, rs = row / (uint32_t)p.Cp;
+        const uint32_t row = fdiv(o, p.fd_Np), j = o - row * (uint32_t)p.Np;
+        const uint32_t rs = fdiv(row, p.fd_Cp), c = row - rs * (uint32_t)p.Cp;
         if (c >= (uint32_t)p.C || j >= (uint32_t)p.K) return -1;
         return ((int64_t)rs * p.C + c) * p.K + j;
     }
     case L_W_DGRAD: {           // [R*S*Kp][Np]: row (R-1-r, S-1-s, k), column c
-        uint32_t j = o % (uint32_t)p.Np, row = o / (uint32_t)p.Np;
-        uint32_t ko = row % (uint32_t)p.Kp, rs = row / (uint32_t)p.Kp;
+        const uint32_t row = fdiv(o, p.fd_Np), j = o - row * (uint32_t)p.Np;
+        const uint32_t rs = fdiv(row, p.fd_Kp), ko = row - rs * (uint32_t)p.Kp;
         if (ko >= (uint32_t)p.K || j >= (uint32_t)p.C) return -1;
-        int rr = p.R - 1 - (int)(rs / (uint32_t)p.S), ss = p.S - 1 - (int)(rs % (uint32_t)p.S);
+        const uint32_t rq = fdiv(rs, p.fd_S);
+        const int rr = p.R - 1 - (int)rq, ss = p.S - 1 - (int)(rs - rq * (uint32_t)p.S);
         return (((int64_t)rr * p.S + ss) * p.C + j) * p.K + ko;
     }
     case L_IMG_WGRAD: {         // [N][Hp][C][Wp], then a zero tail
-        uint32_t body = (uint32_t)p.N * p.Hp * p.C * p.Wp;
+        const uint32_t body = (uint32_t)p.N * p.Hp * p.C * p.Wp;
         if (o >= body) return -1;
         uint32_t r = o;
-        int wq = (int)(r % (uint32_t)p.Wp); r /= (uint32_t)p.Wp;
-        int c = (int)(r % (uint32_t)p.C); r /= (uint32_t)p.C;
-        int hq = (int)(r % (uint32_t)p.Hp);
-        int n = (int)(r / (uint32_t)p.Hp);
-        int h = hq - p.ph, w = wq - p.pw;
+        uint32_t q = fdiv(r, p.fd_Wp);
+        const int wq = (int)(r - q * (uint32_t)p.Wp);
+        r = q; q = fdiv(r, p.fd_C);
+        const int c = (int)(r - q * (uint32_t)p.C);
+        r = q; q = fdiv(r, p.fd_Hp);
+        const int hq = (int)(r - q * (uint32_t)p.Hp), n = (int)q;
+        const int h = hq - p.ph, w = wq - p.pw;
         if (h < 0 || h >= p.H || w < 0 || w >= p.W) return -1;
         return (((int64_t)n * p.H + h) * p.W + w) * p.C + c;
     }
     case L_DY_WGRAD: {          // [Kp][Np]: row = output pixel, column = k
-        uint32_t j = o % (uint32_t)p.Np, kk = o / (uint32_t)p.Np;
+        const uint32_t kk = fdiv(o, p.fd_Np), j = o - kk * (uint32_t)p.Np;
         if (j >= (uint32_t)p.K || kk >= (uint32_t)(p.N * p.P * p.Q)) return -1;
         return (int64_t)kk * p.K + j;
     }
@@ -141,23 +179,130 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p)
     const uint32_t stride = gridDim.x * 256u;
     for (uint32_t o = blockIdx.x * 256u + threadIdx.x; o < (uint32_t)p.count; o += stride) {
         const int64_t s = decode_source(p, o);
-        Word wd;
-        if (s >= 0) {
-            wd = decode_bits(__float_as_uint(src[s]), p.M, p.lane_role, emin, emax);
-        } else {
-            wd.se = 0u;
-            wd.w = p.lane_role ? (1u << p.M) * 2u : 0u;
+        dst[o] = s >= 0 ? decode_bits(__float_as_uint(src[s]), p.M, p.lane_role, emin, emax)
+                        : zero_word(p.M, p.lane_role);
+    }
+    flush_stats(p.stats, emin, emax);
+}
+
+// Image layouts, one workgroup per output row: the source row (an NHWC row
+// of x, or of dy for the padded, dilated errors) is staged in LDS with
+// coalesced loads, then the output row is written contiguously.
+constexpr int IMG_ROW_FLOATS_MAX = 8192;   // 32 KB of LDS per workgroup
+
+__global__ __launch_bounds__(256) void decode_img_kernel(DecodeParams p)
+{
+    __shared__ float row[IMG_ROW_FLOATS_MAX];
+    int emin = 255, emax = 0;
+    const int r = blockIdx.x;                      // output row
+    Word* dst = p.dst;
+    if (r >= p.rows) {                             // zero tail of the weight-gradient image
+        const int64_t body = (int64_t)p.rows * p.C * p.Wp;
+        for (int64_t o = body + (int64_t)(r - p.rows) * 256 * 16 + threadIdx.x; o < p.count &&
+             o < body + (int64_t)(r - p.rows + 1) * 256 * 16; o += 256)
+            dst[o] = zero_word(p.M, p.lane_role);
+        return;
+    }
+    // which source row feeds output row r (or none: a padding / dilation row)
+    int n, srow = -1;
+    if (p.layout == L_IMG_DGRAD) {
+        n = r / p.Hp;
+        const int hh = r - n * p.Hp - (p.R - 1 - p.ph);
+        if (hh >= 0 && hh % p.sh == 0 && hh / p.sh < p.P) srow = hh / p.sh;
+    } else {
+        n = r / p.Hp;
+        const int h = r - n * p.Hp - p.ph;
+        if (h >= 0 && h < p.H) srow = h;
+    }
+    if (srow >= 0) {
+        const int rows_per_image = p.layout == L_IMG_DGRAD ? p.P : p.H;
+        const float* src = p.src + ((int64_t)n * rows_per_image + srow) * p.row_floats;
+        for (int i = threadIdx.x; i < p.row_floats; i += 256) row[i] = src[i];
+    }
+    __syncthreads();
+    if (p.layout == L_IMG_FWD) {                   // [Cb][Wp][4]
+        const int per_row = p.Cb * p.Wp * 4;
+        Word* out = dst + (int64_t)r * per_row;
+        for (int o = threadIdx.x; o < per_row; o += 256) {
+            const uint32_t t = o & 3u, q = (uint32_t)o >> 2;
+            const uint32_t cb = fdiv(q, p.fd_Wp);
+            const int w = (int)(q - cb * (uint32_t)p.Wp) - p.pw, c = (int)(cb * 4u + t);
+            out[o] = (srow >= 0 && c < p.C && w >= 0 && w < p.W)
+                         ? decode_bits(__float_as_uint(row[w * p.C + c]), p.M, p.lane_role, emin, emax)
+                         : zero_word(p.M, p.lane_role);
         }
-        dst[o] = wd;
+    } else if (p.layout == L_IMG_DGRAD) {          // [Kb][Wd][4]
+        const int per_row = p.Kb * p.Wp * 4;
+        Word* out = dst + (int64_t)r * per_row;
+        for (int o = threadIdx.x; o < per_row; o += 256) {
+            const uint32_t t = o & 3u, q = (uint32_t)o >> 2;
+            const uint32_t kb = fdiv(q, p.fd_Wp);
+            const int ww = (int)(q - kb * (uint32_t)p.Wp) - (p.S - 1 - p.pw), ko = (int)(kb * 4u + t);
+            bool ok = srow >= 0 && ko < p.K && ww >= 0 && (p.sw == 1 || ww % p.sw == 0);
+            const int qq = !ok ? 0 : (p.sw == 1 ? ww : ww / p.sw);
+            ok = ok && qq < p.Q;
+            out[o] = ok ? decode_bits(__float_as_uint(row[qq * p.K + ko]), p.M, p.lane_role, emin, emax)
+                        : zero_word(p.M, p.lane_role);
+        }
+    } else {                                       // L_IMG_WGRAD: [C][Wp]
+        const int per_row = p.C * p.Wp;
+        Word* out = dst + (int64_t)r * per_row;
+        for (int o = threadIdx.x; o < per_row; o += 256) {
+            const uint32_t c = fdiv((uint32_t)o, p.fd_Wp);
+            const int w = (int)((uint32_t)o - c * (uint32_t)p.Wp) - p.pw;
+            out[o] = (srow >= 0 && w >= 0 && w < p.W)
+                         ? decode_bits(__float_as_uint(row[w * p.C + (int)c]), p.M, p.lane_role, emin, emax)
+                         : zero_word(p.M, p.lane_role);
+        }
     }
-    for (int off = 32; off > 0; off >>= 1) {
-        emin = min(emin, __shfl_xor(emin, off, 64));
-        emax = max(emax, __shfl_xor(emax, off, 64));
+    flush_stats(p.stats, emin, emax);
+}
+
+// Dense layouts that transpose: 64 x 64 tiles through LDS, read along the
+// source's contiguous dimension and written along the output's.
+//  lane (A not transposed):   out [KB][Mp][4], element (i, kk) = A[i*ld + kk]
+//  uniform (B transposed):    out [Kp][Np],    element (kk, j) = B[j*ld + kk]
+__global__ __launch_bounds__(256) void decode_tile_kernel(DecodeParams p)
+{
+    __shared__ float tile[64][65];
+    int emin = 255, emax = 0;
+    const int b = blockIdx.z;
+    const float* src = p.src + b * p.src_batch_stride;
+    Word* dst = p.dst + b * p.dst_batch_stride;
+    const bool lane = p.layout == L_DENSE_LANE;
+    const int outer0 = blockIdx.x * 64;            // i (lane) or j (uniform)
+    const int k0 = blockIdx.y * 64;                // kk
+    const int outer_n = lane ? p.m : p.n;
+    // load: source row = outer index, contiguous kk
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int ro = e >> 6, kk = e & 63;
+        const int oi = outer0 + ro, ki = k0 + kk;
+        tile[ro][kk] = (oi < outer_n && ki < p.k) ? src[(int64_t)oi * p.ld + ki] : 0.0f;
     }
-    if ((threadIdx.x & 63) == 0 && emin <= emax) {
-        atomicMin(&p.stats[0], emin);
-        atomicMax(&p.stats[1], emax);
+    __syncthreads();
+    if (lane) {
+        // for each of the 16 k-steps of the tile, 64 rows x 4 words are contiguous
+        for (int e = threadIdx.x; e < 16 * 64 * 4; e += 256) {
+            const int kbl = e >> 8, i = (e >> 2) & 63, t = e & 3;
+            const int oi = outer0 + i, ki = k0 + kbl * 4 + t;
+            const int kb = (k0 >> 2) + kbl;
+            if (kb >= p.KB || oi >= p.Mp) continue;
+            dst[((int64_t)kb * p.Mp + oi) * 4 + t] =
+                (oi < p.m && ki < p.k) ? decode_bits(__float_as_uint(tile[i][kbl * 4 + t]), p.M, 1, emin, emax)
+                                       : zero_word(p.M, 1);
+        }
+    } else {
+        // each output row kk holds 64 contiguous columns j
+        for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+            const int kk = e >> 6, j = e & 63;
+            const int oj = outer0 + j, ki = k0 + kk;
+            if (ki >= p.KB * 4 || oj >= p.Np) continue;
+            dst[(int64_t)ki * p.Np + oj] =
+                (oj < p.n && ki < p.k) ? decode_bits(__float_as_uint(tile[j][kk]), p.M, 0, emin, emax)
+                                       : zero_word(p.M, 0);
+        }
     }
+    flush_stats(p.stats, emin, emax);
 }
 
 __global__ void init_stats_kernel(int* stats)
@@ -490,8 +635,36 @@ hipError_t launch_init_stats(int* stats, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeParams& p, hipStream_t s)
+hipError_t launch_decode(const DecodeParams& p0, hipStream_t s)
 {
+    DecodeParams p = p0;
+    auto fd = [](int v) { return make_fastdiv((uint32_t)(v > 0 ? v : 1)); };
+    p.fd_Mp = fd(p.Mp); p.fd_Np = fd(p.Np); p.fd_Cp = fd(p.Cp); p.fd_Kp = fd(p.Kp); p.fd_S = fd(p.S);
+    p.fd_Wp = fd(p.Wp); p.fd_Cb = fd(p.Cb); p.fd_Kb = fd(p.Kb); p.fd_Hp = fd(p.Hp); p.fd_C = fd(p.C);
+    const bool img = p.layout == L_IMG_FWD || p.layout == L_IMG_DGRAD || p.layout == L_IMG_WGRAD;
+    if (img) {
+        p.row_floats = p.layout == L_IMG_DGRAD ? p.Q * p.K : p.W * p.C;
+        p.rows = p.N * p.Hp;
+        if (p.row_floats <= IMG_ROW_FLOATS_MAX && p.batch == 1) {
+            int extra = 0;
+            if (p.layout == L_IMG_WGRAD) {
+                const int64_t tail = p.count - (int64_t)p.rows * p.C * p.Wp;
+                extra = (int)((tail + 256 * 16 - 1) / (256 * 16));
+            }
+            hipLaunchKernelGGL(decode_img_kernel, dim3(p.rows + extra), dim3(256), 0, s, p);
+            return hipGetLastError();
+        }
+    }
+    const bool tile = (p.layout == L_DENSE_LANE && !p.trans) || (p.layout == L_DENSE_UNIFORM && p.trans);
+    if (tile && p.batch <= 65535) {
+        const int outer = p.layout == L_DENSE_LANE ? p.Mp : p.Np;
+        const int kext = p.KB * 4;
+        dim3 g((outer + 63) / 64, (kext + 63) / 64, p.batch);
+        if (g.y <= 65535) {
+            hipLaunchKernelGGL(decode_tile_kernel, g, dim3(256), 0, s, p);
+            return hipGetLastError();
+        }
+    }
     const int gx = grid_for(p.count, 256, 8192);
     hipLaunchKernelGGL(decode_kernel, dim3(gx, p.batch), dim3(256), 0, s, p);
     return hipGetLastError();
