@@ -158,7 +158,7 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     pick_split(tiles, mp.KB, &mp.splits, &mp.chunk);
     mp.items = tiles * mp.splits;
 
-    const size_t stats_b = 256;
+    const size_t stats_b = align256(amx::STAT_INTS * sizeof(int));
     const size_t lane_b = align256((size_t)pl.lane_words * pl.batch * sizeof(Word));
     const size_t uni_b = align256((size_t)pl.uni_words * pl.batch * sizeof(Word));
     const size_t part_b = mp.splits > 1 ? align256((size_t)mp.splits * pl.batch * mp.m_out * mp.n_out * sizeof(float)) : 0;
@@ -415,6 +415,7 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
         u.layout = amx::L_DY_WGRAD;
         mp.KB = (int)cdiv(npq, 4);
         u.Kp = mp.KB * 4;
+        u.KB = mp.KB;
         pl.uni_words = (int64_t)mp.KB * 4 * Np;
         mp.E2 = s.S; mp.E3 = s.C;
         mp.L1 = s.C * Wp; mp.L2 = 1; mp.L3 = Wp;

@@ -58,10 +58,18 @@ inline FastDiv make_fastdiv(uint32_t d)
     return FastDiv{d, (uint32_t)m, l};
 }
 
+// Exponent statistics of one call: STAT_SLOTS slots, each on its own
+// 128-byte line, holding {lane min, lane max, uniform min, uniform max}.
+// Decode workgroups fold their range into slot (block % STAT_SLOTS); the GEMM
+// kernel reduces the slots.
+constexpr int STAT_SLOTS = 64;
+constexpr int STAT_STRIDE = 32;   // ints between slots
+constexpr int STAT_INTS = STAT_SLOTS * STAT_STRIDE;
+
 struct DecodeParams {
     const float* src;
     Word* dst;
-    int* stats;          // [2]: min and max biased exponent of normals seen
+    int* stats;          // slot base + role offset (0: lane, 2: uniform)
     int64_t count;       // words per batch entry
     int64_t src_batch_stride;  // elements
     int64_t dst_batch_stride;  // words
@@ -91,7 +99,7 @@ struct MainParams {
     const Word* panel;        // lane operand words
     const Word* bpanel;       // uniform operand words [Kp][Np]
     const uint16_t* lut;      // table image (lane-first layout)
-    const int* stats;         // [4]: lane min/max, uniform min/max exponent
+    const int* stats;         // STAT_SLOTS slots of {lane min, lane max, uniform min, uniform max}
     float* out;               // C (or split partials when splits > 1)
     int64_t panel_batch;      // Words between batch entries of the lane panel
     int64_t bpanel_batch;     // Words between batch entries of the uniform panel

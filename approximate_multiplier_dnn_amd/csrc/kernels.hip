@@ -25,6 +25,8 @@
 // same FMA produces the rule's zero, infinity and NaN cases. The exponent
 // range test is made from the per-operand min/max exponents gathered by the
 // decode pass. Otherwise the checked path evaluates Algorithm 2 per product.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace amx {
@@ -72,16 +74,34 @@ __device__ __forceinline__ Word zero_word(int M, int lane_role)
 }
 
 // Fold this thread's exponent range into the call's stats: wave reduction,
-// then one atomic per wave.
+// then workgroup reduction through LDS, then one atomic pair per workgroup
+// into slot (block % STAT_SLOTS), so no single address takes every atomic.
+// Must be called by every thread of a 256-thread workgroup.
 __device__ __forceinline__ void flush_stats(int* stats, int emin, int emax)
 {
+    __shared__ int red[2][4];
     for (int off = 32; off > 0; off >>= 1) {
         emin = min(emin, __shfl_xor(emin, off, 64));
         emax = max(emax, __shfl_xor(emax, off, 64));
     }
-    if ((threadIdx.x & 63) == 0 && emin <= emax) {
-        atomicMin(&stats[0], emin);
-        atomicMax(&stats[1], emax);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        red[0][wave] = emin;
+        red[1][wave] = emax;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int nw = blockDim.x >> 6;
+        for (int w = 1; w < nw; ++w) {
+            emin = min(emin, red[0][w]);
+            emax = max(emax, red[1][w]);
+        }
+        if (emin <= emax) {
+            const uint32_t blk = blockIdx.x + blockIdx.y * gridDim.x + blockIdx.z * gridDim.x * gridDim.y;
+            int* slot = stats + (blk % STAT_SLOTS) * STAT_STRIDE;
+            atomicMin(&slot[0], emin);
+            atomicMax(&slot[1], emax);
+        }
     }
 }
 
@@ -305,9 +325,30 @@ __global__ __launch_bounds__(256) void decode_tile_kernel(DecodeParams p)
     flush_stats(p.stats, emin, emax);
 }
 
-__global__ void init_stats_kernel(int* stats)
+__global__ __launch_bounds__(256) void init_stats_kernel(int* stats)
 {
-    if (threadIdx.x < 4) stats[threadIdx.x] = (threadIdx.x & 1) ? 0 : 255;
+    for (int i = threadIdx.x; i < STAT_INTS; i += 256) stats[i] = (i & 1) ? 0 : 255;
+}
+
+// Plain row copies with decode: out[kk][j] (kk < rows_out, j < Np) from
+// src[kk * ld + j] when kk < k and j < n (uniform panels of untransposed B
+// and of the weight-gradient errors). 2-D grid: no per-element division.
+__global__ __launch_bounds__(256) void decode_rows_kernel(DecodeParams p)
+{
+    int emin = 255, emax = 0;
+    const int b = blockIdx.z;
+    const float* src = p.src + b * p.src_batch_stride;
+    Word* dst = p.dst + b * p.dst_batch_stride;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    const int rows_out = p.KB * 4;
+    for (int kk = blockIdx.y; kk < rows_out; kk += gridDim.y) {
+        if (j < p.Np) {
+            dst[(int64_t)kk * p.Np + j] = (kk < p.k && j < p.n)
+                ? decode_bits(__float_as_uint(src[(int64_t)kk * p.ld + j]), p.M, p.lane_role, emin, emax)
+                : zero_word(p.M, p.lane_role);
+        }
+    }
+    flush_stats(p.stats, emin, emax);
 }
 
 // ------------------------------------------------------------------ products
@@ -514,11 +555,23 @@ __global__ __launch_bounds__(NT, 1) void main_kernel(MainParams p)
         const int n16 = p.lut_bytes >> 4;
         for (int t = threadIdx.x; t < n16; t += NT) dst[t] = src[t];
     }
-    const int a_min = p.stats[0], a_max = p.stats[1], b_min = p.stats[2], b_max = p.stats[3];
+    __shared__ int range[4];
+    if (threadIdx.x < 64) {                       // wave 0 folds the stats slots
+        const int* sl = p.stats + (threadIdx.x % STAT_SLOTS) * STAT_STRIDE;
+        int v0 = sl[0], v1 = sl[1], v2 = sl[2], v3 = sl[3];
+        for (int off = 32; off > 0; off >>= 1) {
+            v0 = min(v0, __shfl_xor(v0, off, 64));
+            v1 = max(v1, __shfl_xor(v1, off, 64));
+            v2 = min(v2, __shfl_xor(v2, off, 64));
+            v3 = max(v3, __shfl_xor(v3, off, 64));
+        }
+        if (threadIdx.x == 0) { range[0] = v0; range[1] = v1; range[2] = v2; range[3] = v3; }
+    }
+    __syncthreads();
+    const int a_min = range[0], a_max = range[1], b_min = range[2], b_max = range[3];
     const bool fast = !p.force_checked &&
                       ((a_min > a_max) || (b_min > b_max) ||
                        (a_min + b_min - 127 >= 1 && a_max + b_max - 126 <= 254 && a_max <= 253));
-    __syncthreads();
     uint32_t zero;
     asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
 
@@ -631,7 +684,7 @@ static int grid_for(int64_t work, int per_block, int cap)
 
 hipError_t launch_init_stats(int* stats, hipStream_t s)
 {
-    hipLaunchKernelGGL(init_stats_kernel, dim3(1), dim3(64), 0, s, stats);
+    hipLaunchKernelGGL(init_stats_kernel, dim3(1), dim3(256), 0, s, stats);
     return hipGetLastError();
 }
 
@@ -654,6 +707,14 @@ hipError_t launch_decode(const DecodeParams& p0, hipStream_t s)
             hipLaunchKernelGGL(decode_img_kernel, dim3(p.rows + extra), dim3(256), 0, s, p);
             return hipGetLastError();
         }
+    }
+    const bool rows = (p.layout == L_DENSE_UNIFORM && !p.trans) || p.layout == L_DY_WGRAD;
+    if (rows && p.batch <= 65535) {
+        if (p.layout == L_DY_WGRAD) { p.k = p.N * p.P * p.Q; p.n = p.K; p.ld = p.K; }
+        const int rows_out = p.KB * 4;
+        dim3 g((p.Np + 255) / 256, (unsigned)std::min(rows_out, 4096), p.batch);
+        hipLaunchKernelGGL(decode_rows_kernel, g, dim3(256), 0, s, p);
+        return hipGetLastError();
     }
     const bool tile = (p.layout == L_DENSE_LANE && !p.trans) || (p.layout == L_DENSE_UNIFORM && p.trans);
     if (tile && p.batch <= 65535) {
