@@ -29,7 +29,7 @@ MODEL_MITCHELL = 1
 #: every function the C header declares
 EXPORTS = (
     "approx_lut_build", "approx_lut_build_from_model", "approx_lut_load", "approx_lut_bits",
-    "approx_gemm", "approx_gemm_strided_batched",
+    "approx_gemm", "approx_gemm_strided_batched", "approx_gemm_batched",
     "approx_conv2d_fwd", "approx_conv2d_dgrad", "approx_conv2d_wgrad",
     "approx_profile_enable", "approx_profile_read",
     "approx_status_string", "approx_release",
@@ -48,6 +48,7 @@ _lib.approx_lut_load.argtypes = [_vp, _i]
 _lib.approx_lut_bits.argtypes = []
 _lib.approx_gemm.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, _vp]
 _lib.approx_gemm_strided_batched.argtypes = [_i] * 5 + [_vp, _i, _ll, _vp, _i, _ll, _vp, _i, _ll, _i, _vp]
+_lib.approx_gemm_batched.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, _i, _vp]
 for _n in ("approx_conv2d_fwd", "approx_conv2d_dgrad", "approx_conv2d_wgrad"):
     getattr(_lib, _n).argtypes = [_i] * 11 + [_vp, _vp, _vp, _vp]
 _lib.approx_status_string.argtypes = [_i]
@@ -164,6 +165,27 @@ def approx_gemm_strided_batched(transA, transB, m, n, k, A, lda, strideA, B, ldb
     return _check(_lib.approx_gemm_strided_batched(
         int(transA), int(transB), int(m), int(n), int(k), _ptr(A), int(lda), int(strideA), _ptr(B), int(ldb),
         int(strideB), _ptr(C), int(ldc), int(strideC), int(batch), _stream(stream)), "approx_gemm_strided_batched")
+
+
+def approx_gemm_batched(transA, transB, m, n, k, A_ptrs, lda, B_ptrs, ldb, C_ptrs, ldc, batch, stream=None):
+    """Batched GEMM by device pointer arrays (int64 tensors of data pointers on the GPU)."""
+    def arr(t):
+        if isinstance(t, int):
+            return t
+        import torch
+        if t.dtype != torch.int64 or not t.is_cuda or t.numel() < batch:
+            raise TypeError("pointer arrays must be int64 GPU tensors with one entry per batch")
+        return t.data_ptr()
+    return _check(_lib.approx_gemm_batched(int(transA), int(transB), int(m), int(n), int(k), arr(A_ptrs), int(lda),
+                                           arr(B_ptrs), int(ldb), arr(C_ptrs), int(ldc), int(batch),
+                                           _stream(stream)), "approx_gemm_batched")
+
+
+def pointer_array(tensors_or_ptrs, device="cuda"):
+    """int64 device tensor holding the data pointers of the given tensors."""
+    import torch
+    ptrs = [t if isinstance(t, int) else t.data_ptr() for t in tensors_or_ptrs]
+    return torch.tensor(ptrs, dtype=torch.int64, device=device)
 
 
 def _conv_call(name, N, H, W, C, K, R, S, stride, pad, t1, t2, out, stream):

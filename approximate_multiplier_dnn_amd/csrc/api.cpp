@@ -145,6 +145,7 @@ struct Plan {
     int batch = 1;
     int gather = 0;
     float* C = nullptr;
+    float* const* Cp = nullptr;   // output pointer array (batched by pointers)
     int64_t strideC = 0;
 };
 
@@ -198,6 +199,7 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
         mp.out = partials;
     } else {
         mp.out = pl.C;
+        mp.out_ptrs = pl.Cp;
         mp.out_batch = pl.strideC;
     }
 
@@ -228,6 +230,7 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
         ReduceParams rp{};
         rp.ws = partials;
         rp.out = pl.C;
+        rp.out_ptrs = pl.Cp;
         rp.m = mp.m_out;
         rp.n = mp.n_out;
         rp.ldc = mp.ldc;
@@ -241,8 +244,11 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
 
 int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int lda, long long strideA,
               const float* B, int ldb, long long strideB, float* C, int ldc, long long strideC, int batch,
-              void* stream_v)
+              void* stream_v, const float* const* Ap = nullptr, const float* const* Bp = nullptr,
+              float* const* Cp = nullptr)
 {
+    const bool arrays = Ap != nullptr || Bp != nullptr || Cp != nullptr;
+    if (arrays && (Ap == nullptr || Bp == nullptr || Cp == nullptr)) return APPROX_EINVAL;
     if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1)) return APPROX_EINVAL;
     if (m < 0 || n < 0 || k < 0 || batch < 0) return APPROX_EINVAL;
     if (strideA < 0 || strideB < 0 || strideC < 0) return APPROX_EINVAL;
@@ -251,8 +257,8 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
     if (ldc < std::max(1, n)) return APPROX_EINVAL;
     if (batch > 65535) return APPROX_EUNSUPPORTED;
     if (m == 0 || n == 0 || batch == 0) return APPROX_OK;
-    if (C == nullptr) return APPROX_EINVAL;
-    if (k > 0 && (A == nullptr || B == nullptr)) return APPROX_EINVAL;
+    if (!arrays && C == nullptr) return APPROX_EINVAL;
+    if (!arrays && k > 0 && (A == nullptr || B == nullptr)) return APPROX_EINVAL;
 
     int dev = 0;
     int rc = current_device(&dev);
@@ -264,7 +270,8 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
     hipStream_t stream = static_cast<hipStream_t>(stream_v);
 
     if (k == 0) {
-        return amx::launch_fill_zero(C, m, n, ldc, batch, strideC, stream) == hipSuccess ? APPROX_OK : APPROX_EHIP;
+        return amx::launch_fill_zero(C, Cp, m, n, ldc, batch, strideC, stream) == hipSuccess ? APPROX_OK
+                                                                                          : APPROX_EHIP;
     }
 
     Plan pl;
@@ -282,8 +289,10 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
     const int Mp = mp.tiles_m * TM, Np = mp.tiles_n * TN;
     const int KB = (int)cdiv(k, 4);
 
+    pl.Cp = Cp;
     DecodeParams& a = pl.lane;
     a.src = A;
+    a.src_ptrs = Ap;
     a.src_batch_stride = strideA;
     a.layout = amx::L_DENSE_LANE;
     a.m = m; a.n = n; a.k = k; a.ld = lda; a.trans = transA;
@@ -292,6 +301,7 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
 
     DecodeParams& u = pl.uni;
     u.src = B;
+    u.src_ptrs = Bp;
     u.src_batch_stride = strideB;
     u.layout = amx::L_DENSE_UNIFORM;
     u.m = m; u.n = n; u.k = k; u.ld = ldb; u.trans = transB;
@@ -417,10 +427,11 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
         u.Kp = mp.KB * 4;
         u.KB = mp.KB;
         pl.uni_words = (int64_t)mp.KB * 4 * Np;
+        // lane row (r, s, c) of the padded NHWC image, reduction index (n, p, q)
         mp.E2 = s.S; mp.E3 = s.C;
-        mp.L1 = s.C * Wp; mp.L2 = 1; mp.L3 = Wp;
+        mp.L1 = Wp * s.C; mp.L2 = s.C; mp.L3 = 1;
         mp.U1 = s.N; mp.U2 = s.P; mp.U3 = s.Q;
-        mp.K1 = Hp * s.C * Wp; mp.K2 = s.sh * s.C * Wp; mp.K3 = s.sw;
+        mp.K1 = Hp * Wp * s.C; mp.K2 = s.sh * Wp * s.C; mp.K3 = s.sw * s.C;
         mp.nku = (int)npq;
         mp.zoff = (int)body;
         pl.gather = 1;
@@ -480,6 +491,14 @@ extern "C" int approx_gemm_strided_batched(int transA, int transB, int m, int n,
                                            int ldc, long long strideC, int batch, void* stream)
 {
     return gemm_impl(transA, transB, m, n, k, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, stream);
+}
+
+extern "C" int approx_gemm_batched(int transA, int transB, int m, int n, int k, const float* const* A, int lda,
+                                   const float* const* B, int ldb, float* const* C, int ldc, int batch, void* stream)
+{
+    if (batch > 0 && (A == nullptr || B == nullptr || C == nullptr)) return APPROX_EINVAL;
+    return gemm_impl(transA, transB, m, n, k, nullptr, lda, 0, nullptr, ldb, 0, nullptr, ldc, 0, batch, stream,
+                     A, B, C);
 }
 
 extern "C" int approx_conv2d_fwd(int N, int H, int W, int C, int K, int R, int S, int stride_h, int stride_w,

@@ -38,7 +38,7 @@ enum Layout : int {
     L_IMG_DGRAD,         // conv dy -> padded dilated [N][H+R-1][Kb][W+S-1][4] (lane)
     L_W_FWD,             // conv w  -> [R*S*Cp][Np] (uniform)
     L_W_DGRAD,           // conv w  -> reversed, transposed [R*S*Kp][Np] (uniform)
-    L_IMG_WGRAD,         // conv x  -> [N][H+2ph][C][W+2pw] + zero tail (lane)
+    L_IMG_WGRAD,         // conv x  -> [N][H+2ph][W+2pw][C] + zero tail (lane)
     L_DY_WGRAD,          // conv dy -> [Kp = NPQ rounded up to 4][Np] (uniform)
 };
 
@@ -68,6 +68,7 @@ constexpr int STAT_INTS = STAT_SLOTS * STAT_STRIDE;
 
 struct DecodeParams {
     const float* src;
+    const float* const* src_ptrs;   // batched by pointer array (device), else src + b * stride
     Word* dst;
     int* stats;          // slot base + role offset (0: lane, 2: uniform)
     int64_t count;       // words per batch entry
@@ -101,6 +102,7 @@ struct MainParams {
     const uint16_t* lut;      // table image (lane-first layout)
     const int* stats;         // STAT_SLOTS slots of {lane min, lane max, uniform min, uniform max}
     float* out;               // C (or split partials when splits > 1)
+    float* const* out_ptrs;   // batched by pointer array (device): C of entry b
     int64_t panel_batch;      // Words between batch entries of the lane panel
     int64_t bpanel_batch;     // Words between batch entries of the uniform panel
     int64_t out_batch;        // floats between batch entries of C
@@ -122,6 +124,7 @@ struct MainParams {
 struct ReduceParams {
     const float* ws;
     float* out;
+    float* const* out_ptrs;
     int m, n, ldc, splits, batch;
     int64_t out_batch;
 };
@@ -130,7 +133,8 @@ hipError_t launch_init_stats(int* stats, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_main(const MainParams& p, int lds_class, int gather, int grid, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
-hipError_t launch_fill_zero(float* C, int m, int n, int ldc, int batch, int64_t strideC, hipStream_t s);
+hipError_t launch_fill_zero(float* C, float* const* Cp, int m, int n, int ldc, int batch, int64_t strideC,
+                            hipStream_t s);
 int main_blocks_per_cu(int lds_class, int gather);
 
 }  // namespace amx

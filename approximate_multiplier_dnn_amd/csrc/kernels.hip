@@ -167,14 +167,14 @@ __device__ __forceinline__ int64_t decode_source(const DecodeParams& p, uint32_t
         const int rr = p.R - 1 - (int)rq, ss = p.S - 1 - (int)(rs - rq * (uint32_t)p.S);
         return (((int64_t)rr * p.S + ss) * p.C + j) * p.K + ko;
     }
-    case L_IMG_WGRAD: {         // [N][Hp][C][Wp], then a zero tail
-        const uint32_t body = (uint32_t)p.N * p.Hp * p.C * p.Wp;
+    case L_IMG_WGRAD: {         // [N][Hp][Wp][C], then a zero tail
+        const uint32_t body = (uint32_t)p.N * p.Hp * p.Wp * p.C;
         if (o >= body) return -1;
         uint32_t r = o;
-        uint32_t q = fdiv(r, p.fd_Wp);
-        const int wq = (int)(r - q * (uint32_t)p.Wp);
-        r = q; q = fdiv(r, p.fd_C);
+        uint32_t q = fdiv(r, p.fd_C);
         const int c = (int)(r - q * (uint32_t)p.C);
+        r = q; q = fdiv(r, p.fd_Wp);
+        const int wq = (int)(r - q * (uint32_t)p.Wp);
         r = q; q = fdiv(r, p.fd_Hp);
         const int hq = (int)(r - q * (uint32_t)p.Hp), n = (int)q;
         const int h = hq - p.ph, w = wq - p.pw;
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p)
 {
     int emin = 255, emax = 0;
     const int b = blockIdx.y;
-    const float* src = p.src + b * p.src_batch_stride;
+    const float* src = p.src_ptrs ? p.src_ptrs[b] : p.src + b * p.src_batch_stride;
     Word* dst = p.dst + b * p.dst_batch_stride;
     const uint32_t stride = gridDim.x * 256u;
     for (uint32_t o = blockIdx.x * 256u + threadIdx.x; o < (uint32_t)p.count; o += stride) {
@@ -264,14 +264,14 @@ __global__ __launch_bounds__(256) void decode_img_kernel(DecodeParams p)
             out[o] = ok ? decode_bits(__float_as_uint(row[qq * p.K + ko]), p.M, p.lane_role, emin, emax)
                         : zero_word(p.M, p.lane_role);
         }
-    } else {                                       // L_IMG_WGRAD: [C][Wp]
-        const int per_row = p.C * p.Wp;
+    } else {                                       // L_IMG_WGRAD: [Wp][C]
+        const int per_row = p.Wp * p.C;
         Word* out = dst + (int64_t)r * per_row;
         for (int o = threadIdx.x; o < per_row; o += 256) {
-            const uint32_t c = fdiv((uint32_t)o, p.fd_Wp);
-            const int w = (int)((uint32_t)o - c * (uint32_t)p.Wp) - p.pw;
+            const uint32_t wq = fdiv((uint32_t)o, p.fd_C);
+            const int c = (int)((uint32_t)o - wq * (uint32_t)p.C), w = (int)wq - p.pw;
             out[o] = (srow >= 0 && w >= 0 && w < p.W)
-                         ? decode_bits(__float_as_uint(row[w * p.C + (int)c]), p.M, p.lane_role, emin, emax)
+                         ? decode_bits(__float_as_uint(row[w * p.C + c]), p.M, p.lane_role, emin, emax)
                          : zero_word(p.M, p.lane_role);
         }
     }
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256) void decode_tile_kernel(DecodeParams p)
     __shared__ float tile[64][65];
     int emin = 255, emax = 0;
     const int b = blockIdx.z;
-    const float* src = p.src + b * p.src_batch_stride;
+    const float* src = p.src_ptrs ? p.src_ptrs[b] : p.src + b * p.src_batch_stride;
     Word* dst = p.dst + b * p.dst_batch_stride;
     const bool lane = p.layout == L_DENSE_LANE;
     const int outer0 = blockIdx.x * 64;            // i (lane) or j (uniform)
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeParams p)
 {
     int emin = 255, emax = 0;
     const int b = blockIdx.z;
-    const float* src = p.src + b * p.src_batch_stride;
+    const float* src = p.src_ptrs ? p.src_ptrs[b] : p.src + b * p.src_batch_stride;
     Word* dst = p.dst + b * p.dst_batch_stride;
     const int j = blockIdx.x * 256 + threadIdx.x;
     const int rows_out = p.KB * 4;
@@ -631,7 +631,7 @@ __global__ __launch_bounds__(NT, 1) void main_kernel(MainParams p)
             out = p.out + ((int64_t)b * p.splits + split) * (int64_t)p.m_out * p.n_out;
             ld = p.n_out;
         } else {
-            out = p.out + (int64_t)b * p.out_batch;
+            out = p.out_ptrs ? p.out_ptrs[b] : p.out + (int64_t)b * p.out_batch;
             ld = p.ldc;
         }
 #pragma unroll
@@ -659,16 +659,19 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p)
         float s = 0.0f;
         for (int sp = 0; sp < p.splits; ++sp) s += src[sp * mn];
         const int64_t i = r / p.n, j = r - i * p.n;
-        p.out[b * p.out_batch + i * p.ldc + j] = s;
+        float* out = p.out_ptrs ? p.out_ptrs[b] : p.out + b * p.out_batch;
+        out[i * p.ldc + j] = s;
     }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float* C, int m, int n, int ldc, int batch, int64_t strideC)
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* C, float* const* Cp, int m, int n, int ldc, int batch,
+                                                        int64_t strideC)
 {
     const int64_t mn = (int64_t)m * n, total = mn * batch;
     for (int64_t g = blockIdx.x * 256LL + threadIdx.x; g < total; g += (int64_t)gridDim.x * 256) {
         const int64_t b = g / mn, r = g - b * mn, i = r / n, j = r - i * n;
-        C[b * strideC + i * ldc + j] = 0.0f;
+        float* out = Cp ? Cp[b] : C + b * strideC;
+        out[i * ldc + j] = 0.0f;
     }
 }
 
@@ -764,11 +767,12 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_fill_zero(float* C, int m, int n, int ldc, int batch, int64_t strideC, hipStream_t s)
+hipError_t launch_fill_zero(float* C, float* const* Cp, int m, int n, int ldc, int batch, int64_t strideC,
+                            hipStream_t s)
 {
     const int64_t total = (int64_t)m * n * batch;
     hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(total, 256, 16384)), dim3(256), 0, s,
-                       C, m, n, ldc, batch, strideC);
+                       C, Cp, m, n, ldc, batch, strideC);
     return hipGetLastError();
 }
 

@@ -119,17 +119,24 @@ def build_workload(config, am, torch):
         O = torch.empty((Bz * T, D), dtype=torch.float32, device="cuda")
         Y = torch.empty((Bz * T, D), dtype=torch.float32, device="cuda")
 
+        # per (sequence, head) pointers into the fused QKV buffer, the score
+        # and output tensors: one batched call per product stage
+        pairs = [(b, h) for b in range(Bz) for h in range(Hh)]
+        base, f = qkv.data_ptr(), 4
+        q_ptr = am.pointer_array([base + f * (b * T * 3 * D + h * dh) for b, h in pairs])
+        k_ptr = am.pointer_array([base + f * (b * T * 3 * D + D + h * dh) for b, h in pairs])
+        v_ptr = am.pointer_array([base + f * (b * T * 3 * D + 2 * D + h * dh) for b, h in pairs])
+        s_ptr = am.pointer_array([S_.data_ptr() + f * (b * Hh + h) * T * T for b, h in pairs])
+        P = torch.empty_like(S_)
+        p_ptr = am.pointer_array([P.data_ptr() + f * (b * Hh + h) * T * T for b, h in pairs])
+        o_ptr = am.pointer_array([O.data_ptr() + f * (b * T * D + h * dh) for b, h in pairs])
+        nb = len(pairs)
+
         def step():
             am.approx_gemm(0, 0, Bz * T, 3 * D, D, Xd, D, Wqkvd, 3 * D, qkv, 3 * D)
-            for b in range(Bz):
-                q = qkv[b * T:(b + 1) * T]
-                am.approx_gemm_strided_batched(0, 1, T, T, dh, q, 3 * D, dh, q[:, D:], 3 * D, dh,
-                                               S_[b], T, T * T, Hh)
-            P = torch.softmax(S_ * (1.0 / dh ** 0.5), dim=-1)
-            for b in range(Bz):
-                v = qkv[b * T:(b + 1) * T, 2 * D:]
-                am.approx_gemm_strided_batched(0, 0, T, dh, T, P[b], T, T * T, v, 3 * D, dh,
-                                               O[b * T:(b + 1) * T], D, dh, Hh)
+            am.approx_gemm_batched(0, 1, T, T, dh, q_ptr, 3 * D, k_ptr, 3 * D, s_ptr, T, nb)
+            torch.softmax(S_ * (1.0 / dh ** 0.5), dim=-1, out=P)
+            am.approx_gemm_batched(0, 0, T, dh, T, p_ptr, T, v_ptr, 3 * D, o_ptr, D, nb)
             am.approx_gemm(0, 0, Bz * T, D, D, O, D, Wod, D, Y, D)
 
         workload = "mha_b16_s512_d768_h12_qkv_qk_pv_out_lut_m7_mitchell"

@@ -121,6 +121,21 @@ int approx_gemm_strided_batched(int transA, int transB, int m, int n, int k,
                                 int batch, void *stream);
 
 /*
+ * `batch` independent GEMMs given by arrays of device pointers: A[b], B[b]
+ * and C[b] (the arrays themselves in device memory, caller-owned, read by
+ * the kernels while they run). Each entry is as approx_gemm with the shared
+ * sizes and leading dimensions; output matrices must not overlap. Serves
+ * batches that no single stride describes, such as the (sequence, head)
+ * products of multi-head attention. Errors: as approx_gemm, and
+ * APPROX_EINVAL for NULL arrays.
+ */
+int approx_gemm_batched(int transA, int transB, int m, int n, int k,
+                        const float *const *A, int lda,
+                        const float *const *B, int ldb,
+                        float *const *C, int ldc,
+                        int batch, void *stream);
+
+/*
  * Conv2D as implicit GEMM (ApproxTrain Section VI-B, Algorithms 3 and 4).
  * Activations NHWC [N,H,W,C]; weights RSCK (HWIO) [R,S,C,K]; outputs NHWC
  * [N,P,Q,K] with P = (H + 2*pad_h - R)/stride_h + 1, Q likewise.

@@ -221,6 +221,29 @@ def test_strided_batched_heads(am):
         gate(got[h], R, S, what=f"head {h}")
 
 
+def test_batched_by_pointer_arrays(am):
+    """Matrices at unrelated places in different buffers, one call."""
+    M, t = use(am, "mitchell7")
+    m, n, k = 37, 29, 45
+    bufA = normal(61, (5000,))
+    bufB = normal(62, (7000,))
+    offsA = [0, 1700, 3011]
+    offsB = [4000, 13, 2500]
+    As = [bufA[o:o + m * k].reshape(m, k) for o in offsA]
+    Bs = [bufB[o:o + k * n].reshape(k, n) for o in offsB]
+    dA, dB = dev(bufA), dev(bufB)
+    C = torch.full((3, m, n + 3), -1.0, device="cuda")
+    pa = am.pointer_array([dA.data_ptr() + 4 * o for o in offsA])
+    pb = am.pointer_array([dB.data_ptr() + 4 * o for o in offsB])
+    pc = am.pointer_array([C[i].data_ptr() for i in range(3)])
+    am.approx_gemm_batched(0, 0, m, n, k, pa, k, pb, n, pc, n + 3, 3)
+    got = host(C)
+    for i in range(3):
+        R, S = oracle.gemm(As[i], Bs[i], t, M)
+        gate(got[i][:, :n], R, S, what=f"ptr batch {i}")
+        assert np.all(got[i][:, n:] == -1.0)
+
+
 # ------------------------------------------------------------------ Conv2D
 
 CONV_GEOMS = [
@@ -343,17 +366,24 @@ def test_workload5_attention_stages_sampled(am):
     rows, cols = _sample_pairs(5501, Bz * T, 3 * D, 2048)
     R, S = oracle.gemm_at(X, Wqkv, t, M, rows, cols)
     gate(qkv[rows, cols], R, S, what="w5 qkv")
-    # stage 2: scores per head, on synthetic Q/K (batch element 3)
-    qk = normal(5502, (T, 3 * D), std=0.5)
-    S_d = torch.empty((H, T, T), dtype=torch.float32, device="cuda")
+    # stage 2: scores for every (sequence, head) pair in one pointer-array
+    # call, on a synthetic fused QKV buffer
+    qk = normal(5502, (Bz * T, 3 * D), std=0.5)
     q = dev(qk)
-    am.approx_gemm_strided_batched(0, 1, T, T, dh, q, 3 * D, dh, q[:, D:], 3 * D, dh, S_d, T, T * T, H)
+    S_d = torch.empty((Bz, H, T, T), dtype=torch.float32, device="cuda")
+    pairs = [(b, h) for b in range(Bz) for h in range(H)]
+    f = 4
+    qp = am.pointer_array([q.data_ptr() + f * (b * T * 3 * D + h * dh) for b, h in pairs])
+    kp = am.pointer_array([q.data_ptr() + f * (b * T * 3 * D + D + h * dh) for b, h in pairs])
+    sp = am.pointer_array([S_d.data_ptr() + f * (b * H + h) * T * T for b, h in pairs])
+    am.approx_gemm_batched(0, 1, T, T, dh, qp, 3 * D, kp, 3 * D, sp, T, len(pairs))
     Sc = host(S_d)
-    for h in (0, 7, 11):
-        rr, cc = _sample_pairs(5503 + h, T, T, 512)
-        R, S = oracle.gemm_at(qk[:, h * dh:(h + 1) * dh], qk[:, D + h * dh: D + (h + 1) * dh], t, M, rr, cc,
+    for (b, h) in ((0, 0), (3, 7), (15, 11)):
+        rr, cc = _sample_pairs(5503 + 16 * b + h, T, T, 512)
+        rows = qk[b * T:(b + 1) * T]
+        R, S = oracle.gemm_at(rows[:, h * dh:(h + 1) * dh], rows[:, D + h * dh: D + (h + 1) * dh], t, M, rr, cc,
                               transB=True)
-        gate(Sc[h][rr, cc], R, S, what=f"w5 qk h{h}")
+        gate(Sc[b, h][rr, cc], R, S, what=f"w5 qk b{b} h{h}")
     # stage 3: P V per head
     z = normal(5510, (H, T, T))
     P = np.exp(z - z.max(axis=2, keepdims=True))
