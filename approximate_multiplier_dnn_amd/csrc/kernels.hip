@@ -416,24 +416,6 @@ __device__ __forceinline__ void load_lane(const Word* panel, const uint32_t (&ba
     }
 }
 
-// A group is RPL rows x 2 columns of products at one reduction index: the
-// two columns' uniform words come from one broadcast LDS read (issued two
-// groups ahead), then one table lookup per product (issued one group ahead).
-struct Group {
-    uint4 q;                 // (w, se) of column 2jp, (w, se) of column 2jp+1
-    uint32_t e[2 * RPL];     // table entries
-};
-
-__device__ __forceinline__ void group_lookup(const uint32_t (&wa)[RPL], const uint4& q, const unsigned char* lut,
-                                             uint32_t (&e)[2 * RPL])
-{
-#pragma unroll
-    for (int x = 0; x < RPL; ++x) {
-        e[2 * x] = *reinterpret_cast<const uint16_t*>(lut + (wa[x] + q.x));
-        e[2 * x + 1] = *reinterpret_cast<const uint16_t*>(lut + (wa[x] + q.z));
-    }
-}
-
 // Fast path: fma(as_float(seA + (entry << 8)), as_float(seB), acc).
 __device__ __forceinline__ float fast_product_acc(float acc, uint32_t e, uint32_t seA, uint32_t seB)
 {
@@ -460,23 +442,6 @@ __device__ __forceinline__ float checked_product_acc(float acc, uint32_t e, uint
     return acc + __uint_as_float(bits);
 }
 
-template <bool FAST>
-__device__ __forceinline__ void group_compute(const uint32_t (&sa)[RPL], const uint4& q, const uint32_t (&e)[2 * RPL],
-                                              int jp, float (&acc)[RPL][CPW])
-{
-#pragma unroll
-    for (int x = 0; x < RPL; ++x) {
-        if (FAST) {
-            acc[x][2 * jp] = fast_product_acc(acc[x][2 * jp], e[2 * x], sa[x], q.y);
-            acc[x][2 * jp + 1] = fast_product_acc(acc[x][2 * jp + 1], e[2 * x + 1], sa[x], q.w);
-        } else {
-            acc[x][2 * jp] = checked_product_acc(acc[x][2 * jp], e[2 * x], sa[x], q.y);
-            acc[x][2 * jp + 1] = checked_product_acc(acc[x][2 * jp + 1], e[2 * x + 1], sa[x], q.w);
-        }
-    }
-}
-
-constexpr int GROUPS = 4 * (CPW / 2);   // groups per k-step (4 reduction indices)
 constexpr int TILE_GROUP_M = 4;         // row tiles per swizzle group (L2 reuse inside an XCD)
 
 // Uniform words of one reduction index for this wave's 16 columns, loaded
@@ -490,22 +455,126 @@ __device__ __forceinline__ void load_uniform(const Word* row, uint32_t zero, uin
     for (int j = 0; j < CPW / 2; ++j) q[j] = src[j];
 }
 
-template <bool FAST, bool GATHER>
-__device__ __forceinline__ void mainloop(const MainParams& p, const Word* panel, const Word* bsrc,
-                                         const uint32_t (&base)[RPL], int kb0, int kb1, uint32_t zero,
-                                         const unsigned char* lut, float (&acc)[RPL][CPW])
+// Fast path over one reduction index, finer pipeline: a group is the RPL
+// products of one column; the lookups of group g+LA are issued while group g
+// is folded, so LA*RPL lookups per wave are in flight (within the 4-bit LDS
+// wait counter).
+constexpr int LA = 3;
+
+__device__ __forceinline__ void fast_index(const uint32_t (&wa)[RPL], const uint32_t (&sa)[RPL], const uint4 (&q)[CPW / 2],
+                                           const unsigned char* lut, float (&acc)[RPL][CPW])
+{
+    uint32_t e[LA + 1][RPL];
+#define AMX_COLW(j) ((j) & 1 ? q[(j) >> 1].z : q[(j) >> 1].x)
+#define AMX_COLS(j) ((j) & 1 ? q[(j) >> 1].w : q[(j) >> 1].y)
+#pragma unroll
+    for (int g = 0; g < LA; ++g)
+#pragma unroll
+        for (int x = 0; x < RPL; ++x) e[g][x] = *reinterpret_cast<const uint16_t*>(lut + (wa[x] + AMX_COLW(g)));
+#pragma unroll
+    for (int g = 0; g < CPW; ++g) {
+        if (g + LA < CPW) {
+#pragma unroll
+            for (int x = 0; x < RPL; ++x)
+                e[(g + LA) % (LA + 1)][x] = *reinterpret_cast<const uint16_t*>(lut + (wa[x] + AMX_COLW(g + LA)));
+        }
+        const uint32_t sb = AMX_COLS(g);
+#pragma unroll
+        for (int x = 0; x < RPL; ++x) {
+            acc[x][g] = fast_product_acc(acc[x][g], e[g % (LA + 1)][x], sa[x], sb);
+            asm volatile("" : "+v"(acc[x][g]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#undef AMX_COLW
+#undef AMX_COLS
+}
+
+// Checked path over one reduction index: one product at a time (it only runs
+// for operands that can leave the normal range, so it is kept small in
+// registers rather than fast).
+__device__ __forceinline__ void checked_index(const uint32_t (&wa)[RPL], const uint32_t (&sa)[RPL],
+                                              const uint4 (&q)[CPW / 2], const unsigned char* lut,
+                                              float (&acc)[RPL][CPW])
+{
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+        const uint32_t wb = (j & 1) ? q[j >> 1].z : q[j >> 1].x;
+        const uint32_t sb = (j & 1) ? q[j >> 1].w : q[j >> 1].y;
+#pragma unroll
+        for (int x = 0; x < RPL; ++x) {
+            const uint32_t e = *reinterpret_cast<const uint16_t*>(lut + (wa[x] + wb));
+            acc[x][j] = checked_product_acc(acc[x][j], e, sa[x], sb);
+            asm volatile("" : "+v"(acc[x][j]));
+        }
+    }
+}
+
+// Fast k-loop. Operand words of reduction index u are requested two indices
+// before use, into ring slot u % 3; the loop body covers 3 k-steps (12
+// indices) so every slot number is a compile-time constant.
+template <bool GATHER>
+__device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* panel, const Word* bsrc,
+                                              const uint32_t (&base)[RPL], int kb0, int kb1, uint32_t zero,
+                                              const unsigned char* lut, float (&acc)[RPL][CPW])
+{
+    constexpr int HJ = CPW / 2;
+    KCounter kc = kc_init(p, GATHER ? kb0 * 4 : kb0);
+    int ku = kb0 * 4;
+    int off[4], noff[4];
+    step_offsets<GATHER>(p, kc, ku, off);
+    if (kb0 + 1 < kb1) step_offsets<GATHER>(p, kc, ku, noff);
+    uint32_t wa[3][RPL], sa[3][RPL];
+    uint4 qb[3][HJ];
+    load_lane(panel, base, off[0], wa[0], sa[0]);
+    load_uniform(bsrc + (int64_t)kb0 * 4 * p.Np, zero, qb[0]);
+    load_lane(panel, base, off[1], wa[1], sa[1]);
+    load_uniform(bsrc + ((int64_t)kb0 * 4 + 1) * p.Np, zero, qb[1]);
+
+    for (int kb3 = kb0; kb3 < kb1; kb3 += 3) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int kb = kb3 + j;
+            if (kb >= kb1) break;
+            const bool more = kb + 1 < kb1;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int u = 4 * j + t;               // index within the 12-index body
+                const int tl = t + 2;                  // index to request now
+                const int slot_l = (u + 2) % 3;
+                if (tl < 4) {
+                    load_lane(panel, base, off[tl], wa[slot_l], sa[slot_l]);
+                    load_uniform(bsrc + ((int64_t)kb * 4 + tl) * p.Np, zero, qb[slot_l]);
+                } else if (more) {
+                    load_lane(panel, base, noff[tl - 4], wa[slot_l], sa[slot_l]);
+                    load_uniform(bsrc + ((int64_t)(kb + 1) * 4 + tl - 4) * p.Np, zero, qb[slot_l]);
+                }
+                fast_index(wa[u % 3], sa[u % 3], qb[u % 3], lut, acc);
+            }
+            if (more) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) off[t] = noff[t];
+                if (kb + 2 < kb1) step_offsets<GATHER>(p, kc, ku, noff);
+            }
+        }
+    }
+}
+
+// Checked k-loop: operand words one index ahead, parity slots.
+template <bool GATHER>
+__device__ __forceinline__ void mainloop_checked(const MainParams& p, const Word* panel, const Word* bsrc,
+                                                 const uint32_t (&base)[RPL], int kb0, int kb1, uint32_t zero,
+                                                 const unsigned char* lut, float (&acc)[RPL][CPW])
 {
     constexpr int HJ = CPW / 2;
     KCounter kc = kc_init(p, GATHER ? kb0 * 4 : kb0);
     int ku = kb0 * 4;
     int off[4];
     step_offsets<GATHER>(p, kc, ku, off);
-    // operand words of reduction index t are loaded while index t-1 is folded
     uint32_t wa[2][RPL], sa[2][RPL];
     uint4 qb[2][HJ];
     load_lane(panel, base, off[0], wa[0], sa[0]);
     load_uniform(bsrc + (int64_t)kb0 * 4 * p.Np, zero, qb[0]);
-
     for (int kb = kb0; kb < kb1; ++kb) {
         const bool more = kb + 1 < kb1;
         int noff[4];
@@ -520,23 +589,7 @@ __device__ __forceinline__ void mainloop(const MainParams& p, const Word* panel,
                 load_lane(panel, base, noff[0], wa[nxt], sa[nxt]);
                 load_uniform(bsrc + ((int64_t)kb + 1) * 4 * p.Np, zero, qb[nxt]);
             }
-            // software pipeline over the 8 groups of this reduction index: the
-            // lookups of group g+1 are in flight while group g is folded
-            uint32_t e[2][2 * RPL];
-            group_lookup(wa[cur], qb[cur][0], lut, e[0]);
-#pragma unroll
-            for (int g = 0; g < HJ; ++g) {
-                if (g + 1 < HJ) group_lookup(wa[cur], qb[cur][g + 1], lut, e[(g + 1) & 1]);
-                group_compute<FAST>(sa[cur], qb[cur][g], e[g & 1], g, acc);
-                // keep this group's folds here: without the anchor the compiler
-                // sinks them below every later lookup and spills the entries
-#pragma unroll
-                for (int x = 0; x < RPL; ++x) {
-                    asm volatile("" : "+v"(acc[x][2 * g]));
-                    asm volatile("" : "+v"(acc[x][2 * g + 1]));
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            checked_index(wa[cur], sa[cur], qb[cur], lut, acc);
         }
         if (more) {
 #pragma unroll
@@ -621,8 +674,8 @@ __global__ __launch_bounds__(NT, 1) void main_kernel(MainParams p)
             for (int j = 0; j < CPW; ++j) acc[x][j] = 0.0f;
 
         if (kb0 < kb1) {
-            if (fast) mainloop<true, GATHER>(p, panel, bsrc, base, kb0, kb1, zero, lut, acc);
-            else mainloop<false, GATHER>(p, panel, bsrc, base, kb0, kb1, zero, lut, acc);
+            if (fast) mainloop_fast<GATHER>(p, panel, bsrc, base, kb0, kb1, zero, lut, acc);
+            else mainloop_checked<GATHER>(p, panel, bsrc, base, kb0, kb1, zero, lut, acc);
         }
 
         float* out;
