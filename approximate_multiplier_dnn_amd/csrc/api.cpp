@@ -141,7 +141,8 @@ bool force_checked()
 struct Plan {
     DecodeParams lane{}, uni{};
     MainParams mp{};
-    int64_t lane_words = 0, uni_words = 0;    // per batch entry
+    int64_t lane_words = 0, uni_words = 0;    // per batch entry, allocated (rows padded)
+    int64_t lane_count = 0, uni_count = 0;    // per batch entry, logical Words the decode writes
     int batch = 1;
     int gather = 0;
     float* C = nullptr;
@@ -173,14 +174,14 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
 
     pl.lane.dst = lane_panel;
     pl.lane.stats = stats;
-    pl.lane.count = pl.lane_words;
+    pl.lane.count = pl.lane_count ? pl.lane_count : pl.lane_words;
     pl.lane.dst_batch_stride = pl.lane_words;
     pl.lane.batch = pl.batch;
     pl.lane.lane_role = 1;
     pl.lane.M = M;
     pl.uni.dst = uni_panel;
     pl.uni.stats = stats + 2;
-    pl.uni.count = pl.uni_words;
+    pl.uni.count = pl.uni_count ? pl.uni_count : pl.uni_words;
     pl.uni.dst_batch_stride = pl.uni_words;
     pl.uni.batch = pl.batch;
     pl.uni.lane_role = 0;
@@ -297,7 +298,10 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
     a.layout = amx::L_DENSE_LANE;
     a.m = m; a.n = n; a.k = k; a.ld = lda; a.trans = transA;
     a.Mp = Mp; a.Np = Np; a.KB = KB;
-    pl.lane_words = (int64_t)KB * Mp * 4;
+    a.rowlen = Mp * 4;
+    a.ldw = amx::panel_ld(Mp * 4);
+    pl.lane_count = (int64_t)KB * Mp * 4;
+    pl.lane_words = (int64_t)KB * a.ldw;
 
     DecodeParams& u = pl.uni;
     u.src = B;
@@ -306,15 +310,19 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
     u.layout = amx::L_DENSE_UNIFORM;
     u.m = m; u.n = n; u.k = k; u.ld = ldb; u.trans = transB;
     u.Mp = Mp; u.Np = Np; u.KB = KB;
-    pl.uni_words = (int64_t)KB * 4 * Np;
+    u.rowlen = Np;
+    u.ldw = amx::panel_ld(Np);
+    pl.uni_count = (int64_t)KB * 4 * Np;
+    pl.uni_words = (int64_t)KB * 4 * u.ldw;
 
     mp.m_rows = Mp;
     mp.m_out = m;
     mp.n_out = n;
     mp.ldc = ldc;
     mp.Np = Np;
+    mp.bld = u.ldw;
     mp.E2 = 1; mp.E3 = Mp; mp.L1 = 0; mp.L2 = 0; mp.L3 = 4;
-    mp.U1 = KB; mp.U2 = 1; mp.U3 = 1; mp.K1 = Mp * 4; mp.K2 = 0; mp.K3 = 0;
+    mp.U1 = KB; mp.U2 = 1; mp.U3 = 1; mp.K1 = a.ldw; mp.K2 = 0; mp.K3 = 0;
     mp.KB = KB;
     pl.gather = 0;
     return run_plan(pl, dev, stream, image, M);
@@ -383,6 +391,9 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
     mp.ldc = n;
     mp.Np = Np;
     a.Np = u.Np = Np;
+    u.rowlen = Np;
+    u.ldw = amx::panel_ld(Np);
+    mp.bld = u.ldw;
 
     if (kind == CONV_FWD) {
         const int Hp = s.H + 2 * s.ph, Wp = s.W + 2 * s.pw, Cb = (int)cdiv(s.C, 4), Cp = Cb * 4;
@@ -392,7 +403,8 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
         u.layout = amx::L_W_FWD;
         u.Cp = Cp;
         mp.KB = s.R * s.S * Cb;
-        pl.uni_words = (int64_t)mp.KB * 4 * Np;
+        pl.uni_count = (int64_t)mp.KB * 4 * Np;
+        pl.uni_words = (int64_t)mp.KB * 4 * u.ldw;
         const int rowB = Cb * Wp * 4;                 // one padded image row, in Words
         mp.E2 = s.P; mp.E3 = s.Q;
         mp.L1 = Hp * rowB; mp.L2 = s.sh * rowB; mp.L3 = s.sw * 4;
@@ -407,7 +419,8 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
         u.layout = amx::L_W_DGRAD;
         u.Kp = Kp;
         mp.KB = s.R * s.S * Kb;
-        pl.uni_words = (int64_t)mp.KB * 4 * Np;
+        pl.uni_count = (int64_t)mp.KB * 4 * Np;
+        pl.uni_words = (int64_t)mp.KB * 4 * u.ldw;
         const int rowB = Kb * Wd * 4;
         mp.E2 = s.H; mp.E3 = s.W;
         mp.L1 = Hd * rowB; mp.L2 = rowB; mp.L3 = 4;
@@ -426,7 +439,8 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
         mp.KB = (int)cdiv(npq, 4);
         u.Kp = mp.KB * 4;
         u.KB = mp.KB;
-        pl.uni_words = (int64_t)mp.KB * 4 * Np;
+        pl.uni_count = (int64_t)mp.KB * 4 * Np;
+        pl.uni_words = (int64_t)mp.KB * 4 * u.ldw;
         // lane row (r, s, c) of the padded NHWC image, reduction index (n, p, q)
         mp.E2 = s.S; mp.E3 = s.C;
         mp.L1 = Wp * s.C; mp.L2 = s.C; mp.L3 = 1;

@@ -87,7 +87,19 @@ struct DecodeParams {
     FastDiv fd_Mp, fd_Np, fd_Cp, fd_Kp, fd_S, fd_Wp, fd_Cb, fd_Kb, fd_Hp, fd_C;
     int rows;            // image layouts: output rows (N * rows per image)
     int row_floats;      // image layouts: floats in one source row
+    // dense and uniform panels: Words of one logical row (Mp*4 for the lane
+    // panel, Np for uniform panels) and the padded stride between rows
+    int rowlen, ldw;
+    FastDiv fd_rowlen;
 };
+
+// Row stride of a panel. Kept equal to the row length: padding the large
+// power-of-two rows was measured to raise the GEMM kernel's L2 misses on
+// MI355X (8192^3: FETCH_SIZE 10.3 -> 13.5 M KiB per launch).
+inline int panel_ld(int rowlen)
+{
+    return rowlen;
+}
 
 // GEMM kernel parameters. The lane operand of row i and k-step u is read at
 // panel + lane_base(i) + koff(u) (in Words); lane_base decomposes i into
@@ -110,6 +122,7 @@ struct MainParams {
     int m_rows;               // valid rows (lane rows are clamped below this)
     int m_out, n_out, ldc;    // output extent and leading dimension
     int Np;
+    int bld;                  // Words between rows of the uniform panel (>= Np)
     int E2, E3, L1, L2, L3;
     int U1, U2, U3, K1, K2, K3;
     int nku, zoff;            // gather mode

@@ -199,8 +199,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p)
     const uint32_t stride = gridDim.x * 256u;
     for (uint32_t o = blockIdx.x * 256u + threadIdx.x; o < (uint32_t)p.count; o += stride) {
         const int64_t s = decode_source(p, o);
-        dst[o] = s >= 0 ? decode_bits(__float_as_uint(src[s]), p.M, p.lane_role, emin, emax)
-                        : zero_word(p.M, p.lane_role);
+        const uint32_t row = fdiv(o, p.fd_rowlen);
+        dst[(int64_t)row * p.ldw + (o - row * (uint32_t)p.rowlen)] =
+            s >= 0 ? decode_bits(__float_as_uint(src[s]), p.M, p.lane_role, emin, emax) : zero_word(p.M, p.lane_role);
     }
     flush_stats(p.stats, emin, emax);
 }
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(256) void decode_tile_kernel(DecodeParams p)
             const int oi = outer0 + i, ki = k0 + kbl * 4 + t;
             const int kb = (k0 >> 2) + kbl;
             if (kb >= p.KB || oi >= p.Mp) continue;
-            dst[((int64_t)kb * p.Mp + oi) * 4 + t] =
+            dst[(int64_t)kb * p.ldw + (int64_t)oi * 4 + t] =
                 (oi < p.m && ki < p.k) ? decode_bits(__float_as_uint(tile[i][kbl * 4 + t]), p.M, 1, emin, emax)
                                        : zero_word(p.M, 1);
         }
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(256) void decode_tile_kernel(DecodeParams p)
             const int kk = e >> 6, j = e & 63;
             const int oj = outer0 + j, ki = k0 + kk;
             if (ki >= p.KB * 4 || oj >= p.Np) continue;
-            dst[(int64_t)ki * p.Np + oj] =
+            dst[(int64_t)ki * p.ldw + oj] =
                 (oj < p.n && ki < p.k) ? decode_bits(__float_as_uint(tile[j][kk]), p.M, 0, emin, emax)
                                        : zero_word(p.M, 0);
         }
@@ -343,7 +344,7 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeParams p)
     const int rows_out = p.KB * 4;
     for (int kk = blockIdx.y; kk < rows_out; kk += gridDim.y) {
         if (j < p.Np) {
-            dst[(int64_t)kk * p.Np + j] = (kk < p.k && j < p.n)
+            dst[(int64_t)kk * p.ldw + j] = (kk < p.k && j < p.n)
                 ? decode_bits(__float_as_uint(src[(int64_t)kk * p.ld + j]), p.M, p.lane_role, emin, emax)
                 : zero_word(p.M, p.lane_role);
         }
@@ -442,7 +443,12 @@ __device__ __forceinline__ float checked_product_acc(float acc, uint32_t e, uint
     return acc + __uint_as_float(bits);
 }
 
-constexpr int TILE_GROUP_M = 4;         // row tiles per swizzle group (L2 reuse inside an XCD)
+// Row tiles per swizzle group. 1 = plain row-major tile order, so the 32
+// workgroups of one XCD (consecutive work items, see main_kernel) share one
+// row block of the lane panel. Measured on 8192^3 (FETCH_SIZE per launch):
+// 1 -> 10.3 M KiB, 2 -> 21.0 M KiB, 4 -> 48.0 M KiB; kernel time unchanged
+// within 1% because the LDS lookups bind.
+constexpr int TILE_GROUP_M = 1;
 
 // Uniform words of one reduction index for this wave's 16 columns, loaded
 // straight into VGPRs. `zero` is a VGPR that holds 0: adding it keeps the
@@ -527,9 +533,9 @@ __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* p
     uint32_t wa[3][RPL], sa[3][RPL];
     uint4 qb[3][HJ];
     load_lane(panel, base, off[0], wa[0], sa[0]);
-    load_uniform(bsrc + (int64_t)kb0 * 4 * p.Np, zero, qb[0]);
+    load_uniform(bsrc + (int64_t)kb0 * 4 * p.bld, zero, qb[0]);
     load_lane(panel, base, off[1], wa[1], sa[1]);
-    load_uniform(bsrc + ((int64_t)kb0 * 4 + 1) * p.Np, zero, qb[1]);
+    load_uniform(bsrc + ((int64_t)kb0 * 4 + 1) * p.bld, zero, qb[1]);
 
     for (int kb3 = kb0; kb3 < kb1; kb3 += 3) {
 #pragma unroll
@@ -544,10 +550,10 @@ __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* p
                 const int slot_l = (u + 2) % 3;
                 if (tl < 4) {
                     load_lane(panel, base, off[tl], wa[slot_l], sa[slot_l]);
-                    load_uniform(bsrc + ((int64_t)kb * 4 + tl) * p.Np, zero, qb[slot_l]);
+                    load_uniform(bsrc + ((int64_t)kb * 4 + tl) * p.bld, zero, qb[slot_l]);
                 } else if (more) {
                     load_lane(panel, base, noff[tl - 4], wa[slot_l], sa[slot_l]);
-                    load_uniform(bsrc + ((int64_t)(kb + 1) * 4 + tl - 4) * p.Np, zero, qb[slot_l]);
+                    load_uniform(bsrc + ((int64_t)(kb + 1) * 4 + tl - 4) * p.bld, zero, qb[slot_l]);
                 }
                 fast_index(wa[u % 3], sa[u % 3], qb[u % 3], lut, acc);
             }
@@ -574,7 +580,7 @@ __device__ __forceinline__ void mainloop_checked(const MainParams& p, const Word
     uint32_t wa[2][RPL], sa[2][RPL];
     uint4 qb[2][HJ];
     load_lane(panel, base, off[0], wa[0], sa[0]);
-    load_uniform(bsrc + (int64_t)kb0 * 4 * p.Np, zero, qb[0]);
+    load_uniform(bsrc + (int64_t)kb0 * 4 * p.bld, zero, qb[0]);
     for (int kb = kb0; kb < kb1; ++kb) {
         const bool more = kb + 1 < kb1;
         int noff[4];
@@ -584,10 +590,10 @@ __device__ __forceinline__ void mainloop_checked(const MainParams& p, const Word
             const int cur = t & 1, nxt = cur ^ 1;
             if (t < 3) {
                 load_lane(panel, base, off[t + 1], wa[nxt], sa[nxt]);
-                load_uniform(bsrc + ((int64_t)kb * 4 + t + 1) * p.Np, zero, qb[nxt]);
+                load_uniform(bsrc + ((int64_t)kb * 4 + t + 1) * p.bld, zero, qb[nxt]);
             } else if (more) {
                 load_lane(panel, base, noff[0], wa[nxt], sa[nxt]);
-                load_uniform(bsrc + ((int64_t)kb + 1) * 4 * p.Np, zero, qb[nxt]);
+                load_uniform(bsrc + ((int64_t)kb + 1) * 4 * p.bld, zero, qb[nxt]);
             }
             checked_index(wa[cur], sa[cur], qb[cur], lut, acc);
         }
@@ -631,10 +637,9 @@ __global__ __launch_bounds__(NT, 1) void main_kernel(MainParams p)
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wrow = wave / p.wc, wcol = wave - wrow * p.wc;
     const int G = gridDim.x;
-    // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, so give
-    // the workgroups of one XCD consecutive work items; consecutive items form
-    // TILE_GROUP_M x (n) blocks of output tiles, so they share rows and columns
-    // of the operands in that XCD's L2.
+    // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin (block
+    // b runs on XCD b % 8, checked with HW_REG_XCC_ID), so give the workgroups
+    // of one XCD consecutive work items: they share operand rows in its L2.
     const int v = (G & 7) == 0 ? (int)((blockIdx.x & 7u) * (unsigned)(G >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
     const int TM = p.wr * 64 * RPL, TN = p.wc * CPW;
     const int items = (int)p.items;
@@ -750,6 +755,11 @@ hipError_t launch_decode(const DecodeParams& p0, hipStream_t s)
     auto fd = [](int v) { return make_fastdiv((uint32_t)(v > 0 ? v : 1)); };
     p.fd_Mp = fd(p.Mp); p.fd_Np = fd(p.Np); p.fd_Cp = fd(p.Cp); p.fd_Kp = fd(p.Kp); p.fd_S = fd(p.S);
     p.fd_Wp = fd(p.Wp); p.fd_Cb = fd(p.Cb); p.fd_Kb = fd(p.Kb); p.fd_Hp = fd(p.Hp); p.fd_C = fd(p.C);
+    if (p.rowlen <= 0) {                           // unpadded: one row of `count` Words
+        p.rowlen = (int)p.count;
+        p.ldw = (int)p.count;
+    }
+    p.fd_rowlen = fd(p.rowlen);
     const bool img = p.layout == L_IMG_FWD || p.layout == L_IMG_DGRAD || p.layout == L_IMG_WGRAD;
     if (img) {
         p.row_floats = p.layout == L_IMG_DGRAD ? p.Q * p.K : p.W * p.C;

@@ -156,7 +156,7 @@ def cpu_baseline(config, host):
 
     t0 = time.perf_counter()
     if config in (1, 4):
-        rows = 64 if config == 1 else 4
+        rows = 64 if config == 1 else 32
         A, B = host["A"], host["B"]
         oracle.gemm(np.ascontiguousarray(A[:rows]), B, host["lut"], host["M"])
         macs = rows * B.shape[0] * B.shape[1]
