@@ -196,6 +196,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=4, help="workload 1-5 (4: 8192^3 GEMM, the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="instead of the workload, run the LDS table-lookup rate probe")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the workload, run one plain device copy of this many bytes "
                          "(calibrates the HBM byte counters used for roofline.traffic)")
@@ -206,6 +208,11 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "the approximate GEMM is not sharded across GPUs in this build", file=sys.stderr)
         sys.exit(2)
+
+    if args.lds_probe:
+        import subprocess
+        probe = os.path.join(ROOT, "approximate_multiplier_dnn_amd", "lds_probe")
+        sys.exit(subprocess.run([probe]).returncode)
 
     import torch
 
