@@ -28,7 +28,7 @@ MODEL_MITCHELL = 1
 
 #: every function the C header declares
 EXPORTS = (
-    "approx_lut_build", "approx_lut_build_from_model", "approx_lut_load", "approx_lut_bits",
+    "approx_lut_build", "approx_lut_build_from_model", "approx_lut_load", "approx_native_load", "approx_lut_bits",
     "approx_gemm", "approx_gemm_strided_batched", "approx_gemm_batched",
     "approx_conv2d_fwd", "approx_conv2d_dgrad", "approx_conv2d_wgrad",
     "approx_profile_enable", "approx_profile_read",
@@ -110,6 +110,11 @@ def approx_lut_load(lut, M):
     if t.size != (1 << (2 * M)):
         raise ValueError("table must have 4**M entries")
     _check(_lib.approx_lut_load(t.ctypes.data, int(M)), "approx_lut_load")
+
+
+def approx_native_load():
+    """Select the native FP32 multiplier (fused multiply-add) on the current device."""
+    _check(_lib.approx_native_load(), "approx_native_load")
 
 
 def approx_lut_bits():

@@ -31,6 +31,7 @@ constexpr int64_t kMaxPanelWords = (int64_t)1 << 31;
 struct DeviceTable {
     uint16_t* image = nullptr;  // lane-first LDS image
     int M = 0;
+    bool native = false;        // the native FP32 multiplier is selected (no image)
 };
 
 struct Arena {
@@ -80,7 +81,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Resident GEMM workgroups per device (CUs x blocks per CU), per kernel
 // variant; queried once per device and kept.
-int64_t g_slots[kMaxDevices][2][2];
+int64_t g_slots[kMaxDevices][3][2];
 
 int64_t launch_slots(int dev, int lds_class, int gather)
 {
@@ -97,6 +98,11 @@ int64_t launch_slots(int dev, int lds_class, int gather)
 int table_of(int dev, const uint16_t** image, int* M)
 {
     std::lock_guard<std::mutex> lock(g_mu);
+    if (g_tables[dev].native) {
+        *image = nullptr;
+        *M = 0;
+        return APPROX_OK;
+    }
     if (g_tables[dev].image == nullptr) return APPROX_ENOLUT;
     *image = g_tables[dev].image;
     *M = g_tables[dev].M;
@@ -155,7 +161,7 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     MainParams& mp = pl.mp;
     if (pl.lane_words * pl.batch >= kMaxPanelWords || pl.uni_words * pl.batch >= kMaxPanelWords)
         return APPROX_EUNSUPPORTED;
-    const int lds_class = M <= 7 ? 0 : 1;
+    const int lds_class = M == 0 ? 2 : M <= 7 ? 0 : 1;   // M = 0: native multiplier
     const int64_t tiles = (int64_t)mp.tiles_m * mp.tiles_n * pl.batch;
     pick_split(tiles, mp.KB, &mp.splits, &mp.chunk);
     mp.items = tiles * mp.splits;
@@ -190,7 +196,7 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     mp.panel = lane_panel;
     mp.bpanel = uni_panel;
     mp.lut = image;
-    mp.lut_bytes = amx::lut_image_bytes(M);
+    mp.lut_bytes = M ? amx::lut_image_bytes(M) : 0;
     mp.stats = stats;
     mp.panel_batch = pl.lane_words;
     mp.bpanel_batch = pl.uni_words;
@@ -482,6 +488,22 @@ extern "C" int approx_lut_load(const uint16_t* lut, int M)
     }
     g_tables[dev].image = d;
     g_tables[dev].M = M;
+    g_tables[dev].native = false;
+    return APPROX_OK;
+}
+
+extern "C" int approx_native_load(void)
+{
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc != APPROX_OK) return rc;
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (g_tables[dev].image != nullptr) {
+        if (hipDeviceSynchronize() != hipSuccess) return APPROX_EHIP;
+        (void)hipFree(g_tables[dev].image);
+    }
+    g_tables[dev] = DeviceTable{};
+    g_tables[dev].native = true;
     return APPROX_OK;
 }
 
@@ -491,6 +513,7 @@ extern "C" int approx_lut_bits(void)
     int rc = current_device(&dev);
     if (rc != APPROX_OK) return rc;
     std::lock_guard<std::mutex> lock(g_mu);
+    if (g_tables[dev].native) return 0;
     return g_tables[dev].image ? g_tables[dev].M : APPROX_ENOLUT;
 }
 
@@ -594,6 +617,7 @@ extern "C" int approx_release(void)
     }
     g_arenas.clear();
     for (int d = 0; d < kMaxDevices; ++d) {
+        g_tables[d].native = false;
         if (g_tables[d].image == nullptr) continue;
         if (hipSetDevice(d) != hipSuccess || hipDeviceSynchronize() != hipSuccess) rc = APPROX_EHIP;
         if (hipFree(g_tables[d].image) != hipSuccess) rc = APPROX_EHIP;

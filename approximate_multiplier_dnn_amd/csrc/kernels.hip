@@ -37,8 +37,11 @@ constexpr int CPW = 16;   // output columns per wave
 
 // ------------------------------------------------------------------ decode
 
+// M = 0 selects the native multiplier: the Word carries the operand's own
+// bits (se) and no table offset, and the exponent range is not gathered.
 __device__ __forceinline__ Word decode_bits(uint32_t bits, int M, int lane_role, int& emin, int& emax)
 {
+    if (M == 0) return Word{0u, bits};
     const uint32_t e = (bits >> 23) & 0xFFu;
     const uint32_t frac = bits & 0x7FFFFFu;
     const uint32_t idx = frac >> (23 - M);
@@ -69,7 +72,7 @@ __device__ __forceinline__ Word zero_word(int M, int lane_role)
 {
     Word w;
     w.se = 0u;
-    w.w = lane_role ? (1u << M) * 2u : 0u;
+    w.w = (lane_role && M) ? (1u << M) * 2u : 0u;
     return w;
 }
 
@@ -417,12 +420,6 @@ __device__ __forceinline__ void load_lane(const Word* panel, const uint32_t (&ba
     }
 }
 
-// Fast path: fma(as_float(seA + (entry << 8)), as_float(seB), acc).
-__device__ __forceinline__ float fast_product_acc(float acc, uint32_t e, uint32_t seA, uint32_t seB)
-{
-    return __builtin_fmaf(__uint_as_float((e << 8) + seA), __uint_as_float(seB), acc);
-}
-
 // Checked path: Algorithm 2 with every special case, as selects (no
 // divergence), then acc + product.
 __device__ __forceinline__ float checked_product_acc(float acc, uint32_t e, uint32_t seA, uint32_t seB)
@@ -450,15 +447,58 @@ __device__ __forceinline__ float checked_product_acc(float acc, uint32_t e, uint
 // within 1% because the LDS lookups bind.
 constexpr int TILE_GROUP_M = 1;
 
-// Uniform words of one reduction index for this wave's 16 columns, loaded
-// straight into VGPRs. `zero` is a VGPR that holds 0: adding it keeps the
-// uniform address in vector registers, so the loads stay on the vector
-// memory path and never share the LDS wait counter with scalar loads.
-__device__ __forceinline__ void load_uniform(const Word* row, uint32_t zero, uint4 (&q)[CPW / 2])
+// Uniform words of one reduction index for this wave's 16 columns, spread
+// over the 4 lanes of each quad: lane i of a quad holds, in register
+// 4j + t, dword 16j + 4i + t of the 32 dwords {w0, se0, w1, se1, ...}.
+// 8 VGPRs per index instead of 32 (a quarter of the vector-memory return
+// traffic of a full broadcast); a consumer reads column c's value with a
+// quad_perm DPP broadcast of lane (c >> 1) & 3, folded into its own
+// instruction (v_add_u32_dpp, v_fmac_f32_dpp).
+constexpr int UQ = 8;
+
+__device__ __forceinline__ void load_uniform(const Word* row, uint32_t quad, uint32_t (&q)[UQ])
 {
-    const uint4* src = reinterpret_cast<const uint4*>(row) + zero;
-#pragma unroll
-    for (int j = 0; j < CPW / 2; ++j) q[j] = src[j];
+    const uint4* src = reinterpret_cast<const uint4*>(row) + quad;
+    const uint4 a = src[0], b = src[4];
+    q[0] = a.x; q[1] = a.y; q[2] = a.z; q[3] = a.w;
+    q[4] = b.x; q[5] = b.y; q[6] = b.z; q[7] = b.w;
+}
+
+// Lane i of every quad, broadcast to the quad (quad_perm:[i,i,i,i]). i is a
+// constant once the callers' loops are unrolled.
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v, int i)
+{
+    switch (i) {
+    case 0: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xF, 0xF, true);
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xF, 0xF, true);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xAA, 0xF, 0xF, true);
+    default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xFF, 0xF, 0xF, true);
+    }
+}
+
+// acc += (lane i of this lane's quad in q) * x, one v_fmac_f32 with a DPP
+// broadcast operand (the compiler does not fold a DPP move into an FMA on
+// this target). The asm statement also keeps each fold in place in the
+// schedule. q comes straight from vector-memory loads, so no VALU write
+// precedes its DPP read.
+__device__ __forceinline__ void fmac_quad(float& acc, uint32_t q, float x, int i)
+{
+#define AMX_FMAC_DPP(I)                                                                                  \
+    asm volatile("v_fmac_f32_dpp %0, %1, %2 quad_perm:[" #I "," #I "," #I "," #I "] row_mask:0xf bank_mask:0xf" \
+                 : "+v"(acc) : "v"(q), "v"(x))
+    switch (i) {
+    case 0: AMX_FMAC_DPP(0); break;
+    case 1: AMX_FMAC_DPP(1); break;
+    case 2: AMX_FMAC_DPP(2); break;
+    default: AMX_FMAC_DPP(3); break;
+    }
+#undef AMX_FMAC_DPP
+}
+
+// Column c's w (h = 0) or se (h = 1), in every lane.
+__device__ __forceinline__ uint32_t col_word(const uint32_t (&q)[UQ], int c, int h)
+{
+    return quad_bcast(q[4 * (c >> 3) + 2 * (c & 1) + h], (c >> 1) & 3);
 }
 
 // Fast path over one reduction index, finer pipeline: a group is the RPL
@@ -467,12 +507,11 @@ __device__ __forceinline__ void load_uniform(const Word* row, uint32_t zero, uin
 // wait counter).
 constexpr int LA = 3;
 
-__device__ __forceinline__ void fast_index(const uint32_t (&wa)[RPL], const uint32_t (&sa)[RPL], const uint4 (&q)[CPW / 2],
+__device__ __forceinline__ void fast_index(const uint32_t (&wa)[RPL], const uint32_t (&sa)[RPL], const uint32_t (&q)[UQ],
                                            const unsigned char* lut, float (&acc)[RPL][CPW])
 {
     uint32_t e[LA + 1][RPL];
-#define AMX_COLW(j) ((j) & 1 ? q[(j) >> 1].z : q[(j) >> 1].x)
-#define AMX_COLS(j) ((j) & 1 ? q[(j) >> 1].w : q[(j) >> 1].y)
+#define AMX_COLW(j) col_word(q, (j), 0)
 #pragma unroll
     for (int g = 0; g < LA; ++g)
 #pragma unroll
@@ -484,29 +523,40 @@ __device__ __forceinline__ void fast_index(const uint32_t (&wa)[RPL], const uint
             for (int x = 0; x < RPL; ++x)
                 e[(g + LA) % (LA + 1)][x] = *reinterpret_cast<const uint16_t*>(lut + (wa[x] + AMX_COLW(g + LA)));
         }
-        const uint32_t sb = AMX_COLS(g);
+        // acc += as_float(seA + (entry << 8)) * as_float(seB): the fast-path product
 #pragma unroll
-        for (int x = 0; x < RPL; ++x) {
-            acc[x][g] = fast_product_acc(acc[x][g], e[g % (LA + 1)][x], sa[x], sb);
-            asm volatile("" : "+v"(acc[x][g]));
-        }
+        for (int x = 0; x < RPL; ++x)
+            fmac_quad(acc[x][g], q[4 * (g >> 3) + 2 * (g & 1) + 1], __uint_as_float((e[g % (LA + 1)][x] << 8) + sa[x]),
+                      (g >> 1) & 3);
         __builtin_amdgcn_sched_barrier(0);
     }
 #undef AMX_COLW
-#undef AMX_COLS
+}
+
+// Native multiplier over one reduction index: the IEEE single-precision
+// product folded by the hardware FMA, acc = fma(a, b, acc) (the product is
+// exact inside the FMA; one rounding per step). No table lookup: this is the
+// reference point the approximate product is compared against.
+__device__ __forceinline__ void native_index(const uint32_t (&sa)[RPL], const uint32_t (&q)[UQ],
+                                             float (&acc)[RPL][CPW])
+{
+#pragma unroll
+    for (int g = 0; g < CPW; ++g)
+#pragma unroll
+        for (int x = 0; x < RPL; ++x) fmac_quad(acc[x][g], q[4 * (g >> 3) + 2 * (g & 1) + 1], __uint_as_float(sa[x]), (g >> 1) & 3);
 }
 
 // Checked path over one reduction index: one product at a time (it only runs
 // for operands that can leave the normal range, so it is kept small in
 // registers rather than fast).
 __device__ __forceinline__ void checked_index(const uint32_t (&wa)[RPL], const uint32_t (&sa)[RPL],
-                                              const uint4 (&q)[CPW / 2], const unsigned char* lut,
+                                              const uint32_t (&q)[UQ], const unsigned char* lut,
                                               float (&acc)[RPL][CPW])
 {
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
-        const uint32_t wb = (j & 1) ? q[j >> 1].z : q[j >> 1].x;
-        const uint32_t sb = (j & 1) ? q[j >> 1].w : q[j >> 1].y;
+        const uint32_t wb = col_word(q, j, 0);
+        const uint32_t sb = col_word(q, j, 1);
 #pragma unroll
         for (int x = 0; x < RPL; ++x) {
             const uint32_t e = *reinterpret_cast<const uint16_t*>(lut + (wa[x] + wb));
@@ -516,71 +566,126 @@ __device__ __forceinline__ void checked_index(const uint32_t (&wa)[RPL], const u
     }
 }
 
-// Fast k-loop. Operand words of reduction index u are requested two indices
-// before use, into ring slot u % 3; the loop body covers 3 k-steps (12
-// indices) so every slot number is a compile-time constant.
-template <bool GATHER>
+// Fast k-loop over k-steps [kb0, kb1). The operand words of reduction index u
+// are requested PD = R - 1 indices before use, into ring slot u % R; a loop
+// body covers R indices, so every slot number is a compile-time constant.
+// Vector mode: a k-step is 4 contiguous Words at offset so[q] + t, and the
+// offsets of the NS k-steps a body touches are kept in so[]. Gather mode:
+// every index has its own offset from the counter (the zero region past the
+// last index). The steady-state body has no branch: the compiler's wait
+// counts for the ring stay exact, so the prefetch is never drained early.
+template <bool GATHER, bool NATIVE, int R>
 __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* panel, const Word* bsrc,
-                                              const uint32_t (&base)[RPL], int kb0, int kb1, uint32_t zero,
+                                              const uint32_t (&base)[RPL], int kb0, int kb1, uint32_t quad,
                                               const unsigned char* lut, float (&acc)[RPL][CPW])
 {
-    constexpr int HJ = CPW / 2;
+    constexpr int PD = R - 1;
+    constexpr int NS = R / 2;
+    constexpr int SB = R / 4;                      // k-steps per loop body
+    const int n = (kb1 - kb0) * 4;
     KCounter kc = kc_init(p, GATHER ? kb0 * 4 : kb0);
     int ku = kb0 * 4;
-    int off[4], noff[4];
-    step_offsets<GATHER>(p, kc, ku, off);
-    if (kb0 + 1 < kb1) step_offsets<GATHER>(p, kc, ku, noff);
-    uint32_t wa[3][RPL], sa[3][RPL];
-    uint4 qb[3][HJ];
-    load_lane(panel, base, off[0], wa[0], sa[0]);
-    load_uniform(bsrc + (int64_t)kb0 * 4 * p.bld, zero, qb[0]);
-    load_lane(panel, base, off[1], wa[1], sa[1]);
-    load_uniform(bsrc + ((int64_t)kb0 * 4 + 1) * p.bld, zero, qb[1]);
-
-    for (int kb3 = kb0; kb3 < kb1; kb3 += 3) {
+    int so[NS];
+    if (!GATHER) {
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            const int kb = kb3 + j;
-            if (kb >= kb1) break;
-            const bool more = kb + 1 < kb1;
+        for (int q = 0; q < NS; ++q) {
+            so[q] = kc.off;
+            kc_next(p, kc);
+        }
+    }
+    auto lane_off = [&](int v) -> int {          // offset of the v-th index a body loads
+        if (!GATHER) return so[v >> 2] + (v & 3);
+        const int off = ku < p.nku ? kc.off : p.zoff;
+        ++ku;
+        kc_next(p, kc);
+        return off;
+    };
+    auto advance = [&]() {                       // the body moved SB k-steps on
+        if (!GATHER) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int u = 4 * j + t;               // index within the 12-index body
-                const int tl = t + 2;                  // index to request now
-                const int slot_l = (u + 2) % 3;
-                if (tl < 4) {
-                    load_lane(panel, base, off[tl], wa[slot_l], sa[slot_l]);
-                    load_uniform(bsrc + ((int64_t)kb * 4 + tl) * p.bld, zero, qb[slot_l]);
-                } else if (more) {
-                    load_lane(panel, base, noff[tl - 4], wa[slot_l], sa[slot_l]);
-                    load_uniform(bsrc + ((int64_t)(kb + 1) * 4 + tl - 4) * p.bld, zero, qb[slot_l]);
+            for (int q = 0; q < NS; ++q) {
+                if (q + SB < NS) {
+                    so[q] = so[q + SB];
+                } else {
+                    so[q] = kc.off;
+                    kc_next(p, kc);
                 }
-                fast_index(wa[u % 3], sa[u % 3], qb[u % 3], lut, acc);
-            }
-            if (more) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) off[t] = noff[t];
-                if (kb + 2 < kb1) step_offsets<GATHER>(p, kc, ku, noff);
             }
         }
+    };
+    const Word* urow = bsrc + (int64_t)kb0 * 4 * p.bld;
+    uint32_t wa[R][RPL], sa[R][RPL], qb[R][UQ];
+    int u0 = 0;
+    if (n >= R + PD) {
+        // unconditional prologue: the loop is entered with the same loads in
+        // flight as at its back edge
+#pragma unroll
+        for (int v = 0; v < PD; ++v) {
+            load_lane(panel, base, lane_off(v), wa[v], sa[v]);
+            load_uniform(urow, quad, qb[v]);
+            urow += p.bld;
+            asm volatile("" ::: "memory");       // one load group per index, as in the loop
+        }
+        // The compiler drains the loads in flight at the loop head; folding
+        // index u0 before requesting index u0 + PD means that drain only
+        // waits for loads that were issued at least one index earlier.
+        for (; u0 + R + PD <= n; u0 += R) {
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                if (j == 0) {
+                    if constexpr (NATIVE) native_index(sa[0], qb[0], acc);
+                    else fast_index(wa[0], sa[0], qb[0], lut, acc);
+                }
+                load_lane(panel, base, lane_off(j + PD), wa[(j + PD) % R], sa[(j + PD) % R]);
+                load_uniform(urow, quad, qb[(j + PD) % R]);
+                urow += p.bld;
+                if (j > 0) {
+                    if constexpr (NATIVE) native_index(sa[j], qb[j], acc);
+                    else fast_index(wa[j], sa[j], qb[j], lut, acc);
+                }
+            }
+            advance();
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < PD; ++v) {
+            if (v < n) {
+                load_lane(panel, base, lane_off(v), wa[v], sa[v]);
+                load_uniform(urow, quad, qb[v]);
+                urow += p.bld;
+            }
+        }
+    }
+    for (; u0 < n; u0 += R) {                    // tail: fewer than R + PD indices left
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            if (u0 + j >= n) break;
+            if (u0 + j + PD < n) {
+                load_lane(panel, base, lane_off(j + PD), wa[(j + PD) % R], sa[(j + PD) % R]);
+                load_uniform(urow, quad, qb[(j + PD) % R]);
+                urow += p.bld;
+            }
+            if constexpr (NATIVE) native_index(sa[j], qb[j], acc);
+            else fast_index(wa[j], sa[j], qb[j], lut, acc);
+        }
+        advance();
     }
 }
 
 // Checked k-loop: operand words one index ahead, parity slots.
 template <bool GATHER>
 __device__ __forceinline__ void mainloop_checked(const MainParams& p, const Word* panel, const Word* bsrc,
-                                                 const uint32_t (&base)[RPL], int kb0, int kb1, uint32_t zero,
+                                                 const uint32_t (&base)[RPL], int kb0, int kb1, uint32_t quad,
                                                  const unsigned char* lut, float (&acc)[RPL][CPW])
 {
-    constexpr int HJ = CPW / 2;
     KCounter kc = kc_init(p, GATHER ? kb0 * 4 : kb0);
     int ku = kb0 * 4;
     int off[4];
     step_offsets<GATHER>(p, kc, ku, off);
     uint32_t wa[2][RPL], sa[2][RPL];
-    uint4 qb[2][HJ];
+    uint32_t qb[2][UQ];
     load_lane(panel, base, off[0], wa[0], sa[0]);
-    load_uniform(bsrc + (int64_t)kb0 * 4 * p.bld, zero, qb[0]);
+    load_uniform(bsrc + (int64_t)kb0 * 4 * p.bld, quad, qb[0]);
     for (int kb = kb0; kb < kb1; ++kb) {
         const bool more = kb + 1 < kb1;
         int noff[4];
@@ -590,10 +695,10 @@ __device__ __forceinline__ void mainloop_checked(const MainParams& p, const Word
             const int cur = t & 1, nxt = cur ^ 1;
             if (t < 3) {
                 load_lane(panel, base, off[t + 1], wa[nxt], sa[nxt]);
-                load_uniform(bsrc + ((int64_t)kb * 4 + t + 1) * p.bld, zero, qb[nxt]);
+                load_uniform(bsrc + ((int64_t)kb * 4 + t + 1) * p.bld, quad, qb[nxt]);
             } else if (more) {
                 load_lane(panel, base, noff[0], wa[nxt], sa[nxt]);
-                load_uniform(bsrc + ((int64_t)kb + 1) * 4 * p.bld, zero, qb[nxt]);
+                load_uniform(bsrc + ((int64_t)kb + 1) * 4 * p.bld, quad, qb[nxt]);
             }
             checked_index(wa[cur], sa[cur], qb[cur], lut, acc);
         }
@@ -604,11 +709,15 @@ __device__ __forceinline__ void mainloop_checked(const MainParams& p, const Word
     }
 }
 
-template <int LDSB, bool GATHER>
+// LDSB: bytes of the LDS table image (LDS_SMALL or LDS_LARGE), or NATIVE_LDS
+// with NATIVE = true, where no table is staged.
+constexpr int NATIVE_LDS = 16;
+
+template <int LDSB, bool GATHER, bool NATIVE>
 __global__ __launch_bounds__(NT, 1) void main_kernel(MainParams p)
 {
     __shared__ __align__(16) unsigned char lut[LDSB];
-    {
+    if (!NATIVE) {
         const uint4* src = reinterpret_cast<const uint4*>(p.lut);
         uint4* dst = reinterpret_cast<uint4*>(lut);
         const int n16 = p.lut_bytes >> 4;
@@ -628,13 +737,11 @@ __global__ __launch_bounds__(NT, 1) void main_kernel(MainParams p)
     }
     __syncthreads();
     const int a_min = range[0], a_max = range[1], b_min = range[2], b_max = range[3];
-    const bool fast = !p.force_checked &&
+    const bool fast = NATIVE || (!p.force_checked &&
                       ((a_min > a_max) || (b_min > b_max) ||
-                       (a_min + b_min - 127 >= 1 && a_max + b_max - 126 <= 254 && a_max <= 253));
-    uint32_t zero;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-
+                       (a_min + b_min - 127 >= 1 && a_max + b_max - 126 <= 254 && a_max <= 253)));
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint32_t quad = (uint32_t)lane & 3u;     // this lane's place in the uniform-word quads
     const int wrow = wave / p.wc, wcol = wave - wrow * p.wc;
     const int G = gridDim.x;
     // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin (block
@@ -679,8 +786,8 @@ __global__ __launch_bounds__(NT, 1) void main_kernel(MainParams p)
             for (int j = 0; j < CPW; ++j) acc[x][j] = 0.0f;
 
         if (kb0 < kb1) {
-            if (fast) mainloop_fast<GATHER>(p, panel, bsrc, base, kb0, kb1, zero, lut, acc);
-            else mainloop_checked<GATHER>(p, panel, bsrc, base, kb0, kb1, zero, lut, acc);
+            if (fast) mainloop_fast<GATHER, NATIVE, NATIVE ? 8 : 4>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
+            else if (!NATIVE) mainloop_checked<GATHER>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
         }
 
         float* out;
@@ -797,28 +904,28 @@ hipError_t launch_decode(const DecodeParams& p0, hipStream_t s)
     return hipGetLastError();
 }
 
+// The GEMM kernel variant of (lds_class, gather): lds_class 0 = table of
+// M <= 7, 1 = M == 8, 2 = native multiplier (no table).
+static const void* main_variant(int lds_class, int gather)
+{
+    if (lds_class == 0)
+        return gather ? (const void*)main_kernel<LDS_SMALL, true, false> : (const void*)main_kernel<LDS_SMALL, false, false>;
+    if (lds_class == 1)
+        return gather ? (const void*)main_kernel<LDS_LARGE, true, false> : (const void*)main_kernel<LDS_LARGE, false, false>;
+    return gather ? (const void*)main_kernel<NATIVE_LDS, true, true> : (const void*)main_kernel<NATIVE_LDS, false, true>;
+}
+
 hipError_t launch_main(const MainParams& p, int lds_class, int gather, int grid, hipStream_t s)
 {
-    if (lds_class == 0) {
-        if (gather) hipLaunchKernelGGL((main_kernel<LDS_SMALL, true>), dim3(grid), dim3(NT), 0, s, p);
-        else hipLaunchKernelGGL((main_kernel<LDS_SMALL, false>), dim3(grid), dim3(NT), 0, s, p);
-    } else {
-        if (gather) hipLaunchKernelGGL((main_kernel<LDS_LARGE, true>), dim3(grid), dim3(NT), 0, s, p);
-        else hipLaunchKernelGGL((main_kernel<LDS_LARGE, false>), dim3(grid), dim3(NT), 0, s, p);
-    }
-    return hipGetLastError();
+    MainParams arg = p;
+    void* args[] = {&arg};
+    return hipLaunchKernel(main_variant(lds_class, gather), dim3(grid), dim3(NT), args, 0, s);
 }
 
 int main_blocks_per_cu(int lds_class, int gather)
 {
     int n = 0;
-    hipError_t e;
-    if (lds_class == 0)
-        e = gather ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, main_kernel<LDS_SMALL, true>, NT, 0)
-                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, main_kernel<LDS_SMALL, false>, NT, 0);
-    else
-        e = gather ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, main_kernel<LDS_LARGE, true>, NT, 0)
-                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, main_kernel<LDS_LARGE, false>, NT, 0);
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, main_variant(lds_class, gather), NT, 0);
     if (e != hipSuccess || n < 1) n = 1;
     return n;
 }

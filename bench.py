@@ -11,6 +11,12 @@ Prints ONE JSON line: the metric (G approximate MAC/s), the GEMM kernel's
 roofline record (timed with HIP events inside the library, on the stream the
 kernel runs on) and the oracle's single-thread CPU throughput on a bounded
 sample of the same workload.
+
+--multiplier native runs the same workload with the library's native
+multiplier (the FP32 fused multiply-add in place of the table: ApproxTrain
+Section V / Fig. 6 compare the simulated multiplier against the native one);
+--multiplier library times torch.matmul in FP32 on the GEMM workloads, for
+context. Neither is the headline.
 """
 import argparse
 import hashlib
@@ -27,6 +33,14 @@ CUS, LANES_PER_CU, CLOCK_HZ = 256, 64, 2.4e9
 VALU_PEAK_TOPS = CUS * LANES_PER_CU * CLOCK_HZ / 1e12     # 39.32 T 32-bit lane-ops/s
 OPS_PER_MAC = 3                                           # address, assemble, accumulate
 HBM_PEAK_GBS = 8000.0
+# LDS: 128 bytes per clock per CU, i.e. 32 four-byte lanes: one 16-bit table
+# lookup per lane
+LDS_PEAK_LOOKUPS = CUS * 32 * CLOCK_HZ / 1e12             # 19.66 T lookups/s
+# lookups/s that random rows of one table column sustain, measured by the
+# LDS probe (python3 bench.py --lds-probe): bank conflicts between the 2 (M=7)
+# or 4 (M=8) bank rows a column spans
+LDS_RANDOM_COLUMN_CEILING = {7: 9.42, 8: 6.95}
+FP32_MFMA_PEAK_TFLOPS = 157.3
 
 
 def log(*a):
@@ -52,12 +66,18 @@ def traffic_record(workload):
     return rec.get("bytes_per_launch")
 
 
-def build_workload(config, am, torch):
+def build_workload(config, am, torch, mult="table"):
     from datagen import configs as cfg
 
     model, M, pert = cfg.lut_spec(config)
-    lut = am.approx_lut_build(am.MODEL_EXACT if model == "exact" else am.MODEL_MITCHELL, M, pert)
-    am.approx_lut_load(lut, M)
+    if mult == "table":
+        lut = am.approx_lut_build(am.MODEL_EXACT if model == "exact" else am.MODEL_MITCHELL, M, pert)
+        am.approx_lut_load(lut, M)
+    else:
+        am.approx_native_load()
+        lut, M = None, 0
+    if mult == "library" and config not in (1, 4):
+        raise SystemExit("--multiplier library covers the square GEMM workloads (1 and 4) only")
     d = lambda a: torch.from_numpy(a).cuda()
     info = {}
     if config in (1, 4):
@@ -67,9 +87,14 @@ def build_workload(config, am, torch):
         Cd = torch.empty((size, size), dtype=torch.float32, device="cuda")
 
         def step():
-            am.approx_gemm(0, 0, size, size, size, Ad, size, Bd, size, Cd, size)
+            if mult == "library":
+                torch.matmul(Ad, Bd, out=Cd)
+            else:
+                am.approx_gemm(0, 0, size, size, size, Ad, size, Bd, size, Cd, size)
 
         workload = f"gemm_{size}x{size}x{size}_lut_m{M}_{'perturbed' if pert is not None else model}"
+        if mult != "table":
+            workload = f"gemm_{size}x{size}x{size}_" + ("native_fp32_fma" if mult == "native" else "torch_matmul_fp32")
         info = dict(m=size, n=size, k=size, table=f"{model} M={M}" + (" +-1 perturbed" if pert is not None else ""))
         host = dict(A=A, B=B, lut=lut, M=M)
     elif config == 2:
@@ -87,7 +112,7 @@ def build_workload(config, am, torch):
             for c in calls:
                 am.approx_gemm(*c)
 
-        workload = "mlp_784-1024-1024-10_b256_fwd_dgrad_wgrad_lut_m7_mitchell"
+        workload = "mlp_784-1024-1024-10_b256_fwd_dgrad_wgrad_" + ("lut_m7_mitchell" if lut is not None else "native_fp32_fma")
         info = dict(batch=256, widths=[784, 1024, 1024, 10])
         host = dict(layers=layers, lut=lut, M=M)
     elif config == 3:
@@ -105,7 +130,8 @@ def build_workload(config, am, torch):
             am.approx_conv2d_dgrad(N, H, W, C, K, R, S, st, pd, dyd, wd, dx)
             am.approx_conv2d_wgrad(N, H, W, C, K, R, S, st, pd, xd, dyd, dw)
 
-        workload = "conv2d_3x3_s1_p1_nhwc_128x32x32x64_to_64_fwd_dgrad_wgrad_lut_m7_mitchell"
+        workload = "conv2d_3x3_s1_p1_nhwc_128x32x32x64_to_64_fwd_dgrad_wgrad_" + (
+            "lut_m7_mitchell" if lut is not None else "native_fp32_fma")
         info = dict(N=N, H=H, W=W, C=C, K=K, R=R, S=S)
         host = dict(x=x, w=w, dy=dy, lut=lut, M=M)
     elif config == 5:
@@ -139,7 +165,7 @@ def build_workload(config, am, torch):
             am.approx_gemm_batched(0, 0, T, dh, T, p_ptr, T, v_ptr, 3 * D, o_ptr, D, nb)
             am.approx_gemm(0, 0, Bz * T, D, D, O, D, Wod, D, Y, D)
 
-        workload = "mha_b16_s512_d768_h12_qkv_qk_pv_out_lut_m7_mitchell"
+        workload = "mha_b16_s512_d768_h12_qkv_qk_pv_out_" + ("lut_m7_mitchell" if lut is not None else "native_fp32_fma")
         info = dict(batch=Bz, seq=T, d_model=D, heads=Hh, note="softmax between the products is in the step time")
         host = dict(X=X, Wqkv=Wqkv, lut=lut, M=M)
     else:
@@ -185,7 +211,8 @@ def cpu_baseline(config, host):
         macs = rows * Wqkv.shape[0] * Wqkv.shape[1]
         sample = f"rows 0-{rows - 1} of the QKV projection ({macs:.3g} MACs)"
     dt = time.perf_counter() - t0
-    return {"value": macs / dt / 1e9, "unit": "G approximate MAC/s", "cores": 1, "kind": "oracle",
+    unit = "G approximate MAC/s" if host["lut"] is not None else "G MAC/s"
+    return {"value": macs / dt / 1e9, "unit": unit, "cores": 1, "kind": "oracle",
             "sample": sample, "seconds": round(dt, 2)}
 
 
@@ -196,6 +223,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=4, help="workload 1-5 (4: 8192^3 GEMM, the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--multiplier", choices=("table", "native", "library"), default="table",
+                    help="table: the approximate multiplier (default); native: the library's FP32 FMA in "
+                         "the same kernels; library: torch.matmul FP32 (GEMM workloads only)")
     ap.add_argument("--lds-probe", action="store_true",
                     help="instead of the workload, run the LDS table-lookup rate probe")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -231,7 +261,8 @@ def main():
     import approximate_multiplier_dnn_amd as am
     from datagen import configs as cfg
     log(f"building workload {args.config} ...")
-    step, workload, info, host = build_workload(args.config, am, torch)
+    torch.backends.cuda.matmul.allow_tf32 = False
+    step, workload, info, host = build_workload(args.config, am, torch, args.multiplier)
     macs = cfg.macs(args.config)
 
     for _ in range(args.warmup):
@@ -239,40 +270,67 @@ def main():
     torch.cuda.synchronize()
     am.approx_profile_read()           # drop anything recorded so far
     am.approx_profile_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     for _ in range(args.steps):
         step()
+    ev1.record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     am.approx_profile_enable(False)
     launches, kern_ms = am.approx_profile_read()
+    if args.multiplier == "library":   # torch.matmul runs on torch's stream: time it there
+        launches, kern_ms = args.steps, ev0.elapsed_time(ev1)
     ms_per_step = dt * 1e3 / args.steps
     value = macs * args.steps / dt / 1e9
-    log(f"{workload}: {ms_per_step:.3f} ms/step, {value:.1f} G approx-MAC/s; "
-        f"GEMM kernel {launches} launches, {kern_ms / max(launches, 1):.3f} ms avg")
+    log(f"{workload}: {ms_per_step:.3f} ms/step, {value:.1f} G MAC/s; "
+        f"kernel {launches} launches, {kern_ms / max(launches, 1):.3f} ms avg")
 
-    # roofline of the GEMM kernel: algorithmic lane-ops over kernel time
     kern_s = kern_ms / 1e3
-    achieved = OPS_PER_MAC * macs * args.steps / kern_s / 1e12 if kern_s > 0 else 0.0
-    traffic = traffic_record(workload)
-    roofline = {
-        "bound": "alu",
-        "achieved": round(achieved, 3),
-        "peak": round(VALU_PEAK_TOPS, 2),
-        "unit": "TOP/s",
-        "frac": round(achieved / VALU_PEAK_TOPS, 4),
-        "traffic": traffic,
-        "kernel": "amx::main_kernel",
-        "kernel_ms_avg": round(kern_ms / max(launches, 1), 4),
-        "launches_per_step": launches // max(args.steps, 1),
-        "ops_per_mac": OPS_PER_MAC,
-        "kernel_G_mac_per_s": round(macs * args.steps / kern_s / 1e9, 1) if kern_s > 0 else 0.0,
-    }
+    mac_rate = macs * args.steps / kern_s if kern_s > 0 else 0.0     # MAC/s over kernel time
+    if args.multiplier == "library":
+        achieved = 2 * mac_rate / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": FP32_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": "torch.matmul (FP32)", "kernel_ms_avg": round(kern_ms / max(launches, 1), 4)}
+    else:
+        # roofline of the GEMM kernel: algorithmic lane-ops over kernel time
+        ops = OPS_PER_MAC if args.multiplier == "table" else 1        # native: one FMA per MAC
+        achieved = ops * mac_rate / 1e12
+        roofline = {
+            "bound": "alu",
+            "achieved": round(achieved, 3),
+            "peak": round(VALU_PEAK_TOPS, 2),
+            "unit": "TOP/s",
+            "frac": round(achieved / VALU_PEAK_TOPS, 4),
+            "traffic": traffic_record(workload),
+            "kernel": "amx::main_kernel",
+            "kernel_ms_avg": round(kern_ms / max(launches, 1), 4),
+            "launches_per_step": launches // max(args.steps, 1),
+            "ops_per_mac": ops,
+            "kernel_G_mac_per_s": round(mac_rate / 1e9, 1),
+        }
+        if args.multiplier == "table":
+            # the second roof: one 16-bit LDS lookup per MAC
+            lookups = mac_rate / 1e12
+            M = host["M"]
+            roofline["lds"] = {
+                "achieved_T_lookups_per_s": round(lookups, 3),
+                "peak_T_lookups_per_s": round(LDS_PEAK_LOOKUPS, 2),
+                "frac": round(lookups / LDS_PEAK_LOOKUPS, 4),
+                "random_column_ceiling_T_per_s": LDS_RANDOM_COLUMN_CEILING.get(M),
+                "frac_of_ceiling": round(lookups / LDS_RANDOM_COLUMN_CEILING[M], 4)
+                if M in LDS_RANDOM_COLUMN_CEILING else None,
+            }
+    metric = {"table": "G approximate MAC/s (LUT-simulated FP32 GEMM)",
+              "native": "G MAC/s (native FP32 multiplier, same kernels)",
+              "library": "G MAC/s (torch.matmul FP32)"}[args.multiplier]
     rec = {
-        "metric": "G approximate MAC/s (LUT-simulated FP32 GEMM)",
+        "metric": metric,
         "value": round(value, 2),
-        "unit": "G approximate MAC/s",
+        "unit": "G approximate MAC/s" if args.multiplier == "table" else "G MAC/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -285,7 +343,7 @@ def main():
         "config": dict(workload=workload, **info),
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.multiplier != "library":
         log("timing the oracle on a CPU sample ...")
         rec["cpu_baseline"] = cpu_baseline(args.config, host)
     print(json.dumps(rec), flush=True)

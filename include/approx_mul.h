@@ -45,7 +45,7 @@ extern "C" {
 
 #define APPROX_OK 0
 #define APPROX_EINVAL (-1)       /* bad size, leading dimension, flag or NULL pointer */
-#define APPROX_ENOLUT (-2)       /* no table loaded on the current device */
+#define APPROX_ENOLUT (-2)       /* no table loaded (and no native multiplier selected) on the current device */
 #define APPROX_EUNSUPPORTED (-3) /* M outside [1, 8], or a table the generator cannot express */
 #define APPROX_EHIP (-4)         /* a HIP runtime call failed (allocation, copy, launch) */
 
@@ -90,7 +90,24 @@ int approx_lut_build_from_model(int M, float (*mul)(float a, float b), uint16_t 
  */
 int approx_lut_load(const uint16_t *lut, int M);
 
-/* M of the table loaded on the current device, or APPROX_ENOLUT. */
+/*
+ * Select the native multiplier on the current device instead of a table
+ * (ApproxTrain Section V: the simulator can invoke the hardware's native
+ * multiplication, the reference point of its approximate-versus-native
+ * timing, Fig. 6). Every product of the compute calls that follow is then
+ * the exact product of the two FP32 operands, folded into the FP32
+ * accumulator by a fused multiply-add: one rounding per step, in the same
+ * order as above. Subnormal operands and sums are kept (IEEE-754), an
+ * overflow of the accumulator gives a signed infinity, and the sign of a
+ * zero result is not specified (the hardware FMA may return +0 where a tiny
+ * negative sum rounds to zero). approx_lut_load
+ * selects a table again. Synchronous, like approx_lut_load, when it releases
+ * a loaded table. Errors: APPROX_EHIP.
+ */
+int approx_native_load(void);
+
+/* M of the table loaded on the current device, 0 when the native multiplier
+ * is selected, or APPROX_ENOLUT. */
 int approx_lut_bits(void);
 
 /*

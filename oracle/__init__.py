@@ -48,6 +48,8 @@ def lib():
         L.orc_mul_exact.restype = ctypes.c_float
         L.orc_mul_mitchell.argtypes = [ctypes.c_float, ctypes.c_float]
         L.orc_mul_mitchell.restype = ctypes.c_float
+        L.orc_mul_native.argtypes = [ctypes.c_float, ctypes.c_float]
+        L.orc_mul_native.restype = ctypes.c_double
         L.orc_lut_generate.argtypes = [c_int, vp, vp]
         L.orc_lut_generate.restype = c_int
         L.orc_lut_perturb.argtypes = [c_int, vp, vp]
@@ -75,6 +77,16 @@ def _ptr(a):
 
 def _f32(a):
     return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _table(lut, M):
+    """(table array or None, pointer, M) for the C calls. lut=None selects
+    the native multiplier (exact products; M must then be 0)."""
+    if lut is None:
+        assert M == 0
+        return None, None, 0
+    t = np.ascontiguousarray(lut, dtype=np.uint16)
+    return t, _ptr(t), M
 
 
 # ---------------------------------------------------------------- tables
@@ -127,6 +139,14 @@ def amsim(a, b, lut, M):
     return amsim_bits(a.view(np.uint32), b.view(np.uint32), lut, M).view(np.float32)
 
 
+def mul_native(a, b):
+    """The native multiplier (exact product of two floats, as float64)."""
+    a = _f32(a).ravel()
+    b = _f32(b).ravel()
+    f = lib().orc_mul_native
+    return np.array([f(float(x), float(y)) for x, y in zip(a, b)], dtype=np.float64)
+
+
 # ---------------------------------------------------------------- GEMM
 
 def gemm(A, B, lut, M, transA=False, transB=False):
@@ -142,9 +162,9 @@ def gemm(A, B, lut, M, transA=False, transB=False):
     assert k == kb
     R = np.zeros((m, n), dtype=np.float64)
     S = np.zeros((m, n), dtype=np.float64)
-    lut = np.ascontiguousarray(lut, dtype=np.uint16)
+    t, tp, M = _table(lut, M)
     lib().orc_gemm(int(transA), int(transB), m, n, k, _ptr(A), A.shape[1],
-                   _ptr(B), B.shape[1], _ptr(lut), M, _ptr(R), _ptr(S))
+                   _ptr(B), B.shape[1], tp, M, _ptr(R), _ptr(S))
     return R, S
 
 
@@ -160,9 +180,9 @@ def gemm_at(A, B, lut, M, rows, cols, transA=False, transB=False):
     assert rows.shape == cols.shape
     R = np.zeros(rows.size, dtype=np.float64)
     S = np.zeros(rows.size, dtype=np.float64)
-    lut = np.ascontiguousarray(lut, dtype=np.uint16)
+    t, tp, M = _table(lut, M)
     lib().orc_gemm_at(int(transA), int(transB), m, n, k, _ptr(A), A.shape[1],
-                      _ptr(B), B.shape[1], _ptr(lut), M, rows.size,
+                      _ptr(B), B.shape[1], tp, M, rows.size,
                       _ptr(rows), _ptr(cols), _ptr(R), _ptr(S))
     return R, S
 
@@ -178,18 +198,18 @@ def conv_out_hw(H, W, R, S, stride, pad):
 def _conv(name, shape_out, geomargs, t1, t2, lut, M, idx):
     t1 = _f32(t1)
     t2 = _f32(t2)
-    lut = np.ascontiguousarray(lut, dtype=np.uint16)
+    t, tp, M = _table(lut, M)
     if idx is None:
         total = int(np.prod(shape_out))
         R = np.zeros(total, dtype=np.float64)
         S = np.zeros(total, dtype=np.float64)
-        getattr(lib(), name)(*geomargs, _ptr(t1), _ptr(t2), _ptr(lut), M, 0, None,
+        getattr(lib(), name)(*geomargs, _ptr(t1), _ptr(t2), tp, M, 0, None,
                              _ptr(R), _ptr(S))
         return R.reshape(shape_out), S.reshape(shape_out)
     idx = np.ascontiguousarray(idx, dtype=np.int64)
     R = np.zeros(idx.size, dtype=np.float64)
     S = np.zeros(idx.size, dtype=np.float64)
-    getattr(lib(), name)(*geomargs, _ptr(t1), _ptr(t2), _ptr(lut), M, idx.size,
+    getattr(lib(), name)(*geomargs, _ptr(t1), _ptr(t2), tp, M, idx.size,
                          _ptr(idx), _ptr(R), _ptr(S))
     return R, S
 

@@ -45,6 +45,10 @@
  *       multiplied (the IM2COL buffer holds zeros there), not omitted terms.
  *   R9  Sums are taken in double precision here; the sum of absolute
  *       products is returned beside each output for the error gate.
+ *   R10 The native multiplier (Section V: the simulator can call the
+ *       hardware multiplication instead of the table, the reference point
+ *       of Fig. 6) is the exact product of the two floats, rounded only when
+ *       it is added to a sum. The sums take it when no table is given.
  *
  * Build: gcc -O2 -std=c99 -fPIC -shared -ffp-contract=off oracle.c -lm
  */
@@ -180,6 +184,22 @@ float orc_amsim(float a, float b, const uint16_t *lut, int M)
     return float_of(orc_amsim_bits(bits_of(a), bits_of(b), lut, M));
 }
 
+/* ------------------------------------------------------------------ */
+/* The native multiplier (reading R10)                                 */
+/* ------------------------------------------------------------------ */
+/* Exact: two 24-bit significands give at most 48 bits (double holds 53),
+ * and every product of two floats, subnormals included, lies inside
+ * double's normal range. Inf * 0 and NaN inputs give NaN, as in IEEE-754. */
+double orc_mul_native(float a, float b) { return (double)a * (double)b; }
+
+/* the product the sums below use: Algorithm 2 with a table, the native
+ * multiplier when there is none (lut == NULL) */
+static double product(float a, float b, const uint16_t *lut, int M)
+{
+    if (lut == NULL) return orc_mul_native(a, b);
+    return (double)orc_amsim(a, b, lut, M);
+}
+
 /* element-wise products of two bit arrays (for exhaustive checks) */
 void orc_amsim_many(int64_t count, const uint32_t *a, const uint32_t *b,
                     const uint16_t *lut, int M, uint32_t *out)
@@ -201,7 +221,7 @@ static void gemm_one(int transA, int transB, int i, int j, int k,
     for (int p = 0; p < k; ++p) {
         float a = transA ? A[(long)p * lda + i] : A[(long)i * lda + p];
         float b = transB ? B[(long)j * ldb + p] : B[(long)p * ldb + j];
-        double prod = (double)orc_amsim(a, b, lut, M);
+        double prod = product(a, b, lut, M);
         sum += prod;
         abs_sum += fabs(prod);
     }
@@ -284,7 +304,7 @@ static void fwd_one(const geom *g, const float *x, const float *w, long idx,
         for (int s = 0; s < g->S; ++s)
             for (int c = 0; c < g->C; ++c) {
                 float a = x_at(g, x, n, p * g->sh - g->ph + r, q * g->sw - g->pw + s, c);
-                double prod = (double)orc_amsim(a, w_at(g, w, r, s, c, k), lut, M);
+                double prod = product(a, w_at(g, w, r, s, c, k), lut, M);
                 sum += prod;
                 abs_sum += fabs(prod);
             }
@@ -307,7 +327,7 @@ static void dgrad_one(const geom *g, const float *dy, const float *w, long idx,
         for (int s = 0; s < g->S; ++s)
             for (int k = 0; k < g->K; ++k) {
                 float a = dilated_dy_at(g, dy, n, h + g->ph - r, ww + g->pw - s, k);
-                double prod = (double)orc_amsim(a, w_at(g, w, r, s, c, k), lut, M);
+                double prod = product(a, w_at(g, w, r, s, c, k), lut, M);
                 sum += prod;
                 abs_sum += fabs(prod);
             }
@@ -330,7 +350,7 @@ static void wgrad_one(const geom *g, const float *x, const float *dy, long idx,
             for (int q = 0; q < g->Q; ++q) {
                 float a = x_at(g, x, n, p * g->sh - g->ph + r, q * g->sw - g->pw + s, c);
                 float b = dy[(((long)n * g->P + p) * g->Q + q) * g->K + k];
-                double prod = (double)orc_amsim(a, b, lut, M);
+                double prod = product(a, b, lut, M);
                 sum += prod;
                 abs_sum += fabs(prod);
             }
