@@ -22,10 +22,16 @@ using amx::ReduceParams;
 using amx::Word;
 
 constexpr int kMaxDevices = 64;
-constexpr int kRowsPerWave = 256;   // 64 lanes x 4 rows
-constexpr int kColsPerWave = 16;
-constexpr int kSplitBelowTiles = 256;
-constexpr int kSplitTargetItems = 512;
+using amx::kColsPerWave;
+using amx::kShapes;
+// Reduction-split model (a function of the shapes only, so results never
+// depend on the device): kSplitSlots resident workgroups (the MI355X's 256
+// CUs, one GEMM workgroup each), kSplitMacRate approximate MAC/s over the
+// GPU, kSplitBytesRate bytes/s for the reduction of the chunk partials.
+constexpr int64_t kSplitSlots = 256;
+constexpr double kSplitMacRate = 6.0e12;
+constexpr double kSplitBytesRate = 4.0e12;
+constexpr int kSplitMax = 1024;
 constexpr int64_t kMaxPanelWords = (int64_t)1 << 31;
 
 struct DeviceTable {
@@ -81,16 +87,16 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Resident GEMM workgroups per device (CUs x blocks per CU), per kernel
 // variant; queried once per device and kept.
-int64_t g_slots[kMaxDevices][3][2];
+int64_t g_slots[kMaxDevices][3][2][2];
 
-int64_t launch_slots(int dev, int lds_class, int gather)
+int64_t launch_slots(int dev, int lds_class, int gather, int shape)
 {
     std::lock_guard<std::mutex> lock(g_mu);
-    int64_t& s = g_slots[dev][lds_class][gather];
+    int64_t& s = g_slots[dev][lds_class][gather][shape];
     if (s == 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
-        s = (int64_t)cus * amx::main_blocks_per_cu(lds_class, gather);
+        s = (int64_t)cus * amx::main_blocks_per_cu(lds_class, gather, shape);
     }
     return s;
 }
@@ -111,29 +117,68 @@ int table_of(int dev, const uint16_t** image, int* M)
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Waves of a workgroup are arranged wr x wc (wr * wc = 8); wc follows the
-// number of 16-column groups so narrow outputs waste few waves.
-void pick_waves(int n, int* wr, int* wc)
+// Waves of a workgroup of the given shape are arranged wr x wc (wr * wc =
+// waves): the arrangement whose tiles pad the m x n output least, the wider
+// one on a tie (its waves share more lane-operand rows). Returns the padded
+// output area.
+int64_t pick_waves(int m, int n, int shape, int* wr, int* wc)
 {
-    const int64_t groups = cdiv(n, kColsPerWave);
-    *wc = groups >= 8 ? 8 : groups >= 4 ? 4 : groups >= 2 ? 2 : 1;
-    *wr = 8 / *wc;
+    const int waves = kShapes[shape].waves, rows = 64 * kShapes[shape].rows_per_lane;
+    int64_t best = -1;
+    for (int c = waves; c >= 1; --c) {
+        if (waves % c) continue;
+        const int r = waves / c;
+        const int64_t tm = (int64_t)r * rows, tn = (int64_t)c * kColsPerWave;
+        const int64_t area = cdiv(m, tm) * tm * (cdiv(n, tn) * tn);
+        if (best < 0 || area < best) {
+            best = area;
+            *wr = r;
+            *wc = c;
+        }
+    }
+    return best;
 }
 
-// Reduction split: only when the output tiles cannot occupy the GPU. A
-// function of the shapes alone, so results do not depend on the device.
-void pick_split(int64_t tiles, int KB, int* splits, int* chunk)
+// Workgroup shape of a call. Tables of M <= 7 take the 12-wave shape (its
+// extra wave per SIMD hides lookup latency: 11% faster on the 3x3 conv
+// passes) unless its coarser row tiles pad the output by more than 10% over
+// the 8-wave shape. M = 8 (the LDS lookup rate binds: the 8-wave shape
+// measured 11% faster) and the native multiplier take the 8-wave shape.
+int pick_shape(int M, int m, int n, int* wr, int* wc)
 {
-    int s = 1;
-    if (tiles < kSplitBelowTiles) {
-        s = (int)std::min<int64_t>(cdiv(kSplitTargetItems, tiles), std::max(1, KB / 4));
-        s = std::max(1, s);
+    int r0, c0, r1, c1;
+    const int64_t a0 = pick_waves(m, n, 0, &r0, &c0);
+    const int64_t a1 = pick_waves(m, n, 1, &r1, &c1);
+    const bool twelve = M >= 1 && M <= 7 && a1 * 10 <= a0 * 11;
+    *wr = twelve ? r1 : r0;
+    *wc = twelve ? c1 : c0;
+    return twelve ? 1 : 0;
+}
+
+// Reduction split. The work items (tiles x splits) run in rounds over the
+// resident workgroups; a round costs one chunk of k-steps. A split trades
+// the idle workgroups of a partial last round against the partials it writes
+// and the reduction that reads them back. Picks the split count of least
+// modelled time; ties go to fewer splits.
+void pick_split(int64_t tiles, int KB, int64_t tile_macs_per_kstep, int64_t out_elems, int* splits, int* chunk)
+{
+    const int smax = std::max(1, std::min(kSplitMax, KB / 2));
+    const double kstep_s = (double)tile_macs_per_kstep / (kSplitMacRate / (double)kSplitSlots);
+    double best = -1.0;
+    int bs = 1;
+    for (int sc = 1; sc <= smax; ++sc) {
+        const int c = (int)cdiv(KB, sc);
+        const int64_t items = tiles * cdiv(KB, c);
+        const double gemm = (double)cdiv(items, kSplitSlots) * c * kstep_s;
+        const double red = sc > 1 ? (double)(cdiv(KB, c) + 1) * out_elems * 4.0 / kSplitBytesRate : 0.0;
+        if (best < 0.0 || gemm + red < best * 0.999) {
+            best = gemm + red;
+            bs = sc;
+        }
     }
-    int c = (int)cdiv(KB, s);
-    if (c < 1) c = 1;
+    const int c = (int)cdiv(KB, bs);
     *chunk = c;
     *splits = (int)cdiv(KB, c);
-    if (*splits < 1) *splits = 1;
 }
 
 bool force_checked()
@@ -151,6 +196,7 @@ struct Plan {
     int64_t lane_count = 0, uni_count = 0;    // per batch entry, logical Words the decode writes
     int batch = 1;
     int gather = 0;
+    int shape = 0;                // workgroup shape (index into kShapes)
     float* C = nullptr;
     float* const* Cp = nullptr;   // output pointer array (batched by pointers)
     int64_t strideC = 0;
@@ -163,7 +209,8 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
         return APPROX_EUNSUPPORTED;
     const int lds_class = M == 0 ? 2 : M <= 7 ? 0 : 1;   // M = 0: native multiplier
     const int64_t tiles = (int64_t)mp.tiles_m * mp.tiles_n * pl.batch;
-    pick_split(tiles, mp.KB, &mp.splits, &mp.chunk);
+    const int64_t TM = (int64_t)mp.wr * 64 * kShapes[pl.shape].rows_per_lane, TN = (int64_t)mp.wc * kColsPerWave;
+    pick_split(tiles, mp.KB, TM * TN * 4, (int64_t)mp.m_out * mp.n_out * pl.batch, &mp.splits, &mp.chunk);
     mp.items = tiles * mp.splits;
 
     const size_t stats_b = align256(amx::STAT_INTS * sizeof(int));
@@ -214,7 +261,7 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     if (amx::launch_decode(pl.lane, stream) != hipSuccess) return APPROX_EHIP;
     if (amx::launch_decode(pl.uni, stream) != hipSuccess) return APPROX_EHIP;
 
-    const int64_t slots = launch_slots(dev, lds_class, pl.gather);
+    const int64_t slots = launch_slots(dev, lds_class, pl.gather, pl.shape);
     const int grid = (int)std::min<int64_t>(mp.items, slots);
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     bool prof;
@@ -226,7 +273,7 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
         if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess) return APPROX_EHIP;
         if (hipEventRecord(ev0, stream) != hipSuccess) return APPROX_EHIP;
     }
-    if (amx::launch_main(mp, lds_class, pl.gather, grid, stream) != hipSuccess) return APPROX_EHIP;
+    if (amx::launch_main(mp, lds_class, pl.gather, pl.shape, grid, stream) != hipSuccess) return APPROX_EHIP;
     if (prof) {
         if (hipEventRecord(ev1, stream) != hipSuccess) return APPROX_EHIP;
         std::lock_guard<std::mutex> lock(g_mu);
@@ -286,11 +333,11 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
     pl.C = C;
     pl.strideC = strideC;
     int wr, wc;
-    pick_waves(n, &wr, &wc);
+    pl.shape = pick_shape(M, m, n, &wr, &wc);
     MainParams& mp = pl.mp;
     mp.wr = wr;
     mp.wc = wc;
-    const int TM = wr * kRowsPerWave, TN = wc * kColsPerWave;
+    const int TM = wr * 64 * kShapes[pl.shape].rows_per_lane, TN = wc * kColsPerWave;
     mp.tiles_m = (int)cdiv(m, TM);
     mp.tiles_n = (int)cdiv(n, TN);
     const int Mp = mp.tiles_m * TM, Np = mp.tiles_n * TN;
@@ -384,10 +431,10 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
     else if (kind == CONV_DGRAD) { m = s.N * s.H * s.W; n = s.C; }
     else { m = s.R * s.S * s.C; n = s.K; }
     int wr, wc;
-    pick_waves(n, &wr, &wc);
+    pl.shape = pick_shape(M, m, n, &wr, &wc);
     mp.wr = wr;
     mp.wc = wc;
-    const int TM = wr * kRowsPerWave, TN = wc * kColsPerWave;
+    const int TM = wr * 64 * kShapes[pl.shape].rows_per_lane, TN = wc * kColsPerWave;
     mp.tiles_m = (int)cdiv(m, TM);
     mp.tiles_n = (int)cdiv(n, TN);
     const int Np = mp.tiles_n * TN;

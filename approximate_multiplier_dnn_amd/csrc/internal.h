@@ -21,6 +21,17 @@ struct Word {
     uint32_t se;
 };
 
+// Workgroup shapes of the GEMM kernel: `waves` waves per workgroup, each lane
+// accumulating `rows_per_lane` output rows x kColsPerWave columns, so a wave
+// covers 64 * rows_per_lane rows and kColsPerWave columns. Shape 0: 8 waves
+// (2 per SIMD) x 4 rows; shape 1: 12 waves (3 per SIMD) x 3 rows, which hides
+// more lookup latency at the cost of coarser row tiles.
+struct KernelShape {
+    int waves, rows_per_lane;
+};
+constexpr KernelShape kShapes[2] = {{8, 4}, {12, 3}};
+constexpr int kColsPerWave = 16;
+
 // Table image in device memory, laid out as the LDS copy the kernels use:
 // column c holds the 2^M entries of one uniform-operand mantissa followed by
 // two zero entries (the pad). Column stride = (2^M + 2) entries.
@@ -144,10 +155,10 @@ struct ReduceParams {
 
 hipError_t launch_init_stats(int* stats, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
-hipError_t launch_main(const MainParams& p, int lds_class, int gather, int grid, hipStream_t s);
+hipError_t launch_main(const MainParams& p, int lds_class, int gather, int shape, int grid, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_fill_zero(float* C, float* const* Cp, int m, int n, int ldc, int batch, int64_t strideC,
                             hipStream_t s);
-int main_blocks_per_cu(int lds_class, int gather);
+int main_blocks_per_cu(int lds_class, int gather, int shape);
 
 }  // namespace amx

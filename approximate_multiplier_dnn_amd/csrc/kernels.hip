@@ -9,7 +9,7 @@
 //                produced (zero-padded images, the padded and dilated errors
 //                and the transposed, reversed filter of Section VI-B).
 //   2. main    : the table is staged in LDS once per persistent workgroup;
-//                each lane owns 4 rows x 16 columns of the output; per MAC it
+//                each lane owns 3 or 4 rows x 16 columns of the output; per MAC it
 //                forms the LDS address, reads one 16-bit entry and folds it
 //                into the FP32 accumulator.
 //   3. reduce  : when the reduction is split, sums the chunk partials in
@@ -31,9 +31,9 @@
 
 namespace amx {
 
-constexpr int NT = 512;   // threads per GEMM workgroup (8 waves, 2 per SIMD)
-constexpr int RPL = 4;    // output rows per lane
-constexpr int CPW = 16;   // output columns per wave
+// The GEMM kernel is instantiated for each workgroup shape of internal.h:
+// NW waves per workgroup, RPL output rows per lane; CPW output columns per wave.
+constexpr int CPW = kColsPerWave;
 
 // ------------------------------------------------------------------ decode
 
@@ -409,6 +409,7 @@ __device__ __forceinline__ void step_offsets(const MainParams& p, KCounter& kc, 
 }
 
 // Lane operand words (w, se) of the RPL rows of this lane at one offset.
+template <int RPL>
 __device__ __forceinline__ void load_lane(const Word* panel, const uint32_t (&base)[RPL], int off,
                                           uint32_t (&wa)[RPL], uint32_t (&sa)[RPL])
 {
@@ -507,6 +508,7 @@ __device__ __forceinline__ uint32_t col_word(const uint32_t (&q)[UQ], int c, int
 // wait counter).
 constexpr int LA = 3;
 
+template <int RPL>
 __device__ __forceinline__ void fast_index(const uint32_t (&wa)[RPL], const uint32_t (&sa)[RPL], const uint32_t (&q)[UQ],
                                            const unsigned char* lut, float (&acc)[RPL][CPW])
 {
@@ -537,6 +539,7 @@ __device__ __forceinline__ void fast_index(const uint32_t (&wa)[RPL], const uint
 // product folded by the hardware FMA, acc = fma(a, b, acc) (the product is
 // exact inside the FMA; one rounding per step). No table lookup: this is the
 // reference point the approximate product is compared against.
+template <int RPL>
 __device__ __forceinline__ void native_index(const uint32_t (&sa)[RPL], const uint32_t (&q)[UQ],
                                              float (&acc)[RPL][CPW])
 {
@@ -549,6 +552,7 @@ __device__ __forceinline__ void native_index(const uint32_t (&sa)[RPL], const ui
 // Checked path over one reduction index: one product at a time (it only runs
 // for operands that can leave the normal range, so it is kept small in
 // registers rather than fast).
+template <int RPL>
 __device__ __forceinline__ void checked_index(const uint32_t (&wa)[RPL], const uint32_t (&sa)[RPL],
                                               const uint32_t (&q)[UQ], const unsigned char* lut,
                                               float (&acc)[RPL][CPW])
@@ -574,7 +578,7 @@ __device__ __forceinline__ void checked_index(const uint32_t (&wa)[RPL], const u
 // every index has its own offset from the counter (the zero region past the
 // last index). The steady-state body has no branch: the compiler's wait
 // counts for the ring stay exact, so the prefetch is never drained early.
-template <bool GATHER, bool NATIVE, int R>
+template <bool GATHER, bool NATIVE, int R, int RPL>
 __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* panel, const Word* bsrc,
                                               const uint32_t (&base)[RPL], int kb0, int kb1, uint32_t quad,
                                               const unsigned char* lut, float (&acc)[RPL][CPW])
@@ -673,7 +677,7 @@ __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* p
 }
 
 // Checked k-loop: operand words one index ahead, parity slots.
-template <bool GATHER>
+template <bool GATHER, int RPL>
 __device__ __forceinline__ void mainloop_checked(const MainParams& p, const Word* panel, const Word* bsrc,
                                                  const uint32_t (&base)[RPL], int kb0, int kb1, uint32_t quad,
                                                  const unsigned char* lut, float (&acc)[RPL][CPW])
@@ -713,9 +717,10 @@ __device__ __forceinline__ void mainloop_checked(const MainParams& p, const Word
 // with NATIVE = true, where no table is staged.
 constexpr int NATIVE_LDS = 16;
 
-template <int LDSB, bool GATHER, bool NATIVE>
-__global__ __launch_bounds__(NT, 1) void main_kernel(MainParams p)
+template <int LDSB, bool GATHER, bool NATIVE, int NW, int RPL>
+__global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
 {
+    constexpr int NT = NW * 64;
     __shared__ __align__(16) unsigned char lut[LDSB];
     if (!NATIVE) {
         const uint4* src = reinterpret_cast<const uint4*>(p.lut);
@@ -786,8 +791,8 @@ __global__ __launch_bounds__(NT, 1) void main_kernel(MainParams p)
             for (int j = 0; j < CPW; ++j) acc[x][j] = 0.0f;
 
         if (kb0 < kb1) {
-            if (fast) mainloop_fast<GATHER, NATIVE, NATIVE ? 8 : 4>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
-            else if (!NATIVE) mainloop_checked<GATHER>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
+            if (fast) mainloop_fast<GATHER, NATIVE, NATIVE ? 8 : 4, RPL>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
+            else if (!NATIVE) mainloop_checked<GATHER, RPL>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
         }
 
         float* out;
@@ -904,28 +909,41 @@ hipError_t launch_decode(const DecodeParams& p0, hipStream_t s)
     return hipGetLastError();
 }
 
-// The GEMM kernel variant of (lds_class, gather): lds_class 0 = table of
-// M <= 7, 1 = M == 8, 2 = native multiplier (no table).
-static const void* main_variant(int lds_class, int gather)
+// The GEMM kernel variant of (lds_class, gather, shape): lds_class 0 = table
+// of M <= 7, 1 = M == 8, 2 = native multiplier (no table); shape indexes
+// kShapes.
+template <int S>
+static const void* main_variant_shape(int lds_class, int gather)
 {
+    constexpr int NW = kShapes[S].waves, R = kShapes[S].rows_per_lane;
     if (lds_class == 0)
-        return gather ? (const void*)main_kernel<LDS_SMALL, true, false> : (const void*)main_kernel<LDS_SMALL, false, false>;
+        return gather ? (const void*)main_kernel<LDS_SMALL, true, false, NW, R>
+                      : (const void*)main_kernel<LDS_SMALL, false, false, NW, R>;
     if (lds_class == 1)
-        return gather ? (const void*)main_kernel<LDS_LARGE, true, false> : (const void*)main_kernel<LDS_LARGE, false, false>;
-    return gather ? (const void*)main_kernel<NATIVE_LDS, true, true> : (const void*)main_kernel<NATIVE_LDS, false, true>;
+        return gather ? (const void*)main_kernel<LDS_LARGE, true, false, NW, R>
+                      : (const void*)main_kernel<LDS_LARGE, false, false, NW, R>;
+    return gather ? (const void*)main_kernel<NATIVE_LDS, true, true, NW, R>
+                  : (const void*)main_kernel<NATIVE_LDS, false, true, NW, R>;
 }
 
-hipError_t launch_main(const MainParams& p, int lds_class, int gather, int grid, hipStream_t s)
+static const void* main_variant(int lds_class, int gather, int shape)
+{
+    return shape == 0 ? main_variant_shape<0>(lds_class, gather) : main_variant_shape<1>(lds_class, gather);
+}
+
+hipError_t launch_main(const MainParams& p, int lds_class, int gather, int shape, int grid, hipStream_t s)
 {
     MainParams arg = p;
     void* args[] = {&arg};
-    return hipLaunchKernel(main_variant(lds_class, gather), dim3(grid), dim3(NT), args, 0, s);
+    return hipLaunchKernel(main_variant(lds_class, gather, shape), dim3(grid), dim3(kShapes[shape].waves * 64), args,
+                           0, s);
 }
 
-int main_blocks_per_cu(int lds_class, int gather)
+int main_blocks_per_cu(int lds_class, int gather, int shape)
 {
     int n = 0;
-    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, main_variant(lds_class, gather), NT, 0);
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, main_variant(lds_class, gather, shape),
+                                                                      kShapes[shape].waves * 64, 0);
     if (e != hipSuccess || n < 1) n = 1;
     return n;
 }
