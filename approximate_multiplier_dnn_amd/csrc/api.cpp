@@ -87,7 +87,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Resident GEMM workgroups per device (CUs x blocks per CU), per kernel
 // variant; queried once per device and kept.
-int64_t g_slots[kMaxDevices][3][2][2];
+int64_t g_slots[kMaxDevices][4][2][2];
 
 int64_t launch_slots(int dev, int lds_class, int gather, int shape)
 {
@@ -211,7 +211,8 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     MainParams& mp = pl.mp;
     if (pl.lane_words * pl.batch >= kMaxPanelWords || pl.uni_words * pl.batch >= kMaxPanelWords)
         return APPROX_EUNSUPPORTED;
-    const int lds_class = M == 0 ? 2 : M <= 7 ? 0 : 1;   // M = 0: native multiplier
+    // M = 0: native multiplier; M = 9..11: table in global memory
+    const int lds_class = M == 0 ? 2 : M <= 7 ? 0 : M == 8 ? 1 : 3;
     const int64_t tiles = (int64_t)mp.tiles_m * mp.tiles_n * pl.batch;
     const int64_t TM = (int64_t)mp.wr * 64 * kShapes[pl.shape].rows_per_lane, TN = (int64_t)mp.wc * kColsPerWave;
     pick_split(tiles, mp.KB, TM * TN * 4, (int64_t)mp.m_out * mp.n_out * pl.batch, &mp.splits, &mp.chunk);
@@ -517,7 +518,7 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
 extern "C" int approx_lut_load(const uint16_t* lut, int M)
 {
     if (lut == nullptr) return APPROX_EINVAL;
-    if (M < 1 || M > 8) return APPROX_EUNSUPPORTED;
+    if (M < 1 || M > 11) return APPROX_EUNSUPPORTED;
     int dev = 0;
     int rc = current_device(&dev);
     if (rc != APPROX_OK) return rc;

@@ -38,7 +38,8 @@ constexpr int kColsPerWave = 16;
 inline int lut_col_entries(int M) { return (1 << M) + 2; }
 inline int lut_image_bytes(int M) { return (1 << M) * lut_col_entries(M) * 2; }
 
-// LDS footprint classes of the GEMM kernel.
+// LDS footprint classes of the GEMM kernel (tables of M = 9..11 are read
+// from global memory instead).
 constexpr int LDS_SMALL = (1 << 7) * ((1 << 7) + 2) * 2;  // M <= 7: 33,280 bytes
 constexpr int LDS_LARGE = (1 << 8) * ((1 << 8) + 2) * 2;  // M == 8: 132,096 bytes
 

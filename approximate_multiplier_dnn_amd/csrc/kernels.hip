@@ -504,11 +504,13 @@ __device__ __forceinline__ uint32_t col_word(const uint32_t (&q)[UQ], int c, int
 
 // Fast path over one reduction index, finer pipeline: a group is the RPL
 // products of one column; the lookups of group g+LA are issued while group g
-// is folded, so LA*RPL lookups per wave are in flight (within the 4-bit LDS
-// wait counter).
-constexpr int LA = 3;
+// is folded, so up to (LA+1)*RPL lookups per wave are in flight. LA = 3 for
+// a table in LDS (the 4-bit LDS wait counter), 6 for a table in global
+// memory (longer latency, 6-bit counter).
+constexpr int LA_LDS = 3;
+constexpr int LA_GLOBAL = 6;
 
-template <int RPL>
+template <int RPL, int LA>
 __device__ __forceinline__ void fast_index(const uint32_t (&wa)[RPL], const uint32_t (&sa)[RPL], const uint32_t (&q)[UQ],
                                            const unsigned char* lut, float (&acc)[RPL][CPW])
 {
@@ -578,7 +580,7 @@ __device__ __forceinline__ void checked_index(const uint32_t (&wa)[RPL], const u
 // every index has its own offset from the counter (the zero region past the
 // last index). The steady-state body has no branch: the compiler's wait
 // counts for the ring stay exact, so the prefetch is never drained early.
-template <bool GATHER, bool NATIVE, int R, int RPL>
+template <bool GATHER, bool NATIVE, int R, int RPL, int LA>
 __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* panel, const Word* bsrc,
                                               const uint32_t (&base)[RPL], int kb0, int kb1, uint32_t quad,
                                               const unsigned char* lut, float (&acc)[RPL][CPW])
@@ -638,14 +640,14 @@ __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* p
             for (int j = 0; j < R; ++j) {
                 if (j == 0) {
                     if constexpr (NATIVE) native_index(sa[0], qb[0], acc);
-                    else fast_index(wa[0], sa[0], qb[0], lut, acc);
+                    else fast_index<RPL, LA>(wa[0], sa[0], qb[0], lut, acc);
                 }
                 load_lane(panel, base, lane_off(j + PD), wa[(j + PD) % R], sa[(j + PD) % R]);
                 load_uniform(urow, quad, qb[(j + PD) % R]);
                 urow += p.bld;
                 if (j > 0) {
                     if constexpr (NATIVE) native_index(sa[j], qb[j], acc);
-                    else fast_index(wa[j], sa[j], qb[j], lut, acc);
+                    else fast_index<RPL, LA>(wa[j], sa[j], qb[j], lut, acc);
                 }
             }
             advance();
@@ -670,7 +672,7 @@ __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* p
                 urow += p.bld;
             }
             if constexpr (NATIVE) native_index(sa[j], qb[j], acc);
-            else fast_index(wa[j], sa[j], qb[j], lut, acc);
+            else fast_index<RPL, LA>(wa[j], sa[j], qb[j], lut, acc);
         }
         advance();
     }
@@ -714,20 +716,26 @@ __device__ __forceinline__ void mainloop_checked(const MainParams& p, const Word
 }
 
 // LDSB: bytes of the LDS table image (LDS_SMALL or LDS_LARGE), or NATIVE_LDS
-// with NATIVE = true, where no table is staged.
+// where no table is staged (native multiplier, table in global memory).
 constexpr int NATIVE_LDS = 16;
 
-template <int LDSB, bool GATHER, bool NATIVE, int NW, int RPL>
+// GTAB: the table (M = 9..11, too large for LDS) is read from global memory,
+// where it stays resident in L2 / the last-level cache; LDSB is then unused.
+template <int LDSB, bool GATHER, bool NATIVE, int NW, int RPL, bool GTAB>
 __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
 {
     constexpr int NT = NW * 64;
-    __shared__ __align__(16) unsigned char lut[LDSB];
-    if (!NATIVE) {
+    constexpr int LA = GTAB ? LA_GLOBAL : LA_LDS;
+    __shared__ __align__(16) unsigned char lds_tab[LDSB];
+    if (!NATIVE && !GTAB) {
         const uint4* src = reinterpret_cast<const uint4*>(p.lut);
-        uint4* dst = reinterpret_cast<uint4*>(lut);
+        uint4* dst = reinterpret_cast<uint4*>(lds_tab);
         const int n16 = p.lut_bytes >> 4;
         for (int t = threadIdx.x; t < n16; t += NT) dst[t] = src[t];
     }
+    const unsigned char* lut;
+    if constexpr (GTAB) lut = reinterpret_cast<const unsigned char*>(p.lut);
+    else lut = lds_tab;
     __shared__ int range[4];
     if (threadIdx.x < 64) {                       // wave 0 folds the stats slots
         const int* sl = p.stats + (threadIdx.x % STAT_SLOTS) * STAT_STRIDE;
@@ -791,7 +799,7 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
             for (int j = 0; j < CPW; ++j) acc[x][j] = 0.0f;
 
         if (kb0 < kb1) {
-            if (fast) mainloop_fast<GATHER, NATIVE, NATIVE ? 8 : 4, RPL>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
+            if (fast) mainloop_fast<GATHER, NATIVE, NATIVE ? 8 : 4, RPL, LA>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
             else if (!NATIVE) mainloop_checked<GATHER, RPL>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
         }
 
@@ -910,20 +918,26 @@ hipError_t launch_decode(const DecodeParams& p0, hipStream_t s)
 }
 
 // The GEMM kernel variant of (lds_class, gather, shape): lds_class 0 = table
-// of M <= 7, 1 = M == 8, 2 = native multiplier (no table); shape indexes
-// kShapes.
+// of M <= 7 in LDS, 1 = M == 8 in LDS, 2 = native multiplier (no table),
+// 3 = table of M = 9..11 in global memory; shape indexes kShapes.
 template <int S>
 static const void* main_variant_shape(int lds_class, int gather)
 {
     constexpr int NW = kShapes[S].waves, R = kShapes[S].rows_per_lane;
-    if (lds_class == 0)
-        return gather ? (const void*)main_kernel<LDS_SMALL, true, false, NW, R>
-                      : (const void*)main_kernel<LDS_SMALL, false, false, NW, R>;
-    if (lds_class == 1)
-        return gather ? (const void*)main_kernel<LDS_LARGE, true, false, NW, R>
-                      : (const void*)main_kernel<LDS_LARGE, false, false, NW, R>;
-    return gather ? (const void*)main_kernel<NATIVE_LDS, true, true, NW, R>
-                  : (const void*)main_kernel<NATIVE_LDS, false, true, NW, R>;
+    switch (lds_class) {
+    case 0:
+        return gather ? (const void*)main_kernel<LDS_SMALL, true, false, NW, R, false>
+                      : (const void*)main_kernel<LDS_SMALL, false, false, NW, R, false>;
+    case 1:
+        return gather ? (const void*)main_kernel<LDS_LARGE, true, false, NW, R, false>
+                      : (const void*)main_kernel<LDS_LARGE, false, false, NW, R, false>;
+    case 2:
+        return gather ? (const void*)main_kernel<NATIVE_LDS, true, true, NW, R, false>
+                      : (const void*)main_kernel<NATIVE_LDS, false, true, NW, R, false>;
+    default:
+        return gather ? (const void*)main_kernel<NATIVE_LDS, true, false, NW, R, true>
+                      : (const void*)main_kernel<NATIVE_LDS, false, false, NW, R, true>;
+    }
 }
 
 static const void* main_variant(int lds_class, int gather, int shape)

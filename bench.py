@@ -66,10 +66,15 @@ def traffic_record(workload):
     return rec.get("bytes_per_launch")
 
 
-def build_workload(config, am, torch, mult="table"):
+def build_workload(config, am, torch, mult="table", table_bits=0):
     from datagen import configs as cfg
+    from datagen import PERTURB_SEED, pm_one
 
     model, M, pert = cfg.lut_spec(config)
+    if table_bits:                     # the same table recipe at another mantissa width
+        M = table_bits
+        if pert is not None:
+            pert = pm_one(PERTURB_SEED, 1 << (2 * M))
     if mult == "table":
         lut = am.approx_lut_build(am.MODEL_EXACT if model == "exact" else am.MODEL_MITCHELL, M, pert)
         am.approx_lut_load(lut, M)
@@ -223,6 +228,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=4, help="workload 1-5 (4: 8192^3 GEMM, the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--table-bits", type=int, default=0,
+                    help="build the workload's table at this mantissa width instead (1-11; 9-11 are read "
+                         "from global memory)")
     ap.add_argument("--multiplier", choices=("table", "native", "library"), default="table",
                     help="table: the approximate multiplier (default); native: the library's FP32 FMA in "
                          "the same kernels; library: torch.matmul FP32 (GEMM workloads only)")
@@ -262,7 +270,7 @@ def main():
     from datagen import configs as cfg
     log(f"building workload {args.config} ...")
     torch.backends.cuda.matmul.allow_tf32 = False
-    step, workload, info, host = build_workload(args.config, am, torch, args.multiplier)
+    step, workload, info, host = build_workload(args.config, am, torch, args.multiplier, args.table_bits)
     macs = cfg.macs(args.config)
 
     for _ in range(args.warmup):
@@ -312,7 +320,9 @@ def main():
             "ops_per_mac": ops,
             "kernel_G_mac_per_s": round(mac_rate / 1e9, 1),
         }
-        if args.multiplier == "table":
+        if args.multiplier == "table" and host["M"] > 8:
+            roofline["table"] = "global memory (M > 8 does not fit LDS)"
+        elif args.multiplier == "table":
             # the second roof: one 16-bit LDS lookup per MAC
             lookups = mac_rate / 1e12
             M = host["M"]

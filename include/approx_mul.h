@@ -46,7 +46,7 @@ extern "C" {
 #define APPROX_OK 0
 #define APPROX_EINVAL (-1)       /* bad size, leading dimension, flag or NULL pointer */
 #define APPROX_ENOLUT (-2)       /* no table loaded (and no native multiplier selected) on the current device */
-#define APPROX_EUNSUPPORTED (-3) /* M outside [1, 8], or a table the generator cannot express */
+#define APPROX_EUNSUPPORTED (-3) /* M outside the supported range, or a table the generator cannot express */
 #define APPROX_EHIP (-4)         /* a HIP runtime call failed (allocation, copy, launch) */
 
 /* Built-in C models of multipliers for approx_lut_build. */
@@ -84,9 +84,12 @@ int approx_lut_build_from_model(int M, float (*mul)(float a, float b), uint16_t 
  * time). `lut` is caller-owned host memory of 4^M entries in the format
  * above; it is copied during the call. Synchronous: the device is
  * synchronised before a previous table is released, so do not call it while
- * other threads queue work. Errors: APPROX_EINVAL (NULL lut),
- * APPROX_EUNSUPPORTED (M outside [1, 8]: the table must fit in LDS),
- * APPROX_EHIP.
+ * other threads queue work. Tables of M <= 8 (at most 128 KB) are staged in
+ * each workgroup's LDS; tables of M = 9..11 (512 KB to 8 MB, the top of the
+ * range Section V names) are read from global memory, where they stay
+ * resident in the L2 and last-level caches, at a lower lookup rate.
+ * Errors: APPROX_EINVAL (NULL lut), APPROX_EUNSUPPORTED (M outside
+ * [1, 11]), APPROX_EHIP.
  */
 int approx_lut_load(const uint16_t *lut, int M);
 
