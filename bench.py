@@ -101,6 +101,8 @@ def build_workload(config, am, torch, mult="table", table_bits=0):
         if mult != "table":
             workload = f"gemm_{size}x{size}x{size}_" + ("native_fp32_fma" if mult == "native" else "torch_matmul_fp32")
         info = dict(m=size, n=size, k=size, table=f"{model} M={M}" + (" +-1 perturbed" if pert is not None else ""))
+        if mult != "table":
+            info["table"] = "none (native FP32 multiplier)" if mult == "native" else "none (torch.matmul FP32)"
         host = dict(A=A, B=B, lut=lut, M=M)
     elif config == 2:
         layers = cfg.mlp_tensors()
