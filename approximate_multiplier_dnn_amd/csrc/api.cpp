@@ -35,7 +35,8 @@ constexpr int kSplitMax = 1024;
 constexpr int64_t kMaxPanelWords = (int64_t)1 << 31;
 
 struct DeviceTable {
-    uint16_t* image = nullptr;  // lane-first LDS image
+    uint16_t* image = nullptr;  // lane-first LDS image (the allocation; `flat` lies in it)
+    uint16_t* flat = nullptr;   // the table in index order (ia << M) | ib, for the row-vector kernel
     int M = 0;
     bool native = false;        // the native FP32 multiplier is selected (no image)
 };
@@ -101,9 +102,10 @@ int64_t launch_slots(int dev, int lds_class, int gather, int shape)
     return s;
 }
 
-int table_of(int dev, const uint16_t** image, int* M)
+int table_of(int dev, const uint16_t** image, int* M, const uint16_t** flat = nullptr)
 {
     std::lock_guard<std::mutex> lock(g_mu);
+    if (flat != nullptr) *flat = g_tables[dev].flat;
     if (g_tables[dev].native) {
         *image = nullptr;
         *M = 0;
@@ -301,6 +303,61 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     return APPROX_OK;
 }
 
+// Reduction split of the row-vector kernel (a function of the shapes only):
+// enough blocks to keep about 8 per CU streaming B, chunks of at least 8
+// indices.
+constexpr int64_t kGemvTargetBlocks = 2048;
+
+int gemv_run(amx::GemvParams& g, int batch, float* C, int dev, hipStream_t stream)
+{
+    const int64_t blocks = cdiv(g.n, amx::kGemvColsPerBlock) * batch;
+    int s = (int)std::min<int64_t>(std::max<int64_t>(1, cdiv(kGemvTargetBlocks, blocks)),
+                                   std::max(1, g.k / 8));
+    s = std::min(s, 65535);
+    g.chunk = (int)cdiv(g.k, s);
+    g.splits = (int)cdiv(g.k, g.chunk);
+    float* partials = nullptr;
+    if (g.splits > 1) {
+        char* base = nullptr;
+        int rc = arena_get(dev, stream, (size_t)g.splits * batch * g.m * g.n * sizeof(float), &base);
+        if (rc != APPROX_OK) return rc;
+        partials = reinterpret_cast<float*>(base);
+        g.out = partials;
+    } else {
+        g.out = C;
+    }
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    bool prof;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        prof = g_profile;
+    }
+    if (prof) {
+        if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess) return APPROX_EHIP;
+        if (hipEventRecord(ev0, stream) != hipSuccess) return APPROX_EHIP;
+    }
+    if (amx::launch_gemv(g, batch, g.lut == nullptr || g.M == 0, stream) != hipSuccess) return APPROX_EHIP;
+    if (prof) {
+        if (hipEventRecord(ev1, stream) != hipSuccess) return APPROX_EHIP;
+        std::lock_guard<std::mutex> lock(g_mu);
+        g_events.emplace_back(ev0, ev1);
+    }
+    if (g.splits > 1) {
+        ReduceParams rp{};
+        rp.ws = partials;
+        rp.out = C;
+        rp.out_ptrs = g.out_ptrs;
+        rp.m = g.m;
+        rp.n = g.n;
+        rp.ldc = g.ldc;
+        rp.splits = g.splits;
+        rp.batch = batch;
+        rp.out_batch = g.out_batch;
+        if (amx::launch_reduce(rp, stream) != hipSuccess) return APPROX_EHIP;
+    }
+    return APPROX_OK;
+}
+
 int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int lda, long long strideA,
               const float* B, int ldb, long long strideB, float* C, int ldc, long long strideC, int batch,
               void* stream_v, const float* const* Ap = nullptr, const float* const* Bp = nullptr,
@@ -323,14 +380,24 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
     int rc = current_device(&dev);
     if (rc != APPROX_OK) return rc;
     const uint16_t* image = nullptr;
+    const uint16_t* flat = nullptr;
     int M = 0;
-    rc = table_of(dev, &image, &M);
+    rc = table_of(dev, &image, &M, &flat);
     if (rc != APPROX_OK) return rc;
     hipStream_t stream = static_cast<hipStream_t>(stream_v);
 
     if (k == 0) {
         return amx::launch_fill_zero(C, Cp, m, n, ldc, batch, strideC, stream) == hipSuccess ? APPROX_OK
                                                                                           : APPROX_EHIP;
+    }
+    if (m <= amx::kGemvMaxRows && !transB) {
+        amx::GemvParams g{};
+        g.A = A; g.A_ptrs = Ap; g.A_batch = strideA;
+        g.B = B; g.B_ptrs = Bp; g.B_batch = strideB;
+        g.lut = flat;
+        g.out_ptrs = Cp; g.out_batch = strideC;
+        g.M = M; g.m = m; g.n = n; g.k = k; g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.transA = transA;
+        return gemv_run(g, batch, C, dev, stream);
     }
 
     Plan pl;
@@ -523,10 +590,15 @@ extern "C" int approx_lut_load(const uint16_t* lut, int M)
     int rc = current_device(&dev);
     if (rc != APPROX_OK) return rc;
     // lane-first image: column ib holds entries (ia, ib) for ia = 0..2^M-1, then two zeros
+    // followed (256-byte aligned) by the table in index order for the row-vector kernel
     const int side = 1 << M, cs = amx::lut_col_entries(M);
-    std::vector<uint16_t> img((size_t)side * cs, 0);
+    const size_t img_entries = (size_t)side * cs;
+    const size_t flat_at = (img_entries + 127) & ~(size_t)127;   // entries
+    const size_t entries = (size_t)1 << (2 * M);
+    std::vector<uint16_t> img(flat_at + entries, 0);
     for (int ib = 0; ib < side; ++ib)
         for (int ia = 0; ia < side; ++ia) img[(size_t)ib * cs + ia] = lut[((size_t)ia << M) | ib];
+    std::memcpy(img.data() + flat_at, lut, entries * sizeof(uint16_t));
     uint16_t* d = nullptr;
     if (hipMalloc(&d, img.size() * sizeof(uint16_t)) != hipSuccess) return APPROX_EHIP;
     if (hipMemcpy(d, img.data(), img.size() * sizeof(uint16_t), hipMemcpyHostToDevice) != hipSuccess) {
@@ -539,6 +611,7 @@ extern "C" int approx_lut_load(const uint16_t* lut, int M)
         (void)hipFree(g_tables[dev].image);
     }
     g_tables[dev].image = d;
+    g_tables[dev].flat = d + flat_at;
     g_tables[dev].M = M;
     g_tables[dev].native = false;
     return APPROX_OK;

@@ -154,6 +154,29 @@ struct ReduceParams {
     int64_t out_batch;
 };
 
+// Row-vector GEMM (op(A) has at most kGemvMaxRows rows, B not transposed):
+// lanes run over output columns, each operand is decoded in registers as it
+// is read, the table is read in index order from global memory, and the
+// reduction is split over grid.y into chunks of `chunk` indices.
+constexpr int kGemvMaxRows = 4;
+constexpr int kGemvThreads = 256;
+constexpr int kGemvColsPerLane = 4;          // kGemvThreads apart
+constexpr int kGemvColsPerBlock = kGemvThreads * kGemvColsPerLane;
+
+struct GemvParams {
+    const float* A;
+    const float* const* A_ptrs;   // batched by pointer array (device), else A + b * A_batch
+    const float* B;
+    const float* const* B_ptrs;
+    const uint16_t* lut;          // table in index order (ia << M) | ib; unused by the native multiplier
+    float* out;                   // C, or split partials when splits > 1
+    float* const* out_ptrs;
+    int64_t A_batch, B_batch, out_batch;   // elements
+    int M, m, n, k, lda, ldb, ldc, transA;
+    int splits, chunk;
+};
+
+hipError_t launch_gemv(const GemvParams& p, int batch, bool native, hipStream_t s);
 hipError_t launch_init_stats(int* stats, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_main(const MainParams& p, int lds_class, int gather, int shape, int grid, hipStream_t s);

@@ -825,6 +825,85 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
     }
 }
 
+// ------------------------------------------------------------------ row-vector GEMM
+
+// sign | exponent of an operand for the checked product: 0 for zero and
+// subnormal, +-Inf for Inf, 0x7FC00000 for NaN (as the decode pass writes).
+__device__ __forceinline__ uint32_t se_of(uint32_t bits)
+{
+    const uint32_t e = (bits >> 23) & 0xFFu;
+    const uint32_t se = e == 0u ? 0u : (bits & 0xFF800000u);
+    return (e == 255u && (bits & 0x7FFFFFu)) ? 0x7FC00000u : se;
+}
+
+// C[r][j] = sum_kk approx(op(A)(r, kk), B[kk][j]) for r < m <= kGemvMaxRows.
+// Lane t of block x owns columns x * kGemvColsPerBlock + t + c * kGemvThreads
+// (coalesced across the wave for every c); block y sums reduction indices
+// [y * chunk, (y + 1) * chunk) in ascending order. Every product takes the
+// checked path (Algorithm 2 as selects), so no exponent statistics are
+// needed; the operand fetch from HBM, not the arithmetic, bounds this kernel.
+template <bool NATIVE>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p)
+{
+    const int b = blockIdx.z, split = blockIdx.y;
+    const float* A = p.A_ptrs ? p.A_ptrs[b] : p.A + b * p.A_batch;
+    const float* B = p.B_ptrs ? p.B_ptrs[b] : p.B + b * p.B_batch;
+    const int j0 = blockIdx.x * kGemvColsPerBlock + threadIdx.x;
+    const int k0 = split * p.chunk, k1 = min(p.k, k0 + p.chunk);
+    const int sh = 23 - p.M;
+    float acc[kGemvMaxRows][kGemvColsPerLane];
+#pragma unroll
+    for (int r = 0; r < kGemvMaxRows; ++r)
+#pragma unroll
+        for (int c = 0; c < kGemvColsPerLane; ++c) acc[r][c] = 0.0f;
+    bool col_ok[kGemvColsPerLane];
+#pragma unroll
+    for (int c = 0; c < kGemvColsPerLane; ++c) col_ok[c] = j0 + c * kGemvThreads < p.n;
+
+#pragma unroll 2
+    for (int kk = k0; kk < k1; ++kk) {
+        const float* brow = B + (int64_t)kk * p.ldb + j0;
+        uint32_t bw[kGemvColsPerLane];
+#pragma unroll
+        for (int c = 0; c < kGemvColsPerLane; ++c) bw[c] = col_ok[c] ? __float_as_uint(brow[c * kGemvThreads]) : 0u;
+#pragma unroll
+        for (int r = 0; r < kGemvMaxRows; ++r) {
+            if (r >= p.m) break;
+            const uint32_t xa = __float_as_uint(p.transA ? A[(int64_t)kk * p.lda + r] : A[(int64_t)r * p.lda + kk]);
+            if constexpr (NATIVE) {
+#pragma unroll
+                for (int c = 0; c < kGemvColsPerLane; ++c)
+                    acc[r][c] = __builtin_fmaf(__uint_as_float(xa), __uint_as_float(bw[c]), acc[r][c]);
+            } else {
+                const uint32_t seA = se_of(xa);
+                const uint32_t row = ((xa & 0x7FFFFFu) >> sh) << p.M;
+#pragma unroll
+                for (int c = 0; c < kGemvColsPerLane; ++c) {
+                    const uint32_t e = p.lut[row | ((bw[c] & 0x7FFFFFu) >> sh)];
+                    acc[r][c] = checked_product_acc(acc[r][c], e, seA, se_of(bw[c]));
+                }
+            }
+        }
+    }
+
+    float* out;
+    int64_t ld;
+    if (p.splits > 1) {
+        out = p.out + ((int64_t)b * p.splits + split) * (int64_t)p.m * p.n;
+        ld = p.n;
+    } else {
+        out = p.out_ptrs ? p.out_ptrs[b] : p.out + b * p.out_batch;
+        ld = p.ldc;
+    }
+#pragma unroll
+    for (int r = 0; r < kGemvMaxRows; ++r) {
+        if (r >= p.m) break;
+#pragma unroll
+        for (int c = 0; c < kGemvColsPerLane; ++c)
+            if (col_ok[c]) out[(int64_t)r * ld + j0 + c * kGemvThreads] = acc[r][c];
+    }
+}
+
 // ------------------------------------------------------------------ reduce / fill
 
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p)
@@ -960,6 +1039,14 @@ int main_blocks_per_cu(int lds_class, int gather, int shape)
                                                                       kShapes[shape].waves * 64, 0);
     if (e != hipSuccess || n < 1) n = 1;
     return n;
+}
+
+hipError_t launch_gemv(const GemvParams& p, int batch, bool native, hipStream_t s)
+{
+    const dim3 grid((unsigned)((p.n + kGemvColsPerBlock - 1) / kGemvColsPerBlock), (unsigned)p.splits, (unsigned)batch);
+    if (native) hipLaunchKernelGGL(gemv_kernel<true>, grid, dim3(kGemvThreads), 0, s, p);
+    else hipLaunchKernelGGL(gemv_kernel<false>, grid, dim3(kGemvThreads), 0, s, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s)

@@ -66,7 +66,7 @@ def traffic_record(workload):
     return rec.get("bytes_per_launch")
 
 
-def build_workload(config, am, torch, mult="table", table_bits=0):
+def build_workload(config, am, torch, mult="table", table_bits=0, gemv=False):
     from datagen import configs as cfg
     from datagen import PERTURB_SEED, pm_one
 
@@ -88,22 +88,27 @@ def build_workload(config, am, torch, mult="table", table_bits=0):
     if config in (1, 4):
         size = 64 if config == 1 else 8192
         A, B = cfg.gemm_square(config, size)
+        rows = 1 if gemv else size     # --gemv: batch-1 inference through the same B
+        A = A[:rows].copy()
         Ad, Bd = d(A), d(B)
-        Cd = torch.empty((size, size), dtype=torch.float32, device="cuda")
+        Cd = torch.empty((rows, size), dtype=torch.float32, device="cuda")
 
         def step():
             if mult == "library":
                 torch.matmul(Ad, Bd, out=Cd)
             else:
-                am.approx_gemm(0, 0, size, size, size, Ad, size, Bd, size, Cd, size)
+                am.approx_gemm(0, 0, rows, size, size, Ad, size, Bd, size, Cd, size)
 
         workload = f"gemm_{size}x{size}x{size}_lut_m{M}_{'perturbed' if pert is not None else model}"
         if mult != "table":
             workload = f"gemm_{size}x{size}x{size}_" + ("native_fp32_fma" if mult == "native" else "torch_matmul_fp32")
+        if gemv:
+            workload = workload.replace(f"gemm_{size}x", "gemv_1x", 1)
         info = dict(m=size, n=size, k=size, table=f"{model} M={M}" + (" +-1 perturbed" if pert is not None else ""))
         if mult != "table":
             info["table"] = "none (native FP32 multiplier)" if mult == "native" else "none (torch.matmul FP32)"
-        host = dict(A=A, B=B, lut=lut, M=M)
+        host = dict(A=A, B=B, lut=lut, M=M, macs=rows * size * size)
+        info["m"] = rows
     elif config == 2:
         layers = cfg.mlp_tensors()
         dev_layers = [tuple(d(t) for t in L) for L in layers]
@@ -189,8 +194,8 @@ def cpu_baseline(config, host):
 
     t0 = time.perf_counter()
     if config in (1, 4):
-        rows = 64 if config == 1 else 32
         A, B = host["A"], host["B"]
+        rows = min(64 if config == 1 else 32, A.shape[0])
         oracle.gemm(np.ascontiguousarray(A[:rows]), B, host["lut"], host["M"])
         macs = rows * B.shape[0] * B.shape[1]
         sample = f"rows 0-{rows - 1} of the {A.shape[0]}x{B.shape[1]}x{B.shape[0]} GEMM ({macs:.3g} MACs)"
@@ -233,6 +238,8 @@ def main():
     ap.add_argument("--table-bits", type=int, default=0,
                     help="build the workload's table at this mantissa width instead (1-11; 9-11 are read "
                          "from global memory)")
+    ap.add_argument("--gemv", action="store_true",
+                    help="with --config 1 or 4: one row of A (batch-1 inference), the row-vector kernel")
     ap.add_argument("--multiplier", choices=("table", "native", "library"), default="table",
                     help="table: the approximate multiplier (default); native: the library's FP32 FMA in "
                          "the same kernels; library: torch.matmul FP32 (GEMM workloads only)")
@@ -272,8 +279,10 @@ def main():
     from datagen import configs as cfg
     log(f"building workload {args.config} ...")
     torch.backends.cuda.matmul.allow_tf32 = False
-    step, workload, info, host = build_workload(args.config, am, torch, args.multiplier, args.table_bits)
-    macs = cfg.macs(args.config)
+    if args.gemv and args.config not in (1, 4):
+        raise SystemExit("--gemv goes with the square GEMM workloads (--config 1 or 4)")
+    step, workload, info, host = build_workload(args.config, am, torch, args.multiplier, args.table_bits, args.gemv)
+    macs = host.get("macs") or cfg.macs(args.config)
 
     for _ in range(args.warmup):
         step()
@@ -300,7 +309,16 @@ def main():
 
     kern_s = kern_ms / 1e3
     mac_rate = macs * args.steps / kern_s if kern_s > 0 else 0.0     # MAC/s over kernel time
-    if args.multiplier == "library":
+    if args.gemv and args.multiplier != "library":
+        # the row-vector kernel streams B from HBM: algorithmic bytes = A + B read + C written
+        nbytes = 4 * (host["A"].size + host["B"].size + host["A"].shape[0] * host["B"].shape[1])
+        achieved = nbytes / (kern_s / args.steps) / 1e9 if kern_s > 0 else 0.0
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "amx::gemv_kernel",
+                    "kernel_ms_avg": round(kern_ms / max(launches, 1), 4),
+                    "launches_per_step": launches // max(args.steps, 1),
+                    "kernel_G_mac_per_s": round(mac_rate / 1e9, 1)}
+    elif args.multiplier == "library":
         achieved = 2 * mac_rate / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": FP32_MFMA_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,

@@ -1,0 +1,154 @@
+"""GPU parity of the row-vector path: approx_gemm with at most 4 rows in op(A)
+and B not transposed (batch-1 and few-row dense inference; ApproxTrain,
+arXiv 2209.04161, Section VI-D, keeps a separate matrix-vector kernel for
+this case). The library routes these calls to a kernel whose lanes run over
+the output columns; products must equal the oracle's bit for bit (k = 1) and
+sums pass the gate of tests/parity.py, for tables in LDS range and beyond it,
+and for the native multiplier.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from datagen import PERTURB_SEED, normal, pm_one, special_values, splitmix64
+from parity import gate
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def am():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import approximate_multiplier_dnn_amd as m
+    yield m
+    m.approx_lut_load(oracle.lut_generate(7, "mitchell"), 7)
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+_T = {}
+
+
+def use(am, name):
+    """Load a table (or the native multiplier); returns (table or None, M)."""
+    if name not in _T:
+        if name == "mitchell7":
+            _T[name] = (oracle.lut_generate(7, "mitchell"), 7)
+        elif name == "perturbed8":
+            _T[name] = (oracle.lut_perturb(8, oracle.lut_generate(8, "exact"), pm_one(PERTURB_SEED, 1 << 16)), 8)
+        elif name == "arbitrary11":
+            _T[name] = ((splitmix64(7011, 1 << 22) >> np.uint64(48)).astype(np.uint16), 11)
+        else:
+            _T[name] = (None, 0)
+    t, M = _T[name]
+    if t is None:
+        am.approx_native_load()
+    else:
+        am.approx_lut_load(t, M)
+    return t, M
+
+
+@pytest.mark.parametrize("name", ["mitchell7", "perturbed8", "arbitrary11", "native"])
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("transA", [0, 1])
+@pytest.mark.parametrize("nk", [(1, 1), (5, 7), (1000, 300), (1025, 2049), (4096, 513)])
+def test_gemv_parity(am, name, m, transA, nk):
+    n, k = nk
+    t, M = use(am, name)
+    seed = 11 * m + 7 * n + k + 50 * transA
+    A = normal(seed, (k, m) if transA else (m, k))
+    B = normal(seed + 1, (k, n))
+    R, S = oracle.gemm(A, B, t, M, transA=bool(transA))
+    C = am.gemm(dev(A), dev(B), transA=bool(transA))
+    gate(host(C), R, S, what=f"gemv {name} m={m} {nk} tA={transA}")
+
+
+@pytest.mark.parametrize("name", ["mitchell7", "perturbed8", "arbitrary11"])
+def test_gemv_products_bit_exact(am, name):
+    """k = 1: every output is +0 + one approximate product."""
+    t, M = use(am, name)
+    r = splitmix64(900 + M, 900)
+    mant = (r & np.uint64(0x7FFFFF)).astype(np.uint32)
+    exp = np.array([1, 60, 127, 190, 254], np.uint32)[(r >> np.uint64(32)) % np.uint64(5)]
+    sign = ((r >> np.uint64(40)) & np.uint64(1)).astype(np.uint32)
+    bvals = np.concatenate([(sign << np.uint32(31)) | (exp << np.uint32(23)) | mant,
+                            special_values().view(np.uint32)]).astype(np.uint32)
+    avals = np.concatenate([bvals[:2], special_values().view(np.uint32)[:2]]).astype(np.uint32)  # m = 4 rows
+    C = torch.empty((4, bvals.size), dtype=torch.float32, device="cuda")
+    am.approx_gemm(0, 0, 4, bvals.size, 1, dev(avals.view(np.float32).reshape(4, 1)), 1,
+                   dev(bvals.view(np.float32).reshape(1, -1)), bvals.size, C, bvals.size)
+    got = host(C).view(np.uint32)
+    want = oracle.amsim_bits(np.repeat(avals, bvals.size), np.tile(bvals, 4), t, M).reshape(4, bvals.size)
+    want = np.where(want == 0x80000000, 0, want).astype(np.uint32)
+    gnan = np.isnan(got.view(np.float32))
+    assert np.array_equal(gnan, np.isnan(want.view(np.float32)))
+    assert np.count_nonzero(got[~gnan] != want[~gnan]) == 0
+
+
+def test_gemv_special_values_and_padding(am):
+    t, M = use(am, "perturbed8")
+    m, n, k, lda, ldb, ldc = 3, 700, 90, 100, 710, 720
+    A = normal(931, (m, lda))
+    B = normal(932, (k, ldb))
+    A[0, 5] = np.inf
+    A[1, :] = 0.0
+    A[1, 7] = np.nan
+    A[2, 3] = np.float32(1.0e-41)       # subnormal: counts as zero
+    B[5, 11] = 0.0                      # Inf x 0 -> NaN at (0, 11)
+    B[9, 40] = -np.inf
+    R, S = oracle.gemm(A[:, :k], B[:, :n], t, M)
+    Cd = torch.full((m, ldc), 7.0, device="cuda")
+    am.approx_gemm(0, 0, m, n, k, dev(A), lda, dev(B), ldb, Cd, ldc)
+    Ch = host(Cd)
+    with np.errstate(invalid="ignore"):
+        gate(Ch[:, :n], R, S, what="gemv specials")
+    assert np.all(Ch[:, n:] == 7.0)     # the padding of C is not written
+
+
+def test_gemv_batched(am):
+    t, M = use(am, "mitchell7")
+    nb, n, k = 5, 300, 200
+    As = [normal(940 + i, (1, k)) for i in range(nb)]
+    Bs = [normal(950 + i, (k, n)) for i in range(nb)]
+    Ad = dev(np.stack(As))
+    Bd = dev(np.stack(Bs))
+    C = torch.full((nb, 1, n), -1.0, device="cuda")
+    am.approx_gemm_strided_batched(0, 0, 1, n, k, Ad, k, k, Bd, n, k * n, C, n, n, nb)
+    got = host(C)
+    for i in range(nb):
+        R, S = oracle.gemm(As[i], Bs[i], t, M)
+        gate(got[i], R, S, what=f"gemv strided batch {i}")
+    C2 = torch.full((nb, 1, n), -1.0, device="cuda")
+    ap = am.pointer_array([Ad[i].data_ptr() for i in range(nb)])
+    bp = am.pointer_array([Bd[i].data_ptr() for i in range(nb)])
+    cp = am.pointer_array([C2[i].data_ptr() for i in range(nb)])
+    am.approx_gemm_batched(0, 0, 1, n, k, ap, k, bp, n, cp, n, nb)
+    assert np.array_equal(host(C2), got)   # same kernel, same order
+
+
+def test_gemv_8192_full_size(am):
+    """Batch-1 inference through an 8192 x 8192 layer with the M = 8 perturbed
+    table: the configuration `bench.py --gemv` times; every output checked."""
+    t, M = use(am, "perturbed8")
+    x = normal(961, (1, 8192))
+    W = normal(962, (8192, 8192))
+    R, S = oracle.gemm(x, W, t, M)
+    gate(host(am.gemm(dev(x), dev(W))), R, S, what="gemv 8192")
+
+
+def test_gemv_deterministic(am):
+    use(am, "mitchell7")
+    x = dev(normal(971, (2, 3000)))
+    W = dev(normal(972, (3000, 2500)))
+    c1 = host(am.gemm(x, W))
+    c2 = host(am.gemm(x, W))
+    assert np.array_equal(c1.view(np.uint32), c2.view(np.uint32))
