@@ -303,19 +303,38 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     return APPROX_OK;
 }
 
-// Reduction split of the row-vector kernel (a function of the shapes only):
-// enough blocks to keep about 8 per CU streaming B, chunks of at least 8
-// indices.
-constexpr int64_t kGemvTargetBlocks = 2048;
+// Reduction split of the row-vector kernel (a function of the shapes and the
+// table width only): about 256 x 1024 threads' worth of work items (column
+// block x split), i.e. one 1024-thread workgroup per CU of the MI355X, so each
+// item streams a long stretch of B; chunks of at least 8 indices.
+constexpr int64_t kGemvTargetThreads = 256 * 1024;
+
+int64_t g_gemv_slots[kMaxDevices][4];
 
 int gemv_run(amx::GemvParams& g, int batch, float* C, int dev, hipStream_t stream)
 {
-    const int64_t blocks = cdiv(g.n, amx::kGemvColsPerBlock) * batch;
-    int s = (int)std::min<int64_t>(std::max<int64_t>(1, cdiv(kGemvTargetBlocks, blocks)),
-                                   std::max(1, g.k / 8));
-    s = std::min(s, 65535);
+    const int variant = g.M == 0 ? 3 : g.M <= 7 ? 0 : g.M == 8 ? 1 : 2;
+    const int cols = amx::gemv_threads(variant) * amx::kGemvColsPerLane;
+    const int64_t blocks = cdiv(g.n, cols) * batch;
+    const int64_t target = kGemvTargetThreads / amx::gemv_threads(variant);
+    int s = (int)std::min<int64_t>(std::max<int64_t>(1, cdiv(target, blocks)), std::max(1, g.k / 8));
     g.chunk = (int)cdiv(g.k, s);
     g.splits = (int)cdiv(g.k, g.chunk);
+    g.batch = batch;
+    const int64_t items = blocks * g.splits;
+    if (items > INT32_MAX) return APPROX_EUNSUPPORTED;
+    int64_t slots;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        int64_t& sl = g_gemv_slots[dev][variant];
+        if (sl == 0) {
+            int cus = 0;
+            if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+            sl = (int64_t)cus * amx::gemv_blocks_per_cu(variant);
+        }
+        slots = sl;
+    }
+    const int grid = (int)std::min<int64_t>(items, slots);
     float* partials = nullptr;
     if (g.splits > 1) {
         char* base = nullptr;
@@ -336,7 +355,7 @@ int gemv_run(amx::GemvParams& g, int batch, float* C, int dev, hipStream_t strea
         if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess) return APPROX_EHIP;
         if (hipEventRecord(ev0, stream) != hipSuccess) return APPROX_EHIP;
     }
-    if (amx::launch_gemv(g, batch, g.lut == nullptr || g.M == 0, stream) != hipSuccess) return APPROX_EHIP;
+    if (amx::launch_gemv(g, variant, grid, stream) != hipSuccess) return APPROX_EHIP;
     if (prof) {
         if (hipEventRecord(ev1, stream) != hipSuccess) return APPROX_EHIP;
         std::lock_guard<std::mutex> lock(g_mu);
@@ -595,7 +614,7 @@ extern "C" int approx_lut_load(const uint16_t* lut, int M)
     const size_t img_entries = (size_t)side * cs;
     const size_t flat_at = (img_entries + 127) & ~(size_t)127;   // entries
     const size_t entries = (size_t)1 << (2 * M);
-    std::vector<uint16_t> img(flat_at + entries, 0);
+    std::vector<uint16_t> img(flat_at + entries + 8, 0);   // + a zero entry (and padding) after the table
     for (int ib = 0; ib < side; ++ib)
         for (int ia = 0; ia < side; ++ia) img[(size_t)ib * cs + ia] = lut[((size_t)ia << M) | ib];
     std::memcpy(img.data() + flat_at, lut, entries * sizeof(uint16_t));

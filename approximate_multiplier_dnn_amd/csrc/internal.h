@@ -159,9 +159,9 @@ struct ReduceParams {
 // is read, the table is read in index order from global memory, and the
 // reduction is split over grid.y into chunks of `chunk` indices.
 constexpr int kGemvMaxRows = 4;
-constexpr int kGemvThreads = 256;
-constexpr int kGemvColsPerLane = 4;          // kGemvThreads apart
-constexpr int kGemvColsPerBlock = kGemvThreads * kGemvColsPerLane;
+constexpr int kGemvThreads = 256;            // table in global memory / native
+constexpr int kGemvLdsThreads = 1024;        // table staged in LDS (one copy per workgroup)
+constexpr int kGemvColsPerLane = 4;          // one workgroup's thread count apart
 
 struct GemvParams {
     const float* A;
@@ -173,10 +173,15 @@ struct GemvParams {
     float* const* out_ptrs;
     int64_t A_batch, B_batch, out_batch;   // elements
     int M, m, n, k, lda, ldb, ldc, transA;
-    int splits, chunk;
+    int splits, chunk, batch;
 };
 
-hipError_t launch_gemv(const GemvParams& p, int batch, bool native, hipStream_t s);
+// variant: 0 = table of M <= 7 in LDS, 1 = M == 8 in LDS, 2 = table in global
+// memory, 3 = native multiplier. The kernel is persistent over `grid`
+// workgroups of gemv_threads(variant) threads.
+int gemv_threads(int variant);
+int gemv_blocks_per_cu(int variant);
+hipError_t launch_gemv(const GemvParams& p, int variant, int grid, hipStream_t s);
 hipError_t launch_init_stats(int* stats, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_main(const MainParams& p, int lds_class, int gather, int shape, int grid, hipStream_t s);

@@ -35,6 +35,12 @@ namespace amx {
 // NW waves per workgroup, RPL output rows per lane; CPW output columns per wave.
 constexpr int CPW = kColsPerWave;
 
+// Global-memory views of pointers that may come from a device pointer array:
+// loaded pointers are generic (flat), and flat loads count against the LDS
+// wait counter too, which would serialise every table lookup behind them.
+typedef const float __attribute__((address_space(1)))* gfloat_cptr;
+typedef float __attribute__((address_space(1)))* gfloat_ptr;
+
 // ------------------------------------------------------------------ decode
 
 // M = 0 selects the native multiplier: the Word carries the operand's own
@@ -803,20 +809,20 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
             else if (!NATIVE) mainloop_checked<GATHER, RPL>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
         }
 
-        float* out;
+        gfloat_ptr out;
         int ld;
         if (p.splits > 1) {
-            out = p.out + ((int64_t)b * p.splits + split) * (int64_t)p.m_out * p.n_out;
+            out = (gfloat_ptr)(p.out + ((int64_t)b * p.splits + split) * (int64_t)p.m_out * p.n_out);
             ld = p.n_out;
         } else {
-            out = p.out_ptrs ? p.out_ptrs[b] : p.out + (int64_t)b * p.out_batch;
+            out = (gfloat_ptr)(p.out_ptrs ? p.out_ptrs[b] : p.out + (int64_t)b * p.out_batch);
             ld = p.ldc;
         }
 #pragma unroll
         for (int x = 0; x < RPL; ++x) {
             const int i = row0 + x * 64 + lane;
             if (i < p.m_out) {
-                float* o = out + (int64_t)i * ld + col0;
+                gfloat_ptr o = out + (int64_t)i * ld + col0;
 #pragma unroll
                 for (int j = 0; j < CPW; ++j)
                     if (col0 + j < p.n_out) o[j] = acc[x][j];
@@ -826,6 +832,7 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
 }
 
 // ------------------------------------------------------------------ row-vector GEMM
+
 
 // sign | exponent of an operand for the checked product: 0 for zero and
 // subnormal, +-Inf for Inf, 0x7FC00000 for NaN (as the decode pass writes).
@@ -837,70 +844,200 @@ __device__ __forceinline__ uint32_t se_of(uint32_t bits)
 }
 
 // C[r][j] = sum_kk approx(op(A)(r, kk), B[kk][j]) for r < m <= kGemvMaxRows.
-// Lane t of block x owns columns x * kGemvColsPerBlock + t + c * kGemvThreads
-// (coalesced across the wave for every c); block y sums reduction indices
-// [y * chunk, (y + 1) * chunk) in ascending order. Every product takes the
-// checked path (Algorithm 2 as selects), so no exponent statistics are
-// needed; the operand fetch from HBM, not the arithmetic, bounds this kernel.
-template <bool NATIVE>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p)
+// Work item (column block, split, batch entry): lane t owns columns
+// block * NTG * kGemvColsPerLane + t + c * NTG (coalesced across the wave for
+// every c) and sums reduction indices [split * chunk, (split + 1) * chunk) in
+// ascending order. Columns past n read column n - 1 and are not stored, so
+// the loop has no divergent branch. The table is read in index order; entry
+// 4^M is a zero (the target of zero, Inf and NaN operands, as the pad entry
+// of the GEMM image). TABB > 0: the table is staged once per persistent
+// workgroup in LDS, where the lookups of one op(A) element fall in one
+// 2^M-entry row; TABB = 0: it is read from global memory (M = 9..11).
+//
+// Fast path (as in the GEMM kernel): fma(as_float((e << 8) + seB),
+// as_float(seA), acc), exact while every product stays normal. Per item the
+// wave takes the exponent range of its op(A) chunk and checks each B element
+// against the window that keeps the products normal; if any lane of the wave
+// finds an element outside it, the wave redoes its columns of the item with
+// the checked path (Algorithm 2 as selects), which gives the same bits
+// wherever both apply.
+// Reduction indices whose operands are requested together in the row-vector kernel.
+constexpr int GG = 8;
+
+template <int MR, bool NATIVE, int NTG>
+__device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* lut, gfloat_cptr A, gfloat_cptr B,
+                                          int j0, int k0, int k1, float (&acc)[kGemvMaxRows][kGemvColsPerLane])
 {
-    const int b = blockIdx.z, split = blockIdx.y;
-    const float* A = p.A_ptrs ? p.A_ptrs[b] : p.A + b * p.A_batch;
-    const float* B = p.B_ptrs ? p.B_ptrs[b] : p.B + b * p.B_batch;
-    const int j0 = blockIdx.x * kGemvColsPerBlock + threadIdx.x;
-    const int k0 = split * p.chunk, k1 = min(p.k, k0 + p.chunk);
     const int sh = 23 - p.M;
-    float acc[kGemvMaxRows][kGemvColsPerLane];
+    const uint32_t mmask = (1u << p.M) - 1u;
+    const uint32_t zero_ix = 1u << (2 * p.M);
+    const int lane = threadIdx.x & 63;
+    int jc[kGemvColsPerLane];
+#pragma unroll
+    for (int c = 0; c < kGemvColsPerLane; ++c) jc[c] = min(j0 + c * NTG, p.n - 1);
+    auto a_at = [&](int r, int kk) -> uint32_t {
+        return __float_as_uint(p.transA ? A[(int64_t)kk * p.lda + r] : A[(int64_t)r * p.lda + kk]);
+    };
 #pragma unroll
     for (int r = 0; r < kGemvMaxRows; ++r)
 #pragma unroll
         for (int c = 0; c < kGemvColsPerLane; ++c) acc[r][c] = 0.0f;
-    bool col_ok[kGemvColsPerLane];
-#pragma unroll
-    for (int c = 0; c < kGemvColsPerLane; ++c) col_ok[c] = j0 + c * kGemvThreads < p.n;
 
-#pragma unroll 2
-    for (int kk = k0; kk < k1; ++kk) {
-        const float* brow = B + (int64_t)kk * p.ldb + j0;
-        uint32_t bw[kGemvColsPerLane];
+    bool checked = !NATIVE;
+    if constexpr (!NATIVE) {
+        // exponent range of the normal op(A) elements of this item (whole wave)
+        int emin = 255, emax = 0;
 #pragma unroll
-        for (int c = 0; c < kGemvColsPerLane; ++c) bw[c] = col_ok[c] ? __float_as_uint(brow[c * kGemvThreads]) : 0u;
+        for (int r = 0; r < MR; ++r)
+            for (int kk = k0 + lane; kk < k1; kk += 64) {
+                const int e = (int)((a_at(r, kk) >> 23) & 0xFFu);
+                const bool normal = e != 0 && e != 255;
+                emin = normal ? min(emin, e) : emin;
+                emax = normal ? max(emax, e) : emax;
+            }
+        for (int off = 32; off > 0; off >>= 1) {
+            emin = min(emin, __shfl_xor(emin, off, 64));
+            emax = max(emax, __shfl_xor(emax, off, 64));
+        }
+        // B exponents eb (normal) that keep every product normal
+        const int lo = emin > emax ? 1 : max(1, 128 - emin);
+        const int hi = emin > emax ? 253 : min(253, 380 - emax);
+        checked = lo > hi;
+        if (!checked) {
+            bool bad = false;
+            for (int kg = k0; kg < k1; kg += GG) {
+                // the group's operands first: GG rows of B and op(A) in flight at once
+                uint32_t bw[GG][kGemvColsPerLane], xa[GG][MR];
 #pragma unroll
-        for (int r = 0; r < kGemvMaxRows; ++r) {
-            if (r >= p.m) break;
-            const uint32_t xa = __float_as_uint(p.transA ? A[(int64_t)kk * p.lda + r] : A[(int64_t)r * p.lda + kk]);
-            if constexpr (NATIVE) {
+                for (int g = 0; g < GG; ++g) {
+                    const int kk = min(kg + g, k1 - 1);
+                    const gfloat_cptr brow = B + (int64_t)kk * p.ldb;
 #pragma unroll
-                for (int c = 0; c < kGemvColsPerLane; ++c)
-                    acc[r][c] = __builtin_fmaf(__uint_as_float(xa), __uint_as_float(bw[c]), acc[r][c]);
-            } else {
-                const uint32_t seA = se_of(xa);
-                const uint32_t row = ((xa & 0x7FFFFFu) >> sh) << p.M;
+                    for (int c = 0; c < kGemvColsPerLane; ++c) bw[g][c] = __float_as_uint(brow[jc[c]]);
 #pragma unroll
-                for (int c = 0; c < kGemvColsPerLane; ++c) {
-                    const uint32_t e = p.lut[row | ((bw[c] & 0x7FFFFFu) >> sh)];
-                    acc[r][c] = checked_product_acc(acc[r][c], e, seA, se_of(bw[c]));
+                    for (int r = 0; r < MR; ++r) xa[g][r] = a_at(r, kk);
+                }
+                __builtin_amdgcn_sched_barrier(0);     // keep the group's loads issued together
+#pragma unroll
+                for (int g = 0; g < GG; ++g) {
+                    if (kg + g >= k1) break;
+                    uint32_t ix[kGemvColsPerLane], seB[kGemvColsPerLane];
+#pragma unroll
+                    for (int c = 0; c < kGemvColsPerLane; ++c) {
+                        const uint32_t bits = bw[g][c];
+                        const uint32_t eb = (bits >> 23) & 0xFFu;
+                        const bool special = eb - 1u > 253u;          // zero, subnormal, Inf, NaN
+                        bad |= !special && (eb - (uint32_t)lo > (uint32_t)(hi - lo));
+                        ix[c] = special ? zero_ix : ((bits >> sh) & mmask);
+                        seB[c] = se_of(bits);
+                    }
+#pragma unroll
+                    for (int r = 0; r < MR; ++r) {
+                        const uint32_t seA = se_of(xa[g][r]);
+                        const uint32_t row = ((xa[g][r] >> sh) & mmask) << p.M;
+#pragma unroll
+                        for (int c = 0; c < kGemvColsPerLane; ++c) {
+                            const uint32_t e = lut[ix[c] == zero_ix ? zero_ix : (row | ix[c])];
+                            acc[r][c] = __builtin_fmaf(__uint_as_float((e << 8) + seB[c]), __uint_as_float(seA),
+                                                       acc[r][c]);
+                        }
+                    }
+                }
+            }
+            checked = __any(bad);
+            if (checked) {
+#pragma unroll
+                for (int r = 0; r < kGemvMaxRows; ++r)
+#pragma unroll
+                    for (int c = 0; c < kGemvColsPerLane; ++c) acc[r][c] = 0.0f;
+            }
+        }
+    }
+    if (!checked && !NATIVE) return;
+    for (int kg = k0; kg < k1; kg += GG) {
+        uint32_t bw[GG][kGemvColsPerLane], xa[GG][MR];
+#pragma unroll
+        for (int g = 0; g < GG; ++g) {
+            const int kk = min(kg + g, k1 - 1);
+            const gfloat_cptr brow = B + (int64_t)kk * p.ldb;
+#pragma unroll
+            for (int c = 0; c < kGemvColsPerLane; ++c) bw[g][c] = __float_as_uint(brow[jc[c]]);
+#pragma unroll
+            for (int r = 0; r < MR; ++r) xa[g][r] = a_at(r, kk);
+        }
+        __builtin_amdgcn_sched_barrier(0);             // keep the group's loads issued together
+#pragma unroll
+        for (int g = 0; g < GG; ++g) {
+            if (kg + g >= k1) break;
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                if constexpr (NATIVE) {
+#pragma unroll
+                    for (int c = 0; c < kGemvColsPerLane; ++c)
+                        acc[r][c] = __builtin_fmaf(__uint_as_float(xa[g][r]), __uint_as_float(bw[g][c]), acc[r][c]);
+                } else {
+                    const uint32_t seA = se_of(xa[g][r]);
+                    const uint32_t row = ((xa[g][r] >> sh) & mmask) << p.M;
+#pragma unroll
+                    for (int c = 0; c < kGemvColsPerLane; ++c) {
+                        const uint32_t e = lut[row | ((bw[g][c] >> sh) & mmask)];
+                        acc[r][c] = checked_product_acc(acc[r][c], e, seA, se_of(bw[g][c]));
+                    }
                 }
             }
         }
     }
+}
 
-    float* out;
-    int64_t ld;
-    if (p.splits > 1) {
-        out = p.out + ((int64_t)b * p.splits + split) * (int64_t)p.m * p.n;
-        ld = p.n;
-    } else {
-        out = p.out_ptrs ? p.out_ptrs[b] : p.out + b * p.out_batch;
-        ld = p.ldc;
+template <bool NATIVE, int TABB, int NTG>
+__global__ __launch_bounds__(NTG) void gemv_kernel(GemvParams p)
+{
+    __shared__ __align__(16) uint16_t tab[TABB > 0 ? TABB / 2 + 8 : 8];
+    const uint16_t* lut = p.lut;
+    if constexpr (TABB > 0) {
+        const uint4* src = reinterpret_cast<const uint4*>(p.lut);
+        uint4* dst = reinterpret_cast<uint4*>(tab);
+        const int n16 = (int)((1u << (2 * p.M)) >> 3) + 1;   // the table and the zero entry after it
+        for (int t = threadIdx.x; t < n16; t += NTG) dst[t] = src[t];
+        __syncthreads();
+        lut = tab;
     }
+    constexpr int COLS = NTG * kGemvColsPerLane;
+    const int nblk = (p.n + COLS - 1) / COLS;
+    const int items = nblk * p.splits * p.batch;
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int blk = item % nblk;
+        const int rest = item / nblk;
+        const int split = rest % p.splits;
+        const int b = rest / p.splits;
+        const gfloat_cptr A = (gfloat_cptr)(p.A_ptrs ? p.A_ptrs[b] : p.A + b * p.A_batch);
+        const gfloat_cptr B = (gfloat_cptr)(p.B_ptrs ? p.B_ptrs[b] : p.B + b * p.B_batch);
+        const int j0 = blk * COLS + threadIdx.x;
+        const int k0 = split * p.chunk, k1 = min(p.k, k0 + p.chunk);
+        float acc[kGemvMaxRows][kGemvColsPerLane];
+        switch (p.m) {
+        case 1: gemv_item<1, NATIVE, NTG>(p, lut, A, B, j0, k0, k1, acc); break;
+        case 2: gemv_item<2, NATIVE, NTG>(p, lut, A, B, j0, k0, k1, acc); break;
+        case 3: gemv_item<3, NATIVE, NTG>(p, lut, A, B, j0, k0, k1, acc); break;
+        default: gemv_item<4, NATIVE, NTG>(p, lut, A, B, j0, k0, k1, acc); break;
+        }
+
+        gfloat_ptr out;
+        int64_t ld;
+        if (p.splits > 1) {
+            out = (gfloat_ptr)(p.out + ((int64_t)b * p.splits + split) * (int64_t)p.m * p.n);
+            ld = p.n;
+        } else {
+            out = (gfloat_ptr)(p.out_ptrs ? p.out_ptrs[b] : p.out + b * p.out_batch);
+            ld = p.ldc;
+        }
 #pragma unroll
-    for (int r = 0; r < kGemvMaxRows; ++r) {
-        if (r >= p.m) break;
+        for (int r = 0; r < kGemvMaxRows; ++r) {
+            if (r >= p.m) break;
 #pragma unroll
-        for (int c = 0; c < kGemvColsPerLane; ++c)
-            if (col_ok[c]) out[(int64_t)r * ld + j0 + c * kGemvThreads] = acc[r][c];
+            for (int c = 0; c < kGemvColsPerLane; ++c)
+                if (j0 + c * NTG < p.n) out[(int64_t)r * ld + j0 + c * NTG] = acc[r][c];
+        }
     }
 }
 
@@ -1041,12 +1178,34 @@ int main_blocks_per_cu(int lds_class, int gather, int shape)
     return n;
 }
 
-hipError_t launch_gemv(const GemvParams& p, int batch, bool native, hipStream_t s)
+// Row-vector kernel variants: 0 = table of M <= 7 in LDS, 1 = M == 8 in LDS,
+// 2 = table in global memory, 3 = native multiplier.
+static const void* gemv_variant(int v)
 {
-    const dim3 grid((unsigned)((p.n + kGemvColsPerBlock - 1) / kGemvColsPerBlock), (unsigned)p.splits, (unsigned)batch);
-    if (native) hipLaunchKernelGGL(gemv_kernel<true>, grid, dim3(kGemvThreads), 0, s, p);
-    else hipLaunchKernelGGL(gemv_kernel<false>, grid, dim3(kGemvThreads), 0, s, p);
-    return hipGetLastError();
+    switch (v) {
+    case 0: return (const void*)gemv_kernel<false, (1 << 14) * 2, kGemvLdsThreads>;
+    case 1: return (const void*)gemv_kernel<false, (1 << 16) * 2, kGemvLdsThreads>;
+    case 2: return (const void*)gemv_kernel<false, 0, kGemvThreads>;
+    default: return (const void*)gemv_kernel<true, 0, kGemvThreads>;
+    }
+}
+
+int gemv_threads(int variant) { return variant <= 1 ? kGemvLdsThreads : kGemvThreads; }
+
+int gemv_blocks_per_cu(int variant)
+{
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_variant(variant), gemv_threads(variant), 0) != hipSuccess ||
+        n < 1)
+        n = 1;
+    return n;
+}
+
+hipError_t launch_gemv(const GemvParams& p, int variant, int grid, hipStream_t s)
+{
+    GemvParams arg = p;
+    void* args[] = {&arg};
+    return hipLaunchKernel(gemv_variant(variant), dim3(grid), dim3(gemv_threads(variant)), args, 0, s);
 }
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s)

@@ -105,6 +105,10 @@ def test_gemv_special_values_and_padding(am):
     A[2, 3] = np.float32(1.0e-41)       # subnormal: counts as zero
     B[5, 11] = 0.0                      # Inf x 0 -> NaN at (0, 11)
     B[9, 40] = -np.inf
+    B[20, 300] = np.float32(3.0e38)     # with A[0, 20] the product overflows: the wave falls back
+    A[0, 20] = np.float32(1.0e10)
+    B[21, 600] = np.float32(1.0e-30)    # with A[2, 21] the product underflows to zero
+    A[2, 21] = np.float32(1.0e-12)
     R, S = oracle.gemm(A[:, :k], B[:, :n], t, M)
     Cd = torch.full((m, ldc), 7.0, device="cuda")
     am.approx_gemm(0, 0, m, n, k, dev(A), lda, dev(B), ldb, Cd, ldc)
