@@ -206,6 +206,7 @@ struct Plan {
     float* C = nullptr;
     float* const* Cp = nullptr;   // output pointer array (batched by pointers)
     int64_t strideC = 0;
+    amx::AssignParams asg{};      // M = 8 copy choice of the lane operands (groups of one half-wave)
 };
 
 int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M)
@@ -266,6 +267,14 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
 
     if (amx::launch_init_stats(stats, stream) != hipSuccess) return APPROX_EHIP;
     if (amx::launch_decode(pl.lane, stream) != hipSuccess) return APPROX_EHIP;
+    if (M == 8) {                     // M = 8 columns carry second copies to choose from
+        amx::AssignParams& ap = pl.asg;
+        ap.panel = lane_panel;
+        ap.batch_stride = pl.lane_words;
+        ap.batch = pl.batch;
+        ap.pad_w = (1u << M) * 2u;
+        if (amx::launch_assign(ap, stream) != hipSuccess) return APPROX_EHIP;
+    }
     if (amx::launch_decode(pl.uni, stream) != hipSuccess) return APPROX_EHIP;
 
     const int64_t slots = launch_slots(dev, lds_class, pl.gather, pl.shape);
@@ -469,6 +478,11 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
     mp.U1 = KB; mp.U2 = 1; mp.U3 = 1; mp.K1 = a.ldw; mp.K2 = 0; mp.K3 = 0;
     mp.KB = KB;
     pl.gather = 0;
+    // a half-wave reads rows i0..i0+31 (i0 a multiple of 32) at one index
+    pl.asg.G1 = KB; pl.asg.S1 = a.ldw;
+    pl.asg.G2 = Mp / 32; pl.asg.S2 = 32 * 4;
+    pl.asg.G3 = 4; pl.asg.S3 = 1;
+    pl.asg.LS = 4; pl.asg.O = 0; pl.asg.E = Mp;
     return run_plan(pl, dev, stream, image, M);
 }
 
@@ -555,6 +569,14 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
         mp.U1 = s.R; mp.U2 = s.S; mp.U3 = Cb;
         mp.K1 = rowB; mp.K2 = 4; mp.K3 = Wp * 4;
         pl.gather = 0;
+        // groups: 32 image columns, sw apart, from the one the centre tap
+        // reads for output column 0 (exact when Q = 32, close for the other taps)
+        const int w0 = std::min(std::max((s.S - 1) / 2, 0), Wp - 1);
+        pl.asg.G1 = s.N * Hp * Cb; pl.asg.S1 = (int64_t)Wp * 4;
+        pl.asg.E = (Wp - 1 - w0) / s.sw + 1;
+        pl.asg.G2 = (int)cdiv(pl.asg.E, 32); pl.asg.S2 = 32 * s.sw * 4;
+        pl.asg.G3 = 4; pl.asg.S3 = 1;
+        pl.asg.LS = s.sw * 4; pl.asg.O = w0 * 4;
     } else if (kind == CONV_DGRAD) {
         const int Hd = s.H + s.R - 1, Wd = s.W + s.S - 1, Kb = (int)cdiv(s.K, 4), Kp = Kb * 4;
         a.layout = amx::L_IMG_DGRAD;
@@ -571,6 +593,12 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
         mp.U1 = s.R; mp.U2 = s.S; mp.U3 = Kb;
         mp.K1 = rowB; mp.K2 = 4; mp.K3 = Wd * 4;
         pl.gather = 0;
+        const int w0 = std::min((s.S - 1) / 2, Wd - 1);
+        pl.asg.G1 = s.N * Hd * Kb; pl.asg.S1 = (int64_t)Wd * 4;
+        pl.asg.E = Wd - w0;
+        pl.asg.G2 = (int)cdiv(pl.asg.E, 32); pl.asg.S2 = 32 * 4;
+        pl.asg.G3 = 4; pl.asg.S3 = 1;
+        pl.asg.LS = 4; pl.asg.O = w0 * 4;
     } else {
         const int Hp = s.H + 2 * s.ph, Wp = s.W + 2 * s.pw;
         const int64_t body = (int64_t)s.N * Hp * s.C * Wp;
@@ -593,6 +621,12 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
         mp.nku = (int)npq;
         mp.zoff = (int)body;
         pl.gather = 1;
+        // a half-wave reads 32 consecutive channels of one image pixel
+        pl.asg.G1 = s.N * Hp * Wp; pl.asg.S1 = s.C;
+        pl.asg.E = s.C;
+        pl.asg.G2 = (int)cdiv(s.C, 32); pl.asg.S2 = 32;
+        pl.asg.G3 = 1; pl.asg.S3 = 0;
+        pl.asg.LS = 1; pl.asg.O = 0;
     }
     return run_plan(pl, dev, stream, image, M);
 }
@@ -608,15 +642,24 @@ extern "C" int approx_lut_load(const uint16_t* lut, int M)
     int dev = 0;
     int rc = current_device(&dev);
     if (rc != APPROX_OK) return rc;
-    // lane-first image: column ib holds entries (ia, ib) for ia = 0..2^M-1, then two zeros
-    // followed (256-byte aligned) by the table in index order for the row-vector kernel
+    // lane-first image: column ib holds entries (ia, ib) for ia = 0..2^M-1 and
+    // two zeros (at M = 8 also the second copies of replica.h); then (256-byte
+    // aligned) the table in index order for the row-vector kernel
     const int side = 1 << M, cs = amx::lut_col_entries(M);
-    const size_t img_entries = (size_t)side * cs;
+    const size_t img_entries = (size_t)amx::lut_image_bytes(M) / 2;
     const size_t flat_at = (img_entries + 127) & ~(size_t)127;   // entries
     const size_t entries = (size_t)1 << (2 * M);
     std::vector<uint16_t> img(flat_at + entries + 8, 0);   // + a zero entry (and padding) after the table
     for (int ib = 0; ib < side; ++ib)
-        for (int ia = 0; ia < side; ++ia) img[(size_t)ib * cs + ia] = lut[((size_t)ia << M) | ib];
+        for (int ia = 0; ia < side; ++ia) {
+            const uint16_t e = lut[((size_t)ia << M) | ib];
+            if (M == 8) {                                  // and the second copy of dwords 0..30
+                img[((size_t)ib * cs * 2 + amx::rep8_offset((uint32_t)ia, 0)) / 2] = e;
+                if ((ia >> 1) < amx::kRep8Slots) img[((size_t)ib * cs * 2 + amx::rep8_offset((uint32_t)ia, 1)) / 2] = e;
+            } else {
+                img[(size_t)ib * cs + ia] = e;
+            }
+        }
     std::memcpy(img.data() + flat_at, lut, entries * sizeof(uint16_t));
     uint16_t* d = nullptr;
     if (hipMalloc(&d, img.size() * sizeof(uint16_t)) != hipSuccess) return APPROX_EHIP;

@@ -4,13 +4,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "replica.h"
+
 namespace amx {
 
 // Decoded operand word, one per FP32 element, written by the decode pass and
 // read by the GEMM kernel. Two roles:
-//  - lane operand (varies across the 64 lanes of a wave): w = byte offset of
-//    its mantissa row inside a table column (2 * index), or of the column's
-//    zero pad entry for zero / subnormal / Inf / NaN;
+//  - lane operand (varies across the 64 lanes of a wave): w = byte offset,
+//    relative to a table column, of its mantissa row (2 * index as the decode
+//    writes it; at M = 8 the copy choice may move it to the row's second
+//    copy, replica.h), or of the column's zero pad entry for zero /
+//    subnormal / Inf / NaN;
 //  - uniform operand (the same for every lane at a given step): w = byte
 //    offset of its table column.
 // se = sign | exponent bits for normals (the float +-2^(E-127) * 2^0 with the
@@ -32,16 +36,19 @@ struct KernelShape {
 constexpr KernelShape kShapes[2] = {{8, 4}, {12, 3}};
 constexpr int kColsPerWave = 16;
 
-// Table image in device memory, laid out as the LDS copy the kernels use:
-// column c holds the 2^M entries of one uniform-operand mantissa followed by
-// two zero entries (the pad). Column stride = (2^M + 2) entries.
-inline int lut_col_entries(int M) { return (1 << M) + 2; }
-inline int lut_image_bytes(int M) { return (1 << M) * lut_col_entries(M) * 2; }
+// Table image in device memory, laid out as the LDS copy the kernels use.
+// A column holds the 2^M entries of one uniform-operand mantissa (lane
+// operand's mantissa = row) followed by two zero entries (the pad, read by
+// zero, Inf and NaN lane operands). An M = 8 column is 640 bytes: its 256
+// entries, the pad and second copies of its first 31 dwords (replica.h).
+__host__ __device__ inline int lut_col_entries(int M) { return M == 8 ? kRep8ColBytes / 2 : (1 << M) + 2; }
+__host__ __device__ inline int lut_col_bytes(int M) { return lut_col_entries(M) * 2; }
+__host__ __device__ inline int lut_image_bytes(int M) { return (1 << M) * lut_col_bytes(M); }
 
 // LDS footprint classes of the GEMM kernel (tables of M = 9..11 are read
 // from global memory instead).
 constexpr int LDS_SMALL = (1 << 7) * ((1 << 7) + 2) * 2;  // M <= 7: 33,280 bytes
-constexpr int LDS_LARGE = (1 << 8) * ((1 << 8) + 2) * 2;  // M == 8: 132,096 bytes
+constexpr int LDS_LARGE = (1 << 8) * kRep8ColBytes;       // M == 8: 163,840 bytes (all of the LDS)
 
 enum Layout : int {
     L_DENSE_LANE = 0,    // A of a GEMM -> [batch][KB][Mp][4]
@@ -146,6 +153,20 @@ struct MainParams {
     int force_checked;        // 1: always use the per-product checked path
 };
 
+// Copy choice of the M = 8 lane-operand table offsets (replica.h), one group
+// of up to 32 Words per thread: group (b, g1, g2, g3) holds the Words at
+//   panel + b * batch_stride + g1 * S1 + g2 * S2 + g3 * S3 + O + l * LS
+// for l < min(32, E - 32 * g2): the operands one half-wave of the GEMM
+// kernel reads together at one reduction index.
+struct AssignParams {
+    Word* panel;
+    int64_t batch_stride;
+    int64_t S1;
+    int batch, G1, G2, G3;
+    int S2, S3, LS, O, E;
+    uint32_t pad_w;        // offset of the zero pad entry
+};
+
 struct ReduceParams {
     const float* ws;
     float* out;
@@ -184,6 +205,7 @@ int gemv_blocks_per_cu(int variant);
 hipError_t launch_gemv(const GemvParams& p, int variant, int grid, hipStream_t s);
 hipError_t launch_init_stats(int* stats, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+hipError_t launch_assign(const AssignParams& p, hipStream_t s);
 hipError_t launch_main(const MainParams& p, int lds_class, int gather, int shape, int grid, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_fill_zero(float* C, float* const* Cp, int m, int n, int ldc, int batch, int64_t strideC,

@@ -51,8 +51,8 @@ __device__ __forceinline__ Word decode_bits(uint32_t bits, int M, int lane_role,
     const uint32_t e = (bits >> 23) & 0xFFu;
     const uint32_t frac = bits & 0x7FFFFFu;
     const uint32_t idx = frac >> (23 - M);
-    const uint32_t pad = (1u << M) * 2u;            // zero entry at the end of a column
-    const uint32_t colb = ((1u << M) + 2u) * 2u;    // column stride in bytes
+    const uint32_t pad = (1u << M) * 2u;            // zero entry after the column's 2^M entries
+    const uint32_t colb = (uint32_t)lut_col_bytes(M);   // column stride in bytes
     Word o;
     if (e == 0u) {                                  // zero or subnormal (counts as zero)
         o.se = 0u;
@@ -359,6 +359,35 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeParams p)
         }
     }
     flush_stats(p.stats, emin, emax);
+}
+
+// Copy choice for the M = 8 lane operands (replica.h): one thread per group
+// of up to 32 Words that one half-wave of the GEMM kernel reads at one
+// reduction index; moves some of their table offsets to the rows' second
+// copies so that the group's lookups spread over the LDS banks.
+constexpr int kAssignThreads = 256;
+
+__global__ __launch_bounds__(kAssignThreads) void assign_kernel(AssignParams p)
+{
+    const int64_t groups = (int64_t)p.batch * p.G1 * p.G2 * p.G3;
+    for (int64_t g = (int64_t)blockIdx.x * kAssignThreads + threadIdx.x; g < groups;
+         g += (int64_t)gridDim.x * kAssignThreads) {
+        int64_t r = g;
+        const int g3 = (int)(r % p.G3);
+        r /= p.G3;
+        const int g2 = (int)(r % p.G2);
+        r /= p.G2;
+        const int64_t g1 = r % p.G1, b = r / p.G1;
+        Word* base = p.panel + b * p.batch_stride + g1 * p.S1 + (int64_t)g2 * p.S2 + (int64_t)g3 * p.S3 + p.O;
+        const int count = min(32, p.E - g2 * 32);
+        uint32_t w[32], w0[32];
+#pragma unroll
+        for (int l = 0; l < 32; ++l) w0[l] = w[l] = l < count ? base[(int64_t)l * p.LS].w : p.pad_w;
+        rep8_assign_group(w, count, p.pad_w);
+#pragma unroll
+        for (int l = 0; l < 32; ++l)
+            if (l < count && w[l] != w0[l]) base[(int64_t)l * p.LS].w = w[l];
+    }
 }
 
 // ------------------------------------------------------------------ products
@@ -742,9 +771,11 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
     const unsigned char* lut;
     if constexpr (GTAB) lut = reinterpret_cast<const unsigned char*>(p.lut);
     else lut = lds_tab;
-    __shared__ int range[4];
-    if (threadIdx.x < 64) {                       // wave 0 folds the stats slots
-        const int* sl = p.stats + (threadIdx.x % STAT_SLOTS) * STAT_STRIDE;
+    // every wave folds the stats slots itself (the table takes all of the
+    // LDS at M = 8, so the range is not broadcast through it)
+    int a_min, a_max, b_min, b_max;
+    {
+        const int* sl = p.stats + ((threadIdx.x & 63) % STAT_SLOTS) * STAT_STRIDE;
         int v0 = sl[0], v1 = sl[1], v2 = sl[2], v3 = sl[3];
         for (int off = 32; off > 0; off >>= 1) {
             v0 = min(v0, __shfl_xor(v0, off, 64));
@@ -752,10 +783,12 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
             v2 = min(v2, __shfl_xor(v2, off, 64));
             v3 = max(v3, __shfl_xor(v3, off, 64));
         }
-        if (threadIdx.x == 0) { range[0] = v0; range[1] = v1; range[2] = v2; range[3] = v3; }
+        a_min = __builtin_amdgcn_readfirstlane(v0);
+        a_max = __builtin_amdgcn_readfirstlane(v1);
+        b_min = __builtin_amdgcn_readfirstlane(v2);
+        b_max = __builtin_amdgcn_readfirstlane(v3);
     }
-    __syncthreads();
-    const int a_min = range[0], a_max = range[1], b_min = range[2], b_max = range[3];
+    __syncthreads();                               // the table is staged
     const bool fast = NATIVE || (!p.force_checked &&
                       ((a_min > a_max) || (b_min > b_max) ||
                        (a_min + b_min - 127 >= 1 && a_max + b_max - 126 <= 254 && a_max <= 253)));
@@ -1082,6 +1115,14 @@ static int grid_for(int64_t work, int per_block, int cap)
 hipError_t launch_init_stats(int* stats, hipStream_t s)
 {
     hipLaunchKernelGGL(init_stats_kernel, dim3(1), dim3(256), 0, s, stats);
+    return hipGetLastError();
+}
+
+hipError_t launch_assign(const AssignParams& p, hipStream_t s)
+{
+    const int64_t groups = (int64_t)p.batch * p.G1 * p.G2 * p.G3;
+    if (groups <= 0) return hipSuccess;
+    hipLaunchKernelGGL(assign_kernel, dim3(grid_for(groups, kAssignThreads, 65536)), dim3(kAssignThreads), 0, s, p);
     return hipGetLastError();
 }
 
