@@ -8,8 +8,8 @@ The arithmetic lives in ``oracle.c`` (plain C99, single-threaded, double
 accumulation); this module only builds and loads it and marshals numpy arrays.
 Sources: "ApproxTrain: Fast Simulation of Approximate Multipliers for DNN
 Training and Inference" (arXiv 2209.04161) -- Section V-A Algorithm 1 (table
-generation), Section V Algorithm 2 (AMSim product), Section VI-B Algorithms 3-4
-(Conv2D forward and backprop).
+generation), Section V Algorithm 2 (AMSim product; the (1, e, m) formats with
+an exponent cast), Section VI-B Algorithms 3-4 (Conv2D forward and backprop).
 """
 import ctypes
 import os
@@ -56,16 +56,20 @@ def lib():
         L.orc_lut_perturb.restype = None
         L.orc_amsim_bits.argtypes = [ctypes.c_uint32, ctypes.c_uint32, vp, c_int]
         L.orc_amsim_bits.restype = ctypes.c_uint32
-        L.orc_amsim_many.argtypes = [c_i64, vp, vp, vp, c_int, vp]
+        L.orc_amsim_bits_fmt.argtypes = [ctypes.c_uint32, ctypes.c_uint32, vp, c_int, c_int]
+        L.orc_amsim_bits_fmt.restype = ctypes.c_uint32
+        L.orc_cast_bits.argtypes = [ctypes.c_uint32, c_int]
+        L.orc_cast_bits.restype = ctypes.c_uint32
+        L.orc_amsim_many.argtypes = [c_i64, vp, vp, vp, c_int, c_int, vp]
         L.orc_amsim_many.restype = None
-        L.orc_gemm.argtypes = [c_int] * 5 + [vp, c_int, vp, c_int, vp, c_int, vp, vp]
+        L.orc_gemm.argtypes = [c_int] * 5 + [vp, c_int, vp, c_int, vp, c_int, c_int, vp, vp]
         L.orc_gemm.restype = None
-        L.orc_gemm_at.argtypes = [c_int] * 5 + [vp, c_int, vp, c_int, vp, c_int,
+        L.orc_gemm_at.argtypes = [c_int] * 5 + [vp, c_int, vp, c_int, vp, c_int, c_int,
                                                  c_i64, vp, vp, vp, vp]
         L.orc_gemm_at.restype = None
         for name in ("orc_conv2d_fwd", "orc_conv2d_dgrad", "orc_conv2d_wgrad"):
             f = getattr(L, name)
-            f.argtypes = [c_int] * 11 + [vp, vp, vp, c_int, c_i64, vp, vp, vp]
+            f.argtypes = [c_int] * 11 + [vp, vp, vp, c_int, c_int, c_i64, vp, vp, vp]
             f.restype = None
         _lib = L
     return _lib
@@ -121,22 +125,30 @@ def lut_perturb(M, lut, delta):
 
 # ---------------------------------------------------------------- products
 
-def amsim_bits(a_bits, b_bits, lut, M):
-    """Algorithm 2 element-wise on uint32 bit patterns (same shapes)."""
+def amsim_bits(a_bits, b_bits, lut, M, E=8):
+    """Algorithm 2 element-wise on uint32 bit patterns (same shapes), in the
+    format (1, E, M): operands cast to E exponent bits first (E = 8: FP32)."""
     a = np.ascontiguousarray(a_bits, dtype=np.uint32).ravel()
     b = np.ascontiguousarray(b_bits, dtype=np.uint32).ravel()
     assert a.size == b.size
     lut = np.ascontiguousarray(lut, dtype=np.uint16)
     out = np.empty_like(a)
-    lib().orc_amsim_many(a.size, _ptr(a), _ptr(b), _ptr(lut), M, _ptr(out))
+    lib().orc_amsim_many(a.size, _ptr(a), _ptr(b), _ptr(lut), M, E, _ptr(out))
     return out.reshape(np.shape(a_bits))
 
 
-def amsim(a, b, lut, M):
+def amsim(a, b, lut, M, E=8):
     """Algorithm 2 on float32 arrays; returns float32."""
     a = _f32(a)
     b = _f32(b)
-    return amsim_bits(a.view(np.uint32), b.view(np.uint32), lut, M).view(np.float32)
+    return amsim_bits(a.view(np.uint32), b.view(np.uint32), lut, M, E).view(np.float32)
+
+
+def cast_bits(x_bits, E):
+    """The exponent cast of FP32 bit patterns to E exponent bits."""
+    f = lib().orc_cast_bits
+    x = np.ascontiguousarray(x_bits, dtype=np.uint32).ravel()
+    return np.array([f(int(v), E) for v in x], dtype=np.uint32).reshape(np.shape(x_bits))
 
 
 def mul_native(a, b):
@@ -149,10 +161,11 @@ def mul_native(a, b):
 
 # ---------------------------------------------------------------- GEMM
 
-def gemm(A, B, lut, M, transA=False, transB=False):
+def gemm(A, B, lut, M, transA=False, transB=False, E=8):
     """R = sum of approximate products (float64) and S = sum of their
     magnitudes, for op(A) @ op(B). A and B are 2-D float32 arrays stored
-    row-major (op = transpose of the stored matrix when trans is set)."""
+    row-major (op = transpose of the stored matrix when trans is set).
+    E: exponent bits of the multiplier's format (8 = FP32)."""
     A = _f32(A)
     B = _f32(B)
     m = A.shape[1] if transA else A.shape[0]
@@ -164,11 +177,11 @@ def gemm(A, B, lut, M, transA=False, transB=False):
     S = np.zeros((m, n), dtype=np.float64)
     t, tp, M = _table(lut, M)
     lib().orc_gemm(int(transA), int(transB), m, n, k, _ptr(A), A.shape[1],
-                   _ptr(B), B.shape[1], tp, M, _ptr(R), _ptr(S))
+                   _ptr(B), B.shape[1], tp, M, E, _ptr(R), _ptr(S))
     return R, S
 
 
-def gemm_at(A, B, lut, M, rows, cols, transA=False, transB=False):
+def gemm_at(A, B, lut, M, rows, cols, transA=False, transB=False, E=8):
     """The same sums at the (rows[t], cols[t]) outputs only."""
     A = _f32(A)
     B = _f32(B)
@@ -182,7 +195,7 @@ def gemm_at(A, B, lut, M, rows, cols, transA=False, transB=False):
     S = np.zeros(rows.size, dtype=np.float64)
     t, tp, M = _table(lut, M)
     lib().orc_gemm_at(int(transA), int(transB), m, n, k, _ptr(A), A.shape[1],
-                      _ptr(B), B.shape[1], tp, M, rows.size,
+                      _ptr(B), B.shape[1], tp, M, E, rows.size,
                       _ptr(rows), _ptr(cols), _ptr(R), _ptr(S))
     return R, S
 
@@ -195,7 +208,7 @@ def conv_out_hw(H, W, R, S, stride, pad):
     return (H + 2 * ph - R) // sh + 1, (W + 2 * pw - S) // sw + 1
 
 
-def _conv(name, shape_out, geomargs, t1, t2, lut, M, idx):
+def _conv(name, shape_out, geomargs, t1, t2, lut, M, idx, E=8):
     t1 = _f32(t1)
     t2 = _f32(t2)
     t, tp, M = _table(lut, M)
@@ -203,28 +216,28 @@ def _conv(name, shape_out, geomargs, t1, t2, lut, M, idx):
         total = int(np.prod(shape_out))
         R = np.zeros(total, dtype=np.float64)
         S = np.zeros(total, dtype=np.float64)
-        getattr(lib(), name)(*geomargs, _ptr(t1), _ptr(t2), tp, M, 0, None,
+        getattr(lib(), name)(*geomargs, _ptr(t1), _ptr(t2), tp, M, E, 0, None,
                              _ptr(R), _ptr(S))
         return R.reshape(shape_out), S.reshape(shape_out)
     idx = np.ascontiguousarray(idx, dtype=np.int64)
     R = np.zeros(idx.size, dtype=np.float64)
     S = np.zeros(idx.size, dtype=np.float64)
-    getattr(lib(), name)(*geomargs, _ptr(t1), _ptr(t2), tp, M, idx.size,
+    getattr(lib(), name)(*geomargs, _ptr(t1), _ptr(t2), tp, M, E, idx.size,
                          _ptr(idx), _ptr(R), _ptr(S))
     return R, S
 
 
-def conv2d_fwd(x, w, lut, M, stride=(1, 1), pad=(0, 0), idx=None):
+def conv2d_fwd(x, w, lut, M, stride=(1, 1), pad=(0, 0), idx=None, E=8):
     """x: NHWC, w: RSCK. Returns (Y, YS) of shape NPQK (or at flat idx)."""
     N, H, W, C = x.shape
     R, S, C2, K = w.shape
     assert C == C2
     P, Q = conv_out_hw(H, W, R, S, stride, pad)
     g = (N, H, W, C, K, R, S, stride[0], stride[1], pad[0], pad[1])
-    return _conv("orc_conv2d_fwd", (N, P, Q, K), g, x, w, lut, M, idx)
+    return _conv("orc_conv2d_fwd", (N, P, Q, K), g, x, w, lut, M, idx, E)
 
 
-def conv2d_dgrad(dy, w, x_shape, lut, M, stride=(1, 1), pad=(0, 0), idx=None):
+def conv2d_dgrad(dy, w, x_shape, lut, M, stride=(1, 1), pad=(0, 0), idx=None, E=8):
     """dy: NPQK, w: RSCK, x_shape = (N, H, W, C). Returns (dX, dXS)."""
     N, H, W, C = x_shape
     R, S, C2, K = w.shape
@@ -232,10 +245,10 @@ def conv2d_dgrad(dy, w, x_shape, lut, M, stride=(1, 1), pad=(0, 0), idx=None):
     P, Q = conv_out_hw(H, W, R, S, stride, pad)
     assert dy.shape == (N, P, Q, K)
     g = (N, H, W, C, K, R, S, stride[0], stride[1], pad[0], pad[1])
-    return _conv("orc_conv2d_dgrad", (N, H, W, C), g, dy, w, lut, M, idx)
+    return _conv("orc_conv2d_dgrad", (N, H, W, C), g, dy, w, lut, M, idx, E)
 
 
-def conv2d_wgrad(x, dy, w_shape, lut, M, stride=(1, 1), pad=(0, 0), idx=None):
+def conv2d_wgrad(x, dy, w_shape, lut, M, stride=(1, 1), pad=(0, 0), idx=None, E=8):
     """x: NHWC, dy: NPQK, w_shape = (R, S, C, K). Returns (dW, dWS)."""
     N, H, W, C = x.shape
     R, S, C2, K = w_shape
@@ -243,4 +256,4 @@ def conv2d_wgrad(x, dy, w_shape, lut, M, stride=(1, 1), pad=(0, 0), idx=None):
     P, Q = conv_out_hw(H, W, R, S, stride, pad)
     assert dy.shape == (N, P, Q, K)
     g = (N, H, W, C, K, R, S, stride[0], stride[1], pad[0], pad[1])
-    return _conv("orc_conv2d_wgrad", (R, S, C, K), g, x, dy, lut, M, idx)
+    return _conv("orc_conv2d_wgrad", (R, S, C, K), g, x, dy, lut, M, idx, E)

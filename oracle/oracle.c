@@ -49,6 +49,17 @@
  *       hardware multiplication instead of the table, the reference point
  *       of Fig. 6) is the exact product of the two floats, rounded only when
  *       it is added to a sum. The sums take it when no table is given.
+ *   R11 Formats (1, E, M) with E = 1..8 exponent bits (Section V: "the bits
+ *       of the exponent e can be varied from 1 to 8 provided that a proper
+ *       exponent casting function is given"; the pages give no cast). The
+ *       format's exponent has bias b = 2^(E-1) - 1 and normal unbiased
+ *       exponents 1-b .. b, IEEE style, without subnormals (the table
+ *       assumes a hidden 1). Cast of an operand: a normal FP32 value whose
+ *       unbiased exponent is below 1-b becomes a signed zero, above b a
+ *       signed infinity; zero, Inf and NaN stay. Algorithm 2's underflow and
+ *       overflow tests then use the format's range: the product's unbiased
+ *       exponent (with the carry) below 1-b gives a signed zero, above b a
+ *       signed infinity. E = 8 is FP32's range, so nothing changes there.
  *
  * Build: gcc -O2 -std=c99 -fPIC -shared -ffp-contract=off oracle.c -lm
  */
@@ -146,10 +157,30 @@ void orc_lut_perturb(int M, uint16_t *lut, const int8_t *delta)
 }
 
 /* ------------------------------------------------------------------ */
+/* Exponent cast to a (1, E, M) format (reading R11)                   */
+/* ------------------------------------------------------------------ */
+/* FP32 biased exponents of the format's normal range: lowest and highest. */
+static int fmt_lo(int E) { return 127 + 1 - ((1 << (E - 1)) - 1); }
+static int fmt_hi(int E) { return 127 + ((1 << (E - 1)) - 1); }
+
+uint32_t orc_cast_bits(uint32_t x, int E)
+{
+    uint32_t e = exp_of(x);
+    if (e == 0 || e == 255) return x;                              /* zero, subnormal, Inf, NaN */
+    if ((int)e < fmt_lo(E)) return sign_of(x) << 31;               /* below the format: zero */
+    if ((int)e > fmt_hi(E)) return (sign_of(x) << 31) | 0x7F800000u;   /* above: infinity */
+    return x;
+}
+
+/* ------------------------------------------------------------------ */
 /* Algorithm 2: AMSim, one approximate product (Section V)             */
 /* ------------------------------------------------------------------ */
-uint32_t orc_amsim_bits(uint32_t a, uint32_t b, const uint16_t *lut, int M)
+/* The product of a and b in the format (1, E, M): both operands are cast to
+ * the format first (R11), then Algorithm 2 runs with the format's range. */
+uint32_t orc_amsim_bits_fmt(uint32_t a, uint32_t b, const uint16_t *lut, int M, int E)
 {
+    a = orc_cast_bits(a, E);
+    b = orc_cast_bits(b, E);
     /* extract the mantissas (top M fraction bits) and form the index */
     uint32_t mant_a = frac_of(a) >> (23 - M);
     uint32_t mant_b = frac_of(b) >> (23 - M);
@@ -172,11 +203,18 @@ uint32_t orc_amsim_bits(uint32_t a, uint32_t b, const uint16_t *lut, int M)
     }
     if (a_zero || b_zero) return sign << 31;
 
-    /* normal case: biased exponent with the carry (reading R4) */
+    /* normal case: biased exponent with the carry (reading R4), tested
+     * against the format's range (R11; FP32: 1..254) */
     int e = (int)ea + (int)eb - 127 + (int)carry;
-    if (e <= 0) return sign << 31;
-    if (e >= 255) return (sign << 31) | 0x7F800000u;
+    if (e < fmt_lo(E)) return sign << 31;
+    if (e > fmt_hi(E)) return (sign << 31) | 0x7F800000u;
     return (sign << 31) | ((uint32_t)e << 23) | (mantissa << 8);
+}
+
+/* FP32 operands (E = 8) */
+uint32_t orc_amsim_bits(uint32_t a, uint32_t b, const uint16_t *lut, int M)
+{
+    return orc_amsim_bits_fmt(a, b, lut, M, 8);
 }
 
 float orc_amsim(float a, float b, const uint16_t *lut, int M)
@@ -192,19 +230,20 @@ float orc_amsim(float a, float b, const uint16_t *lut, int M)
  * double's normal range. Inf * 0 and NaN inputs give NaN, as in IEEE-754. */
 double orc_mul_native(float a, float b) { return (double)a * (double)b; }
 
-/* the product the sums below use: Algorithm 2 with a table, the native
- * multiplier when there is none (lut == NULL) */
-static double product(float a, float b, const uint16_t *lut, int M)
+/* the product the sums below use: Algorithm 2 with a table in the format
+ * (1, E, M), the native multiplier when there is none (lut == NULL; E is
+ * then unused) */
+static double product(float a, float b, const uint16_t *lut, int M, int E)
 {
     if (lut == NULL) return orc_mul_native(a, b);
-    return (double)orc_amsim(a, b, lut, M);
+    return (double)float_of(orc_amsim_bits_fmt(bits_of(a), bits_of(b), lut, M, E));
 }
 
 /* element-wise products of two bit arrays (for exhaustive checks) */
 void orc_amsim_many(int64_t count, const uint32_t *a, const uint32_t *b,
-                    const uint16_t *lut, int M, uint32_t *out)
+                    const uint16_t *lut, int M, int E, uint32_t *out)
 {
-    for (int64_t t = 0; t < count; ++t) out[t] = orc_amsim_bits(a[t], b[t], lut, M);
+    for (int64_t t = 0; t < count; ++t) out[t] = orc_amsim_bits_fmt(a[t], b[t], lut, M, E);
 }
 
 /* ------------------------------------------------------------------ */
@@ -215,13 +254,13 @@ void orc_amsim_many(int64_t count, const uint32_t *a, const uint32_t *b,
  * product is op(A)(i,p), the second op(B)(p,j) (reading R3). */
 static void gemm_one(int transA, int transB, int i, int j, int k,
                      const float *A, long lda, const float *B, long ldb,
-                     const uint16_t *lut, int M, double *r, double *s)
+                     const uint16_t *lut, int M, int E, double *r, double *s)
 {
     double sum = 0.0, abs_sum = 0.0;
     for (int p = 0; p < k; ++p) {
         float a = transA ? A[(long)p * lda + i] : A[(long)i * lda + p];
         float b = transB ? B[(long)j * ldb + p] : B[(long)p * ldb + j];
-        double prod = product(a, b, lut, M);
+        double prod = product(a, b, lut, M, E);
         sum += prod;
         abs_sum += fabs(prod);
     }
@@ -231,24 +270,24 @@ static void gemm_one(int transA, int transB, int i, int j, int k,
 
 void orc_gemm(int transA, int transB, int m, int n, int k,
               const float *A, int lda, const float *B, int ldb,
-              const uint16_t *lut, int M, double *R, double *S)
+              const uint16_t *lut, int M, int E, double *R, double *S)
 {
     for (int i = 0; i < m; ++i)
         for (int j = 0; j < n; ++j)
-            gemm_one(transA, transB, i, j, k, A, lda, B, ldb, lut, M,
+            gemm_one(transA, transB, i, j, k, A, lda, B, ldb, lut, M, E,
                      &R[(long)i * n + j], &S[(long)i * n + j]);
 }
 
 /* the same sums at chosen (row, column) pairs only */
 void orc_gemm_at(int transA, int transB, int m, int n, int k,
                  const float *A, int lda, const float *B, int ldb,
-                 const uint16_t *lut, int M,
+                 const uint16_t *lut, int M, int E,
                  int64_t count, const int32_t *rows, const int32_t *cols,
                  double *R, double *S)
 {
     (void)m; (void)n;
     for (int64_t t = 0; t < count; ++t)
-        gemm_one(transA, transB, rows[t], cols[t], k, A, lda, B, ldb, lut, M, &R[t], &S[t]);
+        gemm_one(transA, transB, rows[t], cols[t], k, A, lda, B, ldb, lut, M, E, &R[t], &S[t]);
 }
 
 /* ------------------------------------------------------------------ */
@@ -293,7 +332,7 @@ static float w_at(const geom *g, const float *w, int r, int s, int c, int k)
 
 /* forward: y[n,p,q,k] = sum_{r,s,c} approx(x[n, p*sh-ph+r, q*sw-pw+s, c], w[r,s,c,k]) */
 static void fwd_one(const geom *g, const float *x, const float *w, long idx,
-                    const uint16_t *lut, int M, double *r_out, double *s_out)
+                    const uint16_t *lut, int M, int E, double *r_out, double *s_out)
 {
     int k = (int)(idx % g->K); idx /= g->K;
     int q = (int)(idx % g->Q); idx /= g->Q;
@@ -304,7 +343,7 @@ static void fwd_one(const geom *g, const float *x, const float *w, long idx,
         for (int s = 0; s < g->S; ++s)
             for (int c = 0; c < g->C; ++c) {
                 float a = x_at(g, x, n, p * g->sh - g->ph + r, q * g->sw - g->pw + s, c);
-                double prod = product(a, w_at(g, w, r, s, c, k), lut, M);
+                double prod = product(a, w_at(g, w, r, s, c, k), lut, M, E);
                 sum += prod;
                 abs_sum += fabs(prod);
             }
@@ -316,7 +355,7 @@ static void fwd_one(const geom *g, const float *x, const float *w, long idx,
  * dx[n,h,w,c] = sum_{r,s,k} approx(D[n, h+ph-r, w+pw-s, k], w[r,s,c,k])
  * with D the padded, dilated errors above. */
 static void dgrad_one(const geom *g, const float *dy, const float *w, long idx,
-                      const uint16_t *lut, int M, double *r_out, double *s_out)
+                      const uint16_t *lut, int M, int E, double *r_out, double *s_out)
 {
     int c = (int)(idx % g->C); idx /= g->C;
     int ww = (int)(idx % g->W); idx /= g->W;
@@ -327,7 +366,7 @@ static void dgrad_one(const geom *g, const float *dy, const float *w, long idx,
         for (int s = 0; s < g->S; ++s)
             for (int k = 0; k < g->K; ++k) {
                 float a = dilated_dy_at(g, dy, n, h + g->ph - r, ww + g->pw - s, k);
-                double prod = product(a, w_at(g, w, r, s, c, k), lut, M);
+                double prod = product(a, w_at(g, w, r, s, c, k), lut, M, E);
                 sum += prod;
                 abs_sum += fabs(prod);
             }
@@ -338,7 +377,7 @@ static void dgrad_one(const geom *g, const float *dy, const float *w, long idx,
 /* weight gradient:
  * dw[r,s,c,k] = sum_{n,p,q} approx(x[n, p*sh-ph+r, q*sw-pw+s, c], dy[n,p,q,k]) */
 static void wgrad_one(const geom *g, const float *x, const float *dy, long idx,
-                      const uint16_t *lut, int M, double *r_out, double *s_out)
+                      const uint16_t *lut, int M, int E, double *r_out, double *s_out)
 {
     int k = (int)(idx % g->K); idx /= g->K;
     int c = (int)(idx % g->C); idx /= g->C;
@@ -350,7 +389,7 @@ static void wgrad_one(const geom *g, const float *x, const float *dy, long idx,
             for (int q = 0; q < g->Q; ++q) {
                 float a = x_at(g, x, n, p * g->sh - g->ph + r, q * g->sw - g->pw + s, c);
                 float b = dy[(((long)n * g->P + p) * g->Q + q) * g->K + k];
-                double prod = product(a, b, lut, M);
+                double prod = product(a, b, lut, M, E);
                 sum += prod;
                 abs_sum += fabs(prod);
             }
@@ -362,36 +401,36 @@ static void wgrad_one(const geom *g, const float *x, const float *dy, long idx,
  * indices into the NHWC / RSCK output). */
 void orc_conv2d_fwd(int N, int H, int W, int C, int K, int R, int S,
                     int sh, int sw, int ph, int pw,
-                    const float *x, const float *w, const uint16_t *lut, int M,
+                    const float *x, const float *w, const uint16_t *lut, int M, int E,
                     int64_t count, const int64_t *idx, double *Y, double *YS)
 {
     geom g = make_geom(N, H, W, C, K, R, S, sh, sw, ph, pw);
     long total = (long)N * g.P * g.Q * K;
     long cnt = idx ? (long)count : total;
     for (long t = 0; t < cnt; ++t)
-        fwd_one(&g, x, w, idx ? (long)idx[t] : t, lut, M, &Y[t], &YS[t]);
+        fwd_one(&g, x, w, idx ? (long)idx[t] : t, lut, M, E, &Y[t], &YS[t]);
 }
 
 void orc_conv2d_dgrad(int N, int H, int W, int C, int K, int R, int S,
                       int sh, int sw, int ph, int pw,
-                      const float *dy, const float *w, const uint16_t *lut, int M,
+                      const float *dy, const float *w, const uint16_t *lut, int M, int E,
                       int64_t count, const int64_t *idx, double *DX, double *DXS)
 {
     geom g = make_geom(N, H, W, C, K, R, S, sh, sw, ph, pw);
     long total = (long)N * H * W * C;
     long cnt = idx ? (long)count : total;
     for (long t = 0; t < cnt; ++t)
-        dgrad_one(&g, dy, w, idx ? (long)idx[t] : t, lut, M, &DX[t], &DXS[t]);
+        dgrad_one(&g, dy, w, idx ? (long)idx[t] : t, lut, M, E, &DX[t], &DXS[t]);
 }
 
 void orc_conv2d_wgrad(int N, int H, int W, int C, int K, int R, int S,
                       int sh, int sw, int ph, int pw,
-                      const float *x, const float *dy, const uint16_t *lut, int M,
+                      const float *x, const float *dy, const uint16_t *lut, int M, int E,
                       int64_t count, const int64_t *idx, double *DW, double *DWS)
 {
     geom g = make_geom(N, H, W, C, K, R, S, sh, sw, ph, pw);
     long total = (long)R * S * C * K;
     long cnt = idx ? (long)count : total;
     for (long t = 0; t < cnt; ++t)
-        wgrad_one(&g, x, dy, idx ? (long)idx[t] : t, lut, M, &DW[t], &DWS[t]);
+        wgrad_one(&g, x, dy, idx ? (long)idx[t] : t, lut, M, E, &DW[t], &DWS[t]);
 }

@@ -61,7 +61,7 @@ def test_gemm_with_leading_dimension_larger_than_columns():
     L = oracle.lib()
     Bc = np.ascontiguousarray(B)
     L.orc_gemm(0, 0, 20, 9, 13, oracle._ptr(big), 40, oracle._ptr(Bc), 9,
-               oracle._ptr(lut), M, oracle._ptr(Rf), oracle._ptr(Sf))
+               oracle._ptr(lut), M, 8, oracle._ptr(Rf), oracle._ptr(Sf))
     assert np.array_equal(R1, Rf) and np.array_equal(S1, Sf)
 
 
