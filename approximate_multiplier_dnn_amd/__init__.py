@@ -29,6 +29,7 @@ MODEL_MITCHELL = 1
 #: every function the C header declares
 EXPORTS = (
     "approx_lut_build", "approx_lut_build_from_model", "approx_lut_load", "approx_native_load", "approx_lut_bits",
+    "approx_exponent_bits_set", "approx_exponent_bits",
     "approx_gemm", "approx_gemm_strided_batched", "approx_gemm_batched",
     "approx_conv2d_fwd", "approx_conv2d_dgrad", "approx_conv2d_wgrad",
     "approx_profile_enable", "approx_profile_read",
@@ -46,6 +47,8 @@ _lib.approx_lut_build.argtypes = [_i, _i, _vp, _vp]
 _lib.approx_lut_build_from_model.argtypes = [_i, MUL_FN, _vp]
 _lib.approx_lut_load.argtypes = [_vp, _i]
 _lib.approx_lut_bits.argtypes = []
+_lib.approx_exponent_bits_set.argtypes = [_i]
+_lib.approx_exponent_bits.argtypes = []
 _lib.approx_gemm.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, _vp]
 _lib.approx_gemm_strided_batched.argtypes = [_i] * 5 + [_vp, _i, _ll, _vp, _i, _ll, _vp, _i, _ll, _i, _vp]
 _lib.approx_gemm_batched.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, _i, _vp]
@@ -119,6 +122,15 @@ def approx_native_load():
 
 def approx_lut_bits():
     return _lib.approx_lut_bits()
+
+
+def approx_exponent_bits_set(E):
+    """Exponent width E (1..8) of the multiplier's format (1, E, M) on the current device."""
+    _check(_lib.approx_exponent_bits_set(int(E)), "approx_exponent_bits_set")
+
+
+def approx_exponent_bits():
+    return _lib.approx_exponent_bits()
 
 
 def approx_release():

@@ -48,6 +48,7 @@ struct Arena {
 
 std::mutex g_mu;
 DeviceTable g_tables[kMaxDevices];
+int g_exp_bits[kMaxDevices];       // exponent width of the multiplier's format per device (0 = unset: 8)
 bool g_profile = false;
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events;   // GEMM-kernel launches while profiling
 std::map<std::pair<int, hipStream_t>, Arena> g_arenas;
@@ -118,6 +119,20 @@ int table_of(int dev, const uint16_t** image, int* M, const uint16_t** flat = nu
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The format (1, E, M)'s normal range as FP32 biased exponents: bias
+// b = 2^(E-1) - 1, unbiased exponents 1-b .. b. E = 8 gives 1 .. 254.
+void format_range(int dev, int* elo, int* ehi)
+{
+    int E;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        E = g_exp_bits[dev] ? g_exp_bits[dev] : 8;
+    }
+    const int bias = (1 << (E - 1)) - 1;
+    *elo = 128 - bias;
+    *ehi = 127 + bias;
+}
 
 // Waves of a workgroup of the given shape are arranged wr x wc (wr * wc =
 // waves): the arrangement whose tiles pad the m x n output least, the wider
@@ -240,6 +255,10 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     pl.lane.batch = pl.batch;
     pl.lane.lane_role = 1;
     pl.lane.M = M;
+    int elo, ehi;
+    format_range(dev, &elo, &ehi);
+    pl.lane.elo = pl.uni.elo = mp.elo = elo;
+    pl.lane.ehi = pl.uni.ehi = mp.ehi = ehi;
     pl.uni.dst = uni_panel;
     pl.uni.stats = stats + 2;
     pl.uni.count = pl.uni_count ? pl.uni_count : pl.uni_words;
@@ -425,6 +444,7 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
         g.lut = flat;
         g.out_ptrs = Cp; g.out_batch = strideC;
         g.M = M; g.m = m; g.n = n; g.k = k; g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.transA = transA;
+        format_range(dev, &g.elo, &g.ehi);
         return gemv_run(g, batch, C, dev, stream);
     }
 
@@ -692,6 +712,26 @@ extern "C" int approx_native_load(void)
     g_tables[dev] = DeviceTable{};
     g_tables[dev].native = true;
     return APPROX_OK;
+}
+
+extern "C" int approx_exponent_bits_set(int E)
+{
+    if (E < 1 || E > 8) return APPROX_EUNSUPPORTED;
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc != APPROX_OK) return rc;
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_exp_bits[dev] = E;
+    return APPROX_OK;
+}
+
+extern "C" int approx_exponent_bits(void)
+{
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc != APPROX_OK) return rc;
+    std::lock_guard<std::mutex> lock(g_mu);
+    return g_exp_bits[dev] ? g_exp_bits[dev] : 8;
 }
 
 extern "C" int approx_lut_bits(void)

@@ -97,6 +97,7 @@ struct DecodeParams {
     int layout;
     int lane_role;       // 1: lane operand, 0: uniform operand
     int M;
+    int elo, ehi;        // FP32 biased exponents of the format's normal range (1, 254 for FP32)
     // geometry (meaning depends on layout)
     int m, n, k, ld, trans;    // dense
     int Mp, Np, KB;            // padded extents
@@ -151,6 +152,7 @@ struct MainParams {
     int batch;
     int64_t items;
     int force_checked;        // 1: always use the per-product checked path
+    int elo, ehi;             // FP32 biased exponents of the format's normal range (1, 254 for FP32)
 };
 
 // Copy choice of the M = 8 lane-operand table offsets (replica.h), one group
@@ -195,6 +197,7 @@ struct GemvParams {
     int64_t A_batch, B_batch, out_batch;   // elements
     int M, m, n, k, lda, ldb, ldc, transA;
     int splits, chunk, batch;
+    int elo, ehi;                 // FP32 biased exponents of the format's normal range (1, 254 for FP32)
 };
 
 // variant: 0 = table of M <= 7 in LDS, 1 = M == 8 in LDS, 2 = table in global

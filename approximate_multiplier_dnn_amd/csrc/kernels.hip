@@ -43,11 +43,28 @@ typedef float __attribute__((address_space(1)))* gfloat_ptr;
 
 // ------------------------------------------------------------------ decode
 
+// Exponent cast of an FP32 operand to the multiplier's format (1, E, M)
+// (ApproxTrain Section V: exponent widths below 8 with a casting function):
+// a normal value whose biased exponent lies below elo becomes a signed zero,
+// above ehi a signed infinity; zero, subnormal, Inf and NaN are kept. The
+// identity for FP32's own range (elo = 1, ehi = 254).
+__device__ __forceinline__ uint32_t cast_fmt(uint32_t bits, int elo, int ehi)
+{
+    const int e = (int)((bits >> 23) & 0xFFu);
+    const uint32_t sign = bits & 0x80000000u;
+    bits = (e != 0 && e != 255 && e < elo) ? sign : bits;
+    bits = (e != 0 && e != 255 && e > ehi) ? (sign | 0x7F800000u) : bits;
+    return bits;
+}
+
 // M = 0 selects the native multiplier: the Word carries the operand's own
-// bits (se) and no table offset, and the exponent range is not gathered.
-__device__ __forceinline__ Word decode_bits(uint32_t bits, int M, int lane_role, int& emin, int& emax)
+// bits (se) and no table offset, and the exponent range is not gathered (nor
+// is the operand cast: the native multiplier is FP32).
+__device__ __forceinline__ Word decode_bits(uint32_t bits, int M, int lane_role, int& emin, int& emax, int elo,
+                                            int ehi)
 {
     if (M == 0) return Word{0u, bits};
+    bits = cast_fmt(bits, elo, ehi);
     const uint32_t e = (bits >> 23) & 0xFFu;
     const uint32_t frac = bits & 0x7FFFFFu;
     const uint32_t idx = frac >> (23 - M);
@@ -210,7 +227,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p)
         const int64_t s = decode_source(p, o);
         const uint32_t row = fdiv(o, p.fd_rowlen);
         dst[(int64_t)row * p.ldw + (o - row * (uint32_t)p.rowlen)] =
-            s >= 0 ? decode_bits(__float_as_uint(src[s]), p.M, p.lane_role, emin, emax) : zero_word(p.M, p.lane_role);
+            s >= 0 ? decode_bits(__float_as_uint(src[s]), p.M, p.lane_role, emin, emax, p.elo, p.ehi) : zero_word(p.M, p.lane_role);
     }
     flush_stats(p.stats, emin, emax);
 }
@@ -258,7 +275,7 @@ __global__ __launch_bounds__(256) void decode_img_kernel(DecodeParams p)
             const uint32_t cb = fdiv(q, p.fd_Wp);
             const int w = (int)(q - cb * (uint32_t)p.Wp) - p.pw, c = (int)(cb * 4u + t);
             out[o] = (srow >= 0 && c < p.C && w >= 0 && w < p.W)
-                         ? decode_bits(__float_as_uint(row[w * p.C + c]), p.M, p.lane_role, emin, emax)
+                         ? decode_bits(__float_as_uint(row[w * p.C + c]), p.M, p.lane_role, emin, emax, p.elo, p.ehi)
                          : zero_word(p.M, p.lane_role);
         }
     } else if (p.layout == L_IMG_DGRAD) {          // [Kb][Wd][4]
@@ -271,7 +288,7 @@ __global__ __launch_bounds__(256) void decode_img_kernel(DecodeParams p)
             bool ok = srow >= 0 && ko < p.K && ww >= 0 && (p.sw == 1 || ww % p.sw == 0);
             const int qq = !ok ? 0 : (p.sw == 1 ? ww : ww / p.sw);
             ok = ok && qq < p.Q;
-            out[o] = ok ? decode_bits(__float_as_uint(row[qq * p.K + ko]), p.M, p.lane_role, emin, emax)
+            out[o] = ok ? decode_bits(__float_as_uint(row[qq * p.K + ko]), p.M, p.lane_role, emin, emax, p.elo, p.ehi)
                         : zero_word(p.M, p.lane_role);
         }
     } else {                                       // L_IMG_WGRAD: [Wp][C]
@@ -281,7 +298,7 @@ __global__ __launch_bounds__(256) void decode_img_kernel(DecodeParams p)
             const uint32_t wq = fdiv((uint32_t)o, p.fd_C);
             const int c = (int)((uint32_t)o - wq * (uint32_t)p.C), w = (int)wq - p.pw;
             out[o] = (srow >= 0 && w >= 0 && w < p.W)
-                         ? decode_bits(__float_as_uint(row[w * p.C + c]), p.M, p.lane_role, emin, emax)
+                         ? decode_bits(__float_as_uint(row[w * p.C + c]), p.M, p.lane_role, emin, emax, p.elo, p.ehi)
                          : zero_word(p.M, p.lane_role);
         }
     }
@@ -318,7 +335,7 @@ __global__ __launch_bounds__(256) void decode_tile_kernel(DecodeParams p)
             const int kb = (k0 >> 2) + kbl;
             if (kb >= p.KB || oi >= p.Mp) continue;
             dst[(int64_t)kb * p.ldw + (int64_t)oi * 4 + t] =
-                (oi < p.m && ki < p.k) ? decode_bits(__float_as_uint(tile[i][kbl * 4 + t]), p.M, 1, emin, emax)
+                (oi < p.m && ki < p.k) ? decode_bits(__float_as_uint(tile[i][kbl * 4 + t]), p.M, 1, emin, emax, p.elo, p.ehi)
                                        : zero_word(p.M, 1);
         }
     } else {
@@ -328,7 +345,7 @@ __global__ __launch_bounds__(256) void decode_tile_kernel(DecodeParams p)
             const int oj = outer0 + j, ki = k0 + kk;
             if (ki >= p.KB * 4 || oj >= p.Np) continue;
             dst[(int64_t)ki * p.ldw + oj] =
-                (oj < p.n && ki < p.k) ? decode_bits(__float_as_uint(tile[j][kk]), p.M, 0, emin, emax)
+                (oj < p.n && ki < p.k) ? decode_bits(__float_as_uint(tile[j][kk]), p.M, 0, emin, emax, p.elo, p.ehi)
                                        : zero_word(p.M, 0);
         }
     }
@@ -354,7 +371,7 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeParams p)
     for (int kk = blockIdx.y; kk < rows_out; kk += gridDim.y) {
         if (j < p.Np) {
             dst[(int64_t)kk * p.ldw + j] = (kk < p.k && j < p.n)
-                ? decode_bits(__float_as_uint(src[(int64_t)kk * p.ld + j]), p.M, p.lane_role, emin, emax)
+                ? decode_bits(__float_as_uint(src[(int64_t)kk * p.ld + j]), p.M, p.lane_role, emin, emax, p.elo, p.ehi)
                 : zero_word(p.M, p.lane_role);
         }
     }
@@ -457,15 +474,17 @@ __device__ __forceinline__ void load_lane(const Word* panel, const uint32_t (&ba
 }
 
 // Checked path: Algorithm 2 with every special case, as selects (no
-// divergence), then acc + product.
-__device__ __forceinline__ float checked_product_acc(float acc, uint32_t e, uint32_t seA, uint32_t seB)
+// divergence), then acc + product. seA, seB: operands already cast to the
+// format; elo..ehi: the format's normal range of biased exponents.
+__device__ __forceinline__ float checked_product_acc(float acc, uint32_t e, uint32_t seA, uint32_t seB, int elo,
+                                                     int ehi)
 {
     const uint32_t ea = (seA >> 23) & 0xFFu, eb = (seB >> 23) & 0xFFu;
     const uint32_t sign = (seA ^ seB) & 0x80000000u;
     const int ex = (int)ea + (int)eb - 127 + (int)(e >> 15);
-    uint32_t bits = sign | ((uint32_t)ex << 23) | ((e & 0x7FFFu) << 8);
-    bits = ex >= 255 ? (sign | 0x7F800000u) : bits;           // overflow -> signed Inf
-    bits = ex <= 0 ? sign : bits;                              // underflow -> signed zero
+    uint32_t bits = sign | ((uint32_t)(ex & 0xFF) << 23) | ((e & 0x7FFFu) << 8);
+    bits = ex > ehi ? (sign | 0x7F800000u) : bits;             // overflow -> signed Inf
+    bits = ex < elo ? sign : bits;                             // underflow -> signed zero
     const bool zero = ea == 0u || eb == 0u;                    // zero or subnormal operand
     const bool a_inf = ea == 255u && (seA & 0x7FFFFFu) == 0u;
     const bool b_inf = eb == 255u && (seB & 0x7FFFFFu) == 0u;
@@ -592,7 +611,7 @@ __device__ __forceinline__ void native_index(const uint32_t (&sa)[RPL], const ui
 template <int RPL>
 __device__ __forceinline__ void checked_index(const uint32_t (&wa)[RPL], const uint32_t (&sa)[RPL],
                                               const uint32_t (&q)[UQ], const unsigned char* lut,
-                                              float (&acc)[RPL][CPW])
+                                              float (&acc)[RPL][CPW], int elo, int ehi)
 {
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
@@ -601,7 +620,7 @@ __device__ __forceinline__ void checked_index(const uint32_t (&wa)[RPL], const u
 #pragma unroll
         for (int x = 0; x < RPL; ++x) {
             const uint32_t e = *reinterpret_cast<const uint16_t*>(lut + (wa[x] + wb));
-            acc[x][j] = checked_product_acc(acc[x][j], e, sa[x], sb);
+            acc[x][j] = checked_product_acc(acc[x][j], e, sa[x], sb, elo, ehi);
             asm volatile("" : "+v"(acc[x][j]));
         }
     }
@@ -741,7 +760,7 @@ __device__ __forceinline__ void mainloop_checked(const MainParams& p, const Word
                 load_lane(panel, base, noff[0], wa[nxt], sa[nxt]);
                 load_uniform(bsrc + ((int64_t)kb + 1) * 4 * p.bld, quad, qb[nxt]);
             }
-            checked_index(wa[cur], sa[cur], qb[cur], lut, acc);
+            checked_index(wa[cur], sa[cur], qb[cur], lut, acc, p.elo, p.ehi);
         }
         if (more) {
 #pragma unroll
@@ -791,7 +810,7 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
     __syncthreads();                               // the table is staged
     const bool fast = NATIVE || (!p.force_checked &&
                       ((a_min > a_max) || (b_min > b_max) ||
-                       (a_min + b_min - 127 >= 1 && a_max + b_max - 126 <= 254 && a_max <= 253)));
+                       (a_min + b_min - 127 >= p.elo && a_max + b_max - 126 <= p.ehi && a_max <= 253)));
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const uint32_t quad = (uint32_t)lane & 3u;     // this lane's place in the uniform-word quads
     const int wrow = wave / p.wc, wcol = wave - wrow * p.wc;
@@ -908,8 +927,11 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
     int jc[kGemvColsPerLane];
 #pragma unroll
     for (int c = 0; c < kGemvColsPerLane; ++c) jc[c] = min(j0 + c * NTG, p.n - 1);
+    // operands cast to the multiplier's format as they are read (the native
+    // multiplier takes them as they are)
+    auto cast = [&](uint32_t bits) -> uint32_t { return NATIVE ? bits : cast_fmt(bits, p.elo, p.ehi); };
     auto a_at = [&](int r, int kk) -> uint32_t {
-        return __float_as_uint(p.transA ? A[(int64_t)kk * p.lda + r] : A[(int64_t)r * p.lda + kk]);
+        return cast(__float_as_uint(p.transA ? A[(int64_t)kk * p.lda + r] : A[(int64_t)r * p.lda + kk]));
     };
 #pragma unroll
     for (int r = 0; r < kGemvMaxRows; ++r)
@@ -932,9 +954,10 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
             emin = min(emin, __shfl_xor(emin, off, 64));
             emax = max(emax, __shfl_xor(emax, off, 64));
         }
-        // B exponents eb (normal) that keep every product normal
-        const int lo = emin > emax ? 1 : max(1, 128 - emin);
-        const int hi = emin > emax ? 253 : min(253, 380 - emax);
+        // B exponents eb (normal) that keep every product inside the format's
+        // range elo..ehi (and eb + carry below 255, for the fast assembly)
+        const int lo = emin > emax ? 1 : max(1, p.elo + 127 - emin);
+        const int hi = emin > emax ? 253 : min(253, p.ehi + 126 - emax);
         checked = lo > hi;
         if (!checked) {
             bool bad = false;
@@ -946,7 +969,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
                     const int kk = min(kg + g, k1 - 1);
                     const gfloat_cptr brow = B + (int64_t)kk * p.ldb;
 #pragma unroll
-                    for (int c = 0; c < kGemvColsPerLane; ++c) bw[g][c] = __float_as_uint(brow[jc[c]]);
+                    for (int c = 0; c < kGemvColsPerLane; ++c) bw[g][c] = cast(__float_as_uint(brow[jc[c]]));
 #pragma unroll
                     for (int r = 0; r < MR; ++r) xa[g][r] = a_at(r, kk);
                 }
@@ -994,7 +1017,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
             const int kk = min(kg + g, k1 - 1);
             const gfloat_cptr brow = B + (int64_t)kk * p.ldb;
 #pragma unroll
-            for (int c = 0; c < kGemvColsPerLane; ++c) bw[g][c] = __float_as_uint(brow[jc[c]]);
+            for (int c = 0; c < kGemvColsPerLane; ++c) bw[g][c] = cast(__float_as_uint(brow[jc[c]]));
 #pragma unroll
             for (int r = 0; r < MR; ++r) xa[g][r] = a_at(r, kk);
         }
@@ -1014,7 +1037,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
 #pragma unroll
                     for (int c = 0; c < kGemvColsPerLane; ++c) {
                         const uint32_t e = lut[row | ((bw[g][c] >> sh) & mmask)];
-                        acc[r][c] = checked_product_acc(acc[r][c], e, seA, se_of(bw[g][c]));
+                        acc[r][c] = checked_product_acc(acc[r][c], e, seA, se_of(bw[g][c]), p.elo, p.ehi);
                     }
                 }
             }

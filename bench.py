@@ -200,7 +200,7 @@ def cpu_baseline(config, host):
     if config in (1, 4):
         A, B = host["A"], host["B"]
         rows = min(64 if config == 1 else 32, A.shape[0])
-        oracle.gemm(np.ascontiguousarray(A[:rows]), B, host["lut"], host["M"])
+        oracle.gemm(np.ascontiguousarray(A[:rows]), B, host["lut"], host["M"], E=host.get("E", 8))
         macs = rows * B.shape[0] * B.shape[1]
         sample = f"rows 0-{rows - 1} of the {A.shape[0]}x{B.shape[1]}x{B.shape[0]} GEMM ({macs:.3g} MACs)"
     elif config == 2:
@@ -210,20 +210,20 @@ def cpu_baseline(config, host):
             ops = {"X": X, "W": W, "dY": dY}
             if name.startswith("wgrad"):
                 continue   # the three weight gradients are skipped to bound the sample
-            oracle.gemm(ops[an], ops[bn], host["lut"], host["M"], transA=bool(ta), transB=bool(tb))
+            oracle.gemm(ops[an], ops[bn], host["lut"], host["M"], transA=bool(ta), transB=bool(tb), E=host.get("E", 8))
             macs += m * n * k
         sample = f"the 6 forward and input-gradient GEMMs of one pass ({macs:.3g} MACs)"
     elif config == 3:
         x, w, dy = host["x"][:1], host["w"], host["dy"][:1]
-        oracle.conv2d_fwd(x, w, host["lut"], host["M"], (1, 1), (1, 1))
-        oracle.conv2d_dgrad(dy, w, x.shape, host["lut"], host["M"], (1, 1), (1, 1))
-        oracle.conv2d_wgrad(x, dy, w.shape, host["lut"], host["M"], (1, 1), (1, 1))
+        oracle.conv2d_fwd(x, w, host["lut"], host["M"], (1, 1), (1, 1), E=host.get("E", 8))
+        oracle.conv2d_dgrad(dy, w, x.shape, host["lut"], host["M"], (1, 1), (1, 1), E=host.get("E", 8))
+        oracle.conv2d_wgrad(x, dy, w.shape, host["lut"], host["M"], (1, 1), (1, 1), E=host.get("E", 8))
         macs = 3 * 32 * 32 * 64 * 9 * 64
         sample = f"image 0 of 128, fwd + dgrad + wgrad ({macs:.3g} MACs)"
     else:
         rows = 64
         X, Wqkv = host["X"], host["Wqkv"]
-        oracle.gemm(np.ascontiguousarray(X[:rows]), Wqkv, host["lut"], host["M"])
+        oracle.gemm(np.ascontiguousarray(X[:rows]), Wqkv, host["lut"], host["M"], E=host.get("E", 8))
         macs = rows * Wqkv.shape[0] * Wqkv.shape[1]
         sample = f"rows 0-{rows - 1} of the QKV projection ({macs:.3g} MACs)"
     dt = time.perf_counter() - t0
@@ -242,6 +242,9 @@ def main():
     ap.add_argument("--table-bits", type=int, default=0,
                     help="build the workload's table at this mantissa width instead (1-11; 9-11 are read "
                          "from global memory)")
+    ap.add_argument("--exp-bits", type=int, default=8,
+                    help="exponent width E (1-8) of the approximate multiplier's format (1, E, M); operands are "
+                         "cast to it before each product (8: FP32, the default)")
     ap.add_argument("--gemv", action="store_true",
                     help="with --config 1 or 4: one row of A (batch-1 inference), the row-vector kernel")
     ap.add_argument("--multiplier", choices=("table", "native", "library"), default="table",
@@ -286,6 +289,13 @@ def main():
     if args.gemv and args.config not in (1, 4):
         raise SystemExit("--gemv goes with the square GEMM workloads (--config 1 or 4)")
     step, workload, info, host = build_workload(args.config, am, torch, args.multiplier, args.table_bits, args.gemv)
+    if args.exp_bits != 8:
+        if args.multiplier != "table":
+            raise SystemExit("--exp-bits applies to the table multiplier only")
+        am.approx_exponent_bits_set(args.exp_bits)
+        workload += f"_e{args.exp_bits}"
+        info["exponent_bits"] = args.exp_bits
+        host["E"] = args.exp_bits
     macs = host.get("macs") or cfg.macs(args.config)
 
     for _ in range(args.warmup):

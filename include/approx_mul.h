@@ -84,10 +84,12 @@ int approx_lut_build_from_model(int M, float (*mul)(float a, float b), uint16_t 
  * time). `lut` is caller-owned host memory of 4^M entries in the format
  * above; it is copied during the call. Synchronous: the device is
  * synchronised before a previous table is released, so do not call it while
- * other threads queue work. Tables of M <= 8 (at most 128 KB) are staged in
- * each workgroup's LDS; tables of M = 9..11 (512 KB to 8 MB, the top of the
- * range Section V names) are read from global memory, where they stay
- * resident in the L2 and last-level caches, at a lower lookup rate.
+ * other threads queue work. Tables of M <= 8 (at most 128 KB of entries) are
+ * staged in each workgroup's LDS (at M = 8 with second copies of part of each
+ * column, 160 KB, which spread a wave's lookups over the LDS banks); tables of
+ * M = 9..11 (512 KB to 8 MB, the top of the range Section V names) are read
+ * from global memory, where they stay resident in the L2 and last-level
+ * caches, at a lower lookup rate.
  * Errors: APPROX_EINVAL (NULL lut), APPROX_EUNSUPPORTED (M outside
  * [1, 11]), APPROX_EHIP.
  */
@@ -112,6 +114,28 @@ int approx_native_load(void);
 /* M of the table loaded on the current device, 0 when the native multiplier
  * is selected, or APPROX_ENOLUT. */
 int approx_lut_bits(void);
+
+/*
+ * Exponent width E of the approximate multiplier's format (1, E, M) on the
+ * current device (ApproxTrain Section V: the exponent may have 1 to 8 bits
+ * given an exponent casting function). The format's exponent has bias
+ * b = 2^(E-1) - 1 and normal values 2^(1-b) <= |x| < 2^(b+1), without
+ * subnormals. Before each product both FP32 operands are cast to it: a
+ * normal operand below that range becomes a signed zero, above it a signed
+ * infinity (zero, Inf and NaN operands are kept; the mantissa is chopped to
+ * M bits as always). The product's exponent, with the table's carry, is then
+ * tested against the same range: below gives a signed zero, above a signed
+ * infinity. Accumulation stays FP32. E = 8 (the default) is FP32's own range,
+ * where the cast changes nothing; E = 1 leaves no normal value, so every
+ * finite operand becomes zero or infinity. The setting persists across table
+ * loads; the native multiplier ignores it. Takes effect for calls queued
+ * after it returns. Errors: APPROX_EUNSUPPORTED (E outside [1, 8]),
+ * APPROX_EHIP.
+ */
+int approx_exponent_bits_set(int E);
+
+/* E of the current device's format (8 unless set). */
+int approx_exponent_bits(void);
 
 /*
  * C[i*ldc + j] = sum_p approx(op(A)(i,p), op(B)(p,j)),  0 <= i < m, 0 <= j < n,

@@ -49,9 +49,9 @@
  *       hardware multiplication instead of the table, the reference point
  *       of Fig. 6) is the exact product of the two floats, rounded only when
  *       it is added to a sum. The sums take it when no table is given.
- *   R11 Formats (1, E, M) with E = 1..8 exponent bits (Section V: "the bits
- *       of the exponent e can be varied from 1 to 8 provided that a proper
- *       exponent casting function is given"; the pages give no cast). The
+ *   R11 Formats (1, E, M) with E = 1..8 exponent bits (Section V allows any
+ *       exponent width from 1 to 8 once an exponent cast is supplied, and
+ *       gives no cast). The
  *       format's exponent has bias b = 2^(E-1) - 1 and normal unbiased
  *       exponents 1-b .. b, IEEE style, without subnormals (the table
  *       assumes a hidden 1). Cast of an operand: a normal FP32 value whose

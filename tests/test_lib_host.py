@@ -78,3 +78,10 @@ def test_argument_errors_before_any_device_call(am):
         assert fn(1, 4, 4, 2, 2, 3, 3, 1, 1, -1, 1, p, p, p, None) == am.APPROX_EINVAL
         assert fn(1, 4, 4, 2, 2, 3, 3, 1, 1, 1, 1, None, p, p, None) == am.APPROX_EINVAL
     assert am.approx_status_string(am.APPROX_ENOLUT) == "no table loaded on this device"
+
+
+def test_exponent_width_checked_before_any_device_call(am):
+    L = am.lib()
+    assert L.approx_exponent_bits_set(0) == am.APPROX_EUNSUPPORTED
+    assert L.approx_exponent_bits_set(9) == am.APPROX_EUNSUPPORTED
+    assert L.approx_exponent_bits_set(-3) == am.APPROX_EUNSUPPORTED
