@@ -591,6 +591,55 @@ __device__ __forceinline__ void fast_index(const uint32_t (&wa)[RPL], const uint
 #undef AMX_COLW
 }
 
+// Fast path with underflow, over one reduction index: for calls where some
+// products may fall below the format's range (tiny operands, or a format with
+// fewer exponent bits) but none can exceed it. A product underflows exactly
+// when |x| < 2^(elo - EB), where x = as_float(seA + (entry << 8)) is the
+// lane operand's scaled significand and EB the uniform operand's biased
+// exponent (|x| * 2^(EB - 127) is the product's magnitude; x is normal). Such
+// an x is replaced by zero before the same FMA as the fast path, which gives
+// the rule's signed zero (adding it never changes the +0-started sum). Each
+// lane computes the bound 2^(elo - EB) for the 4 uniform operands it holds;
+// it is 0 for EB >= elo + 127 (no product can underflow) and for Inf / NaN
+// uniform operands, and 2^elo for a zero one, where any product is zero.
+// Compares are unordered-true, so a NaN x is kept.
+template <int RPL, int LA>
+__device__ __forceinline__ void ranged_index(const uint32_t (&wa)[RPL], const uint32_t (&sa)[RPL], const uint32_t (&q)[UQ],
+                                             const unsigned char* lut, float (&acc)[RPL][CPW], int elo)
+{
+    uint32_t tq[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int t = (int)((uint32_t)(elo + 127) << 23) - (int)(q[4 * j + 2 * c + 1] & 0x7F800000u);
+            tq[2 * j + c] = (uint32_t)max(t, 0);
+        }
+    uint32_t e[LA + 1][RPL];
+#define AMX_COLW(j) col_word(q, (j), 0)
+#pragma unroll
+    for (int g = 0; g < LA; ++g)
+#pragma unroll
+        for (int x = 0; x < RPL; ++x) e[g][x] = *reinterpret_cast<const uint16_t*>(lut + (wa[x] + AMX_COLW(g)));
+#pragma unroll
+    for (int g = 0; g < CPW; ++g) {
+        if (g + LA < CPW) {
+#pragma unroll
+            for (int x = 0; x < RPL; ++x)
+                e[(g + LA) % (LA + 1)][x] = *reinterpret_cast<const uint16_t*>(lut + (wa[x] + AMX_COLW(g + LA)));
+        }
+        const float tb = __uint_as_float(quad_bcast(tq[2 * (g >> 3) + (g & 1)], (g >> 1) & 3));
+#pragma unroll
+        for (int x = 0; x < RPL; ++x) {
+            const float xv = __uint_as_float((e[g % (LA + 1)][x] << 8) + sa[x]);
+            const float xk = !(__builtin_fabsf(xv) < tb) ? xv : 0.0f;
+            fmac_quad(acc[x][g], q[4 * (g >> 3) + 2 * (g & 1) + 1], xk, (g >> 1) & 3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#undef AMX_COLW
+}
+
 // Native multiplier over one reduction index: the IEEE single-precision
 // product folded by the hardware FMA, acc = fma(a, b, acc) (the product is
 // exact inside the FMA; one rounding per step). No table lookup: this is the
@@ -634,11 +683,16 @@ __device__ __forceinline__ void checked_index(const uint32_t (&wa)[RPL], const u
 // every index has its own offset from the counter (the zero region past the
 // last index). The steady-state body has no branch: the compiler's wait
 // counts for the ring stay exact, so the prefetch is never drained early.
-template <bool GATHER, bool NATIVE, int R, int RPL, int LA>
+template <bool GATHER, bool NATIVE, bool RANGED, int R, int RPL, int LA>
 __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* panel, const Word* bsrc,
                                               const uint32_t (&base)[RPL], int kb0, int kb1, uint32_t quad,
                                               const unsigned char* lut, float (&acc)[RPL][CPW])
 {
+    auto fold = [&](const uint32_t (&wa)[RPL], const uint32_t (&sa)[RPL], const uint32_t (&q)[UQ]) {
+        if constexpr (NATIVE) native_index(sa, q, acc);
+        else if constexpr (RANGED) ranged_index<RPL, LA>(wa, sa, q, lut, acc, p.elo);
+        else fast_index<RPL, LA>(wa, sa, q, lut, acc);
+    };
     constexpr int PD = R - 1;
     constexpr int NS = R / 2;
     constexpr int SB = R / 4;                      // k-steps per loop body
@@ -692,17 +746,11 @@ __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* p
         for (; u0 + R + PD <= n; u0 += R) {
 #pragma unroll
             for (int j = 0; j < R; ++j) {
-                if (j == 0) {
-                    if constexpr (NATIVE) native_index(sa[0], qb[0], acc);
-                    else fast_index<RPL, LA>(wa[0], sa[0], qb[0], lut, acc);
-                }
+                if (j == 0) fold(wa[0], sa[0], qb[0]);
                 load_lane(panel, base, lane_off(j + PD), wa[(j + PD) % R], sa[(j + PD) % R]);
                 load_uniform(urow, quad, qb[(j + PD) % R]);
                 urow += p.bld;
-                if (j > 0) {
-                    if constexpr (NATIVE) native_index(sa[j], qb[j], acc);
-                    else fast_index<RPL, LA>(wa[j], sa[j], qb[j], lut, acc);
-                }
+                if (j > 0) fold(wa[j], sa[j], qb[j]);
             }
             advance();
         }
@@ -725,8 +773,7 @@ __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* p
                 load_uniform(urow, quad, qb[(j + PD) % R]);
                 urow += p.bld;
             }
-            if constexpr (NATIVE) native_index(sa[j], qb[j], acc);
-            else fast_index<RPL, LA>(wa[j], sa[j], qb[j], lut, acc);
+            fold(wa[j], sa[j], qb[j]);
         }
         advance();
     }
@@ -808,9 +855,13 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
         b_max = __builtin_amdgcn_readfirstlane(v3);
     }
     __syncthreads();                               // the table is staged
-    const bool fast = NATIVE || (!p.force_checked &&
-                      ((a_min > a_max) || (b_min > b_max) ||
-                       (a_min + b_min - 127 >= p.elo && a_max + b_max - 126 <= p.ehi && a_max <= 253)));
+    // fast: no product can leave the format's range; ranged: some may fall
+    // below it (none above); otherwise the checked path
+    const bool none = (a_min > a_max) || (b_min > b_max);       // an operand without normal values
+    const bool no_over = none || (a_max + b_max - 126 <= p.ehi && a_max <= 253);
+    const bool no_under = none || a_min + b_min - 127 >= p.elo;
+    const bool fast = NATIVE || (!p.force_checked && no_over && no_under);
+    const bool ranged = !NATIVE && !p.force_checked && no_over && !no_under;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const uint32_t quad = (uint32_t)lane & 3u;     // this lane's place in the uniform-word quads
     const int wrow = wave / p.wc, wcol = wave - wrow * p.wc;
@@ -857,8 +908,11 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
             for (int j = 0; j < CPW; ++j) acc[x][j] = 0.0f;
 
         if (kb0 < kb1) {
-            if (fast) mainloop_fast<GATHER, NATIVE, NATIVE ? 8 : 4, RPL, LA>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
-            else if (!NATIVE) mainloop_checked<GATHER, RPL>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
+            if (fast) mainloop_fast<GATHER, NATIVE, false, NATIVE ? 8 : 4, RPL, LA>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
+            else if constexpr (!NATIVE) {
+                if (ranged) mainloop_fast<GATHER, false, true, 4, RPL, LA>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
+                else mainloop_checked<GATHER, RPL>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
+            }
         }
 
         gfloat_ptr out;
@@ -907,16 +961,18 @@ __device__ __forceinline__ uint32_t se_of(uint32_t bits)
 // 2^M-entry row; TABB = 0: it is read from global memory (M = 9..11).
 //
 // Fast path (as in the GEMM kernel): fma(as_float((e << 8) + seB),
-// as_float(seA), acc), exact while every product stays normal. Per item the
-// wave takes the exponent range of its op(A) chunk and checks each B element
-// against the window that keeps the products normal; if any lane of the wave
-// finds an element outside it, the wave redoes its columns of the item with
-// the checked path (Algorithm 2 as selects), which gives the same bits
-// wherever both apply.
+// as_float(seA), acc), exact while every product stays inside the range
+// (FP32), or no product exceeds it (a narrower format, whose products below
+// it are zeroed first, as in the GEMM kernel's path with underflow). Per item
+// the wave takes the exponent range of its op(A) chunk and checks each B
+// element against the window that keeps the products inside; if any lane of
+// the wave finds an element outside it, the wave redoes its columns of the
+// item with the checked path (Algorithm 2 as selects), which gives the same
+// bits wherever both apply.
 // Reduction indices whose operands are requested together in the row-vector kernel.
 constexpr int GG = 8;
 
-template <int MR, bool NATIVE, int NTG>
+template <int MR, bool NATIVE, int NTG, bool FMT>
 __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* lut, gfloat_cptr A, gfloat_cptr B,
                                           int j0, int k0, int k1, float (&acc)[kGemvMaxRows][kGemvColsPerLane])
 {
@@ -927,12 +983,14 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
     int jc[kGemvColsPerLane];
 #pragma unroll
     for (int c = 0; c < kGemvColsPerLane; ++c) jc[c] = min(j0 + c * NTG, p.n - 1);
-    // operands cast to the multiplier's format as they are read (the native
-    // multiplier takes them as they are)
-    auto cast = [&](uint32_t bits) -> uint32_t { return NATIVE ? bits : cast_fmt(bits, p.elo, p.ehi); };
-    auto a_at = [&](int r, int kk) -> uint32_t {
-        return cast(__float_as_uint(p.transA ? A[(int64_t)kk * p.lda + r] : A[(int64_t)r * p.lda + kk]));
+    // operands are cast to the multiplier's format where they are used (the
+    // native multiplier takes them as they are); a group's loads stay
+    // together ahead of the casts
+    auto cast = [&](uint32_t bits) -> uint32_t { return FMT ? cast_fmt(bits, p.elo, p.ehi) : bits; };
+    auto a_raw = [&](int r, int kk) -> uint32_t {
+        return __float_as_uint(p.transA ? A[(int64_t)kk * p.lda + r] : A[(int64_t)r * p.lda + kk]);
     };
+    auto a_at = [&](int r, int kk) -> uint32_t { return cast(a_raw(r, kk)); };
 #pragma unroll
     for (int r = 0; r < kGemvMaxRows; ++r)
 #pragma unroll
@@ -954,9 +1012,14 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
             emin = min(emin, __shfl_xor(emin, off, 64));
             emax = max(emax, __shfl_xor(emax, off, 64));
         }
-        // B exponents eb (normal) that keep every product inside the format's
-        // range elo..ehi (and eb + carry below 255, for the fast assembly)
-        const int lo = emin > emax ? 1 : max(1, p.elo + 127 - emin);
+        // B exponents eb (normal) that keep every product at or below the
+        // format's top ehi (and eb + carry below 255, for the fast assembly).
+        // FP32 (FMT false): also at or above its bottom, else the checked
+        // path. A narrower format (FMT): products below the bottom elo are
+        // zeroed in the loop instead: x below 2^(elo - EA) (EA: op(A)'s biased
+        // exponent) means an underflow, the bound being 0 for Inf / NaN op(A)
+        // and 2^elo for a zero op(A).
+        const int lo = (FMT || emin > emax) ? 1 : max(1, p.elo + 127 - emin);
         const int hi = emin > emax ? 253 : min(253, p.ehi + 126 - emax);
         checked = lo > hi;
         if (!checked) {
@@ -969,9 +1032,9 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
                     const int kk = min(kg + g, k1 - 1);
                     const gfloat_cptr brow = B + (int64_t)kk * p.ldb;
 #pragma unroll
-                    for (int c = 0; c < kGemvColsPerLane; ++c) bw[g][c] = cast(__float_as_uint(brow[jc[c]]));
+                    for (int c = 0; c < kGemvColsPerLane; ++c) bw[g][c] = __float_as_uint(brow[jc[c]]);
 #pragma unroll
-                    for (int r = 0; r < MR; ++r) xa[g][r] = a_at(r, kk);
+                    for (int r = 0; r < MR; ++r) xa[g][r] = a_raw(r, kk);
                 }
                 __builtin_amdgcn_sched_barrier(0);     // keep the group's loads issued together
 #pragma unroll
@@ -980,7 +1043,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
                     uint32_t ix[kGemvColsPerLane], seB[kGemvColsPerLane];
 #pragma unroll
                     for (int c = 0; c < kGemvColsPerLane; ++c) {
-                        const uint32_t bits = bw[g][c];
+                        const uint32_t bits = cast(bw[g][c]);
                         const uint32_t eb = (bits >> 23) & 0xFFu;
                         const bool special = eb - 1u > 253u;          // zero, subnormal, Inf, NaN
                         bad |= !special && (eb - (uint32_t)lo > (uint32_t)(hi - lo));
@@ -989,13 +1052,17 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
                     }
 #pragma unroll
                     for (int r = 0; r < MR; ++r) {
-                        const uint32_t seA = se_of(xa[g][r]);
-                        const uint32_t row = ((xa[g][r] >> sh) & mmask) << p.M;
+                        const uint32_t xr = cast(xa[g][r]);
+                        const uint32_t seA = se_of(xr);
+                        const uint32_t row = ((xr >> sh) & mmask) << p.M;
+                        const float tA = __int_as_float(
+                            max((int)((uint32_t)(p.elo + 127) << 23) - (int)(seA & 0x7F800000u), 0));
 #pragma unroll
                         for (int c = 0; c < kGemvColsPerLane; ++c) {
                             const uint32_t e = lut[ix[c] == zero_ix ? zero_ix : (row | ix[c])];
-                            acc[r][c] = __builtin_fmaf(__uint_as_float((e << 8) + seB[c]), __uint_as_float(seA),
-                                                       acc[r][c]);
+                            const float xv = __uint_as_float((e << 8) + seB[c]);
+                            const float xk = (FMT && __builtin_fabsf(xv) < tA) ? 0.0f : xv;
+                            acc[r][c] = __builtin_fmaf(xk, __uint_as_float(seA), acc[r][c]);
                         }
                     }
                 }
@@ -1017,9 +1084,9 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
             const int kk = min(kg + g, k1 - 1);
             const gfloat_cptr brow = B + (int64_t)kk * p.ldb;
 #pragma unroll
-            for (int c = 0; c < kGemvColsPerLane; ++c) bw[g][c] = cast(__float_as_uint(brow[jc[c]]));
+            for (int c = 0; c < kGemvColsPerLane; ++c) bw[g][c] = __float_as_uint(brow[jc[c]]);
 #pragma unroll
-            for (int r = 0; r < MR; ++r) xa[g][r] = a_at(r, kk);
+            for (int r = 0; r < MR; ++r) xa[g][r] = a_raw(r, kk);
         }
         __builtin_amdgcn_sched_barrier(0);             // keep the group's loads issued together
 #pragma unroll
@@ -1032,12 +1099,14 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
                     for (int c = 0; c < kGemvColsPerLane; ++c)
                         acc[r][c] = __builtin_fmaf(__uint_as_float(xa[g][r]), __uint_as_float(bw[g][c]), acc[r][c]);
                 } else {
-                    const uint32_t seA = se_of(xa[g][r]);
-                    const uint32_t row = ((xa[g][r] >> sh) & mmask) << p.M;
+                    const uint32_t xr = cast(xa[g][r]);
+                    const uint32_t seA = se_of(xr);
+                    const uint32_t row = ((xr >> sh) & mmask) << p.M;
 #pragma unroll
                     for (int c = 0; c < kGemvColsPerLane; ++c) {
-                        const uint32_t e = lut[row | ((bw[g][c] >> sh) & mmask)];
-                        acc[r][c] = checked_product_acc(acc[r][c], e, seA, se_of(bw[g][c]), p.elo, p.ehi);
+                        const uint32_t bc = cast(bw[g][c]);
+                        const uint32_t e = lut[row | ((bc >> sh) & mmask)];
+                        acc[r][c] = checked_product_acc(acc[r][c], e, seA, se_of(bc), p.elo, p.ehi);
                     }
                 }
             }
@@ -1071,11 +1140,20 @@ __global__ __launch_bounds__(NTG) void gemv_kernel(GemvParams p)
         const int j0 = blk * COLS + threadIdx.x;
         const int k0 = split * p.chunk, k1 = min(p.k, k0 + p.chunk);
         float acc[kGemvMaxRows][kGemvColsPerLane];
-        switch (p.m) {
-        case 1: gemv_item<1, NATIVE, NTG>(p, lut, A, B, j0, k0, k1, acc); break;
-        case 2: gemv_item<2, NATIVE, NTG>(p, lut, A, B, j0, k0, k1, acc); break;
-        case 3: gemv_item<3, NATIVE, NTG>(p, lut, A, B, j0, k0, k1, acc); break;
-        default: gemv_item<4, NATIVE, NTG>(p, lut, A, B, j0, k0, k1, acc); break;
+        if (!NATIVE && (p.elo != 1 || p.ehi != 254)) {      // a format narrower than FP32
+            switch (p.m) {
+            case 1: gemv_item<1, NATIVE, NTG, !NATIVE>(p, lut, A, B, j0, k0, k1, acc); break;
+            case 2: gemv_item<2, NATIVE, NTG, !NATIVE>(p, lut, A, B, j0, k0, k1, acc); break;
+            case 3: gemv_item<3, NATIVE, NTG, !NATIVE>(p, lut, A, B, j0, k0, k1, acc); break;
+            default: gemv_item<4, NATIVE, NTG, !NATIVE>(p, lut, A, B, j0, k0, k1, acc); break;
+            }
+        } else {
+            switch (p.m) {
+            case 1: gemv_item<1, NATIVE, NTG, false>(p, lut, A, B, j0, k0, k1, acc); break;
+            case 2: gemv_item<2, NATIVE, NTG, false>(p, lut, A, B, j0, k0, k1, acc); break;
+            case 3: gemv_item<3, NATIVE, NTG, false>(p, lut, A, B, j0, k0, k1, acc); break;
+            default: gemv_item<4, NATIVE, NTG, false>(p, lut, A, B, j0, k0, k1, acc); break;
+            }
         }
 
         gfloat_ptr out;

@@ -169,3 +169,35 @@ def test_width_persists_and_native_ignores_it(am, fmt):
     got = host(am.gemm(dev(A), dev(B)))
     assert got[0, 0] == np.float32(1000.0 * 1000.0 + 3 * 2.0 ** -20)
     am.approx_lut_load(t, M)
+
+
+@pytest.mark.parametrize("name", ["exact7", "mitchell3", "perturbed8", "mitchell9"])
+@pytest.mark.parametrize("E", [2, 3, 5, 8])
+def test_products_with_underflow_take_the_ranged_path(am, fmt, name, E):
+    """Operand exponents from 3 below the format's range up to the middle of
+    it: products can fall below the range but not above it (the fast path
+    with underflow). Bit-exact against the oracle and the forced checked
+    path; E = 8 covers FP32's own underflow."""
+    M, t = TABLES[name]()
+    am.approx_lut_load(t, M)
+    fmt(E)
+    bias = (1 << (E - 1)) - 1
+    lo, hi = max(1, 128 - bias - 3), 127 + bias // 2
+    r = splitmix64(990 + E, 3 * 500)
+    bits = ((r[0::3] & np.uint64(1)).astype(np.uint32) << np.uint32(31)) | \
+        ((lo + r[1::3] % np.uint64(hi - lo + 1)).astype(np.uint32) << np.uint32(23)) | \
+        ((r[2::3] >> np.uint64(41)).astype(np.uint32) & np.uint32(0x7FFFFF))
+    zeros_nan = np.array([0x00000000, 0x80000000, 0x7FC00000, 0x00000001], np.uint32)
+    a = np.concatenate([bits[:280], zeros_nan])
+    b = np.concatenate([bits[280:], zeros_nan])
+    print(f"ranged products {name} E={E}", flush=True)
+    got = products(am, a, b)
+    compare(got, a, b, t, M, E)
+    os.environ["APPROX_FORCE_CHECKED"] = "1"
+    try:
+        got2 = products(am, a, b)
+    finally:
+        os.environ.pop("APPROX_FORCE_CHECKED", None)
+    gnan = np.isnan(got.view(np.float32))
+    assert np.array_equal(gnan, np.isnan(got2.view(np.float32)))
+    assert np.array_equal(got[~gnan], got2[~gnan])
