@@ -40,6 +40,8 @@ constexpr int CPW = kColsPerWave;
 // wait counter too, which would serialise every table lookup behind them.
 typedef const float __attribute__((address_space(1)))* gfloat_cptr;
 typedef float __attribute__((address_space(1)))* gfloat_ptr;
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef v4f __attribute__((address_space(1)))* gv4f_ptr;
 
 // ------------------------------------------------------------------ decode
 
@@ -924,14 +926,23 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
             out = (gfloat_ptr)(p.out_ptrs ? p.out_ptrs[b] : p.out + (int64_t)b * p.out_batch);
             ld = p.ldc;
         }
+        // a lane's 16 columns of a row are contiguous: 16-byte stores when
+        // the rows are 16-byte aligned and the wave's columns are all inside
+        const bool vec = ((reinterpret_cast<uintptr_t>(out) & 15u) == 0) && ((ld & 3) == 0) && (col0 + CPW <= p.n_out);
 #pragma unroll
         for (int x = 0; x < RPL; ++x) {
             const int i = row0 + x * 64 + lane;
             if (i < p.m_out) {
                 gfloat_ptr o = out + (int64_t)i * ld + col0;
+                if (vec) {
 #pragma unroll
-                for (int j = 0; j < CPW; ++j)
-                    if (col0 + j < p.n_out) o[j] = acc[x][j];
+                    for (int j = 0; j < CPW; j += 4)
+                        *reinterpret_cast<gv4f_ptr>(o + j) = v4f{acc[x][j], acc[x][j + 1], acc[x][j + 2], acc[x][j + 3]};
+                } else {
+#pragma unroll
+                    for (int j = 0; j < CPW; ++j)
+                        if (col0 + j < p.n_out) o[j] = acc[x][j];
+                }
             }
         }
     }
