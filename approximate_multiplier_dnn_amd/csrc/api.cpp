@@ -41,9 +41,15 @@ struct DeviceTable {
     bool native = false;        // the native FP32 multiplier is selected (no image)
 };
 
+// Per (device, stream) scratch: the exponent stats of the GEMM calls first
+// (kStatsBytes), then decoded panels and split partials. The GEMM kernel
+// leaves the stats reset for the next call on the stream, so they are
+// initialised only when the arena is new or a call stopped between its decode
+// and GEMM launches (stats_ready false).
 struct Arena {
     void* ptr = nullptr;
     size_t bytes = 0;
+    bool stats_ready = false;
 };
 
 std::mutex g_mu;
@@ -60,13 +66,20 @@ int current_device(int* dev)
     return APPROX_OK;
 }
 
-// Scratch memory for one call on (device, stream). Grows only. Before
-// freeing a smaller arena the stream is synchronised, so earlier calls on it
-// have finished reading their operands.
-int arena_get(int dev, hipStream_t stream, size_t bytes, char** out)
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+const size_t kStatsBytes = align256((amx::STAT_INTS + 1) * sizeof(int));
+
+// Scratch memory for one call on (device, stream): `bytes` after the stats
+// region (*out points past it; *stats at it). Grows only. Before freeing a
+// smaller arena the stream is synchronised, so earlier calls on it have
+// finished reading their operands. *ready: whether the stats hold the reset
+// values (the caller initialises them and sets it).
+int arena_get(int dev, hipStream_t stream, size_t bytes, char** out, int** stats = nullptr, bool** ready = nullptr)
 {
     std::lock_guard<std::mutex> lock(g_mu);
     Arena& a = g_arenas[{dev, stream}];
+    bytes += kStatsBytes;
     if (a.bytes < bytes) {
         if (a.ptr != nullptr) {
             if (hipStreamSynchronize(stream) != hipSuccess) return APPROX_EHIP;
@@ -80,12 +93,13 @@ int arena_get(int dev, hipStream_t stream, size_t bytes, char** out)
             return APPROX_EHIP;
         }
         a.bytes = want;
+        a.stats_ready = false;
     }
-    *out = static_cast<char*>(a.ptr);
+    *out = static_cast<char*>(a.ptr) + kStatsBytes;
+    if (stats != nullptr) *stats = static_cast<int*>(a.ptr);
+    if (ready != nullptr) *ready = &a.stats_ready;   // std::map nodes are stable
     return APPROX_OK;
 }
-
-size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Resident GEMM workgroups per device (CUs x blocks per CU), per kernel
 // variant; queried once per device and kept.
@@ -236,17 +250,17 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     pick_split(tiles, mp.KB, TM * TN * 4, (int64_t)mp.m_out * mp.n_out * pl.batch, &mp.splits, &mp.chunk);
     mp.items = tiles * mp.splits;
 
-    const size_t stats_b = align256(amx::STAT_INTS * sizeof(int));
     const size_t lane_b = align256((size_t)pl.lane_words * pl.batch * sizeof(Word));
     const size_t uni_b = align256((size_t)pl.uni_words * pl.batch * sizeof(Word));
     const size_t part_b = mp.splits > 1 ? align256((size_t)mp.splits * pl.batch * mp.m_out * mp.n_out * sizeof(float)) : 0;
     char* base = nullptr;
-    int rc = arena_get(dev, stream, stats_b + lane_b + uni_b + part_b, &base);
+    int* stats = nullptr;
+    bool* stats_ready = nullptr;
+    int rc = arena_get(dev, stream, lane_b + uni_b + part_b, &base, &stats, &stats_ready);
     if (rc != APPROX_OK) return rc;
-    int* stats = reinterpret_cast<int*>(base);
-    Word* lane_panel = reinterpret_cast<Word*>(base + stats_b);
-    Word* uni_panel = reinterpret_cast<Word*>(base + stats_b + lane_b);
-    float* partials = reinterpret_cast<float*>(base + stats_b + lane_b + uni_b);
+    Word* lane_panel = reinterpret_cast<Word*>(base);
+    Word* uni_panel = reinterpret_cast<Word*>(base + lane_b);
+    float* partials = reinterpret_cast<float*>(base + lane_b + uni_b);
 
     pl.lane.dst = lane_panel;
     pl.lane.stats = stats;
@@ -284,7 +298,15 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
         mp.out_batch = pl.strideC;
     }
 
-    if (amx::launch_init_stats(stats, stream) != hipSuccess) return APPROX_EHIP;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        if (!*stats_ready) {
+            if (amx::launch_init_stats(stats, stream) != hipSuccess) return APPROX_EHIP;
+            *stats_ready = true;
+        }
+        // until the GEMM kernel is queued, the stats the decodes fill are not reset
+        *stats_ready = false;
+    }
     if (amx::launch_decode(pl.lane, stream) != hipSuccess) return APPROX_EHIP;
     if (M == 8) {                     // M = 8 columns carry second copies to choose from
         amx::AssignParams& ap = pl.asg;
@@ -309,6 +331,10 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
         if (hipEventRecord(ev0, stream) != hipSuccess) return APPROX_EHIP;
     }
     if (amx::launch_main(mp, lds_class, pl.gather, pl.shape, grid, stream) != hipSuccess) return APPROX_EHIP;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        *stats_ready = true;      // the GEMM kernel's last workgroup resets them
+    }
     if (prof) {
         if (hipEventRecord(ev1, stream) != hipSuccess) return APPROX_EHIP;
         std::lock_guard<std::mutex> lock(g_mu);

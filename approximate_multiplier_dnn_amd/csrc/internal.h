@@ -81,9 +81,13 @@ inline FastDiv make_fastdiv(uint32_t d)
 // 128-byte line, holding {lane min, lane max, uniform min, uniform max}.
 // Decode workgroups fold their range into slot (block % STAT_SLOTS); the GEMM
 // kernel reduces the slots.
+// The int after the slots counts the GEMM workgroups that have read them: the
+// last one resets the slots (and the count) for the stream's next call, so a
+// stream's stats need initialising only once.
 constexpr int STAT_SLOTS = 64;
 constexpr int STAT_STRIDE = 32;   // ints between slots
 constexpr int STAT_INTS = STAT_SLOTS * STAT_STRIDE;
+constexpr int STAT_READERS = STAT_INTS;   // index of the reader count
 
 struct DecodeParams {
     const float* src;

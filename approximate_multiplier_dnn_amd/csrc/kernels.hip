@@ -354,9 +354,13 @@ __global__ __launch_bounds__(256) void decode_tile_kernel(DecodeParams p)
     flush_stats(p.stats, emin, emax);
 }
 
+// Empty slots: min 255, max 0 (lane and uniform), and no readers yet.
+__device__ __forceinline__ int stat_reset_value(int i) { return (i & 1) ? 0 : 255; }
+
 __global__ __launch_bounds__(256) void init_stats_kernel(int* stats)
 {
-    for (int i = threadIdx.x; i < STAT_INTS; i += 256) stats[i] = (i & 1) ? 0 : 255;
+    for (int i = threadIdx.x; i < STAT_INTS; i += 256) stats[i] = stat_reset_value(i);
+    if (threadIdx.x == 0) stats[STAT_READERS] = 0;
 }
 
 // Plain row copies with decode: out[kk][j] (kk < rows_out, j < Np) from
@@ -856,7 +860,20 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
         b_min = __builtin_amdgcn_readfirstlane(v2);
         b_max = __builtin_amdgcn_readfirstlane(v3);
     }
-    __syncthreads();                               // the table is staged
+    __syncthreads();                               // the table is staged; every wave has read the stats
+    if (threadIdx.x < 64) {
+        // the last workgroup to read the stats resets them for the stream's
+        // next call (4 ints per slot; lane l resets slot l)
+        static_assert(STAT_SLOTS == 64, "one slot per lane of a wave");
+        int ticket = 0;
+        if (threadIdx.x == 0) ticket = atomicAdd(const_cast<int*>(p.stats) + STAT_READERS, 1);
+        ticket = __shfl(ticket, 0, 64);
+        if (ticket == (int)gridDim.x - 1) {
+            int* slot = const_cast<int*>(p.stats) + threadIdx.x * STAT_STRIDE;
+            for (int t = 0; t < 4; ++t) slot[t] = stat_reset_value(t);
+            if (threadIdx.x == 0) const_cast<int*>(p.stats)[STAT_READERS] = 0;
+        }
+    }
     // fast: no product can leave the format's range; ranged: some may fall
     // below it (none above); otherwise the checked path
     const bool none = (a_min > a_max) || (b_min > b_max);       // an operand without normal values
@@ -1188,18 +1205,43 @@ __global__ __launch_bounds__(NTG) void gemv_kernel(GemvParams p)
 
 // ------------------------------------------------------------------ reduce / fill
 
+// C = sum of the split partials in ascending split order, from +0. When the
+// partials of one batch entry hold a multiple of 4 values, each thread sums 4
+// consecutive outputs with 16-byte loads; the loads of 8 splits are issued
+// ahead of their (ordered) adds.
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p)
 {
     const int64_t mn = (int64_t)p.m * p.n;
-    const int64_t total = mn * p.batch;
+    const bool quad = (mn & 3) == 0;
+    const int64_t units = quad ? mn / 4 : mn;
+    const int64_t total = units * p.batch;
     for (int64_t g = blockIdx.x * 256LL + threadIdx.x; g < total; g += (int64_t)gridDim.x * 256) {
-        const int64_t b = g / mn, r = g - b * mn;
-        const float* src = p.ws + b * p.splits * mn + r;
-        float s = 0.0f;
-        for (int sp = 0; sp < p.splits; ++sp) s += src[sp * mn];
-        const int64_t i = r / p.n, j = r - i * p.n;
+        const int64_t b = g / units, u = g - b * units;
         float* out = p.out_ptrs ? p.out_ptrs[b] : p.out + b * p.out_batch;
-        out[i * p.ldc + j] = s;
+        if (quad) {
+            const int64_t r = u * 4;
+            const v4f* src = reinterpret_cast<const v4f*>(p.ws + b * p.splits * mn + r);
+            const int64_t step = mn / 4;
+            v4f s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+            for (int sp = 0; sp < p.splits; ++sp) s += src[sp * step];
+            int64_t i = r / p.n, j = r - i * p.n;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                out[i * p.ldc + j] = s[t];
+                if (++j == p.n) {
+                    j = 0;
+                    ++i;
+                }
+            }
+        } else {
+            const float* src = p.ws + b * p.splits * mn + u;
+            float s = 0.0f;
+#pragma unroll 8
+            for (int sp = 0; sp < p.splits; ++sp) s += src[sp * mn];
+            const int64_t i = u / p.n, j = u - i * p.n;
+            out[i * p.ldc + j] = s;
+        }
     }
 }
 
