@@ -501,12 +501,14 @@ __device__ __forceinline__ float checked_product_acc(float acc, uint32_t e, uint
     return acc + __uint_as_float(bits);
 }
 
-// Row tiles per swizzle group. 1 = plain row-major tile order, so the 32
-// workgroups of one XCD (consecutive work items, see main_kernel) share one
-// row block of the lane panel. Measured on 8192^3 (FETCH_SIZE per launch):
-// 1 -> 10.3 M KiB, 2 -> 21.0 M KiB, 4 -> 48.0 M KiB; kernel time unchanged
-// within 1% because the LDS lookups bind.
-constexpr int TILE_GROUP_M = 1;
+// Row tiles per swizzle group: the 32 workgroups of one XCD (consecutive work
+// items, see main_kernel) take 2 row tiles x 16 column tiles, which they
+// share through that XCD's L2 (per reduction index 2 x 256 rows and 16 x 128
+// columns of operand words at 8192^3, against 256 rows and 32 x 128 columns
+// in plain row-major order). Measured on 8192^3 (FETCH_SIZE per launch): 1 ->
+// 9.44 M KiB, 2 -> 6.38 M KiB, 4 -> 6.40 M KiB; the kernel time is unchanged
+// because the LDS lookups bind.
+constexpr int TILE_GROUP_M = 2;
 
 // Uniform words of one reduction index for this wave's 16 columns, spread
 // over the 4 lanes of each quad: lane i of a quad holds, in register
