@@ -85,3 +85,13 @@ def test_exponent_width_checked_before_any_device_call(am):
     assert L.approx_exponent_bits_set(0) == am.APPROX_EUNSUPPORTED
     assert L.approx_exponent_bits_set(9) == am.APPROX_EUNSUPPORTED
     assert L.approx_exponent_bits_set(-3) == am.APPROX_EUNSUPPORTED
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
