@@ -307,7 +307,7 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
         // until the GEMM kernel is queued, the stats the decodes fill are not reset
         *stats_ready = false;
     }
-    if (amx::launch_decode(pl.lane, stream) != hipSuccess) return APPROX_EHIP;
+    if (amx::launch_decode_pair(pl.lane, pl.uni, stream) != hipSuccess) return APPROX_EHIP;
     if (M == 8) {                     // M = 8 columns carry second copies to choose from
         amx::AssignParams& ap = pl.asg;
         ap.panel = lane_panel;
@@ -316,7 +316,6 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
         ap.pad_w = (1u << M) * 2u;
         if (amx::launch_assign(ap, stream) != hipSuccess) return APPROX_EHIP;
     }
-    if (amx::launch_decode(pl.uni, stream) != hipSuccess) return APPROX_EHIP;
 
     const int64_t slots = launch_slots(dev, lds_class, pl.gather, pl.shape);
     const int grid = (int)std::min<int64_t>(mp.items, slots);

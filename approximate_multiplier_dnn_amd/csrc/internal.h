@@ -117,6 +117,16 @@ struct DecodeParams {
     FastDiv fd_rowlen;
 };
 
+// One operand's decode in a combined launch: the variant for its layout and
+// its own grid of 256-thread workgroups.
+enum DecodeVariant : int { DV_IMG = 0, DV_ROWS, DV_TILE, DV_GENERIC };
+struct DecodeJob {
+    DecodeParams p;
+    int variant;
+    uint32_t gx, gy, gz;
+    int rb;              // row copies: rows per workgroup
+};
+
 // Row stride of a panel. Kept equal to the row length: padding the large
 // power-of-two rows was measured to raise the GEMM kernel's L2 misses on
 // MI355X (8192^3: FETCH_SIZE 10.3 -> 13.5 M KiB per launch).
@@ -211,7 +221,7 @@ int gemv_threads(int variant);
 int gemv_blocks_per_cu(int variant);
 hipError_t launch_gemv(const GemvParams& p, int variant, int grid, hipStream_t s);
 hipError_t launch_init_stats(int* stats, hipStream_t s);
-hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_pair(const DecodeParams& a, const DecodeParams& b, hipStream_t s);
 hipError_t launch_assign(const AssignParams& p, hipStream_t s);
 hipError_t launch_main(const MainParams& p, int lds_class, int gather, int shape, int grid, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);

@@ -103,9 +103,10 @@ __device__ __forceinline__ Word zero_word(int M, int lane_role)
 
 // Fold this thread's exponent range into the call's stats: wave reduction,
 // then workgroup reduction through LDS, then one atomic pair per workgroup
-// into slot (block % STAT_SLOTS), so no single address takes every atomic.
-// Must be called by every thread of a 256-thread workgroup.
-__device__ __forceinline__ void flush_stats(int* stats, int emin, int emax)
+// into slot (blk % STAT_SLOTS; blk: the workgroup's index in its decode), so
+// no single address takes every atomic. Must be called by every thread of a
+// 256-thread workgroup.
+__device__ __forceinline__ void flush_stats(int* stats, int emin, int emax, uint32_t blk)
 {
     __shared__ int red[2][4];
     for (int off = 32; off > 0; off >>= 1) {
@@ -125,7 +126,6 @@ __device__ __forceinline__ void flush_stats(int* stats, int emin, int emax)
             emax = max(emax, red[1][w]);
         }
         if (emin <= emax) {
-            const uint32_t blk = blockIdx.x + blockIdx.y * gridDim.x + blockIdx.z * gridDim.x * gridDim.y;
             int* slot = stats + (blk % STAT_SLOTS) * STAT_STRIDE;
             atomicMin(&slot[0], emin);
             atomicMax(&slot[1], emax);
@@ -218,20 +218,27 @@ __device__ __forceinline__ int64_t decode_source(const DecodeParams& p, uint32_t
     return -1;
 }
 
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p)
+// Each decode below runs as one part of decode_pair_kernel: bid / gdim are
+// the workgroup's index and the grid of its own part, blk its linear index.
+__device__ __forceinline__ uint32_t linear_block(uint3 bid, uint3 gdim)
+{
+    return bid.x + bid.y * gdim.x + bid.z * gdim.x * gdim.y;
+}
+
+__device__ __forceinline__ void decode_generic_body(const DecodeParams& p, uint3 bid, uint3 gdim)
 {
     int emin = 255, emax = 0;
-    const int b = blockIdx.y;
+    const int b = (int)bid.y;
     const float* src = p.src_ptrs ? p.src_ptrs[b] : p.src + b * p.src_batch_stride;
     Word* dst = p.dst + b * p.dst_batch_stride;
-    const uint32_t stride = gridDim.x * 256u;
-    for (uint32_t o = blockIdx.x * 256u + threadIdx.x; o < (uint32_t)p.count; o += stride) {
+    const uint32_t stride = gdim.x * 256u;
+    for (uint32_t o = bid.x * 256u + threadIdx.x; o < (uint32_t)p.count; o += stride) {
         const int64_t s = decode_source(p, o);
         const uint32_t row = fdiv(o, p.fd_rowlen);
         dst[(int64_t)row * p.ldw + (o - row * (uint32_t)p.rowlen)] =
             s >= 0 ? decode_bits(__float_as_uint(src[s]), p.M, p.lane_role, emin, emax, p.elo, p.ehi) : zero_word(p.M, p.lane_role);
     }
-    flush_stats(p.stats, emin, emax);
+    flush_stats(p.stats, emin, emax, linear_block(bid, gdim));
 }
 
 // Image layouts, one workgroup per output row: the source row (an NHWC row
@@ -239,11 +246,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p)
 // coalesced loads, then the output row is written contiguously.
 constexpr int IMG_ROW_FLOATS_MAX = 8192;   // 32 KB of LDS per workgroup
 
-__global__ __launch_bounds__(256) void decode_img_kernel(DecodeParams p)
+__device__ __forceinline__ void decode_img_body(const DecodeParams& p, uint3 bid, uint3 gdim, float* row)
 {
-    __shared__ float row[IMG_ROW_FLOATS_MAX];
     int emin = 255, emax = 0;
-    const int r = blockIdx.x;                      // output row
+    const int r = (int)bid.x;                      // output row
     Word* dst = p.dst;
     if (r >= p.rows) {                             // zero tail of the weight-gradient image
         const int64_t body = (int64_t)p.rows * p.C * p.Wp;
@@ -304,54 +310,98 @@ __global__ __launch_bounds__(256) void decode_img_kernel(DecodeParams p)
                          : zero_word(p.M, p.lane_role);
         }
     }
-    flush_stats(p.stats, emin, emax);
+    flush_stats(p.stats, emin, emax, linear_block(bid, gdim));
 }
 
 // Dense layouts that transpose: 64 x 64 tiles through LDS, read along the
-// source's contiguous dimension and written along the output's.
-//  lane (A not transposed):   out [KB][Mp][4], element (i, kk) = A[i*ld + kk]
-//  uniform (B transposed):    out [Kp][Np],    element (kk, j) = B[j*ld + kk]
-__global__ __launch_bounds__(256) void decode_tile_kernel(DecodeParams p)
+// source's contiguous dimension (16-byte loads where the source is aligned)
+// and written along the output's.
+//  lane (A not transposed):   out [KB][Mp][4], element (i, kk) = A[i*ld + kk];
+//    a lane reads 4 consecutive kk of one tile row i (16 bytes of LDS, rows
+//    kTileLaneLd floats apart) and writes their 4 Words (32 contiguous bytes)
+//  uniform (B transposed):    out [Kp][Np],    element (kk, j) = B[j*ld + kk];
+//    a lane reads tile rows j, j+1 at one kk (rows kTileUniLd floats apart:
+//    the 32 lanes of a half-wave hit distinct banks) and writes 2 Words.
+constexpr int kTileLaneLd = 68;
+constexpr int kTileUniLd = 65;
+constexpr int kTileLdsBytes = 64 * kTileLaneLd * 4;
+
+__device__ __forceinline__ void decode_tile_body(const DecodeParams& p, uint3 bid, uint3 gdim, float* tile)
 {
-    __shared__ float tile[64][65];
     int emin = 255, emax = 0;
-    const int b = blockIdx.z;
+    const int b = (int)bid.z;
     const float* src = p.src_ptrs ? p.src_ptrs[b] : p.src + b * p.src_batch_stride;
     Word* dst = p.dst + b * p.dst_batch_stride;
     const bool lane = p.layout == L_DENSE_LANE;
-    const int outer0 = blockIdx.x * 64;            // i (lane) or j (uniform)
-    const int k0 = blockIdx.y * 64;                // kk
+    const int tld = lane ? kTileLaneLd : kTileUniLd;
+    const int outer0 = (int)bid.x * 64;            // i (lane) or j (uniform)
+    const int k0 = (int)bid.y * 64;                // kk
     const int outer_n = lane ? p.m : p.n;
-    // load: source row = outer index, contiguous kk
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-        const int ro = e >> 6, kk = e & 63;
-        const int oi = outer0 + ro, ki = k0 + kk;
-        tile[ro][kk] = (oi < outer_n && ki < p.k) ? src[(int64_t)oi * p.ld + ki] : 0.0f;
+    const bool vec = (((uintptr_t)src & 15u) == 0) && (p.ld & 3) == 0;
+    // load: source row = outer index, 4 consecutive kk per lane
+    for (int e = threadIdx.x; e < 64 * 16; e += 256) {
+        const int ro = e >> 4, c = (e & 15) * 4;
+        const int oi = outer0 + ro, ki = k0 + c;
+        float v[4];
+        if (oi < outer_n && vec && ki + 3 < p.k) {
+            const float4 q = *reinterpret_cast<const float4*>(src + (int64_t)oi * p.ld + ki);
+            v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                v[t] = (oi < outer_n && ki + t < p.k) ? src[(int64_t)oi * p.ld + ki + t] : 0.0f;
+        }
+        if (lane) {
+            *reinterpret_cast<float4*>(tile + ro * kTileLaneLd + c) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) tile[ro * tld + c + t] = v[t];
+        }
     }
     __syncthreads();
     if (lane) {
-        // for each of the 16 k-steps of the tile, 64 rows x 4 words are contiguous
-        for (int e = threadIdx.x; e < 16 * 64 * 4; e += 256) {
-            const int kbl = e >> 8, i = (e >> 2) & 63, t = e & 3;
-            const int oi = outer0 + i, ki = k0 + kbl * 4 + t;
-            const int kb = (k0 >> 2) + kbl;
+        // k-step kbl of the tile: rows outer0.. of [Mp][4] are contiguous
+        for (int f = threadIdx.x; f < 16 * 64; f += 256) {
+            const int kbl = f >> 6, i = f & 63;
+            const int oi = outer0 + i, kb = (k0 >> 2) + kbl;
             if (kb >= p.KB || oi >= p.Mp) continue;
-            dst[(int64_t)kb * p.ldw + (int64_t)oi * 4 + t] =
-                (oi < p.m && ki < p.k) ? decode_bits(__float_as_uint(tile[i][kbl * 4 + t]), p.M, 1, emin, emax, p.elo, p.ehi)
-                                       : zero_word(p.M, 1);
+            const float4 q = *reinterpret_cast<const float4*>(tile + i * kTileLaneLd + kbl * 4);
+            const float v[4] = {q.x, q.y, q.z, q.w};
+            uint32_t o[8];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const Word wd = (oi < p.m && k0 + kbl * 4 + t < p.k)
+                    ? decode_bits(__float_as_uint(v[t]), p.M, 1, emin, emax, p.elo, p.ehi)
+                    : zero_word(p.M, 1);
+                o[2 * t] = wd.w;
+                o[2 * t + 1] = wd.se;
+            }
+            uint4* out = reinterpret_cast<uint4*>(dst + (int64_t)kb * p.ldw + (int64_t)oi * 4);
+            out[0] = make_uint4(o[0], o[1], o[2], o[3]);
+            out[1] = make_uint4(o[4], o[5], o[6], o[7]);
         }
     } else {
-        // each output row kk holds 64 contiguous columns j
-        for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-            const int kk = e >> 6, j = e & 63;
+        // output row kk holds 64 contiguous columns j: a lane takes j, j+1
+        for (int f = threadIdx.x; f < 64 * 32; f += 256) {
+            const int kk = ((f >> 6) << 1) | ((f >> 5) & 1), j = (f & 31) * 2;
             const int oj = outer0 + j, ki = k0 + kk;
-            if (ki >= p.KB * 4 || oj >= p.Np) continue;
-            dst[(int64_t)ki * p.ldw + oj] =
-                (oj < p.n && ki < p.k) ? decode_bits(__float_as_uint(tile[j][kk]), p.M, 0, emin, emax, p.elo, p.ehi)
-                                       : zero_word(p.M, 0);
+            if (ki >= p.KB * 4) continue;
+            Word wd[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                wd[t] = (oj + t < p.n && ki < p.k)
+                    ? decode_bits(__float_as_uint(tile[(j + t) * kTileUniLd + kk]), p.M, 0, emin, emax, p.elo, p.ehi)
+                    : zero_word(p.M, 0);
+            Word* out = dst + (int64_t)ki * p.ldw + oj;
+            if (oj + 1 < p.Np && (p.ldw & 1) == 0) {
+                *reinterpret_cast<uint4*>(out) = make_uint4(wd[0].w, wd[0].se, wd[1].w, wd[1].se);
+            } else {
+                if (oj < p.Np) out[0] = wd[0];
+                if (oj + 1 < p.Np) out[1] = wd[1];
+            }
         }
     }
-    flush_stats(p.stats, emin, emax);
+    flush_stats(p.stats, emin, emax, linear_block(bid, gdim));
 }
 
 // Empty slots: min 255, max 0 (lane and uniform), and no readers yet.
@@ -365,23 +415,63 @@ __global__ __launch_bounds__(256) void init_stats_kernel(int* stats)
 
 // Plain row copies with decode: out[kk][j] (kk < rows_out, j < Np) from
 // src[kk * ld + j] when kk < k and j < n (uniform panels of untransposed B
-// and of the weight-gradient errors). 2-D grid: no per-element division.
-__global__ __launch_bounds__(256) void decode_rows_kernel(DecodeParams p)
+// and of the weight-gradient errors). Workgroup (x, ., z) takes rows
+// [x * rb, x * rb + rb) of batch entry z as one run of elements, 4 loads in
+// flight per thread, so narrow panels still give every thread work.
+__device__ __forceinline__ void decode_rows_body(const DecodeParams& p, uint3 bid, uint3 gdim, int rb)
 {
     int emin = 255, emax = 0;
-    const int b = blockIdx.z;
+    const int b = (int)bid.z;
     const float* src = p.src_ptrs ? p.src_ptrs[b] : p.src + b * p.src_batch_stride;
     Word* dst = p.dst + b * p.dst_batch_stride;
-    const int j = blockIdx.x * 256 + threadIdx.x;
-    const int rows_out = p.KB * 4;
-    for (int kk = blockIdx.y; kk < rows_out; kk += gridDim.y) {
-        if (j < p.Np) {
-            dst[(int64_t)kk * p.ldw + j] = (kk < p.k && j < p.n)
-                ? decode_bits(__float_as_uint(src[(int64_t)kk * p.ld + j]), p.M, p.lane_role, emin, emax, p.elo, p.ehi)
+    const int r0 = (int)bid.x * rb;
+    const uint32_t total = (uint32_t)min(rb, p.KB * 4 - r0) * (uint32_t)p.Np;
+    for (uint32_t e0 = threadIdx.x; e0 < total; e0 += 4 * 256) {
+        float v[4];
+        uint32_t row[4], col[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t e = e0 + u * 256;
+            row[u] = fdiv(e, p.fd_Np);
+            col[u] = e - row[u] * (uint32_t)p.Np;
+            const int kk = r0 + (int)row[u];
+            v[u] = (e < total && kk < p.k && (int)col[u] < p.n) ? src[(int64_t)kk * p.ld + col[u]] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t e = e0 + u * 256;
+            if (e >= total) break;
+            const int kk = r0 + (int)row[u];
+            dst[(int64_t)kk * p.ldw + col[u]] = (kk < p.k && (int)col[u] < p.n)
+                ? decode_bits(__float_as_uint(v[u]), p.M, p.lane_role, emin, emax, p.elo, p.ehi)
                 : zero_word(p.M, p.lane_role);
         }
     }
-    flush_stats(p.stats, emin, emax);
+    flush_stats(p.stats, emin, emax, linear_block(bid, gdim));
+}
+
+// The decodes of both operands of a call in one launch: workgroups [0, na)
+// run job a's decode, the rest job b's. The dynamic LDS buffer holds the
+// image row or the 64 x 65 transposing tile (sized by the host for the
+// larger of the two jobs' needs).
+__device__ __forceinline__ void decode_job(const DecodeJob& jb, uint32_t blk, float* smem)
+{
+    const uint3 gdim = make_uint3(jb.gx, jb.gy, jb.gz);
+    const uint3 bid = make_uint3(blk % jb.gx, (blk / jb.gx) % jb.gy, blk / (jb.gx * jb.gy));
+    switch (jb.variant) {
+    case DV_IMG: decode_img_body(jb.p, bid, gdim, smem); break;
+    case DV_ROWS: decode_rows_body(jb.p, bid, gdim, jb.rb); break;
+    case DV_TILE: decode_tile_body(jb.p, bid, gdim, smem); break;
+    default: decode_generic_body(jb.p, bid, gdim); break;
+    }
+}
+
+__global__ __launch_bounds__(256) void decode_pair_kernel(DecodeJob a, DecodeJob b)
+{
+    extern __shared__ __align__(16) float smem[];
+    const uint32_t na = a.gx * a.gy * a.gz;
+    if (blockIdx.x < na) decode_job(a, blockIdx.x, smem);
+    else decode_job(b, blockIdx.x - na, smem);
 }
 
 // Copy choice for the M = 8 lane operands (replica.h): one thread per group
@@ -1282,9 +1372,15 @@ hipError_t launch_assign(const AssignParams& p, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeParams& p0, hipStream_t s)
+// The decode of one operand: its layout's variant and grid (the per-element
+// divisors filled in).
+static DecodeJob plan_decode(const DecodeParams& p0)
 {
-    DecodeParams p = p0;
+    constexpr int kRowsWgElems = 1024;   // elements per workgroup of a row copy (whole rows)
+    DecodeJob jb;
+    jb.rb = 0;
+    DecodeParams& p = jb.p;
+    p = p0;
     auto fd = [](int v) { return make_fastdiv((uint32_t)(v > 0 ? v : 1)); };
     p.fd_Mp = fd(p.Mp); p.fd_Np = fd(p.Np); p.fd_Cp = fd(p.Cp); p.fd_Kp = fd(p.Kp); p.fd_S = fd(p.S);
     p.fd_Wp = fd(p.Wp); p.fd_Cb = fd(p.Cb); p.fd_Kb = fd(p.Kb); p.fd_Hp = fd(p.Hp); p.fd_C = fd(p.C);
@@ -1293,6 +1389,13 @@ hipError_t launch_decode(const DecodeParams& p0, hipStream_t s)
         p.ldw = (int)p.count;
     }
     p.fd_rowlen = fd(p.rowlen);
+    auto grid = [&](int variant, uint32_t x, uint32_t y, uint32_t z) {
+        jb.variant = variant;
+        jb.gx = x;
+        jb.gy = y;
+        jb.gz = z;
+        return jb;
+    };
     const bool img = p.layout == L_IMG_FWD || p.layout == L_IMG_DGRAD || p.layout == L_IMG_WGRAD;
     if (img) {
         p.row_floats = p.layout == L_IMG_DGRAD ? p.Q * p.K : p.W * p.C;
@@ -1303,30 +1406,39 @@ hipError_t launch_decode(const DecodeParams& p0, hipStream_t s)
                 const int64_t tail = p.count - (int64_t)p.rows * p.C * p.Wp;
                 extra = (int)((tail + 256 * 16 - 1) / (256 * 16));
             }
-            hipLaunchKernelGGL(decode_img_kernel, dim3(p.rows + extra), dim3(256), 0, s, p);
-            return hipGetLastError();
+            return grid(DV_IMG, (uint32_t)(p.rows + extra), 1, 1);
         }
     }
     const bool rows = (p.layout == L_DENSE_UNIFORM && !p.trans) || p.layout == L_DY_WGRAD;
     if (rows && p.batch <= 65535) {
         if (p.layout == L_DY_WGRAD) { p.k = p.N * p.P * p.Q; p.n = p.K; p.ld = p.K; }
         const int rows_out = p.KB * 4;
-        dim3 g((p.Np + 255) / 256, (unsigned)std::min(rows_out, 4096), p.batch);
-        hipLaunchKernelGGL(decode_rows_kernel, g, dim3(256), 0, s, p);
-        return hipGetLastError();
+        jb.rb = std::max(1, kRowsWgElems / std::max(p.Np, 1));
+        return grid(DV_ROWS, (uint32_t)((rows_out + jb.rb - 1) / jb.rb), 1, (uint32_t)p.batch);
     }
     const bool tile = (p.layout == L_DENSE_LANE && !p.trans) || (p.layout == L_DENSE_UNIFORM && p.trans);
     if (tile && p.batch <= 65535) {
         const int outer = p.layout == L_DENSE_LANE ? p.Mp : p.Np;
         const int kext = p.KB * 4;
-        dim3 g((outer + 63) / 64, (kext + 63) / 64, p.batch);
-        if (g.y <= 65535) {
-            hipLaunchKernelGGL(decode_tile_kernel, g, dim3(256), 0, s, p);
-            return hipGetLastError();
-        }
+        const int gy = (kext + 63) / 64;
+        if (gy <= 65535) return grid(DV_TILE, (uint32_t)((outer + 63) / 64), (uint32_t)gy, (uint32_t)p.batch);
     }
-    const int gx = grid_for(p.count, 256, 8192);
-    hipLaunchKernelGGL(decode_kernel, dim3(gx, p.batch), dim3(256), 0, s, p);
+    return grid(DV_GENERIC, (uint32_t)grid_for(p.count, 256, 8192), (uint32_t)p.batch, 1);
+}
+
+hipError_t launch_decode_pair(const DecodeParams& a, const DecodeParams& b, hipStream_t s)
+{
+    const DecodeJob ja = plan_decode(a), jb = plan_decode(b);
+    const uint64_t blocks = (uint64_t)ja.gx * ja.gy * ja.gz + (uint64_t)jb.gx * jb.gy * jb.gz;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    auto lds = [](const DecodeJob& j) -> size_t {
+        if (j.variant == DV_IMG) return (size_t)j.p.row_floats * sizeof(float);
+        if (j.variant == DV_TILE) return (size_t)kTileLdsBytes;
+        return 0;
+    };
+    const size_t bytes = std::max(lds(ja), lds(jb));
+    hipLaunchKernelGGL(decode_pair_kernel, dim3((uint32_t)blocks), dim3(256), bytes, s, ja, jb);
     return hipGetLastError();
 }
 

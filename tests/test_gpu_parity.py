@@ -142,6 +142,31 @@ def test_gemm_leading_dimensions_and_untouched_padding(am):
     assert np.all(Ch[:, n:] == 7.0)
 
 
+@pytest.mark.parametrize("offset", [0, 1, 2])
+@pytest.mark.parametrize("ld_extra", [0, 3, 4])
+def test_gemm_source_alignment(am, offset, ld_extra):
+    """Operands that start off a 16-byte boundary, or whose rows are not a
+    multiple of 4 floats apart, against the same operands aligned: the decode
+    reads them 4 at a time only where that is possible."""
+    M, t = use(am, "mitchell7")
+    m, n, k = 90, 75, 131
+    lda, ldb = k + ld_extra, k + ld_extra
+    seed = 500 + 10 * offset + ld_extra
+    A = normal(seed, (m, k))
+    Bt = normal(seed + 1, (n, k))
+    bufA = np.zeros(offset + m * lda, np.float32)
+    bufB = np.zeros(offset + n * ldb, np.float32)
+    bufA[offset:].reshape(m, lda)[:, :k] = A
+    bufB[offset:].reshape(n, ldb)[:, :k] = Bt
+    dA, dB = dev(bufA), dev(bufB)
+    C = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    am.approx_gemm(0, 1, m, n, k, dA[offset:], lda, dB[offset:], ldb, C, n)
+    R, S = oracle.gemm(A, Bt, t, M, transB=True)
+    gate(host(C), R, S, what=f"alignment {offset} {ld_extra}")
+    ref = am.gemm(dev(A), dev(Bt), transB=True)
+    assert np.array_equal(host(C).view(np.uint32), host(ref).view(np.uint32))
+
+
 def test_gemm_k_zero_and_empty(am):
     use(am, "mitchell7")
     C = torch.full((5, 6), 3.0, device="cuda")
