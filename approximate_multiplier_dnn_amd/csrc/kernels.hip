@@ -1074,11 +1074,13 @@ __device__ __forceinline__ uint32_t se_of(uint32_t bits)
 // block * NTG * kGemvColsPerLane + t + c * NTG (coalesced across the wave for
 // every c) and sums reduction indices [split * chunk, (split + 1) * chunk) in
 // ascending order. Columns past n read column n - 1 and are not stored, so
-// the loop has no divergent branch. The table is read in index order; entry
-// 4^M is a zero (the target of zero, Inf and NaN operands, as the pad entry
-// of the GEMM image). TABB > 0: the table is staged once per persistent
-// workgroup in LDS, where the lookups of one op(A) element fall in one
-// 2^M-entry row; TABB = 0: it is read from global memory (M = 9..11).
+// the loop has no divergent branch. TABB > 0 (PADROWS): the table is staged
+// once per persistent workgroup in LDS as 2^M rows (one per op(A) mantissa
+// index) of 2^M entries plus a pad, where a zero, subnormal or Inf B element
+// reads the row's entry 0 and a NaN its entry 1, so the product assembly
+// below needs no special case. TABB = 0 (M = 9..11): the table is read from
+// global memory in index order, entry 4^M being a zero (the target of zero,
+// Inf and NaN operands, as the pad entry of the GEMM image).
 //
 // Fast path (as in the GEMM kernel): fma(as_float((e << 8) + seB),
 // as_float(seA), acc), exact while every product stays inside the range
@@ -1092,13 +1094,15 @@ __device__ __forceinline__ uint32_t se_of(uint32_t bits)
 // Reduction indices whose operands are requested together in the row-vector kernel.
 constexpr int GG = 8;
 
-template <int MR, bool NATIVE, int NTG, bool FMT>
+template <int MR, bool NATIVE, int NTG, bool FMT, bool PADROWS>
 __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* lut, gfloat_cptr A, gfloat_cptr B,
                                           int j0, int k0, int k1, float (&acc)[kGemvMaxRows][kGemvColsPerLane])
 {
     const int sh = 23 - p.M;
     const uint32_t mmask = (1u << p.M) - 1u;
     const uint32_t zero_ix = 1u << (2 * p.M);
+    const uint32_t pad = 1u << p.M;                 // PADROWS: the row's zero entry (pad + 1: its NaN entry)
+    const uint32_t rs = pad + 8u;                   // PADROWS: entries per row
     const int lane = threadIdx.x & 63;
     int jc[kGemvColsPerLane];
 #pragma unroll
@@ -1167,20 +1171,36 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
                         const uint32_t eb = (bits >> 23) & 0xFFu;
                         const bool special = eb - 1u > 253u;          // zero, subnormal, Inf, NaN
                         bad |= !special && (eb - (uint32_t)lo > (uint32_t)(hi - lo));
-                        ix[c] = special ? zero_ix : ((bits >> sh) & mmask);
-                        seB[c] = se_of(bits);
+                        if constexpr (PADROWS) {
+                            // zero, subnormal and Inf read the row's zero entry, NaN its entry 1:
+                            // (e << 8) + (sign | exponent) is then +-0, +-Inf or a NaN
+                            const uint32_t pix = pad + (__builtin_isnan(__uint_as_float(bits)) ? 1u : 0u);
+                            ix[c] = special ? pix : ((bits >> sh) & mmask);
+                            seB[c] = bits & 0xFF800000u;
+                        } else {
+                            ix[c] = special ? zero_ix : ((bits >> sh) & mmask);
+                            seB[c] = se_of(bits);
+                        }
                     }
+                    // the group's lookups are issued together, then used
+                    uint32_t e[MR][kGemvColsPerLane];
 #pragma unroll
                     for (int r = 0; r < MR; ++r) {
-                        const uint32_t xr = cast(xa[g][r]);
-                        const uint32_t seA = se_of(xr);
-                        const uint32_t row = ((xr >> sh) & mmask) << p.M;
+                        const uint32_t ia = (cast(xa[g][r]) >> sh) & mmask;
+                        const uint32_t row = PADROWS ? ia * rs : ia << p.M;
+#pragma unroll
+                        for (int c = 0; c < kGemvColsPerLane; ++c)
+                            e[r][c] = PADROWS ? lut[row + ix[c]] : lut[ix[c] == zero_ix ? zero_ix : (row | ix[c])];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int r = 0; r < MR; ++r) {
+                        const uint32_t seA = se_of(cast(xa[g][r]));
                         const float tA = __int_as_float(
                             max((int)((uint32_t)(p.elo + 127) << 23) - (int)(seA & 0x7F800000u), 0));
 #pragma unroll
                         for (int c = 0; c < kGemvColsPerLane; ++c) {
-                            const uint32_t e = lut[ix[c] == zero_ix ? zero_ix : (row | ix[c])];
-                            const float xv = __uint_as_float((e << 8) + seB[c]);
+                            const float xv = __uint_as_float((e[r][c] << 8) + seB[c]);
                             const float xk = (FMT && __builtin_fabsf(xv) < tA) ? 0.0f : xv;
                             acc[r][c] = __builtin_fmaf(xk, __uint_as_float(seA), acc[r][c]);
                         }
@@ -1221,11 +1241,12 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
                 } else {
                     const uint32_t xr = cast(xa[g][r]);
                     const uint32_t seA = se_of(xr);
-                    const uint32_t row = ((xr >> sh) & mmask) << p.M;
+                    const uint32_t ia = (xr >> sh) & mmask;
+                    const uint32_t row = PADROWS ? ia * rs : ia << p.M;
 #pragma unroll
                     for (int c = 0; c < kGemvColsPerLane; ++c) {
                         const uint32_t bc = cast(bw[g][c]);
-                        const uint32_t e = lut[row | ((bc >> sh) & mmask)];
+                        const uint32_t e = lut[row + ((bc >> sh) & mmask)];
                         acc[r][c] = checked_product_acc(acc[r][c], e, seA, se_of(bc), p.elo, p.ehi);
                     }
                 }
@@ -1234,16 +1255,31 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
     }
 }
 
+// TABB > 0: bytes of the LDS table image, 2^M rows of 2^M + 8 entries (the
+// op(A) element's row; entry 2^M of a row is 0, entry 2^M + 1 is 1).
 template <bool NATIVE, int TABB, int NTG>
 __global__ __launch_bounds__(NTG) void gemv_kernel(GemvParams p)
 {
-    __shared__ __align__(16) uint16_t tab[TABB > 0 ? TABB / 2 + 8 : 8];
+    constexpr bool PR = TABB > 0;
+    __shared__ __align__(16) uint16_t tab[TABB > 0 ? TABB / 2 : 8];
     const uint16_t* lut = p.lut;
     if constexpr (TABB > 0) {
-        const uint4* src = reinterpret_cast<const uint4*>(p.lut);
-        uint4* dst = reinterpret_cast<uint4*>(tab);
-        const int n16 = (int)((1u << (2 * p.M)) >> 3) + 1;   // the table and the zero entry after it
-        for (int t = threadIdx.x; t < n16; t += NTG) dst[t] = src[t];
+        const int rl = 1 << p.M, rs = rl + 8;
+        if (p.M >= 3) {                            // 16-byte chunks: rows of 2 * rl bytes, 2 * rs apart
+            const int cpr = rl >> 3;
+            const uint4* src = reinterpret_cast<const uint4*>(p.lut);
+            uint4* dst = reinterpret_cast<uint4*>(tab);
+            for (int t = threadIdx.x; t < rl * cpr; t += NTG) {
+                const int r = t / cpr, q = t - r * cpr;
+                dst[r * (rs >> 3) + q] = src[t];
+            }
+        } else {
+            for (int t = threadIdx.x; t < rl * rl; t += NTG) tab[(t >> p.M) * rs + (t & (rl - 1))] = p.lut[t];
+        }
+        for (int r = threadIdx.x; r < rl; r += NTG) {
+            tab[r * rs + rl] = 0;
+            tab[r * rs + rl + 1] = 1;
+        }
         __syncthreads();
         lut = tab;
     }
@@ -1262,17 +1298,17 @@ __global__ __launch_bounds__(NTG) void gemv_kernel(GemvParams p)
         float acc[kGemvMaxRows][kGemvColsPerLane];
         if (!NATIVE && (p.elo != 1 || p.ehi != 254)) {      // a format narrower than FP32
             switch (p.m) {
-            case 1: gemv_item<1, NATIVE, NTG, !NATIVE>(p, lut, A, B, j0, k0, k1, acc); break;
-            case 2: gemv_item<2, NATIVE, NTG, !NATIVE>(p, lut, A, B, j0, k0, k1, acc); break;
-            case 3: gemv_item<3, NATIVE, NTG, !NATIVE>(p, lut, A, B, j0, k0, k1, acc); break;
-            default: gemv_item<4, NATIVE, NTG, !NATIVE>(p, lut, A, B, j0, k0, k1, acc); break;
+            case 1: gemv_item<1, NATIVE, NTG, !NATIVE, PR>(p, lut, A, B, j0, k0, k1, acc); break;
+            case 2: gemv_item<2, NATIVE, NTG, !NATIVE, PR>(p, lut, A, B, j0, k0, k1, acc); break;
+            case 3: gemv_item<3, NATIVE, NTG, !NATIVE, PR>(p, lut, A, B, j0, k0, k1, acc); break;
+            default: gemv_item<4, NATIVE, NTG, !NATIVE, PR>(p, lut, A, B, j0, k0, k1, acc); break;
             }
         } else {
             switch (p.m) {
-            case 1: gemv_item<1, NATIVE, NTG, false>(p, lut, A, B, j0, k0, k1, acc); break;
-            case 2: gemv_item<2, NATIVE, NTG, false>(p, lut, A, B, j0, k0, k1, acc); break;
-            case 3: gemv_item<3, NATIVE, NTG, false>(p, lut, A, B, j0, k0, k1, acc); break;
-            default: gemv_item<4, NATIVE, NTG, false>(p, lut, A, B, j0, k0, k1, acc); break;
+            case 1: gemv_item<1, NATIVE, NTG, false, PR>(p, lut, A, B, j0, k0, k1, acc); break;
+            case 2: gemv_item<2, NATIVE, NTG, false, PR>(p, lut, A, B, j0, k0, k1, acc); break;
+            case 3: gemv_item<3, NATIVE, NTG, false, PR>(p, lut, A, B, j0, k0, k1, acc); break;
+            default: gemv_item<4, NATIVE, NTG, false, PR>(p, lut, A, B, j0, k0, k1, acc); break;
             }
         }
 
@@ -1492,8 +1528,8 @@ int main_blocks_per_cu(int lds_class, int gather, int shape)
 static const void* gemv_variant(int v)
 {
     switch (v) {
-    case 0: return (const void*)gemv_kernel<false, (1 << 14) * 2, kGemvLdsThreads>;
-    case 1: return (const void*)gemv_kernel<false, (1 << 16) * 2, kGemvLdsThreads>;
+    case 0: return (const void*)gemv_kernel<false, (1 << 7) * ((1 << 7) + 8) * 2, kGemvLdsThreads>;
+    case 1: return (const void*)gemv_kernel<false, (1 << 8) * ((1 << 8) + 8) * 2, kGemvLdsThreads>;
     case 2: return (const void*)gemv_kernel<false, 0, kGemvThreads>;
     default: return (const void*)gemv_kernel<true, 0, kGemvThreads>;
     }

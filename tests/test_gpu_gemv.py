@@ -94,6 +94,32 @@ def test_gemv_products_bit_exact(am, name):
     assert np.count_nonzero(got[~gnan] != want[~gnan]) == 0
 
 
+@pytest.mark.parametrize("name", ["mitchell7", "perturbed8", "arbitrary11"])
+def test_gemv_special_b_on_the_fast_path(am, name):
+    """k = 1 with op(A) and B of moderate exponents (no product can leave the
+    range, so every wave stays on the fast path) and B holding +-0,
+    subnormals, +-Inf and NaN: every product bit for bit."""
+    t, M = use(am, name)
+    r = splitmix64(950 + M, 700)
+    mant = (r & np.uint64(0x7FFFFF)).astype(np.uint32)
+    exp = (100 + (r >> np.uint64(32)) % np.uint64(50)).astype(np.uint32)
+    sign = ((r >> np.uint64(40)) & np.uint64(1)).astype(np.uint32)
+    bvals = ((sign << np.uint32(31)) | (exp << np.uint32(23)) | mant).astype(np.uint32)
+    spec = np.array([0x00000000, 0x80000000, 0x00000001, 0x807FFFFF, 0x7F800000, 0xFF800000,
+                     0x7FC00000, 0xFFC00001, 0x7F800001], np.uint32)
+    bvals[3::61] = spec[np.arange(bvals[3::61].size) % spec.size]
+    avals = np.array([0x3FC00000, 0xC1234567, 0x00000000, 0x7F800000], np.uint32)   # 1.5, -10.2, 0, Inf
+    C = torch.empty((4, bvals.size), dtype=torch.float32, device="cuda")
+    am.approx_gemm(0, 0, 4, bvals.size, 1, dev(avals.view(np.float32).reshape(4, 1)), 1,
+                   dev(bvals.view(np.float32).reshape(1, -1)), bvals.size, C, bvals.size)
+    got = host(C).view(np.uint32)
+    want = oracle.amsim_bits(np.repeat(avals, bvals.size), np.tile(bvals, 4), t, M).reshape(4, bvals.size)
+    want = np.where(want == 0x80000000, 0, want).astype(np.uint32)     # +0 + (-0) = +0
+    gnan = np.isnan(got.view(np.float32))
+    assert np.array_equal(gnan, np.isnan(want.view(np.float32)))
+    assert np.count_nonzero(got[~gnan] != want[~gnan]) == 0
+
+
 def test_gemv_special_values_and_padding(am):
     t, M = use(am, "perturbed8")
     m, n, k, lda, ldb, ldc = 3, 700, 90, 100, 710, 720
