@@ -125,9 +125,26 @@ def build_workload(config, am, torch, mult="table", table_bits=0, gemv=False):
             C = torch.empty((m, n), dtype=torch.float32, device="cuda")
             calls.append((ta, tb, m, n, k, A, A.shape[1], B, B.shape[1], C, n))
 
+        # A training step's dependencies: the forward chain, then per layer
+        # (top down) the input gradient on this stream and the weight
+        # gradient, which needs the layer's output gradient, on a second one.
+        names = [g[0] for g in cfg.mlp_gemms()]
+        byname = dict(zip(names, calls))
+        nl = len(names) // 3
+        side = torch.cuda.Stream()
+        evs = [torch.cuda.Event() for _ in range(nl + 1)]
+
         def step():
-            for c in calls:
-                am.approx_gemm(*c)
+            cur = torch.cuda.current_stream()
+            for l in range(nl):
+                am.approx_gemm(*byname[f"fwd{l}"], stream=cur)
+            evs[0].record(cur)
+            for i, l in enumerate(reversed(range(nl))):
+                side.wait_event(evs[i])
+                am.approx_gemm(*byname[f"wgrad{l}"], stream=side)
+                am.approx_gemm(*byname[f"dgrad{l}"], stream=cur)
+                evs[i + 1].record(cur)
+            cur.wait_stream(side)
 
         workload = "mlp_784-1024-1024-10_b256_fwd_dgrad_wgrad_" + ("lut_m7_mitchell" if lut is not None else "native_fp32_fma")
         info = dict(batch=256, widths=[784, 1024, 1024, 10])
