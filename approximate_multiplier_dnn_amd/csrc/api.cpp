@@ -190,30 +190,54 @@ int pick_shape(int m, int n, int* wr, int* wc)
     return twelve ? 1 : 0;
 }
 
-// Reduction split. The work items (tiles x splits) run in rounds over the
-// resident workgroups; a round costs one chunk of k-steps. A split trades
-// the idle workgroups of a partial last round against the partials it writes
-// and the reduction that reads them back. Picks the split count of least
-// modelled time; ties go to fewer splits.
-void pick_split(int64_t tiles, int KB, int64_t tile_macs_per_kstep, int64_t out_elems, int* splits, int* chunk)
+// Reduction split. The work items run in rounds over the resident
+// workgroups; a round costs its longest item. Two layouts are modelled:
+//  - every tile split into the same number of chunks (a split trades the
+//    idle workgroups of a partial last round against the partials it writes
+//    and the reduction that reads them back);
+//  - when the tiles fill at least one round: whole tiles for the full
+//    rounds, and only the tiles of the partial last round split, so that
+//    their chunks fill that round.
+// Picks the layout and split count of least modelled time; ties go to fewer
+// splits and to the uniform layout.
+void plan_split(int64_t tiles, int KB, int64_t tile_macs_per_kstep, int64_t tile_outs, int64_t out_elems,
+                MainParams& mp)
 {
     const int smax = std::max(1, std::min(kSplitMax, KB / 2));
     const double kstep_s = (double)tile_macs_per_kstep / (kSplitMacRate / (double)kSplitSlots);
+    const double out_s = 4.0 / kSplitBytesRate;           // per output and pass over the partials
     double best = -1.0;
     int bs = 1;
+    int64_t tail = tiles;
     for (int sc = 1; sc <= smax; ++sc) {
-        const int c = (int)cdiv(KB, sc);
-        const int64_t items = tiles * cdiv(KB, c);
-        const double gemm = (double)cdiv(items, kSplitSlots) * c * kstep_s;
-        const double red = sc > 1 ? (double)(cdiv(KB, c) + 1) * out_elems * 4.0 / kSplitBytesRate : 0.0;
+        const int c = (int)cdiv(KB, sc), sp = (int)cdiv(KB, c);
+        const double gemm = (double)cdiv(tiles * sp, kSplitSlots) * c * kstep_s;
+        const double red = sp > 1 ? (double)(sp + 1) * out_elems * out_s : 0.0;
         if (best < 0.0 || gemm + red < best * 0.999) {
             best = gemm + red;
-            bs = sc;
+            bs = sp;
+            tail = tiles;
         }
     }
-    const int c = (int)cdiv(KB, bs);
-    *chunk = c;
-    *splits = (int)cdiv(KB, c);
+    const int64_t rem = tiles % kSplitSlots, full = tiles - rem;
+    if (full > 0 && rem > 0) {
+        for (int sc = 2; sc <= smax; ++sc) {
+            const int c = (int)cdiv(KB, sc), sp = (int)cdiv(KB, c);
+            const double gemm = (double)(full / kSplitSlots) * KB * kstep_s + (double)cdiv(rem * sp, kSplitSlots) * c * kstep_s;
+            const double red = (double)(sp + 1) * std::min(out_elems, rem * tile_outs) * out_s;
+            if (gemm + red < best * 0.999) {
+                best = gemm + red;
+                bs = sp;
+                tail = rem;
+            }
+        }
+    }
+    if (bs == 1) tail = 0;
+    mp.splits = bs;
+    mp.chunk = (int)cdiv(KB, bs);
+    mp.tail_tiles = (int)tail;
+    mp.full_items = (int)(tiles - tail);
+    mp.items = (int64_t)mp.full_items + (int64_t)tail * bs;
 }
 
 bool force_checked()
@@ -247,8 +271,7 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     const int lds_class = M == 0 ? 2 : M <= 7 ? 0 : M == 8 ? 1 : 3;
     const int64_t tiles = (int64_t)mp.tiles_m * mp.tiles_n * pl.batch;
     const int64_t TM = (int64_t)mp.wr * 64 * kShapes[pl.shape].rows_per_lane, TN = (int64_t)mp.wc * kColsPerWave;
-    pick_split(tiles, mp.KB, TM * TN * 4, (int64_t)mp.m_out * mp.n_out * pl.batch, &mp.splits, &mp.chunk);
-    mp.items = tiles * mp.splits;
+    plan_split(tiles, mp.KB, TM * TN * 4, TM * TN, (int64_t)mp.m_out * mp.n_out * pl.batch, mp);
 
     const size_t lane_b = align256((size_t)pl.lane_words * pl.batch * sizeof(Word));
     const size_t uni_b = align256((size_t)pl.uni_words * pl.batch * sizeof(Word));
@@ -290,13 +313,10 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     mp.bpanel_batch = pl.uni_words;
     mp.batch = pl.batch;
     mp.force_checked = force_checked() ? 1 : 0;
-    if (mp.splits > 1) {
-        mp.out = partials;
-    } else {
-        mp.out = pl.C;
-        mp.out_ptrs = pl.Cp;
-        mp.out_batch = pl.strideC;
-    }
+    mp.out = pl.C;
+    mp.out_ptrs = pl.Cp;
+    mp.out_batch = pl.strideC;
+    mp.ws = mp.splits > 1 ? partials : nullptr;
 
     {
         std::lock_guard<std::mutex> lock(g_mu);
@@ -340,7 +360,7 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
         g_events.emplace_back(ev0, ev1);
     }
 
-    if (mp.splits > 1) {
+    if (mp.splits > 1 && mp.full_items == 0) {     // every tile split: sum all of C
         ReduceParams rp{};
         rp.ws = partials;
         rp.out = pl.C;
@@ -352,6 +372,23 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
         rp.batch = pl.batch;
         rp.out_batch = pl.strideC;
         if (amx::launch_reduce(rp, stream) != hipSuccess) return APPROX_EHIP;
+    } else if (mp.splits > 1) {                    // only the tail tiles are split
+        amx::ReduceTilesParams rp{};
+        rp.ws = partials;
+        rp.out = pl.C;
+        rp.out_ptrs = pl.Cp;
+        rp.m = mp.m_out;
+        rp.n = mp.n_out;
+        rp.ldc = mp.ldc;
+        rp.splits = mp.splits;
+        rp.out_batch = pl.strideC;
+        rp.tiles_m = mp.tiles_m;
+        rp.tiles_n = mp.tiles_n;
+        rp.TM = (int)TM;
+        rp.TN = (int)TN;
+        rp.first_tile = mp.full_items;
+        rp.n_tiles = mp.tail_tiles;
+        if (amx::launch_reduce_tiles(rp, stream) != hipSuccess) return APPROX_EHIP;
     }
     return APPROX_OK;
 }

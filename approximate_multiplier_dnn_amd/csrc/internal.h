@@ -147,8 +147,9 @@ struct MainParams {
     const Word* bpanel;       // uniform operand words [Kp][Np]
     const uint16_t* lut;      // table image (lane-first layout)
     const int* stats;         // STAT_SLOTS slots of {lane min, lane max, uniform min, uniform max}
-    float* out;               // C (or split partials when splits > 1)
+    float* out;               // C
     float* const* out_ptrs;   // batched by pointer array (device): C of entry b
+    float* ws;                // chunk partials of the split tiles (splits > 1)
     int64_t panel_batch;      // Words between batch entries of the lane panel
     int64_t bpanel_batch;     // Words between batch entries of the uniform panel
     int64_t out_batch;        // floats between batch entries of C
@@ -162,7 +163,13 @@ struct MainParams {
     int nku, zoff;            // gather mode
     int KB;                   // k-steps of 4 reduction indices (vector) / 4-groups (gather)
     int wr, wc;               // waves per workgroup along rows / columns (wr*wc = 8)
-    int tiles_m, tiles_n, splits, chunk;  // chunk = k-steps (of 4) per split
+    int tiles_m, tiles_n;
+    // Work items: the first full_items (batch entry, tile) pairs whole, in
+    // the order b * tiles + tile; then the remaining tail_tiles pairs in
+    // `splits` reduction chunks of `chunk` k-steps (of 4) each, item
+    // full_items + split * tail_tiles + t. Chunk partials go to
+    // ws[(b * splits + split) * m_out * n_out + ...]; whole tiles to C.
+    int full_items, tail_tiles, splits, chunk;
     int batch;
     int64_t items;
     int force_checked;        // 1: always use the per-product checked path
@@ -189,6 +196,19 @@ struct ReduceParams {
     float* const* out_ptrs;
     int m, n, ldc, splits, batch;
     int64_t out_batch;
+};
+
+// Sum of the chunk partials of the GEMM kernel's split tiles (the tail of
+// its work items): tiles first_tile .. first_tile + n_tiles - 1 of the order
+// b * tiles + tile, each TM x TN outputs of C.
+struct ReduceTilesParams {
+    const float* ws;
+    float* out;
+    float* const* out_ptrs;
+    int m, n, ldc, splits;
+    int64_t out_batch;
+    int tiles_m, tiles_n, TM, TN;
+    int first_tile, n_tiles;
 };
 
 // Row-vector GEMM (op(A) has at most kGemvMaxRows rows, B not transposed):
@@ -225,6 +245,7 @@ hipError_t launch_decode_pair(const DecodeParams& a, const DecodeParams& b, hipS
 hipError_t launch_assign(const AssignParams& p, hipStream_t s);
 hipError_t launch_main(const MainParams& p, int lds_class, int gather, int shape, int grid, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
+hipError_t launch_reduce_tiles(const ReduceTilesParams& p, hipStream_t s);
 hipError_t launch_fill_zero(float* C, float* const* Cp, int m, int n, int ldc, int batch, int64_t strideC,
                             hipStream_t s);
 int main_blocks_per_cu(int lds_class, int gather, int shape);

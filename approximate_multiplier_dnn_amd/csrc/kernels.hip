@@ -914,6 +914,18 @@ __device__ __forceinline__ void mainloop_checked(const MainParams& p, const Word
     }
 }
 
+// Tile order of the GEMM kernel's work items: groups of TILE_GROUP_M row
+// tiles, column tiles outer, row tiles inner within a group.
+__device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, int& tm, int& tn)
+{
+    const int group = tile / (TILE_GROUP_M * tiles_n);
+    const int first_m = group * TILE_GROUP_M;
+    const int gm = min(tiles_m - first_m, TILE_GROUP_M);
+    const int in_group = tile - group * TILE_GROUP_M * tiles_n;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+}
+
 // LDSB: bytes of the LDS table image (LDS_SMALL or LDS_LARGE), or NATIVE_LDS
 // where no table is staged (native multiplier, table in global memory).
 constexpr int NATIVE_LDS = 16;
@@ -986,16 +998,19 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
     const int tiles = p.tiles_m * p.tiles_n;
 
     for (int item = v; item < items; item += G) {
-        const int tile = item % tiles;
-        const int rest = item / tiles;
-        const int split = rest % p.splits;
-        const int b = rest / p.splits;
-        const int group = tile / (TILE_GROUP_M * p.tiles_n);
-        const int first_m = group * TILE_GROUP_M;
-        const int gm = min(p.tiles_m - first_m, TILE_GROUP_M);
-        const int in_group = tile - group * TILE_GROUP_M * p.tiles_n;
-        const int tm = first_m + in_group % gm;
-        const int tn = in_group / gm;
+        int tl, split;                             // (batch entry, tile) pair; split -1: whole
+        if (item < p.full_items) {
+            tl = item;
+            split = -1;
+        } else {
+            const int t2 = item - p.full_items;
+            split = t2 / p.tail_tiles;
+            tl = p.full_items + (t2 - split * p.tail_tiles);
+        }
+        const int tile = tl % tiles;
+        const int b = tl / tiles;
+        int tm, tn;
+        tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
         const int row0 = tm * TM + wrow * 64 * RPL;
         const int col0 = tn * TN + wcol * CPW;
         if (row0 >= p.m_out || col0 >= p.n_out) continue;   // this wave has no output in the tile
@@ -1009,8 +1024,8 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
         }
         const Word* panel = p.panel + (int64_t)b * p.panel_batch;
         const Word* bsrc = p.bpanel + (int64_t)b * p.bpanel_batch + col0;
-        const int kb0 = split * p.chunk;
-        const int kb1 = min(p.KB, kb0 + p.chunk);
+        const int kb0 = split < 0 ? 0 : split * p.chunk;
+        const int kb1 = split < 0 ? p.KB : min(p.KB, kb0 + p.chunk);
 
         float acc[RPL][CPW];
 #pragma unroll
@@ -1028,8 +1043,8 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
 
         gfloat_ptr out;
         int ld;
-        if (p.splits > 1) {
-            out = (gfloat_ptr)(p.out + ((int64_t)b * p.splits + split) * (int64_t)p.m_out * p.n_out);
+        if (split >= 0) {
+            out = (gfloat_ptr)(p.ws + ((int64_t)b * p.splits + split) * (int64_t)p.m_out * p.n_out);
             ld = p.n_out;
         } else {
             out = (gfloat_ptr)(p.out_ptrs ? p.out_ptrs[b] : p.out + (int64_t)b * p.out_batch);
@@ -1373,6 +1388,49 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p)
     }
 }
 
+// The split tiles' outputs: C = sum of their chunk partials in ascending
+// split order, from +0. Thread unit = 4 consecutive columns of one tile row
+// (16-byte loads when the rows are 4-float aligned and the 4 are inside).
+__global__ __launch_bounds__(256) void reduce_tiles_kernel(ReduceTilesParams p)
+{
+    const int quads = p.TN / 4;
+    const int64_t per_tile = (int64_t)p.TM * quads;
+    const int64_t total = per_tile * p.n_tiles;
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int64_t mn = (int64_t)p.m * p.n;
+    for (int64_t g = blockIdx.x * 256LL + threadIdx.x; g < total; g += (int64_t)gridDim.x * 256) {
+        const int tt = (int)(g / per_tile);
+        const int q = (int)(g - (int64_t)tt * per_tile);
+        const int tl = p.first_tile + tt;
+        const int b = tl / tiles;
+        int tm, tn;
+        tile_coords(tl - b * tiles, p.tiles_m, p.tiles_n, tm, tn);
+        const int i = tm * p.TM + q / quads;
+        const int j = tn * p.TN + (q % quads) * 4;
+        if (i >= p.m || j >= p.n) continue;
+        const float* src = p.ws + (int64_t)b * p.splits * mn + (int64_t)i * p.n + j;
+        float* out = (p.out_ptrs ? p.out_ptrs[b] : p.out + b * p.out_batch) + (int64_t)i * p.ldc + j;
+        if ((p.n & 3) == 0) {                      // j + 3 < n as well
+            v4f sum = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+            for (int sp = 0; sp < p.splits; ++sp) sum += *reinterpret_cast<const v4f*>(src + sp * mn);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) out[t] = sum[t];
+        } else {
+            const int nt = min(4, p.n - j);
+            float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+            for (int sp = 0; sp < p.splits; ++sp)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    if (t < nt) sum[t] += src[sp * mn + t];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (t < nt) out[t] = sum[t];
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* C, float* const* Cp, int m, int n, int ldc, int batch,
                                                         int64_t strideC)
 {
@@ -1557,6 +1615,13 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t s)
 {
     const int64_t total = (int64_t)p.m * p.n * p.batch;
     hipLaunchKernelGGL(reduce_kernel, dim3(grid_for(total, 256, 16384)), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_tiles(const ReduceTilesParams& p, hipStream_t s)
+{
+    const int64_t total = (int64_t)p.TM * (p.TN / 4) * p.n_tiles;
+    hipLaunchKernelGGL(reduce_tiles_kernel, dim3(grid_for(total, 256, 16384)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
