@@ -167,6 +167,26 @@ def test_gemm_source_alignment(am, offset, ld_extra):
     assert np.array_equal(host(C).view(np.uint32), host(ref).view(np.uint32))
 
 
+@pytest.mark.parametrize("name", ["mitchell7", "perturbed8"])
+def test_gemm_tail_tiles_split(am, name):
+    """257-258 output tiles (one more than a round of resident workgroups):
+    the full round's tiles are computed whole, only the last tile(s) in
+    reduction chunks whose partials are summed afterwards. Checked on every
+    output of the last 256 columns (where the split tiles lie) and on random
+    outputs everywhere."""
+    M, t = use(am, name)
+    m, n, k = 512, 64 * 257, 1024
+    A = normal(811, (m, k))
+    B = normal(812, (k, n))
+    C = host(am.gemm(dev(A), dev(B)))
+    rr, cc = np.meshgrid(np.arange(m, dtype=np.int32), np.arange(n - 256, n, dtype=np.int32), indexing="ij")
+    sr, sc = _sample_pairs(813, m, n, 4096)
+    rows = np.concatenate([rr.ravel(), sr])
+    cols = np.concatenate([cc.ravel(), sc])
+    R, S = oracle.gemm_at(A, B, t, M, rows, cols)
+    gate(C[rows, cols], R, S, what=f"tail split {name}")
+
+
 def test_gemm_k_zero_and_empty(am):
     use(am, "mitchell7")
     C = torch.full((5, 6), 3.0, device="cuda")
