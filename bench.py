@@ -278,7 +278,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the approximate GEMM is not sharded across GPUs in this build", file=sys.stderr)
+              "the library runs each call on one GPU and has no sharding across GPUs", file=sys.stderr)
         sys.exit(2)
 
     if args.lds_probe:
