@@ -1184,15 +1184,19 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
                     for (int c = 0; c < kGemvColsPerLane; ++c) {
                         const uint32_t bits = cast(bw[g][c]);
                         const uint32_t eb = (bits >> 23) & 0xFFu;
-                        const bool special = eb - 1u > 253u;          // zero, subnormal, Inf, NaN
-                        bad |= !special && (eb - (uint32_t)lo > (uint32_t)(hi - lo));
                         if constexpr (PADROWS) {
                             // zero, subnormal and Inf read the row's zero entry, NaN its entry 1:
-                            // (e << 8) + (sign | exponent) is then +-0, +-Inf or a NaN
-                            const uint32_t pix = pad + (__builtin_isnan(__uint_as_float(bits)) ? 1u : 0u);
-                            ix[c] = special ? pix : ((bits >> sh) & mmask);
+                            // (e << 8) + (sign | exponent) is then +-0, +-Inf or a NaN. The
+                            // classes come from v_cmp_class (mask 0x108: +-normal; 0x3: NaN)
+                            const float bf = __uint_as_float(bits);
+                            const bool normal = __builtin_amdgcn_classf(bf, 0x108);
+                            bad |= normal && (eb - (uint32_t)lo > (uint32_t)(hi - lo));
+                            const uint32_t pix = pad + (__builtin_amdgcn_classf(bf, 0x3) ? 1u : 0u);
+                            ix[c] = normal ? __builtin_amdgcn_ubfe(bits, (uint32_t)sh, (uint32_t)p.M) : pix;
                             seB[c] = bits & 0xFF800000u;
                         } else {
+                            const bool special = eb - 1u > 253u;      // zero, subnormal, Inf, NaN
+                            bad |= !special && (eb - (uint32_t)lo > (uint32_t)(hi - lo));
                             ix[c] = special ? zero_ix : ((bits >> sh) & mmask);
                             seB[c] = se_of(bits);
                         }
@@ -1210,7 +1214,10 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int r = 0; r < MR; ++r) {
-                        const uint32_t seA = se_of(cast(xa[g][r]));
+                        uint32_t seA = se_of(cast(xa[g][r]));
+                        // opaque to the optimiser: a NaN op(A) then goes through the FMA
+                        // like any value, instead of a select per product
+                        if constexpr (PADROWS) asm volatile("" : "+v"(seA));
                         const float tA = __int_as_float(
                             max((int)((uint32_t)(p.elo + 127) << 23) - (int)(seA & 0x7F800000u), 0));
 #pragma unroll
