@@ -1,19 +1,22 @@
 // kernels.hip -- gfx950 kernels of the LUT-based approximate GEMM.
 //
 // The product of every multiply-accumulate is the AMSim approximate product
-// ("ApproxTrain", arXiv 2209.04161, Section V, Algorithm 2). Three kernels
-// make up one call:
-//   1. decode  : each FP32 operand element is decoded once into a Word
-//                (table offset + sign|exponent bits), laid out for step 3.
-//                This is also where implicit-GEMM layouts for Conv2D are
-//                produced (zero-padded images, the padded and dilated errors
-//                and the transposed, reversed filter of Section VI-B).
-//   2. main    : the table is staged in LDS once per persistent workgroup;
-//                each lane owns 3 or 4 rows x 16 columns of the output; per MAC it
-//                forms the LDS address, reads one 16-bit entry and folds it
-//                into the FP32 accumulator.
-//   3. reduce  : when the reduction is split, sums the chunk partials in
-//                ascending chunk order.
+// ("ApproxTrain", arXiv 2209.04161, Section V, Algorithm 2). One call queues:
+//   1. decode  : one launch for both operands; each FP32 element is decoded
+//                once into a Word (table offset + sign|exponent bits), laid
+//                out for step 3. This is also where implicit-GEMM layouts for
+//                Conv2D are produced (zero-padded images, the padded and
+//                dilated errors and the transposed, reversed filter of
+//                Section VI-B).
+//   2. assign  : M = 8 only: the copy of each lane operand's table row
+//                (replica.h), chosen per group of 32 operands.
+//   3. main    : the table is staged in LDS once per persistent workgroup;
+//                each lane owns 3 or 4 rows x 16 columns of the output; per
+//                MAC it forms the LDS address, reads one 16-bit entry and
+//                folds it into the FP32 accumulator.
+//   4. reduce  : when reductions are split, sums the chunk partials in
+//                ascending chunk order (all tiles, or only the tiles of the
+//                last round).
 //
 // Fast path (3 VALU ops + 1 LDS read per MAC). When no product of the call
 // can leave the normal range, the AMSim product equals exactly
@@ -24,7 +27,9 @@
 // and NaN operands are encoded (zero pad entry, se = 0 / +-Inf / NaN) so the
 // same FMA produces the rule's zero, infinity and NaN cases. The exponent
 // range test is made from the per-operand min/max exponents gathered by the
-// decode pass. Otherwise the checked path evaluates Algorithm 2 per product.
+// decode pass. When products may fall below the range but none above it, the
+// fast path zeroes those products first; otherwise the checked path
+// evaluates Algorithm 2 per product.
 #include <algorithm>
 
 #include "internal.h"
