@@ -47,6 +47,9 @@ def use(am, name):
             _T[name] = (oracle.lut_perturb(8, oracle.lut_generate(8, "exact"), pm_one(PERTURB_SEED, 1 << 16)), 8)
         elif name == "arbitrary11":
             _T[name] = ((splitmix64(7011, 1 << 22) >> np.uint64(48)).astype(np.uint16), 11)
+        elif name.startswith("arbitrary"):      # arbitrary 16-bit entries, M = 1..8
+            M = int(name[len("arbitrary"):])
+            _T[name] = ((splitmix64(7100 + M, 1 << (2 * M)) >> np.uint64(48)).astype(np.uint16), M)
         else:
             _T[name] = (None, 0)
     t, M = _T[name]
@@ -118,6 +121,35 @@ def test_gemv_special_b_on_the_fast_path(am, name):
     gnan = np.isnan(got.view(np.float32))
     assert np.array_equal(gnan, np.isnan(want.view(np.float32)))
     assert np.count_nonzero(got[~gnan] != want[~gnan]) == 0
+
+
+@pytest.mark.parametrize("name", ["arbitrary1", "arbitrary2", "arbitrary3", "arbitrary5", "arbitrary8"])
+def test_gemv_small_tables_bit_exact(am, name):
+    """Tables of M = 1..8 with arbitrary entries, staged in LDS as padded rows
+    (rows of 2 and 4 entries copied one entry at a time, wider rows 16 bytes
+    at a time): k = 1 products bit for bit, specials included, then a
+    row-vector sum."""
+    t, M = use(am, name)
+    r = splitmix64(960 + M, 600)
+    mant = (r & np.uint64(0x7FFFFF)).astype(np.uint32)
+    exp = (110 + (r >> np.uint64(32)) % np.uint64(30)).astype(np.uint32)
+    sign = ((r >> np.uint64(40)) & np.uint64(1)).astype(np.uint32)
+    bvals = ((sign << np.uint32(31)) | (exp << np.uint32(23)) | mant).astype(np.uint32)
+    bvals[5::47] = special_values().view(np.uint32)[[0, 1, 2, 19, 20, 21, 22, 23, 0, 1, 2, 19, 20]][:bvals[5::47].size]
+    avals = np.concatenate([bvals[100:103], np.array([0x7FC00000], np.uint32)])
+    C = torch.empty((4, bvals.size), dtype=torch.float32, device="cuda")
+    am.approx_gemm(0, 0, 4, bvals.size, 1, dev(avals.view(np.float32).reshape(4, 1)), 1,
+                   dev(bvals.view(np.float32).reshape(1, -1)), bvals.size, C, bvals.size)
+    got = host(C).view(np.uint32)
+    want = oracle.amsim_bits(np.repeat(avals, bvals.size), np.tile(bvals, 4), t, M).reshape(4, bvals.size)
+    want = np.where(want == 0x80000000, 0, want).astype(np.uint32)
+    gnan = np.isnan(got.view(np.float32))
+    assert np.array_equal(gnan, np.isnan(want.view(np.float32)))
+    assert np.count_nonzero(got[~gnan] != want[~gnan]) == 0
+    A = normal(970 + M, (2, 700))
+    B = normal(971 + M, (700, 900))
+    R, S = oracle.gemm(A, B, t, M)
+    gate(host(am.gemm(dev(A), dev(B))), R, S, what=f"gemv {name}")
 
 
 def test_gemv_special_values_and_padding(am):
