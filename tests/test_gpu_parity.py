@@ -40,6 +40,9 @@ def table(name):
             _TABLES[name] = (8, oracle.lut_perturb(8, oracle.lut_generate(8, "exact"), pm_one(PERTURB_SEED, 1 << 16)))
         elif name == "mitchell3":
             _TABLES[name] = (3, oracle.lut_generate(3, "mitchell"))
+        elif name.startswith("arbitrary"):      # every entry a seeded random 16-bit word
+            M = int(name[len("arbitrary"):])
+            _TABLES[name] = (M, (splitmix64(7200 + M, 1 << (2 * M)) >> np.uint64(48)).astype(np.uint16))
         else:
             raise KeyError(name)
     return _TABLES[name]
@@ -82,7 +85,10 @@ def _operand_values(M, exps):
     return np.concatenate(vals + [sp]).astype(np.uint32)
 
 
-@pytest.mark.parametrize("name", ["exact7", "mitchell7", "perturbed8", "mitchell3"])
+ALL_WIDTHS = ["arbitrary1", "arbitrary2", "arbitrary4", "arbitrary5", "arbitrary6", "arbitrary8"]
+
+
+@pytest.mark.parametrize("name", ["exact7", "mitchell7", "perturbed8", "mitchell3"] + ALL_WIDTHS)
 @pytest.mark.parametrize("exps", ["moderate", "extreme", "moderate_checked"])
 def test_products_bit_exact(am, name, exps):
     """C = a b^T with k = 1: every output is +0 + one approximate product."""
@@ -127,6 +133,21 @@ def test_gemm_parity(am, shape, transA, transB):
     R, S = oracle.gemm(A, B, t, M, transA=bool(transA), transB=bool(transB))
     C = am.gemm(dev(A), dev(B), transA=bool(transA), transB=bool(transB))
     gate(host(C), R, S, what=f"gemm {shape} {transA}{transB}")
+
+
+@pytest.mark.parametrize("name", ALL_WIDTHS)
+def test_gemm_and_conv_every_table_width(am, name):
+    """Tables of M = 1..8 with arbitrary entries (the LDS image's column
+    stride and pad position follow M): a GEMM and a Conv2D forward pass."""
+    M, t = use(am, name)
+    A = normal(640 + M, (150, 333))
+    B = normal(641 + M, (333, 90))
+    R, S = oracle.gemm(A, B, t, M)
+    gate(host(am.gemm(dev(A), dev(B))), R, S, what=f"gemm {name}")
+    x = normal(642 + M, (2, 9, 11, 5))
+    w = normal(643 + M, (3, 3, 5, 7))
+    Y, YS = oracle.conv2d_fwd(x, w, t, M, (1, 2), (1, 1))
+    gate(host(am.conv2d_fwd(dev(x), dev(w), (1, 2), (1, 1))), Y, YS, what=f"conv {name}")
 
 
 def test_gemm_leading_dimensions_and_untouched_padding(am):
