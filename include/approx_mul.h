@@ -31,6 +31,10 @@
  *    stream (decoded operands, split-reduction partials). Calls queued on one
  *    stream reuse that stream's arena in order; calls on different streams
  *    use different arenas. The arena only grows; approx_release() frees it.
+ *  - Once a stream's arena is large enough (after a call of the same or
+ *    larger sizes on that stream), a compute call queues kernel launches
+ *    only: no allocation, copy, memset or synchronisation. Such calls can be
+ *    captured into a HIP graph on that stream and replayed.
  *  - Return value: APPROX_OK (0) or a negative status. Argument checks run
  *    before any work is queued; on an error nothing is written.
  */
