@@ -248,8 +248,20 @@ __device__ __forceinline__ void decode_generic_body(const DecodeParams& p, uint3
 
 // Image layouts, one workgroup per output row: the source row (an NHWC row
 // of x, or of dy for the padded, dilated errors) is staged in LDS with
-// coalesced loads, then the output row is written contiguously.
+// coalesced (16-byte where aligned) loads, then the output row is written
+// contiguously, 2 or 4 Words (16 or 32 bytes) per thread and step.
 constexpr int IMG_ROW_FLOATS_MAX = 8192;   // 32 KB of LDS per workgroup
+
+__device__ __forceinline__ void store_words(Word* out, const Word (&wd)[4], int n, bool vec)
+{
+    if (vec) {
+        uint4* o = reinterpret_cast<uint4*>(out);
+        o[0] = make_uint4(wd[0].w, wd[0].se, wd[1].w, wd[1].se);
+        if (n == 4) o[1] = make_uint4(wd[2].w, wd[2].se, wd[3].w, wd[3].se);
+    } else {
+        for (int t = 0; t < n; ++t) out[t] = wd[t];
+    }
+}
 
 __device__ __forceinline__ void decode_img_body(const DecodeParams& p, uint3 bid, uint3 gdim, float* row)
 {
@@ -277,42 +289,65 @@ __device__ __forceinline__ void decode_img_body(const DecodeParams& p, uint3 bid
     if (srow >= 0) {
         const int rows_per_image = p.layout == L_IMG_DGRAD ? p.P : p.H;
         const float* src = p.src + ((int64_t)n * rows_per_image + srow) * p.row_floats;
-        for (int i = threadIdx.x; i < p.row_floats; i += 256) row[i] = src[i];
+        if ((p.row_floats & 3) == 0 && (reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
+            const float4* s4 = reinterpret_cast<const float4*>(src);
+            float4* r4 = reinterpret_cast<float4*>(row);
+            for (int i = threadIdx.x; i < (p.row_floats >> 2); i += 256) r4[i] = s4[i];
+        } else {
+            for (int i = threadIdx.x; i < p.row_floats; i += 256) row[i] = src[i];
+        }
     }
     __syncthreads();
-    if (p.layout == L_IMG_FWD) {                   // [Cb][Wp][4]
-        const int per_row = p.Cb * p.Wp * 4;
-        Word* out = dst + (int64_t)r * per_row;
-        for (int o = threadIdx.x; o < per_row; o += 256) {
-            const uint32_t t = o & 3u, q = (uint32_t)o >> 2;
-            const uint32_t cb = fdiv(q, p.fd_Wp);
-            const int w = (int)(q - cb * (uint32_t)p.Wp) - p.pw, c = (int)(cb * 4u + t);
-            out[o] = (srow >= 0 && c < p.C && w >= 0 && w < p.W)
-                         ? decode_bits(__float_as_uint(row[w * p.C + c]), p.M, p.lane_role, emin, emax, p.elo, p.ehi)
-                         : zero_word(p.M, p.lane_role);
+    auto dec = [&](float v) { return decode_bits(__float_as_uint(v), p.M, p.lane_role, emin, emax, p.elo, p.ehi); };
+    const Word z = zero_word(p.M, p.lane_role);
+    if (p.layout == L_IMG_FWD || p.layout == L_IMG_DGRAD) {
+        // [Cb][Wp][4] (fwd) or [Kb][Wd][4] (dgrad): item q = one (channel block, column), 4 Words
+        const bool fwd = p.layout == L_IMG_FWD;
+        const int CH = fwd ? p.C : p.K;            // channels of a source pixel
+        const int items = (fwd ? p.Cb : p.Kb) * p.Wp;
+        Word* out = dst + (int64_t)r * items * 4;
+        for (int q = threadIdx.x; q < items; q += 256) {
+            const uint32_t blk = fdiv((uint32_t)q, p.fd_Wp);
+            const int wq = q - (int)blk * p.Wp;
+            int px = -1;                           // source pixel of this column
+            if (srow >= 0) {
+                if (fwd) {
+                    const int w = wq - p.pw;
+                    if (w >= 0 && w < p.W) px = w;
+                } else {
+                    const int ww = wq - (p.S - 1 - p.pw);
+                    if (ww >= 0 && (p.sw == 1 || ww % p.sw == 0)) {
+                        const int qq = p.sw == 1 ? ww : ww / p.sw;
+                        if (qq < p.Q) px = qq;
+                    }
+                }
+            }
+            const int c0 = (int)blk * 4;
+            Word wd[4];
+            if (px >= 0 && (CH & 3) == 0) {        // 4 channels inside, 16 bytes of LDS
+                const float4 v = *reinterpret_cast<const float4*>(row + px * CH + c0);
+                wd[0] = dec(v.x); wd[1] = dec(v.y); wd[2] = dec(v.z); wd[3] = dec(v.w);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) wd[t] = (px >= 0 && c0 + t < CH) ? dec(row[px * CH + c0 + t]) : z;
+            }
+            store_words(out + (int64_t)q * 4, wd, 4, true);
         }
-    } else if (p.layout == L_IMG_DGRAD) {          // [Kb][Wd][4]
-        const int per_row = p.Kb * p.Wp * 4;
-        Word* out = dst + (int64_t)r * per_row;
-        for (int o = threadIdx.x; o < per_row; o += 256) {
-            const uint32_t t = o & 3u, q = (uint32_t)o >> 2;
-            const uint32_t kb = fdiv(q, p.fd_Wp);
-            const int ww = (int)(q - kb * (uint32_t)p.Wp) - (p.S - 1 - p.pw), ko = (int)(kb * 4u + t);
-            bool ok = srow >= 0 && ko < p.K && ww >= 0 && (p.sw == 1 || ww % p.sw == 0);
-            const int qq = !ok ? 0 : (p.sw == 1 ? ww : ww / p.sw);
-            ok = ok && qq < p.Q;
-            out[o] = ok ? decode_bits(__float_as_uint(row[qq * p.K + ko]), p.M, p.lane_role, emin, emax, p.elo, p.ehi)
-                        : zero_word(p.M, p.lane_role);
-        }
-    } else {                                       // L_IMG_WGRAD: [Wp][C]
+    } else {                                       // L_IMG_WGRAD: [Wp][C], 2 Words per item
         const int per_row = p.Wp * p.C;
         Word* out = dst + (int64_t)r * per_row;
-        for (int o = threadIdx.x; o < per_row; o += 256) {
-            const uint32_t wq = fdiv((uint32_t)o, p.fd_C);
-            const int c = (int)((uint32_t)o - wq * (uint32_t)p.C), w = (int)wq - p.pw;
-            out[o] = (srow >= 0 && w >= 0 && w < p.W)
-                         ? decode_bits(__float_as_uint(row[w * p.C + c]), p.M, p.lane_role, emin, emax, p.elo, p.ehi)
-                         : zero_word(p.M, p.lane_role);
+        const bool vec = (per_row & 1) == 0;       // rows (and so the pairs) 16-byte aligned
+        for (int o = threadIdx.x * 2; o < per_row; o += 512) {
+            Word wd[4];
+            const int cnt = min(2, per_row - o);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint32_t e = (uint32_t)(o + t);
+                const uint32_t wq = fdiv(e, p.fd_C);
+                const int c = (int)(e - wq * (uint32_t)p.C), w = (int)wq - p.pw;
+                wd[t] = (t < cnt && srow >= 0 && w >= 0 && w < p.W) ? dec(row[w * p.C + c]) : z;
+            }
+            store_words(out + o, wd, cnt, vec && cnt == 2);
         }
     }
     flush_stats(p.stats, emin, emax, linear_block(bid, gdim));
@@ -421,8 +456,9 @@ __global__ __launch_bounds__(256) void init_stats_kernel(int* stats)
 // Plain row copies with decode: out[kk][j] (kk < rows_out, j < Np) from
 // src[kk * ld + j] when kk < k and j < n (uniform panels of untransposed B
 // and of the weight-gradient errors). Workgroup (x, ., z) takes rows
-// [x * rb, x * rb + rb) of batch entry z as one run of elements, 4 loads in
-// flight per thread, so narrow panels still give every thread work.
+// [x * rb, x * rb + rb) of batch entry z as one run of 4-column quads (Np is
+// a multiple of 16): a 16-byte load where the source allows it, 32 bytes of
+// Words stored.
 __device__ __forceinline__ void decode_rows_body(const DecodeParams& p, uint3 bid, uint3 gdim, int rb)
 {
     int emin = 255, emax = 0;
@@ -430,27 +466,28 @@ __device__ __forceinline__ void decode_rows_body(const DecodeParams& p, uint3 bi
     const float* src = p.src_ptrs ? p.src_ptrs[b] : p.src + b * p.src_batch_stride;
     Word* dst = p.dst + b * p.dst_batch_stride;
     const int r0 = (int)bid.x * rb;
-    const uint32_t total = (uint32_t)min(rb, p.KB * 4 - r0) * (uint32_t)p.Np;
-    for (uint32_t e0 = threadIdx.x; e0 < total; e0 += 4 * 256) {
+    const uint32_t quads = (uint32_t)min(rb, p.KB * 4 - r0) * (uint32_t)(p.Np >> 2);
+    const bool vsrc = ((reinterpret_cast<uintptr_t>(src) & 15u) == 0) && ((p.ld & 3) == 0);
+    for (uint32_t q = threadIdx.x; q < quads; q += 256) {
+        const uint32_t row = fdiv(q * 4u, p.fd_Np);
+        const int col = (int)(q * 4u - row * (uint32_t)p.Np);
+        const int kk = r0 + (int)row;
+        const float* s = src + (int64_t)kk * p.ld + col;
         float v[4];
-        uint32_t row[4], col[4];
+        if (kk < p.k && vsrc && col + 3 < p.n) {
+            const float4 f = *reinterpret_cast<const float4*>(s);
+            v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+        } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t e = e0 + u * 256;
-            row[u] = fdiv(e, p.fd_Np);
-            col[u] = e - row[u] * (uint32_t)p.Np;
-            const int kk = r0 + (int)row[u];
-            v[u] = (e < total && kk < p.k && (int)col[u] < p.n) ? src[(int64_t)kk * p.ld + col[u]] : 0.0f;
+            for (int t = 0; t < 4; ++t) v[t] = (kk < p.k && col + t < p.n) ? s[t] : 0.0f;
         }
+        Word wd[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t e = e0 + u * 256;
-            if (e >= total) break;
-            const int kk = r0 + (int)row[u];
-            dst[(int64_t)kk * p.ldw + col[u]] = (kk < p.k && (int)col[u] < p.n)
-                ? decode_bits(__float_as_uint(v[u]), p.M, p.lane_role, emin, emax, p.elo, p.ehi)
+        for (int t = 0; t < 4; ++t)
+            wd[t] = (kk < p.k && col + t < p.n)
+                ? decode_bits(__float_as_uint(v[t]), p.M, p.lane_role, emin, emax, p.elo, p.ehi)
                 : zero_word(p.M, p.lane_role);
-        }
+        store_words(dst + (int64_t)kk * p.ldw + col, wd, 4, true);
     }
     flush_stats(p.stats, emin, emax, linear_block(bid, gdim));
 }
