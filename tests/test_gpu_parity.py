@@ -208,6 +208,34 @@ def test_gemm_tail_tiles_split(am, name):
     gate(C[rows, cols], R, S, what=f"tail split {name}")
 
 
+@pytest.mark.parametrize("mode", ["pointers", "strided"])
+def test_batched_tail_tiles_split(am, mode):
+    """257 or 260 batch entries of one output tile each: the entries of the
+    full round are computed whole, the last ones in reduction chunks (split
+    partials summed per entry, outputs found through the pointer array or the
+    batch stride)."""
+    M, t = use(am, "mitchell7")
+    m, n, k = 64, 16, 1024
+    batch = 257 if mode == "pointers" else 260
+    A = normal(821, (batch, m, k))
+    B = normal(822, (batch, k, n))
+    C = torch.full((batch, m, n + 2), -3.0, dtype=torch.float32, device="cuda")
+    dA, dB = dev(A), dev(B)
+    if mode == "pointers":
+        order = [(7 * i) % batch for i in range(batch)]   # entries not in memory order
+        pa = am.pointer_array([dA[i].data_ptr() for i in order])
+        pb = am.pointer_array([dB[i].data_ptr() for i in order])
+        pc = am.pointer_array([C[i].data_ptr() for i in order])
+        am.approx_gemm_batched(0, 0, m, n, k, pa, k, pb, n, pc, n + 2, batch)
+    else:
+        am.approx_gemm_strided_batched(0, 0, m, n, k, dA, k, m * k, dB, n, k * n, C, n + 2, m * (n + 2), batch)
+    got = host(C)
+    for i in range(batch):
+        R, S = oracle.gemm(A[i], B[i], t, M)
+        gate(got[i][:, :n], R, S, what=f"{mode} entry {i}")
+    assert np.all(got[:, :, n:] == -3.0)
+
+
 def test_gemm_k_zero_and_empty(am):
     use(am, "mitchell7")
     C = torch.full((5, 6), 3.0, device="cuda")
