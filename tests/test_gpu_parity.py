@@ -434,6 +434,28 @@ def test_workload3_conv_full_size_sampled(am):
         gate(full[idx], R, S, what=f"w3 {name}")
 
 
+def test_conv_tail_tiles_split(am):
+    """A 3 x 3 forward and input-gradient pass over 130 images of 32 x 32:
+    133,120 output pixels make 260 row tiles, so the last 4 tiles (the last
+    two images) are split and their partials summed. Every output of those
+    images is checked, and random outputs elsewhere."""
+    M, t = use(am, "mitchell7")
+    N, H, W, C, K = 130, 32, 32, 64, 64
+    x = normal(831, (N, H, W, C))
+    w = normal(832, (3, 3, C, K), std=0.06)
+    dy = normal(833, (N, H, W, K))
+    y = host(am.conv2d_fwd(dev(x), dev(w), (1, 1), (1, 1))).ravel()
+    dx = host(am.conv2d_dgrad(dev(dy), dev(w), x.shape, (1, 1), (1, 1))).ravel()
+    per_image = H * W * K
+    tail = np.arange((N - 2) * per_image, N * per_image, dtype=np.int64)
+    r = splitmix64(834, 2048)
+    for name, full, fn, args in (("fwd", y, oracle.conv2d_fwd, (x, w)),
+                                 ("dgrad", dx, oracle.conv2d_dgrad, (dy, w, x.shape))):
+        idx = np.concatenate([tail, (r % np.uint64(full.size)).astype(np.int64)])
+        R, S = fn(*args, t, M, (1, 1), (1, 1), idx=idx)
+        gate(full[idx], R, S, what=f"conv tail {name}")
+
+
 def test_workload4_gemm8192_sampled(am):
     M, t = use(am, "perturbed8")
     A, B = cfg.gemm_square(4, 8192)
