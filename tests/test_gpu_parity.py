@@ -468,6 +468,29 @@ def test_workload4_gemm8192_sampled(am):
     gate(C[rows, cols], R, S, what="w4")
 
 
+def test_gemm8192_exact_table_every_output(am):
+    """8192^3 with the exact M = 7 table: every approximate product is then
+    the exact product of the operands truncated to 7 fraction bits (no
+    N(0, 1) product leaves the range), so every one of the 67 M outputs must
+    lie within the gate of the float64 product of the truncated matrices
+    (a library routine: torch's float64 matmul)."""
+    M, t = use(am, "exact7")
+    A, B = cfg.gemm_square(4, 8192)
+    mask = np.uint32(0xFFFFFFFF ^ ((1 << (23 - M)) - 1))
+    At = (A.view(np.uint32) & mask).view(np.float32)
+    Bt = (B.view(np.uint32) & mask).view(np.float32)
+    print("gemm 8192^3, exact M = 7 table", flush=True)
+    dA, dB = dev(A), dev(B)
+    C = am.gemm(dA, dB)
+    del dA, dB
+    dAt, dBt = dev(At).double(), dev(Bt).double()
+    R = torch.matmul(dAt, dBt)
+    S = torch.matmul(dAt.abs(), dBt.abs())
+    del dAt, dBt
+    err = ((C.double() - R).abs() / S).max().item()
+    assert err <= 1e-5, err
+
+
 def test_workload5_attention_stages_sampled(am):
     """Each of the four approximate GEMM stages of multi-head attention on
     synthetic inputs of the workload's shapes (softmax probabilities are
