@@ -491,6 +491,49 @@ def test_gemm8192_exact_table_every_output(am):
     assert err <= 1e-5, err
 
 
+def test_conv_exact_table_every_output(am):
+    """The 3 x 3 Conv2D workload (NHWC 128 x 32 x 32 x 64 -> 64) with the
+    exact M = 7 table: every output of the forward, input-gradient and
+    weight-gradient passes against the float64 convolution of the truncated
+    tensors (IM2COL and matrix products in float64, padding slots zero), the
+    same property as for the 8192^3 GEMM above."""
+    import torch.nn.functional as F
+    M, t = use(am, "exact7")
+    sh = cfg.CONV_SHAPE
+    x, w, dy = cfg.conv_tensors()
+    st, pd = sh["stride"], sh["pad"]
+    N, H, W, C, K, R, S_ = sh["N"], sh["H"], sh["W"], sh["C"], sh["K"], sh["R"], sh["S"]
+    print("conv 3x3 workload, exact M = 7 table", flush=True)
+    y = am.conv2d_fwd(dev(x), dev(w), st, pd)
+    dx = am.conv2d_dgrad(dev(dy), dev(w), x.shape, st, pd)
+    dw = am.conv2d_wgrad(dev(x), dev(dy), w.shape, st, pd)
+    mask = np.uint32(0xFFFFFFFF ^ ((1 << (23 - M)) - 1))
+    trunc = lambda a: dev((a.view(np.uint32) & mask).view(np.float32)).double()
+    xt, wt, dyt = trunc(x), trunc(w), trunc(dy)
+    L = H * W                                   # stride 1, pad 1: P x Q = H x W
+    Wm = wt.permute(2, 0, 1, 3).reshape(C * R * S_, K)           # rows (c, r, s)
+    dym = dyt.reshape(N, L, K)
+
+    def check(got, ref, mag, what):
+        err = ((got.double() - ref).abs() / mag).max().item()
+        assert err <= 1e-5, (what, err)
+
+    for sign in (1, -1):      # sign 1: values; -1: magnitudes (the gate's sum of |products|)
+        f = (lambda v: v) if sign == 1 else torch.abs
+        cols = F.unfold(f(xt).permute(0, 3, 1, 2), (R, S_), padding=pd, stride=st)   # N x (C R S) x L
+        Y = (cols.transpose(1, 2) @ f(Wm)).reshape(N, H, W, K)
+        DW = (cols.permute(1, 0, 2).reshape(C * R * S_, N * L) @ f(dym).reshape(N * L, K))
+        DW = DW.reshape(C, R, S_, K).permute(1, 2, 0, 3)
+        DX = F.fold((f(dym) @ f(Wm).T).transpose(1, 2), (H, W), (R, S_), padding=pd, stride=st).permute(0, 2, 3, 1)
+        del cols
+        if sign == 1:
+            refs = (Y, DX, DW)
+        else:
+            check(y, refs[0], Y, "fwd")
+            check(dx, refs[1], DX, "dgrad")
+            check(dw, refs[2], DW, "wgrad")
+
+
 def test_workload5_attention_stages_sampled(am):
     """Each of the four approximate GEMM stages of multi-head attention on
     synthetic inputs of the workload's shapes (softmax probabilities are
