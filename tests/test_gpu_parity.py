@@ -351,6 +351,9 @@ CONV_GEOMS = [
     (3, 12, 12, 16, 24, 3, 3, (1, 1), (1, 1)),
     (2, 9, 11, 7, 33, 5, 5, (1, 1), (2, 2)),
     (2, 16, 16, 64, 64, 3, 3, (1, 1), (1, 1)),
+    (2, 5, 6, 3, 4, 1, 2, (2, 2), (2, 3)),     # padding wider than the filter: all-zero border outputs
+    (1, 1, 1, 3, 2, 3, 3, (1, 1), (1, 1)),     # a 1 x 1 image under a 3 x 3 filter
+    (1, 4, 5, 6, 3, 4, 5, (4, 5), (0, 0)),     # one output pixel, stride equal to the filter
 ]
 
 
