@@ -25,8 +25,8 @@
  * "Binarized Convolutional Neural Networks for Efficient Inference on GPUs",
  * arXiv 1808.00209, eq. (3)).
  *
- * Readings taken where the pages are silent or loose (each is restated in the
- * design notes of the repository):
+ * Readings taken where the pages are silent or loose (numbered as in the
+ * design notes of the repository, where each is restated):
  *   R1  Table entry: 16 bits. Bit 15 is the carry, bits 14..0 are the top 15
  *       bits of the product's 23-bit fraction (truncated).
  *   R2  Operand mantissa = the top M bits of the 23-bit fraction (truncated).
@@ -43,13 +43,13 @@
  *       exceeds it by one (carry 1). Anything else is rejected.
  *   R8  Convolution padding and dilation slots are zero operands that are
  *       multiplied (the IM2COL buffer holds zeros there), not omitted terms.
- *   R9  Sums are taken in double precision here; the sum of absolute
+ *   R13 Sums are taken in double precision here; the sum of absolute
  *       products is returned beside each output for the error gate.
- *   R10 The native multiplier (Section V: the simulator can call the
+ *   R17 The native multiplier (Section V: the simulator can call the
  *       hardware multiplication instead of the table, the reference point
  *       of Fig. 6) is the exact product of the two floats, rounded only when
  *       it is added to a sum. The sums take it when no table is given.
- *   R11 Formats (1, E, M) with E = 1..8 exponent bits (Section V allows any
+ *   R19 Formats (1, E, M) with E = 1..8 exponent bits (Section V allows any
  *       exponent width from 1 to 8 once an exponent cast is supplied, and
  *       gives no cast). The
  *       format's exponent has bias b = 2^(E-1) - 1 and normal unbiased
@@ -157,7 +157,7 @@ void orc_lut_perturb(int M, uint16_t *lut, const int8_t *delta)
 }
 
 /* ------------------------------------------------------------------ */
-/* Exponent cast to a (1, E, M) format (reading R11)                   */
+/* Exponent cast to a (1, E, M) format (reading R19)                   */
 /* ------------------------------------------------------------------ */
 /* FP32 biased exponents of the format's normal range: lowest and highest. */
 static int fmt_lo(int E) { return 127 + 1 - ((1 << (E - 1)) - 1); }
@@ -176,7 +176,7 @@ uint32_t orc_cast_bits(uint32_t x, int E)
 /* Algorithm 2: AMSim, one approximate product (Section V)             */
 /* ------------------------------------------------------------------ */
 /* The product of a and b in the format (1, E, M): both operands are cast to
- * the format first (R11), then Algorithm 2 runs with the format's range. */
+ * the format first (R19), then Algorithm 2 runs with the format's range. */
 uint32_t orc_amsim_bits_fmt(uint32_t a, uint32_t b, const uint16_t *lut, int M, int E)
 {
     a = orc_cast_bits(a, E);
@@ -204,7 +204,7 @@ uint32_t orc_amsim_bits_fmt(uint32_t a, uint32_t b, const uint16_t *lut, int M, 
     if (a_zero || b_zero) return sign << 31;
 
     /* normal case: biased exponent with the carry (reading R4), tested
-     * against the format's range (R11; FP32: 1..254) */
+     * against the format's range (R19; FP32: 1..254) */
     int e = (int)ea + (int)eb - 127 + (int)carry;
     if (e < fmt_lo(E)) return sign << 31;
     if (e > fmt_hi(E)) return (sign << 31) | 0x7F800000u;
@@ -223,7 +223,7 @@ float orc_amsim(float a, float b, const uint16_t *lut, int M)
 }
 
 /* ------------------------------------------------------------------ */
-/* The native multiplier (reading R10)                                 */
+/* The native multiplier (reading R17)                                 */
 /* ------------------------------------------------------------------ */
 /* Exact: two 24-bit significands give at most 48 bits (double holds 53),
  * and every product of two floats, subnormals included, lies inside
