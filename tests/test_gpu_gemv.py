@@ -61,9 +61,9 @@ def use(am, name):
 
 
 @pytest.mark.parametrize("name", ["mitchell7", "perturbed8", "arbitrary11", "native"])
-@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 13, 16])
 @pytest.mark.parametrize("transA", [0, 1])
-@pytest.mark.parametrize("nk", [(1, 1), (5, 7), (1000, 300), (1025, 2049), (4096, 513)])
+@pytest.mark.parametrize("nk", [(1, 1), (5, 7), (1000, 300), (1025, 2049), (4096, 513), (2050, 2048)])
 def test_gemv_parity(am, name, m, transA, nk):
     n, k = nk
     t, M = use(am, name)
@@ -150,6 +150,29 @@ def test_gemv_small_tables_bit_exact(am, name):
     B = normal(971 + M, (700, 900))
     R, S = oracle.gemm(A, B, t, M)
     gate(host(am.gemm(dev(A), dev(B))), R, S, what=f"gemv {name}")
+
+
+@pytest.mark.parametrize("m", [6, 16])
+def test_gemv_row_blocks_strided_batch_and_padding(am, m):
+    """5..16 rows (with k x n of at least 2^22) run as blocks of 4 rows
+    through the row-vector kernel: a strided batch with padded leading
+    dimensions, op(A) transposed or not; the padding of C is not written."""
+    t, M = use(am, "perturbed8")
+    n, k, batch = 2100, 2000, 2
+    for transA in (0, 1):
+        lda = (m if transA else k) + 5
+        ar = k if transA else m
+        A = normal(990 + m + transA, (batch, ar, lda))
+        B = normal(991 + m, (batch, k, n + 2))
+        C = torch.full((batch, m, n + 4), 5.0, dtype=torch.float32, device="cuda")
+        am.approx_gemm_strided_batched(transA, 0, m, n, k, dev(A), lda, ar * lda, dev(B), n + 2, k * (n + 2),
+                                       C, n + 4, m * (n + 4), batch)
+        got = host(C)
+        for b in range(batch):
+            Ab = A[b][:, :m] if transA else A[b][:, :k]
+            R, S = oracle.gemm(Ab, B[b][:, :n], t, M, transA=bool(transA))
+            gate(got[b][:, :n], R, S, what=f"row blocks m={m} tA={transA} b={b}")
+        assert np.all(got[:, :, n:] == 5.0)
 
 
 def test_gemv_special_values_and_padding(am):
