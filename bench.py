@@ -71,7 +71,7 @@ def traffic_record(workload):
     return rec.get("bytes_per_launch")
 
 
-def build_workload(config, am, torch, mult="table", table_bits=0, gemv=False):
+def build_workload(config, am, torch, mult="table", table_bits=0, gemv=False, gemv_rows=1):
     from datagen import configs as cfg
     from datagen import PERTURB_SEED, pm_one
 
@@ -93,7 +93,7 @@ def build_workload(config, am, torch, mult="table", table_bits=0, gemv=False):
     if config in (1, 4):
         size = 64 if config == 1 else 8192
         A, B = cfg.gemm_square(config, size)
-        rows = 1 if gemv else size     # --gemv: batch-1 inference through the same B
+        rows = gemv_rows if gemv else size     # --gemv: batch-1 (or few-row) inference through the same B
         A = A[:rows].copy()
         Ad, Bd = d(A), d(B)
         Cd = torch.empty((rows, size), dtype=torch.float32, device="cuda")
@@ -108,7 +108,7 @@ def build_workload(config, am, torch, mult="table", table_bits=0, gemv=False):
         if mult != "table":
             workload = f"gemm_{size}x{size}x{size}_" + ("native_fp32_fma" if mult == "native" else "torch_matmul_fp32")
         if gemv:
-            workload = workload.replace(f"gemm_{size}x", "gemv_1x", 1)
+            workload = workload.replace(f"gemm_{size}x", f"gemv_{rows}x", 1)
         info = dict(m=size, n=size, k=size, table=f"{model} M={M}" + (" +-1 perturbed" if pert is not None else ""))
         if mult != "table":
             info["table"] = "none (native FP32 multiplier)" if mult == "native" else "none (torch.matmul FP32)"
@@ -265,6 +265,9 @@ def main():
                          "cast to it before each product (8: FP32, the default)")
     ap.add_argument("--gemv", action="store_true",
                     help="with --config 1 or 4: one row of A (batch-1 inference), the row-vector kernel")
+    ap.add_argument("--rows", type=int, default=1,
+                    help="with --gemv: rows of A (small-batch inference; up to 16 run as 4-row blocks of the "
+                         "row-vector kernel)")
     ap.add_argument("--multiplier", choices=("table", "native", "library"), default="table",
                     help="table: the approximate multiplier (default); native: the library's FP32 FMA in "
                          "the same kernels; library: torch.matmul FP32 (GEMM workloads only)")
@@ -306,7 +309,12 @@ def main():
     torch.backends.cuda.matmul.allow_tf32 = False
     if args.gemv and args.config not in (1, 4):
         raise SystemExit("--gemv goes with the square GEMM workloads (--config 1 or 4)")
-    step, workload, info, host = build_workload(args.config, am, torch, args.multiplier, args.table_bits, args.gemv)
+    if args.rows != 1 and not args.gemv:
+        raise SystemExit("--rows goes with --gemv")
+    if args.gemv and not 1 <= args.rows <= 16:
+        raise SystemExit("--rows: 1 to 16")
+    step, workload, info, host = build_workload(args.config, am, torch, args.multiplier, args.table_bits, args.gemv,
+                                                args.rows)
     if args.exp_bits != 8:
         if args.multiplier != "table":
             raise SystemExit("--exp-bits applies to the table multiplier only")
@@ -350,9 +358,14 @@ def main():
     kern_s = kern_ms / 1e3
     mac_rate = macs * args.steps / kern_s if kern_s > 0 else 0.0     # MAC/s over kernel time
     if args.gemv and args.multiplier != "library":
-        # the row-vector kernel streams B from HBM: algorithmic bytes = A + B read + C written
-        nbytes = 4 * (host["A"].size + host["B"].size + host["A"].shape[0] * host["B"].shape[1])
-        achieved = nbytes / (kern_s / args.steps) / 1e9 if kern_s > 0 else 0.0
+        # the row-vector kernel streams B from HBM once per launch (a launch
+        # takes up to 4 rows of A): algorithmic bytes per launch = its rows of
+        # A + B read + its rows of C written
+        per_step = max(launches // max(args.steps, 1), 1)
+        rb = host["A"].shape[0] / per_step
+        kk, nn = host["B"].shape
+        nbytes = 4 * (rb * kk + kk * nn + rb * nn)
+        achieved = nbytes / (kern_s / max(launches, 1)) / 1e9 if kern_s > 0 else 0.0
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "amx::gemv_kernel",
                     "kernel_ms_avg": round(kern_ms / max(launches, 1), 4),
