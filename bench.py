@@ -17,7 +17,10 @@ same workload.
 multiplier (the FP32 fused multiply-add in place of the table: ApproxTrain
 Section V / Fig. 6 compare the simulated multiplier against the native one);
 --multiplier library times torch.matmul in FP32 on the GEMM workloads, for
-context. Neither is the headline.
+context. --table-bits M (9..11: tables in global memory), --exp-bits E
+(formats with fewer exponent bits) and --gemv [--rows R] (batch-1 or
+few-row inference through the row-vector kernel) time the other parts of
+the library. None of these is the headline.
 """
 import argparse
 import hashlib
