@@ -33,14 +33,20 @@ constexpr double kSplitMacRate = 6.0e12;
 constexpr double kSplitBytesRate = 4.0e12;
 constexpr int kSplitMax = 1024;
 constexpr int64_t kMaxPanelWords = (int64_t)1 << 31;
-// GEMMs with at most kRowVectorMaxRows rows in op(A) (B not transposed) and
-// a large enough k x n run as blocks of 4 rows through the row-vector kernel:
-// each block streams B once, well below the cost of the GEMM kernel's
-// 256-row tiles there (measured: 16 x 8192 x 8192 0.52 ms in 4 launches,
-// 17 x 8192 x 8192 1.60 ms in the GEMM kernel). For small k x n the launches'
-// fixed cost dominates (16 x 1024 x 1024: 0.111 against 0.088 ms).
-constexpr int kRowVectorMaxRows = 16;
-constexpr int64_t kRowVectorMinKN = (int64_t)1 << 22;
+// Few-row GEMMs (B not transposed) run in the row-vector kernel, in blocks
+// of 4 rows, instead of the GEMM kernel's 256-row tiles: always up to
+// kRowVectorRows rows; up to kRowVectorRowsWide rows when k * n is large (B
+// streams at full rate) or tiny (the launch dominates). Measured (M = 8,
+// row-vector against GEMM kernel): 32 x 8192 x 8192 0.78 / 1.62 ms,
+// 64 x 8192 x 8192 1.49 / 1.62 ms, 64 x 64 x 64 0.020 / 0.045 ms, but
+// 64 x 1024 x 1024 0.103 / 0.093 ms.
+constexpr int kRowVectorRows = 32;
+constexpr int kRowVectorRowsWide = 64;
+inline bool row_vector_fits(int m, int n, int k)
+{
+    const int64_t kn = (int64_t)k * n;
+    return m <= kRowVectorRows || (m <= kRowVectorRowsWide && (kn >= ((int64_t)1 << 22) || kn <= ((int64_t)1 << 16)));
+}
 
 struct DeviceTable {
     uint16_t* image = nullptr;  // lane-first LDS image (the allocation; `flat` lies in it)
@@ -413,9 +419,11 @@ int gemv_run(amx::GemvParams& g, int batch, float* C, int dev, hipStream_t strea
 {
     const int variant = g.M == 0 ? 3 : g.M <= 7 ? 0 : g.M == 8 ? 1 : 2;
     const int cols = amx::gemv_threads(variant) * amx::kGemvColsPerLane;
-    const int64_t blocks = cdiv(g.n, cols) * batch;
+    const int64_t blocks = cdiv(g.n, cols) * cdiv(g.m, amx::kGemvMaxRows) * batch;
     const int64_t target = kGemvTargetThreads / amx::gemv_threads(variant);
-    int s = (int)std::min<int64_t>(std::max<int64_t>(1, cdiv(target, blocks)), std::max(1, g.k / 8));
+    // as many splits as keep the items within one round of `target`
+    // workgroups (a few more items than that would run in a second round)
+    int s = (int)std::min<int64_t>(std::max<int64_t>(1, target / blocks), std::max(1, g.k / 8));
     g.chunk = (int)cdiv(g.k, s);
     g.splits = (int)cdiv(g.k, g.chunk);
     g.batch = batch;
@@ -507,26 +515,18 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
         return amx::launch_fill_zero(C, Cp, m, n, ldc, batch, strideC, stream) == hipSuccess ? APPROX_OK
                                                                                           : APPROX_EHIP;
     }
-    // Few rows: the row-vector kernel, 4 rows of op(A) per launch (each
-    // output is still summed by exactly one launch, in the same order).
-    // Pointer-array batches take it for up to 4 rows only: the row offsets of
-    // the later blocks would need pointer arrays of their own.
-    if (!transB && (m <= amx::kGemvMaxRows ||
-                    (m <= kRowVectorMaxRows && !arrays && (int64_t)k * n >= kRowVectorMinKN))) {
-        for (int r0 = 0; r0 < m; r0 += amx::kGemvMaxRows) {
-            amx::GemvParams g{};
-            g.A = A == nullptr ? nullptr : A + (transA ? (int64_t)r0 : (int64_t)r0 * lda);
-            g.A_ptrs = Ap; g.A_batch = strideA;
-            g.B = B; g.B_ptrs = Bp; g.B_batch = strideB;
-            g.lut = flat;
-            g.out_ptrs = Cp; g.out_batch = strideC;
-            g.M = M; g.m = std::min(amx::kGemvMaxRows, m - r0); g.n = n; g.k = k; g.lda = lda; g.ldb = ldb;
-            g.ldc = ldc; g.transA = transA;
-            format_range(dev, &g.elo, &g.ehi);
-            rc = gemv_run(g, batch, C == nullptr ? nullptr : C + (int64_t)r0 * ldc, dev, stream);
-            if (rc != APPROX_OK) return rc;
-        }
-        return APPROX_OK;
+    // Few rows: the row-vector kernel, in blocks of 4 rows of op(A) within
+    // one launch (each block streams its B columns; neighbouring blocks read
+    // them while they are in L2).
+    if (!transB && row_vector_fits(m, n, k)) {
+        amx::GemvParams g{};
+        g.A = A; g.A_ptrs = Ap; g.A_batch = strideA;
+        g.B = B; g.B_ptrs = Bp; g.B_batch = strideB;
+        g.lut = flat;
+        g.out_ptrs = Cp; g.out_batch = strideC;
+        g.M = M; g.m = m; g.n = n; g.k = k; g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.transA = transA;
+        format_range(dev, &g.elo, &g.ehi);
+        return gemv_run(g, batch, C, dev, stream);
     }
 
     Plan pl;

@@ -211,7 +211,8 @@ struct ReduceTilesParams {
     int first_tile, n_tiles;
 };
 
-// Row-vector GEMM (op(A) has at most kGemvMaxRows rows, B not transposed):
+// Row-vector GEMM (few rows of op(A), in blocks of kGemvMaxRows rows; B not
+// transposed):
 // lanes run over output columns, each operand is decoded in registers as it
 // is read, the table is read in index order from global memory, and the
 // reduction is split over grid.y into chunks of `chunk` indices.

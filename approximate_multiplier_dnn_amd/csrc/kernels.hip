@@ -1126,8 +1126,9 @@ __device__ __forceinline__ uint32_t se_of(uint32_t bits)
     return (e == 255u && (bits & 0x7FFFFFu)) ? 0x7FC00000u : se;
 }
 
-// C[r][j] = sum_kk approx(op(A)(r, kk), B[kk][j]) for r < m <= kGemvMaxRows.
-// Work item (column block, split, batch entry): lane t owns columns
+// C[r][j] = sum_kk approx(op(A)(r, kk), B[kk][j]) for few rows r < m.
+// Work item (column block, block of up to kGemvMaxRows rows, split, batch
+// entry): lane t owns columns
 // block * NTG * kGemvColsPerLane + t + c * NTG (coalesced across the wave for
 // every c) and sums reduction indices [split * chunk, (split + 1) * chunk) in
 // ascending order. Columns past n read column n - 1 and are not stored, so
@@ -1349,26 +1350,31 @@ __global__ __launch_bounds__(NTG) void gemv_kernel(GemvParams p)
     }
     constexpr int COLS = NTG * kGemvColsPerLane;
     const int nblk = (p.n + COLS - 1) / COLS;
-    const int items = nblk * p.splits * p.batch;
+    const int rblk = (p.m + kGemvMaxRows - 1) / kGemvMaxRows;    // blocks of up to 4 rows of op(A)
+    const int items = nblk * rblk * p.splits * p.batch;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
-        const int blk = item % nblk;
-        const int rest = item / nblk;
+        const int blk = item % nblk;               // column blocks fastest: a row block's
+        int rest = item / nblk;                    // neighbours read the same rows of B
+        const int rb = rest % rblk;
+        rest /= rblk;
         const int split = rest % p.splits;
         const int b = rest / p.splits;
-        const gfloat_cptr A = (gfloat_cptr)(p.A_ptrs ? p.A_ptrs[b] : p.A + b * p.A_batch);
+        const int r0 = rb * kGemvMaxRows, mr = min(kGemvMaxRows, p.m - r0);
+        const gfloat_cptr A = (gfloat_cptr)(p.A_ptrs ? p.A_ptrs[b] : p.A + b * p.A_batch) +
+                              (p.transA ? (int64_t)r0 : (int64_t)r0 * p.lda);
         const gfloat_cptr B = (gfloat_cptr)(p.B_ptrs ? p.B_ptrs[b] : p.B + b * p.B_batch);
         const int j0 = blk * COLS + threadIdx.x;
         const int k0 = split * p.chunk, k1 = min(p.k, k0 + p.chunk);
         float acc[kGemvMaxRows][kGemvColsPerLane];
         if (!NATIVE && (p.elo != 1 || p.ehi != 254)) {      // a format narrower than FP32
-            switch (p.m) {
+            switch (mr) {
             case 1: gemv_item<1, NATIVE, NTG, !NATIVE, PR>(p, lut, A, B, j0, k0, k1, acc); break;
             case 2: gemv_item<2, NATIVE, NTG, !NATIVE, PR>(p, lut, A, B, j0, k0, k1, acc); break;
             case 3: gemv_item<3, NATIVE, NTG, !NATIVE, PR>(p, lut, A, B, j0, k0, k1, acc); break;
             default: gemv_item<4, NATIVE, NTG, !NATIVE, PR>(p, lut, A, B, j0, k0, k1, acc); break;
             }
         } else {
-            switch (p.m) {
+            switch (mr) {
             case 1: gemv_item<1, NATIVE, NTG, false, PR>(p, lut, A, B, j0, k0, k1, acc); break;
             case 2: gemv_item<2, NATIVE, NTG, false, PR>(p, lut, A, B, j0, k0, k1, acc); break;
             case 3: gemv_item<3, NATIVE, NTG, false, PR>(p, lut, A, B, j0, k0, k1, acc); break;
@@ -1387,10 +1393,10 @@ __global__ __launch_bounds__(NTG) void gemv_kernel(GemvParams p)
         }
 #pragma unroll
         for (int r = 0; r < kGemvMaxRows; ++r) {
-            if (r >= p.m) break;
+            if (r >= mr) break;
 #pragma unroll
             for (int c = 0; c < kGemvColsPerLane; ++c)
-                if (j0 + c * NTG < p.n) out[(int64_t)r * ld + j0 + c * NTG] = acc[r][c];
+                if (j0 + c * NTG < p.n) out[(int64_t)(r0 + r) * ld + j0 + c * NTG] = acc[r][c];
         }
     }
 }

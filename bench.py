@@ -390,7 +390,7 @@ def main():
             "unit": "TOP/s",
             "frac": round(achieved / VALU_PEAK_TOPS, 4),
             "traffic": traffic_record(workload),
-            "kernel": "amx::main_kernel",
+            "kernel": "amx::gemv_kernel" if args.config == 1 else "amx::main_kernel",
             "kernel_ms_avg": round(kern_ms / max(launches, 1), 4),
             "launches_per_step": launches // max(args.steps, 1),
             "ops_per_mac": ops,

@@ -148,11 +148,11 @@ int approx_exponent_bits(void);
  * The first table operand of each product is the element of op(A).
  * (The GEMM kernel of ApproxTrain Section VI-D, behind Dense and, through
  * IM2COL, Conv2D.) m = 0 or n = 0 does nothing; k = 0 writes zeros. Calls
- * with transB = 0 and m <= 4, or m <= 16 with k * n >= 2^22 (batch-1 and
- * few-row inference), run a row-vector kernel (the section's separate
- * matrix-vector kernel), 4 rows of op(A) per launch: the same products and
- * order, with the reduction split into chunks as described above. In a
- * pointer-array batch only m <= 4 takes it.
+ * with transB = 0 and m <= 32 (or m <= 64 when k * n >= 2^22 or
+ * k * n <= 2^16), i.e. batch-1 and few-row inference, run a row-vector
+ * kernel (the section's separate matrix-vector kernel) in blocks of 4 rows
+ * of op(A): the same products and order, with the reduction split into
+ * chunks as described above.
  * Errors: APPROX_EINVAL (negative sizes, NULL pointers with non-empty
  * operands, lda/ldb/ldc smaller than the stored row length, flags not 0/1),
  * APPROX_ENOLUT, APPROX_EHIP.

@@ -154,9 +154,9 @@ def test_gemv_small_tables_bit_exact(am, name):
 
 @pytest.mark.parametrize("m", [6, 16])
 def test_gemv_row_blocks_strided_batch_and_padding(am, m):
-    """5..16 rows (with k x n of at least 2^22) run as blocks of 4 rows
-    through the row-vector kernel: a strided batch with padded leading
-    dimensions, op(A) transposed or not; the padding of C is not written."""
+    """5..16 rows run as blocks of 4 rows in the row-vector kernel: a strided
+    batch with padded leading dimensions, op(A) transposed or not; the
+    padding of C is not written."""
     t, M = use(am, "perturbed8")
     n, k, batch = 2100, 2000, 2
     for transA in (0, 1):
@@ -217,6 +217,31 @@ def test_gemv_batched(am):
     bp = am.pointer_array([Bd[i].data_ptr() for i in range(nb)])
     cp = am.pointer_array([C2[i].data_ptr() for i in range(nb)])
     am.approx_gemm_batched(0, 0, 1, n, k, ap, k, bp, n, cp, n, nb)
+    assert np.array_equal(host(C2), got)   # same kernel, same order
+
+
+@pytest.mark.parametrize("m,transA", [(7, 0), (11, 1), (16, 0)])
+def test_gemv_row_blocks_pointer_arrays(am, m, transA):
+    """5..16 rows through device pointer arrays: each entry's row blocks are
+    offset from its own pointer; results equal the strided batch's bits."""
+    t, M = use(am, "mitchell7")
+    nb, n, k = 4, 500, 300
+    ar, ac = (k, m) if transA else (m, k)
+    As = np.stack([normal(1940 + i, (ar, ac)) for i in range(nb)])
+    Bs = np.stack([normal(1950 + i, (k, n)) for i in range(nb)])
+    Ad, Bd = dev(As), dev(Bs)
+    C = torch.full((nb, m, n), -1.0, device="cuda")
+    am.approx_gemm_strided_batched(transA, 0, m, n, k, Ad, ac, ar * ac, Bd, n, k * n, C, n, m * n, nb)
+    got = host(C)
+    for i in range(nb):
+        R, S = oracle.gemm(As[i], Bs[i], t, M, transA=bool(transA))
+        gate(got[i], R, S, what=f"row blocks batch {i}")
+    order = [2, 0, 3, 1]
+    C2 = torch.full((nb, m, n), -1.0, device="cuda")
+    ap = am.pointer_array([Ad[i].data_ptr() for i in order])
+    bp = am.pointer_array([Bd[i].data_ptr() for i in order])
+    cp = am.pointer_array([C2[i].data_ptr() for i in order])
+    am.approx_gemm_batched(transA, 0, m, n, k, ap, ac, bp, n, cp, n, nb)
     assert np.array_equal(host(C2), got)   # same kernel, same order
 
 

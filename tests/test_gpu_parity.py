@@ -97,14 +97,16 @@ def test_products_bit_exact(am, name, exps):
     a = _operand_values(M, e)
     b = _operand_values(M, e[::-1])
     A = dev(a.view(np.float32).reshape(-1, 1))
-    B = dev(b.view(np.float32).reshape(1, -1))
+    B = dev(b.view(np.float32).reshape(-1, 1))
     C = torch.empty((a.size, b.size), dtype=torch.float32, device="cuda")
     print(f"products {name} {exps}: {a.size} x {b.size}", flush=True)
+    # B as a transposed k = 1 operand: the GEMM kernel for every row count
+    # (the row-vector kernel has its own products tests)
     if exps == "moderate_checked":
         with forced_checked():
-            am.approx_gemm(0, 0, a.size, b.size, 1, A, 1, B, b.size, C, b.size)
+            am.approx_gemm(0, 1, a.size, b.size, 1, A, 1, B, 1, C, b.size)
     else:
-        am.approx_gemm(0, 0, a.size, b.size, 1, A, 1, B, b.size, C, b.size)
+        am.approx_gemm(0, 1, a.size, b.size, 1, A, 1, B, 1, C, b.size)
     got = host(C).view(np.uint32)
     want = oracle.amsim_bits(np.repeat(a, b.size), np.tile(b, a.size), t, M).reshape(a.size, b.size)
     want = np.where(want == 0x80000000, 0, want).astype(np.uint32)     # +0 + (-0) = +0
