@@ -269,8 +269,8 @@ def main():
     ap.add_argument("--gemv", action="store_true",
                     help="with --config 1 or 4: one row of A (batch-1 inference), the row-vector kernel")
     ap.add_argument("--rows", type=int, default=1,
-                    help="with --gemv: rows of A (small-batch inference; up to 16 run as 4-row blocks of the "
-                         "row-vector kernel)")
+                    help="with --gemv: rows of A (small-batch inference, 1 to 64: 4-row blocks of the row-vector "
+                         "kernel)")
     ap.add_argument("--multiplier", choices=("table", "native", "library"), default="table",
                     help="table: the approximate multiplier (default); native: the library's FP32 FMA in "
                          "the same kernels; library: torch.matmul FP32 (GEMM workloads only)")
@@ -314,8 +314,8 @@ def main():
         raise SystemExit("--gemv goes with the square GEMM workloads (--config 1 or 4)")
     if args.rows != 1 and not args.gemv:
         raise SystemExit("--rows goes with --gemv")
-    if args.gemv and not 1 <= args.rows <= 16:
-        raise SystemExit("--rows: 1 to 16")
+    if args.gemv and not 1 <= args.rows <= 64:
+        raise SystemExit("--rows: 1 to 64")
     step, workload, info, host = build_workload(args.config, am, torch, args.multiplier, args.table_bits, args.gemv,
                                                 args.rows)
     if args.exp_bits != 8:
