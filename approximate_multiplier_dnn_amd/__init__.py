@@ -23,6 +23,8 @@ APPROX_ENOLUT = -2
 APPROX_EUNSUPPORTED = -3
 APPROX_EHIP = -4
 
+CONV_PASSES = {"fwd": 0, "dgrad": 1, "wgrad": 2}
+
 MODEL_EXACT = 0
 MODEL_MITCHELL = 1
 
@@ -32,8 +34,9 @@ EXPORTS = (
     "approx_exponent_bits_set", "approx_exponent_bits",
     "approx_gemm", "approx_gemm_strided_batched", "approx_gemm_batched",
     "approx_conv2d_fwd", "approx_conv2d_dgrad", "approx_conv2d_wgrad",
+    "approx_gemm_chunks", "approx_conv2d_chunks",
     "approx_profile_enable", "approx_profile_read",
-    "approx_status_string", "approx_release",
+    "approx_status_string", "approx_build_id", "approx_release",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -54,13 +57,17 @@ _lib.approx_gemm_strided_batched.argtypes = [_i] * 5 + [_vp, _i, _ll, _vp, _i, _
 _lib.approx_gemm_batched.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, _i, _vp]
 for _n in ("approx_conv2d_fwd", "approx_conv2d_dgrad", "approx_conv2d_wgrad"):
     getattr(_lib, _n).argtypes = [_i] * 11 + [_vp, _vp, _vp, _vp]
+_lib.approx_gemm_chunks.argtypes = [_i] * 6 + [_ll, _vp, _vp, _vp, _vp]
+_lib.approx_conv2d_chunks.argtypes = [_i] * 12 + [_ll, _vp, _vp]
 _lib.approx_status_string.argtypes = [_i]
 _lib.approx_status_string.restype = ctypes.c_char_p
+_lib.approx_build_id.argtypes = []
+_lib.approx_build_id.restype = ctypes.c_char_p
 _lib.approx_release.argtypes = []
 _lib.approx_profile_enable.argtypes = [_i]
 _lib.approx_profile_read.argtypes = [_vp, _vp]
 for _n in EXPORTS:
-    if _n != "approx_status_string":
+    if _n not in ("approx_status_string", "approx_build_id"):
         getattr(_lib, _n).restype = ctypes.c_int
 
 
@@ -82,6 +89,11 @@ def _check(rc, what):
 
 def approx_status_string(status):
     return _lib.approx_status_string(int(status)).decode()
+
+
+def approx_build_id():
+    """Stamp of the sources the loaded library was built from."""
+    return _lib.approx_build_id().decode()
 
 
 # ------------------------------------------------------------------ tables
@@ -175,6 +187,31 @@ def approx_gemm(transA, transB, m, n, k, A, lda, B, ldb, C, ldc, stream=None):
     """C (m x n, leading dimension ldc) = op(A) op(B) with approximate products."""
     return _check(_lib.approx_gemm(int(transA), int(transB), int(m), int(n), int(k), _ptr(A), int(lda),
                                    _ptr(B), int(ldb), _ptr(C), int(ldc), _stream(stream)), "approx_gemm")
+
+
+def approx_gemm_chunks(transA, transB, m, n, k, batch, b, i, j):
+    """Summation chunk length of each output (b[t], i[t], j[t]) of a GEMM
+    call with these sizes on the current device (k: one chunk)."""
+    bb = np.ascontiguousarray(np.broadcast_to(np.asarray(b, dtype=np.int32), np.shape(i)), dtype=np.int32).ravel()
+    ii = np.ascontiguousarray(i, dtype=np.int32).ravel()
+    jj = np.ascontiguousarray(j, dtype=np.int32).ravel()
+    assert ii.shape == jj.shape == bb.shape
+    out = np.zeros(ii.size, dtype=np.int64)
+    _check(_lib.approx_gemm_chunks(int(transA), int(transB), int(m), int(n), int(k), int(batch), ii.size,
+                                   bb.ctypes.data, ii.ctypes.data, jj.ctypes.data, out.ctypes.data),
+           "approx_gemm_chunks")
+    return out
+
+
+def approx_conv2d_chunks(pass_name, N, H, W, C, K, R, S, stride, pad, idx):
+    """Summation chunk length of the outputs at flat indices idx of a Conv2D
+    pass ("fwd", "dgrad" or "wgrad") on the current device."""
+    ix = np.ascontiguousarray(idx, dtype=np.int64).ravel()
+    out = np.zeros(ix.size, dtype=np.int64)
+    _check(_lib.approx_conv2d_chunks(CONV_PASSES[pass_name], int(N), int(H), int(W), int(C), int(K), int(R),
+                                     int(S), int(stride[0]), int(stride[1]), int(pad[0]), int(pad[1]), ix.size,
+                                     ix.ctypes.data, out.ctypes.data), "approx_conv2d_chunks")
+    return out
 
 
 def approx_gemm_strided_batched(transA, transB, m, n, k, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,

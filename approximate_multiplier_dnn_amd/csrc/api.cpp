@@ -72,6 +72,10 @@ int g_exp_bits[kMaxDevices];       // exponent width of the multiplier's format 
 bool g_profile = false;
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events;   // GEMM-kernel launches while profiling
 std::map<std::pair<int, hipStream_t>, Arena> g_arenas;
+// Device memory that a table load or an arena's growth superseded: kept until
+// approx_release, so that work already queued and HIP graphs captured
+// earlier never read freed memory.
+std::vector<std::pair<int, void*>> g_retired;
 
 int current_device(int* dev)
 {
@@ -85,27 +89,21 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 const size_t kStatsBytes = align256((amx::STAT_INTS + 1) * sizeof(int));
 
 // Scratch memory for one call on (device, stream): `bytes` after the stats
-// region (*out points past it; *stats at it). Grows only. Before freeing a
-// smaller arena the stream is synchronised, so earlier calls on it have
-// finished reading their operands. *ready: whether the stats hold the reset
-// values (the caller initialises them and sets it).
+// region (*out points past it; *stats at it). Grows only, at least doubling,
+// so the superseded arenas (retired, not freed) hold less memory than the
+// current one. *ready: whether the stats hold the reset values (the caller
+// initialises them and sets it).
 int arena_get(int dev, hipStream_t stream, size_t bytes, char** out, int** stats = nullptr, bool** ready = nullptr)
 {
     std::lock_guard<std::mutex> lock(g_mu);
     Arena& a = g_arenas[{dev, stream}];
     bytes += kStatsBytes;
     if (a.bytes < bytes) {
-        if (a.ptr != nullptr) {
-            if (hipStreamSynchronize(stream) != hipSuccess) return APPROX_EHIP;
-            if (hipFree(a.ptr) != hipSuccess) return APPROX_EHIP;
-            a.ptr = nullptr;
-            a.bytes = 0;
-        }
-        size_t want = bytes + bytes / 8;
-        if (hipMalloc(&a.ptr, want) != hipSuccess) {
-            a.ptr = nullptr;
-            return APPROX_EHIP;
-        }
+        const size_t want = std::max(bytes + bytes / 8, 2 * a.bytes);
+        void* p = nullptr;
+        if (hipMalloc(&p, want) != hipSuccess) return APPROX_EHIP;
+        if (a.ptr != nullptr) g_retired.emplace_back(dev, a.ptr);
+        a.ptr = p;
         a.bytes = want;
         a.stats_ready = false;
     }
@@ -113,6 +111,18 @@ int arena_get(int dev, hipStream_t stream, size_t bytes, char** out, int** stats
     if (stats != nullptr) *stats = static_cast<int*>(a.ptr);
     if (ready != nullptr) *ready = &a.stats_ready;   // std::map nodes are stable
     return APPROX_OK;
+}
+
+// Where a call's scratch comes from: the stream's arena.
+struct ScratchSource {
+    char* fixed = nullptr;
+};
+
+int scratch_get(const ScratchSource& src, int dev, hipStream_t stream, size_t bytes, char** out, int** stats,
+                bool** ready)
+{
+    (void)src;
+    return arena_get(dev, stream, bytes, out, stats, ready);
 }
 
 // Resident GEMM workgroups per device (CUs x blocks per CU), per kernel
@@ -204,6 +214,22 @@ int pick_shape(int m, int n, int* wr, int* wc)
     return twelve ? 1 : 0;
 }
 
+// Tile geometry of a GEMM-kernel call with an m x n output per batch entry.
+struct Tiling {
+    int shape, wr, wc, TM, TN, tiles_m, tiles_n;
+};
+
+Tiling tiling_of(int m, int n)
+{
+    Tiling t;
+    t.shape = pick_shape(m, n, &t.wr, &t.wc);
+    t.TM = t.wr * 64 * kShapes[t.shape].rows_per_lane;
+    t.TN = t.wc * kColsPerWave;
+    t.tiles_m = (int)cdiv(m, t.TM);
+    t.tiles_n = (int)cdiv(n, t.TN);
+    return t;
+}
+
 // Reduction split. The work items run in rounds over the resident
 // workgroups; a round costs its longest item. Two layouts are modelled:
 //  - every tile split into the same number of chunks (a split trades the
@@ -254,6 +280,35 @@ void plan_split(int64_t tiles, int KB, int64_t tile_macs_per_kstep, int64_t tile
     mp.items = (int64_t)mp.full_items + (int64_t)tail * bs;
 }
 
+// The split of a GEMM-kernel call (a function of its tiling, reduction
+// length and batch only).
+void split_of(int tiles_m, int tiles_n, int TM, int TN, int KB, int m, int n, int batch, MainParams& mp)
+{
+    const int64_t tiles = (int64_t)tiles_m * tiles_n * batch;
+    plan_split(tiles, KB, (int64_t)TM * TN * 4, (int64_t)TM * TN, (int64_t)m * n * batch, mp);
+}
+
+// Summation chunk, in positions of the reduction sequence (4 per k-step), of
+// output (b, i, j) of a GEMM-kernel call; KB * 4 when the output is summed
+// in one chunk.
+struct KernelOrder {
+    Tiling t;
+    MainParams mp{};
+    int KB = 0;
+
+    KernelOrder(int m, int n, int KB_, int batch) : t(tiling_of(m, n)), KB(KB_)
+    {
+        split_of(t.tiles_m, t.tiles_n, t.TM, t.TN, KB, m, n, batch, mp);
+    }
+    int64_t chunk(int b, int i, int j) const
+    {
+        if (mp.splits <= 1) return (int64_t)KB * 4;
+        const int tile = amx::tile_index(i / t.TM, j / t.TN, t.tiles_m, t.tiles_n);
+        const int64_t tl = (int64_t)b * t.tiles_m * t.tiles_n + tile;
+        return tl < mp.full_items ? (int64_t)KB * 4 : (int64_t)mp.chunk * 4;
+    }
+};
+
 bool force_checked()
 {
     const char* v = std::getenv("APPROX_FORCE_CHECKED");
@@ -276,16 +331,15 @@ struct Plan {
     amx::AssignParams asg{};      // M = 8 copy choice of the lane operands (groups of one half-wave)
 };
 
-int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M)
+int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M, const ScratchSource& src)
 {
     MainParams& mp = pl.mp;
     if (pl.lane_words * pl.batch >= kMaxPanelWords || pl.uni_words * pl.batch >= kMaxPanelWords)
         return APPROX_EUNSUPPORTED;
     // M = 0: native multiplier; M = 9..11: table in global memory
     const int lds_class = M == 0 ? 2 : M <= 7 ? 0 : M == 8 ? 1 : 3;
-    const int64_t tiles = (int64_t)mp.tiles_m * mp.tiles_n * pl.batch;
     const int64_t TM = (int64_t)mp.wr * 64 * kShapes[pl.shape].rows_per_lane, TN = (int64_t)mp.wc * kColsPerWave;
-    plan_split(tiles, mp.KB, TM * TN * 4, TM * TN, (int64_t)mp.m_out * mp.n_out * pl.batch, mp);
+    split_of(mp.tiles_m, mp.tiles_n, (int)TM, (int)TN, mp.KB, mp.m_out, mp.n_out, pl.batch, mp);
 
     const size_t lane_b = align256((size_t)pl.lane_words * pl.batch * sizeof(Word));
     const size_t uni_b = align256((size_t)pl.uni_words * pl.batch * sizeof(Word));
@@ -293,7 +347,7 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     char* base = nullptr;
     int* stats = nullptr;
     bool* stats_ready = nullptr;
-    int rc = arena_get(dev, stream, lane_b + uni_b + part_b, &base, &stats, &stats_ready);
+    int rc = scratch_get(src, dev, stream, lane_b + uni_b + part_b, &base, &stats, &stats_ready);
     if (rc != APPROX_OK) return rc;
     Word* lane_panel = reinterpret_cast<Word*>(base);
     Word* uni_panel = reinterpret_cast<Word*>(base + lane_b);
@@ -332,7 +386,9 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     mp.out_batch = pl.strideC;
     mp.ws = mp.splits > 1 ? partials : nullptr;
 
-    {
+    if (stats_ready == nullptr) {         // fixed scratch: initialised by every call
+        if (amx::launch_init_stats(stats, stream) != hipSuccess) return APPROX_EHIP;
+    } else {
         std::lock_guard<std::mutex> lock(g_mu);
         if (!*stats_ready) {
             if (amx::launch_init_stats(stats, stream) != hipSuccess) return APPROX_EHIP;
@@ -357,14 +413,14 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     bool prof;
     {
         std::lock_guard<std::mutex> lock(g_mu);
-        prof = g_profile;
+        prof = g_profile && src.fixed == nullptr;     // the allocation-free calls record no events
     }
     if (prof) {
         if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess) return APPROX_EHIP;
         if (hipEventRecord(ev0, stream) != hipSuccess) return APPROX_EHIP;
     }
     if (amx::launch_main(mp, lds_class, pl.gather, pl.shape, grid, stream) != hipSuccess) return APPROX_EHIP;
-    {
+    if (stats_ready != nullptr) {
         std::lock_guard<std::mutex> lock(g_mu);
         *stats_ready = true;      // the GEMM kernel's last workgroup resets them
     }
@@ -415,9 +471,13 @@ constexpr int64_t kGemvTargetThreads = 256 * 1024;
 
 int64_t g_gemv_slots[kMaxDevices][4];
 
-int gemv_run(amx::GemvParams& g, int batch, float* C, int dev, hipStream_t stream)
+int gemv_variant_of(int M) { return M == 0 ? 3 : M <= 7 ? 0 : M == 8 ? 1 : 2; }
+
+// The row-vector kernel's reduction split (sets g.chunk and g.splits); returns
+// the work items (column blocks x row blocks x splits x batch).
+int64_t gemv_split(amx::GemvParams& g, int batch)
 {
-    const int variant = g.M == 0 ? 3 : g.M <= 7 ? 0 : g.M == 8 ? 1 : 2;
+    const int variant = gemv_variant_of(g.M);
     const int cols = amx::gemv_threads(variant) * amx::kGemvColsPerLane;
     const int64_t blocks = cdiv(g.n, cols) * cdiv(g.m, amx::kGemvMaxRows) * batch;
     const int64_t target = kGemvTargetThreads / amx::gemv_threads(variant);
@@ -426,8 +486,14 @@ int gemv_run(amx::GemvParams& g, int batch, float* C, int dev, hipStream_t strea
     int s = (int)std::min<int64_t>(std::max<int64_t>(1, target / blocks), std::max(1, g.k / 8));
     g.chunk = (int)cdiv(g.k, s);
     g.splits = (int)cdiv(g.k, g.chunk);
+    return blocks * g.splits;
+}
+
+int gemv_run(amx::GemvParams& g, int batch, float* C, int dev, hipStream_t stream, const ScratchSource& src)
+{
+    const int variant = gemv_variant_of(g.M);
+    const int64_t items = gemv_split(g, batch);
     g.batch = batch;
-    const int64_t items = blocks * g.splits;
     if (items > INT32_MAX) return APPROX_EUNSUPPORTED;
     int64_t slots;
     {
@@ -444,7 +510,8 @@ int gemv_run(amx::GemvParams& g, int batch, float* C, int dev, hipStream_t strea
     float* partials = nullptr;
     if (g.splits > 1) {
         char* base = nullptr;
-        int rc = arena_get(dev, stream, (size_t)g.splits * batch * g.m * g.n * sizeof(float), &base);
+        int rc = scratch_get(src, dev, stream, (size_t)g.splits * batch * g.m * g.n * sizeof(float), &base, nullptr,
+                             nullptr);
         if (rc != APPROX_OK) return rc;
         partials = reinterpret_cast<float*>(base);
         g.out = partials;
@@ -455,7 +522,7 @@ int gemv_run(amx::GemvParams& g, int batch, float* C, int dev, hipStream_t strea
     bool prof;
     {
         std::lock_guard<std::mutex> lock(g_mu);
-        prof = g_profile;
+        prof = g_profile && src.fixed == nullptr;
     }
     if (prof) {
         if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess) return APPROX_EHIP;
@@ -510,14 +577,15 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
     rc = table_of(dev, &image, &M, &flat);
     if (rc != APPROX_OK) return rc;
     hipStream_t stream = static_cast<hipStream_t>(stream_v);
+    ScratchSource src;
 
     if (k == 0) {
         return amx::launch_fill_zero(C, Cp, m, n, ldc, batch, strideC, stream) == hipSuccess ? APPROX_OK
                                                                                           : APPROX_EHIP;
     }
     // Few rows: the row-vector kernel, in blocks of 4 rows of op(A) within
-    // one launch (each block streams its B columns; neighbouring blocks read
-    // them while they are in L2).
+    // one launch (the row blocks of one column block and chunk run on one
+    // XCD, so B is streamed once into its L2 for all of them).
     if (!transB && row_vector_fits(m, n, k)) {
         amx::GemvParams g{};
         g.A = A; g.A_ptrs = Ap; g.A_batch = strideA;
@@ -526,22 +594,22 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
         g.out_ptrs = Cp; g.out_batch = strideC;
         g.M = M; g.m = m; g.n = n; g.k = k; g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.transA = transA;
         format_range(dev, &g.elo, &g.ehi);
-        return gemv_run(g, batch, C, dev, stream);
+        g.force_checked = force_checked() ? 1 : 0;
+        return gemv_run(g, batch, C, dev, stream, src);
     }
 
     Plan pl;
     pl.batch = batch;
     pl.C = C;
     pl.strideC = strideC;
-    int wr, wc;
-    pl.shape = pick_shape(m, n, &wr, &wc);
+    const Tiling tg = tiling_of(m, n);
+    pl.shape = tg.shape;
     MainParams& mp = pl.mp;
-    mp.wr = wr;
-    mp.wc = wc;
-    const int TM = wr * 64 * kShapes[pl.shape].rows_per_lane, TN = wc * kColsPerWave;
-    mp.tiles_m = (int)cdiv(m, TM);
-    mp.tiles_n = (int)cdiv(n, TN);
-    const int Mp = mp.tiles_m * TM, Np = mp.tiles_n * TN;
+    mp.wr = tg.wr;
+    mp.wc = tg.wc;
+    mp.tiles_m = tg.tiles_m;
+    mp.tiles_n = tg.tiles_n;
+    const int Mp = mp.tiles_m * tg.TM, Np = mp.tiles_n * tg.TN;
     const int KB = (int)cdiv(k, 4);
 
     pl.Cp = Cp;
@@ -584,7 +652,7 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
     pl.asg.G2 = Mp / 32; pl.asg.S2 = 32 * 4;
     pl.asg.G3 = 4; pl.asg.S3 = 1;
     pl.asg.LS = 4; pl.asg.O = 0; pl.asg.E = Mp;
-    return run_plan(pl, dev, stream, image, M);
+    return run_plan(pl, dev, stream, image, M, src);
 }
 
 struct ConvShape {
@@ -610,6 +678,24 @@ void fill_geom(DecodeParams& d, const ConvShape& s)
 
 enum ConvKind { CONV_FWD, CONV_DGRAD, CONV_WGRAD };
 
+// The implicit GEMM of a pass: rows = output pixels (fwd, dgrad) or filter
+// taps x input channels (wgrad); columns = the output's channels.
+void conv_gemm_extent(ConvKind kind, const ConvShape& s, int* m, int* n)
+{
+    if (kind == CONV_FWD) { *m = s.N * s.P * s.Q; *n = s.K; }
+    else if (kind == CONV_DGRAD) { *m = s.N * s.H * s.W; *n = s.C; }
+    else { *m = s.R * s.S * s.C; *n = s.K; }
+}
+
+// k-steps (4 reduction positions each) of a pass: the sequences of the
+// header's Conv2D order, channels rounded up to a multiple of 4.
+int conv_ksteps(ConvKind kind, const ConvShape& s)
+{
+    if (kind == CONV_FWD) return s.R * s.S * (int)cdiv(s.C, 4);
+    if (kind == CONV_DGRAD) return s.R * s.S * (int)cdiv(s.K, 4);
+    return (int)cdiv((int64_t)s.N * s.P * s.Q, 4);
+}
+
 int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t2, float* out, void* stream_v)
 {
     int dev = 0;
@@ -633,17 +719,14 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
     u.src = t2;
 
     int m, n;
-    if (kind == CONV_FWD) { m = s.N * s.P * s.Q; n = s.K; }
-    else if (kind == CONV_DGRAD) { m = s.N * s.H * s.W; n = s.C; }
-    else { m = s.R * s.S * s.C; n = s.K; }
-    int wr, wc;
-    pl.shape = pick_shape(m, n, &wr, &wc);
-    mp.wr = wr;
-    mp.wc = wc;
-    const int TM = wr * 64 * kShapes[pl.shape].rows_per_lane, TN = wc * kColsPerWave;
-    mp.tiles_m = (int)cdiv(m, TM);
-    mp.tiles_n = (int)cdiv(n, TN);
-    const int Np = mp.tiles_n * TN;
+    conv_gemm_extent(kind, s, &m, &n);
+    const Tiling tg = tiling_of(m, n);
+    pl.shape = tg.shape;
+    mp.wr = tg.wr;
+    mp.wc = tg.wc;
+    mp.tiles_m = tg.tiles_m;
+    mp.tiles_n = tg.tiles_n;
+    const int Np = mp.tiles_n * tg.TN;
     mp.m_rows = m;
     mp.m_out = m;
     mp.n_out = n;
@@ -661,7 +744,7 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
         pl.lane_words = (int64_t)s.N * Hp * Cb * Wp * 4;
         u.layout = amx::L_W_FWD;
         u.Cp = Cp;
-        mp.KB = s.R * s.S * Cb;
+        mp.KB = conv_ksteps(kind, s);
         pl.uni_count = (int64_t)mp.KB * 4 * Np;
         pl.uni_words = (int64_t)mp.KB * 4 * u.ldw;
         const int rowB = Cb * Wp * 4;                 // one padded image row, in Words
@@ -685,7 +768,7 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
         pl.lane_words = (int64_t)s.N * Hd * Kb * Wd * 4;
         u.layout = amx::L_W_DGRAD;
         u.Kp = Kp;
-        mp.KB = s.R * s.S * Kb;
+        mp.KB = conv_ksteps(kind, s);
         pl.uni_count = (int64_t)mp.KB * 4 * Np;
         pl.uni_words = (int64_t)mp.KB * 4 * u.ldw;
         const int rowB = Kb * Wd * 4;
@@ -709,7 +792,7 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
         a.Hp = Hp; a.Wp = Wp;
         pl.lane_words = body + (int64_t)s.R * s.C * Wp;
         u.layout = amx::L_DY_WGRAD;
-        mp.KB = (int)cdiv(npq, 4);
+        mp.KB = conv_ksteps(kind, s);
         u.Kp = mp.KB * 4;
         u.KB = mp.KB;
         pl.uni_count = (int64_t)mp.KB * 4 * Np;
@@ -729,7 +812,7 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
         pl.asg.G3 = 1; pl.asg.S3 = 0;
         pl.asg.LS = 1; pl.asg.O = 0;
     }
-    return run_plan(pl, dev, stream, image, M);
+    return run_plan(pl, dev, stream, image, M, ScratchSource{});
 }
 
 }  // namespace
@@ -769,10 +852,7 @@ extern "C" int approx_lut_load(const uint16_t* lut, int M)
         return APPROX_EHIP;
     }
     std::lock_guard<std::mutex> lock(g_mu);
-    if (g_tables[dev].image != nullptr) {
-        if (hipDeviceSynchronize() != hipSuccess) { (void)hipFree(d); return APPROX_EHIP; }
-        (void)hipFree(g_tables[dev].image);
-    }
+    if (g_tables[dev].image != nullptr) g_retired.emplace_back(dev, g_tables[dev].image);
     g_tables[dev].image = d;
     g_tables[dev].flat = d + flat_at;
     g_tables[dev].M = M;
@@ -786,10 +866,7 @@ extern "C" int approx_native_load(void)
     int rc = current_device(&dev);
     if (rc != APPROX_OK) return rc;
     std::lock_guard<std::mutex> lock(g_mu);
-    if (g_tables[dev].image != nullptr) {
-        if (hipDeviceSynchronize() != hipSuccess) return APPROX_EHIP;
-        (void)hipFree(g_tables[dev].image);
-    }
+    if (g_tables[dev].image != nullptr) g_retired.emplace_back(dev, g_tables[dev].image);
     g_tables[dev] = DeviceTable{};
     g_tables[dev].native = true;
     return APPROX_OK;
@@ -873,6 +950,58 @@ extern "C" int approx_conv2d_wgrad(int N, int H, int W, int C, int K, int R, int
     return conv_impl(CONV_WGRAD, s, x, dy, dw, stream);
 }
 
+extern "C" int approx_gemm_chunks(int transA, int transB, int m, int n, int k, int batch, long long count,
+                                  const int* b, const int* i, const int* j, long long* chunk)
+{
+    if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1)) return APPROX_EINVAL;
+    if (m < 0 || n < 0 || k < 0 || batch < 0 || count < 0) return APPROX_EINVAL;
+    if (count > 0 && (b == nullptr || i == nullptr || j == nullptr || chunk == nullptr)) return APPROX_EINVAL;
+    for (long long t = 0; t < count; ++t)
+        if (b[t] < 0 || b[t] >= batch || i[t] < 0 || i[t] >= m || j[t] < 0 || j[t] >= n) return APPROX_EINVAL;
+    if (count == 0) return APPROX_OK;
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc != APPROX_OK) return rc;
+    const uint16_t* image = nullptr;
+    int M = 0;
+    rc = table_of(dev, &image, &M);
+    if (rc != APPROX_OK) return rc;
+    if (k == 0) {
+        for (long long t = 0; t < count; ++t) chunk[t] = 0;
+        return APPROX_OK;
+    }
+    if (!transB && row_vector_fits(m, n, k)) {        // the row-vector kernel: one split for every output
+        amx::GemvParams g{};
+        g.M = M; g.m = m; g.n = n; g.k = k;
+        gemv_split(g, batch);
+        for (long long t = 0; t < count; ++t) chunk[t] = g.splits > 1 ? g.chunk : k;
+        return APPROX_OK;
+    }
+    const KernelOrder ord(m, n, (int)cdiv(k, 4), batch);
+    for (long long t = 0; t < count; ++t) chunk[t] = std::min<int64_t>(ord.chunk(b[t], i[t], j[t]), k);
+    return APPROX_OK;
+}
+
+extern "C" int approx_conv2d_chunks(int pass, int N, int H, int W, int C, int K, int R, int S, int stride_h,
+                                    int stride_w, int pad_h, int pad_w, long long count, const long long* idx,
+                                    long long* chunk)
+{
+    if (pass < APPROX_CONV_FWD || pass > APPROX_CONV_WGRAD || count < 0) return APPROX_EINVAL;
+    ConvShape s;
+    // the shape checks of the compute calls (the tensor pointers are not used)
+    int rc = conv_check(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, &s, &s, &s, &s);
+    if (rc != APPROX_OK) return rc;
+    if (count > 0 && (idx == nullptr || chunk == nullptr)) return APPROX_EINVAL;
+    const ConvKind kind = pass == APPROX_CONV_FWD ? CONV_FWD : pass == APPROX_CONV_DGRAD ? CONV_DGRAD : CONV_WGRAD;
+    int m, n;
+    conv_gemm_extent(kind, s, &m, &n);
+    for (long long t = 0; t < count; ++t)
+        if (idx[t] < 0 || idx[t] >= (long long)m * n) return APPROX_EINVAL;
+    const KernelOrder ord(m, n, conv_ksteps(kind, s), 1);
+    for (long long t = 0; t < count; ++t) chunk[t] = ord.chunk(0, (int)(idx[t] / n), (int)(idx[t] % n));
+    return APPROX_OK;
+}
+
 extern "C" int approx_profile_enable(int on)
 {
     std::lock_guard<std::mutex> lock(g_mu);
@@ -912,6 +1041,15 @@ extern "C" const char* approx_status_string(int status)
     }
 }
 
+#ifndef APPROX_BUILD_ID
+#define APPROX_BUILD_ID "unstamped"
+#endif
+
+extern "C" const char* approx_build_id(void)
+{
+    return APPROX_BUILD_ID;
+}
+
 extern "C" int approx_release(void)
 {
     std::lock_guard<std::mutex> lock(g_mu);
@@ -924,6 +1062,11 @@ extern "C" int approx_release(void)
         if (hipFree(kv.second.ptr) != hipSuccess) rc = APPROX_EHIP;
     }
     g_arenas.clear();
+    for (auto& r : g_retired) {
+        if (hipSetDevice(r.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess) rc = APPROX_EHIP;
+        if (hipFree(r.second) != hipSuccess) rc = APPROX_EHIP;
+    }
+    g_retired.clear();
     for (int d = 0; d < kMaxDevices; ++d) {
         g_tables[d].native = false;
         if (g_tables[d].image == nullptr) continue;

@@ -45,6 +45,36 @@ __host__ __device__ inline int lut_col_entries(int M) { return M == 8 ? kRep8Col
 __host__ __device__ inline int lut_col_bytes(int M) { return lut_col_entries(M) * 2; }
 __host__ __device__ inline int lut_image_bytes(int M) { return (1 << M) * lut_col_bytes(M); }
 
+// Row tiles per swizzle group: the 32 workgroups of one XCD (consecutive work
+// items, see main_kernel) take 2 row tiles x 16 column tiles, which they
+// share through that XCD's L2 (per reduction index 2 x 256 rows and 16 x 128
+// columns of operand words at 8192^3, against 256 rows and 32 x 128 columns
+// in plain row-major order). Measured on 8192^3 (FETCH_SIZE per launch): 1 ->
+// 9.44 M KiB, 2 -> 6.38 M KiB, 4 -> 6.40 M KiB; the kernel time is unchanged
+// because the LDS lookups bind.
+constexpr int TILE_GROUP_M = 2;
+
+// Tile order of the GEMM kernel's work items: groups of TILE_GROUP_M row
+// tiles, column tiles outer, row tiles inner within a group.
+__host__ __device__ inline void tile_coords(int tile, int tiles_m, int tiles_n, int& tm, int& tn)
+{
+    const int group = tile / (TILE_GROUP_M * tiles_n);
+    const int first_m = group * TILE_GROUP_M;
+    const int gm = (tiles_m - first_m < TILE_GROUP_M ? tiles_m - first_m : TILE_GROUP_M);
+    const int in_group = tile - group * TILE_GROUP_M * tiles_n;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+}
+
+// The inverse: the position in that order of row tile tm, column tile tn.
+__host__ __device__ inline int tile_index(int tm, int tn, int tiles_m, int tiles_n)
+{
+    const int group = tm / TILE_GROUP_M;
+    const int first_m = group * TILE_GROUP_M;
+    const int gm = tiles_m - first_m < TILE_GROUP_M ? tiles_m - first_m : TILE_GROUP_M;
+    return group * TILE_GROUP_M * tiles_n + tn * gm + (tm - first_m);
+}
+
 // LDS footprint classes of the GEMM kernel (tables of M = 9..11 are read
 // from global memory instead).
 constexpr int LDS_SMALL = (1 << 7) * ((1 << 7) + 2) * 2;  // M <= 7: 33,280 bytes
@@ -211,11 +241,12 @@ struct ReduceTilesParams {
     int first_tile, n_tiles;
 };
 
-// Row-vector GEMM (few rows of op(A), in blocks of kGemvMaxRows rows; B not
-// transposed):
-// lanes run over output columns, each operand is decoded in registers as it
-// is read, the table is read in index order from global memory, and the
-// reduction is split over grid.y into chunks of `chunk` indices.
+// Row-vector GEMM (few rows of op(A): up to 32, or 64 when k * n >= 2^22 or
+// k * n <= 2^16; B not transposed), one launch of a persistent grid: a work
+// item is a block of kGemvMaxRows rows x a column block x a reduction chunk
+// of `chunk` indices; lanes run over output columns and each operand is
+// decoded in registers as it is read. Tables of M <= 8 are staged in LDS
+// once per workgroup, larger ones are read from global memory.
 constexpr int kGemvMaxRows = 4;
 constexpr int kGemvThreads = 256;            // table in global memory / native
 constexpr int kGemvLdsThreads = 1024;        // table staged in LDS (one copy per workgroup)
@@ -233,6 +264,7 @@ struct GemvParams {
     int M, m, n, k, lda, ldb, ldc, transA;
     int splits, chunk, batch;
     int elo, ehi;                 // FP32 biased exponents of the format's normal range (1, 254 for FP32)
+    int force_checked;            // 1: always use the per-product checked path
 };
 
 // variant: 0 = table of M <= 7 in LDS, 1 = M == 8 in LDS, 2 = table in global

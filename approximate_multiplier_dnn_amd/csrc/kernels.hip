@@ -633,14 +633,6 @@ __device__ __forceinline__ float checked_product_acc(float acc, uint32_t e, uint
     return acc + __uint_as_float(bits);
 }
 
-// Row tiles per swizzle group: the 32 workgroups of one XCD (consecutive work
-// items, see main_kernel) take 2 row tiles x 16 column tiles, which they
-// share through that XCD's L2 (per reduction index 2 x 256 rows and 16 x 128
-// columns of operand words at 8192^3, against 256 rows and 32 x 128 columns
-// in plain row-major order). Measured on 8192^3 (FETCH_SIZE per launch): 1 ->
-// 9.44 M KiB, 2 -> 6.38 M KiB, 4 -> 6.40 M KiB; the kernel time is unchanged
-// because the LDS lookups bind.
-constexpr int TILE_GROUP_M = 2;
 
 // Uniform words of one reduction index for this wave's 16 columns, spread
 // over the 4 lanes of each quad: lane i of a quad holds, in register
@@ -956,17 +948,6 @@ __device__ __forceinline__ void mainloop_checked(const MainParams& p, const Word
     }
 }
 
-// Tile order of the GEMM kernel's work items: groups of TILE_GROUP_M row
-// tiles, column tiles outer, row tiles inner within a group.
-__device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, int& tm, int& tn)
-{
-    const int group = tile / (TILE_GROUP_M * tiles_n);
-    const int first_m = group * TILE_GROUP_M;
-    const int gm = min(tiles_m - first_m, TILE_GROUP_M);
-    const int in_group = tile - group * TILE_GROUP_M * tiles_n;
-    tm = first_m + in_group % gm;
-    tn = in_group / gm;
-}
 
 // LDSB: bytes of the LDS table image (LDS_SMALL or LDS_LARGE), or NATIVE_LDS
 // where no table is staged (native multiplier, table in global memory).
@@ -1203,7 +1184,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
         // and 2^elo for a zero op(A).
         const int lo = (FMT || emin > emax) ? 1 : max(1, p.elo + 127 - emin);
         const int hi = emin > emax ? 253 : min(253, p.ehi + 126 - emax);
-        checked = lo > hi;
+        checked = lo > hi || p.force_checked;
         if (!checked) {
             bool bad = false;
             for (int kg = k0; kg < k1; kg += GG) {
@@ -1352,11 +1333,17 @@ __global__ __launch_bounds__(NTG) void gemv_kernel(GemvParams p)
     const int nblk = (p.n + COLS - 1) / COLS;
     const int rblk = (p.m + kGemvMaxRows - 1) / kGemvMaxRows;    // blocks of up to 4 rows of op(A)
     const int items = nblk * rblk * p.splits * p.batch;
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
-        const int blk = item % nblk;               // column blocks fastest: a row block's
-        int rest = item / nblk;                    // neighbours read the same rows of B
-        const int rb = rest % rblk;
-        rest /= rblk;
+    // Row blocks fastest: the items of one (column block, chunk) read the same
+    // stretch of B. Workgroup b runs on XCD b % 8, so the workgroups of one
+    // XCD take consecutive items (as in the GEMM kernel): those row blocks
+    // then share B through that XCD's L2.
+    const int G = gridDim.x;
+    const int v = (G & 7) == 0 ? (int)((blockIdx.x & 7u) * (unsigned)(G >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
+    for (int item = v; item < items; item += G) {
+        const int rb = item % rblk;
+        int rest = item / rblk;
+        const int blk = rest % nblk;
+        rest /= nblk;
         const int split = rest % p.splits;
         const int b = rest / p.splits;
         const int r0 = rb * kGemvMaxRows, mr = min(kGemvMaxRows, p.m - r0);

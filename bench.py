@@ -61,6 +61,20 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def build_lds_probe():
+    """The LDS lookup-rate probe (lds_probe.hip, beside this script), built
+    into _build/ with hipcc when missing or older than its sources."""
+    import subprocess
+    src = os.path.join(ROOT, "lds_probe.hip")
+    dep = os.path.join(ROOT, "approximate_multiplier_dnn_amd", "csrc", "replica.h")
+    out = os.path.join(ROOT, "_build", "lds_probe")
+    if not os.path.exists(out) or os.path.getmtime(out) < max(os.path.getmtime(src), os.path.getmtime(dep)):
+        os.makedirs(os.path.dirname(out), exist_ok=True)
+        subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang",
+                        "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", ROOT, "-o", out, src], check=True)
+    return out
+
+
 def traffic_record(workload):
     """HBM bytes per GEMM-kernel launch from the committed counter summary,
     if it was taken on the current kernel source; else None."""
@@ -289,8 +303,7 @@ def main():
 
     if args.lds_probe:
         import subprocess
-        probe = os.path.join(ROOT, "approximate_multiplier_dnn_amd", "lds_probe")
-        sys.exit(subprocess.run([probe]).returncode)
+        sys.exit(subprocess.run([build_lds_probe()]).returncode)
 
     import torch
 
@@ -361,9 +374,9 @@ def main():
     kern_s = kern_ms / 1e3
     mac_rate = macs * args.steps / kern_s if kern_s > 0 else 0.0     # MAC/s over kernel time
     if args.gemv and args.multiplier != "library":
-        # the row-vector kernel streams B from HBM once per launch (a launch
-        # takes up to 4 rows of A): algorithmic bytes per launch = its rows of
-        # A + B read + its rows of C written
+        # the row-vector kernel streams B from HBM once per launch (one launch
+        # takes all rows of A, in blocks of 4): algorithmic bytes per launch =
+        # its rows of A + B read + its rows of C written
         per_step = max(launches // max(args.steps, 1), 1)
         rb = host["A"].shape[0] / per_step
         kk, nn = host["B"].shape

@@ -14,10 +14,15 @@
  * gives NaN; infinity times a non-zero gives a signed infinity.
  *
  * Products are accumulated in FP32 (round to nearest even), starting from
- * +0.0, in ascending order of the reduction index. When a reduction is split
- * into chunks, each chunk is summed in ascending order and the chunk sums are
- * added in ascending chunk order; the chunking depends only on the shapes.
- * Results are therefore bitwise reproducible for the same inputs.
+ * +0.0, in ascending order of the reduction sequence. When an output's
+ * reduction is split, the sequence is cut into chunks of L consecutive
+ * positions; each chunk is summed from +0.0 in ascending order and the chunk
+ * sums are added from +0.0 in ascending chunk order. L depends only on the
+ * call's shapes and the loaded table's width (approx_gemm_chunks and
+ * approx_conv2d_chunks report it per output), so results are bitwise
+ * reproducible for the same inputs. The sequences: GEMM, the index p of
+ * op(A)(i,p) op(B)(p,j); Conv2D, see approx_conv2d_chunks. With the native
+ * multiplier every step is a fused multiply-add (one rounding).
  *
  * Conventions shared by all calls:
  *  - Tensors are FP32, row-major (C order), in device memory owned by the
@@ -30,11 +35,16 @@
  *  - The library keeps, per device, the loaded table and a scratch arena per
  *    stream (decoded operands, split-reduction partials). Calls queued on one
  *    stream reuse that stream's arena in order; calls on different streams
- *    use different arenas. The arena only grows; approx_release() frees it.
+ *    use different arenas. An arena only grows, at least doubling; a
+ *    superseded arena, like a superseded table, stays allocated until
+ *    approx_release(), which frees them all.
  *  - Once a stream's arena is large enough (after a call of the same or
  *    larger sizes on that stream), a compute call queues kernel launches
  *    only: no allocation, copy, memset or synchronisation. Such calls can be
- *    captured into a HIP graph on that stream and replayed.
+ *    captured into a HIP graph on that stream and replayed there; the graph
+ *    stays valid when later calls grow the arena or load another table (it
+ *    keeps using the memory it captured, including the table loaded at
+ *    capture time), until approx_release().
  *  - Return value: APPROX_OK (0) or a negative status. Argument checks run
  *    before any work is queued; on an error nothing is written.
  */
@@ -86,9 +96,11 @@ int approx_lut_build_from_model(int M, float (*mul)(float a, float b), uint16_t 
  * Load a table for use by the compute calls on the current device
  * (ApproxTrain Section VI: tables are loaded into the run-time library at run
  * time). `lut` is caller-owned host memory of 4^M entries in the format
- * above; it is copied during the call. Synchronous: the device is
- * synchronised before a previous table is released, so do not call it while
- * other threads queue work. Tables of M <= 8 (at most 128 KB of entries) are
+ * above; it is copied during the call (the copy is complete when it
+ * returns). Calls queued after it returns use the new table; work queued
+ * before keeps the previous one, which stays allocated until
+ * approx_release(). Not thread-safe against compute calls queued by other
+ * threads at the same time. Tables of M <= 8 (at most 128 KB of entries) are
  * staged in each workgroup's LDS (at M = 8 with second copies of part of each
  * column, 160 KB, which spread a wave's lookups over the LDS banks); tables of
  * M = 9..11 (512 KB to 8 MB, the top of the range Section V names) are read
@@ -110,8 +122,8 @@ int approx_lut_load(const uint16_t *lut, int M);
  * overflow of the accumulator gives a signed infinity, and the sign of a
  * zero result is not specified (the hardware FMA may return +0 where a tiny
  * negative sum rounds to zero). approx_lut_load
- * selects a table again. Synchronous, like approx_lut_load, when it releases
- * a loaded table. Errors: APPROX_EHIP.
+ * selects a table again. A previously loaded table is kept until
+ * approx_release(), as by approx_lut_load. Errors: APPROX_EHIP.
  */
 int approx_native_load(void);
 
@@ -220,6 +232,36 @@ int approx_conv2d_wgrad(int N, int H, int W, int C, int K, int R, int S,
                         const float *x, const float *dy, float *dw, void *stream);
 
 /*
+ * The summation order of compute calls (see the top of this header), for
+ * callers that reproduce results exactly. Host only: queues nothing, but
+ * uses the current device's table width, which selects between kernels.
+ *
+ * approx_gemm_chunks: for a GEMM call with these arguments (batch = 1 for
+ * approx_gemm), chunk[t] = the chunk length L of output (b[t], i[t], j[t]):
+ * L = k when that output's reduction is one chunk, 0 when k = 0.
+ *
+ * approx_conv2d_chunks: pass APPROX_CONV_FWD, _DGRAD or _WGRAD, output at
+ * flat index idx[t] of [N,P,Q,K], [N,H,W,C] or [R,S,C,K]. The reduction
+ * sequences (C4, K4: C and K rounded up to a multiple of 4; positions past C
+ * or K hold no product):
+ *   fwd:   term (r, s, c) at position (r*S + s)*C4 + c;
+ *   dgrad: term (r, s, k) at position ((R-1-r)*S + (S-1-s))*K4 + k (the
+ *          transposed, reversed filter of Section VI-B);
+ *   wgrad: term (n, p, q) at position (n*P + p)*Q + q.
+ * chunk[t] >= the sequence's length means one chunk.
+ * Errors: APPROX_EINVAL (bad sizes, flags, NULL arrays with count > 0,
+ * indices out of range), APPROX_ENOLUT.
+ */
+#define APPROX_CONV_FWD 0
+#define APPROX_CONV_DGRAD 1
+#define APPROX_CONV_WGRAD 2
+int approx_gemm_chunks(int transA, int transB, int m, int n, int k, int batch, long long count,
+                       const int *b, const int *i, const int *j, long long *chunk);
+int approx_conv2d_chunks(int pass, int N, int H, int W, int C, int K, int R, int S,
+                         int stride_h, int stride_w, int pad_h, int pad_w,
+                         long long count, const long long *idx, long long *chunk);
+
+/*
  * Kernel timing for benchmarks. While enabled (on != 0), every compute call
  * records a HIP event pair around its GEMM kernel, on the call's stream.
  * approx_profile_read waits for the recorded events, returns the number of
@@ -231,6 +273,11 @@ int approx_profile_read(int *launches, double *total_ms);
 
 /* Static text for a status code. */
 const char *approx_status_string(int status);
+
+/* Static text: the first 16 hex digits of a SHA-256 over the library's
+ * source files at build time ("unstamped" when built without it), so that a
+ * binary can be matched with the sources it came from. */
+const char *approx_build_id(void);
 
 /* Synchronise every device the library used, then free its tables and
  * arenas. A table must be loaded again before the next compute call. */

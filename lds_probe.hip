@@ -19,7 +19,7 @@
 #include <cstdio>
 #include <vector>
 
-#include "replica.h"
+#include "approximate_multiplier_dnn_amd/csrc/replica.h"
 
 namespace {
 

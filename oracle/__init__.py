@@ -67,6 +67,11 @@ def lib():
         L.orc_gemm_at.argtypes = [c_int] * 5 + [vp, c_int, vp, c_int, vp, c_int, c_int,
                                                  c_i64, vp, vp, vp, vp]
         L.orc_gemm_at.restype = None
+        L.orc_gemm_f32_at.argtypes = [c_int] * 5 + [vp, c_int, vp, c_int, vp, c_int, c_int,
+                                                     c_i64, vp, vp, vp, vp]
+        L.orc_gemm_f32_at.restype = None
+        L.orc_conv2d_f32.argtypes = [c_int] * 12 + [vp, vp, vp, c_int, c_int, c_i64, vp, vp, vp]
+        L.orc_conv2d_f32.restype = None
         for name in ("orc_conv2d_fwd", "orc_conv2d_dgrad", "orc_conv2d_wgrad"):
             f = getattr(L, name)
             f.argtypes = [c_int] * 11 + [vp, vp, vp, c_int, c_int, c_i64, vp, vp, vp]
@@ -181,23 +186,123 @@ def gemm(A, B, lut, M, transA=False, transB=False, E=8):
     return R, S
 
 
-def gemm_at(A, B, lut, M, rows, cols, transA=False, transB=False, E=8):
-    """The same sums at the (rows[t], cols[t]) outputs only."""
+def default_threads():
+    """Host threads for the threaded driver: the cores this process may use,
+    at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _threaded(count, threads, run):
+    """The threaded driver: run(lo, hi) computes outputs [lo, hi) with the
+    same per-output C code and returns a tuple of arrays; the output range is
+    cut into `threads` disjoint blocks run side by side (ctypes releases the
+    interpreter lock during the C calls). threads None or 1: one call."""
+    if not threads or threads <= 1 or count < 2 * threads:
+        return run(0, count)
+    from concurrent.futures import ThreadPoolExecutor
+    bounds = np.linspace(0, count, threads + 1).astype(np.int64)
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda i: run(int(bounds[i]), int(bounds[i + 1])), range(threads)))
+    return tuple(np.concatenate([p[j] for p in parts]) for j in range(len(parts[0])))
+
+
+def gemm_at(A, B, lut, M, rows, cols, transA=False, transB=False, E=8, threads=None):
+    """The same sums at the (rows[t], cols[t]) outputs only (threads: the
+    threaded driver over disjoint blocks of the outputs)."""
     A = _f32(A)
     B = _f32(B)
     m = A.shape[1] if transA else A.shape[0]
     k = A.shape[0] if transA else A.shape[1]
     n = B.shape[0] if transB else B.shape[1]
-    rows = np.ascontiguousarray(rows, dtype=np.int32)
-    cols = np.ascontiguousarray(cols, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32).ravel()
+    cols = np.ascontiguousarray(cols, dtype=np.int32).ravel()
     assert rows.shape == cols.shape
-    R = np.zeros(rows.size, dtype=np.float64)
-    S = np.zeros(rows.size, dtype=np.float64)
     t, tp, M = _table(lut, M)
-    lib().orc_gemm_at(int(transA), int(transB), m, n, k, _ptr(A), A.shape[1],
-                      _ptr(B), B.shape[1], tp, M, E, rows.size,
-                      _ptr(rows), _ptr(cols), _ptr(R), _ptr(S))
-    return R, S
+
+    def run(lo, hi):
+        R = np.zeros(hi - lo, dtype=np.float64)
+        S = np.zeros(hi - lo, dtype=np.float64)
+        r, c = rows[lo:hi], cols[lo:hi]
+        lib().orc_gemm_at(int(transA), int(transB), m, n, k, _ptr(A), A.shape[1],
+                          _ptr(B), B.shape[1], tp, M, E, hi - lo,
+                          _ptr(r), _ptr(c), _ptr(R), _ptr(S))
+        return R, S
+
+    return _threaded(rows.size, threads, run)
+
+
+def _chunks(chunk, count):
+    c = np.ascontiguousarray(np.broadcast_to(np.asarray(chunk, dtype=np.int64), (count,)))
+    assert np.all(c > 0)
+    return c
+
+
+def gemm_f32_at(A, B, lut, M, rows, cols, chunk, transA=False, transB=False, E=8, threads=None):
+    """The FP32 sums in the documented order (reading R20) at the outputs
+    (rows[t], cols[t]): reduction chunks of chunk[t] indices (a scalar
+    applies to every output; chunk >= k means one chunk). float32 array."""
+    A = _f32(A)
+    B = _f32(B)
+    m = A.shape[1] if transA else A.shape[0]
+    k = A.shape[0] if transA else A.shape[1]
+    n = B.shape[0] if transB else B.shape[1]
+    rows = np.ascontiguousarray(rows, dtype=np.int32).ravel()
+    cols = np.ascontiguousarray(cols, dtype=np.int32).ravel()
+    assert rows.shape == cols.shape
+    ch = _chunks(chunk, rows.size)
+    t, tp, M = _table(lut, M)
+
+    def run(lo, hi):
+        out = np.zeros(hi - lo, dtype=np.float32)
+        r, c, cc = rows[lo:hi], cols[lo:hi], ch[lo:hi]
+        lib().orc_gemm_f32_at(int(transA), int(transB), m, n, k, _ptr(A), A.shape[1],
+                              _ptr(B), B.shape[1], tp, M, E, hi - lo,
+                              _ptr(r), _ptr(c), _ptr(cc), _ptr(out))
+        return (out,)
+
+    return _threaded(rows.size, threads, run)[0]
+
+
+def gemm_f32(A, B, lut, M, chunk, transA=False, transB=False, E=8):
+    """gemm_f32_at over every output; chunk: scalar or an m x n array."""
+    m = A.shape[1] if transA else A.shape[0]
+    n = B.shape[0] if transB else B.shape[1]
+    rows, cols = np.meshgrid(np.arange(m, dtype=np.int32), np.arange(n, dtype=np.int32), indexing="ij")
+    ch = np.broadcast_to(np.asarray(chunk, dtype=np.int64), (m, n)).ravel()
+    return gemm_f32_at(A, B, lut, M, rows.ravel(), cols.ravel(), ch, transA, transB, E).reshape(m, n)
+
+
+CONV_PASSES = {"fwd": 0, "dgrad": 1, "wgrad": 2}
+
+
+def conv2d_f32(pass_name, t1, t2, geom, lut, M, chunk, idx=None, E=8, threads=None):
+    """FP32 sums of a Conv2D pass in the documented order (reading R20) at
+    flat output indices idx (all outputs when None). geom = (N, H, W, C, K,
+    R, S, (sh, sw), (ph, pw)); t1, t2 as for conv2d_fwd / dgrad / wgrad
+    (x, w / dy, w / x, dy)."""
+    N, H, W, C, K, R, S, (sh, sw), (ph, pw) = geom
+    P, Q = conv_out_hw(H, W, R, S, (sh, sw), (ph, pw))
+    total = {"fwd": N * P * Q * K, "dgrad": N * H * W * C, "wgrad": R * S * C * K}[pass_name]
+    if idx is None:
+        idx = np.arange(total, dtype=np.int64)
+    idx = np.ascontiguousarray(idx, dtype=np.int64).ravel()
+    assert idx.size == 0 or (idx.min() >= 0 and idx.max() < total)
+    ch = _chunks(chunk, idx.size)
+    t1, t2 = _f32(t1), _f32(t2)
+    t, tp, M = _table(lut, M)
+
+    def run(lo, hi):
+        out = np.zeros(hi - lo, dtype=np.float32)
+        ix, cc = idx[lo:hi], ch[lo:hi]
+        lib().orc_conv2d_f32(CONV_PASSES[pass_name], N, H, W, C, K, R, S, sh, sw, ph, pw, _ptr(t1), _ptr(t2),
+                             tp, M, E, hi - lo, _ptr(ix), _ptr(cc), _ptr(out))
+        return (out,)
+
+    return _threaded(idx.size, threads, run)[0]
 
 
 # ---------------------------------------------------------------- Conv2D
@@ -208,36 +313,45 @@ def conv_out_hw(H, W, R, S, stride, pad):
     return (H + 2 * ph - R) // sh + 1, (W + 2 * pw - S) // sw + 1
 
 
-def _conv(name, shape_out, geomargs, t1, t2, lut, M, idx, E=8):
+def _conv(name, shape_out, geomargs, t1, t2, lut, M, idx, E=8, threads=None):
     t1 = _f32(t1)
     t2 = _f32(t2)
     t, tp, M = _table(lut, M)
-    if idx is None:
+    if idx is None and not threads:
         total = int(np.prod(shape_out))
         R = np.zeros(total, dtype=np.float64)
         S = np.zeros(total, dtype=np.float64)
         getattr(lib(), name)(*geomargs, _ptr(t1), _ptr(t2), tp, M, E, 0, None,
                              _ptr(R), _ptr(S))
         return R.reshape(shape_out), S.reshape(shape_out)
-    idx = np.ascontiguousarray(idx, dtype=np.int64)
-    R = np.zeros(idx.size, dtype=np.float64)
-    S = np.zeros(idx.size, dtype=np.float64)
-    getattr(lib(), name)(*geomargs, _ptr(t1), _ptr(t2), tp, M, E, idx.size,
-                         _ptr(idx), _ptr(R), _ptr(S))
-    return R, S
+    whole = idx is None
+    if whole:
+        idx = np.arange(int(np.prod(shape_out)), dtype=np.int64)
+    idx = np.ascontiguousarray(idx, dtype=np.int64).ravel()
+
+    def run(lo, hi):
+        R = np.zeros(hi - lo, dtype=np.float64)
+        S = np.zeros(hi - lo, dtype=np.float64)
+        ix = idx[lo:hi]
+        getattr(lib(), name)(*geomargs, _ptr(t1), _ptr(t2), tp, M, E, hi - lo,
+                             _ptr(ix), _ptr(R), _ptr(S))
+        return R, S
+
+    R, S = _threaded(idx.size, threads, run)
+    return (R.reshape(shape_out), S.reshape(shape_out)) if whole else (R, S)
 
 
-def conv2d_fwd(x, w, lut, M, stride=(1, 1), pad=(0, 0), idx=None, E=8):
+def conv2d_fwd(x, w, lut, M, stride=(1, 1), pad=(0, 0), idx=None, E=8, threads=None):
     """x: NHWC, w: RSCK. Returns (Y, YS) of shape NPQK (or at flat idx)."""
     N, H, W, C = x.shape
     R, S, C2, K = w.shape
     assert C == C2
     P, Q = conv_out_hw(H, W, R, S, stride, pad)
     g = (N, H, W, C, K, R, S, stride[0], stride[1], pad[0], pad[1])
-    return _conv("orc_conv2d_fwd", (N, P, Q, K), g, x, w, lut, M, idx, E)
+    return _conv("orc_conv2d_fwd", (N, P, Q, K), g, x, w, lut, M, idx, E, threads)
 
 
-def conv2d_dgrad(dy, w, x_shape, lut, M, stride=(1, 1), pad=(0, 0), idx=None, E=8):
+def conv2d_dgrad(dy, w, x_shape, lut, M, stride=(1, 1), pad=(0, 0), idx=None, E=8, threads=None):
     """dy: NPQK, w: RSCK, x_shape = (N, H, W, C). Returns (dX, dXS)."""
     N, H, W, C = x_shape
     R, S, C2, K = w.shape
@@ -245,10 +359,10 @@ def conv2d_dgrad(dy, w, x_shape, lut, M, stride=(1, 1), pad=(0, 0), idx=None, E=
     P, Q = conv_out_hw(H, W, R, S, stride, pad)
     assert dy.shape == (N, P, Q, K)
     g = (N, H, W, C, K, R, S, stride[0], stride[1], pad[0], pad[1])
-    return _conv("orc_conv2d_dgrad", (N, H, W, C), g, dy, w, lut, M, idx, E)
+    return _conv("orc_conv2d_dgrad", (N, H, W, C), g, dy, w, lut, M, idx, E, threads)
 
 
-def conv2d_wgrad(x, dy, w_shape, lut, M, stride=(1, 1), pad=(0, 0), idx=None, E=8):
+def conv2d_wgrad(x, dy, w_shape, lut, M, stride=(1, 1), pad=(0, 0), idx=None, E=8, threads=None):
     """x: NHWC, dy: NPQK, w_shape = (R, S, C, K). Returns (dW, dWS)."""
     N, H, W, C = x.shape
     R, S, C2, K = w_shape
@@ -256,4 +370,4 @@ def conv2d_wgrad(x, dy, w_shape, lut, M, stride=(1, 1), pad=(0, 0), idx=None, E=
     P, Q = conv_out_hw(H, W, R, S, stride, pad)
     assert dy.shape == (N, P, Q, K)
     g = (N, H, W, C, K, R, S, stride[0], stride[1], pad[0], pad[1])
-    return _conv("orc_conv2d_wgrad", (R, S, C, K), g, x, dy, lut, M, idx, E)
+    return _conv("orc_conv2d_wgrad", (R, S, C, K), g, x, dy, lut, M, idx, E, threads)

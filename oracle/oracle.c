@@ -45,6 +45,14 @@
  *       multiplied (the IM2COL buffer holds zeros there), not omitted terms.
  *   R13 Sums are taken in double precision here; the sum of absolute
  *       products is returned beside each output for the error gate.
+ *   R20 The FP32 order (the *_f32 functions below): the sum the library
+ *       documents for its outputs, taken in single precision. The reduction
+ *       sequence of an output is cut into chunks of L consecutive positions;
+ *       each chunk is summed from +0 in ascending order, then the chunk sums
+ *       are added from +0 in ascending order (one chunk when L covers the
+ *       sequence). Every addition rounds to nearest even; with the native
+ *       multiplier each step is a fused multiply-add (one rounding). The
+ *       chunk length of each output is an input (the library reports it).
  *   R17 The native multiplier (Section V: the simulator can call the
  *       hardware multiplication instead of the table, the reference point
  *       of Fig. 6) is the exact product of the two floats, rounded only when
@@ -433,4 +441,133 @@ void orc_conv2d_wgrad(int N, int H, int W, int C, int K, int R, int S,
     long cnt = idx ? (long)count : total;
     for (long t = 0; t < cnt; ++t)
         wgrad_one(&g, x, dy, idx ? (long)idx[t] : t, lut, M, E, &DW[t], &DWS[t]);
+}
+
+/* ------------------------------------------------------------------ */
+/* The same sums in FP32, in the documented order (reading R20)        */
+/* ------------------------------------------------------------------ */
+/* Running state of one FP32 sum: `total` holds the finished chunks, `part`
+ * the chunk in progress, which is chunk number `cur` (position t lies in
+ * chunk t / L). Positions must come in ascending order. */
+typedef struct {
+    float total, part;
+    int64_t L, cur;
+} f32sum;
+
+static void f32_begin(f32sum *f, int64_t L)
+{
+    f->total = 0.0f;
+    f->part = 0.0f;
+    f->L = L > 0 ? L : 1;
+    f->cur = 0;
+}
+
+/* position t of the sequence: when it lies past the chunk in progress, that
+ * chunk's sum is added to the total and a new chunk starts from +0 (a chunk
+ * with no product in between adds +0, which changes nothing) */
+static void f32_at(f32sum *f, int64_t t)
+{
+    while (t / f->L > f->cur) {
+        f->total = f->total + f->part;
+        f->part = 0.0f;
+        ++f->cur;
+    }
+}
+
+/* add the product of a and b (approximate, or native: fused) at position t */
+static void f32_add(f32sum *f, int64_t t, float a, float b, const uint16_t *lut, int M, int E)
+{
+    f32_at(f, t);
+    if (lut == NULL)
+        f->part = fmaf(a, b, f->part);
+    else
+        f->part = f->part + float_of(orc_amsim_bits_fmt(bits_of(a), bits_of(b), lut, M, E));
+}
+
+static float f32_end(f32sum *f)
+{
+    f->total = f->total + f->part;
+    return f->total;
+}
+
+/* GEMM outputs (rows[t], cols[t]) with reduction chunks of chunk[t]
+ * positions of the reduction index p */
+void orc_gemm_f32_at(int transA, int transB, int m, int n, int k,
+                     const float *A, int lda, const float *B, int ldb,
+                     const uint16_t *lut, int M, int E,
+                     int64_t count, const int32_t *rows, const int32_t *cols,
+                     const int64_t *chunk, float *out)
+{
+    (void)m; (void)n;
+    for (int64_t t = 0; t < count; ++t) {
+        int i = rows[t], j = cols[t];
+        f32sum f;
+        f32_begin(&f, chunk[t]);
+        for (int p = 0; p < k; ++p) {
+            float a = transA ? A[(long)p * lda + i] : A[(long)i * lda + p];
+            float b = transB ? B[(long)j * ldb + p] : B[(long)p * ldb + j];
+            f32_add(&f, p, a, b, lut, M, E);
+        }
+        out[t] = f32_end(&f);
+    }
+}
+
+/* Conv2D outputs at flat indices idx[t] with chunks of chunk[t] positions.
+ * Reduction sequences (positions in ascending order; C4 and K4 are C and K
+ * rounded up to a multiple of 4, the positions past C or K holding no
+ * product):
+ *   fwd:   (r, s, c) at position (r*S + s)*C4 + c;
+ *   dgrad: (r, s, k) at position ((R-1-r)*S + (S-1-s))*K4 + k, i.e. the
+ *          filter taps in reverse order (the transposed, reversed filter of
+ *          Section VI-B), channels ascending;
+ *   wgrad: (n, p, q) at position (n*P + p)*Q + q. */
+void orc_conv2d_f32(int pass, int N, int H, int W, int C, int K, int R, int S,
+                    int sh, int sw, int ph, int pw,
+                    const float *t1, const float *t2, const uint16_t *lut, int M, int E,
+                    int64_t count, const int64_t *idx, const int64_t *chunk, float *out)
+{
+    geom g = make_geom(N, H, W, C, K, R, S, sh, sw, ph, pw);
+    const int C4 = (C + 3) / 4 * 4, K4 = (K + 3) / 4 * 4;
+    for (int64_t t = 0; t < count; ++t) {
+        long o = (long)idx[t];
+        f32sum f;
+        f32_begin(&f, chunk[t]);
+        if (pass == 0) {                         /* y[n,p,q,k]: t1 = x, t2 = w */
+            int k = (int)(o % K); o /= K;
+            int q = (int)(o % g.Q); o /= g.Q;
+            int p = (int)(o % g.P);
+            int n = (int)(o / g.P);
+            for (int r = 0; r < R; ++r)
+                for (int s = 0; s < S; ++s)
+                    for (int c = 0; c < C; ++c) {
+                        float a = x_at(&g, t1, n, p * sh - ph + r, q * sw - pw + s, c);
+                        f32_add(&f, ((int64_t)r * S + s) * C4 + c, a, w_at(&g, t2, r, s, c, k), lut, M, E);
+                    }
+        } else if (pass == 1) {                  /* dx[n,h,w,c]: t1 = dy, t2 = w */
+            int c = (int)(o % C); o /= C;
+            int ww = (int)(o % W); o /= W;
+            int h = (int)(o % H);
+            int n = (int)(o / H);
+            for (int r = R - 1; r >= 0; --r)
+                for (int s = S - 1; s >= 0; --s)
+                    for (int k = 0; k < K; ++k) {
+                        float a = dilated_dy_at(&g, t1, n, h + ph - r, ww + pw - s, k);
+                        int64_t pos = ((int64_t)(R - 1 - r) * S + (S - 1 - s)) * K4 + k;
+                        f32_add(&f, pos, a, w_at(&g, t2, r, s, c, k), lut, M, E);
+                    }
+        } else {                                 /* dw[r,s,c,k]: t1 = x, t2 = dy */
+            int k = (int)(o % K); o /= K;
+            int c = (int)(o % C); o /= C;
+            int s = (int)(o % S);
+            int r = (int)(o / S);
+            for (int n = 0; n < N; ++n)
+                for (int p = 0; p < g.P; ++p)
+                    for (int q = 0; q < g.Q; ++q) {
+                        float a = x_at(&g, t1, n, p * sh - ph + r, q * sw - pw + s, c);
+                        float b = t2[(((long)n * g.P + p) * g.Q + q) * K + k];
+                        f32_add(&f, ((int64_t)n * g.P + p) * g.Q + q, a, b, lut, M, E);
+                    }
+        }
+        out[t] = f32_end(&f);
+    }
 }

@@ -32,3 +32,22 @@ def gate(c, r, s, tol=TOL, what=""):
     worst = float(err.max()) if err.size else 0.0
     assert worst <= tol, f"{what}: max |c-r|/S = {worst:.3e} > {tol}"
     return worst
+
+
+def same_bits(c, want, what="", zero_sign=True):
+    """Bitwise equality of float32 results with the oracle's FP32-order sums
+    (reading R20): NaN matches any NaN; with zero_sign False, +0 and -0 match
+    each other (the native multiplier leaves the sign of a zero sum open)."""
+    c = np.ascontiguousarray(c, dtype=np.float32).ravel()
+    w = np.ascontiguousarray(want, dtype=np.float32).ravel()
+    assert c.shape == w.shape, (c.shape, w.shape)
+    cn, wn = np.isnan(c), np.isnan(w)
+    assert np.array_equal(cn, wn), f"{what}: NaN at {np.flatnonzero(cn != wn)[:8]}"
+    cb, wb = c.view(np.uint32), w.view(np.uint32)
+    diff = (cb != wb) & ~cn
+    if not zero_sign:
+        diff &= ~((c == 0) & (w == 0))
+    bad = np.flatnonzero(diff)
+    assert bad.size == 0, (f"{what}: {bad.size} of {c.size} outputs differ from the FP32-order sums, "
+                           f"first at {bad[:4]}: got {c[bad[:4]]}, want {w[bad[:4]]}")
+    return c.size

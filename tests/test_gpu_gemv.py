@@ -1,5 +1,6 @@
-"""GPU parity of the row-vector path: approx_gemm with at most 4 rows in op(A)
-and B not transposed (batch-1 and few-row dense inference; ApproxTrain,
+"""GPU parity of the row-vector path: approx_gemm with at most 32 rows in
+op(A) (64 when k * n >= 2^22 or k * n <= 2^16), in blocks of 4 rows, and B not
+transposed (batch-1 and few-row dense inference; ApproxTrain,
 arXiv 2209.04161, Section VI-D, keeps a separate matrix-vector kernel for
 this case). The library routes these calls to a kernel whose lanes run over
 the output columns; products must equal the oracle's bit for bit (k = 1) and
@@ -154,7 +155,7 @@ def test_gemv_small_tables_bit_exact(am, name):
 
 @pytest.mark.parametrize("m", [6, 16])
 def test_gemv_row_blocks_strided_batch_and_padding(am, m):
-    """5..16 rows run as blocks of 4 rows in the row-vector kernel: a strided
+    """More than 4 rows run as blocks of 4 rows in the row-vector kernel: a strided
     batch with padded leading dimensions, op(A) transposed or not; the
     padding of C is not written."""
     t, M = use(am, "perturbed8")
@@ -222,7 +223,7 @@ def test_gemv_batched(am):
 
 @pytest.mark.parametrize("m,transA", [(7, 0), (11, 1), (16, 0)])
 def test_gemv_row_blocks_pointer_arrays(am, m, transA):
-    """5..16 rows through device pointer arrays: each entry's row blocks are
+    """More than 4 rows through device pointer arrays: each entry's row blocks are
     offset from its own pointer; results equal the strided batch's bits."""
     t, M = use(am, "mitchell7")
     nb, n, k = 4, 500, 300

@@ -86,3 +86,41 @@ def test_captured_calls_replay_the_eager_bits(am, name):
             calls()
         torch.cuda.synchronize()
         assert np.array_equal(C1.cpu().numpy().view(np.uint32), eager[0].view(np.uint32))
+
+
+def test_graph_survives_arena_growth_and_table_reload(am):
+    """A graph captured on a stream keeps the arena memory and the table it
+    captured: a later, larger eager call on the same stream grows the arena
+    and another table is loaded, yet every replay still gives the bits of the
+    eager call made before the capture (the superseded arena and table are
+    kept until approx_release)."""
+    M, t = TABLES["perturbed8"]()
+    am.approx_lut_load(t, M)
+    A, B = normal(1311, (300, 500)), normal(1312, (500, 200))
+    dA, dB = dev(A), dev(B)
+    C = torch.empty((300, 200), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        am.approx_gemm(0, 0, 300, 200, 500, dA, 500, dB, 200, C, 200, stream=s)
+    torch.cuda.synchronize()
+    eager = C.cpu().numpy().copy()
+    R, S = oracle.gemm(A, B, t, M)
+    gate(eager, R, S, what="eager before capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        am.approx_gemm(0, 0, 300, 200, 500, dA, 500, dB, 200, C, 200, stream=s)
+    # a call of 16x the scratch on the same stream, then another table
+    A3, B3 = dev(normal(1313, (1200, 2000))), dev(normal(1314, (2000, 800)))
+    C3 = torch.empty((1200, 800), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(s):
+        am.approx_gemm(0, 0, 1200, 800, 2000, A3, 2000, B3, 800, C3, 800, stream=s)
+    am.approx_lut_load(oracle.lut_generate(7, "mitchell"), 7)
+    for rep in range(3):
+        C.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy().view(np.uint32), eager.view(np.uint32)), f"replay {rep}"
+        with torch.cuda.stream(s):          # eager work with the new table between replays
+            am.approx_gemm(0, 0, 1200, 800, 2000, A3, 2000, B3, 800, C3, 800, stream=s)
+        torch.cuda.synchronize()

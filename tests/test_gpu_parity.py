@@ -12,7 +12,7 @@ import pytest
 import oracle
 from datagen import PERTURB_SEED, normal, pm_one, special_values, splitmix64, uniform
 from datagen import configs as cfg
-from parity import gate
+from parity import gate, same_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -273,10 +273,16 @@ def test_gemm_special_values_and_extremes(am):
     gate(C, R, S, what="specials")
 
 
-def test_fast_and_checked_paths_agree_bitwise(am):
-    use(am, "perturbed8")
-    A = dev(normal(21, (300, 200)))
-    B = dev(normal(22, (200, 150)))
+@pytest.mark.parametrize("name,shape", [
+    ("perturbed8", (300, 150, 200)),      # GEMM kernel
+    ("exact7", (64, 64, 64)),             # row-vector kernel (k * n <= 2^16: up to 64 rows)
+    ("perturbed8", (48, 2048, 2048)),     # row-vector kernel (k * n >= 2^22), 12 row blocks
+])
+def test_fast_and_checked_paths_agree_bitwise(am, name, shape):
+    use(am, name)
+    m, n, k = shape
+    A = dev(normal(21 + m, (m, k)))
+    B = dev(normal(22 + n, (k, n)))
     C1 = host(am.gemm(A, B))
     with forced_checked():
         C2 = host(am.gemm(A, B))
@@ -291,12 +297,15 @@ def test_deterministic_including_split_reduction(am):
         C1 = host(am.gemm(A, B))
         C2 = host(am.gemm(A, B))
         assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32))
-    # the split reduction still meets the gate
+    # split reductions still meet the gate: 16 rows run in the row-vector
+    # kernel (its chunk partials summed by the reduction kernel), 100 rows in
+    # the GEMM kernel (one row tile, its reduction split over the chunks)
     M, t = table("mitchell7")
-    A = normal(33, (16, 40000))
-    B = normal(34, (40000, 20))
-    R, S = oracle.gemm(A, B, t, M)
-    gate(host(am.gemm(dev(A), dev(B))), R, S, what="split")
+    for m, what in ((16, "split, row-vector kernel"), (100, "split, GEMM kernel")):
+        A = normal(33, (m, 40000))
+        B = normal(34, (40000, 20))
+        R, S = oracle.gemm(A, B, t, M)
+        gate(host(am.gemm(dev(A), dev(B))), R, S, what=what)
 
 
 def test_strided_batched_heads(am):
@@ -417,26 +426,70 @@ def test_workload2_mlp_all_gemms(am):
         gate(C, R, S, what=f"mlp {name}")
 
 
-def test_workload3_conv_full_size_sampled(am):
+def _rows_cols_sample(seed, m, n, n_rows=64, n_cols=64, n_rand=4096):
+    """The full-size sample: n_rows full rows and n_cols full columns (the
+    first and last of each included) and n_rand random outputs, as flat
+    (row, column) arrays."""
+    r = splitmix64(seed, n_rows + n_cols)
+    rsel = np.unique(np.concatenate([[0, m - 1], (r[:n_rows - 2] % np.uint64(m)).astype(np.int64)]))
+    csel = np.unique(np.concatenate([[0, n - 1], (r[n_rows:n_rows + n_cols - 2] % np.uint64(n)).astype(np.int64)]))
+    rows = [np.repeat(rsel, n), np.repeat(np.arange(m), csel.size)]
+    cols = [np.tile(np.arange(n), rsel.size), np.tile(csel, m)]
+    rr, cc = _sample_pairs(seed + 1, m, n, n_rand)
+    rows = np.concatenate(rows + [rr]).astype(np.int32)
+    cols = np.concatenate(cols + [cc]).astype(np.int32)
+    return rows, cols, rsel.size, csel.size
+
+
+def _check_gemm_sample(am, C, A, B, t, M, rows, cols, what, transA=False, transB=False, batch=1, b=0):
+    """Sampled outputs of a GEMM: the double-precision gate and the FP32
+    sums in the reported order, bit for bit (threaded oracle driver)."""
+    m, n = C.shape
+    k = A.shape[0] if transA else A.shape[1]
+    th = oracle.default_threads()
+    R, S = oracle.gemm_at(A, B, t, M, rows, cols, transA=transA, transB=transB, threads=th)
+    gate(C[rows, cols], R, S, what=what)
+    L = am.approx_gemm_chunks(int(transA), int(transB), m, n, k, batch, b, rows, cols)
+    F = oracle.gemm_f32_at(A, B, t, M, rows, cols, np.maximum(L, 1), transA=transA, transB=transB, threads=th)
+    same_bits(C[rows, cols], F, what=what)
+
+
+def test_workload3_conv_full_size(am):
+    """The 3 x 3 Conv2D workload (NHWC 128 x 32 x 32 x 64 -> 64, Mitchell
+    M = 7) in the launch configuration bench.py times: every output of all
+    three passes equals the FP32 sums in the reported order bit for bit; every
+    weight-gradient output and 4,096 random outputs of the other passes pass
+    the double-precision gate."""
+    import time
     M, t = use(am, "mitchell7")
     sh = cfg.CONV_SHAPE
     x, w, dy = cfg.conv_tensors()
     st, pd = sh["stride"], sh["pad"]
+    geom = (sh["N"], sh["H"], sh["W"], sh["C"], sh["K"], sh["R"], sh["S"], st, pd)
     y = host(am.conv2d_fwd(dev(x), dev(w), st, pd)).ravel()
     dx = host(am.conv2d_dgrad(dev(dy), dev(w), x.shape, st, pd)).ravel()
     dw = host(am.conv2d_wgrad(dev(x), dev(dy), w.shape, st, pd)).ravel()
+    th = oracle.default_threads()
     r = splitmix64(3301, 4096)
-    for name, full, fn, args, count in (
-        ("fwd", y, oracle.conv2d_fwd, (x, w), 4096),
-        ("dgrad", dx, oracle.conv2d_dgrad, (dy, w, x.shape), 4096),
-        ("wgrad", dw, oracle.conv2d_wgrad, (x, dy, w.shape), 512),
+    for name, full, fn, args, t1, t2 in (
+        ("fwd", y, oracle.conv2d_fwd, (x, w), x, w),
+        ("dgrad", dx, oracle.conv2d_dgrad, (dy, w, x.shape), dy, w),
+        ("wgrad", dw, oracle.conv2d_wgrad, (x, dy, w.shape), x, dy),
     ):
-        idx = (r[:count] % np.uint64(full.size)).astype(np.int64)
-        edges = np.array([0, full.size - 1, 31 * 64, 32 * 64 * 31, 32 * 32 * 64 - 1]) % full.size
-        idx = np.concatenate([idx, edges])   # corners and image borders
-        R, S = fn(*args, t, M, st, pd, idx=idx)
-        print(f"w3 {name}: {idx.size} samples", flush=True)
+        t0 = time.time()
+        if name == "wgrad":
+            idx = np.arange(full.size, dtype=np.int64)
+        else:
+            idx = (r % np.uint64(full.size)).astype(np.int64)
+            edges = np.array([0, full.size - 1, 31 * 64, 32 * 64 * 31, 32 * 32 * 64 - 1]) % full.size
+            idx = np.concatenate([idx, edges])   # corners and image borders
+        R, S = fn(*args, t, M, st, pd, idx=idx, threads=th)
         gate(full[idx], R, S, what=f"w3 {name}")
+        every = np.arange(full.size, dtype=np.int64)
+        L = am.approx_conv2d_chunks(name, *geom[:7], st, pd, every)
+        F = oracle.conv2d_f32(name, t1, t2, geom, t, M, L, threads=th)
+        same_bits(full, F, what=f"w3 {name}")
+        print(f"w3 {name}: {idx.size} outputs gated, {full.size} bit-exact, {time.time() - t0:.1f} s", flush=True)
 
 
 def test_conv_tail_tiles_split(am):
@@ -462,15 +515,21 @@ def test_conv_tail_tiles_split(am):
 
 
 def test_workload4_gemm8192_sampled(am):
+    """The headline GEMM (8192^3, M = 8 perturbed table) in the launch
+    configuration bench.py times: 64 full rows, 64 full columns and 4,096
+    random outputs (the first and last row and column included) against the
+    double-precision gate and, bit for bit, the FP32 sums in the reported
+    order."""
+    import time
     M, t = use(am, "perturbed8")
     A, B = cfg.gemm_square(4, 8192)
     print("w4: gemm 8192^3", flush=True)
     C = host(am.gemm(dev(A), dev(B)))
-    rows, cols = _sample_pairs(4401, 8192, 8192, 2048)
-    rows = np.concatenate([rows, np.full(512, 8191, np.int32), np.arange(0, 8192, 16, dtype=np.int32)])
-    cols = np.concatenate([cols, np.arange(0, 8192, 16, dtype=np.int32), np.full(512, 8191, np.int32)])
-    R, S = oracle.gemm_at(A, B, t, M, rows, cols)
-    gate(C[rows, cols], R, S, what="w4")
+    rows, cols, nr, nc = _rows_cols_sample(4401, 8192, 8192)
+    t0 = time.time()
+    Bt = np.ascontiguousarray(B.T)            # the same op(B), read along its columns
+    _check_gemm_sample(am, C, A, Bt, t, M, rows, cols, "w4", transB=True)
+    print(f"w4: {nr} rows, {nc} columns, {rows.size} outputs checked in {time.time() - t0:.1f} s", flush=True)
 
 
 def test_gemm8192_exact_table_every_output(am):
@@ -539,10 +598,14 @@ def test_conv_exact_table_every_output(am):
             check(dw, refs[2], DW, "wgrad")
 
 
-def test_workload5_attention_stages_sampled(am):
-    """Each of the four approximate GEMM stages of multi-head attention on
-    synthetic inputs of the workload's shapes (softmax probabilities are
-    generated as row-normalised exponentials of normal draws)."""
+def test_workload5_attention_stages(am):
+    """The four approximate GEMM stages of multi-head attention at the
+    workload's shapes, each called as bench.py calls it (softmax
+    probabilities are synthetic: row-normalised exponentials of normal
+    draws). Projections: 64 full rows, 64 full columns and 4,096 random
+    outputs; QK^T and P V: every output of 16 (sequence, head) pairs, the
+    first and the last included; all against the double-precision gate and,
+    bit for bit, the FP32 sums in the reported order."""
     M, t = use(am, "mitchell7")
     sh = cfg.MHA_SHAPE
     Bz, T, D, H = sh["batch"], sh["seq"], sh["d_model"], sh["heads"]
@@ -550,9 +613,8 @@ def test_workload5_attention_stages_sampled(am):
     X, Wqkv, Wo = cfg.mha_tensors()
     # stage 1: QKV projection
     qkv = host(am.gemm(dev(X), dev(Wqkv)))
-    rows, cols = _sample_pairs(5501, Bz * T, 3 * D, 2048)
-    R, S = oracle.gemm_at(X, Wqkv, t, M, rows, cols)
-    gate(qkv[rows, cols], R, S, what="w5 qkv")
+    rows, cols, _, _ = _rows_cols_sample(5501, Bz * T, 3 * D)
+    _check_gemm_sample(am, qkv, X, Wqkv, t, M, rows, cols, "w5 qkv")
     # stage 2: scores for every (sequence, head) pair in one pointer-array
     # call, on a synthetic fused QKV buffer
     qk = normal(5502, (Bz * T, 3 * D), std=0.5)
@@ -565,30 +627,40 @@ def test_workload5_attention_stages_sampled(am):
     sp = am.pointer_array([S_d.data_ptr() + f * (b * H + h) * T * T for b, h in pairs])
     am.approx_gemm_batched(0, 1, T, T, dh, qp, 3 * D, kp, 3 * D, sp, T, len(pairs))
     Sc = host(S_d)
-    for (b, h) in ((0, 0), (3, 7), (15, 11)):
-        rr, cc = _sample_pairs(5503 + 16 * b + h, T, T, 512)
-        rows = qk[b * T:(b + 1) * T]
-        R, S = oracle.gemm_at(rows[:, h * dh:(h + 1) * dh], rows[:, D + h * dh: D + (h + 1) * dh], t, M, rr, cc,
-                              transB=True)
-        gate(Sc[b, h][rr, cc], R, S, what=f"w5 qk b{b} h{h}")
-    # stage 3: P V per head
-    z = normal(5510, (H, T, T))
+    pick = [0, len(pairs) - 1] + [int(v) for v in splitmix64(5503, 14) % np.uint64(len(pairs) - 2) + np.uint64(1)]
+    full_r, full_c = np.meshgrid(np.arange(T, dtype=np.int32), np.arange(T, dtype=np.int32), indexing="ij")
+    for e in pick:
+        b, h = pairs[e]
+        rows_ = qk[b * T:(b + 1) * T]
+        Qh, Kh = rows_[:, h * dh:(h + 1) * dh], rows_[:, D + h * dh: D + (h + 1) * dh]
+        _check_gemm_sample(am, Sc[b, h], Qh, Kh, t, M, full_r.ravel(), full_c.ravel(), f"w5 qk b{b} h{h}",
+                           transB=True, batch=len(pairs), b=e)
+    # stage 3: P V for every (sequence, head) pair in one pointer-array call
+    z = normal(5510, (len(pairs), T, T))
     P = np.exp(z - z.max(axis=2, keepdims=True))
     P = (P / P.sum(axis=2, keepdims=True)).astype(np.float32)
-    V = normal(5511, (T, D))
-    O_d = torch.empty((T, D), dtype=torch.float32, device="cuda")
-    am.approx_gemm_strided_batched(0, 0, T, dh, T, dev(P), T, T * T, dev(V), D, dh, O_d, D, dh, H)
+    del z
+    V = normal(5511, (Bz * T, 3 * D))         # the V columns of a fused QKV buffer
+    dP, dV = dev(P), dev(V)
+    O_d = torch.empty((Bz * T, D), dtype=torch.float32, device="cuda")
+    pp = am.pointer_array([dP.data_ptr() + f * e * T * T for e in range(len(pairs))])
+    vp = am.pointer_array([dV.data_ptr() + f * (b * T * 3 * D + 2 * D + h * dh) for b, h in pairs])
+    op = am.pointer_array([O_d.data_ptr() + f * (b * T * D + h * dh) for b, h in pairs])
+    am.approx_gemm_batched(0, 0, T, dh, T, pp, T, vp, 3 * D, op, D, len(pairs))
     O = host(O_d)
-    for h in (0, 5, 11):
-        rr, cc = _sample_pairs(5520 + h, T, dh, 512)
-        R, S = oracle.gemm_at(P[h], V[:, h * dh:(h + 1) * dh], t, M, rr, cc)
-        gate(O[:, h * dh:(h + 1) * dh][rr, cc], R, S, what=f"w5 pv h{h}")
+    full_r, full_c = np.meshgrid(np.arange(T, dtype=np.int32), np.arange(dh, dtype=np.int32), indexing="ij")
+    for e in pick:
+        b, h = pairs[e]
+        Vh = V[b * T:(b + 1) * T, 2 * D + h * dh: 2 * D + (h + 1) * dh]
+        Oh = O[b * T:(b + 1) * T, h * dh:(h + 1) * dh]
+        _check_gemm_sample(am, Oh, P[e], Vh, t, M, full_r.ravel(), full_c.ravel(), f"w5 pv b{b} h{h}",
+                           batch=len(pairs), b=e)
+    del P, dP
     # stage 4: output projection
     Oin = normal(5530, (Bz * T, D), std=0.3)
     Y = host(am.gemm(dev(Oin), dev(Wo)))
-    rows, cols = _sample_pairs(5531, Bz * T, D, 2048)
-    R, S = oracle.gemm_at(Oin, Wo, t, M, rows, cols)
-    gate(Y[rows, cols], R, S, what="w5 out")
+    rows, cols, _, _ = _rows_cols_sample(5531, Bz * T, D)
+    _check_gemm_sample(am, Y, Oin, Wo, t, M, rows, cols, "w5 out")
 
 
 # ------------------------------------------------------------------ API

@@ -8,15 +8,17 @@ case that can be rerun alone.
 
 Expected values come from the oracle only (ApproxTrain, arXiv 2209.04161,
 Algorithm 2 for each product; GEMM and Conv2D as sums of those products).
-Sums must pass the gate of tests/parity.py; outputs outside op(A) op(B)'s
-extent (the padding of C) must be left untouched.
+Sums must pass the gate of tests/parity.py against the double-precision sums,
+and equal bit for bit the oracle's FP32 sums in the order the library
+reports (approx_gemm_chunks / approx_conv2d_chunks); outputs outside
+op(A) op(B)'s extent (the padding of C) must be left untouched.
 """
 import numpy as np
 import pytest
 
 import oracle
 from datagen import PERTURB_SEED, normal, pm_one, special_values, splitmix64
-from parity import gate
+from parity import gate, same_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -141,6 +143,13 @@ def test_random_gemm(am, case):
         Cb = got[b * sC: b * sC + m * ldc].reshape(m, ldc)
         with np.errstate(invalid="ignore", over="ignore"):
             gate(Cb[:, :n], R, S, what=f"random gemm {c['i']} batch {b}")
+        # bit for bit against the FP32 sums in the library's reported order
+        rows, cols = np.meshgrid(np.arange(m, dtype=np.int32), np.arange(n, dtype=np.int32), indexing="ij")
+        rows, cols = rows.ravel(), cols.ravel()
+        L = am.approx_gemm_chunks(c["tA"], c["tB"], m, n, k, batch, b, rows, cols)
+        F = oracle.gemm_f32_at(A, B, t, M, rows, cols, np.maximum(L, 1), transA=bool(c["tA"]),
+                               transB=bool(c["tB"]), E=c["E"])
+        same_bits(Cb[:, :n], F, what=f"random gemm {c['i']} batch {b}", zero_sign=t is not None)
         assert np.all(Cb[:, n:] == 7.0)
         gap = got[b * sC + m * ldc: (b + 1) * sC] if b + 1 < batch else got[b * sC + m * ldc:]
         assert np.all(gap == 7.0)
@@ -181,10 +190,20 @@ def test_random_conv(am, case):
     x = operand(seed, (N, H, W, C), 0, c["special"])
     w = operand(seed + 1, (R, S, C, K), -2, c["special"])
     dy = operand(seed + 2, (N, P, Q, K), 0, c["special"])
+    geom = (N, H, W, C, K, R, S, st, pd)
     with np.errstate(invalid="ignore", over="ignore"):
         Y, YS = oracle.conv2d_fwd(x, w, t, M, st, pd, E=E)
-        gate(host(am.conv2d_fwd(dev(x), dev(w), st, pd)), Y, YS, what=f"random conv {c['i']} fwd")
+        y = host(am.conv2d_fwd(dev(x), dev(w), st, pd))
+        gate(y, Y, YS, what=f"random conv {c['i']} fwd")
         DX, DXS = oracle.conv2d_dgrad(dy, w, x.shape, t, M, st, pd, E=E)
-        gate(host(am.conv2d_dgrad(dev(dy), dev(w), x.shape, st, pd)), DX, DXS, what=f"random conv {c['i']} dgrad")
+        dx = host(am.conv2d_dgrad(dev(dy), dev(w), x.shape, st, pd))
+        gate(dx, DX, DXS, what=f"random conv {c['i']} dgrad")
         DW, DWS = oracle.conv2d_wgrad(x, dy, w.shape, t, M, st, pd, E=E)
-        gate(host(am.conv2d_wgrad(dev(x), dev(dy), w.shape, st, pd)), DW, DWS, what=f"random conv {c['i']} wgrad")
+        dw = host(am.conv2d_wgrad(dev(x), dev(dy), w.shape, st, pd))
+        gate(dw, DW, DWS, what=f"random conv {c['i']} wgrad")
+    # bit for bit against the FP32 sums in the library's reported order
+    for pname, got, t1, t2 in (("fwd", y, x, w), ("dgrad", dx, dy, w), ("wgrad", dw, x, dy)):
+        idx = np.arange(got.size, dtype=np.int64)
+        L = am.approx_conv2d_chunks(pname, N, H, W, C, K, R, S, st, pd, idx)
+        F = oracle.conv2d_f32(pname, t1, t2, geom, t, M, L, idx=idx, E=E)
+        same_bits(got, F, what=f"random conv {c['i']} {pname}", zero_sign=t is not None)

@@ -24,11 +24,22 @@ def am():
 def test_library_exports_every_declared_function(am):
     with open(os.path.join(ROOT, "include", "approx_mul.h")) as f:
         header = f.read()
-    declared = set(re.findall(r"^\s*(?:int|const char \*)\s*(approx_\w+)\s*\(", header, re.M))
+    declared = set(re.findall(r"^\s*(?:int|long long|const char \*)\s*(approx_\w+)\s*\(", header, re.M))
     assert declared == set(am.EXPORTS)
     lib = ctypes.CDLL(am.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
+
+
+def test_library_built_from_these_sources(am):
+    """The loaded binary carries the stamp of the sources beside it (a stale
+    build would not)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_approx_build", os.path.join(ROOT, "approximate_multiplier_dnn_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    assert am.approx_build_id() == b.source_hash()
 
 
 @pytest.mark.parametrize("M", list(range(1, 12)))
