@@ -22,6 +22,7 @@ APPROX_EINVAL = -1
 APPROX_ENOLUT = -2
 APPROX_EUNSUPPORTED = -3
 APPROX_EHIP = -4
+APPROX_ESCRATCH = -5
 
 CONV_PASSES = {"fwd": 0, "dgrad": 1, "wgrad": 2}
 
@@ -32,7 +33,8 @@ MODEL_MITCHELL = 1
 EXPORTS = (
     "approx_lut_build", "approx_lut_build_from_model", "approx_lut_load", "approx_native_load", "approx_lut_bits",
     "approx_exponent_bits_set", "approx_exponent_bits",
-    "approx_gemm", "approx_gemm_strided_batched", "approx_gemm_batched",
+    "approx_gemm", "approx_gemm_noalloc", "approx_gemm_noalloc_max_bytes",
+    "approx_gemm_strided_batched", "approx_gemm_batched",
     "approx_conv2d_fwd", "approx_conv2d_dgrad", "approx_conv2d_wgrad",
     "approx_gemm_chunks", "approx_conv2d_chunks",
     "approx_profile_enable", "approx_profile_read",
@@ -53,6 +55,8 @@ _lib.approx_lut_bits.argtypes = []
 _lib.approx_exponent_bits_set.argtypes = [_i]
 _lib.approx_exponent_bits.argtypes = []
 _lib.approx_gemm.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, _vp]
+_lib.approx_gemm_noalloc.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, _vp]
+_lib.approx_gemm_noalloc_max_bytes.argtypes = []
 _lib.approx_gemm_strided_batched.argtypes = [_i] * 5 + [_vp, _i, _ll, _vp, _i, _ll, _vp, _i, _ll, _i, _vp]
 _lib.approx_gemm_batched.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, _i, _vp]
 for _n in ("approx_conv2d_fwd", "approx_conv2d_dgrad", "approx_conv2d_wgrad"):
@@ -67,8 +71,9 @@ _lib.approx_release.argtypes = []
 _lib.approx_profile_enable.argtypes = [_i]
 _lib.approx_profile_read.argtypes = [_vp, _vp]
 for _n in EXPORTS:
-    if _n not in ("approx_status_string", "approx_build_id"):
+    if _n not in ("approx_status_string", "approx_build_id", "approx_gemm_noalloc_max_bytes"):
         getattr(_lib, _n).restype = ctypes.c_int
+_lib.approx_gemm_noalloc_max_bytes.restype = ctypes.c_longlong
 
 
 class ApproxError(RuntimeError):
@@ -212,6 +217,17 @@ def approx_conv2d_chunks(pass_name, N, H, W, C, K, R, S, stride, pad, idx):
                                      int(S), int(stride[0]), int(stride[1]), int(pad[0]), int(pad[1]), ix.size,
                                      ix.ctypes.data, out.ctypes.data), "approx_conv2d_chunks")
     return out
+
+
+def approx_gemm_noalloc(transA, transB, m, n, k, A, lda, B, ldb, C, ldc, stream=None):
+    """approx_gemm without any allocation (fixed per-device scratch)."""
+    return _check(_lib.approx_gemm_noalloc(int(transA), int(transB), int(m), int(n), int(k), _ptr(A), int(lda),
+                                           _ptr(B), int(ldb), _ptr(C), int(ldc), _stream(stream)),
+                  "approx_gemm_noalloc")
+
+
+def approx_gemm_noalloc_max_bytes():
+    return int(_lib.approx_gemm_noalloc_max_bytes())
 
 
 def approx_gemm_strided_batched(transA, transB, m, n, k, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,

@@ -113,7 +113,32 @@ int arena_get(int dev, hipStream_t stream, size_t bytes, char** out, int** stats
     return APPROX_OK;
 }
 
-// Where a call's scratch comes from: the stream's arena.
+// Fixed scratch of the allocation-free entry point: one array per device,
+// in the code object's device memory, shared by every such call on that
+// device. Its device address comes from hipGetSymbolAddress (the array's
+// name in host code is a host-side stand-in, not a device address).
+constexpr size_t kFixedScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kFixedScratchBytes];
+char* g_scratch_ptr[kMaxDevices];
+
+// The device address of this device's fixed scratch (the current device),
+// looked up once per device: at its table load (the set-up call every
+// device needs), or else on its first allocation-free call.
+int fixed_scratch(int dev, char** out)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return APPROX_EHIP;
+        g_scratch_ptr[dev] = static_cast<char*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return APPROX_OK;
+}
+
+// Where a call's scratch comes from: the stream's arena, or (fixed != nullptr)
+// the device's fixed scratch, whose stats region is initialised by every call
+// (the previous call on the device may have left anything there).
 struct ScratchSource {
     char* fixed = nullptr;
 };
@@ -121,8 +146,12 @@ struct ScratchSource {
 int scratch_get(const ScratchSource& src, int dev, hipStream_t stream, size_t bytes, char** out, int** stats,
                 bool** ready)
 {
-    (void)src;
-    return arena_get(dev, stream, bytes, out, stats, ready);
+    if (src.fixed == nullptr) return arena_get(dev, stream, bytes, out, stats, ready);
+    if (bytes > kFixedScratchBytes - kStatsBytes) return APPROX_ESCRATCH;
+    *out = src.fixed + kStatsBytes;
+    if (stats != nullptr) *stats = reinterpret_cast<int*>(src.fixed);
+    if (ready != nullptr) *ready = nullptr;
+    return APPROX_OK;
 }
 
 // Resident GEMM workgroups per device (CUs x blocks per CU), per kernel
@@ -553,7 +582,7 @@ int gemv_run(amx::GemvParams& g, int batch, float* C, int dev, hipStream_t strea
 int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int lda, long long strideA,
               const float* B, int ldb, long long strideB, float* C, int ldc, long long strideC, int batch,
               void* stream_v, const float* const* Ap = nullptr, const float* const* Bp = nullptr,
-              float* const* Cp = nullptr)
+              float* const* Cp = nullptr, bool noalloc = false)
 {
     const bool arrays = Ap != nullptr || Bp != nullptr || Cp != nullptr;
     if (arrays && (Ap == nullptr || Bp == nullptr || Cp == nullptr)) return APPROX_EINVAL;
@@ -578,6 +607,10 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
     if (rc != APPROX_OK) return rc;
     hipStream_t stream = static_cast<hipStream_t>(stream_v);
     ScratchSource src;
+    if (noalloc) {
+        rc = fixed_scratch(dev, &src.fixed);
+        if (rc != APPROX_OK) return rc;
+    }
 
     if (k == 0) {
         return amx::launch_fill_zero(C, Cp, m, n, ldc, batch, strideC, stream) == hipSuccess ? APPROX_OK
@@ -845,6 +878,9 @@ extern "C" int approx_lut_load(const uint16_t* lut, int M)
             }
         }
     std::memcpy(img.data() + flat_at, lut, entries * sizeof(uint16_t));
+    char* fixed = nullptr;
+    rc = fixed_scratch(dev, &fixed);
+    if (rc != APPROX_OK) return rc;
     uint16_t* d = nullptr;
     if (hipMalloc(&d, img.size() * sizeof(uint16_t)) != hipSuccess) return APPROX_EHIP;
     if (hipMemcpy(d, img.data(), img.size() * sizeof(uint16_t), hipMemcpyHostToDevice) != hipSuccess) {
@@ -864,6 +900,9 @@ extern "C" int approx_native_load(void)
 {
     int dev = 0;
     int rc = current_device(&dev);
+    if (rc != APPROX_OK) return rc;
+    char* fixed = nullptr;
+    rc = fixed_scratch(dev, &fixed);
     if (rc != APPROX_OK) return rc;
     std::lock_guard<std::mutex> lock(g_mu);
     if (g_tables[dev].image != nullptr) g_retired.emplace_back(dev, g_tables[dev].image);
@@ -906,6 +945,18 @@ extern "C" int approx_gemm(int transA, int transB, int m, int n, int k, const fl
                            int ldb, float* C, int ldc, void* stream)
 {
     return gemm_impl(transA, transB, m, n, k, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, stream);
+}
+
+extern "C" int approx_gemm_noalloc(int transA, int transB, int m, int n, int k, const float* A, int lda,
+                                   const float* B, int ldb, float* C, int ldc, void* stream)
+{
+    return gemm_impl(transA, transB, m, n, k, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, stream, nullptr, nullptr, nullptr,
+                     true);
+}
+
+extern "C" long long approx_gemm_noalloc_max_bytes(void)
+{
+    return (long long)(kFixedScratchBytes - kStatsBytes);
 }
 
 extern "C" int approx_gemm_strided_batched(int transA, int transB, int m, int n, int k, const float* A, int lda,
@@ -1037,6 +1088,7 @@ extern "C" const char* approx_status_string(int status)
     case APPROX_ENOLUT: return "no table loaded on this device";
     case APPROX_EUNSUPPORTED: return "unsupported (table size or problem size)";
     case APPROX_EHIP: return "HIP runtime error";
+    case APPROX_ESCRATCH: return "the call needs more scratch than the allocation-free entry point's fixed maximum";
     default: return "unknown status";
     }
 }

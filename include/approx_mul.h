@@ -62,6 +62,7 @@ extern "C" {
 #define APPROX_ENOLUT (-2)       /* no table loaded (and no native multiplier selected) on the current device */
 #define APPROX_EUNSUPPORTED (-3) /* M outside the supported range, or a table the generator cannot express */
 #define APPROX_EHIP (-4)         /* a HIP runtime call failed (allocation, copy, launch) */
+#define APPROX_ESCRATCH (-5)     /* the call needs more scratch than approx_gemm_noalloc's fixed maximum */
 
 /* Built-in C models of multipliers for approx_lut_build. */
 #define APPROX_MODEL_EXACT 0    /* the exact product of the M-bit mantissas */
@@ -172,6 +173,34 @@ int approx_exponent_bits(void);
 int approx_gemm(int transA, int transB, int m, int n, int k,
                 const float *A, int lda, const float *B, int ldb,
                 float *C, int ldc, void *stream);
+
+/*
+ * approx_gemm without any allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation while they run): the same arguments, kernels,
+ * products and summation order as approx_gemm, so the results are
+ * bitwise identical. Its scratch (decoded operands, exponent statistics,
+ * split partials) is one fixed array per device, reserved in the library's
+ * code object for the life of the process: approx_gemm_noalloc_max_bytes()
+ * bytes (64 MiB less the statistics). Its device address is looked up when
+ * a table (or the native multiplier) is loaded on the device, so these calls
+ * make no runtime lookups either. A call that needs more (about
+ * 8 * (ceil(k/4)*4) * (m + n) bytes of decoded operands, rows and columns
+ * rounded up to the kernel's tiles, plus split partials; row-vector calls
+ * need only their partials) returns APPROX_ESCRATCH before queuing
+ * anything. Every call on a device shares that device's array and
+ * re-initialises what must start at zero, so calls that overlap in time on
+ * one device (on different streams, or from different threads) race:
+ * order them on one stream. The table must be loaded beforehand
+ * (approx_lut_load allocates). Kernel timing (approx_profile_enable) skips
+ * these calls. Errors: as approx_gemm, and APPROX_ESCRATCH.
+ */
+int approx_gemm_noalloc(int transA, int transB, int m, int n, int k,
+                        const float *A, int lda, const float *B, int ldb,
+                        float *C, int ldc, void *stream);
+
+/* Bytes of scratch available to one approx_gemm_noalloc call. */
+long long approx_gemm_noalloc_max_bytes(void);
 
 /*
  * `batch` independent GEMMs: matrix b uses A + b*strideA, B + b*strideB and
