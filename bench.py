@@ -1,26 +1,34 @@
 #!/usr/bin/env python3
 """Throughput of the LUT-based approximate FP32 GEMM on one MI355X.
 
-Default workload: one approximate GEMM C = A B with m = n = k = 8192, A and B
-~ N(0, 1) (seeded, synthetic), and the M = 8 table of the exact mantissa
+Metric (the headline): one approximate GEMM C = A B with m = n = k = 8192, A and
+B ~ N(0, 1) (seeded, synthetic), and the M = 8 table of the exact mantissa
 product with a seeded +/-1 perturbation of every entry. A step is one
 ``approx_gemm`` call (decode pass + GEMM kernel) with the inputs already in
-HBM. Other workloads (--config 1, 2, 3, 5) are available for reference runs.
+HBM; `value` is G approximate MAC/s over K timed steps.
 
-Prints ONE JSON line: the metric (G approximate MAC/s over K timed steps),
-the GEMM kernel's roofline record (timed with HIP events inside the library,
-on the stream the kernel runs on, over K more steps that follow the timed
-ones) and the oracle's single-thread CPU throughput on a bounded sample of the
-same workload.
+The default run then times the other four workloads the same way and reports
+each under "workloads": 1 (64^3 GEMM, exact M = 7 table), 2 (MLP
+784-1024-1024-10, batch 256, forward + input and weight gradients), 3 (3x3
+Conv2D, NHWC 128x32x32x64 -> 64, three passes) and 5 (multi-head attention,
+16 x 512 x 768, 12 heads: QKV, QK^T, P V, output projection), all with the
+M = 7 Mitchell table; per workload: ms per step, G approximate MAC/s, the GEMM
+kernel's time and its fractions of the VALU and LDS-lookup roofs, and the
+oracle's CPU baseline (one core and all cores, on a stated sample).
 
---multiplier native runs the same workload with the library's native
-multiplier (the FP32 fused multiply-add in place of the table: ApproxTrain
-Section V / Fig. 6 compare the simulated multiplier against the native one);
---multiplier library times torch.matmul in FP32 on the GEMM workloads, for
-context. --table-bits M (9..11: tables in global memory), --exp-bits E
-(formats with fewer exponent bits) and --gemv [--rows R] (batch-1 or
-few-row inference through the row-vector kernel) time the other parts of
-the library. None of these is the headline.
+One JSON line: the metric, the GEMM kernel's roofline record (kernel time
+from HIP events inside the library, on the stream the kernel runs on, over K
+more steps that follow the timed ones), the CPU baseline, the per-workload
+records and the library's build stamp.
+
+--config N times workload N alone (its own line). --multiplier native runs it
+with the library's native multiplier (the FP32 fused multiply-add in place of
+the table: ApproxTrain Section V / Fig. 6 compare the simulated multiplier
+against the native one); --multiplier library times torch.matmul in FP32 on
+the GEMM workloads, for context. --table-bits M (9..11: tables in global
+memory), --exp-bits E (formats with fewer exponent bits) and --gemv [--rows R]
+(batch-1 or few-row inference through the row-vector kernel) time the other
+parts of the library. None of these is the headline.
 """
 import argparse
 import hashlib
@@ -59,6 +67,16 @@ def kernel_source_hash():
     p = os.path.join(ROOT, "approximate_multiplier_dnn_amd", "csrc", "kernels.hip")
     with open(p, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def library_source_hash():
+    """The stamp the library's build script computes from the sources beside it."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_approx_build", os.path.join(ROOT, "approximate_multiplier_dnn_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    return b.source_hash()
 
 
 def build_lds_probe():
@@ -218,53 +236,136 @@ def build_workload(config, am, torch, mult="table", table_bits=0, gemv=False, ge
 
         workload = "mha_b16_s512_d768_h12_qkv_qk_pv_out_" + ("lut_m7_mitchell" if lut is not None else "native_fp32_fma")
         info = dict(batch=Bz, seq=T, d_model=D, heads=Hh, note="softmax between the products is in the step time")
-        host = dict(X=X, Wqkv=Wqkv, lut=lut, M=M)
+        host = dict(X=X, Wqkv=Wqkv, Wo=Wo, lut=lut, M=M)
     else:
         raise SystemExit(f"unknown config {config}")
     return step, workload, info, host
 
 
-def cpu_baseline(config, host):
-    """The oracle, single-threaded, on a bounded sample of the workload."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_threads():
+    """Host threads for the all-cores baseline: the cores this process may
+    use (at most 16, the host share of one GPU on the box)."""
+    import oracle
+    return oracle.default_threads()
+
+
+def cpu_baseline(config, host, threads):
+    """The oracle as it stands, on a bounded sample of the workload: once on
+    one core, then the same sample over `threads` host threads (the oracle's
+    threaded driver: disjoint blocks of the outputs, the same per-output
+    code). `value` is the all-cores rate; `single_core_value` the one-core
+    rate."""
     import numpy as np
 
     import oracle
     from datagen import configs as cfg
 
-    t0 = time.perf_counter()
+    lut, M, E = host["lut"], host["M"], host.get("E", 8)
+
+    def all_outputs(m, n):
+        r, c = np.meshgrid(np.arange(m, dtype=np.int32), np.arange(n, dtype=np.int32), indexing="ij")
+        return r.ravel(), c.ravel()
+
     if config in (1, 4):
         A, B = host["A"], host["B"]
-        rows = min(64 if config == 1 else 32, A.shape[0])
-        oracle.gemm(np.ascontiguousarray(A[:rows]), B, host["lut"], host["M"], E=host.get("E", 8))
+        rows = min(64 if config == 1 else 16, A.shape[0])
+        Ar = np.ascontiguousarray(A[:rows])
+        rr, cc = all_outputs(rows, B.shape[1])
         macs = rows * B.shape[0] * B.shape[1]
         sample = f"rows 0-{rows - 1} of the {A.shape[0]}x{B.shape[1]}x{B.shape[0]} GEMM ({macs:.3g} MACs)"
+
+        def work(th):
+            oracle.gemm_at(Ar, B, lut, M, rr, cc, E=E, threads=th)
     elif config == 2:
+        calls = []
         macs = 0
         for (name, ta, tb, m, n, k, an, bn) in cfg.mlp_gemms():
             X, W, dY = host["layers"][int(name[-1])]
             ops = {"X": X, "W": W, "dY": dY}
-            if name.startswith("wgrad"):
-                continue   # the three weight gradients are skipped to bound the sample
-            oracle.gemm(ops[an], ops[bn], host["lut"], host["M"], transA=bool(ta), transB=bool(tb), E=host.get("E", 8))
+            calls.append((ops[an], ops[bn], bool(ta), bool(tb), all_outputs(m, n)))
             macs += m * n * k
-        sample = f"the 6 forward and input-gradient GEMMs of one pass ({macs:.3g} MACs)"
+        sample = f"the whole step: 9 GEMMs, forward, input and weight gradients of 3 layers ({macs:.3g} MACs)"
+
+        def work(th):
+            for (A, B, ta, tb, (rr, cc)) in calls:
+                oracle.gemm_at(A, B, lut, M, rr, cc, transA=ta, transB=tb, E=E, threads=th)
     elif config == 3:
-        x, w, dy = host["x"][:1], host["w"], host["dy"][:1]
-        oracle.conv2d_fwd(x, w, host["lut"], host["M"], (1, 1), (1, 1), E=host.get("E", 8))
-        oracle.conv2d_dgrad(dy, w, x.shape, host["lut"], host["M"], (1, 1), (1, 1), E=host.get("E", 8))
-        oracle.conv2d_wgrad(x, dy, w.shape, host["lut"], host["M"], (1, 1), (1, 1), E=host.get("E", 8))
-        macs = 3 * 32 * 32 * 64 * 9 * 64
-        sample = f"image 0 of 128, fwd + dgrad + wgrad ({macs:.3g} MACs)"
+        imgs = 4
+        x, w, dy = host["x"][:imgs], host["w"], host["dy"][:imgs]
+        macs = 3 * imgs * 32 * 32 * 64 * 9 * 64
+        sample = f"images 0-{imgs - 1} of 128, fwd + dgrad + wgrad over those images ({macs:.3g} MACs)"
+
+        def work(th):
+            oracle.conv2d_fwd(x, w, lut, M, (1, 1), (1, 1), E=E, threads=th)
+            oracle.conv2d_dgrad(dy, w, x.shape, lut, M, (1, 1), (1, 1), E=E, threads=th)
+            oracle.conv2d_wgrad(x, dy, w.shape, lut, M, (1, 1), (1, 1), E=E, threads=th)
     else:
-        rows = 64
-        X, Wqkv = host["X"], host["Wqkv"]
-        oracle.gemm(np.ascontiguousarray(X[:rows]), Wqkv, host["lut"], host["M"], E=host.get("E", 8))
-        macs = rows * Wqkv.shape[0] * Wqkv.shape[1]
-        sample = f"rows 0-{rows - 1} of the QKV projection ({macs:.3g} MACs)"
+        s = cfg.MHA_SHAPE
+        T, D, H = s["seq"], s["d_model"], s["heads"]
+        dh = D // H
+        X0 = np.ascontiguousarray(host["X"][:T])
+        Wqkv, Wo = host["Wqkv"], host["Wo"]
+        macs = T * 3 * D * D + 2 * H * T * T * dh + T * D * D
+        sample = f"sequence 0 of 16: QKV projection, QK^T and P V for its 12 heads, output projection ({macs:.3g} MACs)"
+
+        def work(th):
+            rr, cc = all_outputs(T, 3 * D)
+            qkv = oracle.gemm_at(X0, Wqkv, lut, M, rr, cc, E=E, threads=th)[0].astype(np.float32).reshape(T, 3 * D)
+            O = np.zeros((T, D), np.float32)
+            for h in range(H):
+                q, k, v = (np.ascontiguousarray(qkv[:, o * D + h * dh: o * D + (h + 1) * dh]) for o in range(3))
+                rr, cc = all_outputs(T, T)
+                sc = oracle.gemm_at(q, k, lut, M, rr, cc, transB=True, E=E, threads=th)[0].reshape(T, T) / dh ** 0.5
+                p = np.exp(sc - sc.max(axis=1, keepdims=True))
+                p = (p / p.sum(axis=1, keepdims=True)).astype(np.float32)
+                rr, cc = all_outputs(T, dh)
+                O[:, h * dh:(h + 1) * dh] = oracle.gemm_at(p, v, lut, M, rr, cc, E=E, threads=th)[0].reshape(T, dh)
+            rr, cc = all_outputs(T, D)
+            oracle.gemm_at(O, Wo, lut, M, rr, cc, E=E, threads=th)
+
+    t0 = time.perf_counter()
+    work(1)
+    t1 = time.perf_counter()
+    work(threads)
+    t2 = time.perf_counter()
+    unit = "G approximate MAC/s" if lut is not None else "G MAC/s"
+    return {"value": round(macs / (t2 - t1) / 1e9, 4), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(t2 - t1, 2),
+            "single_core_value": round(macs / (t1 - t0) / 1e9, 4), "single_core_seconds": round(t1 - t0, 2),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def time_workload(step, steps, warmup, am, torch):
+    """Warm-up steps, then `steps` timed steps bracketed by synchronisations
+    (the metric), then `steps` more with the library's HIP events around
+    every GEMM-kernel launch on its stream (the kernel time)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    unit = "G approximate MAC/s" if host["lut"] is not None else "G MAC/s"
-    return {"value": macs / dt / 1e9, "unit": unit, "cores": 1, "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 2)}
+    am.approx_profile_read()           # drop anything recorded so far
+    am.approx_profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    am.approx_profile_enable(False)
+    launches, kern_ms = am.approx_profile_read()
+    return dt, launches, kern_ms
 
 
 def main():
@@ -272,7 +373,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", type=int, default=4, help="workload 1-5 (4: 8192^3 GEMM, the headline)")
+    ap.add_argument("--config", type=int, default=None,
+                    help="time only this workload (1-5); default: workload 4 (8192^3 GEMM, the headline) as the "
+                         "metric, with workloads 1-5 each timed and reported under 'workloads'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--table-bits", type=int, default=0,
                     help="build the workload's table at this mantissa width instead (1-11; 9-11 are read "
@@ -320,16 +423,56 @@ def main():
         return
 
     import approximate_multiplier_dnn_amd as am
-    from datagen import configs as cfg
-    log(f"building workload {args.config} ...")
+
     torch.backends.cuda.matmul.allow_tf32 = False
-    if args.gemv and args.config not in (1, 4):
+    single = args.config is not None
+    config = args.config if single else 4
+    if args.gemv and config not in (1, 4):
         raise SystemExit("--gemv goes with the square GEMM workloads (--config 1 or 4)")
     if args.rows != 1 and not args.gemv:
         raise SystemExit("--rows goes with --gemv")
     if args.gemv and not 1 <= args.rows <= 64:
         raise SystemExit("--rows: 1 to 64")
-    step, workload, info, host = build_workload(args.config, am, torch, args.multiplier, args.table_bits, args.gemv,
+    if not single and (args.gemv or args.table_bits or args.exp_bits != 8 or args.multiplier != "table"):
+        raise SystemExit("--gemv, --table-bits, --exp-bits and --multiplier time one workload: give --config")
+    threads = cpu_threads()
+    rec, host = run_one(config, args, am, torch, threads)
+    if not single:
+        # the other workloads, each with its own timing, kernel fractions and
+        # CPU baseline (the headline's record above stays the metric)
+        work = {rec["config"]["workload"]: summary(rec)}
+        del host
+        for c in (1, 2, 3, 5):
+            torch.cuda.empty_cache()
+            r, h = run_one(c, args, am, torch, threads)
+            work[r["config"]["workload"]] = summary(r)
+            del h
+        rec["workloads"] = work
+    build = am.approx_build_id()
+    rec["build"] = {"id": build, "matches_sources": build == library_source_hash()}
+    print(json.dumps(rec), flush=True)
+
+
+def summary(rec):
+    """The per-workload entry of the default run."""
+    rf = rec["roofline"]
+    out = {"ms_per_step": rec["ms_per_step"], "value": rec["value"], "unit": rec["unit"],
+           "kernel": rf.get("kernel"), "kernel_ms_per_step": rf.get("kernel_ms_per_step"),
+           "kernel_G_mac_per_s": rf.get("kernel_G_mac_per_s"),
+           "valu_frac": rf.get("frac") if rf.get("bound") == "alu" else None,
+           "valu_frac_at_survey_ops": rf.get("frac_at_survey_ops"),
+           "lds_frac": (rf.get("lds") or {}).get("frac"),
+           "lds_frac_of_ceiling": (rf.get("lds") or {}).get("frac_of_ceiling")}
+    if "cpu_baseline" in rec:
+        out["cpu_baseline"] = rec["cpu_baseline"]
+    return out
+
+
+def run_one(config, args, am, torch, threads):
+    """Build, time and describe one workload; returns (record, host inputs)."""
+    from datagen import configs as cfg
+    log(f"building workload {config} ...")
+    step, workload, info, host = build_workload(config, am, torch, args.multiplier, args.table_bits, args.gemv,
                                                 args.rows)
     if args.exp_bits != 8:
         if args.multiplier != "table":
@@ -338,34 +481,24 @@ def main():
         workload += f"_e{args.exp_bits}"
         info["exponent_bits"] = args.exp_bits
         host["E"] = args.exp_bits
-    macs = host.get("macs") or cfg.macs(args.config)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # timed steps (the metric): nothing inside them but the steps themselves
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    # the same number of steps again with the library's HIP events around
-    # every GEMM-kernel launch, on the stream it runs on (the roofline's
-    # kernel time; the event records add a few microseconds per launch, so
-    # they stay out of the metric's steps)
-    am.approx_profile_read()           # drop anything recorded so far
-    am.approx_profile_enable(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    am.approx_profile_enable(False)
-    launches, kern_ms = am.approx_profile_read()
-    if args.multiplier == "library":   # torch.matmul runs on torch's stream: time it there
-        launches, kern_ms = args.steps, ev0.elapsed_time(ev1)
+    else:
+        am.approx_exponent_bits_set(8)
+    macs = host.get("macs") or cfg.macs(config)
+    if args.multiplier == "library":
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record()
+        for _ in range(args.steps):
+            step()
+        ev1.record()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        launches, kern_ms = args.steps, ev0.elapsed_time(ev1)   # torch.matmul runs on torch's stream
+    else:
+        dt, launches, kern_ms = time_workload(step, args.steps, args.warmup, am, torch)
     ms_per_step = dt * 1e3 / args.steps
     value = macs * args.steps / dt / 1e9
     log(f"{workload}: {ms_per_step:.3f} ms/step, {value:.1f} G MAC/s; "
@@ -373,25 +506,26 @@ def main():
 
     kern_s = kern_ms / 1e3
     mac_rate = macs * args.steps / kern_s if kern_s > 0 else 0.0     # MAC/s over kernel time
+    per_step = max(launches // max(args.steps, 1), 1)
+    common = {"kernel_ms_avg": round(kern_ms / max(launches, 1), 4), "launches_per_step": launches // max(args.steps, 1),
+              "kernel_ms_per_step": round(kern_ms / max(args.steps, 1), 4),
+              "kernel_G_mac_per_s": round(mac_rate / 1e9, 1)}
     if args.gemv and args.multiplier != "library":
         # the row-vector kernel streams B from HBM once per launch (one launch
         # takes all rows of A, in blocks of 4): algorithmic bytes per launch =
         # its rows of A + B read + its rows of C written
-        per_step = max(launches // max(args.steps, 1), 1)
         rb = host["A"].shape[0] / per_step
         kk, nn = host["B"].shape
         nbytes = 4 * (rb * kk + kk * nn + rb * nn)
         achieved = nbytes / (kern_s / max(launches, 1)) / 1e9 if kern_s > 0 else 0.0
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "amx::gemv_kernel",
-                    "kernel_ms_avg": round(kern_ms / max(launches, 1), 4),
-                    "launches_per_step": launches // max(args.steps, 1),
-                    "kernel_G_mac_per_s": round(mac_rate / 1e9, 1)}
+                    **common}
     elif args.multiplier == "library":
         achieved = 2 * mac_rate / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": FP32_MFMA_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                    "kernel": "torch.matmul (FP32)", "kernel_ms_avg": round(kern_ms / max(launches, 1), 4)}
+                    "kernel": "torch.matmul (FP32)", **common}
     else:
         # roofline of the GEMM kernel: algorithmic lane-ops over kernel time
         ops = OPS_PER_MAC if args.multiplier == "table" else 1        # native: one FMA per MAC
@@ -403,12 +537,17 @@ def main():
             "unit": "TOP/s",
             "frac": round(achieved / VALU_PEAK_TOPS, 4),
             "traffic": traffic_record(workload),
-            "kernel": "amx::gemv_kernel" if args.config == 1 else "amx::main_kernel",
-            "kernel_ms_avg": round(kern_ms / max(launches, 1), 4),
-            "launches_per_step": launches // max(args.steps, 1),
+            "kernel": "amx::gemv_kernel" if config == 1 else "amx::main_kernel",
             "ops_per_mac": ops,
-            "kernel_G_mac_per_s": round(mac_rate / 1e9, 1),
+            **common,
         }
+        if args.multiplier == "table":
+            # the survey's count: 2.5 lane-ops per MAC at M <= 7 (pre-shifted
+            # 32-bit entries, a packed FP32 add as half an op) and 3.5 at M = 8;
+            # packed FP32 is not used here, so this is context, not the metric
+            survey_ops = 2.5 if host["M"] <= 7 else 3.5
+            roofline["survey_ops_per_mac"] = survey_ops
+            roofline["frac_at_survey_ops"] = round(survey_ops * mac_rate / 1e12 / VALU_PEAK_TOPS, 4)
         if args.multiplier == "table" and host["M"] > 8:
             roofline["table"] = "global memory (M > 8 does not fit LDS)"
         elif args.multiplier == "table":
@@ -445,8 +584,8 @@ def main():
     }
     if not args.no_cpu_baseline and args.multiplier != "library":
         log("timing the oracle on a CPU sample ...")
-        rec["cpu_baseline"] = cpu_baseline(args.config, host)
-    print(json.dumps(rec), flush=True)
+        rec["cpu_baseline"] = cpu_baseline(config, host, threads)
+    return rec, host
 
 
 if __name__ == "__main__":
