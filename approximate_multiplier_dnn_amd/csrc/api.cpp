@@ -350,7 +350,7 @@ struct Plan {
     DecodeParams lane{}, uni{};
     MainParams mp{};
     int64_t lane_words = 0, uni_words = 0;    // per batch entry, allocated (rows padded)
-    int64_t lane_count = 0, uni_count = 0;    // per batch entry, logical Words the decode writes
+    int64_t lane_count = 0, uni_count = 0;    // per batch entry, logical words the decode writes
     int batch = 1;
     int gather = 0;
     int shape = 0;                // workgroup shape (index into kShapes)
@@ -370,19 +370,22 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     const int64_t TM = (int64_t)mp.wr * 64 * kShapes[pl.shape].rows_per_lane, TN = (int64_t)mp.wc * kColsPerWave;
     split_of(mp.tiles_m, mp.tiles_n, (int)TM, (int)TN, mp.KB, mp.m_out, mp.n_out, pl.batch, mp);
 
-    const size_t lane_b = align256((size_t)pl.lane_words * pl.batch * sizeof(Word));
-    const size_t uni_b = align256((size_t)pl.uni_words * pl.batch * sizeof(Word));
+    const int wbytes = M == 0 ? 4 : (int)sizeof(Word);      // the native multiplier keeps only the operands' bits
+    const size_t lane_b = align256((size_t)pl.lane_words * pl.batch * wbytes);
+    const size_t uni_b = align256((size_t)pl.uni_words * pl.batch * wbytes);
     const size_t part_b = mp.splits > 1 ? align256((size_t)mp.splits * pl.batch * mp.m_out * mp.n_out * sizeof(float)) : 0;
     char* base = nullptr;
     int* stats = nullptr;
     bool* stats_ready = nullptr;
     int rc = scratch_get(src, dev, stream, lane_b + uni_b + part_b, &base, &stats, &stats_ready);
     if (rc != APPROX_OK) return rc;
-    Word* lane_panel = reinterpret_cast<Word*>(base);
-    Word* uni_panel = reinterpret_cast<Word*>(base + lane_b);
+    void* lane_panel = base;
+    void* uni_panel = base + lane_b;
     float* partials = reinterpret_cast<float*>(base + lane_b + uni_b);
 
     pl.lane.dst = lane_panel;
+    pl.lane.wbytes = wbytes;
+    pl.uni.wbytes = wbytes;
     pl.lane.stats = stats;
     pl.lane.count = pl.lane_count ? pl.lane_count : pl.lane_words;
     pl.lane.dst_batch_stride = pl.lane_words;
@@ -429,7 +432,7 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     if (amx::launch_decode_pair(pl.lane, pl.uni, stream) != hipSuccess) return APPROX_EHIP;
     if (M == 8) {                     // M = 8 columns carry second copies to choose from
         amx::AssignParams& ap = pl.asg;
-        ap.panel = lane_panel;
+        ap.panel = static_cast<Word*>(lane_panel);
         ap.batch_stride = pl.lane_words;
         ap.batch = pl.batch;
         ap.pad_w = (1u << M) * 2u;
@@ -780,7 +783,7 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
         mp.KB = conv_ksteps(kind, s);
         pl.uni_count = (int64_t)mp.KB * 4 * Np;
         pl.uni_words = (int64_t)mp.KB * 4 * u.ldw;
-        const int rowB = Cb * Wp * 4;                 // one padded image row, in Words
+        const int rowB = Cb * Wp * 4;                 // one padded image row, in words
         mp.E2 = s.P; mp.E3 = s.Q;
         mp.L1 = Hp * rowB; mp.L2 = s.sh * rowB; mp.L3 = s.sw * 4;
         mp.U1 = s.R; mp.U2 = s.S; mp.U3 = Cb;

@@ -9,7 +9,8 @@
 namespace amx {
 
 // Decoded operand word, one per FP32 element, written by the decode pass and
-// read by the GEMM kernel. Two roles:
+// read by the GEMM kernel (with the native multiplier, M = 0, the panels hold
+// only the se half: 4 bytes per element, the operand's own bits). Two roles:
 //  - lane operand (varies across the 64 lanes of a wave): w = byte offset,
 //    relative to a table column, of its mantissa row (2 * index as the decode
 //    writes it; at M = 8 the copy choice may move it to the row's second
@@ -122,7 +123,8 @@ constexpr int STAT_READERS = STAT_INTS;   // index of the reader count
 struct DecodeParams {
     const float* src;
     const float* const* src_ptrs;   // batched by pointer array (device), else src + b * stride
-    Word* dst;
+    void* dst;           // Words (wbytes 8) or, for the native multiplier, the operands' bits (wbytes 4)
+    int wbytes;
     int* stats;          // slot base + role offset (0: lane, 2: uniform)
     int64_t count;       // words per batch entry
     int64_t src_batch_stride;  // elements
@@ -173,8 +175,8 @@ inline int panel_ld(int rowlen)
 // reduction indices stored contiguously; in gather mode every reduction index
 // is its own step and steps >= nku read the zero region at zoff.
 struct MainParams {
-    const Word* panel;        // lane operand words
-    const Word* bpanel;       // uniform operand words [Kp][Np]
+    const void* panel;        // lane operand words (Words; 4-byte words for the native multiplier)
+    const void* bpanel;       // uniform operand words [Kp][Np] (likewise)
     const uint16_t* lut;      // table image (lane-first layout)
     const int* stats;         // STAT_SLOTS slots of {lane min, lane max, uniform min, uniform max}
     float* out;               // C

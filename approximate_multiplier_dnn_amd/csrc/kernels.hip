@@ -106,6 +106,35 @@ __device__ __forceinline__ Word zero_word(int M, int lane_role)
     return w;
 }
 
+// Stores decoded words: 8-byte Words for a table; for the native multiplier
+// (wbytes 4) only the operand's own bits, the se half of its Word.
+__device__ __forceinline__ void put_word(void* dst, int64_t i, const Word& w, int wbytes)
+{
+    if (wbytes == 8) static_cast<Word*>(dst)[i] = w;
+    else static_cast<uint32_t*>(dst)[i] = w.se;
+}
+
+// n (2 or 4) consecutive words from index i; `vec`: the destination is
+// aligned for one 16- or 32-byte store (8 or 16 bytes for 4-byte words).
+__device__ __forceinline__ void put_words(void* dst, int64_t i, const Word (&wd)[4], int n, bool vec, int wbytes)
+{
+    if (wbytes == 8) {
+        Word* out = static_cast<Word*>(dst) + i;
+        if (vec) {
+            uint4* o = reinterpret_cast<uint4*>(out);
+            o[0] = make_uint4(wd[0].w, wd[0].se, wd[1].w, wd[1].se);
+            if (n == 4) o[1] = make_uint4(wd[2].w, wd[2].se, wd[3].w, wd[3].se);
+        } else {
+            for (int t = 0; t < n; ++t) out[t] = wd[t];
+        }
+    } else {
+        uint32_t* out = static_cast<uint32_t*>(dst) + i;
+        if (vec && n == 4) *reinterpret_cast<uint4*>(out) = make_uint4(wd[0].se, wd[1].se, wd[2].se, wd[3].se);
+        else if (vec && n == 2) *reinterpret_cast<uint2*>(out) = make_uint2(wd[0].se, wd[1].se);
+        else for (int t = 0; t < n; ++t) out[t] = wd[t].se;
+    }
+}
+
 // Fold this thread's exponent range into the call's stats: wave reduction,
 // then workgroup reduction through LDS, then one atomic pair per workgroup
 // into slot (blk % STAT_SLOTS; blk: the workgroup's index in its decode), so
@@ -235,13 +264,14 @@ __device__ __forceinline__ void decode_generic_body(const DecodeParams& p, uint3
     int emin = 255, emax = 0;
     const int b = (int)bid.y;
     const float* src = p.src_ptrs ? p.src_ptrs[b] : p.src + b * p.src_batch_stride;
-    Word* dst = p.dst + b * p.dst_batch_stride;
+    const int64_t d0 = b * p.dst_batch_stride;
     const uint32_t stride = gdim.x * 256u;
     for (uint32_t o = bid.x * 256u + threadIdx.x; o < (uint32_t)p.count; o += stride) {
         const int64_t s = decode_source(p, o);
         const uint32_t row = fdiv(o, p.fd_rowlen);
-        dst[(int64_t)row * p.ldw + (o - row * (uint32_t)p.rowlen)] =
-            s >= 0 ? decode_bits(__float_as_uint(src[s]), p.M, p.lane_role, emin, emax, p.elo, p.ehi) : zero_word(p.M, p.lane_role);
+        put_word(p.dst, d0 + (int64_t)row * p.ldw + (o - row * (uint32_t)p.rowlen),
+                 s >= 0 ? decode_bits(__float_as_uint(src[s]), p.M, p.lane_role, emin, emax, p.elo, p.ehi)
+                        : zero_word(p.M, p.lane_role), p.wbytes);
     }
     flush_stats(p.stats, emin, emax, linear_block(bid, gdim));
 }
@@ -252,27 +282,15 @@ __device__ __forceinline__ void decode_generic_body(const DecodeParams& p, uint3
 // contiguously, 2 or 4 Words (16 or 32 bytes) per thread and step.
 constexpr int IMG_ROW_FLOATS_MAX = 8192;   // 32 KB of LDS per workgroup
 
-__device__ __forceinline__ void store_words(Word* out, const Word (&wd)[4], int n, bool vec)
-{
-    if (vec) {
-        uint4* o = reinterpret_cast<uint4*>(out);
-        o[0] = make_uint4(wd[0].w, wd[0].se, wd[1].w, wd[1].se);
-        if (n == 4) o[1] = make_uint4(wd[2].w, wd[2].se, wd[3].w, wd[3].se);
-    } else {
-        for (int t = 0; t < n; ++t) out[t] = wd[t];
-    }
-}
-
 __device__ __forceinline__ void decode_img_body(const DecodeParams& p, uint3 bid, uint3 gdim, float* row)
 {
     int emin = 255, emax = 0;
     const int r = (int)bid.x;                      // output row
-    Word* dst = p.dst;
     if (r >= p.rows) {                             // zero tail of the weight-gradient image
         const int64_t body = (int64_t)p.rows * p.C * p.Wp;
         for (int64_t o = body + (int64_t)(r - p.rows) * 256 * 16 + threadIdx.x; o < p.count &&
              o < body + (int64_t)(r - p.rows + 1) * 256 * 16; o += 256)
-            dst[o] = zero_word(p.M, p.lane_role);
+            put_word(p.dst, o, zero_word(p.M, p.lane_role), p.wbytes);
         return;
     }
     // which source row feeds output row r (or none: a padding / dilation row)
@@ -305,7 +323,7 @@ __device__ __forceinline__ void decode_img_body(const DecodeParams& p, uint3 bid
         const bool fwd = p.layout == L_IMG_FWD;
         const int CH = fwd ? p.C : p.K;            // channels of a source pixel
         const int items = (fwd ? p.Cb : p.Kb) * p.Wp;
-        Word* out = dst + (int64_t)r * items * 4;
+        const int64_t out = (int64_t)r * items * 4;
         for (int q = threadIdx.x; q < items; q += 256) {
             const uint32_t blk = fdiv((uint32_t)q, p.fd_Wp);
             const int wq = q - (int)blk * p.Wp;
@@ -331,11 +349,11 @@ __device__ __forceinline__ void decode_img_body(const DecodeParams& p, uint3 bid
 #pragma unroll
                 for (int t = 0; t < 4; ++t) wd[t] = (px >= 0 && c0 + t < CH) ? dec(row[px * CH + c0 + t]) : z;
             }
-            store_words(out + (int64_t)q * 4, wd, 4, true);
+            put_words(p.dst, out + (int64_t)q * 4, wd, 4, true, p.wbytes);
         }
     } else {                                       // L_IMG_WGRAD: [Wp][C], 2 Words per item
         const int per_row = p.Wp * p.C;
-        Word* out = dst + (int64_t)r * per_row;
+        const int64_t out = (int64_t)r * per_row;
         const bool vec = (per_row & 1) == 0;       // rows (and so the pairs) 16-byte aligned
         for (int o = threadIdx.x * 2; o < per_row; o += 512) {
             Word wd[4];
@@ -347,7 +365,7 @@ __device__ __forceinline__ void decode_img_body(const DecodeParams& p, uint3 bid
                 const int c = (int)(e - wq * (uint32_t)p.C), w = (int)wq - p.pw;
                 wd[t] = (t < cnt && srow >= 0 && w >= 0 && w < p.W) ? dec(row[w * p.C + c]) : z;
             }
-            store_words(out + o, wd, cnt, vec && cnt == 2);
+            put_words(p.dst, out + o, wd, cnt, vec && cnt == 2, p.wbytes);
         }
     }
     flush_stats(p.stats, emin, emax, linear_block(bid, gdim));
@@ -371,7 +389,7 @@ __device__ __forceinline__ void decode_tile_body(const DecodeParams& p, uint3 bi
     int emin = 255, emax = 0;
     const int b = (int)bid.z;
     const float* src = p.src_ptrs ? p.src_ptrs[b] : p.src + b * p.src_batch_stride;
-    Word* dst = p.dst + b * p.dst_batch_stride;
+    const int64_t d0 = b * p.dst_batch_stride;
     const bool lane = p.layout == L_DENSE_LANE;
     const int tld = lane ? kTileLaneLd : kTileUniLd;
     const int outer0 = (int)bid.x * 64;            // i (lane) or j (uniform)
@@ -407,18 +425,13 @@ __device__ __forceinline__ void decode_tile_body(const DecodeParams& p, uint3 bi
             if (kb >= p.KB || oi >= p.Mp) continue;
             const float4 q = *reinterpret_cast<const float4*>(tile + i * kTileLaneLd + kbl * 4);
             const float v[4] = {q.x, q.y, q.z, q.w};
-            uint32_t o[8];
+            Word wd[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const Word wd = (oi < p.m && k0 + kbl * 4 + t < p.k)
+            for (int t = 0; t < 4; ++t)
+                wd[t] = (oi < p.m && k0 + kbl * 4 + t < p.k)
                     ? decode_bits(__float_as_uint(v[t]), p.M, 1, emin, emax, p.elo, p.ehi)
                     : zero_word(p.M, 1);
-                o[2 * t] = wd.w;
-                o[2 * t + 1] = wd.se;
-            }
-            uint4* out = reinterpret_cast<uint4*>(dst + (int64_t)kb * p.ldw + (int64_t)oi * 4);
-            out[0] = make_uint4(o[0], o[1], o[2], o[3]);
-            out[1] = make_uint4(o[4], o[5], o[6], o[7]);
+            put_words(p.dst, d0 + (int64_t)kb * p.ldw + (int64_t)oi * 4, wd, 4, true, p.wbytes);
         }
     } else {
         // output row kk holds 64 contiguous columns j: a lane takes j, j+1
@@ -426,18 +439,18 @@ __device__ __forceinline__ void decode_tile_body(const DecodeParams& p, uint3 bi
             const int kk = ((f >> 6) << 1) | ((f >> 5) & 1), j = (f & 31) * 2;
             const int oj = outer0 + j, ki = k0 + kk;
             if (ki >= p.KB * 4) continue;
-            Word wd[2];
+            Word wd[4];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
                 wd[t] = (oj + t < p.n && ki < p.k)
                     ? decode_bits(__float_as_uint(tile[(j + t) * kTileUniLd + kk]), p.M, 0, emin, emax, p.elo, p.ehi)
                     : zero_word(p.M, 0);
-            Word* out = dst + (int64_t)ki * p.ldw + oj;
+            const int64_t out = d0 + (int64_t)ki * p.ldw + oj;
             if (oj + 1 < p.Np && (p.ldw & 1) == 0) {
-                *reinterpret_cast<uint4*>(out) = make_uint4(wd[0].w, wd[0].se, wd[1].w, wd[1].se);
+                put_words(p.dst, out, wd, 2, true, p.wbytes);
             } else {
-                if (oj < p.Np) out[0] = wd[0];
-                if (oj + 1 < p.Np) out[1] = wd[1];
+                if (oj < p.Np) put_word(p.dst, out, wd[0], p.wbytes);
+                if (oj + 1 < p.Np) put_word(p.dst, out + 1, wd[1], p.wbytes);
             }
         }
     }
@@ -464,7 +477,7 @@ __device__ __forceinline__ void decode_rows_body(const DecodeParams& p, uint3 bi
     int emin = 255, emax = 0;
     const int b = (int)bid.z;
     const float* src = p.src_ptrs ? p.src_ptrs[b] : p.src + b * p.src_batch_stride;
-    Word* dst = p.dst + b * p.dst_batch_stride;
+    const int64_t d0 = b * p.dst_batch_stride;
     const int r0 = (int)bid.x * rb;
     const uint32_t quads = (uint32_t)min(rb, p.KB * 4 - r0) * (uint32_t)(p.Np >> 2);
     const bool vsrc = ((reinterpret_cast<uintptr_t>(src) & 15u) == 0) && ((p.ld & 3) == 0);
@@ -487,7 +500,7 @@ __device__ __forceinline__ void decode_rows_body(const DecodeParams& p, uint3 bi
             wd[t] = (kk < p.k && col + t < p.n)
                 ? decode_bits(__float_as_uint(v[t]), p.M, p.lane_role, emin, emax, p.elo, p.ehi)
                 : zero_word(p.M, p.lane_role);
-        store_words(dst + (int64_t)kk * p.ldw + col, wd, 4, true);
+        put_words(p.dst, d0 + (int64_t)kk * p.ldw + col, wd, 4, true, p.wbytes);
     }
     flush_stats(p.stats, emin, emax, linear_block(bid, gdim));
 }
@@ -772,20 +785,6 @@ __device__ __forceinline__ void ranged_index(const uint32_t (&wa)[RPL], const ui
 #undef AMX_COLW
 }
 
-// Native multiplier over one reduction index: the IEEE single-precision
-// product folded by the hardware FMA, acc = fma(a, b, acc) (the product is
-// exact inside the FMA; one rounding per step). No table lookup: this is the
-// reference point the approximate product is compared against.
-template <int RPL>
-__device__ __forceinline__ void native_index(const uint32_t (&sa)[RPL], const uint32_t (&q)[UQ],
-                                             float (&acc)[RPL][CPW])
-{
-#pragma unroll
-    for (int g = 0; g < CPW; ++g)
-#pragma unroll
-        for (int x = 0; x < RPL; ++x) fmac_quad(acc[x][g], q[4 * (g >> 3) + 2 * (g & 1) + 1], __uint_as_float(sa[x]), (g >> 1) & 3);
-}
-
 // Checked path over one reduction index: one product at a time (it only runs
 // for operands that can leave the normal range, so it is kept small in
 // registers rather than fast).
@@ -815,14 +814,13 @@ __device__ __forceinline__ void checked_index(const uint32_t (&wa)[RPL], const u
 // every index has its own offset from the counter (the zero region past the
 // last index). The steady-state body has no branch: the compiler's wait
 // counts for the ring stay exact, so the prefetch is never drained early.
-template <bool GATHER, bool NATIVE, bool RANGED, int R, int RPL, int LA>
+template <bool GATHER, bool RANGED, int R, int RPL, int LA>
 __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* panel, const Word* bsrc,
                                               const uint32_t (&base)[RPL], int kb0, int kb1, uint32_t quad,
                                               const unsigned char* lut, float (&acc)[RPL][CPW])
 {
     auto fold = [&](const uint32_t (&wa)[RPL], const uint32_t (&sa)[RPL], const uint32_t (&q)[UQ]) {
-        if constexpr (NATIVE) native_index(sa, q, acc);
-        else if constexpr (RANGED) ranged_index<RPL, LA>(wa, sa, q, lut, acc, p.elo);
+        if constexpr (RANGED) ranged_index<RPL, LA>(wa, sa, q, lut, acc, p.elo);
         else fast_index<RPL, LA>(wa, sa, q, lut, acc);
     };
     constexpr int PD = R - 1;
@@ -949,6 +947,132 @@ __device__ __forceinline__ void mainloop_checked(const MainParams& p, const Word
 }
 
 
+// Native multiplier (4-byte words: the operands' own bits). The words of one
+// k-step (4 consecutive reduction indices) for this lane: its RPL
+// lane-operand rows, and its quarter of the wave's 16 uniform columns. The
+// uniform words of an index are spread over the 4 lanes of every quad: lane
+// i of a quad holds the words of columns 4i .. 4i + 3, read by the FMA with a
+// DPP quad_perm broadcast of lane c >> 2 (register c & 3).
+template <int RPL>
+struct StepWords {
+    uint32_t a[RPL][4];      // lane operand: row x, index t
+    uint32_t u[4][4];        // uniform operand: index t, column 4 * quad + c
+};
+
+// Loads one k-step. Vector mode: a row's 4 words are contiguous (one 16-byte
+// load at the counter's offset). Gather mode: every index has its own
+// offset (or the zero region past the last index). urow: the uniform row of
+// the k-step's first index plus this lane's quad offset.
+template <bool GATHER, int RPL>
+__device__ __forceinline__ void load_step(const MainParams& p, const uint32_t* panel, const uint32_t (&base)[RPL],
+                                          const uint32_t* urow, KCounter& kc, int& ku, StepWords<RPL>& s)
+{
+    if (!GATHER) {
+#pragma unroll
+        for (int x = 0; x < RPL; ++x) {
+            const uint4 q = *reinterpret_cast<const uint4*>(panel + base[x] + kc.off);
+            s.a[x][0] = q.x; s.a[x][1] = q.y; s.a[x][2] = q.z; s.a[x][3] = q.w;
+        }
+        kc_next(p, kc);
+    } else {
+        int off[4];
+        step_offsets<true>(p, kc, ku, off);
+#pragma unroll
+        for (int x = 0; x < RPL; ++x)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) s.a[x][t] = panel[base[x] + off[t]];
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint4 q = *reinterpret_cast<const uint4*>(urow + (int64_t)t * p.bld);
+        s.u[t][0] = q.x; s.u[t][1] = q.y; s.u[t][2] = q.z; s.u[t][3] = q.w;
+    }
+}
+
+// Native multiplier over one reduction index: the IEEE single-precision
+// product folded by the hardware FMA, acc = fma(a, b, acc) (the product is
+// exact inside the FMA; one rounding per step). No table lookup: this is the
+// reference point the approximate product is compared against. The words are
+// the operands' own bits, straight from their loads.
+template <int RPL>
+__device__ __forceinline__ void native_step_index(const uint32_t (&a)[RPL], const uint32_t (&u)[4], float (&acc)[RPL][CPW])
+{
+#pragma unroll
+    for (int g = 0; g < CPW; ++g)
+#pragma unroll
+        for (int x = 0; x < RPL; ++x) fmac_quad(acc[x][g], u[g & 3], __uint_as_float(a[x]), g >> 2);
+}
+
+// The native multiplier's k-loop over k-steps [kb0, kb1): the words of
+// k-step v are requested NS - 1 k-steps before use, into ring slot v % NS; a
+// loop body covers NS k-steps, so every slot number is a compile-time
+// constant, and the steady-state body has no branch (the compiler's wait
+// counts for the ring stay exact).
+template <bool GATHER, int NS, int RPL>
+__device__ __forceinline__ void mainloop_native(const MainParams& p, const uint32_t* panel, const uint32_t* bsrc,
+                                                const uint32_t (&base)[RPL], int kb0, int kb1, uint32_t quad,
+                                                float (&acc)[RPL][CPW])
+{
+    auto fold = [&](const StepWords<RPL>& s) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            uint32_t a[RPL];
+#pragma unroll
+            for (int x = 0; x < RPL; ++x) a[x] = s.a[x][t];
+            native_step_index(a, s.u[t], acc);
+        }
+    };
+    constexpr int PD = NS - 1;
+    const int n = kb1 - kb0;
+    KCounter kc = kc_init(p, GATHER ? kb0 * 4 : kb0);
+    int ku = kb0 * 4;
+    const uint32_t* urow = bsrc + quad * 4 + (int64_t)kb0 * 4 * p.bld;
+    const int64_t ustep = (int64_t)4 * p.bld;
+    StepWords<RPL> s[NS];
+    int v0 = 0;
+    if (n >= NS + PD) {
+        // unconditional prologue: the loop is entered with the same loads in
+        // flight as at its back edge
+#pragma unroll
+        for (int v = 0; v < PD; ++v) {
+            load_step<GATHER, RPL>(p, panel, base, urow, kc, ku, s[v]);
+            urow += ustep;
+            asm volatile("" ::: "memory");
+        }
+        // The compiler drains the loads in flight at the loop head; folding
+        // k-step v0 before requesting k-step v0 + PD means that drain only
+        // waits for loads that were issued at least one k-step earlier.
+        for (; v0 + NS + PD <= n; v0 += NS) {
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                if (j == 0) fold(s[0]);
+                load_step<GATHER, RPL>(p, panel, base, urow, kc, ku, s[(j + PD) % NS]);
+                urow += ustep;
+                if (j > 0) fold(s[j]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < PD; ++v) {
+            if (v < n) {
+                load_step<GATHER, RPL>(p, panel, base, urow, kc, ku, s[v]);
+                urow += ustep;
+            }
+        }
+    }
+    for (; v0 < n; v0 += NS) {                   // tail: fewer than NS + PD k-steps left
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            if (v0 + j >= n) break;
+            if (v0 + j + PD < n) {
+                load_step<GATHER, RPL>(p, panel, base, urow, kc, ku, s[(j + PD) % NS]);
+                urow += ustep;
+            }
+            fold(s[j]);
+        }
+    }
+}
+
 // LDSB: bytes of the LDS table image (LDS_SMALL or LDS_LARGE), or NATIVE_LDS
 // where no table is staged (native multiplier, table in global memory).
 constexpr int NATIVE_LDS = 16;
@@ -1045,8 +1169,11 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
             const int i2 = r2 % p.E2, i1 = r2 / p.E2;
             base[x] = (uint32_t)(i1 * p.L1 + i2 * p.L2 + i3 * p.L3);
         }
-        const Word* panel = p.panel + (int64_t)b * p.panel_batch;
-        const Word* bsrc = p.bpanel + (int64_t)b * p.bpanel_batch + col0;
+        // table: 8-byte Words; native multiplier: 4-byte words (the operands' bits)
+        const Word* panel = static_cast<const Word*>(p.panel) + (int64_t)b * p.panel_batch;
+        const Word* bsrc = static_cast<const Word*>(p.bpanel) + (int64_t)b * p.bpanel_batch + col0;
+        const uint32_t* npanel = static_cast<const uint32_t*>(p.panel) + (int64_t)b * p.panel_batch;
+        const uint32_t* nbsrc = static_cast<const uint32_t*>(p.bpanel) + (int64_t)b * p.bpanel_batch + col0;
         const int kb0 = split < 0 ? 0 : split * p.chunk;
         const int kb1 = split < 0 ? p.KB : min(p.KB, kb0 + p.chunk);
 
@@ -1057,9 +1184,11 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
             for (int j = 0; j < CPW; ++j) acc[x][j] = 0.0f;
 
         if (kb0 < kb1) {
-            if (fast) mainloop_fast<GATHER, NATIVE, false, NATIVE ? 8 : 4, RPL, LA>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
-            else if constexpr (!NATIVE) {
-                if (ranged) mainloop_fast<GATHER, false, true, 4, RPL, LA>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
+            // a ring of 3 k-steps; 2 in the 12-wave shape, whose registers hold no third
+            if constexpr (NATIVE) mainloop_native<GATHER, NW == 12 ? 2 : 3, RPL>(p, npanel, nbsrc, base, kb0, kb1, quad, acc);
+            else if (fast) mainloop_fast<GATHER, false, 4, RPL, LA>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
+            else {
+                if (ranged) mainloop_fast<GATHER, true, 4, RPL, LA>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
                 else mainloop_checked<GATHER, RPL>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
             }
         }

@@ -185,8 +185,9 @@ int approx_gemm(int transA, int transB, int m, int n, int k,
  * bytes (64 MiB less the statistics). Its device address is looked up when
  * a table (or the native multiplier) is loaded on the device, so these calls
  * make no runtime lookups either. A call that needs more (about
- * 8 * (ceil(k/4)*4) * (m + n) bytes of decoded operands, rows and columns
- * rounded up to the kernel's tiles, plus split partials; row-vector calls
+ * 8 * (ceil(k/4)*4) * (m + n) bytes of decoded operands (4 * ... with the
+ * native multiplier), rows and columns rounded up to the kernel's tiles,
+ * plus split partials; row-vector calls
  * need only their partials) returns APPROX_ESCRATCH before queuing
  * anything. Every call on a device shares that device's array and
  * re-initialises what must start at zero, so calls that overlap in time on

@@ -106,7 +106,7 @@ def test_noalloc_refuses_oversized_call(am):
     am.approx_lut_load(t, M)
     cap = am.approx_gemm_noalloc_max_bytes()
     assert cap > 0
-    # 8 bytes per decoded element: (m + n) * k * 8 > cap
+    # 8 bytes per decoded element (a table is loaded): (m + n) * k * 8 > cap
     m = n = 2048
     k = int(cap // (8 * (m + n))) + 64
     A = torch.zeros((m, k), dtype=torch.float32, device="cuda")
