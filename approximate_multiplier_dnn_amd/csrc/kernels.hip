@@ -736,6 +736,89 @@ __device__ __forceinline__ void fast_index(const uint32_t (&wa)[RPL], const uint
 #undef AMX_COLW
 }
 
+// Columns of an index whose lookups go to the table image in global memory
+// (L2-resident) instead of the LDS copy: GOFF of the 16, evenly spaced. The
+// LDS then serves (16 - GOFF) / 16 of the lookups and the vector-memory path
+// the rest, each at its own rate; both read the same image, so the entries
+// are the same. Measured on MI355X (GEMM-kernel ms; 8192^3 at M = 8, the
+// 3 x 3 conv passes at M = 7): GOFF 0: 70.07 / 0.598, 1: 67.86 / 0.587,
+// 2: 73.74 / 0.598, 4: 103.4 / 1.295 (the gathers then saturate the
+// texture path, which also carries the operand words).
+#ifndef AMX_GOFF
+#define AMX_GOFF 1
+#endif
+template <int GOFF>
+__host__ __device__ constexpr bool gcol_is(int c)
+{
+    return GOFF > 0 && c % (CPW / GOFF) == CPW / GOFF - 1;
+}
+template <int GOFF>
+__host__ __device__ constexpr int gcol(int s)
+{
+    return (s + 1) * (CPW / GOFF) - 1;
+}
+template <int GOFF>
+__host__ __device__ constexpr int lcol(int i)          // i-th column served by the LDS
+{
+    int k = -1;
+    for (int c = 0; c < CPW; ++c)
+        if (!gcol_is<GOFF>(c) && ++k == i) return c;
+    return 0;
+}
+typedef const unsigned char __attribute__((address_space(1)))* gbyte_ptr;
+
+// The fast path with GOFF columns from global memory: their entries for this
+// index (gcur) were requested during the previous index; those of the next
+// index (wan, qn: its lane and uniform words) are requested here, before the
+// LDS lookups, so they have a whole index to arrive.
+template <int RPL, int LA, int GOFF>
+__device__ __forceinline__ void fast_index_split(const uint32_t (&wa)[RPL], const uint32_t (&sa)[RPL],
+                                                 const uint32_t (&q)[UQ], const unsigned char* lut,
+                                                 float (&acc)[RPL][CPW], const uint32_t (&gcur)[GOFF][RPL], bool pre,
+                                                 const uint32_t (&wan)[RPL], const uint32_t (&qn)[UQ], gbyte_ptr gtab,
+                                                 uint32_t (&gnext)[GOFF][RPL])
+{
+    constexpr int NL = CPW - GOFF;
+    uint32_t e[LA + 1][RPL];
+#define AMX_COLW(j) col_word(q, (j), 0)
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+#pragma unroll
+        for (int x = 0; x < RPL; ++x) e[i][x] = *reinterpret_cast<const uint16_t*>(lut + (wa[x] + AMX_COLW(lcol<GOFF>(i))));
+    if (pre) {
+#pragma unroll
+        for (int s2 = 0; s2 < GOFF; ++s2) {
+            const uint32_t wb = col_word(qn, gcol<GOFF>(s2), 0);
+#pragma unroll
+            for (int x = 0; x < RPL; ++x)
+                gnext[s2][x] = *reinterpret_cast<const uint16_t __attribute__((address_space(1)))*>(gtab + (wan[x] + wb));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int g = lcol<GOFF>(i);
+        if (i + LA < NL) {
+#pragma unroll
+            for (int x = 0; x < RPL; ++x)
+                e[(i + LA) % (LA + 1)][x] = *reinterpret_cast<const uint16_t*>(lut + (wa[x] + AMX_COLW(lcol<GOFF>(i + LA))));
+        }
+#pragma unroll
+        for (int x = 0; x < RPL; ++x)
+            fmac_quad(acc[x][g], q[4 * (g >> 3) + 2 * (g & 1) + 1], __uint_as_float((e[i % (LA + 1)][x] << 8) + sa[x]),
+                      (g >> 1) & 3);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < GOFF; ++s2) {
+        const int g = gcol<GOFF>(s2);
+#pragma unroll
+        for (int x = 0; x < RPL; ++x)
+            fmac_quad(acc[x][g], q[4 * (g >> 3) + 2 * (g & 1) + 1], __uint_as_float((gcur[s2][x] << 8) + sa[x]),
+                      (g >> 1) & 3);
+    }
+#undef AMX_COLW
+}
+
 // Fast path with underflow, over one reduction index: for calls where some
 // products may fall below the format's range (tiny operands, or a format with
 // fewer exponent bits) but none can exceed it. A product underflows exactly
@@ -814,14 +897,22 @@ __device__ __forceinline__ void checked_index(const uint32_t (&wa)[RPL], const u
 // every index has its own offset from the counter (the zero region past the
 // last index). The steady-state body has no branch: the compiler's wait
 // counts for the ring stay exact, so the prefetch is never drained early.
-template <bool GATHER, bool RANGED, int R, int RPL, int LA>
+template <bool GATHER, bool RANGED, int R, int RPL, int LA, int GOFF = 0>
 __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* panel, const Word* bsrc,
                                               const uint32_t (&base)[RPL], int kb0, int kb1, uint32_t quad,
                                               const unsigned char* lut, float (&acc)[RPL][CPW])
 {
-    auto fold = [&](const uint32_t (&wa)[RPL], const uint32_t (&sa)[RPL], const uint32_t (&q)[UQ]) {
+    constexpr int NG = GOFF > 0 ? GOFF : 1;
+    uint32_t gl[2][NG][RPL];                     // global-memory entries of the current / next index
+    const gbyte_ptr gtab = (gbyte_ptr)p.lut;
+    // index v's fold; v's words in slot s, the next index's in slot sn
+    auto fold_at = [&](const uint32_t (&wa)[RPL], const uint32_t (&sa)[RPL], const uint32_t (&q)[UQ], int par,
+                       bool pre, const uint32_t (&wan)[RPL], const uint32_t (&qn)[UQ]) {
         if constexpr (RANGED) ranged_index<RPL, LA>(wa, sa, q, lut, acc, p.elo);
-        else fast_index<RPL, LA>(wa, sa, q, lut, acc);
+        else if constexpr (GOFF > 0) {
+            if (par == 0) fast_index_split<RPL, LA, NG>(wa, sa, q, lut, acc, gl[0], pre, wan, qn, gtab, gl[1]);
+            else fast_index_split<RPL, LA, NG>(wa, sa, q, lut, acc, gl[1], pre, wan, qn, gtab, gl[0]);
+        } else fast_index<RPL, LA>(wa, sa, q, lut, acc);
     };
     constexpr int PD = R - 1;
     constexpr int NS = R / 2;
@@ -859,6 +950,18 @@ __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* p
     };
     const Word* urow = bsrc + (int64_t)kb0 * 4 * p.bld;
     uint32_t wa[R][RPL], sa[R][RPL], qb[R][UQ];
+    // the global-memory entries of the first index (its words are in slot 0)
+    auto first_global = [&]() {
+        if constexpr (GOFF > 0 && !RANGED) {
+#pragma unroll
+            for (int s2 = 0; s2 < GOFF; ++s2) {
+                const uint32_t wb = col_word(qb[0], gcol<GOFF>(s2), 0);
+#pragma unroll
+                for (int x = 0; x < RPL; ++x)
+                    gl[0][s2][x] = *reinterpret_cast<const uint16_t __attribute__((address_space(1)))*>(gtab + (wa[0][x] + wb));
+            }
+        }
+    };
     int u0 = 0;
     if (n >= R + PD) {
         // unconditional prologue: the loop is entered with the same loads in
@@ -870,17 +973,18 @@ __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* p
             urow += p.bld;
             asm volatile("" ::: "memory");       // one load group per index, as in the loop
         }
+        first_global();
         // The compiler drains the loads in flight at the loop head; folding
         // index u0 before requesting index u0 + PD means that drain only
         // waits for loads that were issued at least one index earlier.
         for (; u0 + R + PD <= n; u0 += R) {
 #pragma unroll
             for (int j = 0; j < R; ++j) {
-                if (j == 0) fold(wa[0], sa[0], qb[0]);
+                if (j == 0) fold_at(wa[0], sa[0], qb[0], 0, true, wa[1], qb[1]);
                 load_lane(panel, base, lane_off(j + PD), wa[(j + PD) % R], sa[(j + PD) % R]);
                 load_uniform(urow, quad, qb[(j + PD) % R]);
                 urow += p.bld;
-                if (j > 0) fold(wa[j], sa[j], qb[j]);
+                if (j > 0) fold_at(wa[j], sa[j], qb[j], j & 1, true, wa[(j + 1) % R], qb[(j + 1) % R]);
             }
             advance();
         }
@@ -893,6 +997,7 @@ __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* p
                 urow += p.bld;
             }
         }
+        if (n > 0) first_global();
     }
     for (; u0 < n; u0 += R) {                    // tail: fewer than R + PD indices left
 #pragma unroll
@@ -903,7 +1008,7 @@ __device__ __forceinline__ void mainloop_fast(const MainParams& p, const Word* p
                 load_uniform(urow, quad, qb[(j + PD) % R]);
                 urow += p.bld;
             }
-            fold(wa[j], sa[j], qb[j]);
+            fold_at(wa[j], sa[j], qb[j], j & 1, u0 + j + 1 < n, wa[(j + 1) % R], qb[(j + 1) % R]);
         }
         advance();
     }
@@ -1186,7 +1291,7 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
         if (kb0 < kb1) {
             // a ring of 3 k-steps; 2 in the 12-wave shape, whose registers hold no third
             if constexpr (NATIVE) mainloop_native<GATHER, NW == 12 ? 2 : 3, RPL>(p, npanel, nbsrc, base, kb0, kb1, quad, acc);
-            else if (fast) mainloop_fast<GATHER, false, 4, RPL, LA>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
+            else if (fast) mainloop_fast<GATHER, false, 4, RPL, LA, GTAB ? 0 : AMX_GOFF>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
             else {
                 if (ranged) mainloop_fast<GATHER, true, 4, RPL, LA>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
                 else mainloop_checked<GATHER, RPL>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
