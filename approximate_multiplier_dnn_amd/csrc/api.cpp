@@ -93,6 +93,15 @@ const size_t kStatsBytes = align256((amx::STAT_INTS + 1) * sizeof(int));
 // so the superseded arenas (retired, not freed) hold less memory than the
 // current one. *ready: whether the stats hold the reset values (the caller
 // initialises them and sets it).
+// Test hook for the allocation-failure path: with APPROX_TEST_ALLOC_LIMIT set
+// to a byte count, a scratch allocation larger than it fails as a failed
+// hipMalloc would (APPROX_EHIP, nothing queued).
+bool alloc_refused(size_t bytes)
+{
+    const char* v = std::getenv("APPROX_TEST_ALLOC_LIMIT");
+    return v != nullptr && v[0] != '\0' && bytes > (size_t)std::strtoull(v, nullptr, 10);
+}
+
 int arena_get(int dev, hipStream_t stream, size_t bytes, char** out, int** stats = nullptr, bool** ready = nullptr)
 {
     std::lock_guard<std::mutex> lock(g_mu);
@@ -101,7 +110,7 @@ int arena_get(int dev, hipStream_t stream, size_t bytes, char** out, int** stats
     if (a.bytes < bytes) {
         const size_t want = std::max(bytes + bytes / 8, 2 * a.bytes);
         void* p = nullptr;
-        if (hipMalloc(&p, want) != hipSuccess) return APPROX_EHIP;
+        if (alloc_refused(want) || hipMalloc(&p, want) != hipSuccess) return APPROX_EHIP;
         if (a.ptr != nullptr) g_retired.emplace_back(dev, a.ptr);
         a.ptr = p;
         a.bytes = want;
@@ -358,26 +367,46 @@ struct Plan {
     float* const* Cp = nullptr;   // output pointer array (batched by pointers)
     int64_t strideC = 0;
     amx::AssignParams asg{};      // M = 8 copy choice of the lane operands (groups of one half-wave)
+    // set by plan_finalize: word size, scratch bytes of each part, kernel variant
+    int wbytes = 8;
+    size_t lane_b = 0, uni_b = 0, part_b = 0;
+    int lds_class = 0;
 };
 
-int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M, const ScratchSource& src)
+// The table-dependent part of a plan (a function of the shapes and M only):
+// the reduction split, the word size, the scratch layout and the GEMM-kernel
+// variant. APPROX_EUNSUPPORTED when a panel would exceed the word limit.
+int plan_finalize(Plan& pl, int M)
 {
     MainParams& mp = pl.mp;
     if (pl.lane_words * pl.batch >= kMaxPanelWords || pl.uni_words * pl.batch >= kMaxPanelWords)
         return APPROX_EUNSUPPORTED;
     // M = 0: native multiplier; M = 9..11: table in global memory
-    const int lds_class = M == 0 ? 2 : M <= 7 ? 0 : M == 8 ? 1 : 3;
+    pl.lds_class = M == 0 ? 2 : M <= 7 ? 0 : M == 8 ? 1 : 3;
     const int64_t TM = (int64_t)mp.wr * 64 * kShapes[pl.shape].rows_per_lane, TN = (int64_t)mp.wc * kColsPerWave;
     split_of(mp.tiles_m, mp.tiles_n, (int)TM, (int)TN, mp.KB, mp.m_out, mp.n_out, pl.batch, mp);
+    pl.wbytes = M == 0 ? 4 : (int)sizeof(Word);     // the native multiplier keeps only the operands' bits
+    pl.lane_b = align256((size_t)pl.lane_words * pl.batch * pl.wbytes);
+    pl.uni_b = align256((size_t)pl.uni_words * pl.batch * pl.wbytes);
+    pl.part_b = mp.splits > 1 ? align256((size_t)mp.splits * pl.batch * mp.m_out * mp.n_out * sizeof(float)) : 0;
+    pl.lane.count = pl.lane_count ? pl.lane_count : pl.lane_words;
+    pl.uni.count = pl.uni_count ? pl.uni_count : pl.uni_words;
+    return APPROX_OK;
+}
 
-    const int wbytes = M == 0 ? 4 : (int)sizeof(Word);      // the native multiplier keeps only the operands' bits
-    const size_t lane_b = align256((size_t)pl.lane_words * pl.batch * wbytes);
-    const size_t uni_b = align256((size_t)pl.uni_words * pl.batch * wbytes);
-    const size_t part_b = mp.splits > 1 ? align256((size_t)mp.splits * pl.batch * mp.m_out * mp.n_out * sizeof(float)) : 0;
+int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M, const ScratchSource& src)
+{
+    MainParams& mp = pl.mp;
+    int rc = plan_finalize(pl, M);
+    if (rc != APPROX_OK) return rc;
+    const int lds_class = pl.lds_class;
+    const int64_t TM = (int64_t)mp.wr * 64 * kShapes[pl.shape].rows_per_lane, TN = (int64_t)mp.wc * kColsPerWave;
+    const int wbytes = pl.wbytes;
+    const size_t lane_b = pl.lane_b, uni_b = pl.uni_b, part_b = pl.part_b;
     char* base = nullptr;
     int* stats = nullptr;
     bool* stats_ready = nullptr;
-    int rc = scratch_get(src, dev, stream, lane_b + uni_b + part_b, &base, &stats, &stats_ready);
+    rc = scratch_get(src, dev, stream, lane_b + uni_b + part_b, &base, &stats, &stats_ready);
     if (rc != APPROX_OK) return rc;
     void* lane_panel = base;
     void* uni_panel = base + lane_b;
@@ -387,7 +416,6 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     pl.lane.wbytes = wbytes;
     pl.uni.wbytes = wbytes;
     pl.lane.stats = stats;
-    pl.lane.count = pl.lane_count ? pl.lane_count : pl.lane_words;
     pl.lane.dst_batch_stride = pl.lane_words;
     pl.lane.batch = pl.batch;
     pl.lane.lane_role = 1;
@@ -398,7 +426,6 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
     pl.lane.ehi = pl.uni.ehi = mp.ehi = ehi;
     pl.uni.dst = uni_panel;
     pl.uni.stats = stats + 2;
-    pl.uni.count = pl.uni_count ? pl.uni_count : pl.uni_words;
     pl.uni.dst_batch_stride = pl.uni_words;
     pl.uni.batch = pl.batch;
     pl.uni.lane_role = 0;
@@ -582,6 +609,57 @@ int gemv_run(amx::GemvParams& g, int batch, float* C, int dev, hipStream_t strea
     return APPROX_OK;
 }
 
+// The GEMM-kernel plan of a call's shapes (no pointers; leading dimensions
+// default to the packed ones): decode layouts, tiling, k-step counters and
+// the M = 8 copy-choice groups. A function of the arguments only.
+void build_gemm_plan(int transA, int transB, int m, int n, int k, int batch, Plan& pl)
+{
+    pl.batch = batch;
+    const Tiling tg = tiling_of(m, n);
+    pl.shape = tg.shape;
+    MainParams& mp = pl.mp;
+    mp.wr = tg.wr;
+    mp.wc = tg.wc;
+    mp.tiles_m = tg.tiles_m;
+    mp.tiles_n = tg.tiles_n;
+    const int Mp = mp.tiles_m * tg.TM, Np = mp.tiles_n * tg.TN;
+    const int KB = (int)cdiv(k, 4);
+
+    DecodeParams& a = pl.lane;
+    a.layout = amx::L_DENSE_LANE;
+    a.m = m; a.n = n; a.k = k; a.ld = transA ? m : k; a.trans = transA;
+    a.Mp = Mp; a.Np = Np; a.KB = KB;
+    a.rowlen = Mp * 4;
+    a.ldw = amx::panel_ld(Mp * 4);
+    pl.lane_count = (int64_t)KB * Mp * 4;
+    pl.lane_words = (int64_t)KB * a.ldw;
+
+    DecodeParams& u = pl.uni;
+    u.layout = amx::L_DENSE_UNIFORM;
+    u.m = m; u.n = n; u.k = k; u.ld = transB ? k : n; u.trans = transB;
+    u.Mp = Mp; u.Np = Np; u.KB = KB;
+    u.rowlen = Np;
+    u.ldw = amx::panel_ld(Np);
+    pl.uni_count = (int64_t)KB * 4 * Np;
+    pl.uni_words = (int64_t)KB * 4 * u.ldw;
+
+    mp.m_rows = Mp;
+    mp.m_out = m;
+    mp.n_out = n;
+    mp.ldc = n;
+    mp.Np = Np;
+    mp.bld = u.ldw;
+    mp.E2 = 1; mp.E3 = Mp; mp.L1 = 0; mp.L2 = 0; mp.L3 = 4;
+    mp.U1 = KB; mp.U2 = 1; mp.U3 = 1; mp.K1 = a.ldw; mp.K2 = 0; mp.K3 = 0;
+    mp.KB = KB;
+    pl.gather = 0;
+    // a half-wave reads rows i0..i0+31 (i0 a multiple of 32) at one index
+    pl.asg.G1 = KB; pl.asg.S1 = a.ldw;
+    pl.asg.G2 = Mp / 32; pl.asg.S2 = 32 * 4;
+    pl.asg.G3 = 4; pl.asg.S3 = 1;
+    pl.asg.LS = 4; pl.asg.O = 0; pl.asg.E = Mp;
+}
+
 int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int lda, long long strideA,
               const float* B, int ldb, long long strideB, float* C, int ldc, long long strideC, int batch,
               void* stream_v, const float* const* Ap = nullptr, const float* const* Bp = nullptr,
@@ -635,59 +713,19 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
     }
 
     Plan pl;
-    pl.batch = batch;
+    build_gemm_plan(transA, transB, m, n, k, batch, pl);
     pl.C = C;
     pl.strideC = strideC;
-    const Tiling tg = tiling_of(m, n);
-    pl.shape = tg.shape;
-    MainParams& mp = pl.mp;
-    mp.wr = tg.wr;
-    mp.wc = tg.wc;
-    mp.tiles_m = tg.tiles_m;
-    mp.tiles_n = tg.tiles_n;
-    const int Mp = mp.tiles_m * tg.TM, Np = mp.tiles_n * tg.TN;
-    const int KB = (int)cdiv(k, 4);
-
     pl.Cp = Cp;
-    DecodeParams& a = pl.lane;
-    a.src = A;
-    a.src_ptrs = Ap;
-    a.src_batch_stride = strideA;
-    a.layout = amx::L_DENSE_LANE;
-    a.m = m; a.n = n; a.k = k; a.ld = lda; a.trans = transA;
-    a.Mp = Mp; a.Np = Np; a.KB = KB;
-    a.rowlen = Mp * 4;
-    a.ldw = amx::panel_ld(Mp * 4);
-    pl.lane_count = (int64_t)KB * Mp * 4;
-    pl.lane_words = (int64_t)KB * a.ldw;
-
-    DecodeParams& u = pl.uni;
-    u.src = B;
-    u.src_ptrs = Bp;
-    u.src_batch_stride = strideB;
-    u.layout = amx::L_DENSE_UNIFORM;
-    u.m = m; u.n = n; u.k = k; u.ld = ldb; u.trans = transB;
-    u.Mp = Mp; u.Np = Np; u.KB = KB;
-    u.rowlen = Np;
-    u.ldw = amx::panel_ld(Np);
-    pl.uni_count = (int64_t)KB * 4 * Np;
-    pl.uni_words = (int64_t)KB * 4 * u.ldw;
-
-    mp.m_rows = Mp;
-    mp.m_out = m;
-    mp.n_out = n;
-    mp.ldc = ldc;
-    mp.Np = Np;
-    mp.bld = u.ldw;
-    mp.E2 = 1; mp.E3 = Mp; mp.L1 = 0; mp.L2 = 0; mp.L3 = 4;
-    mp.U1 = KB; mp.U2 = 1; mp.U3 = 1; mp.K1 = a.ldw; mp.K2 = 0; mp.K3 = 0;
-    mp.KB = KB;
-    pl.gather = 0;
-    // a half-wave reads rows i0..i0+31 (i0 a multiple of 32) at one index
-    pl.asg.G1 = KB; pl.asg.S1 = a.ldw;
-    pl.asg.G2 = Mp / 32; pl.asg.S2 = 32 * 4;
-    pl.asg.G3 = 4; pl.asg.S3 = 1;
-    pl.asg.LS = 4; pl.asg.O = 0; pl.asg.E = Mp;
+    pl.lane.src = A;
+    pl.lane.src_ptrs = Ap;
+    pl.lane.src_batch_stride = strideA;
+    pl.uni.src = B;
+    pl.uni.src_ptrs = Bp;
+    pl.uni.src_batch_stride = strideB;
+    pl.mp.ldc = ldc;
+    pl.lane.ld = lda;
+    pl.uni.ld = ldb;
     return run_plan(pl, dev, stream, image, M, src);
 }
 
@@ -732,27 +770,18 @@ int conv_ksteps(ConvKind kind, const ConvShape& s)
     return (int)cdiv((int64_t)s.N * s.P * s.Q, 4);
 }
 
-int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t2, float* out, void* stream_v)
+// The GEMM-kernel plan of a Conv2D pass (no pointers): the implicit-GEMM
+// layouts of both operands, tiling, k-step counters and the M = 8
+// copy-choice groups. APPROX_EUNSUPPORTED when the image exceeds the word
+// limit. A function of the shapes only.
+int build_conv_plan(ConvKind kind, const ConvShape& s, Plan& pl)
 {
-    int dev = 0;
-    int rc = current_device(&dev);
-    if (rc != APPROX_OK) return rc;
-    const uint16_t* image = nullptr;
-    int M = 0;
-    rc = table_of(dev, &image, &M);
-    if (rc != APPROX_OK) return rc;
-    hipStream_t stream = static_cast<hipStream_t>(stream_v);
-
-    Plan pl;
     pl.batch = 1;
-    pl.C = out;
     MainParams& mp = pl.mp;
     DecodeParams& a = pl.lane;
     DecodeParams& u = pl.uni;
     fill_geom(a, s);
     fill_geom(u, s);
-    a.src = t1;
-    u.src = t2;
 
     int m, n;
     conv_gemm_extent(kind, s, &m, &n);
@@ -848,10 +877,151 @@ int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t
         pl.asg.G3 = 1; pl.asg.S3 = 0;
         pl.asg.LS = 1; pl.asg.O = 0;
     }
+    return APPROX_OK;
+}
+
+int conv_impl(ConvKind kind, const ConvShape& s, const float* t1, const float* t2, float* out, void* stream_v)
+{
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc != APPROX_OK) return rc;
+    const uint16_t* image = nullptr;
+    int M = 0;
+    rc = table_of(dev, &image, &M);
+    if (rc != APPROX_OK) return rc;
+    hipStream_t stream = static_cast<hipStream_t>(stream_v);
+
+    Plan pl;
+    rc = build_conv_plan(kind, s, pl);
+    if (rc != APPROX_OK) return rc;
+    pl.C = out;
+    pl.lane.src = t1;
+    pl.uni.src = t2;
     return run_plan(pl, dev, stream, image, M, ScratchSource{});
 }
 
+// ---------------------------------------------------------------- plan check
+// Host-side bounds check of a planned call (a test hook, not part of the C
+// ABI's header): the largest offset each kernel of the plan reads or writes,
+// computed with the kernels' own index formulas (row bases, k-step counters,
+// the zero region of gather mode, uniform rows and columns, split partials,
+// copy-choice groups, table lookups), against what the plan allocates.
+enum PlanSlot {
+    PS_DECODE_LANE = 0,   // decode writes, lane panel (words)
+    PS_DECODE_UNI,        // decode writes, uniform panel (words)
+    PS_READ_LANE,         // GEMM-kernel reads, lane panel (words)
+    PS_READ_UNI,          // GEMM-kernel reads, uniform panel (words)
+    PS_PARTIALS,          // split partials written and summed (floats)
+    PS_COPY_GROUPS,       // M = 8 copy choice, lane panel (words)
+    PS_TABLE,             // table lookups (bytes of the table image)
+    PS_SCRATCH,           // the three scratch parts together (bytes)
+    PS_COUNT
+};
+
+void check_plan(const Plan& pl, int M, int64_t* need, int64_t* have)
+{
+    const MainParams& mp = pl.mp;
+    for (int i = 0; i < PS_COUNT; ++i) need[i] = have[i] = 0;
+    const int64_t lane_total = pl.lane_words * pl.batch, uni_total = pl.uni_words * pl.batch;
+    // decode: word o < count of a batch entry goes to row o / rowlen, column
+    // o % rowlen of rows ldw apart (every decode variant writes these places)
+    auto decode_max = [&](const DecodeParams& d, int64_t batch_words) {
+        const int64_t rowlen = d.rowlen > 0 ? d.rowlen : d.count, ldw = d.rowlen > 0 ? d.ldw : d.count;
+        const int64_t o = d.count - 1, row = o / rowlen;
+        return (pl.batch - 1) * batch_words + row * ldw + (o - row * rowlen) + 1;
+    };
+    need[PS_DECODE_LANE] = decode_max(pl.lane, pl.lane_words);
+    have[PS_DECODE_LANE] = lane_total;
+    need[PS_DECODE_UNI] = decode_max(pl.uni, pl.uni_words);
+    have[PS_DECODE_UNI] = uni_total;
+    // GEMM kernel, lane operand: row base of every row the kernel may read
+    // (rows are clamped below m_rows), plus the largest k-step offset
+    int64_t max_base = 0;
+    for (int i = 0; i < mp.m_rows; ++i) {
+        const int i3 = i % mp.E3, r2 = i / mp.E3, i2 = r2 % mp.E2, i1 = r2 / mp.E2;
+        max_base = std::max<int64_t>(max_base, (int64_t)i1 * mp.L1 + (int64_t)i2 * mp.L2 + (int64_t)i3 * mp.L3);
+    }
+    int64_t max_off = 0;
+    const int steps = pl.gather ? mp.nku : mp.KB;
+    for (int u = 0; u < steps; ++u) {
+        const int u3 = u % mp.U3, r = u / mp.U3, u2 = r % mp.U2, u1 = r / mp.U2;
+        max_off = std::max<int64_t>(max_off, (int64_t)u1 * mp.K1 + (int64_t)u2 * mp.K2 + (int64_t)u3 * mp.K3);
+    }
+    if (!pl.gather) max_off += 3;                         // a k-step's 4 contiguous words
+    else if ((int64_t)mp.KB * 4 > mp.nku) max_off = std::max<int64_t>(max_off, mp.zoff);   // the zero region
+    need[PS_READ_LANE] = (pl.batch - 1) * pl.lane_words + max_base + max_off + 1;
+    have[PS_READ_LANE] = lane_total;
+    // uniform operand: rows 0 .. KB*4 - 1, a wave's 16 columns from its col0
+    const int64_t TN = (int64_t)mp.wc * kColsPerWave;
+    need[PS_READ_UNI] = (pl.batch - 1) * pl.uni_words + ((int64_t)mp.KB * 4 - 1) * mp.bld +
+                        ((int64_t)mp.tiles_n * TN - kColsPerWave) + kColsPerWave;
+    have[PS_READ_UNI] = uni_total;
+    // partials: item (b, split, tile) writes ws[(b * splits + split) * m * n + i * n + j]
+    if (mp.splits > 1) {
+        need[PS_PARTIALS] = ((int64_t)pl.batch * mp.splits - 1) * mp.m_out * mp.n_out +
+                            ((int64_t)mp.m_out - 1) * mp.n_out + mp.n_out;
+        have[PS_PARTIALS] = (int64_t)(pl.part_b / sizeof(float));
+    }
+    // M = 8 copy choice: the last word of the last group
+    if (M == 8) {
+        const amx::AssignParams& a = pl.asg;
+        const int count = std::min(32, a.E - (a.G2 - 1) * 32);
+        need[PS_COPY_GROUPS] = (int64_t)(pl.batch - 1) * pl.lane_words + (int64_t)(a.G1 - 1) * a.S1 +
+                               (int64_t)(a.G2 - 1) * a.S2 + (int64_t)(a.G3 - 1) * a.S3 + a.O +
+                               (int64_t)(count - 1) * a.LS + 1;
+        have[PS_COPY_GROUPS] = lane_total;
+    }
+    // table lookups: the last column's offset plus the largest row offset a
+    // lane word can hold (the pad, or at M = 8 a second copy), 2 bytes read
+    if (M >= 1) {
+        const int64_t col = amx::lut_col_bytes(M);
+        const int64_t row_max = M == 8 ? amx::kRep8ColBytes - 2 : (int64_t)2 << M;
+        need[PS_TABLE] = ((int64_t)(1 << M) - 1) * col + row_max + 2;
+        have[PS_TABLE] = amx::lut_image_bytes(M);
+    }
+    need[PS_SCRATCH] = (int64_t)pl.wbytes * (lane_total + uni_total) + 4 * need[PS_PARTIALS];
+    have[PS_SCRATCH] = (int64_t)(pl.lane_b + pl.uni_b + pl.part_b);
+}
+
 }  // namespace
+
+// Test hook (host only, no HIP call): plans a GEMM (kind 0: args transA,
+// transB, m, n, k, batch) or a Conv2D pass (kind 1..3: fwd, dgrad, wgrad;
+// args N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w) for a table of
+// width M (0: the native multiplier) through the GEMM kernel and writes, per
+// PlanSlot, the largest offset + 1 each kernel touches (need) and what the
+// plan allocates (have). Returns the number of slots with need > have, or a
+// negative status for invalid arguments.
+extern "C" int amx_plan_check(int kind, const int* args, int M, long long* need, long long* have)
+{
+    if (args == nullptr || need == nullptr || have == nullptr || M < 0 || M > 11) return APPROX_EINVAL;
+    Plan pl;
+    if (kind == 0) {
+        const int tA = args[0], tB = args[1], m = args[2], n = args[3], k = args[4], batch = args[5];
+        if (m < 1 || n < 1 || k < 1 || batch < 1 || (tA & ~1) || (tB & ~1)) return APPROX_EINVAL;
+        build_gemm_plan(tA, tB, m, n, k, batch, pl);
+    } else if (kind >= 1 && kind <= 3) {
+        ConvShape cs;
+        int rc = conv_check(args[0], args[1], args[2], args[3], args[4], args[5], args[6], args[7], args[8], args[9],
+                            args[10], &cs, &cs, &cs, &cs);
+        if (rc != APPROX_OK) return rc;
+        rc = build_conv_plan(kind == 1 ? CONV_FWD : kind == 2 ? CONV_DGRAD : CONV_WGRAD, cs, pl);
+        if (rc != APPROX_OK) return rc;
+    } else {
+        return APPROX_EINVAL;
+    }
+    int rc = plan_finalize(pl, M);
+    if (rc != APPROX_OK) return rc;
+    int64_t nd[PS_COUNT], hv[PS_COUNT];
+    check_plan(pl, M, nd, hv);
+    int bad = 0;
+    for (int i = 0; i < PS_COUNT; ++i) {
+        need[i] = nd[i];
+        have[i] = hv[i];
+        bad += nd[i] > hv[i];
+    }
+    return bad;
+}
 
 // ====================================================================== C ABI
 

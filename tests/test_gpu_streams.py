@@ -1,7 +1,7 @@
 """GPU: calls queued on several streams at once (each stream has its own
-scratch arena and exponent statistics; the table is shared read-only), and a
+scratch arena and exponent statistics; the table is shared read-only), a
 call larger than the library's panel limit, which must be refused before any
-work is queued."""
+work is queued, and a failed scratch allocation (APPROX_EHIP)."""
 import numpy as np
 import pytest
 
@@ -82,3 +82,30 @@ def test_call_beyond_the_panel_limit_is_refused(am):
     assert rc == am.APPROX_EUNSUPPORTED
     torch.cuda.synchronize()
     assert torch.all(C == 3.0)
+
+
+def test_allocation_failure_returns_ehip_and_writes_nothing(am):
+    """The allocation-failure path (APPROX_EHIP): a scratch allocation the
+    test hook refuses, as a failed hipMalloc would be. The call queues
+    nothing (C keeps its contents); once allowed, the same call succeeds and
+    matches the oracle."""
+    import os
+    M, t = 7, oracle.lut_generate(7, "mitchell")
+    am.approx_lut_load(t, M)
+    A, B = normal(1701, (300, 700)), normal(1702, (700, 200))
+    dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    C = torch.full((300, 200), 5.0, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()                      # a fresh stream: its arena must be allocated
+    os.environ["APPROX_TEST_ALLOC_LIMIT"] = "4096"
+    try:
+        rc = am.lib().approx_gemm(0, 0, 300, 200, 700, dA.data_ptr(), 700, dB.data_ptr(), 200, C.data_ptr(), 200,
+                                  s.cuda_stream)
+    finally:
+        os.environ.pop("APPROX_TEST_ALLOC_LIMIT", None)
+    assert rc == am.APPROX_EHIP
+    torch.cuda.synchronize()
+    assert bool((C == 5.0).all())
+    am.approx_gemm(0, 0, 300, 200, 700, dA, 700, dB, 200, C, 200, stream=s)
+    torch.cuda.synchronize()
+    R, S = oracle.gemm(A, B, t, M)
+    gate(C.cpu().numpy(), R, S, what="after the refused allocation")

@@ -1,0 +1,95 @@
+"""Host-side bounds check of the library's plans (no GPU): for every GEMM
+and Conv2D case the GPU tests draw (tests/test_gpu_random_cases.py), the five
+workloads, and extreme shapes, at table widths 0 (native), 3, 7, 8 and 10,
+the largest offset each kernel of the planned call touches must lie inside
+the buffer the plan allocates: the decoded panels (decode writes, GEMM-kernel
+reads of row bases plus k-step offsets, gather mode's zero region, uniform
+rows and columns), the split partials, the M = 8 copy-choice groups, the
+table image and the scratch total. The offsets come from the library's
+test hook amx_plan_check, which walks them with the kernels' index
+formulas."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from datagen import configs as cfg
+
+SLOTS = ["decode lane", "decode uniform", "read lane", "read uniform", "partials", "copy groups", "table",
+         "scratch"]
+WIDTHS = [0, 3, 7, 8, 10]
+
+
+@pytest.fixture(scope="module")
+def check():
+    import approximate_multiplier_dnn_amd as am
+    f = am.lib().amx_plan_check
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+
+    def run(kind, args, M):
+        a = np.ascontiguousarray(args, dtype=np.int32)
+        need = np.zeros(len(SLOTS), np.int64)
+        have = np.zeros(len(SLOTS), np.int64)
+        rc = f(kind, a.ctypes.data, M, need.ctypes.data, have.ctypes.data)
+        assert rc >= 0, (kind, list(args), M, rc)
+        bad = [(SLOTS[i], int(need[i]), int(have[i])) for i in range(len(SLOTS)) if need[i] > have[i]]
+        assert not bad, (kind, list(args), M, bad)
+        assert need[2] > 0 and need[3] > 0, "the check walked no offsets"
+        return need, have
+    return run
+
+
+def _gemm_cases():
+    from test_gpu_random_cases import GEMM_CASES
+    out = [(c["tA"], c["tB"], c["m"], c["n"], c["k"], c["batch"]) for c in GEMM_CASES]
+    # the workloads' GEMMs (the row-vector route aside, every shape also through the GEMM kernel)
+    out += [(0, 0, 64, 64, 64, 1), (0, 0, 8192, 8192, 8192, 1)]
+    out += [(ta, tb, m, n, k, 1) for (_, ta, tb, m, n, k, _, _) in cfg.mlp_gemms()]
+    out += [(0, 0, 8192, 2304, 768, 1), (0, 1, 512, 512, 64, 192), (0, 0, 512, 64, 512, 192), (0, 0, 8192, 768, 768, 1)]
+    # extremes: one row, one column, k = 1, ragged tiles, tail-split tiles
+    out += [(0, 0, 1, 1, 1, 1), (1, 1, 1, 3000, 1, 3), (0, 1, 2049, 17, 5, 2), (1, 0, 133020, 64, 400, 1),
+            (0, 0, 257, 129, 4097, 4)]
+    return out
+
+
+def _conv_cases():
+    from test_gpu_random_cases import CONV_CASES
+    out = [(c["N"], c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], *c["stride"], *c["pad"]) for c in CONV_CASES]
+    s = cfg.CONV_SHAPE
+    out.append((s["N"], s["H"], s["W"], s["C"], s["K"], s["R"], s["S"], *s["stride"], *s["pad"]))
+    out += [(1, 1, 1, 1, 1, 1, 1, 1, 1, 0, 0), (3, 7, 5, 5, 3, 5, 5, 3, 2, 4, 4), (130, 32, 32, 64, 64, 3, 3, 1, 1, 1, 1),
+            (2, 33, 9, 3, 70, 3, 1, 2, 3, 1, 0)]
+    return out
+
+
+@pytest.mark.parametrize("M", WIDTHS)
+def test_gemm_plans_stay_inside_their_buffers(check, M):
+    for args in _gemm_cases():
+        check(0, args, M)
+
+
+@pytest.mark.parametrize("M", WIDTHS)
+def test_conv_plans_stay_inside_their_buffers(check, M):
+    for args in _conv_cases():
+        for kind in (1, 2, 3):
+            check(kind, args, M)
+
+
+def test_check_sees_the_gather_mode_zero_region(check):
+    """The weight gradient reads a zero region past the image for reduction
+    indices beyond N P Q: the lane reads must reach into it (and stay inside
+    the allocation)."""
+    need, have = check(3, (1, 5, 5, 3, 2, 3, 3, 1, 1, 1, 1), 7)   # N P Q = 25: indices 25..27 padded
+    assert need[2] > 1 * 7 * 7 * 3          # beyond the padded image body
+    assert need[2] <= have[2]
+
+
+def test_check_rejects_invalid_arguments(check):
+    import approximate_multiplier_dnn_amd as am
+    f = am.lib().amx_plan_check
+    need = np.zeros(len(SLOTS), np.int64)
+    have = np.zeros(len(SLOTS), np.int64)
+    bad = np.array([0, 0, 0, 5, 5, 1], np.int32)
+    assert f(0, bad.ctypes.data, 7, need.ctypes.data, have.ctypes.data) == am.APPROX_EINVAL
+    assert f(9, bad.ctypes.data, 7, need.ctypes.data, have.ctypes.data) == am.APPROX_EINVAL
