@@ -45,6 +45,7 @@ constexpr int kRowVectorRowsWide = 64;
 inline bool row_vector_fits(int m, int n, int k)
 {
     const int64_t kn = (int64_t)k * n;
+    if (n >= (1 << 30)) return false;          // the kernel's column offsets are 32-bit byte offsets
     return m <= kRowVectorRows || (m <= kRowVectorRowsWide && (kn >= ((int64_t)1 << 22) || kn <= ((int64_t)1 << 16)));
 }
 
@@ -528,15 +529,20 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
 // item streams a long stretch of B; chunks of at least 8 indices.
 constexpr int64_t kGemvTargetThreads = 256 * 1024;
 
-int64_t g_gemv_slots[kMaxDevices][4];
+int64_t g_gemv_slots[kMaxDevices][5];
 
-int gemv_variant_of(int M) { return M == 0 ? 3 : M <= 7 ? 0 : M == 8 ? 1 : 2; }
+int gemv_variant_of(int M, int m)
+{
+    if (M == 0) return 3;
+    if (m == 1 && M <= 8) return 4;
+    return M <= 7 ? 0 : M == 8 ? 1 : 2;
+}
 
 // The row-vector kernel's reduction split (sets g.chunk and g.splits); returns
 // the work items (column blocks x row blocks x splits x batch).
 int64_t gemv_split(amx::GemvParams& g, int batch)
 {
-    const int variant = gemv_variant_of(g.M);
+    const int variant = gemv_variant_of(g.M, g.m);
     const int cols = amx::gemv_threads(variant) * amx::kGemvColsPerLane;
     const int64_t blocks = cdiv(g.n, cols) * cdiv(g.m, amx::kGemvMaxRows) * batch;
     const int64_t target = kGemvTargetThreads / amx::gemv_threads(variant);
@@ -550,7 +556,7 @@ int64_t gemv_split(amx::GemvParams& g, int batch)
 
 int gemv_run(amx::GemvParams& g, int batch, float* C, int dev, hipStream_t stream, const ScratchSource& src)
 {
-    const int variant = gemv_variant_of(g.M);
+    const int variant = gemv_variant_of(g.M, g.m);
     const int64_t items = gemv_split(g, batch);
     g.batch = batch;
     if (items > INT32_MAX) return APPROX_EUNSUPPORTED;
@@ -984,6 +990,18 @@ void check_plan(const Plan& pl, int M, int64_t* need, int64_t* have)
 }
 
 }  // namespace
+
+// Test hook (host only, no HIP call): the rows of B that one group load of
+// the row-vector kernel reads, for an item ending at index k1 (exclusive) and
+// a group of ng indices starting at kg: writes them to rows[0 .. ng) and
+// returns the descriptor's base row (-1 for invalid arguments).
+extern "C" int amx_gemv_group_rows(int k1, int kg, int ng, int* rows)
+{
+    if (rows == nullptr || k1 < 1 || ng < 1 || kg < 0) return -1;
+    const int base = amx::gemv_group_base(kg, k1);
+    for (int g = 0; g < ng; ++g) rows[g] = base + amx::gemv_group_step(kg, k1, g);
+    return base;
+}
 
 // Test hook (host only, no HIP call): plans a GEMM (kind 0: args transA,
 // transB, m, n, k, batch) or a Conv2D pass (kind 1..3: fwd, dgrad, wgrad;

@@ -253,6 +253,23 @@ constexpr int kGemvMaxRows = 4;
 constexpr int kGemvThreads = 256;            // table in global memory / native
 constexpr int kGemvLdsThreads = 1024;        // table staged in LDS (one copy per workgroup)
 constexpr int kGemvColsPerLane = 4;          // one workgroup's thread count apart
+constexpr int kGemv1Threads = 256;           // one-row kernel (m = 1, M <= 8): table rows staged per window
+constexpr int kGemv1Window = 32;             // reduction indices per staged window (one table row each)
+constexpr int kGemv1Stage = 4;               // 16-byte pieces of a window (M = 8) per thread
+
+// Group loads of the row-vector kernel. A work item sums reduction indices
+// [k0, k1); a load of the group that starts at index kg >= k0 (kg may lie
+// past k1 - 1: a request made ahead of the item's end) addresses B through a
+// buffer descriptor based at row gemv_group_base(kg, k1), and its index g
+// reads row base + gemv_group_step(kg, k1, g). Every row read lies in
+// [k0, k1 - 1] and no offset from the base is negative; for kg + g < k1 the
+// row is kg + g itself.
+__host__ __device__ inline int gemv_group_base(int kg, int k1) { return kg < k1 - 1 ? kg : k1 - 1; }
+__host__ __device__ inline int gemv_group_step(int kg, int k1, int g)
+{
+    const int last = k1 - 1 - gemv_group_base(kg, k1);
+    return g < last ? g : last;
+}
 
 struct GemvParams {
     const float* A;
@@ -270,8 +287,9 @@ struct GemvParams {
 };
 
 // variant: 0 = table of M <= 7 in LDS, 1 = M == 8 in LDS, 2 = table in global
-// memory, 3 = native multiplier. The kernel is persistent over `grid`
-// workgroups of gemv_threads(variant) threads.
+// memory, 3 = native multiplier, 4 = one row of op(A) with M <= 8 (table rows
+// staged per window). The kernel is persistent over `grid` workgroups of
+// gemv_threads(variant) threads.
 int gemv_threads(int variant);
 int gemv_blocks_per_cu(int variant);
 hipError_t launch_gemv(const GemvParams& p, int variant, int grid, hipStream_t s);
@@ -280,6 +298,15 @@ hipError_t launch_decode_pair(const DecodeParams& a, const DecodeParams& b, hipS
 hipError_t launch_assign(const AssignParams& p, hipStream_t s);
 hipError_t launch_main(const MainParams& p, int lds_class, int gather, int shape, int grid, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
+
+// The reduction runs 16 lanes per 4 outputs (reduce_rows_kernel) when the
+// outputs are few (m * n * batch a multiple of 4, below 2^18) and the splits
+// many (at least 16); otherwise a thread per 4 outputs (or one).
+inline bool reduce_by_rows(int m, int n, int batch, int splits)
+{
+    const int64_t total = (int64_t)m * n * batch;
+    return ((int64_t)m * n) % 4 == 0 && total < ((int64_t)1 << 18) && splits >= 16;
+}
 hipError_t launch_reduce_tiles(const ReduceTilesParams& p, hipStream_t s);
 hipError_t launch_fill_zero(float* C, float* const* Cp, int m, int n, int ldc, int batch, int64_t strideC,
                             hipStream_t s);

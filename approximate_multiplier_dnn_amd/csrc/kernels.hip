@@ -31,6 +31,8 @@
 // fast path zeroes those products first; otherwise the checked path
 // evaluates Algorithm 2 per product.
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "internal.h"
 
@@ -47,6 +49,11 @@ typedef const float __attribute__((address_space(1)))* gfloat_cptr;
 typedef float __attribute__((address_space(1)))* gfloat_ptr;
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef v4f __attribute__((address_space(1)))* gv4f_ptr;
+
+// Dword 3 of a raw buffer descriptor on this GPU family: data format field
+// (bits 18:15) = 4, 32-bit elements; every other field zero (no swizzle, no
+// index stride). Raw loads then address base + scalar offset + lane offset.
+constexpr int kBufferConfig = 0x00020000;
 
 // ------------------------------------------------------------------ decode
 
@@ -1347,47 +1354,194 @@ __device__ __forceinline__ uint32_t se_of(uint32_t bits)
 // block * NTG * kGemvColsPerLane + t + c * NTG (coalesced across the wave for
 // every c) and sums reduction indices [split * chunk, (split + 1) * chunk) in
 // ascending order. Columns past n read column n - 1 and are not stored, so
-// the loop has no divergent branch. TABB > 0 (PADROWS): the table is staged
-// once per persistent workgroup in LDS as 2^M rows (one per op(A) mantissa
-// index) of 2^M entries plus a pad, where a zero, subnormal or Inf B element
-// reads the row's entry 0 and a NaN its entry 1, so the product assembly
-// below needs no special case. TABB = 0 (M = 9..11): the table is read from
-// global memory in index order, entry 4^M being a zero (the target of zero,
-// Inf and NaN operands, as the pad entry of the GEMM image).
+// the loop has no divergent branch. op(A) is the same for the whole wave at
+// each index, so it is read with scalar loads and its sign, exponent and
+// table row are worked out in scalar registers; a row of B is addressed as a
+// wave-uniform base plus the lane's 32-bit column offset. PADROWS: the table
+// is staged once per persistent workgroup in LDS as 2^M rows (one per op(A)
+// mantissa index) of 2^M entries plus a pad (the pad entries are read by the
+// checked path only). Otherwise (M = 9..11, and the checked path of the
+// one-row kernel below) the table is read from global memory in index order.
 //
-// Fast path (as in the GEMM kernel): fma(as_float((e << 8) + seB),
-// as_float(seA), acc), exact while every product stays inside the range
-// (FP32), or no product exceeds it (a narrower format, whose products below
-// it are zeroed first, as in the GEMM kernel's path with underflow). Per item
-// the wave takes the exponent range of its op(A) chunk and checks each B
-// element against the window that keeps the products inside; if any lane of
-// the wave finds an element outside it, the wave redoes its columns of the
-// item with the checked path (Algorithm 2 as selects), which gives the same
-// bits wherever both apply.
-// Reduction indices whose operands are requested together in the row-vector kernel.
+// Fast path: with e the pair's table entry and seB the sign|exponent bits of
+// B, y = as_float(0x3F800000 + (e << 8)) * as_float(seB) is
+// +-(1.f) * 2^(EB-127+carry), the AMSim product of B with an op(A) operand of
+// exponent 0, and fma(y, as_float(seA), acc) adds the product with one
+// rounding: exact while every product stays inside the range (FP32), or no
+// product exceeds it (a narrower format, whose products below it are zeroed
+// first, as in the GEMM kernel's path with underflow). A zero or subnormal B
+// has seB = +-0, so y is +-0 whatever entry is read. Per item the wave takes
+// the exponent range of its op(A) chunk, which fixes the window [lo, hi] of
+// B exponents that keeps every product inside; each lane keeps the largest
+// |as_float(seB)|, which is below 2^(hi + 1 - 127) exactly when no exponent
+// exceeds hi and no B is Inf or NaN (their seB is +-Inf), and the smallest
+// (B bits << 1) - 2^24, which is at least (lo - 1) << 24 exactly when no
+// normal exponent is below lo (zero and subnormal B wrap past every normal
+// value). If any lane of the
+// wave finds an element outside the window, the wave redoes its columns of
+// the item with the checked path (Algorithm 2 as selects), which gives the
+// same bits wherever both apply.
+// Reduction indices whose operands are requested together in the row-vector kernels.
 constexpr int GG = 8;
 
+typedef const float __attribute__((address_space(4)))* cfloat_cptr;
+typedef const uint32_t __attribute__((address_space(1)))* gu32_cptr;
+typedef const uint16_t __attribute__((address_space(1)))* gu16_cptr;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef const u32x4 __attribute__((address_space(1)))* gu4_cptr;
+
+// Operand loads of the row-vector kernels for one work item over reduction
+// indices [k0, k1). op(A) is read through the constant address space: it is
+// not written while a kernel runs, and a wave-uniform index then gives a
+// scalar load. A group of rows of B is read through a buffer descriptor
+// (gemv_group_base: its rows and offsets): the lane's column offset plus a
+// wave-uniform row offset, no 64-bit address arithmetic per load; the
+// descriptor's extent ends with the group's last row. Rows of 2^26 floats or
+// more (a group's row offsets would pass 2^32 bytes): one descriptor per row.
+template <int MR, int NTG>
+struct GemvOperands {
+    const GemvParams& p;
+    gfloat_cptr B;
+    cfloat_cptr As;
+    int k1;
+    uint32_t ldb4;
+    bool wide;
+    uint32_t boff[kGemvColsPerLane];        // the lane's columns as byte offsets within a row of B (n < 2^30)
+
+    __device__ __forceinline__ GemvOperands(const GemvParams& p_, gfloat_cptr A, gfloat_cptr B_, int j0, int k1_)
+        : p(p_), B(B_), As((cfloat_cptr)(uintptr_t)A), k1(k1_), ldb4((uint32_t)p_.ldb * 4u), wide(p_.ldb >= (1 << 26))
+    {
+#pragma unroll
+        for (int c = 0; c < kGemvColsPerLane; ++c) boff[c] = (uint32_t)min(j0 + c * NTG, p.n - 1) * 4u;
+    }
+
+    __device__ __forceinline__ uint32_t a_raw(int r, int kk) const
+    {
+        return __float_as_uint(p.transA ? As[(int64_t)kk * p.lda + r] : As[(int64_t)r * p.lda + kk]);
+    }
+
+    template <int NG>
+    __device__ __forceinline__ void load(int kg, uint32_t (&bw)[NG][kGemvColsPerLane], uint32_t (&xa)[NG][MR]) const
+    {
+        const int base = gemv_group_base(kg, k1);
+        if (!wide) {
+            const uint32_t extent = (uint32_t)gemv_group_step(kg, k1, NG - 1) * ldb4 + (uint32_t)p.n * 4u;
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(uintptr_t)((gbyte_ptr)B + (int64_t)base * p.ldb * 4), 0, (int)extent, kBufferConfig);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const uint32_t so = (uint32_t)gemv_group_step(kg, k1, g) * ldb4;
+#pragma unroll
+                for (int c = 0; c < kGemvColsPerLane; ++c)
+                    bw[g][c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)boff[c], (int)so, 0);
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int64_t row = base + gemv_group_step(kg, k1, g);
+                const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(uintptr_t)((gbyte_ptr)B + row * p.ldb * 4), 0, (int)((uint32_t)p.n * 4u), kBufferConfig);
+#pragma unroll
+                for (int c = 0; c < kGemvColsPerLane; ++c)
+                    bw[g][c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)boff[c], 0, 0);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int r = 0; r < MR; ++r) xa[g][r] = a_raw(r, base + gemv_group_step(kg, k1, g));
+    }
+};
+
+// Exponent range of the normal op(A) elements of rows [0, MR) over indices
+// [k0, k1) (whole wave), and whether any is NaN; the window [lo, hi] of B
+// exponents that keeps every product of them inside the format's range
+// (lo > hi: none does).
+//   B exponents eb (normal) that keep every product at or below the format's
+// top ehi (and eb + carry below 255, so y stays finite). FP32 (FMT false):
+// also at or above its bottom, else the checked path. A narrower format
+// (FMT): products below the bottom elo are zeroed in the loop instead: y below
+// 2^(elo - EA) (EA: op(A)'s biased exponent) means an underflow, the bound
+// being 0 for Inf / NaN op(A) and 2^elo for a zero op(A).
+template <int MR, bool FMT, typename Ops>
+__device__ __forceinline__ void gemv_window(const GemvParams& p, const Ops& ops, int k0, int k1, int& lo, int& hi,
+                                            bool& a_nan_any)
+{
+    const int lane = threadIdx.x & 63;
+    int emin = 255, emax = 0;
+    bool a_nan = false;
+#pragma unroll
+    for (int r = 0; r < MR; ++r)
+        for (int kk = k0 + lane; kk < k1; kk += 64) {
+            uint32_t bits = ops.a_raw(r, kk);
+            if constexpr (FMT) bits = cast_fmt(bits, p.elo, p.ehi);
+            const int e = (int)((bits >> 23) & 0xFFu);
+            const bool normal = e != 0 && e != 255;
+            emin = normal ? min(emin, e) : emin;
+            emax = normal ? max(emax, e) : emax;
+            a_nan |= (bits & 0x7FFFFFFFu) > 0x7F800000u;
+        }
+    for (int off = 32; off > 0; off >>= 1) {
+        emin = min(emin, __shfl_xor(emin, off, 64));
+        emax = max(emax, __shfl_xor(emax, off, 64));
+    }
+    lo = (FMT || emin > emax) ? 1 : max(1, p.elo + 127 - emin);
+    hi = emin > emax ? 253 : min(253, p.ehi + 126 - emax);
+    a_nan_any = __any(a_nan);
+}
+
+// One B element of the fast path: the table column index, the sign|exponent
+// of B as a float (+-2^(EB-127), +-0 for zero and subnormal, +-Inf for Inf
+// and NaN), and the lane's window accumulators: the largest |sign|exponent|
+// and the smallest (B bits << 1) - 2^24.
+__device__ __forceinline__ void gemv_fast_b(uint32_t bits, int sh, int M, float& smax, uint32_t& wmin, uint32_t& ix,
+                                            float& sb)
+{
+    ix = __builtin_amdgcn_ubfe(bits, (uint32_t)sh, (uint32_t)M);
+    sb = __uint_as_float(bits & 0xFF800000u);
+    smax = __builtin_fmaxf(smax, __builtin_fabsf(sb));
+    wmin = min(wmin, (bits << 1) - (1u << 24));
+}
+
+// One fast-path product added to acc: e the table entry, sb B's sign|exponent,
+// seA op(A)'s sign|exponent bits (+-0 for a zero or subnormal op(A): the sign
+// of a zero product never shows, as every sum starts from +0; +-Inf for Inf).
+template <bool FMT>
+__device__ __forceinline__ void gemv_fast_fma(float& acc, uint32_t e, float sb, uint32_t seA, int elo)
+{
+    const float y = __uint_as_float(0x3F800000u + (e << 8)) * sb;
+    float yk = y;
+    if constexpr (FMT) {
+        const float tA = __int_as_float(max((int)((uint32_t)(elo + 127) << 23) - (int)(seA & 0x7F800000u), 0));
+        yk = __builtin_fabsf(y) < tA ? 0.0f : y;
+    }
+    acc = __builtin_fmaf(yk, __uint_as_float(seA), acc);
+}
+
+// force: skip the fast path (the caller's fast path has failed its window).
 template <int MR, bool NATIVE, int NTG, bool FMT, bool PADROWS>
 __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* lut, gfloat_cptr A, gfloat_cptr B,
-                                          int j0, int k0, int k1, float (&acc)[kGemvMaxRows][kGemvColsPerLane])
+                                          int j0, int k0, int k1, float (&acc)[kGemvMaxRows][kGemvColsPerLane],
+                                          bool force = false)
 {
     const int sh = 23 - p.M;
     const uint32_t mmask = (1u << p.M) - 1u;
-    const uint32_t zero_ix = 1u << (2 * p.M);
-    const uint32_t pad = 1u << p.M;                 // PADROWS: the row's zero entry (pad + 1: its NaN entry)
-    const uint32_t rs = pad + 8u;                   // PADROWS: entries per row
-    const int lane = threadIdx.x & 63;
-    int jc[kGemvColsPerLane];
-#pragma unroll
-    for (int c = 0; c < kGemvColsPerLane; ++c) jc[c] = min(j0 + c * NTG, p.n - 1);
+    const uint32_t rs = (1u << p.M) + 8u;           // PADROWS: entries per row of the LDS image
+    const GemvOperands<MR, NTG> ops(p, A, B, j0, k1);
     // operands are cast to the multiplier's format where they are used (the
     // native multiplier takes them as they are); a group's loads stay
     // together ahead of the casts
     auto cast = [&](uint32_t bits) -> uint32_t { return FMT ? cast_fmt(bits, p.elo, p.ehi) : bits; };
-    auto a_raw = [&](int r, int kk) -> uint32_t {
-        return __float_as_uint(p.transA ? A[(int64_t)kk * p.lda + r] : A[(int64_t)r * p.lda + kk]);
+    // the item's indices in groups of GG, handed to use(count, B words, op(A)
+    // words) in ascending order (a group past k1 - 1 reads row k1 - 1, unused)
+    auto stream = [&](auto&& use) {
+        for (int kg = k0; kg < k1; kg += GG) {
+            uint32_t bw[GG][kGemvColsPerLane], xa[GG][MR];
+            ops.load(kg, bw, xa);
+            __builtin_amdgcn_sched_barrier(0);     // keep the group's loads issued together
+            use(min(GG, k1 - kg), bw, xa);
+        }
     };
-    auto a_at = [&](int r, int kk) -> uint32_t { return cast(a_raw(r, kk)); };
 #pragma unroll
     for (int r = 0; r < kGemvMaxRows; ++r)
 #pragma unroll
@@ -1395,99 +1549,50 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
 
     bool checked = !NATIVE;
     if constexpr (!NATIVE) {
-        // exponent range of the normal op(A) elements of this item (whole wave)
-        int emin = 255, emax = 0;
-#pragma unroll
-        for (int r = 0; r < MR; ++r)
-            for (int kk = k0 + lane; kk < k1; kk += 64) {
-                const int e = (int)((a_at(r, kk) >> 23) & 0xFFu);
-                const bool normal = e != 0 && e != 255;
-                emin = normal ? min(emin, e) : emin;
-                emax = normal ? max(emax, e) : emax;
-            }
-        for (int off = 32; off > 0; off >>= 1) {
-            emin = min(emin, __shfl_xor(emin, off, 64));
-            emax = max(emax, __shfl_xor(emax, off, 64));
-        }
-        // B exponents eb (normal) that keep every product at or below the
-        // format's top ehi (and eb + carry below 255, for the fast assembly).
-        // FP32 (FMT false): also at or above its bottom, else the checked
-        // path. A narrower format (FMT): products below the bottom elo are
-        // zeroed in the loop instead: x below 2^(elo - EA) (EA: op(A)'s biased
-        // exponent) means an underflow, the bound being 0 for Inf / NaN op(A)
-        // and 2^elo for a zero op(A).
-        const int lo = (FMT || emin > emax) ? 1 : max(1, p.elo + 127 - emin);
-        const int hi = emin > emax ? 253 : min(253, p.ehi + 126 - emax);
-        checked = lo > hi || p.force_checked;
+        int lo, hi;
+        bool a_nan;
+        gemv_window<MR, FMT>(p, ops, k0, k1, lo, hi, a_nan);
+        // a NaN op(A) element sends the item to the checked path (the fast
+        // product takes op(A)'s sign|exponent bits as they are)
+        checked = force || lo > hi || p.force_checked || a_nan;
         if (!checked) {
-            bool bad = false;
-            for (int kg = k0; kg < k1; kg += GG) {
-                // the group's operands first: GG rows of B and op(A) in flight at once
-                uint32_t bw[GG][kGemvColsPerLane], xa[GG][MR];
+            const float hi_s = __uint_as_float((uint32_t)(hi + 1) << 23);
+            const uint32_t lo_w = (uint32_t)(lo - 1) << 24;
+            float smax = 0.0f;
+            uint32_t wmin = 0xFFFFFFFFu;
+            stream([&](int cnt, const uint32_t (&bw)[GG][kGemvColsPerLane], const uint32_t (&xa)[GG][MR]) {
 #pragma unroll
                 for (int g = 0; g < GG; ++g) {
-                    const int kk = min(kg + g, k1 - 1);
-                    const gfloat_cptr brow = B + (int64_t)kk * p.ldb;
+                    if (g >= cnt) break;
+                    uint32_t ix[kGemvColsPerLane];
+                    float sb[kGemvColsPerLane];
 #pragma unroll
-                    for (int c = 0; c < kGemvColsPerLane; ++c) bw[g][c] = __float_as_uint(brow[jc[c]]);
-#pragma unroll
-                    for (int r = 0; r < MR; ++r) xa[g][r] = a_raw(r, kk);
-                }
-                __builtin_amdgcn_sched_barrier(0);     // keep the group's loads issued together
-#pragma unroll
-                for (int g = 0; g < GG; ++g) {
-                    if (kg + g >= k1) break;
-                    uint32_t ix[kGemvColsPerLane], seB[kGemvColsPerLane];
-#pragma unroll
-                    for (int c = 0; c < kGemvColsPerLane; ++c) {
-                        const uint32_t bits = cast(bw[g][c]);
-                        const uint32_t eb = (bits >> 23) & 0xFFu;
-                        if constexpr (PADROWS) {
-                            // zero, subnormal and Inf read the row's zero entry, NaN its entry 1:
-                            // (e << 8) + (sign | exponent) is then +-0, +-Inf or a NaN. The
-                            // classes come from v_cmp_class (mask 0x108: +-normal; 0x3: NaN)
-                            const float bf = __uint_as_float(bits);
-                            const bool normal = __builtin_amdgcn_classf(bf, 0x108);
-                            bad |= normal && (eb - (uint32_t)lo > (uint32_t)(hi - lo));
-                            const uint32_t pix = pad + (__builtin_amdgcn_classf(bf, 0x3) ? 1u : 0u);
-                            ix[c] = normal ? __builtin_amdgcn_ubfe(bits, (uint32_t)sh, (uint32_t)p.M) : pix;
-                            seB[c] = bits & 0xFF800000u;
-                        } else {
-                            const bool special = eb - 1u > 253u;      // zero, subnormal, Inf, NaN
-                            bad |= !special && (eb - (uint32_t)lo > (uint32_t)(hi - lo));
-                            ix[c] = special ? zero_ix : ((bits >> sh) & mmask);
-                            seB[c] = se_of(bits);
-                        }
-                    }
-                    // the group's lookups are issued together, then used
+                    for (int c = 0; c < kGemvColsPerLane; ++c) gemv_fast_b(cast(bw[g][c]), sh, p.M, smax, wmin, ix[c], sb[c]);
+                    // the index's lookups are issued together, then used
                     uint32_t e[MR][kGemvColsPerLane];
 #pragma unroll
                     for (int r = 0; r < MR; ++r) {
                         const uint32_t ia = (cast(xa[g][r]) >> sh) & mmask;
-                        const uint32_t row = PADROWS ? ia * rs : ia << p.M;
+                        if constexpr (PADROWS) {
+                            const uint16_t* row = lut + ia * rs;
 #pragma unroll
-                        for (int c = 0; c < kGemvColsPerLane; ++c)
-                            e[r][c] = PADROWS ? lut[row + ix[c]] : lut[ix[c] == zero_ix ? zero_ix : (row | ix[c])];
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
+                            for (int c = 0; c < kGemvColsPerLane; ++c) e[r][c] = row[ix[c]];
+                        } else {
+                            const gbyte_ptr row = (gbyte_ptr)lut + (ia << (p.M + 1));
 #pragma unroll
-                    for (int r = 0; r < MR; ++r) {
-                        uint32_t seA = se_of(cast(xa[g][r]));
-                        // opaque to the optimiser: a NaN op(A) then goes through the FMA
-                        // like any value, instead of a select per product
-                        if constexpr (PADROWS) asm volatile("" : "+v"(seA));
-                        const float tA = __int_as_float(
-                            max((int)((uint32_t)(p.elo + 127) << 23) - (int)(seA & 0x7F800000u), 0));
-#pragma unroll
-                        for (int c = 0; c < kGemvColsPerLane; ++c) {
-                            const float xv = __uint_as_float((e[r][c] << 8) + seB[c]);
-                            const float xk = (FMT && __builtin_fabsf(xv) < tA) ? 0.0f : xv;
-                            acc[r][c] = __builtin_fmaf(xk, __uint_as_float(seA), acc[r][c]);
+                            for (int c = 0; c < kGemvColsPerLane; ++c)
+                                e[r][c] = *reinterpret_cast<gu16_cptr>(row + (ix[c] << 1));
                         }
                     }
+#pragma unroll
+                    for (int r = 0; r < MR; ++r) {
+                        const uint32_t seA = cast(xa[g][r]) & 0xFF800000u;
+#pragma unroll
+                        for (int c = 0; c < kGemvColsPerLane; ++c) gemv_fast_fma<FMT>(acc[r][c], e[r][c], sb[c], seA, p.elo);
+                    }
                 }
-            }
-            checked = __any(bad);
+            });
+            checked = __any(!(smax < hi_s) || wmin < lo_w);
             if (checked) {
 #pragma unroll
                 for (int r = 0; r < kGemvMaxRows; ++r)
@@ -1497,21 +1602,10 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
         }
     }
     if (!checked && !NATIVE) return;
-    for (int kg = k0; kg < k1; kg += GG) {
-        uint32_t bw[GG][kGemvColsPerLane], xa[GG][MR];
+    stream([&](int cnt, const uint32_t (&bw)[GG][kGemvColsPerLane], const uint32_t (&xa)[GG][MR]) {
 #pragma unroll
         for (int g = 0; g < GG; ++g) {
-            const int kk = min(kg + g, k1 - 1);
-            const gfloat_cptr brow = B + (int64_t)kk * p.ldb;
-#pragma unroll
-            for (int c = 0; c < kGemvColsPerLane; ++c) bw[g][c] = __float_as_uint(brow[jc[c]]);
-#pragma unroll
-            for (int r = 0; r < MR; ++r) xa[g][r] = a_raw(r, kk);
-        }
-        __builtin_amdgcn_sched_barrier(0);             // keep the group's loads issued together
-#pragma unroll
-        for (int g = 0; g < GG; ++g) {
-            if (kg + g >= k1) break;
+            if (g >= cnt) break;
 #pragma unroll
             for (int r = 0; r < MR; ++r) {
                 if constexpr (NATIVE) {
@@ -1532,6 +1626,40 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, const uint16_t* l
                 }
             }
         }
+    });
+}
+
+// Item order of the row-vector kernels: row blocks fastest, so the items of
+// one (column block, chunk) read the same stretch of B. Workgroup b runs on
+// XCD b % 8, so the workgroups of one XCD take consecutive items (as in the
+// GEMM kernel): those row blocks then share B through that XCD's L2.
+__device__ __forceinline__ int gemv_first_item()
+{
+    const int G = gridDim.x;
+    return (G & 7) == 0 ? (int)((blockIdx.x & 7u) * (unsigned)(G >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
+}
+
+// The item's outputs: rows r0 .. r0 + mr - 1 of C, or of the item's split
+// partials.
+template <int NTG>
+__device__ __forceinline__ void gemv_store(const GemvParams& p, int b, int split, int r0, int mr, int j0,
+                                           const float (&acc)[kGemvMaxRows][kGemvColsPerLane])
+{
+    gfloat_ptr out;
+    int64_t ld;
+    if (p.splits > 1) {
+        out = (gfloat_ptr)(p.out + ((int64_t)b * p.splits + split) * (int64_t)p.m * p.n);
+        ld = p.n;
+    } else {
+        out = (gfloat_ptr)(p.out_ptrs ? p.out_ptrs[b] : p.out + b * p.out_batch);
+        ld = p.ldc;
+    }
+#pragma unroll
+    for (int r = 0; r < kGemvMaxRows; ++r) {
+        if (r >= mr) break;
+#pragma unroll
+        for (int c = 0; c < kGemvColsPerLane; ++c)
+            if (j0 + c * NTG < p.n) out[(int64_t)(r0 + r) * ld + j0 + c * NTG] = acc[r][c];
     }
 }
 
@@ -1567,13 +1695,7 @@ __global__ __launch_bounds__(NTG) void gemv_kernel(GemvParams p)
     const int nblk = (p.n + COLS - 1) / COLS;
     const int rblk = (p.m + kGemvMaxRows - 1) / kGemvMaxRows;    // blocks of up to 4 rows of op(A)
     const int items = nblk * rblk * p.splits * p.batch;
-    // Row blocks fastest: the items of one (column block, chunk) read the same
-    // stretch of B. Workgroup b runs on XCD b % 8, so the workgroups of one
-    // XCD take consecutive items (as in the GEMM kernel): those row blocks
-    // then share B through that XCD's L2.
-    const int G = gridDim.x;
-    const int v = (G & 7) == 0 ? (int)((blockIdx.x & 7u) * (unsigned)(G >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
-    for (int item = v; item < items; item += G) {
+    for (int item = gemv_first_item(); item < items; item += gridDim.x) {
         const int rb = item % rblk;
         int rest = item / rblk;
         const int blk = rest % nblk;
@@ -1602,23 +1724,163 @@ __global__ __launch_bounds__(NTG) void gemv_kernel(GemvParams p)
             default: gemv_item<4, NATIVE, NTG, false, PR>(p, lut, A, B, j0, k0, k1, acc); break;
             }
         }
+        gemv_store<NTG>(p, b, split, r0, mr, j0, acc);
+    }
+}
 
-        gfloat_ptr out;
-        int64_t ld;
-        if (p.splits > 1) {
-            out = (gfloat_ptr)(p.out + ((int64_t)b * p.splits + split) * (int64_t)p.m * p.n);
-            ld = p.n;
-        } else {
-            out = (gfloat_ptr)(p.out_ptrs ? p.out_ptrs[b] : p.out + b * p.out_batch);
-            ld = p.ldc;
-        }
+// One row of op(A) (m = 1) and a table of M <= 8: the lookups of index kk all
+// read table row ia(kk), so instead of a whole-table copy per 1024-thread
+// workgroup, a 256-thread workgroup stages, per window of kG1Window indices,
+// just the window's rows (one per index, in index order) into LDS, double-
+// buffered: the next window's rows are requested while the lookups of the
+// current window read the other buffer, and stored after them. 32 KB of LDS
+// per workgroup leaves room for several workgroups per CU. Same work items,
+// window test and fast product as gemv_item; a wave that fails its window
+// redoes its columns with gemv_item's checked path (table in global memory).
+template <bool FMT>
+__device__ __forceinline__ void gemv1_item(const GemvParams& p, unsigned char* rows, gfloat_cptr A, gfloat_cptr B,
+                                           int j0, int k0, int k1, float (&acc)[kGemvMaxRows][kGemvColsPerLane])
+{
+    constexpr int NTG = kGemv1Threads, W = kGemv1Window;
+    constexpr int G1 = 4;                               // indices per group load (8: 119 VGPRs, 3% slower)
+    const int M = p.M, sh = 23 - M;
+    const uint32_t mmask = (1u << M) - 1u;
+    const GemvOperands<1, NTG> ops(p, A, B, j0, k1);
+    auto cast = [&](uint32_t bits) -> uint32_t { return FMT ? cast_fmt(bits, p.elo, p.ehi) : bits; };
 #pragma unroll
-        for (int r = 0; r < kGemvMaxRows; ++r) {
-            if (r >= mr) break;
+    for (int r = 0; r < kGemvMaxRows; ++r)
 #pragma unroll
-            for (int c = 0; c < kGemvColsPerLane; ++c)
-                if (j0 + c * NTG < p.n) out[(int64_t)(r0 + r) * ld + j0 + c * NTG] = acc[r][c];
+        for (int c = 0; c < kGemvColsPerLane; ++c) acc[r][c] = 0.0f;
+
+    int lo, hi;
+    bool a_nan;
+    gemv_window<1, FMT>(p, ops, k0, k1, lo, hi, a_nan);
+    // the same for every wave of the workgroup (one op(A) chunk), so all of
+    // them run the windows and their barriers, or none
+    bool checked = lo > hi || p.force_checked || a_nan;
+    if (!checked) {
+        // staging: a window's rows in pieces of 16 bytes (M >= 3) or 4 bytes
+        // (M = 1, 2: rows of 4 and 8 bytes); at most W * 512 / 16 = 1024
+        // pieces, kGemv1Stage per thread (a window past k1 - 1 loads rows it
+        // does not store)
+        const int rlog = M + 1;                             // log2 of the bytes per row
+        const int ulog = M >= 3 ? 4 : 2;
+        const int plog = rlog - ulog;                       // log2 of the pieces per row
+        const int pieces = W << plog;
+        const int tid = threadIdx.x;
+        // piece q of a window: row t = q >> plog of the window (the table row
+        // of op(A) at the window's index t, clamped to k1 - 1), stored at byte
+        // q << ulog of the window's buffer. a_for reads that op(A) element
+        // (one window ahead of fetch, so fetch waits on nothing recent); fetch
+        // reads the piece from the table in global memory.
+        auto a_for = [&](int q, int w0) -> uint32_t {
+            return ops.a_raw(0, w0 >= k1 - 1 ? k1 - 1 : w0 + min(q >> plog, k1 - 1 - w0));
+        };
+        auto fetch = [&](int q, uint32_t abits) -> u32x4 {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (q < pieces) {
+                const uint32_t ia = (cast(abits) >> sh) & mmask;
+                const gbyte_ptr src =
+                    (gbyte_ptr)p.lut + ((size_t)ia << rlog) + ((size_t)(q & ((1 << plog) - 1)) << ulog);
+                if (ulog == 4) v = *reinterpret_cast<gu4_cptr>(src);
+                else v.x = *reinterpret_cast<gu32_cptr>(src);
+            }
+            return v;
+        };
+        auto put = [&](int buf, int q, u32x4 v) {
+            if (q < pieces) {
+                unsigned char* d = rows + ((size_t)buf << (rlog + 5)) + ((size_t)q << ulog);   // 32 rows a buffer
+                if (ulog == 4) *reinterpret_cast<u32x4*>(d) = v;
+                else *reinterpret_cast<uint32_t*>(d) = v.x;
+            }
+        };
+        static_assert(kGemv1Stage == 4 && kGemv1Window == 32, "four pieces per thread, 32 rows per buffer");
+        const float hi_s = __uint_as_float((uint32_t)(hi + 1) << 23);
+        const uint32_t lo_w = (uint32_t)(lo - 1) << 24;
+        float smax = 0.0f;
+        uint32_t wmin = 0xFFFFFFFFu;
+        const int q0 = tid, q1 = tid + NTG, q2 = tid + 2 * NTG, q3 = tid + 3 * NTG;
+        uint32_t a0 = a_for(q0, k0), a1 = a_for(q1, k0), a2 = a_for(q2, k0), a3 = a_for(q3, k0);
+        put(0, q0, fetch(q0, a0));
+        put(0, q1, fetch(q1, a1));
+        put(0, q2, fetch(q2, a2));
+        put(0, q3, fetch(q3, a3));
+        {
+            const int wn = min(k0 + W, k1);                 // op(A) of the second window
+            a0 = a_for(q0, wn), a1 = a_for(q1, wn), a2 = a_for(q2, wn), a3 = a_for(q3, wn);
         }
+        __syncthreads();
+        int buf = 0;
+        for (int w0 = k0; w0 < k1; w0 += W) {
+            const int w1 = min(w0 + W, k1);
+            const bool more = w1 < k1;
+            // the next window's rows, requested now and stored after this
+            // window's lookups; then op(A) of the window after it
+            const u32x4 s0 = fetch(q0, a0), s1 = fetch(q1, a1), s2 = fetch(q2, a2), s3 = fetch(q3, a3);
+            {
+                const int wn = min(w1 + W, k1);
+                a0 = a_for(q0, wn), a1 = a_for(q1, wn), a2 = a_for(q2, wn), a3 = a_for(q3, wn);
+            }
+            const uint16_t* wrows = reinterpret_cast<const uint16_t*>(rows + ((size_t)buf << (rlog + 5)));
+            for (int kg = w0; kg < w1; kg += G1) {
+                uint32_t bw[G1][kGemvColsPerLane], xa[G1][1];
+                ops.load(kg, bw, xa);
+                __builtin_amdgcn_sched_barrier(0);         // keep the group's loads issued together
+                const int cnt = min(G1, w1 - kg);
+#pragma unroll
+                for (int g = 0; g < G1; ++g) {
+                    if (g >= cnt) break;
+                    uint32_t ix[kGemvColsPerLane];
+                    float sb[kGemvColsPerLane];
+#pragma unroll
+                    for (int c = 0; c < kGemvColsPerLane; ++c) gemv_fast_b(cast(bw[g][c]), sh, M, smax, wmin, ix[c], sb[c]);
+                    const uint16_t* row = wrows + ((kg - w0 + g) << M);     // the index's staged row
+                    uint32_t e[kGemvColsPerLane];
+#pragma unroll
+                    for (int c = 0; c < kGemvColsPerLane; ++c) e[c] = row[ix[c]];
+                    const uint32_t seA = cast(xa[g][0]) & 0xFF800000u;
+#pragma unroll
+                    for (int c = 0; c < kGemvColsPerLane; ++c) gemv_fast_fma<FMT>(acc[0][c], e[c], sb[c], seA, p.elo);
+                }
+            }
+            if (more) {
+                put(buf ^ 1, q0, s0);
+                put(buf ^ 1, q1, s1);
+                put(buf ^ 1, q2, s2);
+                put(buf ^ 1, q3, s3);
+            }
+            __syncthreads();
+            buf ^= 1;
+        }
+        checked = __any(!(smax < hi_s) || wmin < lo_w);
+        if (checked) {
+#pragma unroll
+            for (int c = 0; c < kGemvColsPerLane; ++c) acc[0][c] = 0.0f;
+        }
+    }
+    if (checked) gemv_item<1, false, NTG, FMT, false>(p, p.lut, A, B, j0, k0, k1, acc, true);
+}
+
+__global__ __launch_bounds__(kGemv1Threads) void gemv1_kernel(GemvParams p)
+{
+    constexpr int NTG = kGemv1Threads;
+    __shared__ __align__(16) unsigned char rows[2 * kGemv1Window * 512];
+    constexpr int COLS = NTG * kGemvColsPerLane;
+    const int nblk = (p.n + COLS - 1) / COLS;
+    const int items = nblk * p.splits * p.batch;
+    for (int item = gemv_first_item(); item < items; item += gridDim.x) {
+        const int blk = item % nblk;
+        const int rest = item / nblk;
+        const int split = rest % p.splits;
+        const int b = rest / p.splits;
+        const gfloat_cptr A = (gfloat_cptr)(p.A_ptrs ? p.A_ptrs[b] : p.A + b * p.A_batch);
+        const gfloat_cptr B = (gfloat_cptr)(p.B_ptrs ? p.B_ptrs[b] : p.B + b * p.B_batch);
+        const int j0 = blk * COLS + threadIdx.x;
+        const int k0 = split * p.chunk, k1 = min(p.k, k0 + p.chunk);
+        float acc[kGemvMaxRows][kGemvColsPerLane];
+        if (p.elo != 1 || p.ehi != 254) gemv1_item<true>(p, rows, A, B, j0, k0, k1, acc);
+        else gemv1_item<false>(p, rows, A, B, j0, k0, k1, acc);
+        gemv_store<NTG>(p, b, split, 0, 1, j0, acc);
     }
 }
 
@@ -1661,6 +1923,62 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p)
             const int64_t i = u / p.n, j = u - i * p.n;
             out[i * p.ldc + j] = s;
         }
+    }
+}
+
+// Few outputs with many chunk partials each (the row-vector kernel's
+// splits): 16 lanes (one DPP row) per 4 consecutive outputs. Lane l of a row
+// requests partials l, l + 16, ... of its 4 outputs together; the row then
+// adds them in ascending split order from +0, taking each partial from its
+// lane with a row broadcast, so every lane of the row holds the same sums.
+// Slots past the last split hold +0, which leaves such a sum unchanged (a sum
+// started from +0 is never -0).
+constexpr int kReduceRowLoads = 8;           // partials per lane per round (128 splits)
+
+template <int T>
+__device__ __forceinline__ float row_bcast(float v)
+{
+    // row_newbcast:T, lane T of each row of 16 to the whole row
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + T, 0xF, 0xF, false));
+}
+
+template <int... T>
+__device__ __forceinline__ void row_chain(v4f& s, const v4f& v, std::integer_sequence<int, T...>)
+{
+    ((s[0] += row_bcast<T>(v[0]), s[1] += row_bcast<T>(v[1]), s[2] += row_bcast<T>(v[2]),
+      s[3] += row_bcast<T>(v[3])),
+     ...);
+}
+
+__global__ __launch_bounds__(256) void reduce_rows_kernel(ReduceParams p)
+{
+    const int64_t mn = (int64_t)p.m * p.n;       // a multiple of 4
+    const int64_t units = mn / 4;
+    const int64_t unit = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+    if (unit >= units * p.batch) return;          // the 16 lanes of a row leave together
+    const int l = threadIdx.x & 15;
+    const int64_t b = unit / units, u = unit - b * units;
+    const v4f* src = reinterpret_cast<const v4f*>(p.ws + b * p.splits * mn) + u;
+    const int64_t step = mn / 4;
+    v4f s = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i0 = 0; i0 < p.splits; i0 += 16 * kReduceRowLoads) {
+        v4f v[kReduceRowLoads];
+#pragma unroll
+        for (int j = 0; j < kReduceRowLoads; ++j) {
+            const int sp = i0 + j * 16 + l;
+            v[j] = sp < p.splits ? src[(int64_t)sp * step] : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+#pragma unroll
+        for (int j = 0; j < kReduceRowLoads; ++j) {
+            if (i0 + j * 16 >= p.splits) break;
+            row_chain(s, v[j], std::make_integer_sequence<int, 16>{});
+        }
+    }
+    if (l < 4) {
+        float* out = p.out_ptrs ? p.out_ptrs[b] : p.out + b * p.out_batch;
+        const int64_t r = u * 4 + l;
+        const int64_t i = r / p.n, j = r - i * p.n;
+        out[i * p.ldc + j] = l == 0 ? s[0] : l == 1 ? s[1] : l == 2 ? s[2] : s[3];
     }
 }
 
@@ -1865,11 +2183,12 @@ static const void* gemv_variant(int v)
     case 0: return (const void*)gemv_kernel<false, (1 << 7) * ((1 << 7) + 8) * 2, kGemvLdsThreads>;
     case 1: return (const void*)gemv_kernel<false, (1 << 8) * ((1 << 8) + 8) * 2, kGemvLdsThreads>;
     case 2: return (const void*)gemv_kernel<false, 0, kGemvThreads>;
-    default: return (const void*)gemv_kernel<true, 0, kGemvThreads>;
+    case 3: return (const void*)gemv_kernel<true, 0, kGemvThreads>;
+    default: return (const void*)gemv1_kernel;
     }
 }
 
-int gemv_threads(int variant) { return variant <= 1 ? kGemvLdsThreads : kGemvThreads; }
+int gemv_threads(int variant) { return variant <= 1 ? kGemvLdsThreads : variant == 4 ? kGemv1Threads : kGemvThreads; }
 
 int gemv_blocks_per_cu(int variant)
 {
@@ -1889,8 +2208,15 @@ hipError_t launch_gemv(const GemvParams& p, int variant, int grid, hipStream_t s
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s)
 {
-    const int64_t total = (int64_t)p.m * p.n * p.batch;
-    hipLaunchKernelGGL(reduce_kernel, dim3(grid_for(total, 256, 16384)), dim3(256), 0, s, p);
+    const int64_t mn = (int64_t)p.m * p.n;
+    const int64_t total = mn * p.batch;
+    // few outputs (fewer than 64 Ki threads' worth of 4) and many splits:
+    // 16 lanes per 4 outputs; one workgroup of 256 lanes per 64 outputs
+    if (reduce_by_rows(p.m, p.n, p.batch, p.splits)) {
+        hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)((total + 63) / 64)), dim3(256), 0, s, p);
+    } else {
+        hipLaunchKernelGGL(reduce_kernel, dim3(grid_for(total, 256, 16384)), dim3(256), 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -518,9 +518,13 @@ def run_one(config, args, am, torch, threads):
         kk, nn = host["B"].shape
         nbytes = 4 * (rb * kk + kk * nn + rb * nn)
         achieved = nbytes / (kern_s / max(launches, 1)) / 1e9 if kern_s > 0 else 0.0
+        # one row of A with a table of M <= 8: the kernel that stages table rows per window
+        from datagen import configs as cfg
+        M = args.table_bits or cfg.lut_spec(config)[1]
+        one_row = args.multiplier == "table" and args.rows == 1 and M <= 8
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "amx::gemv_kernel",
-                    **common}
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "amx::gemv1_kernel" if one_row else "amx::gemv_kernel", **common}
     elif args.multiplier == "library":
         achieved = 2 * mac_rate / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": FP32_MFMA_PEAK_TFLOPS,

@@ -64,7 +64,10 @@ def use(am, name):
 @pytest.mark.parametrize("name", ["mitchell7", "perturbed8", "arbitrary11", "native"])
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 13, 16])
 @pytest.mark.parametrize("transA", [0, 1])
-@pytest.mark.parametrize("nk", [(1, 1), (5, 7), (1000, 300), (1025, 2049), (4096, 513), (2050, 2048)])
+# the per-item index counts (chunks) these shapes give cover every residue
+# of the kernel's groups of 4 and 8 indices: 1, 7, 9, 8, 12, 16 and 10 among them
+@pytest.mark.parametrize("nk", [(1, 1), (5, 7), (1000, 300), (1025, 2049), (4096, 513), (2050, 2048),
+                                (600, 3072), (300, 4096), (700, 2560)])
 def test_gemv_parity(am, name, m, transA, nk):
     n, k = nk
     t, M = use(am, name)
@@ -101,8 +104,9 @@ def test_gemv_products_bit_exact(am, name):
 @pytest.mark.parametrize("name", ["mitchell7", "perturbed8", "arbitrary11"])
 def test_gemv_special_b_on_the_fast_path(am, name):
     """k = 1 with op(A) and B of moderate exponents (no product can leave the
-    range, so every wave stays on the fast path) and B holding +-0,
-    subnormals, +-Inf and NaN: every product bit for bit."""
+    range) and B holding +-0, subnormals, +-Inf and NaN: every product bit for
+    bit. Zeros and subnormals keep a wave on the fast path; an Inf or NaN B
+    sends its wave to the checked path."""
     t, M = use(am, name)
     r = splitmix64(950 + M, 700)
     mant = (r & np.uint64(0x7FFFFF)).astype(np.uint32)

@@ -93,3 +93,28 @@ def test_check_rejects_invalid_arguments(check):
     bad = np.array([0, 0, 0, 5, 5, 1], np.int32)
     assert f(0, bad.ctypes.data, 7, need.ctypes.data, have.ctypes.data) == am.APPROX_EINVAL
     assert f(9, bad.ctypes.data, 7, need.ctypes.data, have.ctypes.data) == am.APPROX_EINVAL
+
+
+def test_row_vector_group_rows_stay_inside_the_item():
+    """The row-vector kernel loads B in groups of indices and may request a
+    group that starts past the item's last index (the next group, asked for
+    ahead of use). Every row a group load reads must lie inside the item
+    [k0, k1), offsets from the load's base row must be non-negative (they are
+    unsigned 32-bit byte offsets on the GPU), and index kg + g must read row
+    kg + g while that is inside the item (else row k1 - 1)."""
+    import approximate_multiplier_dnn_amd as am
+    f = am.lib().amx_gemv_group_rows
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    rows = np.zeros(8, np.int32)
+    for k0 in (0, 3, 64):
+        for k1 in range(k0 + 1, k0 + 41):
+            for kg in range(k0, k1 + 17):
+                for ng in (4, 8):
+                    base = f(k1, kg, ng, rows.ctypes.data)
+                    got = rows[:ng]
+                    assert k0 <= base <= k1 - 1, (k0, k1, kg, ng, base)
+                    assert np.all(got >= base) and np.all(got <= k1 - 1), (k0, k1, kg, ng, list(got))
+                    want = np.minimum(kg + np.arange(ng), k1 - 1)
+                    assert np.array_equal(got, want), (k0, k1, kg, ng, list(got))
+    assert f(0, 0, 4, rows.ctypes.data) == -1
