@@ -23,6 +23,7 @@ APPROX_ENOLUT = -2
 APPROX_EUNSUPPORTED = -3
 APPROX_EHIP = -4
 APPROX_ESCRATCH = -5
+APPROX_MAX_GROUP = 4
 
 CONV_PASSES = {"fwd": 0, "dgrad": 1, "wgrad": 2}
 
@@ -33,7 +34,7 @@ MODEL_MITCHELL = 1
 EXPORTS = (
     "approx_lut_build", "approx_lut_build_from_model", "approx_lut_load", "approx_native_load", "approx_lut_bits",
     "approx_exponent_bits_set", "approx_exponent_bits",
-    "approx_gemm", "approx_gemm_noalloc", "approx_gemm_noalloc_max_bytes",
+    "approx_gemm", "approx_gemm_noalloc", "approx_gemm_noalloc_max_bytes", "approx_gemm_grouped",
     "approx_gemm_strided_batched", "approx_gemm_batched",
     "approx_conv2d_fwd", "approx_conv2d_dgrad", "approx_conv2d_wgrad",
     "approx_gemm_chunks", "approx_conv2d_chunks",
@@ -59,6 +60,7 @@ _lib.approx_gemm_noalloc.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, _vp]
 _lib.approx_gemm_noalloc_max_bytes.argtypes = []
 _lib.approx_gemm_strided_batched.argtypes = [_i] * 5 + [_vp, _i, _ll, _vp, _i, _ll, _vp, _i, _ll, _i, _vp]
 _lib.approx_gemm_batched.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, _i, _vp]
+_lib.approx_gemm_grouped.argtypes = [_i] + [_vp] * 12
 for _n in ("approx_conv2d_fwd", "approx_conv2d_dgrad", "approx_conv2d_wgrad"):
     getattr(_lib, _n).argtypes = [_i] * 11 + [_vp, _vp, _vp, _vp]
 _lib.approx_gemm_chunks.argtypes = [_i] * 6 + [_ll, _vp, _vp, _vp, _vp]
@@ -192,6 +194,22 @@ def approx_gemm(transA, transB, m, n, k, A, lda, B, ldb, C, ldc, stream=None):
     """C (m x n, leading dimension ldc) = op(A) op(B) with approximate products."""
     return _check(_lib.approx_gemm(int(transA), int(transB), int(m), int(n), int(k), _ptr(A), int(lda),
                                    _ptr(B), int(ldb), _ptr(C), int(ldc), _stream(stream)), "approx_gemm")
+
+
+def approx_gemm_grouped(calls, stream=None):
+    """Independent GEMMs in one call: `calls` holds 1 .. APPROX_MAX_GROUP
+    tuples (transA, transB, m, n, k, A, lda, B, ldb, C, ldc), approx_gemm's
+    arguments; each C gets the bits approx_gemm would give it."""
+    calls = list(calls)
+    cnt = len(calls)
+    if not 1 <= cnt <= APPROX_MAX_GROUP:
+        return _check(APPROX_EINVAL, "approx_gemm_grouped")
+    ints = [(ctypes.c_int * cnt)(*(int(c[f]) for c in calls)) for f in (0, 1, 2, 3, 4, 6, 8, 10)]
+    ptrs = [(ctypes.c_void_p * cnt)(*(_ptr(c[f]) for c in calls)) for f in (5, 7, 9)]
+    tA, tB, m, n, k, lda, ldb, ldc = ints
+    A, B, C = ptrs
+    return _check(_lib.approx_gemm_grouped(cnt, tA, tB, m, n, k, A, lda, B, ldb, C, ldc, _stream(stream)),
+                  "approx_gemm_grouped")
 
 
 def approx_gemm_chunks(transA, transB, m, n, k, batch, b, i, j):

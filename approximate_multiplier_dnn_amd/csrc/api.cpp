@@ -87,7 +87,8 @@ int current_device(int* dev)
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-const size_t kStatsBytes = align256((amx::STAT_INTS + 1) * sizeof(int));
+// One statistics block per GEMM of a grouped call (a single call uses the first).
+const size_t kStatsBytes = align256((size_t)amx::STAT_BLOCK_INTS * amx::kMaxGroup * sizeof(int));
 
 // Scratch memory for one call on (device, stream): `bytes` after the stats
 // region (*out points past it; *stats at it). Grows only, at least doubling,
@@ -176,6 +177,21 @@ int64_t launch_slots(int dev, int lds_class, int gather, int shape)
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
         s = (int64_t)cus * amx::main_blocks_per_cu(lds_class, gather, shape);
+    }
+    return s;
+}
+
+// Resident workgroups of the grouped GEMM kernel (8-wave shape, vector mode).
+int64_t g_group_slots[kMaxDevices][4];
+
+int64_t group_slots(int dev, int lds_class)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    int64_t& s = g_group_slots[dev][lds_class];
+    if (s == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+        s = (int64_t)cus * amx::main_group_blocks_per_cu(lds_class);
     }
     return s;
 }
@@ -395,80 +411,105 @@ int plan_finalize(Plan& pl, int M)
     return APPROX_OK;
 }
 
-int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M, const ScratchSource& src)
+// Runs plans[0 .. count) as one call: one scratch request, one decode launch
+// for all their operands, the M = 8 copy choices, one GEMM-kernel launch and
+// each plan's reduction. count > 1 (at most kMaxGroup): plans of one grouped
+// kernel variant (amx::main_group_supported), each with its own stats block.
+int run_group(Plan* const* plans, int count, int dev, hipStream_t stream, const uint16_t* image, int M,
+              const ScratchSource& src)
 {
-    MainParams& mp = pl.mp;
-    int rc = plan_finalize(pl, M);
-    if (rc != APPROX_OK) return rc;
-    const int lds_class = pl.lds_class;
-    const int64_t TM = (int64_t)mp.wr * 64 * kShapes[pl.shape].rows_per_lane, TN = (int64_t)mp.wc * kColsPerWave;
-    const int wbytes = pl.wbytes;
-    const size_t lane_b = pl.lane_b, uni_b = pl.uni_b, part_b = pl.part_b;
+    if (count < 1 || count > amx::kMaxGroup) return APPROX_EINVAL;
+    size_t total = 0;
+    for (int g = 0; g < count; ++g) {
+        const int rc = plan_finalize(*plans[g], M);
+        if (rc != APPROX_OK) return rc;
+        total += plans[g]->lane_b + plans[g]->uni_b + plans[g]->part_b;
+    }
+    const Plan& p0 = *plans[0];
+    const int lds_class = p0.lds_class, gather = p0.gather, shape = p0.shape;
     char* base = nullptr;
     int* stats = nullptr;
     bool* stats_ready = nullptr;
-    rc = scratch_get(src, dev, stream, lane_b + uni_b + part_b, &base, &stats, &stats_ready);
+    int rc = scratch_get(src, dev, stream, total, &base, &stats, &stats_ready);
     if (rc != APPROX_OK) return rc;
-    void* lane_panel = base;
-    void* uni_panel = base + lane_b;
-    float* partials = reinterpret_cast<float*>(base + lane_b + uni_b);
-
-    pl.lane.dst = lane_panel;
-    pl.lane.wbytes = wbytes;
-    pl.uni.wbytes = wbytes;
-    pl.lane.stats = stats;
-    pl.lane.dst_batch_stride = pl.lane_words;
-    pl.lane.batch = pl.batch;
-    pl.lane.lane_role = 1;
-    pl.lane.M = M;
     int elo, ehi;
     format_range(dev, &elo, &ehi);
-    pl.lane.elo = pl.uni.elo = mp.elo = elo;
-    pl.lane.ehi = pl.uni.ehi = mp.ehi = ehi;
-    pl.uni.dst = uni_panel;
-    pl.uni.stats = stats + 2;
-    pl.uni.dst_batch_stride = pl.uni_words;
-    pl.uni.batch = pl.batch;
-    pl.uni.lane_role = 0;
-    pl.uni.M = M;
+    const bool forced = force_checked();
+    const DecodeParams* jobs[2 * amx::kMaxGroup];
+    const MainParams* mps[amx::kMaxGroup];
+    int64_t items = 0;
+    size_t off = 0;
+    for (int g = 0; g < count; ++g) {
+        Plan& pl = *plans[g];
+        MainParams& mp = pl.mp;
+        void* lane_panel = base + off;
+        void* uni_panel = base + off + pl.lane_b;
+        float* partials = reinterpret_cast<float*>(base + off + pl.lane_b + pl.uni_b);
+        off += pl.lane_b + pl.uni_b + pl.part_b;
+        int* sg = stats + (size_t)g * amx::STAT_BLOCK_INTS;
 
-    mp.panel = lane_panel;
-    mp.bpanel = uni_panel;
-    mp.lut = image;
-    mp.lut_bytes = M ? amx::lut_image_bytes(M) : 0;
-    mp.stats = stats;
-    mp.panel_batch = pl.lane_words;
-    mp.bpanel_batch = pl.uni_words;
-    mp.batch = pl.batch;
-    mp.force_checked = force_checked() ? 1 : 0;
-    mp.out = pl.C;
-    mp.out_ptrs = pl.Cp;
-    mp.out_batch = pl.strideC;
-    mp.ws = mp.splits > 1 ? partials : nullptr;
+        pl.lane.dst = lane_panel;
+        pl.lane.wbytes = pl.wbytes;
+        pl.uni.wbytes = pl.wbytes;
+        pl.lane.stats = sg;
+        pl.lane.dst_batch_stride = pl.lane_words;
+        pl.lane.batch = pl.batch;
+        pl.lane.lane_role = 1;
+        pl.lane.M = M;
+        pl.lane.elo = pl.uni.elo = mp.elo = elo;
+        pl.lane.ehi = pl.uni.ehi = mp.ehi = ehi;
+        pl.uni.dst = uni_panel;
+        pl.uni.stats = sg + 2;
+        pl.uni.dst_batch_stride = pl.uni_words;
+        pl.uni.batch = pl.batch;
+        pl.uni.lane_role = 0;
+        pl.uni.M = M;
+
+        mp.panel = lane_panel;
+        mp.bpanel = uni_panel;
+        mp.lut = image;
+        mp.lut_bytes = M ? amx::lut_image_bytes(M) : 0;
+        mp.stats = sg;
+        mp.panel_batch = pl.lane_words;
+        mp.bpanel_batch = pl.uni_words;
+        mp.batch = pl.batch;
+        mp.force_checked = forced ? 1 : 0;
+        mp.out = pl.C;
+        mp.out_ptrs = pl.Cp;
+        mp.out_batch = pl.strideC;
+        mp.ws = mp.splits > 1 ? partials : nullptr;
+        jobs[2 * g] = &pl.lane;
+        jobs[2 * g + 1] = &pl.uni;
+        mps[g] = &mp;
+        items += mp.items;
+    }
 
     if (stats_ready == nullptr) {         // fixed scratch: initialised by every call
-        if (amx::launch_init_stats(stats, stream) != hipSuccess) return APPROX_EHIP;
+        if (amx::launch_init_stats(stats, count, stream) != hipSuccess) return APPROX_EHIP;
     } else {
         std::lock_guard<std::mutex> lock(g_mu);
         if (!*stats_ready) {
-            if (amx::launch_init_stats(stats, stream) != hipSuccess) return APPROX_EHIP;
+            if (amx::launch_init_stats(stats, amx::kMaxGroup, stream) != hipSuccess) return APPROX_EHIP;
             *stats_ready = true;
         }
         // until the GEMM kernel is queued, the stats the decodes fill are not reset
         *stats_ready = false;
     }
-    if (amx::launch_decode_pair(pl.lane, pl.uni, stream) != hipSuccess) return APPROX_EHIP;
+    if (amx::launch_decode_group(jobs, 2 * count, stream) != hipSuccess) return APPROX_EHIP;
     if (M == 8) {                     // M = 8 columns carry second copies to choose from
-        amx::AssignParams& ap = pl.asg;
-        ap.panel = static_cast<Word*>(lane_panel);
-        ap.batch_stride = pl.lane_words;
-        ap.batch = pl.batch;
-        ap.pad_w = (1u << M) * 2u;
-        if (amx::launch_assign(ap, stream) != hipSuccess) return APPROX_EHIP;
+        for (int g = 0; g < count; ++g) {
+            Plan& pl = *plans[g];
+            amx::AssignParams& ap = pl.asg;
+            ap.panel = static_cast<Word*>(const_cast<void*>(pl.mp.panel));
+            ap.batch_stride = pl.lane_words;
+            ap.batch = pl.batch;
+            ap.pad_w = (1u << M) * 2u;
+            if (amx::launch_assign(ap, stream) != hipSuccess) return APPROX_EHIP;
+        }
     }
 
-    const int64_t slots = launch_slots(dev, lds_class, pl.gather, pl.shape);
-    const int grid = (int)std::min<int64_t>(mp.items, slots);
+    const int64_t slots = count == 1 ? launch_slots(dev, lds_class, gather, shape) : group_slots(dev, lds_class);
+    const int grid = (int)std::min<int64_t>(items, slots);
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     bool prof;
     {
@@ -479,10 +520,10 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
         if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess) return APPROX_EHIP;
         if (hipEventRecord(ev0, stream) != hipSuccess) return APPROX_EHIP;
     }
-    if (amx::launch_main(mp, lds_class, pl.gather, pl.shape, grid, stream) != hipSuccess) return APPROX_EHIP;
+    if (amx::launch_main_group(mps, count, lds_class, gather, shape, grid, stream) != hipSuccess) return APPROX_EHIP;
     if (stats_ready != nullptr) {
         std::lock_guard<std::mutex> lock(g_mu);
-        *stats_ready = true;      // the GEMM kernel's last workgroup resets them
+        *stats_ready = true;      // the GEMM kernel's last workgroups reset them
     }
     if (prof) {
         if (hipEventRecord(ev1, stream) != hipSuccess) return APPROX_EHIP;
@@ -490,37 +531,48 @@ int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M
         g_events.emplace_back(ev0, ev1);
     }
 
-    if (mp.splits > 1 && mp.full_items == 0) {     // every tile split: sum all of C
-        ReduceParams rp{};
-        rp.ws = partials;
-        rp.out = pl.C;
-        rp.out_ptrs = pl.Cp;
-        rp.m = mp.m_out;
-        rp.n = mp.n_out;
-        rp.ldc = mp.ldc;
-        rp.splits = mp.splits;
-        rp.batch = pl.batch;
-        rp.out_batch = pl.strideC;
-        if (amx::launch_reduce(rp, stream) != hipSuccess) return APPROX_EHIP;
-    } else if (mp.splits > 1) {                    // only the tail tiles are split
-        amx::ReduceTilesParams rp{};
-        rp.ws = partials;
-        rp.out = pl.C;
-        rp.out_ptrs = pl.Cp;
-        rp.m = mp.m_out;
-        rp.n = mp.n_out;
-        rp.ldc = mp.ldc;
-        rp.splits = mp.splits;
-        rp.out_batch = pl.strideC;
-        rp.tiles_m = mp.tiles_m;
-        rp.tiles_n = mp.tiles_n;
-        rp.TM = (int)TM;
-        rp.TN = (int)TN;
-        rp.first_tile = mp.full_items;
-        rp.n_tiles = mp.tail_tiles;
-        if (amx::launch_reduce_tiles(rp, stream) != hipSuccess) return APPROX_EHIP;
+    for (int g = 0; g < count; ++g) {
+        const Plan& pl = *plans[g];
+        const MainParams& mp = pl.mp;
+        if (mp.splits <= 1) continue;
+        if (mp.full_items == 0) {                  // every tile split: sum all of C
+            ReduceParams rp{};
+            rp.ws = mp.ws;
+            rp.out = pl.C;
+            rp.out_ptrs = pl.Cp;
+            rp.m = mp.m_out;
+            rp.n = mp.n_out;
+            rp.ldc = mp.ldc;
+            rp.splits = mp.splits;
+            rp.batch = pl.batch;
+            rp.out_batch = pl.strideC;
+            if (amx::launch_reduce(rp, stream) != hipSuccess) return APPROX_EHIP;
+        } else {                                   // only the tail tiles are split
+            amx::ReduceTilesParams rp{};
+            rp.ws = mp.ws;
+            rp.out = pl.C;
+            rp.out_ptrs = pl.Cp;
+            rp.m = mp.m_out;
+            rp.n = mp.n_out;
+            rp.ldc = mp.ldc;
+            rp.splits = mp.splits;
+            rp.out_batch = pl.strideC;
+            rp.tiles_m = mp.tiles_m;
+            rp.tiles_n = mp.tiles_n;
+            rp.TM = mp.wr * 64 * kShapes[pl.shape].rows_per_lane;
+            rp.TN = mp.wc * kColsPerWave;
+            rp.first_tile = mp.full_items;
+            rp.n_tiles = mp.tail_tiles;
+            if (amx::launch_reduce_tiles(rp, stream) != hipSuccess) return APPROX_EHIP;
+        }
     }
     return APPROX_OK;
+}
+
+int run_plan(Plan& pl, int dev, hipStream_t stream, const uint16_t* image, int M, const ScratchSource& src)
+{
+    Plan* plans[1] = {&pl};
+    return run_group(plans, 1, dev, stream, image, M, src);
 }
 
 // Reduction split of the row-vector kernel (a function of the shapes and the
@@ -666,6 +718,22 @@ void build_gemm_plan(int transA, int transB, int m, int n, int k, int batch, Pla
     pl.asg.LS = 4; pl.asg.O = 0; pl.asg.E = Mp;
 }
 
+// Argument checks of one GEMM (row-major; pointer arrays: the matrices come
+// from device pointer arrays, not A / B / C).
+int gemm_check(int transA, int transB, int m, int n, int k, const float* A, int lda, const float* B, int ldb,
+               const float* C, int ldc, bool arrays)
+{
+    if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1)) return APPROX_EINVAL;
+    if (m < 0 || n < 0 || k < 0) return APPROX_EINVAL;
+    if (lda < std::max(1, transA ? m : k)) return APPROX_EINVAL;
+    if (ldb < std::max(1, transB ? k : n)) return APPROX_EINVAL;
+    if (ldc < std::max(1, n)) return APPROX_EINVAL;
+    if (m == 0 || n == 0) return APPROX_OK;
+    if (!arrays && C == nullptr) return APPROX_EINVAL;
+    if (!arrays && k > 0 && (A == nullptr || B == nullptr)) return APPROX_EINVAL;
+    return APPROX_OK;
+}
+
 int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int lda, long long strideA,
               const float* B, int ldb, long long strideB, float* C, int ldc, long long strideC, int batch,
               void* stream_v, const float* const* Ap = nullptr, const float* const* Bp = nullptr,
@@ -673,19 +741,14 @@ int gemm_impl(int transA, int transB, int m, int n, int k, const float* A, int l
 {
     const bool arrays = Ap != nullptr || Bp != nullptr || Cp != nullptr;
     if (arrays && (Ap == nullptr || Bp == nullptr || Cp == nullptr)) return APPROX_EINVAL;
-    if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1)) return APPROX_EINVAL;
-    if (m < 0 || n < 0 || k < 0 || batch < 0) return APPROX_EINVAL;
-    if (strideA < 0 || strideB < 0 || strideC < 0) return APPROX_EINVAL;
-    if (lda < std::max(1, transA ? m : k)) return APPROX_EINVAL;
-    if (ldb < std::max(1, transB ? k : n)) return APPROX_EINVAL;
-    if (ldc < std::max(1, n)) return APPROX_EINVAL;
+    if (strideA < 0 || strideB < 0 || strideC < 0 || batch < 0) return APPROX_EINVAL;
+    int rc = gemm_check(transA, transB, m, n, k, A, lda, B, ldb, C, ldc, arrays);
+    if (rc != APPROX_OK) return rc;
     if (batch > 65535) return APPROX_EUNSUPPORTED;
     if (m == 0 || n == 0 || batch == 0) return APPROX_OK;
-    if (!arrays && C == nullptr) return APPROX_EINVAL;
-    if (!arrays && k > 0 && (A == nullptr || B == nullptr)) return APPROX_EINVAL;
 
     int dev = 0;
-    int rc = current_device(&dev);
+    rc = current_device(&dev);
     if (rc != APPROX_OK) return rc;
     const uint16_t* image = nullptr;
     const uint16_t* flat = nullptr;
@@ -991,6 +1054,37 @@ void check_plan(const Plan& pl, int M, int64_t* need, int64_t* have)
 
 }  // namespace
 
+// Test hook (host only, no HIP call): the GEMM-kernel plan of a GEMM (kind 0)
+// or Conv2D pass (kind 1..3), arguments as amx_plan_check. Writes out[0..11]:
+// shape, wr, wc, TM, TN, tiles_m, tiles_n, KB, splits, chunk, full_items,
+// tail_tiles; returns the work items (or a negative status).
+extern "C" long long amx_plan_info(int kind, const int* args, int M, int* out)
+{
+    if (args == nullptr || out == nullptr || M < 0 || M > 11) return APPROX_EINVAL;
+    Plan pl;
+    if (kind == 0) {
+        const int tA = args[0], tB = args[1], m = args[2], n = args[3], k = args[4], batch = args[5];
+        if (m < 1 || n < 1 || k < 1 || batch < 1 || (tA & ~1) || (tB & ~1)) return APPROX_EINVAL;
+        build_gemm_plan(tA, tB, m, n, k, batch, pl);
+    } else if (kind >= 1 && kind <= 3) {
+        ConvShape cs;
+        int rc = conv_check(args[0], args[1], args[2], args[3], args[4], args[5], args[6], args[7], args[8], args[9],
+                            args[10], &cs, &cs, &cs, &cs);
+        if (rc != APPROX_OK) return rc;
+        rc = build_conv_plan(kind == 1 ? CONV_FWD : kind == 2 ? CONV_DGRAD : CONV_WGRAD, cs, pl);
+        if (rc != APPROX_OK) return rc;
+    } else {
+        return APPROX_EINVAL;
+    }
+    int rc = plan_finalize(pl, M);
+    if (rc != APPROX_OK) return rc;
+    const MainParams& mp = pl.mp;
+    const int v[12] = {pl.shape, mp.wr, mp.wc, mp.wr * 64 * kShapes[pl.shape].rows_per_lane, mp.wc * kColsPerWave,
+                       mp.tiles_m, mp.tiles_n, mp.KB, mp.splits, mp.chunk, mp.full_items, mp.tail_tiles};
+    for (int i = 0; i < 12; ++i) out[i] = v[i];
+    return (long long)mp.items;
+}
+
 // Test hook (host only, no HIP call): the rows of B that one group load of
 // the row-vector kernel reads, for an item ending at index k1 (exclusive) and
 // a group of ng indices starting at kg: writes them to rows[0 .. ng) and
@@ -1143,6 +1237,57 @@ extern "C" int approx_gemm_noalloc(int transA, int transB, int m, int n, int k, 
 {
     return gemm_impl(transA, transB, m, n, k, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, stream, nullptr, nullptr, nullptr,
                      true);
+}
+
+extern "C" int approx_gemm_grouped(int count, const int* transA, const int* transB, const int* m, const int* n,
+                                   const int* k, const float* const* A, const int* lda, const float* const* B,
+                                   const int* ldb, float* const* C, const int* ldc, void* stream_v)
+{
+    if (count < 1 || count > APPROX_MAX_GROUP) return APPROX_EINVAL;
+    if (!transA || !transB || !m || !n || !k || !A || !lda || !B || !ldb || !C || !ldc) return APPROX_EINVAL;
+    for (int g = 0; g < count; ++g) {         // every member checked before anything is queued
+        const int rc = gemm_check(transA[g], transB[g], m[g], n[g], k[g], A[g], lda[g], B[g], ldb[g], C[g], ldc[g],
+                                  false);
+        if (rc != APPROX_OK) return rc;
+    }
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc != APPROX_OK) return rc;
+    const uint16_t* image = nullptr;
+    int M = 0;
+    rc = table_of(dev, &image, &M);
+    if (rc != APPROX_OK) return rc;
+    hipStream_t stream = static_cast<hipStream_t>(stream_v);
+    // members that approx_gemm runs in the GEMM kernel share launches when
+    // their kernel variant allows it; the others run as approx_gemm would
+    Plan plans[APPROX_MAX_GROUP];
+    Plan* grouped[APPROX_MAX_GROUP];
+    int ng = 0;
+    for (int g = 0; g < count; ++g) {
+        if (m[g] == 0 || n[g] == 0) continue;
+        if (k[g] == 0 || (!transB[g] && row_vector_fits(m[g], n[g], k[g]))) {
+            rc = gemm_impl(transA[g], transB[g], m[g], n[g], k[g], A[g], lda[g], 0, B[g], ldb[g], 0, C[g], ldc[g], 0, 1,
+                           stream_v);
+            if (rc != APPROX_OK) return rc;
+            continue;
+        }
+        Plan& pl = plans[g];
+        build_gemm_plan(transA[g], transB[g], m[g], n[g], k[g], 1, pl);
+        pl.C = C[g];
+        pl.lane.src = A[g];
+        pl.uni.src = B[g];
+        pl.mp.ldc = ldc[g];
+        pl.lane.ld = lda[g];
+        pl.uni.ld = ldb[g];
+        if (!amx::main_group_supported(pl.gather, pl.shape)) {
+            rc = run_plan(pl, dev, stream, image, M, ScratchSource{});
+            if (rc != APPROX_OK) return rc;
+            continue;
+        }
+        grouped[ng++] = &pl;
+    }
+    if (ng == 0) return APPROX_OK;
+    return run_group(grouped, ng, dev, stream, image, M, ScratchSource{});
 }
 
 extern "C" long long approx_gemm_noalloc_max_bytes(void)

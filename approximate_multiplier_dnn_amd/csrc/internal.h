@@ -114,11 +114,16 @@ inline FastDiv make_fastdiv(uint32_t d)
 // kernel reduces the slots.
 // The int after the slots counts the GEMM workgroups that have read them: the
 // last one resets the slots (and the count) for the stream's next call, so a
-// stream's stats need initialising only once.
+// stream's stats need initialising only once. A grouped call keeps one such
+// block per GEMM of the group, STAT_BLOCK_INTS apart.
 constexpr int STAT_SLOTS = 64;
 constexpr int STAT_STRIDE = 32;   // ints between slots
 constexpr int STAT_INTS = STAT_SLOTS * STAT_STRIDE;
 constexpr int STAT_READERS = STAT_INTS;   // index of the reader count
+constexpr int STAT_BLOCK_INTS = STAT_INTS + 64;   // one block: slots, reader count, padding to 256 bytes
+
+// GEMMs of one grouped call (one decode launch, one GEMM-kernel launch).
+constexpr int kMaxGroup = 4;
 
 struct DecodeParams {
     const float* src;
@@ -293,10 +298,21 @@ struct GemvParams {
 int gemv_threads(int variant);
 int gemv_blocks_per_cu(int variant);
 hipError_t launch_gemv(const GemvParams& p, int variant, int grid, hipStream_t s);
-hipError_t launch_init_stats(int* stats, hipStream_t s);
+// Initialises `blocks` statistics blocks (STAT_BLOCK_INTS apart).
+hipError_t launch_init_stats(int* stats, int blocks, hipStream_t s);
+// The decodes of `count` operands (at most 2 * kMaxGroup) in one launch.
+hipError_t launch_decode_group(const DecodeParams* const* jobs, int count, hipStream_t s);
 hipError_t launch_decode_pair(const DecodeParams& a, const DecodeParams& b, hipStream_t s);
 hipError_t launch_assign(const AssignParams& p, hipStream_t s);
 hipError_t launch_main(const MainParams& p, int lds_class, int gather, int shape, int grid, hipStream_t s);
+// `count` (at most kMaxGroup) GEMM-kernel calls of one variant in one launch:
+// their work items in order, ps[g]->items each; each keeps its own stats.
+hipError_t launch_main_group(const MainParams* const* ps, int count, int lds_class, int gather, int shape, int grid,
+                             hipStream_t s);
+// Whether several calls of this variant can share a launch (count > 1), and
+// the resident workgroups per CU of that grouped kernel.
+bool main_group_supported(int gather, int shape);
+int main_group_blocks_per_cu(int lds_class);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 
 // The reduction runs 16 lanes per 4 outputs (reduce_rows_kernel) when the

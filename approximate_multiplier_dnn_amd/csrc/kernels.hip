@@ -259,7 +259,7 @@ __device__ __forceinline__ int64_t decode_source(const DecodeParams& p, uint32_t
     return -1;
 }
 
-// Each decode below runs as one part of decode_pair_kernel: bid / gdim are
+// Each decode below runs as one part of decode_group_kernel: bid / gdim are
 // the workgroup's index and the grid of its own part, blk its linear index.
 __device__ __forceinline__ uint32_t linear_block(uint3 bid, uint3 gdim)
 {
@@ -467,10 +467,12 @@ __device__ __forceinline__ void decode_tile_body(const DecodeParams& p, uint3 bi
 // Empty slots: min 255, max 0 (lane and uniform), and no readers yet.
 __device__ __forceinline__ int stat_reset_value(int i) { return (i & 1) ? 0 : 255; }
 
+// One workgroup per statistics block.
 __global__ __launch_bounds__(256) void init_stats_kernel(int* stats)
 {
-    for (int i = threadIdx.x; i < STAT_INTS; i += 256) stats[i] = stat_reset_value(i);
-    if (threadIdx.x == 0) stats[STAT_READERS] = 0;
+    int* blk = stats + (int64_t)blockIdx.x * STAT_BLOCK_INTS;
+    for (int i = threadIdx.x; i < STAT_INTS; i += 256) blk[i] = stat_reset_value(i);
+    if (threadIdx.x == 0) blk[STAT_READERS] = 0;
 }
 
 // Plain row copies with decode: out[kk][j] (kk < rows_out, j < Np) from
@@ -528,12 +530,20 @@ __device__ __forceinline__ void decode_job(const DecodeJob& jb, uint32_t blk, fl
     }
 }
 
-__global__ __launch_bounds__(256) void decode_pair_kernel(DecodeJob a, DecodeJob b)
+// The decodes of up to 2 * kMaxGroup operands in one launch: job j takes
+// workgroups [first[j], first[j + 1]).
+struct DecodeGroup {
+    int count;
+    uint32_t first[2 * kMaxGroup + 1];
+    DecodeJob job[2 * kMaxGroup];
+};
+
+__global__ __launch_bounds__(256) void decode_group_kernel(DecodeGroup g)
 {
     extern __shared__ __align__(16) float smem[];
-    const uint32_t na = a.gx * a.gy * a.gz;
-    if (blockIdx.x < na) decode_job(a, blockIdx.x, smem);
-    else decode_job(b, blockIdx.x - na, smem);
+    int j = 0;
+    while (j + 1 < g.count && blockIdx.x >= g.first[j + 1]) ++j;
+    decode_job(g.job[j], blockIdx.x - g.first[j], smem);
 }
 
 // Copy choice for the M = 8 lane operands (replica.h): one thread per group
@@ -1189,80 +1199,125 @@ __device__ __forceinline__ void mainloop_native(const MainParams& p, const uint3
 // where no table is staged (native multiplier, table in global memory).
 constexpr int NATIVE_LDS = 16;
 
+// GEMM-kernel calls of one variant run by one launch: call g owns work items
+// [first[g], first[g + 1]) and its own exponent stats (p[g].stats); they
+// share the table.
+struct MainGroup {
+    int count;
+    int first[kMaxGroup + 1];
+    MainParams p[kMaxGroup];
+};
+
+// Exponent-range test of one call from its stats slots (every wave folds
+// them itself: the table takes all of the LDS at M = 8, so the range is not
+// broadcast through it). fast: no product can leave the format's range;
+// ranged: some may fall below it (none above); otherwise the checked path.
+template <bool NATIVE>
+__device__ __forceinline__ void fold_stats(const MainParams& p, bool& fast, bool& ranged)
+{
+    const int* sl = p.stats + ((threadIdx.x & 63) % STAT_SLOTS) * STAT_STRIDE;
+    int v0 = sl[0], v1 = sl[1], v2 = sl[2], v3 = sl[3];
+    for (int off = 32; off > 0; off >>= 1) {
+        v0 = min(v0, __shfl_xor(v0, off, 64));
+        v1 = max(v1, __shfl_xor(v1, off, 64));
+        v2 = min(v2, __shfl_xor(v2, off, 64));
+        v3 = max(v3, __shfl_xor(v3, off, 64));
+    }
+    const int a_min = __builtin_amdgcn_readfirstlane(v0), a_max = __builtin_amdgcn_readfirstlane(v1);
+    const int b_min = __builtin_amdgcn_readfirstlane(v2), b_max = __builtin_amdgcn_readfirstlane(v3);
+    const bool none = (a_min > a_max) || (b_min > b_max);       // an operand without normal values
+    const bool no_over = none || (a_max + b_max - 126 <= p.ehi && a_max <= 253);
+    const bool no_under = none || a_min + b_min - 127 >= p.elo;
+    fast = NATIVE || (!p.force_checked && no_over && no_under);
+    ranged = !NATIVE && !p.force_checked && no_over && !no_under;
+}
+
+// After every wave of the workgroup has read a call's stats (a barrier
+// between): the last of the `readers` workgroups to do so resets them (and
+// the count) for the stream's next call. Wave 0 only.
+__device__ __forceinline__ void release_stats(const MainParams& p, int readers)
+{
+    static_assert(STAT_SLOTS == 64, "one slot per lane of a wave");
+    int* stats = const_cast<int*>(p.stats);
+    int ticket = 0;
+    if (threadIdx.x == 0) ticket = atomicAdd(stats + STAT_READERS, 1);
+    ticket = __shfl(ticket, 0, 64);
+    if (ticket == readers - 1) {
+        int* slot = stats + threadIdx.x * STAT_STRIDE;
+        for (int t = 0; t < 4; ++t) slot[t] = stat_reset_value(t);
+        if (threadIdx.x == 0) stats[STAT_READERS] = 0;
+    }
+}
+
 // GTAB: the table (M = 9..11, too large for LDS) is read from global memory,
 // where it stays resident in L2 / the last-level cache; LDSB is then unused.
-template <int LDSB, bool GATHER, bool NATIVE, int NW, int RPL, bool GTAB>
-__global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainParams p)
+// GROUP: the kernel argument is a MainGroup (calls chosen per work item);
+// otherwise one call's MainParams, kept as the kernel's own argument so its
+// fields stay in scalar registers through the main loop.
+template <bool GROUP>
+using MainArg = typename std::conditional<GROUP, MainGroup, MainParams>::type;
+
+template <bool GROUP>
+__device__ __forceinline__ const MainParams& call_params(const MainArg<GROUP>& a, int g)
+{
+    if constexpr (GROUP) return a.p[g];
+    else return a;
+}
+
+template <int LDSB, bool GATHER, bool NATIVE, int NW, int RPL, bool GTAB, bool GROUP>
+__global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainArg<GROUP> grp)
 {
     constexpr int NT = NW * 64;
     constexpr int LA = GTAB ? LA_GLOBAL : LA_LDS;
     __shared__ __align__(16) unsigned char lds_tab[LDSB];
+    const MainParams& p0 = call_params<GROUP>(grp, 0);
     if (!NATIVE && !GTAB) {
-        const uint4* src = reinterpret_cast<const uint4*>(p.lut);
+        const uint4* src = reinterpret_cast<const uint4*>(p0.lut);
         uint4* dst = reinterpret_cast<uint4*>(lds_tab);
-        const int n16 = p.lut_bytes >> 4;
+        const int n16 = p0.lut_bytes >> 4;
         for (int t = threadIdx.x; t < n16; t += NT) dst[t] = src[t];
     }
     const unsigned char* lut;
-    if constexpr (GTAB) lut = reinterpret_cast<const unsigned char*>(p.lut);
+    if constexpr (GTAB) lut = reinterpret_cast<const unsigned char*>(p0.lut);
     else lut = lds_tab;
-    // every wave folds the stats slots itself (the table takes all of the
-    // LDS at M = 8, so the range is not broadcast through it)
-    int a_min, a_max, b_min, b_max;
-    {
-        const int* sl = p.stats + ((threadIdx.x & 63) % STAT_SLOTS) * STAT_STRIDE;
-        int v0 = sl[0], v1 = sl[1], v2 = sl[2], v3 = sl[3];
-        for (int off = 32; off > 0; off >>= 1) {
-            v0 = min(v0, __shfl_xor(v0, off, 64));
-            v1 = max(v1, __shfl_xor(v1, off, 64));
-            v2 = min(v2, __shfl_xor(v2, off, 64));
-            v3 = max(v3, __shfl_xor(v3, off, 64));
-        }
-        a_min = __builtin_amdgcn_readfirstlane(v0);
-        a_max = __builtin_amdgcn_readfirstlane(v1);
-        b_min = __builtin_amdgcn_readfirstlane(v2);
-        b_max = __builtin_amdgcn_readfirstlane(v3);
-    }
-    __syncthreads();                               // the table is staged; every wave has read the stats
-    if (threadIdx.x < 64) {
-        // the last workgroup to read the stats resets them for the stream's
-        // next call (4 ints per slot; lane l resets slot l)
-        static_assert(STAT_SLOTS == 64, "one slot per lane of a wave");
-        int ticket = 0;
-        if (threadIdx.x == 0) ticket = atomicAdd(const_cast<int*>(p.stats) + STAT_READERS, 1);
-        ticket = __shfl(ticket, 0, 64);
-        if (ticket == (int)gridDim.x - 1) {
-            int* slot = const_cast<int*>(p.stats) + threadIdx.x * STAT_STRIDE;
-            for (int t = 0; t < 4; ++t) slot[t] = stat_reset_value(t);
-            if (threadIdx.x == 0) const_cast<int*>(p.stats)[STAT_READERS] = 0;
-        }
-    }
-    // fast: no product can leave the format's range; ranged: some may fall
-    // below it (none above); otherwise the checked path
-    const bool none = (a_min > a_max) || (b_min > b_max);       // an operand without normal values
-    const bool no_over = none || (a_max + b_max - 126 <= p.ehi && a_max <= 253);
-    const bool no_under = none || a_min + b_min - 127 >= p.elo;
-    const bool fast = NATIVE || (!p.force_checked && no_over && no_under);
-    const bool ranged = !NATIVE && !p.force_checked && no_over && !no_under;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const uint32_t quad = (uint32_t)lane & 3u;     // this lane's place in the uniform-word quads
-    const int wrow = wave / p.wc, wcol = wave - wrow * p.wc;
     const int G = gridDim.x;
     // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin (block
     // b runs on XCD b % 8, checked with HW_REG_XCC_ID), so give the workgroups
     // of one XCD consecutive work items: they share operand rows in its L2.
+    // (A bijection of the block index: with the items of a call consecutive,
+    // min(G, its items) workgroups read its stats.)
     const int v = (G & 7) == 0 ? (int)((blockIdx.x & 7u) * (unsigned)(G >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
-    const int TM = p.wr * 64 * RPL, TN = p.wc * CPW;
-    const int items = (int)p.items;
-    const int tiles = p.tiles_m * p.tiles_n;
+    int items, cur = -1;                           // cur: the call whose stats this workgroup has folded
+    if constexpr (GROUP) items = grp.first[grp.count];
+    else items = (int)grp.items;
+    bool fast = false, ranged = false;
 
     for (int item = v; item < items; item += G) {
+        int g = 0, first = 0, count = items;
+        if constexpr (GROUP) {
+            while (g + 1 < grp.count && item >= grp.first[g + 1]) ++g;
+            first = grp.first[g];
+            count = grp.first[g + 1] - first;
+        }
+        const MainParams& p = call_params<GROUP>(grp, g);
+        if (g != cur) {                            // uniform: every wave of the workgroup enters together
+            fold_stats<NATIVE>(p, fast, ranged);
+            __syncthreads();                       // the table is staged; every wave has read the stats
+            if (threadIdx.x < 64) release_stats(p, min(G, count));
+            cur = g;
+        }
+        const int wrow = wave / p.wc, wcol = wave - wrow * p.wc;
+        const int TM = p.wr * 64 * RPL, TN = p.wc * CPW;
+        const int tiles = p.tiles_m * p.tiles_n;
+        const int li = item - first;               // the item within its call
         int tl, split;                             // (batch entry, tile) pair; split -1: whole
-        if (item < p.full_items) {
-            tl = item;
+        if (li < p.full_items) {
+            tl = li;
             split = -1;
         } else {
-            const int t2 = item - p.full_items;
+            const int t2 = li - p.full_items;
             split = t2 / p.tail_tiles;
             tl = p.full_items + (t2 - split * p.tail_tiles);
         }
@@ -2046,9 +2101,9 @@ static int grid_for(int64_t work, int per_block, int cap)
     return (int)g;
 }
 
-hipError_t launch_init_stats(int* stats, hipStream_t s)
+hipError_t launch_init_stats(int* stats, int blocks, hipStream_t s)
 {
-    hipLaunchKernelGGL(init_stats_kernel, dim3(1), dim3(256), 0, s, stats);
+    hipLaunchKernelGGL(init_stats_kernel, dim3(blocks), dim3(256), 0, s, stats);
     return hipGetLastError();
 }
 
@@ -2114,20 +2169,36 @@ static DecodeJob plan_decode(const DecodeParams& p0)
     return grid(DV_GENERIC, (uint32_t)grid_for(p.count, 256, 8192), (uint32_t)p.batch, 1);
 }
 
+hipError_t launch_decode_group(const DecodeParams* const* jobs, int count, hipStream_t s)
+{
+    if (count < 1 || count > 2 * kMaxGroup) return hipErrorInvalidValue;
+    DecodeGroup g{};
+    uint64_t blocks = 0;
+    size_t bytes = 0;
+    int n = 0;
+    for (int i = 0; i < count; ++i) {
+        const DecodeJob jb = plan_decode(*jobs[i]);
+        const uint64_t nb = (uint64_t)jb.gx * jb.gy * jb.gz;
+        if (nb == 0) continue;
+        g.job[n] = jb;
+        g.first[n] = (uint32_t)blocks;
+        blocks += nb;
+        if (jb.variant == DV_IMG) bytes = std::max(bytes, (size_t)jb.p.row_floats * sizeof(float));
+        if (jb.variant == DV_TILE) bytes = std::max(bytes, (size_t)kTileLdsBytes);
+        ++n;
+        if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    }
+    if (n == 0) return hipSuccess;
+    g.count = n;
+    g.first[n] = (uint32_t)blocks;
+    hipLaunchKernelGGL(decode_group_kernel, dim3((uint32_t)blocks), dim3(256), bytes, s, g);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode_pair(const DecodeParams& a, const DecodeParams& b, hipStream_t s)
 {
-    const DecodeJob ja = plan_decode(a), jb = plan_decode(b);
-    const uint64_t blocks = (uint64_t)ja.gx * ja.gy * ja.gz + (uint64_t)jb.gx * jb.gy * jb.gz;
-    if (blocks == 0) return hipSuccess;
-    if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    auto lds = [](const DecodeJob& j) -> size_t {
-        if (j.variant == DV_IMG) return (size_t)j.p.row_floats * sizeof(float);
-        if (j.variant == DV_TILE) return (size_t)kTileLdsBytes;
-        return 0;
-    };
-    const size_t bytes = std::max(lds(ja), lds(jb));
-    hipLaunchKernelGGL(decode_pair_kernel, dim3((uint32_t)blocks), dim3(256), bytes, s, ja, jb);
-    return hipGetLastError();
+    const DecodeParams* jobs[2] = {&a, &b};
+    return launch_decode_group(jobs, 2, s);
 }
 
 // The GEMM kernel variant of (lds_class, gather, shape): lds_class 0 = table
@@ -2139,17 +2210,17 @@ static const void* main_variant_shape(int lds_class, int gather)
     constexpr int NW = kShapes[S].waves, R = kShapes[S].rows_per_lane;
     switch (lds_class) {
     case 0:
-        return gather ? (const void*)main_kernel<LDS_SMALL, true, false, NW, R, false>
-                      : (const void*)main_kernel<LDS_SMALL, false, false, NW, R, false>;
+        return gather ? (const void*)main_kernel<LDS_SMALL, true, false, NW, R, false, false>
+                      : (const void*)main_kernel<LDS_SMALL, false, false, NW, R, false, false>;
     case 1:
-        return gather ? (const void*)main_kernel<LDS_LARGE, true, false, NW, R, false>
-                      : (const void*)main_kernel<LDS_LARGE, false, false, NW, R, false>;
+        return gather ? (const void*)main_kernel<LDS_LARGE, true, false, NW, R, false, false>
+                      : (const void*)main_kernel<LDS_LARGE, false, false, NW, R, false, false>;
     case 2:
-        return gather ? (const void*)main_kernel<NATIVE_LDS, true, true, NW, R, false>
-                      : (const void*)main_kernel<NATIVE_LDS, false, true, NW, R, false>;
+        return gather ? (const void*)main_kernel<NATIVE_LDS, true, true, NW, R, false, false>
+                      : (const void*)main_kernel<NATIVE_LDS, false, true, NW, R, false, false>;
     default:
-        return gather ? (const void*)main_kernel<NATIVE_LDS, true, false, NW, R, true>
-                      : (const void*)main_kernel<NATIVE_LDS, false, false, NW, R, true>;
+        return gather ? (const void*)main_kernel<NATIVE_LDS, true, false, NW, R, true, false>
+                      : (const void*)main_kernel<NATIVE_LDS, false, false, NW, R, true, false>;
     }
 }
 
@@ -2158,12 +2229,55 @@ static const void* main_variant(int lds_class, int gather, int shape)
     return shape == 0 ? main_variant_shape<0>(lds_class, gather) : main_variant_shape<1>(lds_class, gather);
 }
 
+// Grouped launches: the 8-wave shape, operands in vector mode (dense GEMMs).
+bool main_group_supported(int gather, int shape) { return gather == 0 && shape == 0; }
+
+static const void* main_group_variant(int lds_class)
+{
+    constexpr int NW = kShapes[0].waves, R = kShapes[0].rows_per_lane;
+    switch (lds_class) {
+    case 0: return (const void*)main_kernel<LDS_SMALL, false, false, NW, R, false, true>;
+    case 1: return (const void*)main_kernel<LDS_LARGE, false, false, NW, R, false, true>;
+    case 2: return (const void*)main_kernel<NATIVE_LDS, false, true, NW, R, false, true>;
+    default: return (const void*)main_kernel<NATIVE_LDS, false, false, NW, R, true, true>;
+    }
+}
+
 hipError_t launch_main(const MainParams& p, int lds_class, int gather, int shape, int grid, hipStream_t s)
 {
     MainParams arg = p;
     void* args[] = {&arg};
     return hipLaunchKernel(main_variant(lds_class, gather, shape), dim3(grid), dim3(kShapes[shape].waves * 64), args,
                            0, s);
+}
+
+hipError_t launch_main_group(const MainParams* const* ps, int count, int lds_class, int gather, int shape, int grid,
+                             hipStream_t s)
+{
+    if (count < 1 || count > kMaxGroup) return hipErrorInvalidValue;
+    if (count == 1) return launch_main(*ps[0], lds_class, gather, shape, grid, s);
+    if (!main_group_supported(gather, shape)) return hipErrorInvalidValue;
+    MainGroup arg{};
+    int64_t total = 0;
+    for (int g = 0; g < count; ++g) {
+        arg.p[g] = *ps[g];
+        arg.first[g] = (int)total;
+        total += ps[g]->items;
+    }
+    if (total > INT32_MAX) return hipErrorInvalidValue;
+    arg.count = count;
+    arg.first[count] = (int)total;
+    void* args[] = {&arg};
+    return hipLaunchKernel(main_group_variant(lds_class), dim3(grid), dim3(kShapes[0].waves * 64), args, 0, s);
+}
+
+int main_group_blocks_per_cu(int lds_class)
+{
+    int n = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, main_group_variant(lds_class),
+                                                                      kShapes[0].waves * 64, 0);
+    if (e != hipSuccess || n < 1) n = 1;
+    return n;
 }
 
 int main_blocks_per_cu(int lds_class, int gather, int shape)

@@ -64,6 +64,8 @@ extern "C" {
 #define APPROX_EHIP (-4)         /* a HIP runtime call failed (allocation, copy, launch) */
 #define APPROX_ESCRATCH (-5)     /* the call needs more scratch than approx_gemm_noalloc's fixed maximum */
 
+#define APPROX_MAX_GROUP 4       /* GEMMs per approx_gemm_grouped call */
+
 /* Built-in C models of multipliers for approx_lut_build. */
 #define APPROX_MODEL_EXACT 0    /* the exact product of the M-bit mantissas */
 #define APPROX_MODEL_MITCHELL 1 /* Mitchell's logarithmic multiplier: 1+x+y, or 2(x+y) when x+y >= 1 */
@@ -173,6 +175,29 @@ int approx_exponent_bits(void);
 int approx_gemm(int transA, int transB, int m, int n, int k,
                 const float *A, int lda, const float *B, int ldb,
                 float *C, int ldc, void *stream);
+
+/*
+ * Several independent GEMMs in one call: `count` (1 .. APPROX_MAX_GROUP)
+ * members, member g given by element g of each host array with the meaning
+ * of approx_gemm's arguments (transA[g], transB[g], m[g], n[g], k[g], the
+ * device pointers A[g], B[g], C[g], lda[g], ldb[g], ldc[g]). For callers that
+ * run GEMMs that do not depend on each other back to back, such as the input
+ * and weight gradients of a dense layer's backpropagation (ApproxTrain,
+ * Section VI-D, AMDENSE): members that approx_gemm would run in its GEMM
+ * kernel share one operand-decode launch and one GEMM-kernel launch, which
+ * a small GEMM alone cannot fill. Each member is computed exactly as
+ * approx_gemm computes it (same products and summation order, so the same
+ * bits; approx_gemm_chunks describes each member's order); members that
+ * approx_gemm runs otherwise (few rows, k = 0, or a kernel shape that cannot
+ * be shared) run as approx_gemm runs them, on the same stream. The C of
+ * different members must not overlap, nor alias any member's A or B. The
+ * host arrays are read during the call only. Errors: APPROX_EINVAL (count
+ * outside 1 .. APPROX_MAX_GROUP, a NULL array, or any member failing
+ * approx_gemm's checks: nothing is queued then), APPROX_ENOLUT, APPROX_EHIP.
+ */
+int approx_gemm_grouped(int count, const int *transA, const int *transB, const int *m, const int *n,
+                        const int *k, const float *const *A, const int *lda, const float *const *B,
+                        const int *ldb, float *const *C, const int *ldc, void *stream);
 
 /*
  * approx_gemm without any allocation, for callers that cannot allocate
