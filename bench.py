@@ -161,25 +161,17 @@ def build_workload(config, am, torch, mult="table", table_bits=0, gemv=False, ge
             calls.append((ta, tb, m, n, k, A, A.shape[1], B, B.shape[1], C, n))
 
         # A training step's dependencies: the forward chain, then per layer
-        # (top down) the input gradient on this stream and the weight
-        # gradient, which needs the layer's output gradient, on a second one.
+        # (top down) the weight gradient and the input gradient, which both
+        # need only the layer's output gradient: one grouped call per layer.
         names = [g[0] for g in cfg.mlp_gemms()]
         byname = dict(zip(names, calls))
         nl = len(names) // 3
-        side = torch.cuda.Stream()
-        evs = [torch.cuda.Event() for _ in range(nl + 1)]
 
         def step():
-            cur = torch.cuda.current_stream()
             for l in range(nl):
-                am.approx_gemm(*byname[f"fwd{l}"], stream=cur)
-            evs[0].record(cur)
-            for i, l in enumerate(reversed(range(nl))):
-                side.wait_event(evs[i])
-                am.approx_gemm(*byname[f"wgrad{l}"], stream=side)
-                am.approx_gemm(*byname[f"dgrad{l}"], stream=cur)
-                evs[i + 1].record(cur)
-            cur.wait_stream(side)
+                am.approx_gemm(*byname[f"fwd{l}"])
+            for l in reversed(range(nl)):
+                am.approx_gemm_grouped([byname[f"wgrad{l}"], byname[f"dgrad{l}"]])
 
         workload = "mlp_784-1024-1024-10_b256_fwd_dgrad_wgrad_" + ("lut_m7_mitchell" if lut is not None else "native_fp32_fma")
         info = dict(batch=256, widths=[784, 1024, 1024, 10])
