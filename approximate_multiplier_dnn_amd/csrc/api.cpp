@@ -65,6 +65,7 @@ struct Arena {
     void* ptr = nullptr;
     size_t bytes = 0;
     bool stats_ready = false;
+    uint32_t gen = 0;           // generation of the last call's k-segment ranges (1 .. SEG_GEN_MAX - 1)
 };
 
 std::mutex g_mu;
@@ -104,7 +105,8 @@ bool alloc_refused(size_t bytes)
     return v != nullptr && v[0] != '\0' && bytes > (size_t)std::strtoull(v, nullptr, 10);
 }
 
-int arena_get(int dev, hipStream_t stream, size_t bytes, char** out, int** stats = nullptr, bool** ready = nullptr)
+int arena_get(int dev, hipStream_t stream, size_t bytes, char** out, int** stats = nullptr, bool** ready = nullptr,
+              uint32_t** gen = nullptr)
 {
     std::lock_guard<std::mutex> lock(g_mu);
     Arena& a = g_arenas[{dev, stream}];
@@ -121,6 +123,7 @@ int arena_get(int dev, hipStream_t stream, size_t bytes, char** out, int** stats
     *out = static_cast<char*>(a.ptr) + kStatsBytes;
     if (stats != nullptr) *stats = static_cast<int*>(a.ptr);
     if (ready != nullptr) *ready = &a.stats_ready;   // std::map nodes are stable
+    if (gen != nullptr) *gen = &a.gen;
     return APPROX_OK;
 }
 
@@ -155,13 +158,14 @@ struct ScratchSource {
 };
 
 int scratch_get(const ScratchSource& src, int dev, hipStream_t stream, size_t bytes, char** out, int** stats,
-                bool** ready)
+                bool** ready, uint32_t** gen = nullptr)
 {
-    if (src.fixed == nullptr) return arena_get(dev, stream, bytes, out, stats, ready);
+    if (src.fixed == nullptr) return arena_get(dev, stream, bytes, out, stats, ready, gen);
     if (bytes > kFixedScratchBytes - kStatsBytes) return APPROX_ESCRATCH;
     *out = src.fixed + kStatsBytes;
     if (stats != nullptr) *stats = reinterpret_cast<int*>(src.fixed);
     if (ready != nullptr) *ready = nullptr;
+    if (gen != nullptr) *gen = nullptr;
     return APPROX_OK;
 }
 
@@ -430,8 +434,21 @@ int run_group(Plan* const* plans, int count, int dev, hipStream_t stream, const 
     char* base = nullptr;
     int* stats = nullptr;
     bool* stats_ready = nullptr;
-    int rc = scratch_get(src, dev, stream, total, &base, &stats, &stats_ready);
+    uint32_t* gen_ptr = nullptr;
+    int rc = scratch_get(src, dev, stream, total, &base, &stats, &stats_ready, &gen_ptr);
     if (rc != APPROX_OK) return rc;
+    // this call's generation for its k-segment ranges (the fixed scratch is
+    // initialised by every call: generation 1 always)
+    uint32_t gen = 1;
+    bool wrapped = false;
+    if (gen_ptr != nullptr) {
+        std::lock_guard<std::mutex> lock(g_mu);
+        if (++*gen_ptr >= amx::SEG_GEN_MAX) {
+            *gen_ptr = 1;
+            wrapped = true;
+        }
+        gen = *gen_ptr;
+    }
     int elo, ehi;
     format_range(dev, &elo, &ehi);
     const bool forced = force_checked();
@@ -458,6 +475,17 @@ int run_group(Plan* const* plans, int count, int dev, hipStream_t stream, const 
         pl.lane.M = M;
         pl.lane.elo = pl.uni.elo = mp.elo = elo;
         pl.lane.ehi = pl.uni.ehi = mp.ehi = ehi;
+        // k-segment ranges: dense operands decoded a segment per workgroup,
+        // one batch entry (a batch's entries would meet in the same
+        // segments) and more than one segment (else the call's range says
+        // it all); the native multiplier is always on its fast path
+        const bool segs = M != 0 && !pl.gather && pl.batch == 1 && mp.KB > amx::SEG_KSTEPS &&
+                          mp.KB <= amx::SEG_MAX * amx::SEG_KSTEPS && amx::decode_covers_segments(pl.lane) &&
+                          amx::decode_covers_segments(pl.uni);
+        mp.segs = segs ? (int)cdiv(mp.KB, amx::SEG_KSTEPS) : 0;
+        pl.lane.seg = segs ? sg + amx::STAT_SEG : nullptr;
+        pl.uni.seg = segs ? sg + amx::STAT_SEG + 2 : nullptr;
+        pl.lane.seg_gen = pl.uni.seg_gen = mp.seg_gen = gen << 8;
         pl.uni.dst = uni_panel;
         pl.uni.stats = sg + 2;
         pl.uni.dst_batch_stride = pl.uni_words;
@@ -488,7 +516,7 @@ int run_group(Plan* const* plans, int count, int dev, hipStream_t stream, const 
         if (amx::launch_init_stats(stats, count, stream) != hipSuccess) return APPROX_EHIP;
     } else {
         std::lock_guard<std::mutex> lock(g_mu);
-        if (!*stats_ready) {
+        if (!*stats_ready || wrapped) {         // new arena, or the generations start again
             if (amx::launch_init_stats(stats, amx::kMaxGroup, stream) != hipSuccess) return APPROX_EHIP;
             *stats_ready = true;
         }

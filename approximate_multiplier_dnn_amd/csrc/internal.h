@@ -120,12 +120,30 @@ constexpr int STAT_SLOTS = 64;
 constexpr int STAT_STRIDE = 32;   // ints between slots
 constexpr int STAT_INTS = STAT_SLOTS * STAT_STRIDE;
 constexpr int STAT_READERS = STAT_INTS;   // index of the reader count
-constexpr int STAT_BLOCK_INTS = STAT_INTS + 64;   // one block: slots, reader count, padding to 256 bytes
+// Per k-segment ranges (dense GEMMs whose decodes write them): segment s
+// covers reduction indices [64 s, 64 s + 64), that is k-steps [16 s, 16 s + 16),
+// and holds SEG_REPL replicas of {lane min, lane max, uniform min, uniform max}
+// at STAT_SEG + 4 (SEG_REPL s + r) (a decode workgroup folds into replica
+// (its index mod SEG_REPL), so fewer workgroups meet at one address), each as
+// (call generation << 8) | value, folded with atomicMax (a minimum e as
+// 255 - e); a reader takes the maximum over the replicas. A call whose whole range fails the fast test still runs its
+// fast path on every segment whose own ranges pass it. Nothing resets them:
+// a tag older than the call's generation means the call wrote nothing there
+// (no normal values), a newer one (a graph replayed after later calls) that
+// the segment's ranges are unknown, so the call's own range decides it.
+constexpr int STAT_SEG = STAT_INTS + 64;
+constexpr uint32_t SEG_GEN_MAX = 1u << 24;   // generations run 1 .. 2^24 - 1, then the blocks are re-initialised
+constexpr int SEG_KSTEPS = 16;
+constexpr int SEG_MAX = 1024;             // segments per call (k up to 65,536)
+constexpr int SEG_REPL = 4;
+constexpr int STAT_BLOCK_INTS = STAT_SEG + 4 * SEG_REPL * SEG_MAX;   // one block: slots, counts, segments
 
 // GEMMs of one grouped call (one decode launch, one GEMM-kernel launch).
 constexpr int kMaxGroup = 4;
 
 struct DecodeParams {
+    int* seg;                       // this operand's k-segment ranges (segment s, replica r: min at seg[4 (SEG_REPL s + r)], max after it), or null
+    uint32_t seg_gen;               // the call's generation, shifted left by 8
     const float* src;
     const float* const* src_ptrs;   // batched by pointer array (device), else src + b * stride
     void* dst;           // Words (wbytes 8) or, for the native multiplier, the operands' bits (wbytes 4)
@@ -211,6 +229,8 @@ struct MainParams {
     int64_t items;
     int force_checked;        // 1: always use the per-product checked path
     int elo, ehi;             // FP32 biased exponents of the format's normal range (1, 254 for FP32)
+    int segs;                 // k-segments with ranges in stats (0: the call's range only)
+    uint32_t seg_gen;         // the call's generation, shifted left by 8
 };
 
 // Copy choice of the M = 8 lane-operand table offsets (replica.h), one group
@@ -302,6 +322,9 @@ hipError_t launch_gemv(const GemvParams& p, int variant, int grid, hipStream_t s
 hipError_t launch_init_stats(int* stats, int blocks, hipStream_t s);
 // The decodes of `count` operands (at most 2 * kMaxGroup) in one launch.
 hipError_t launch_decode_group(const DecodeParams* const* jobs, int count, hipStream_t s);
+// Whether this operand's decode runs in workgroups that each cover reduction
+// indices of one k-segment only (and can so record the segment ranges).
+bool decode_covers_segments(const DecodeParams& p);
 hipError_t launch_decode_pair(const DecodeParams& a, const DecodeParams& b, hipStream_t s);
 hipError_t launch_assign(const AssignParams& p, hipStream_t s);
 hipError_t launch_main(const MainParams& p, int lds_class, int gather, int shape, int grid, hipStream_t s);

@@ -145,9 +145,11 @@ __device__ __forceinline__ void put_words(void* dst, int64_t i, const Word (&wd)
 // Fold this thread's exponent range into the call's stats: wave reduction,
 // then workgroup reduction through LDS, then one atomic pair per workgroup
 // into slot (blk % STAT_SLOTS; blk: the workgroup's index in its decode), so
-// no single address takes every atomic. Must be called by every thread of a
-// 256-thread workgroup.
-__device__ __forceinline__ void flush_stats(int* stats, int emin, int emax, uint32_t blk)
+// no single address takes every atomic; and into a replica of the k-segment's
+// range `seg` when the workgroup's elements lie in one segment (else null). Must be
+// called by every thread of a 256-thread workgroup.
+__device__ __forceinline__ void flush_stats(int* stats, int emin, int emax, uint32_t blk, int* seg = nullptr,
+                                            uint32_t seg_gen = 0)
 {
     __shared__ int red[2][4];
     for (int off = 32; off > 0; off >>= 1) {
@@ -170,6 +172,11 @@ __device__ __forceinline__ void flush_stats(int* stats, int emin, int emax, uint
             int* slot = stats + (blk % STAT_SLOTS) * STAT_STRIDE;
             atomicMin(&slot[0], emin);
             atomicMax(&slot[1], emax);
+            if (seg != nullptr) {
+                unsigned int* r = reinterpret_cast<unsigned int*>(seg + 4 * (blk % SEG_REPL));
+                atomicMax(&r[0], seg_gen | (uint32_t)(255 - emin));
+                atomicMax(&r[1], seg_gen | (uint32_t)emax);
+            }
         }
     }
 }
@@ -461,17 +468,20 @@ __device__ __forceinline__ void decode_tile_body(const DecodeParams& p, uint3 bi
             }
         }
     }
-    flush_stats(p.stats, emin, emax, linear_block(bid, gdim));
+    // reduction indices [64 bid.y, 64 bid.y + 64): one k-segment
+    flush_stats(p.stats, emin, emax, linear_block(bid, gdim), p.seg ? p.seg + 4 * SEG_REPL * bid.y : nullptr,
+                p.seg_gen);
 }
 
 // Empty slots: min 255, max 0 (lane and uniform), and no readers yet.
 __device__ __forceinline__ int stat_reset_value(int i) { return (i & 1) ? 0 : 255; }
 
-// One workgroup per statistics block.
+// One workgroup per statistics block: slots, counts and k-segments.
 __global__ __launch_bounds__(256) void init_stats_kernel(int* stats)
 {
     int* blk = stats + (int64_t)blockIdx.x * STAT_BLOCK_INTS;
     for (int i = threadIdx.x; i < STAT_INTS; i += 256) blk[i] = stat_reset_value(i);
+    for (int i = threadIdx.x; i < 4 * SEG_REPL * SEG_MAX; i += 256) blk[STAT_SEG + i] = 0;   // generation 0: no call's
     if (threadIdx.x == 0) blk[STAT_READERS] = 0;
 }
 
@@ -511,7 +521,9 @@ __device__ __forceinline__ void decode_rows_body(const DecodeParams& p, uint3 bi
                 : zero_word(p.M, p.lane_role);
         put_words(p.dst, d0 + (int64_t)kk * p.ldw + col, wd, 4, true, p.wbytes);
     }
-    flush_stats(p.stats, emin, emax, linear_block(bid, gdim));
+    // rows [r0, r0 + rb) with rb dividing 64 (the host gives a segment pointer only then): one k-segment
+    flush_stats(p.stats, emin, emax, linear_block(bid, gdim), p.seg ? p.seg + 4 * SEG_REPL * (r0 >> 6) : nullptr,
+                p.seg_gen);
 }
 
 // The decodes of both operands of a call in one launch: workgroups [0, na)
@@ -1232,6 +1244,32 @@ __device__ __forceinline__ void fold_stats(const MainParams& p, bool& fast, bool
     ranged = !NATIVE && !p.force_checked && no_over && !no_under;
 }
 
+// Path of k-segment s of a call whose own range failed the fast test (as
+// fold_stats, from the segment's ranges): 0 fast, 1 fast with underflow, 2
+// checked; `call_mode` (1 or 2) where a range is unknown.
+__device__ __forceinline__ int seg_mode(const MainParams& p, int s, int call_mode)
+{
+    const uint32_t* r = reinterpret_cast<const uint32_t*>(p.stats) + STAT_SEG + 4 * SEG_REPL * s;
+    const uint32_t g = p.seg_gen;
+    uint32_t la = 0, lb = 0, ua = 0, ub = 0;
+#pragma unroll
+    for (int q = 0; q < SEG_REPL; ++q) {
+        la = max(la, r[4 * q]);
+        lb = max(lb, r[4 * q + 1]);
+        ua = max(ua, r[4 * q + 2]);
+        ub = max(ub, r[4 * q + 3]);
+    }
+    // a tag below the call's: the call wrote nothing there (that operand has
+    // no normal values in the segment, so no product can leave the range)
+    if ((la & ~0xFFu) < g || (ua & ~0xFFu) < g) return 0;
+    if ((la & ~0xFFu) != g || (lb & ~0xFFu) != g || (ua & ~0xFFu) != g || (ub & ~0xFFu) != g) return call_mode;
+    const int a_min = 255 - (int)(la & 0xFFu), a_max = (int)(lb & 0xFFu);
+    const int b_min = 255 - (int)(ua & 0xFFu), b_max = (int)(ub & 0xFFu);
+    const bool no_over = a_max + b_max - 126 <= p.ehi && a_max <= 253;
+    const bool no_under = a_min + b_min - 127 >= p.elo;
+    return no_over ? (no_under ? 0 : 1) : 2;
+}
+
 // After every wave of the workgroup has read a call's stats (a barrier
 // between): the last of the `readers` workgroups to do so resets them (and
 // the count) for the stream's next call. Wave 0 only.
@@ -1354,7 +1392,22 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainArg<GROUP> grp)
             // a ring of 3 k-steps; 2 in the 12-wave shape, whose registers hold no third
             if constexpr (NATIVE) mainloop_native<GATHER, NW == 12 ? 2 : 3, RPL>(p, npanel, nbsrc, base, kb0, kb1, quad, acc);
             else if (fast) mainloop_fast<GATHER, false, 4, RPL, LA, GTAB ? 0 : AMX_GOFF>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
-            else {
+            else if (p.segs > 0 && !p.force_checked) {
+                // the call's range failed the fast test: each k-segment (16
+                // k-steps) on the path its own ranges allow, in ascending order
+                // (the paths give the same bits wherever more than one applies)
+                for (int ka = kb0; ka < kb1;) {
+                    const int sg = ka / SEG_KSTEPS, kz = min(kb1, (sg + 1) * SEG_KSTEPS);
+                    const int mode = seg_mode(p, sg, ranged ? 1 : 2);
+                    if (mode == 0)
+                        mainloop_fast<GATHER, false, 4, RPL, LA, GTAB ? 0 : AMX_GOFF>(p, panel, bsrc, base, ka, kz, quad, lut, acc);
+                    else if (mode == 1)
+                        mainloop_fast<GATHER, true, 4, RPL, LA>(p, panel, bsrc, base, ka, kz, quad, lut, acc);
+                    else
+                        mainloop_checked<GATHER, RPL>(p, panel, bsrc, base, ka, kz, quad, lut, acc);
+                    ka = kz;
+                }
+            } else {
                 if (ranged) mainloop_fast<GATHER, true, 4, RPL, LA>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
                 else mainloop_checked<GATHER, RPL>(p, panel, bsrc, base, kb0, kb1, quad, lut, acc);
             }
@@ -2193,6 +2246,14 @@ hipError_t launch_decode_group(const DecodeParams* const* jobs, int count, hipSt
     g.first[n] = (uint32_t)blocks;
     hipLaunchKernelGGL(decode_group_kernel, dim3((uint32_t)blocks), dim3(256), bytes, s, g);
     return hipGetLastError();
+}
+
+bool decode_covers_segments(const DecodeParams& p)
+{
+    const DecodeJob jb = plan_decode(p);
+    if (jb.variant == DV_TILE) return true;              // 64 indices of k per workgroup, from a multiple of 64
+    if (jb.variant == DV_ROWS) return p.layout == L_DENSE_UNIFORM && jb.rb > 0 && 64 % jb.rb == 0;
+    return false;
 }
 
 hipError_t launch_decode_pair(const DecodeParams& a, const DecodeParams& b, hipStream_t s)

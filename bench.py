@@ -106,7 +106,36 @@ def traffic_record(workload):
     return rec.get("bytes_per_launch")
 
 
-def build_workload(config, am, torch, mult="table", table_bits=0, gemv=False, gemv_rows=1):
+def per_gemm(args, am, torch):
+    """The MLP workload's GEMMs one at a time: for each, `steps` back-to-back
+    approx_gemm calls on the current stream after `warmup`, timed with
+    events around them (decode, GEMM kernel and reduction of every call)."""
+    from datagen import configs as cfg
+    model, M, _ = cfg.lut_spec(2)
+    lut = am.approx_lut_build(am.MODEL_EXACT if model == "exact" else am.MODEL_MITCHELL, M, None)
+    am.approx_lut_load(lut, M)
+    d = lambda a: torch.from_numpy(a).cuda()
+    dev_layers = [tuple(d(t) for t in L) for L in cfg.mlp_tensors()]
+    for (name, ta, tb, m, n, k, an, bn) in cfg.mlp_gemms():
+        X, W, dY = dev_layers[int(name[-1])]
+        A, B = {"X": X, "W": W, "dY": dY}[an], {"X": X, "W": W, "dY": dY}[bn]
+        C = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        call = (ta, tb, m, n, k, A, A.shape[1], B, B.shape[1], C, n)
+        for _ in range(args.warmup):
+            am.approx_gemm(*call)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            am.approx_gemm(*call)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        print(json.dumps({"gemm": name, "transA": ta, "transB": tb, "m": m, "n": n, "k": k,
+                          "us_per_call": round(us, 2), "T_mac_per_s": round(m * n * k / us / 1e6, 3)}), flush=True)
+
+
+def build_workload(config, am, torch, mult="table", table_bits=0, gemv=False, gemv_rows=1, plant=False):
     from datagen import configs as cfg
     from datagen import PERTURB_SEED, pm_one
 
@@ -130,6 +159,8 @@ def build_workload(config, am, torch, mult="table", table_bits=0, gemv=False, ge
         A, B = cfg.gemm_square(config, size)
         rows = gemv_rows if gemv else size     # --gemv: batch-1 (or few-row) inference through the same B
         A = A[:rows].copy()
+        if plant:
+            A[min(rows - 1, 4321), 5678 % size] = 2.0 ** 126
         Ad, Bd = d(A), d(B)
         Cd = torch.empty((rows, size), dtype=torch.float32, device="cuda")
 
@@ -144,6 +175,8 @@ def build_workload(config, am, torch, mult="table", table_bits=0, gemv=False, ge
             workload = f"gemm_{size}x{size}x{size}_" + ("native_fp32_fma" if mult == "native" else "torch_matmul_fp32")
         if gemv:
             workload = workload.replace(f"gemm_{size}x", f"gemv_{rows}x", 1)
+        if plant:
+            workload += "_one_element_2e126"
         info = dict(m=size, n=size, k=size, table=f"{model} M={M}" + (" +-1 perturbed" if pert is not None else ""))
         if mult != "table":
             info["table"] = "none (native FP32 multiplier)" if mult == "native" else "none (torch.matmul FP32)"
@@ -375,6 +408,13 @@ def main():
     ap.add_argument("--exp-bits", type=int, default=8,
                     help="exponent width E (1-8) of the approximate multiplier's format (1, E, M); operands are "
                          "cast to it before each product (8: FP32, the default)")
+    ap.add_argument("--plant-overflow", action="store_true",
+                    help="with --config 4: set one element of A to 2^126, so that some of its products can "
+                         "overflow (the call's range fails the fast test; only that element's k-segment needs "
+                         "the checked path)")
+    ap.add_argument("--per-gemm", action="store_true",
+                    help="with --config 2: time each of the MLP's 9 GEMMs alone (approx_gemm on one stream, "
+                         "--steps calls each after --warmup) and print one JSON line per GEMM")
     ap.add_argument("--gemv", action="store_true",
                     help="with --config 1 or 4: one row of A (batch-1 inference), the row-vector kernel")
     ap.add_argument("--rows", type=int, default=1,
@@ -427,6 +467,13 @@ def main():
         raise SystemExit("--rows: 1 to 64")
     if not single and (args.gemv or args.table_bits or args.exp_bits != 8 or args.multiplier != "table"):
         raise SystemExit("--gemv, --table-bits, --exp-bits and --multiplier time one workload: give --config")
+    if args.plant_overflow and config != 4:
+        raise SystemExit("--plant-overflow goes with --config 4")
+    if args.per_gemm:
+        if config != 2:
+            raise SystemExit("--per-gemm goes with --config 2")
+        per_gemm(args, am, torch)
+        return
     threads = cpu_threads()
     rec, host = run_one(config, args, am, torch, threads)
     if not single:
@@ -465,7 +512,7 @@ def run_one(config, args, am, torch, threads):
     from datagen import configs as cfg
     log(f"building workload {config} ...")
     step, workload, info, host = build_workload(config, am, torch, args.multiplier, args.table_bits, args.gemv,
-                                                args.rows)
+                                                args.rows, args.plant_overflow)
     if args.exp_bits != 8:
         if args.multiplier != "table":
             raise SystemExit("--exp-bits applies to the table multiplier only")
