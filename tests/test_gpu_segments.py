@@ -7,8 +7,9 @@ must equal, bit for bit, both the same call forced onto the checked path and
 the oracle's FP32 sums in the library's order. Both operand decodes that
 record segments are covered (op(B) copied by rows, and op(B) transposed
 through tiles), as are a route that records none (op(A) transposed), split
-reductions, the table in global memory, and repeated calls (the kernel's last
-workgroup resets the segment ranges).
+reductions, the table in global memory (M = 10), and repeated calls and graph
+replays (the ranges that earlier calls recorded carry another generation tag
+and are never taken as the current call's).
 """
 import os
 
