@@ -217,7 +217,7 @@ struct MainParams {
     int U1, U2, U3, K1, K2, K3;
     int nku, zoff;            // gather mode
     int KB;                   // k-steps of 4 reduction indices (vector) / 4-groups (gather)
-    int wr, wc;               // waves per workgroup along rows / columns (wr*wc = 8)
+    int wr, wc;               // waves per workgroup along rows / columns (wr*wc = the shape's waves)
     int tiles_m, tiles_n;
     // Work items: the first full_items (batch entry, tile) pairs whole, in
     // the order b * tiles + tile; then the remaining tail_tiles pairs in

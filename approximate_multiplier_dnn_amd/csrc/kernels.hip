@@ -132,13 +132,19 @@ __device__ __forceinline__ void put_words(void* dst, int64_t i, const Word (&wd)
             o[0] = make_uint4(wd[0].w, wd[0].se, wd[1].w, wd[1].se);
             if (n == 4) o[1] = make_uint4(wd[2].w, wd[2].se, wd[3].w, wd[3].se);
         } else {
-            for (int t = 0; t < n; ++t) out[t] = wd[t];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)          // constant indices: wd stays in registers
+                if (t < n) out[t] = wd[t];
         }
     } else {
         uint32_t* out = static_cast<uint32_t*>(dst) + i;
         if (vec && n == 4) *reinterpret_cast<uint4*>(out) = make_uint4(wd[0].se, wd[1].se, wd[2].se, wd[3].se);
         else if (vec && n == 2) *reinterpret_cast<uint2*>(out) = make_uint2(wd[0].se, wd[1].se);
-        else for (int t = 0; t < n; ++t) out[t] = wd[t].se;
+        else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (t < n) out[t] = wd[t].se;
+        }
     }
 }
 
@@ -2209,7 +2215,10 @@ static DecodeJob plan_decode(const DecodeParams& p0)
     if (rows && p.batch <= 65535) {
         if (p.layout == L_DY_WGRAD) { p.k = p.N * p.P * p.Q; p.n = p.K; p.ld = p.K; }
         const int rows_out = p.KB * 4;
-        jb.rb = std::max(1, kRowsWgElems / std::max(p.Np, 1));
+        // a power of two up to 64 rows, so that a workgroup's rows lie in one
+        // k-segment (64 reduction indices) whatever the row length
+        jb.rb = 1;
+        while (jb.rb < 64 && 2 * jb.rb * std::max(p.Np, 1) <= kRowsWgElems) jb.rb *= 2;
         return grid(DV_ROWS, (uint32_t)((rows_out + jb.rb - 1) / jb.rb), 1, (uint32_t)p.batch);
     }
     const bool tile = (p.layout == L_DENSE_LANE && !p.trans) || (p.layout == L_DENSE_UNIFORM && p.trans);

@@ -7,6 +7,8 @@ the output columns; products must equal the oracle's bit for bit (k = 1) and
 sums pass the gate of tests/parity.py, for tables in LDS range and beyond it,
 and for the native multiplier.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -44,6 +46,8 @@ def use(am, name):
     if name not in _T:
         if name == "mitchell7":
             _T[name] = (oracle.lut_generate(7, "mitchell"), 7)
+        elif name == "exact7":
+            _T[name] = (oracle.lut_generate(7, "exact"), 7)
         elif name == "perturbed8":
             _T[name] = (oracle.lut_perturb(8, oracle.lut_generate(8, "exact"), pm_one(PERTURB_SEED, 1 << 16)), 8)
         elif name == "arbitrary11":
@@ -126,6 +130,33 @@ def test_gemv_special_b_on_the_fast_path(am, name):
     gnan = np.isnan(got.view(np.float32))
     assert np.array_equal(gnan, np.isnan(want.view(np.float32)))
     assert np.count_nonzero(got[~gnan] != want[~gnan]) == 0
+
+
+@pytest.mark.parametrize("name,m,n,k", [("exact7", 64, 64, 64), ("perturbed8", 48, 8192, 1024),
+                                        ("perturbed8", 1, 8192, 4096), ("mitchell7", 1, 2050, 2048),
+                                        ("mitchell7", 5, 3000, 700), ("arbitrary11", 3, 2000, 900)])
+def test_gemv_fast_and_forced_checked_agree_bitwise(am, name, m, n, k):
+    """The row-vector kernels' fast path (and the one-row kernel's per-window
+    test) against the same call forced onto the per-product checked path:
+    every output bit for bit. N(0, 1) operands, on which every wave takes the
+    fast path unless forced: 64 x 64 x 64 (the smallest bench workload), 48
+    rows with k * n >= 2^22, the one-row kernel, and the table in global
+    memory."""
+    use(am, name)
+    A = dev(normal(9870 + m, (m, k)))
+    B = dev(normal(9871 + m, (k, n)))
+    outs = []
+    for forced in (False, True):
+        C = torch.full((m, n), -5.0, dtype=torch.float32, device="cuda")
+        if forced:
+            os.environ["APPROX_FORCE_CHECKED"] = "1"
+        try:
+            am.approx_gemm(0, 0, m, n, k, A, k, B, n, C, n)
+            outs.append(host(C).view(np.uint32).copy())
+        finally:
+            os.environ.pop("APPROX_FORCE_CHECKED", None)
+    assert np.isfinite(outs[0].view(np.float32)).all()
+    assert np.count_nonzero(outs[0] != outs[1]) == 0, f"{name} {m}x{n}x{k}: fast and checked differ"
 
 
 @pytest.mark.parametrize("name", ["arbitrary1", "arbitrary2", "arbitrary3", "arbitrary5", "arbitrary8"])
