@@ -32,6 +32,11 @@ constexpr int64_t kSplitSlots = 256;
 constexpr double kSplitMacRate = 6.0e12;
 constexpr double kSplitBytesRate = 4.0e12;
 constexpr int kSplitMax = 1024;
+// Fold rate of one workgroup of each shape relative to shape 0's, as the
+// split model takes it. Shape 2 measured at least shape 0's rate where both
+// fill the GPU (M = 7: 2048^3 1.09 against 1.13 ms, 4096 x 4096 x 1024 2.12 ms
+// each), although it loads its uniform words twice as often per MAC.
+constexpr double kShapeFoldRate[amx::kNumShapes] = {1.0, 1.0, 1.0};
 constexpr int64_t kMaxPanelWords = (int64_t)1 << 31;
 // Few-row GEMMs (B not transposed) run in the row-vector kernel, in blocks
 // of 4 rows, instead of the GEMM kernel's 256-row tiles: always up to
@@ -171,7 +176,7 @@ int scratch_get(const ScratchSource& src, int dev, hipStream_t stream, size_t by
 
 // Resident GEMM workgroups per device (CUs x blocks per CU), per kernel
 // variant; queried once per device and kept.
-int64_t g_slots[kMaxDevices][4][2][2];
+int64_t g_slots[kMaxDevices][4][2][amx::kNumShapes];
 
 int64_t launch_slots(int dev, int lds_class, int gather, int shape)
 {
@@ -185,17 +190,17 @@ int64_t launch_slots(int dev, int lds_class, int gather, int shape)
     return s;
 }
 
-// Resident workgroups of the grouped GEMM kernel (8-wave shape, vector mode).
-int64_t g_group_slots[kMaxDevices][4];
+// Resident workgroups of the grouped GEMM kernel (vector mode, shape 0 or 2).
+int64_t g_group_slots[kMaxDevices][4][amx::kNumShapes];
 
-int64_t group_slots(int dev, int lds_class)
+int64_t group_slots(int dev, int lds_class, int shape)
 {
     std::lock_guard<std::mutex> lock(g_mu);
-    int64_t& s = g_group_slots[dev][lds_class];
+    int64_t& s = g_group_slots[dev][lds_class][shape];
     if (s == 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
-        s = (int64_t)cus * amx::main_group_blocks_per_cu(lds_class);
+        s = (int64_t)cus * amx::main_group_blocks_per_cu(lds_class, shape);
     }
     return s;
 }
@@ -253,42 +258,6 @@ int64_t pick_waves(int m, int n, int shape, int* wr, int* wc)
     return best;
 }
 
-// Workgroup shape of a call: the 8-wave shape, unless the 12-wave shape's
-// row tiles (576 rows for 3 x 3 x 64 weight gradients, say) pad the output
-// by at least 10% less; per MAC the 12-wave shape measured about 10% slower
-// (3 x 3 conv forward: 0.720 against 0.653 ms; attention 1.019 against 0.938
-// ms per GEMM launch on average), while its exact 576-row tiles cut the 3 x 3
-// x 64 weight gradient from 1.065 to 0.622 ms.
-// APPROX_KERNEL_SHAPE=0 or 1 forces a shape (for measurements).
-int pick_shape(int m, int n, int* wr, int* wc)
-{
-    int r0, c0, r1, c1;
-    const int64_t a0 = pick_waves(m, n, 0, &r0, &c0);
-    const int64_t a1 = pick_waves(m, n, 1, &r1, &c1);
-    bool twelve = a1 * 10 <= a0 * 9;
-    const char* force = std::getenv("APPROX_KERNEL_SHAPE");
-    if (force != nullptr && (force[0] == '0' || force[0] == '1')) twelve = force[0] == '1';
-    *wr = twelve ? r1 : r0;
-    *wc = twelve ? c1 : c0;
-    return twelve ? 1 : 0;
-}
-
-// Tile geometry of a GEMM-kernel call with an m x n output per batch entry.
-struct Tiling {
-    int shape, wr, wc, TM, TN, tiles_m, tiles_n;
-};
-
-Tiling tiling_of(int m, int n)
-{
-    Tiling t;
-    t.shape = pick_shape(m, n, &t.wr, &t.wc);
-    t.TM = t.wr * 64 * kShapes[t.shape].rows_per_lane;
-    t.TN = t.wc * kColsPerWave;
-    t.tiles_m = (int)cdiv(m, t.TM);
-    t.tiles_n = (int)cdiv(n, t.TN);
-    return t;
-}
-
 // Reduction split. The work items run in rounds over the resident
 // workgroups; a round costs its longest item. Two layouts are modelled:
 //  - every tile split into the same number of chunks (a split trades the
@@ -297,10 +266,10 @@ Tiling tiling_of(int m, int n)
 //  - when the tiles fill at least one round: whole tiles for the full
 //    rounds, and only the tiles of the partial last round split, so that
 //    their chunks fill that round.
-// Picks the layout and split count of least modelled time; ties go to fewer
-// splits and to the uniform layout.
-void plan_split(int64_t tiles, int KB, int64_t tile_macs_per_kstep, int64_t tile_outs, int64_t out_elems,
-                MainParams& mp)
+// Picks the layout and split count of least modelled time (returned); ties go
+// to fewer splits and to the uniform layout.
+double plan_split(int64_t tiles, int KB, double tile_macs_per_kstep, int64_t tile_outs, int64_t out_elems,
+                  MainParams& mp)
 {
     const int smax = std::max(1, std::min(kSplitMax, KB / 2));
     const double kstep_s = (double)tile_macs_per_kstep / (kSplitMacRate / (double)kSplitSlots);
@@ -337,14 +306,68 @@ void plan_split(int64_t tiles, int KB, int64_t tile_macs_per_kstep, int64_t tile
     mp.tail_tiles = (int)tail;
     mp.full_items = (int)(tiles - tail);
     mp.items = (int64_t)mp.full_items + (int64_t)tail * bs;
+    return best;
 }
 
 // The split of a GEMM-kernel call (a function of its tiling, reduction
-// length and batch only).
-void split_of(int tiles_m, int tiles_n, int TM, int TN, int KB, int m, int n, int batch, MainParams& mp)
+// length, batch and workgroup shape only); returns its modelled time.
+double split_of(int tiles_m, int tiles_n, int TM, int TN, int KB, int m, int n, int batch, int shape, MainParams& mp)
 {
     const int64_t tiles = (int64_t)tiles_m * tiles_n * batch;
-    plan_split(tiles, KB, (int64_t)TM * TN * 4, (int64_t)TM * TN, (int64_t)m * n * batch, mp);
+    return plan_split(tiles, KB, (double)TM * TN * 4 / kShapeFoldRate[shape], (int64_t)TM * TN, (int64_t)m * n * batch,
+                      mp);
+}
+
+// Workgroup shape of a call: the 8-wave shape, unless the 12-wave shape's
+// row tiles (576 rows for 3 x 3 x 64 weight gradients, say) pad the output
+// by at least 10% less; per MAC the 12-wave shape measured about 10% slower
+// (3 x 3 conv forward: 0.720 against 0.653 ms; attention 1.019 against 0.938
+// ms per GEMM launch on average), while its exact 576-row tiles cut the 3 x 3
+// x 64 weight gradient from 1.065 to 0.622 ms. A dense call (`dense`: a GEMM,
+// not a convolution) takes shape 2 instead of shape 0 when the split model
+// gives it at least 3% less time: outputs whose 256 x 128 tiles do not fill
+// the GPU, so that shape 0 splits their reductions into many chunks (the
+// MLP's 256 x 1024 x 1024 GEMMs: 16 chunks of 128 x 128 tiles instead of 32
+// of 256 x 128, 64-71 against 69-76 us per call).
+// APPROX_KERNEL_SHAPE=0, 1 or 2 (2: dense calls only) forces a shape (for
+// measurements).
+int pick_shape(int m, int n, bool dense, int KB, int batch, int* wr, int* wc)
+{
+    int r[amx::kNumShapes], c[amx::kNumShapes];
+    const int64_t a0 = pick_waves(m, n, 0, &r[0], &c[0]);
+    const int64_t a1 = pick_waves(m, n, 1, &r[1], &c[1]);
+    pick_waves(m, n, 2, &r[2], &c[2]);
+    int shape = a1 * 10 <= a0 * 9 ? 1 : 0;
+    if (dense && shape == 0 && KB > 0) {
+        auto modelled = [&](int sh) {
+            const int TM = r[sh] * 64 * kShapes[sh].rows_per_lane, TN = c[sh] * kColsPerWave;
+            MainParams tmp{};
+            return split_of((int)cdiv(m, TM), (int)cdiv(n, TN), TM, TN, KB, m, n, batch, sh, tmp);
+        };
+        if (modelled(2) < 0.97 * modelled(0)) shape = 2;
+    }
+    const char* force = std::getenv("APPROX_KERNEL_SHAPE");
+    if (force != nullptr && (force[0] == '0' || force[0] == '1' || (force[0] == '2' && dense))) shape = force[0] - '0';
+    *wr = r[shape];
+    *wc = c[shape];
+    return shape;
+}
+
+// Tile geometry of a GEMM-kernel call with an m x n output per batch entry
+// (KB k-steps; `dense`: see pick_shape).
+struct Tiling {
+    int shape, wr, wc, TM, TN, tiles_m, tiles_n;
+};
+
+Tiling tiling_of(int m, int n, bool dense, int KB, int batch)
+{
+    Tiling t;
+    t.shape = pick_shape(m, n, dense, KB, batch, &t.wr, &t.wc);
+    t.TM = t.wr * 64 * kShapes[t.shape].rows_per_lane;
+    t.TN = t.wc * kColsPerWave;
+    t.tiles_m = (int)cdiv(m, t.TM);
+    t.tiles_n = (int)cdiv(n, t.TN);
+    return t;
 }
 
 // Summation chunk, in positions of the reduction sequence (4 per k-step), of
@@ -355,9 +378,9 @@ struct KernelOrder {
     MainParams mp{};
     int KB = 0;
 
-    KernelOrder(int m, int n, int KB_, int batch) : t(tiling_of(m, n)), KB(KB_)
+    KernelOrder(int m, int n, int KB_, int batch, bool dense) : t(tiling_of(m, n, dense, KB_, batch)), KB(KB_)
     {
-        split_of(t.tiles_m, t.tiles_n, t.TM, t.TN, KB, m, n, batch, mp);
+        split_of(t.tiles_m, t.tiles_n, t.TM, t.TN, KB, m, n, batch, t.shape, mp);
     }
     int64_t chunk(int b, int i, int j) const
     {
@@ -405,7 +428,7 @@ int plan_finalize(Plan& pl, int M)
     // M = 0: native multiplier; M = 9..11: table in global memory
     pl.lds_class = M == 0 ? 2 : M <= 7 ? 0 : M == 8 ? 1 : 3;
     const int64_t TM = (int64_t)mp.wr * 64 * kShapes[pl.shape].rows_per_lane, TN = (int64_t)mp.wc * kColsPerWave;
-    split_of(mp.tiles_m, mp.tiles_n, (int)TM, (int)TN, mp.KB, mp.m_out, mp.n_out, pl.batch, mp);
+    split_of(mp.tiles_m, mp.tiles_n, (int)TM, (int)TN, mp.KB, mp.m_out, mp.n_out, pl.batch, pl.shape, mp);
     pl.wbytes = M == 0 ? 4 : (int)sizeof(Word);     // the native multiplier keeps only the operands' bits
     pl.lane_b = align256((size_t)pl.lane_words * pl.batch * pl.wbytes);
     pl.uni_b = align256((size_t)pl.uni_words * pl.batch * pl.wbytes);
@@ -536,7 +559,7 @@ int run_group(Plan* const* plans, int count, int dev, hipStream_t stream, const 
         }
     }
 
-    const int64_t slots = count == 1 ? launch_slots(dev, lds_class, gather, shape) : group_slots(dev, lds_class);
+    const int64_t slots = count == 1 ? launch_slots(dev, lds_class, gather, shape) : group_slots(dev, lds_class, shape);
     const int grid = (int)std::min<int64_t>(items, slots);
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     bool prof;
@@ -701,7 +724,8 @@ int gemv_run(amx::GemvParams& g, int batch, float* C, int dev, hipStream_t strea
 void build_gemm_plan(int transA, int transB, int m, int n, int k, int batch, Plan& pl)
 {
     pl.batch = batch;
-    const Tiling tg = tiling_of(m, n);
+    const int KB = (int)cdiv(k, 4);
+    const Tiling tg = tiling_of(m, n, true, KB, batch);
     pl.shape = tg.shape;
     MainParams& mp = pl.mp;
     mp.wr = tg.wr;
@@ -709,7 +733,6 @@ void build_gemm_plan(int transA, int transB, int m, int n, int k, int batch, Pla
     mp.tiles_m = tg.tiles_m;
     mp.tiles_n = tg.tiles_n;
     const int Mp = mp.tiles_m * tg.TM, Np = mp.tiles_n * tg.TN;
-    const int KB = (int)cdiv(k, 4);
 
     DecodeParams& a = pl.lane;
     a.layout = amx::L_DENSE_LANE;
@@ -882,7 +905,7 @@ int build_conv_plan(ConvKind kind, const ConvShape& s, Plan& pl)
 
     int m, n;
     conv_gemm_extent(kind, s, &m, &n);
-    const Tiling tg = tiling_of(m, n);
+    const Tiling tg = tiling_of(m, n, false, 0, 1);
     pl.shape = tg.shape;
     mp.wr = tg.wr;
     mp.wc = tg.wc;
@@ -1307,7 +1330,8 @@ extern "C" int approx_gemm_grouped(int count, const int* transA, const int* tran
         pl.mp.ldc = ldc[g];
         pl.lane.ld = lda[g];
         pl.uni.ld = ldb[g];
-        if (!amx::main_group_supported(pl.gather, pl.shape)) {
+        // one launch holds calls of one shape: the first grouped member's
+        if (!amx::main_group_supported(pl.gather, pl.shape) || (ng > 0 && pl.shape != grouped[0]->shape)) {
             rc = run_plan(pl, dev, stream, image, M, ScratchSource{});
             if (rc != APPROX_OK) return rc;
             continue;
@@ -1392,7 +1416,7 @@ extern "C" int approx_gemm_chunks(int transA, int transB, int m, int n, int k, i
         for (long long t = 0; t < count; ++t) chunk[t] = g.splits > 1 ? g.chunk : k;
         return APPROX_OK;
     }
-    const KernelOrder ord(m, n, (int)cdiv(k, 4), batch);
+    const KernelOrder ord(m, n, (int)cdiv(k, 4), batch, true);
     for (long long t = 0; t < count; ++t) chunk[t] = std::min<int64_t>(ord.chunk(b[t], i[t], j[t]), k);
     return APPROX_OK;
 }
@@ -1412,7 +1436,7 @@ extern "C" int approx_conv2d_chunks(int pass, int N, int H, int W, int C, int K,
     conv_gemm_extent(kind, s, &m, &n);
     for (long long t = 0; t < count; ++t)
         if (idx[t] < 0 || idx[t] >= (long long)m * n) return APPROX_EINVAL;
-    const KernelOrder ord(m, n, conv_ksteps(kind, s), 1);
+    const KernelOrder ord(m, n, conv_ksteps(kind, s), 1, false);
     for (long long t = 0; t < count; ++t) chunk[t] = ord.chunk(0, (int)(idx[t] / n), (int)(idx[t] % n));
     return APPROX_OK;
 }

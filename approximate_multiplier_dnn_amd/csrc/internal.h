@@ -30,11 +30,14 @@ struct Word {
 // accumulating `rows_per_lane` output rows x kColsPerWave columns, so a wave
 // covers 64 * rows_per_lane rows and kColsPerWave columns. Shape 0: 8 waves
 // (2 per SIMD) x 4 rows; shape 1: 12 waves (3 per SIMD) x 3 rows, which hides
-// more lookup latency at the cost of coarser row tiles.
+// more lookup latency at the cost of coarser row tiles; shape 2: 8 waves x 2
+// rows, tiles of half the area of shape 0's for small dense GEMMs, whose
+// reductions then split into half as many chunks (dense calls only).
 struct KernelShape {
     int waves, rows_per_lane;
 };
-constexpr KernelShape kShapes[2] = {{8, 4}, {12, 3}};
+constexpr int kNumShapes = 3;
+constexpr KernelShape kShapes[kNumShapes] = {{8, 4}, {12, 3}, {8, 2}};
 constexpr int kColsPerWave = 16;
 
 // Table image in device memory, laid out as the LDS copy the kernels use.
@@ -335,7 +338,7 @@ hipError_t launch_main_group(const MainParams* const* ps, int count, int lds_cla
 // Whether several calls of this variant can share a launch (count > 1), and
 // the resident workgroups per CU of that grouped kernel.
 bool main_group_supported(int gather, int shape);
-int main_group_blocks_per_cu(int lds_class);
+int main_group_blocks_per_cu(int lds_class, int shape);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 
 // The reduction runs 16 lanes per 4 outputs (reduce_rows_kernel) when the

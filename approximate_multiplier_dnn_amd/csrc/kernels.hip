@@ -2294,27 +2294,38 @@ static const void* main_variant_shape(int lds_class, int gather)
     }
 }
 
+// Dense calls (operands in vector mode) only: the variants of shape S.
+template <int S, bool GROUP>
+static const void* main_variant_dense(int lds_class)
+{
+    constexpr int NW = kShapes[S].waves, R = kShapes[S].rows_per_lane;
+    switch (lds_class) {
+    case 0: return (const void*)main_kernel<LDS_SMALL, false, false, NW, R, false, GROUP>;
+    case 1: return (const void*)main_kernel<LDS_LARGE, false, false, NW, R, false, GROUP>;
+    case 2: return (const void*)main_kernel<NATIVE_LDS, false, true, NW, R, false, GROUP>;
+    default: return (const void*)main_kernel<NATIVE_LDS, false, false, NW, R, true, GROUP>;
+    }
+}
+
+// (shape 2 is never planned for a gather-mode call)
 static const void* main_variant(int lds_class, int gather, int shape)
 {
+    if (shape == 2) return gather ? nullptr : main_variant_dense<2, false>(lds_class);
     return shape == 0 ? main_variant_shape<0>(lds_class, gather) : main_variant_shape<1>(lds_class, gather);
 }
 
-// Grouped launches: the 8-wave shape, operands in vector mode (dense GEMMs).
-bool main_group_supported(int gather, int shape) { return gather == 0 && shape == 0; }
+// Grouped launches: operands in vector mode (dense GEMMs), shape 0 or 2, one
+// shape per launch.
+bool main_group_supported(int gather, int shape) { return gather == 0 && (shape == 0 || shape == 2); }
 
-static const void* main_group_variant(int lds_class)
+static const void* main_group_variant(int lds_class, int shape)
 {
-    constexpr int NW = kShapes[0].waves, R = kShapes[0].rows_per_lane;
-    switch (lds_class) {
-    case 0: return (const void*)main_kernel<LDS_SMALL, false, false, NW, R, false, true>;
-    case 1: return (const void*)main_kernel<LDS_LARGE, false, false, NW, R, false, true>;
-    case 2: return (const void*)main_kernel<NATIVE_LDS, false, true, NW, R, false, true>;
-    default: return (const void*)main_kernel<NATIVE_LDS, false, false, NW, R, true, true>;
-    }
+    return shape == 2 ? main_variant_dense<2, true>(lds_class) : main_variant_dense<0, true>(lds_class);
 }
 
 hipError_t launch_main(const MainParams& p, int lds_class, int gather, int shape, int grid, hipStream_t s)
 {
+    if (shape < 0 || shape >= kNumShapes || main_variant(lds_class, gather, shape) == nullptr) return hipErrorInvalidValue;
     MainParams arg = p;
     void* args[] = {&arg};
     return hipLaunchKernel(main_variant(lds_class, gather, shape), dim3(grid), dim3(kShapes[shape].waves * 64), args,
@@ -2338,14 +2349,15 @@ hipError_t launch_main_group(const MainParams* const* ps, int count, int lds_cla
     arg.count = count;
     arg.first[count] = (int)total;
     void* args[] = {&arg};
-    return hipLaunchKernel(main_group_variant(lds_class), dim3(grid), dim3(kShapes[0].waves * 64), args, 0, s);
+    return hipLaunchKernel(main_group_variant(lds_class, shape), dim3(grid), dim3(kShapes[shape].waves * 64), args, 0,
+                           s);
 }
 
-int main_group_blocks_per_cu(int lds_class)
+int main_group_blocks_per_cu(int lds_class, int shape)
 {
     int n = 0;
-    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, main_group_variant(lds_class),
-                                                                      kShapes[0].waves * 64, 0);
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, main_group_variant(lds_class, shape),
+                                                                      kShapes[shape].waves * 64, 0);
     if (e != hipSuccess || n < 1) n = 1;
     return n;
 }

@@ -118,3 +118,43 @@ def test_row_vector_group_rows_stay_inside_the_item():
                     want = np.minimum(kg + np.arange(ng), k1 - 1)
                     assert np.array_equal(got, want), (k0, k1, kg, ng, list(got))
     assert f(0, 0, 4, rows.ctypes.data) == -1
+
+
+@pytest.mark.parametrize("shape", ["0", "1", "2"])
+def test_gemm_plans_of_every_forced_shape_stay_inside(check, shape, monkeypatch):
+    """The same GEMM cases with each workgroup shape forced
+    (APPROX_KERNEL_SHAPE), at a table in LDS and one in global memory."""
+    monkeypatch.setenv("APPROX_KERNEL_SHAPE", shape)
+    for M in (7, 8, 10):
+        for args in _gemm_cases():
+            check(0, args, M)
+
+
+def _plan_info(kind, args, M):
+    import approximate_multiplier_dnn_amd as am
+    f = am.lib().amx_plan_info
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_longlong
+    a = np.zeros(12, np.int32)
+    a[:len(args)] = args
+    out = np.zeros(12, np.int32)
+    items = f(kind, a.ctypes.data, M, out.ctypes.data)
+    assert items >= 0, (kind, args, M, items)
+    return int(items), out
+
+
+def test_shape_choice_follows_the_split_model():
+    """Small dense GEMMs (the MLP's) take the 128 x 128 tiles of shape 2 and
+    half as many reduction chunks as shape 0 would cut; GEMMs whose 256 x 128
+    tiles fill the GPU keep shape 0; convolutions never take shape 2."""
+    _, o = _plan_info(0, (0, 0, 256, 1024, 1024, 1), 7)
+    assert (o[0], o[3], o[4], o[8]) == (2, 128, 128, 16), list(o)
+    _, o = _plan_info(0, (1, 0, 1024, 1024, 256, 1), 7)
+    assert o[0] == 2, list(o)
+    for args in ((0, 0, 8192, 8192, 8192, 1), (0, 0, 4096, 4096, 1024, 1)):
+        _, o = _plan_info(0, args, 8)
+        assert o[0] == 0, (args, list(o))
+    for args in _conv_cases():
+        for kind in (1, 2, 3):
+            _, o = _plan_info(kind, args, 7)
+            assert o[0] in (0, 1), (kind, args, list(o))
