@@ -1226,15 +1226,22 @@ struct MainGroup {
     MainParams p[kMaxGroup];
 };
 
-// Exponent-range test of one call from its stats slots (every wave folds
-// them itself: the table takes all of the LDS at M = 8, so the range is not
-// broadcast through it). fast: no product can leave the format's range;
-// ranged: some may fall below it (none above); otherwise the checked path.
-template <bool NATIVE>
-__device__ __forceinline__ void fold_stats(const MainParams& p, bool& fast, bool& ranged)
+// This lane's slot of a call's exponent stats (a wave holds all 64 slots).
+__device__ __forceinline__ int4 stats_slot(const MainParams& p)
 {
     const int* sl = p.stats + ((threadIdx.x & 63) % STAT_SLOTS) * STAT_STRIDE;
-    int v0 = sl[0], v1 = sl[1], v2 = sl[2], v3 = sl[3];
+    return make_int4(sl[0], sl[1], sl[2], sl[3]);
+}
+
+// Exponent-range test of one call from its stats slots, as loaded by
+// stats_slot (every wave folds them itself: the table takes all of the LDS at
+// M = 8, so the range is not broadcast through it). fast: no product can
+// leave the format's range; ranged: some may fall below it (none above);
+// otherwise the checked path.
+template <bool NATIVE>
+__device__ __forceinline__ void fold_stats(const MainParams& p, const int4& slot, bool& fast, bool& ranged)
+{
+    int v0 = slot.x, v1 = slot.y, v2 = slot.z, v3 = slot.w;
     for (int off = 32; off > 0; off >>= 1) {
         v0 = min(v0, __shfl_xor(v0, off, 64));
         v1 = max(v1, __shfl_xor(v1, off, 64));
@@ -1315,6 +1322,22 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainArg<GROUP> grp)
     constexpr int LA = GTAB ? LA_GLOBAL : LA_LDS;
     __shared__ __align__(16) unsigned char lds_tab[LDSB];
     const MainParams& p0 = call_params<GROUP>(grp, 0);
+    const int G = gridDim.x;
+    // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin (block
+    // b runs on XCD b % 8, checked with HW_REG_XCC_ID), so give the workgroups
+    // of one XCD consecutive work items: they share operand rows in its L2.
+    // (A bijection of the block index: with the items of a call consecutive,
+    // min(G, its items) workgroups read its stats.)
+    const int v = (G & 7) == 0 ? (int)((blockIdx.x & 7u) * (unsigned)(G >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
+    int items, cur = -1;                           // cur: the call whose stats this workgroup has folded
+    if constexpr (GROUP) items = grp.first[grp.count];
+    else items = (int)grp.items;
+    // the stats of the first item's call, requested before the table copy so
+    // that the two loads' latencies overlap
+    int g0 = 0;
+    if constexpr (GROUP)
+        while (g0 + 1 < grp.count && v >= (int)grp.first[g0 + 1]) ++g0;
+    const int4 slot0 = v < items ? stats_slot(call_params<GROUP>(grp, g0)) : make_int4(0, 0, 0, 0);
     if (!NATIVE && !GTAB) {
         const uint4* src = reinterpret_cast<const uint4*>(p0.lut);
         uint4* dst = reinterpret_cast<uint4*>(lds_tab);
@@ -1326,17 +1349,8 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainArg<GROUP> grp)
     else lut = lds_tab;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const uint32_t quad = (uint32_t)lane & 3u;     // this lane's place in the uniform-word quads
-    const int G = gridDim.x;
-    // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin (block
-    // b runs on XCD b % 8, checked with HW_REG_XCC_ID), so give the workgroups
-    // of one XCD consecutive work items: they share operand rows in its L2.
-    // (A bijection of the block index: with the items of a call consecutive,
-    // min(G, its items) workgroups read its stats.)
-    const int v = (G & 7) == 0 ? (int)((blockIdx.x & 7u) * (unsigned)(G >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
-    int items, cur = -1;                           // cur: the call whose stats this workgroup has folded
-    if constexpr (GROUP) items = grp.first[grp.count];
-    else items = (int)grp.items;
     bool fast = false, ranged = false;
+    uint32_t folded = 0;                           // the calls whose stats this workgroup has read
 
     for (int item = v; item < items; item += G) {
         int g = 0, first = 0, count = items;
@@ -1347,9 +1361,9 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainArg<GROUP> grp)
         }
         const MainParams& p = call_params<GROUP>(grp, g);
         if (g != cur) {                            // uniform: every wave of the workgroup enters together
-            fold_stats<NATIVE>(p, fast, ranged);
+            fold_stats<NATIVE>(p, cur < 0 ? slot0 : stats_slot(p), fast, ranged);
             __syncthreads();                       // the table is staged; every wave has read the stats
-            if (threadIdx.x < 64) release_stats(p, min(G, count));
+            folded |= 1u << g;
             cur = g;
         }
         const int wrow = wave / p.wc, wcol = wave - wrow * p.wc;
@@ -1446,6 +1460,18 @@ __global__ __launch_bounds__(NW * 64, 1) void main_kernel(MainArg<GROUP> grp)
                         if (col0 + j < p.n_out) o[j] = acc[x][j];
                 }
             }
+        }
+    }
+    // Release the stats of the calls this workgroup read, after its last
+    // item rather than at the first (the release's atomic round trip then
+    // holds back no wave's k-loop); every wave read them before the barrier
+    // that followed its fold.
+    if (threadIdx.x < 64) {
+        if constexpr (GROUP) {
+            for (int g = 0; g < grp.count; ++g)
+                if ((folded >> g) & 1u) release_stats(grp.p[g], min(G, (int)(grp.first[g + 1] - grp.first[g])));
+        } else {
+            if (folded & 1u) release_stats(grp, min(G, items));
         }
     }
 }
