@@ -177,7 +177,7 @@ struct DecodeParams {
 
 // One operand's decode in a combined launch: the variant for its layout and
 // its own grid of 256-thread workgroups.
-enum DecodeVariant : int { DV_IMG = 0, DV_ROWS, DV_TILE, DV_GENERIC };
+enum DecodeVariant : int { DV_IMG = 0, DV_ROWS, DV_TILE, DV_GENERIC, DV_DIRECT };
 struct DecodeJob {
     DecodeParams p;
     int variant;

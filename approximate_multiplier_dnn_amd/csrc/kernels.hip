@@ -479,6 +479,61 @@ __device__ __forceinline__ void decode_tile_body(const DecodeParams& p, uint3 bi
                 p.seg_gen);
 }
 
+// The same two layouts without the trip through LDS, for small operands
+// (panels of at most kDirectElems words over all batch entries): thread t of
+// batch entry b takes k-step kb
+// = t / outer of row (lane) or column (uniform) o = t % outer of the panel,
+// reads its 4 source elements (16 bytes where aligned) and writes their 4
+// Words: 32 contiguous bytes at (kb, o) of [KB][Mp][4] (lane), or one Word in
+// each of the rows 4 kb .. 4 kb + 3 of [Kp][Np] (uniform; consecutive threads
+// write consecutive columns). A workgroup's 256 threads lie in one k-segment
+// (64 indices): outer is a multiple of 16, so 16 * outer is one of 256.
+// One load, decode and store per thread: for such operands the transposing
+// tile's LDS round trip and barrier were most of the launch's time.
+constexpr int64_t kDirectElems = (int64_t)1 << 22;
+
+__device__ __forceinline__ void decode_direct_body(const DecodeParams& p, uint3 bid, uint3 gdim)
+{
+    int emin = 255, emax = 0;
+    const int b = (int)bid.y;
+    const float* src = p.src_ptrs ? p.src_ptrs[b] : p.src + b * p.src_batch_stride;
+    const int64_t d0 = b * p.dst_batch_stride;
+    const bool lane = p.layout == L_DENSE_LANE;
+    const int outer = lane ? p.Mp : p.Np;          // panel rows (lane) or columns (uniform)
+    const int outer_n = lane ? p.m : p.n;          // of which hold source elements
+    const uint32_t t0 = bid.x * 256u;
+    const uint32_t t = t0 + threadIdx.x;
+    const uint32_t kb = fdiv(t, lane ? p.fd_Mp : p.fd_Np), o = t - kb * (uint32_t)outer;
+    if (kb < (uint32_t)p.KB) {
+        const int k0 = (int)kb * 4;
+        const bool in = (int)o < outer_n;
+        const float* s = src + (int64_t)o * p.ld + k0;
+        float v[4];
+        if (in && k0 + 3 < p.k && ((reinterpret_cast<uintptr_t>(s) & 15u) == 0)) {
+            const float4 q = *reinterpret_cast<const float4*>(s);
+            v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = (in && k0 + u < p.k) ? s[u] : 0.0f;
+        }
+        const int role = lane ? 1 : 0;
+        Word wd[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            wd[u] = (in && k0 + u < p.k) ? decode_bits(__float_as_uint(v[u]), p.M, role, emin, emax, p.elo, p.ehi)
+                                         : zero_word(p.M, role);
+        if (lane) {
+            put_words(p.dst, d0 + (int64_t)kb * p.ldw + (int64_t)o * 4, wd, 4, true, p.wbytes);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) put_word(p.dst, d0 + (int64_t)(k0 + u) * p.ldw + o, wd[u], p.wbytes);
+        }
+    }
+    const uint32_t seg = fdiv(t0, lane ? p.fd_Mp : p.fd_Np) >> 4;   // the workgroup's k-segment
+    flush_stats(p.stats, emin, emax, linear_block(bid, gdim), p.seg ? p.seg + 4 * SEG_REPL * seg : nullptr,
+                p.seg_gen);
+}
+
 // Empty slots: min 255, max 0 (lane and uniform), and no readers yet.
 __device__ __forceinline__ int stat_reset_value(int i) { return (i & 1) ? 0 : 255; }
 
@@ -544,6 +599,7 @@ __device__ __forceinline__ void decode_job(const DecodeJob& jb, uint32_t blk, fl
     case DV_IMG: decode_img_body(jb.p, bid, gdim, smem); break;
     case DV_ROWS: decode_rows_body(jb.p, bid, gdim, jb.rb); break;
     case DV_TILE: decode_tile_body(jb.p, bid, gdim, smem); break;
+    case DV_DIRECT: decode_direct_body(jb.p, bid, gdim); break;
     default: decode_generic_body(jb.p, bid, gdim); break;
     }
 }
@@ -2248,6 +2304,9 @@ static DecodeJob plan_decode(const DecodeParams& p0)
         return grid(DV_ROWS, (uint32_t)((rows_out + jb.rb - 1) / jb.rb), 1, (uint32_t)p.batch);
     }
     const bool tile = (p.layout == L_DENSE_LANE && !p.trans) || (p.layout == L_DENSE_UNIFORM && p.trans);
+    const int64_t outer = p.layout == L_DENSE_LANE ? p.Mp : p.Np;
+    if (tile && p.batch <= 65535 && outer % 16 == 0 && outer * p.KB * 4 * p.batch <= kDirectElems)
+        return grid(DV_DIRECT, (uint32_t)((outer * p.KB + 255) / 256), (uint32_t)p.batch, 1);
     if (tile && p.batch <= 65535) {
         const int outer = p.layout == L_DENSE_LANE ? p.Mp : p.Np;
         const int kext = p.KB * 4;
@@ -2287,6 +2346,7 @@ bool decode_covers_segments(const DecodeParams& p)
 {
     const DecodeJob jb = plan_decode(p);
     if (jb.variant == DV_TILE) return true;              // 64 indices of k per workgroup, from a multiple of 64
+    if (jb.variant == DV_DIRECT) return true;            // a workgroup's threads lie in one k-segment
     if (jb.variant == DV_ROWS) return p.layout == L_DENSE_UNIFORM && jb.rb > 0 && 64 % jb.rb == 0;
     return false;
 }
