@@ -582,6 +582,9 @@ int run_group(Plan* const* plans, int count, int dev, hipStream_t stream, const 
         g_events.emplace_back(ev0, ev1);
     }
 
+    // the members' reductions, in one launch
+    amx::ReduceJob red[amx::kMaxGroup];
+    int nred = 0;
     for (int g = 0; g < count; ++g) {
         const Plan& pl = *plans[g];
         const MainParams& mp = pl.mp;
@@ -597,7 +600,7 @@ int run_group(Plan* const* plans, int count, int dev, hipStream_t stream, const 
             rp.splits = mp.splits;
             rp.batch = pl.batch;
             rp.out_batch = pl.strideC;
-            if (amx::launch_reduce(rp, stream) != hipSuccess) return APPROX_EHIP;
+            red[nred++] = amx::reduce_job(rp);
         } else {                                   // only the tail tiles are split
             amx::ReduceTilesParams rp{};
             rp.ws = mp.ws;
@@ -614,8 +617,15 @@ int run_group(Plan* const* plans, int count, int dev, hipStream_t stream, const 
             rp.TN = mp.wc * kColsPerWave;
             rp.first_tile = mp.full_items;
             rp.n_tiles = mp.tail_tiles;
-            if (amx::launch_reduce_tiles(rp, stream) != hipSuccess) return APPROX_EHIP;
+            red[nred++] = amx::reduce_tiles_job(rp);
         }
+    }
+    if (nred == 1 && red[0].variant != amx::RV_TILES) {
+        if (amx::launch_reduce(red[0].r, stream) != hipSuccess) return APPROX_EHIP;
+    } else if (nred == 1) {
+        if (amx::launch_reduce_tiles(red[0].t, stream) != hipSuccess) return APPROX_EHIP;
+    } else if (nred > 1) {
+        if (amx::launch_reduce_group(red, nred, stream) != hipSuccess) return APPROX_EHIP;
     }
     return APPROX_OK;
 }

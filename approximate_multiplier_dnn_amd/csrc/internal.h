@@ -271,6 +271,17 @@ struct ReduceTilesParams {
     int first_tile, n_tiles;
 };
 
+// One call's reduction as a part of a combined launch: the variant (plain:
+// a thread per 4 outputs; rows: 16 lanes per 4 outputs; tiles: the split
+// tiles only), its parameters and its workgroups.
+enum ReduceVariant : int { RV_PLAIN = 0, RV_ROWS, RV_TILES };
+struct ReduceJob {
+    int variant;
+    uint32_t blocks;
+    ReduceParams r;           // plain and rows
+    ReduceTilesParams t;      // tiles
+};
+
 // Row-vector GEMM (few rows of op(A): up to 32, or 64 when k * n >= 2^22 or
 // k * n <= 2^16; B not transposed), one launch of a persistent grid: a work
 // item is a block of kGemvMaxRows rows x a column block x a reduction chunk
@@ -350,6 +361,11 @@ inline bool reduce_by_rows(int m, int n, int batch, int splits)
     return ((int64_t)m * n) % 4 == 0 && total < ((int64_t)1 << 18) && splits >= 16;
 }
 hipError_t launch_reduce_tiles(const ReduceTilesParams& p, hipStream_t s);
+// The reductions of several calls (their jobs, as reduce_job and
+// reduce_tiles_job plan them) in one launch; count <= kMaxGroup.
+ReduceJob reduce_job(const ReduceParams& p);
+ReduceJob reduce_tiles_job(const ReduceTilesParams& p);
+hipError_t launch_reduce_group(const ReduceJob* jobs, int count, hipStream_t s);
 hipError_t launch_fill_zero(float* C, float* const* Cp, int m, int n, int ldc, int batch, int64_t strideC,
                             hipStream_t s);
 int main_blocks_per_cu(int lds_class, int gather, int shape);

@@ -2086,13 +2086,15 @@ __global__ __launch_bounds__(kGemv1Threads) void gemv1_kernel(GemvParams p)
 // partials of one batch entry hold a multiple of 4 values, each thread sums 4
 // consecutive outputs with 16-byte loads; the loads of 8 splits are issued
 // ahead of their (ordered) adds.
-__global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p)
+// The bodies below take the workgroup's index and the number of workgroups
+// of their own part of the grid (a reduction launch may hold several).
+__device__ __forceinline__ void reduce_body(const ReduceParams& p, uint32_t blk, uint32_t nblk)
 {
     const int64_t mn = (int64_t)p.m * p.n;
     const bool quad = (mn & 3) == 0;
     const int64_t units = quad ? mn / 4 : mn;
     const int64_t total = units * p.batch;
-    for (int64_t g = blockIdx.x * 256LL + threadIdx.x; g < total; g += (int64_t)gridDim.x * 256) {
+    for (int64_t g = blk * 256LL + threadIdx.x; g < total; g += (int64_t)nblk * 256) {
         const int64_t b = g / units, u = g - b * units;
         float* out = p.out_ptrs ? p.out_ptrs[b] : p.out + b * p.out_batch;
         if (quad) {
@@ -2122,6 +2124,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p)
     }
 }
 
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) { reduce_body(p, blockIdx.x, gridDim.x); }
+
 // Few outputs with many chunk partials each (the row-vector kernel's
 // splits): 16 lanes (one DPP row) per 4 consecutive outputs. Lane l of a row
 // requests partials l, l + 16, ... of its 4 outputs together; the row then
@@ -2146,11 +2150,11 @@ __device__ __forceinline__ void row_chain(v4f& s, const v4f& v, std::integer_seq
      ...);
 }
 
-__global__ __launch_bounds__(256) void reduce_rows_kernel(ReduceParams p)
+__device__ __forceinline__ void reduce_rows_body(const ReduceParams& p, uint32_t blk)
 {
     const int64_t mn = (int64_t)p.m * p.n;       // a multiple of 4
     const int64_t units = mn / 4;
-    const int64_t unit = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+    const int64_t unit = ((int64_t)blk * 256 + threadIdx.x) >> 4;
     if (unit >= units * p.batch) return;          // the 16 lanes of a row leave together
     const int l = threadIdx.x & 15;
     const int64_t b = unit / units, u = unit - b * units;
@@ -2178,17 +2182,19 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(ReduceParams p)
     }
 }
 
+__global__ __launch_bounds__(256) void reduce_rows_kernel(ReduceParams p) { reduce_rows_body(p, blockIdx.x); }
+
 // The split tiles' outputs: C = sum of their chunk partials in ascending
 // split order, from +0. Thread unit = 4 consecutive columns of one tile row
 // (16-byte loads when the rows are 4-float aligned and the 4 are inside).
-__global__ __launch_bounds__(256) void reduce_tiles_kernel(ReduceTilesParams p)
+__device__ __forceinline__ void reduce_tiles_body(const ReduceTilesParams& p, uint32_t blk, uint32_t nblk)
 {
     const int quads = p.TN / 4;
     const int64_t per_tile = (int64_t)p.TM * quads;
     const int64_t total = per_tile * p.n_tiles;
     const int tiles = p.tiles_m * p.tiles_n;
     const int64_t mn = (int64_t)p.m * p.n;
-    for (int64_t g = blockIdx.x * 256LL + threadIdx.x; g < total; g += (int64_t)gridDim.x * 256) {
+    for (int64_t g = blk * 256LL + threadIdx.x; g < total; g += (int64_t)nblk * 256) {
         const int tt = (int)(g / per_tile);
         const int q = (int)(g - (int64_t)tt * per_tile);
         const int tl = p.first_tile + tt;
@@ -2219,6 +2225,30 @@ __global__ __launch_bounds__(256) void reduce_tiles_kernel(ReduceTilesParams p)
                 if (t < nt) out[t] = sum[t];
         }
     }
+}
+
+__global__ __launch_bounds__(256) void reduce_tiles_kernel(ReduceTilesParams p)
+{
+    reduce_tiles_body(p, blockIdx.x, gridDim.x);
+}
+
+// The reductions of up to kMaxGroup calls in one launch (a grouped call's
+// members): job j takes workgroups [first[j], first[j + 1]).
+struct ReduceGroup {
+    int count;
+    uint32_t first[kMaxGroup + 1];
+    ReduceJob job[kMaxGroup];
+};
+
+__global__ __launch_bounds__(256) void reduce_group_kernel(ReduceGroup g)
+{
+    int j = 0;
+    while (j + 1 < g.count && blockIdx.x >= g.first[j + 1]) ++j;
+    const ReduceJob& jb = g.job[j];
+    const uint32_t blk = blockIdx.x - g.first[j], nblk = g.first[j + 1] - g.first[j];
+    if (jb.variant == RV_ROWS) reduce_rows_body(jb.r, blk);
+    else if (jb.variant == RV_TILES) reduce_tiles_body(jb.t, blk, nblk);
+    else reduce_body(jb.r, blk, nblk);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* C, float* const* Cp, int m, int n, int ldc, int batch,
@@ -2488,24 +2518,64 @@ hipError_t launch_gemv(const GemvParams& p, int variant, int grid, hipStream_t s
     return hipLaunchKernel(gemv_variant(variant), dim3(grid), dim3(gemv_threads(variant)), args, 0, s);
 }
 
-hipError_t launch_reduce(const ReduceParams& p, hipStream_t s)
+ReduceJob reduce_job(const ReduceParams& p)
 {
-    const int64_t mn = (int64_t)p.m * p.n;
-    const int64_t total = mn * p.batch;
+    ReduceJob jb{};
+    jb.r = p;
+    const int64_t total = (int64_t)p.m * p.n * p.batch;
     // few outputs (fewer than 64 Ki threads' worth of 4) and many splits:
     // 16 lanes per 4 outputs; one workgroup of 256 lanes per 64 outputs
     if (reduce_by_rows(p.m, p.n, p.batch, p.splits)) {
-        hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)((total + 63) / 64)), dim3(256), 0, s, p);
+        jb.variant = RV_ROWS;
+        jb.blocks = (uint32_t)((total + 63) / 64);
     } else {
-        hipLaunchKernelGGL(reduce_kernel, dim3(grid_for(total, 256, 16384)), dim3(256), 0, s, p);
+        jb.variant = RV_PLAIN;
+        jb.blocks = (uint32_t)grid_for(total, 256, 16384);
     }
+    return jb;
+}
+
+ReduceJob reduce_tiles_job(const ReduceTilesParams& p)
+{
+    ReduceJob jb{};
+    jb.t = p;
+    jb.variant = RV_TILES;
+    jb.blocks = (uint32_t)grid_for((int64_t)p.TM * (p.TN / 4) * p.n_tiles, 256, 16384);
+    return jb;
+}
+
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t s)
+{
+    const ReduceJob jb = reduce_job(p);
+    if (jb.variant == RV_ROWS) hipLaunchKernelGGL(reduce_rows_kernel, dim3(jb.blocks), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(reduce_kernel, dim3(jb.blocks), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_reduce_tiles(const ReduceTilesParams& p, hipStream_t s)
 {
-    const int64_t total = (int64_t)p.TM * (p.TN / 4) * p.n_tiles;
-    hipLaunchKernelGGL(reduce_tiles_kernel, dim3(grid_for(total, 256, 16384)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(reduce_tiles_kernel, dim3(reduce_tiles_job(p).blocks), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_group(const ReduceJob* jobs, int count, hipStream_t s)
+{
+    if (count < 1 || count > kMaxGroup) return hipErrorInvalidValue;
+    ReduceGroup g{};
+    uint64_t blocks = 0;
+    int n = 0;
+    for (int i = 0; i < count; ++i) {
+        if (jobs[i].blocks == 0) continue;
+        g.job[n] = jobs[i];
+        g.first[n] = (uint32_t)blocks;
+        blocks += jobs[i].blocks;
+        if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+        ++n;
+    }
+    if (n == 0) return hipSuccess;
+    g.count = n;
+    g.first[n] = (uint32_t)blocks;
+    hipLaunchKernelGGL(reduce_group_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
