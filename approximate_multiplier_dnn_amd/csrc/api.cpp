@@ -644,10 +644,17 @@ constexpr int64_t kGemvTargetThreads = 256 * 1024;
 
 int64_t g_gemv_slots[kMaxDevices][5];
 
-int gemv_variant_of(int M, int m)
+// Row-vector kernel variant of a call: the native multiplier (3); one row at
+// M <= 8 (4: table rows staged per window); at most 256 columns (2: the
+// 256-thread kernel reading the table from global memory, since a 1024-thread
+// workgroup that stages the whole table would leave 15 of 16 lanes without a
+// column of their own); else the table in LDS (0: M <= 7, 1: M = 8) or in
+// global memory (2: M = 9..11).
+int gemv_variant_of(int M, int m, int n)
 {
     if (M == 0) return 3;
     if (m == 1 && M <= 8) return 4;
+    if (n <= 256) return 2;
     return M <= 7 ? 0 : M == 8 ? 1 : 2;
 }
 
@@ -655,7 +662,7 @@ int gemv_variant_of(int M, int m)
 // the work items (column blocks x row blocks x splits x batch).
 int64_t gemv_split(amx::GemvParams& g, int batch)
 {
-    const int variant = gemv_variant_of(g.M, g.m);
+    const int variant = gemv_variant_of(g.M, g.m, g.n);
     const int cols = amx::gemv_threads(variant) * amx::kGemvColsPerLane;
     const int64_t blocks = cdiv(g.n, cols) * cdiv(g.m, amx::kGemvMaxRows) * batch;
     const int64_t target = kGemvTargetThreads / amx::gemv_threads(variant);
@@ -669,7 +676,7 @@ int64_t gemv_split(amx::GemvParams& g, int batch)
 
 int gemv_run(amx::GemvParams& g, int batch, float* C, int dev, hipStream_t stream, const ScratchSource& src)
 {
-    const int variant = gemv_variant_of(g.M, g.m);
+    const int variant = gemv_variant_of(g.M, g.m, g.n);
     const int64_t items = gemv_split(g, batch);
     g.batch = batch;
     if (items > INT32_MAX) return APPROX_EUNSUPPORTED;
