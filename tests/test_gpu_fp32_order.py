@@ -12,6 +12,8 @@ split into chunks, only the last round's tiles split, the row-vector kernel
 with and without a split, batches by stride and by pointer array, tables in
 LDS and in global memory, the native multiplier, and the three Conv2D passes.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -119,7 +121,8 @@ def test_tail_tiles_split_bit_exact(am):
     B = normal(1511, (k, n))
     C = host(am.gemm(dev(A), dev(B)))
     L = check_gemm(am, "mitchell7", A, B, C, what="tail tiles")
-    assert np.any(L == k) and np.any(L < k), np.unique(L)
+    if not os.environ.get("APPROX_KERNEL_SHAPE"):    # the tiling described above is the default shape's
+        assert np.any(L == k) and np.any(L < k), np.unique(L)
 
 
 @pytest.mark.parametrize("transA,transB", [(0, 1), (1, 0), (1, 1)])
