@@ -381,17 +381,20 @@ def time_workload(step, steps, warmup, am, torch):
     """Warm-up steps, then `steps` timed steps bracketed by synchronisations
     (the metric), then `steps` more with the library's HIP events around
     every GEMM-kernel launch on its stream (the kernel time)."""
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    # the interpreter's cyclic garbage collector stays off over the timed
-    # steps (as timeit keeps it): a full collection among the objects the CPU
-    # baselines leave behind took tens of milliseconds and landed inside the
-    # short workloads' timed regions (the MLP's 50 steps: 70.7 against 19.2 ms)
+    # the interpreter's cyclic garbage collector stays off over the warm-up
+    # and timed steps (as timeit keeps it): a full collection among the
+    # objects the CPU baselines leave behind took tens of milliseconds and
+    # landed inside the short workloads' timed regions (the MLP's 50 steps:
+    # 70.7 against 19.2 ms). The collection that precedes runs before the
+    # warm-up, so the GPU does not sit idle right before the timed steps
+    # (that gap had slowed the 10 timed conv steps by 5%).
     gc.collect()
     gc_was_on = gc.isenabled()
     gc.disable()
     try:
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(steps):
             step()
