@@ -32,11 +32,6 @@ constexpr int64_t kSplitSlots = 256;
 constexpr double kSplitMacRate = 6.0e12;
 constexpr double kSplitBytesRate = 4.0e12;
 constexpr int kSplitMax = 1024;
-// Fold rate of one workgroup of each shape relative to shape 0's, as the
-// split model takes it. Shape 2 measured at least shape 0's rate where both
-// fill the GPU (M = 7: 2048^3 1.09 against 1.13 ms, 4096 x 4096 x 1024 2.12 ms
-// each), although it loads its uniform words twice as often per MAC.
-constexpr double kShapeFoldRate[amx::kNumShapes] = {1.0, 1.0, 1.0};
 constexpr int64_t kMaxPanelWords = (int64_t)1 << 31;
 // Few-row GEMMs (B not transposed) run in the row-vector kernel, in blocks
 // of 4 rows, instead of the GEMM kernel's 256-row tiles: always up to
@@ -310,12 +305,15 @@ double plan_split(int64_t tiles, int KB, double tile_macs_per_kstep, int64_t til
 }
 
 // The split of a GEMM-kernel call (a function of its tiling, reduction
-// length, batch and workgroup shape only); returns its modelled time.
-double split_of(int tiles_m, int tiles_n, int TM, int TN, int KB, int m, int n, int batch, int shape, MainParams& mp)
+// length and batch only); returns its modelled time. Every shape is modelled
+// at the same fold rate per workgroup: shape 2 measured at least shape 0's
+// rate where both fill the GPU (M = 7: 2048^3 1.09 against 1.13 ms,
+// 4096 x 4096 x 1024 2.12 ms each), although it loads its uniform words twice
+// as often per MAC.
+double split_of(int tiles_m, int tiles_n, int TM, int TN, int KB, int m, int n, int batch, MainParams& mp)
 {
     const int64_t tiles = (int64_t)tiles_m * tiles_n * batch;
-    return plan_split(tiles, KB, (double)TM * TN * 4 / kShapeFoldRate[shape], (int64_t)TM * TN, (int64_t)m * n * batch,
-                      mp);
+    return plan_split(tiles, KB, (double)TM * TN * 4, (int64_t)TM * TN, (int64_t)m * n * batch, mp);
 }
 
 // Workgroup shape of a call: the 8-wave shape, unless the 12-wave shape's
@@ -342,7 +340,7 @@ int pick_shape(int m, int n, bool dense, int KB, int batch, int* wr, int* wc)
         auto modelled = [&](int sh) {
             const int TM = r[sh] * 64 * kShapes[sh].rows_per_lane, TN = c[sh] * kColsPerWave;
             MainParams tmp{};
-            return split_of((int)cdiv(m, TM), (int)cdiv(n, TN), TM, TN, KB, m, n, batch, sh, tmp);
+            return split_of((int)cdiv(m, TM), (int)cdiv(n, TN), TM, TN, KB, m, n, batch, tmp);
         };
         if (modelled(2) < 0.97 * modelled(0)) shape = 2;
     }
@@ -380,7 +378,7 @@ struct KernelOrder {
 
     KernelOrder(int m, int n, int KB_, int batch, bool dense) : t(tiling_of(m, n, dense, KB_, batch)), KB(KB_)
     {
-        split_of(t.tiles_m, t.tiles_n, t.TM, t.TN, KB, m, n, batch, t.shape, mp);
+        split_of(t.tiles_m, t.tiles_n, t.TM, t.TN, KB, m, n, batch, mp);
     }
     int64_t chunk(int b, int i, int j) const
     {
@@ -428,7 +426,7 @@ int plan_finalize(Plan& pl, int M)
     // M = 0: native multiplier; M = 9..11: table in global memory
     pl.lds_class = M == 0 ? 2 : M <= 7 ? 0 : M == 8 ? 1 : 3;
     const int64_t TM = (int64_t)mp.wr * 64 * kShapes[pl.shape].rows_per_lane, TN = (int64_t)mp.wc * kColsPerWave;
-    split_of(mp.tiles_m, mp.tiles_n, (int)TM, (int)TN, mp.KB, mp.m_out, mp.n_out, pl.batch, pl.shape, mp);
+    split_of(mp.tiles_m, mp.tiles_n, (int)TM, (int)TN, mp.KB, mp.m_out, mp.n_out, pl.batch, mp);
     pl.wbytes = M == 0 ? 4 : (int)sizeof(Word);     // the native multiplier keeps only the operands' bits
     pl.lane_b = align256((size_t)pl.lane_words * pl.batch * pl.wbytes);
     pl.uni_b = align256((size_t)pl.uni_words * pl.batch * pl.wbytes);
