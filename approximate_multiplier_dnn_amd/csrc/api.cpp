@@ -321,13 +321,15 @@ double split_of(int tiles_m, int tiles_n, int TM, int TN, int KB, int m, int n, 
 // by at least 10% less; per MAC the 12-wave shape measured about 10% slower
 // (3 x 3 conv forward: 0.720 against 0.653 ms; attention 1.019 against 0.938
 // ms per GEMM launch on average), while its exact 576-row tiles cut the 3 x 3
-// x 64 weight gradient from 1.065 to 0.622 ms. A dense call (`dense`: a GEMM,
-// not a convolution) takes shape 2 instead of shape 0 when the split model
+// x 64 weight gradient from 1.065 to 0.622 ms. A call in vector mode
+// (`dense`: a GEMM, or a convolution's forward or input-gradient pass; the
+// weight gradient's gather mode has no shape-2 kernel) takes shape 2 instead
+// of shape 0 when the split model
 // gives it at least 3% less time: outputs whose 256 x 128 tiles do not fill
 // the GPU, so that shape 0 splits their reductions into many chunks (the
 // MLP's 256 x 1024 x 1024 GEMMs: 16 chunks of 128 x 128 tiles instead of 32
 // of 256 x 128, 64-71 against 69-76 us per call).
-// APPROX_KERNEL_SHAPE=0, 1 or 2 (2: dense calls only) forces a shape (for
+// APPROX_KERNEL_SHAPE=0, 1 or 2 (2: vector mode only) forces a shape (for
 // measurements).
 int pick_shape(int m, int n, bool dense, int KB, int batch, int* wr, int* wc)
 {
@@ -920,7 +922,8 @@ int build_conv_plan(ConvKind kind, const ConvShape& s, Plan& pl)
 
     int m, n;
     conv_gemm_extent(kind, s, &m, &n);
-    const Tiling tg = tiling_of(m, n, false, 0, 1);
+    // the forward and input-gradient passes run in vector mode: any shape
+    const Tiling tg = tiling_of(m, n, kind != CONV_WGRAD, conv_ksteps(kind, s), 1);
     pl.shape = tg.shape;
     mp.wr = tg.wr;
     mp.wc = tg.wc;
@@ -1451,7 +1454,7 @@ extern "C" int approx_conv2d_chunks(int pass, int N, int H, int W, int C, int K,
     conv_gemm_extent(kind, s, &m, &n);
     for (long long t = 0; t < count; ++t)
         if (idx[t] < 0 || idx[t] >= (long long)m * n) return APPROX_EINVAL;
-    const KernelOrder ord(m, n, conv_ksteps(kind, s), 1, false);
+    const KernelOrder ord(m, n, conv_ksteps(kind, s), 1, kind != CONV_WGRAD);
     for (long long t = 0; t < count; ++t) chunk[t] = ord.chunk(0, (int)(idx[t] / n), (int)(idx[t] % n));
     return APPROX_OK;
 }

@@ -31,8 +31,9 @@ struct Word {
 // covers 64 * rows_per_lane rows and kColsPerWave columns. Shape 0: 8 waves
 // (2 per SIMD) x 4 rows; shape 1: 12 waves (3 per SIMD) x 3 rows, which hides
 // more lookup latency at the cost of coarser row tiles; shape 2: 8 waves x 2
-// rows, tiles of half the area of shape 0's for small dense GEMMs, whose
-// reductions then split into half as many chunks (dense calls only).
+// rows, tiles of half the area of shape 0's for small outputs, whose
+// reductions then split into half as many chunks (vector mode only: GEMMs and
+// the convolution's forward and input-gradient passes).
 struct KernelShape {
     int waves, rows_per_lane;
 };

@@ -143,10 +143,12 @@ def _plan_info(kind, args, M):
     return int(items), out
 
 
-def test_shape_choice_follows_the_split_model():
+def test_shape_choice_follows_the_split_model(monkeypatch):
     """Small dense GEMMs (the MLP's) take the 128 x 128 tiles of shape 2 and
     half as many reduction chunks as shape 0 would cut; GEMMs whose 256 x 128
-    tiles fill the GPU keep shape 0; convolutions never take shape 2."""
+    tiles fill the GPU keep shape 0; the convolution's weight gradient (gather
+    mode, which has no shape-2 kernel) never takes shape 2."""
+    monkeypatch.delenv("APPROX_KERNEL_SHAPE", raising=False)
     _, o = _plan_info(0, (0, 0, 256, 1024, 1024, 1), 7)
     assert (o[0], o[3], o[4], o[8]) == (2, 128, 128, 16), list(o)
     _, o = _plan_info(0, (1, 0, 1024, 1024, 256, 1), 7)
@@ -155,6 +157,5 @@ def test_shape_choice_follows_the_split_model():
         _, o = _plan_info(0, args, 8)
         assert o[0] == 0, (args, list(o))
     for args in _conv_cases():
-        for kind in (1, 2, 3):
-            _, o = _plan_info(kind, args, 7)
-            assert o[0] in (0, 1), (kind, args, list(o))
+        _, o = _plan_info(3, args, 7)
+        assert o[0] in (0, 1), (args, list(o))
