@@ -6,7 +6,8 @@ oracle's FP32 sums in the summation order the library reports for that
 shape (approx_gemm_chunks under the same setting), bit for bit, on whole
 rows and columns and a random sample: tables in LDS (M = 7, M = 8 with its
 second copies) and in global memory (M = 10), all four transposes, split
-and whole tiles, ragged edges.
+and whole tiles, ragged edges; and the convolution's three passes, whose
+forward and input-gradient passes run in vector mode like the GEMMs.
 """
 import os
 
@@ -75,3 +76,43 @@ def test_forced_shape_gives_the_fp32_order_sums(am, shape, name, case):
     F = oracle.gemm_f32_at(A, B, t, M, rows, cols, np.maximum(L, 1), transA=bool(tA), transB=bool(tB),
                            threads=oracle.default_threads())
     same_bits(C.cpu().numpy()[rows, cols], F, what=f"shape {shape} {name} {CASES[case]}", zero_sign=True)
+
+
+CONV_GEOMS = [
+    # (N, H, W, C, K, R, S, stride, pad)
+    (2, 9, 11, 5, 7, 3, 3, (1, 1), (1, 1)),
+    (3, 16, 16, 8, 12, 3, 3, (2, 2), (1, 0)),
+]
+
+
+@pytest.mark.parametrize("shape", ["0", "1", "2"])
+@pytest.mark.parametrize("name", ["mitchell7", "perturbed8"])
+@pytest.mark.parametrize("g", range(len(CONV_GEOMS)))
+def test_forced_shape_conv_passes(am, shape, name, g):
+    """The convolution's three passes with a shape forced (the weight
+    gradient's gather mode ignores shape 2 and keeps its own choice): every
+    output the oracle's FP32 sums in the reported order, bit for bit."""
+    M, t = TABLES[name]()
+    am.approx_lut_load(t, M)
+    N, H, W, C, K, R, S, st, pd = geom = CONV_GEOMS[g]
+    P, Q = oracle.conv_out_hw(H, W, R, S, st, pd)
+    x = normal(9440 + g, (N, H, W, C))
+    w = normal(9441 + g, (R, S, C, K))
+    dy = normal(9442 + g, (N, P, Q, K))
+    print(f"shape {shape} {name} conv {geom}", flush=True)
+    os.environ["APPROX_KERNEL_SHAPE"] = shape
+    try:
+        outs = {"fwd": (am.conv2d_fwd(dev(x), dev(w), st, pd), x, w),
+                "dgrad": (am.conv2d_dgrad(dev(dy), dev(w), x.shape, st, pd), dy, w),
+                "wgrad": (am.conv2d_wgrad(dev(x), dev(dy), w.shape, st, pd), x, dy)}
+        torch.cuda.synchronize()
+        chunks = {}
+        for pname, (got, _, _) in outs.items():
+            idx = np.arange(got.numel(), dtype=np.int64)
+            chunks[pname] = (idx, am.approx_conv2d_chunks(pname, N, H, W, C, K, R, S, st, pd, idx))
+    finally:
+        os.environ.pop("APPROX_KERNEL_SHAPE", None)
+    for pname, (got, t1, t2) in outs.items():
+        idx, L = chunks[pname]
+        F = oracle.conv2d_f32(pname, t1, t2, geom, t, M, L, idx=idx, threads=oracle.default_threads())
+        same_bits(got.cpu().numpy(), F, what=f"shape {shape} {name} conv {geom} {pname}", zero_sign=True)
